@@ -1,0 +1,237 @@
+"""Float64 CPU oracle for fused scaled dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent reference that the
+HIP kernels are checked against.  Only the test suite, the smoke entry point
+and the CPU-baseline leg of the benchmark may import or call it; the library's
+product path never does.  It shares no code, constant or helper with the HIP
+path and imports nothing from it.
+
+What it computes (plain definitions, written out; one (batch, head) at a time,
+materialising the whole S x S score matrix exactly as the naive attention of
+the codelab "Speed up attention on GPU with cuDNN and TransformerEngine",
+section 4 "Implement attention from scratch", does):
+
+  * scores  s_ij = scale * q_i . k_j                 (codelab, "How attention works",
+                                                      steps 1-2; scale defaults to
+                                                      1/sqrt(d_qk): TransformerEngine
+                                                      "JAX: Single-GPU Attention",
+                                                      "Other attention knobs", score scaling)
+  * mask    causal / sliding window / padding        (TE single-GPU page, sections 1-2;
+                                                      codelab section 7)
+  * softmax vanilla, off-by-one or learnable sink     (PR "[JAX] Add support for sink
+                                                      attention in JAX" #2225, the
+                                                      softmax formulas in the review
+                                                      summaries' sequence diagrams)
+  * output  O = P V                                  (codelab, "How attention works", step 3)
+  * LSE     natural-log log-sum-exp of each row, sink term included
+  * grads   dQ, dK, dV of L = sum(dO * O), and the gradient of the sink logit
+            (PR #2225: the backward returns grad_q, grad_k, grad_v and
+            grad_softmax_offset)
+
+Readings taken where the pages are silent or disagree (each also listed in the
+design notes):
+  * off-by-one softmax = one extra logit of value 0 (denominator 1 + sum exp);
+    PR #2225 review thread on the Softmax module offset settles 0, not 1.
+  * learnable softmax: softmax_offset holds the raw logit alpha_h per query head;
+    denominator adds exp(alpha_h), unscaled by scale_factor.
+  * GQA: query head h reads kv head floor(h / (Hq/Hkv)) (K/V heads repeated, TE
+    single-GPU page section 1; codelab section 9 "each shared by 4 query heads").
+  * window (left, right) is inclusive: key j is visible from row i iff
+    i-left <= j <= i+right; -1 means unbounded.
+  * seqlens[b] right-pads both queries and keys; rows and keys at or beyond it
+    are invisible.  Empty rows give O = 0, LSE = -inf (vanilla) or the sink logit.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+VANILLA = "vanilla"
+OFF_BY_ONE = "off_by_one"
+LEARNABLE = "learnable"
+SOFTMAX_TYPES = (VANILLA, OFF_BY_ONE, LEARNABLE)
+
+
+def kv_head(h: int, num_heads: int, num_kv_heads: int) -> int:
+    """KV head read by query head h: contiguous groups of Hq/Hkv query heads.
+
+    TE single-GPU page, section 1 (the baseline repeats K/V heads for GQA) and
+    section 2 (num_gqa_groups = number of KV heads); codelab section 9.
+    """
+    return h // (num_heads // num_kv_heads)
+
+
+def visible_mask(S: int, L: int, causal: bool, window_left: int, window_right: int) -> np.ndarray:
+    """Boolean [S, S] matrix: True where query row i may attend to key j.
+
+    Intersection of padding (i < L and j < L), the causal lower triangle
+    (codelab section 7, j <= i) and the sliding window (TE single-GPU page
+    section 2, window_size = (left, right), -1 unbounded).
+    """
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    m = (i < L) & (j < L)
+    if causal:
+        m &= j <= i
+    if window_left >= 0:
+        m &= j >= i - window_left
+    if window_right >= 0:
+        m &= j <= i + window_right
+    return m
+
+
+def sink_logit(softmax_type: str, softmax_offset, h: int):
+    """The extra softmax logit z for query head h, or None for vanilla.
+
+    PR #2225 sequence diagrams: off-by-one adds 1 = exp(0) to the denominator,
+    learnable adds exp(alpha[h]).
+    """
+    if softmax_type == VANILLA:
+        return None
+    if softmax_type == OFF_BY_ONE:
+        return 0.0
+    if softmax_type == LEARNABLE:
+        return float(np.asarray(softmax_offset, dtype=np.float64).reshape(-1)[h])
+    raise ValueError(f"unknown softmax_type {softmax_type!r}")
+
+
+def _softmax_rows(s: np.ndarray, mask: np.ndarray, z):
+    """Masked row softmax with optional sink logit z (a logit with no value row).
+
+    Returns (P, LSE): P_ij = exp(s_ij - LSE_i) on visible entries, 0 elsewhere;
+    LSE_i = log(sum_visible exp(s_ij) + [sink] exp(z)).
+    """
+    neg = np.where(mask, s, -np.inf)
+    m = neg.max(axis=1)
+    if z is not None:
+        m = np.maximum(m, z)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(mask, np.exp(neg - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    if z is not None:
+        l = l + np.exp(z - m_safe)
+    with np.errstate(divide="ignore"):
+        lse = np.where(l > 0, m_safe + np.log(l), -np.inf)
+    lse_safe = np.where(np.isfinite(lse), lse, 0.0)
+    p = np.where(mask, np.exp(neg - lse_safe[:, None]), 0.0)
+    return p, lse
+
+
+def _resolve(q, k, v, num_gqa_groups, scale_factor):
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    if k.shape != (B, S, Hkv, dqk) or v.shape[:3] != (B, S, Hkv):
+        raise ValueError("K/V shapes do not match Q and num_gqa_groups")
+    if Hq % Hkv:
+        raise ValueError("num_heads must be a multiple of num_gqa_groups")
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    return B, S, Hq, Hkv, dqk, v.shape[3], scale
+
+
+def attention_group(q, k, v, d_o, *, b, g, num_gqa_groups=None, causal=True,
+                    window=(-1, -1), scale_factor=None, softmax_type=VANILLA,
+                    softmax_offset=None, seqlens=None, want_grads=True):
+    """Forward (and backward) for one batch b and one KV head g, in float64.
+
+    Computes every query head of the group.  Returns a dict with
+      o    [S, G, dv]   lse [G, S]   (forward)
+      dq   [S, G, dqk]  dk  [S, dqk]  dv [S, dv]
+      dz   [G]          this batch's share of d(sink logit) per query head
+    Inputs may be any float dtype; they are upcast to float64 exactly.
+    """
+    B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
+    G = Hq // Hkv
+    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+    mask = visible_mask(S, L, causal, int(window[0]), int(window[1]))
+    kb = np.asarray(k[b, :, g, :], dtype=np.float64)
+    vb = np.asarray(v[b, :, g, :], dtype=np.float64)
+    out = {"o": np.zeros((S, G, dv_dim)), "lse": np.zeros((G, S))}
+    if want_grads:
+        out.update(dq=np.zeros((S, G, dqk)), dk=np.zeros((S, dqk)),
+                   dv=np.zeros((S, dv_dim)), dz=np.zeros(G))
+    for gi in range(G):
+        h = g * G + gi
+        assert kv_head(h, Hq, Hkv) == g
+        qh = np.asarray(q[b, :, h, :], dtype=np.float64)
+        z = sink_logit(softmax_type, softmax_offset, h)
+        s = scale * (qh @ kb.T)                       # score + scale
+        p, lse = _softmax_rows(s, mask, z)            # softmax (+ sink)
+        o = p @ vb                                    # attend
+        out["o"][:, gi, :] = o
+        out["lse"][gi] = lse
+        if not want_grads:
+            continue
+        doh = np.asarray(d_o[b, :, h, :], dtype=np.float64)
+        dp = doh @ vb.T                               # dL/dP
+        delta = (doh * o).sum(axis=1)                 # rowsum(dO * O) = sum_j P_ij dP_ij
+        ds = p * (dp - delta[:, None])                # softmax Jacobian applied to dP
+        out["dq"][:, gi, :] = scale * (ds @ kb)
+        out["dk"] += scale * (ds.T @ qh)
+        out["dv"] += p.T @ doh
+        if z is not None:
+            # dL/dz_i = -p_sink,i * delta_i with p_sink,i = exp(z - LSE_i):
+            # the sink enters only the denominator and carries a zero value row.
+            lse_safe = np.where(np.isfinite(lse), lse, z)
+            out["dz"][gi] = -(np.exp(z - lse_safe) * delta).sum()
+    return out
+
+
+def attention(q, k, v, d_o=None, *, num_gqa_groups=None, causal=True, window=(-1, -1),
+              scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None):
+    """Whole-problem oracle (small shapes): assembles every (batch, kv head) group.
+
+    Returns dict o [B,S,Hq,dv], lse [B,Hq,S] and, when d_o is given,
+    dq [B,S,Hq,dqk], dk [B,S,Hkv,dqk], dv [B,S,Hkv,dv], dalpha [Hq]
+    (dalpha is None for vanilla softmax).
+    """
+    B, S, Hq, Hkv, dqk, dv_dim, _ = _resolve(q, k, v, num_gqa_groups, scale_factor)
+    G = Hq // Hkv
+    grads = d_o is not None
+    res = {"o": np.zeros((B, S, Hq, dv_dim)), "lse": np.zeros((B, Hq, S))}
+    if grads:
+        res.update(dq=np.zeros((B, S, Hq, dqk)), dk=np.zeros((B, S, Hkv, dqk)),
+                   dv=np.zeros((B, S, Hkv, dv_dim)), dalpha=np.zeros(Hq))
+    for b in range(B):
+        for g in range(Hkv):
+            r = attention_group(q, k, v, d_o, b=b, g=g, num_gqa_groups=Hkv, causal=causal,
+                                window=window, scale_factor=scale_factor,
+                                softmax_type=softmax_type, softmax_offset=softmax_offset,
+                                seqlens=seqlens, want_grads=grads)
+            hs = slice(g * G, (g + 1) * G)
+            res["o"][b, :, hs, :] = r["o"]
+            res["lse"][b, hs, :] = r["lse"]
+            if grads:
+                res["dq"][b, :, hs, :] = r["dq"]
+                res["dk"][b, :, g, :] = r["dk"]
+                res["dv"][b, :, g, :] = r["dv"]
+                res["dalpha"][hs] += r["dz"]
+    if grads and softmax_type == VANILLA:
+        res["dalpha"] = None
+    return res
+
+
+def visible_pairs(S: int, L: int, causal: bool, window_left: int, window_right: int) -> int:
+    """Number of visible (query, key) pairs of one (batch, head), in closed form.
+
+    Row i < L sees keys max(0, i-left) .. min(L-1, i [causal], i+right).
+    """
+    total = 0
+    for i in range(min(L, S)):
+        hi = L - 1
+        if causal:
+            hi = min(hi, i)
+        if window_right >= 0:
+            hi = min(hi, i + window_right)
+        lo = max(0, i - window_left) if window_left >= 0 else 0
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def effective_flops(pairs: int, d_qk: int, d_v: int):
+    """Effective FLOPs of forward and backward over the visible pairs.
+
+    forward: score (2 d_qk) and attend (2 d_v) per pair; backward: score
+    recompute, dP, dV, dK, dQ = 2 (3 d_qk + 2 d_v) per pair.
+    """
+    return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)

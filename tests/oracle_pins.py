@@ -1,0 +1,454 @@
+"""Pins for the float64 oracle: checks against things other than the oracle itself.
+
+Each pin is a function of the oracle *module*, so the same pins run against the
+real oracle (test_oracle_pins.py) and against copies of it with a planted
+mistake (test_oracle_mutants.py), which must fail at least one pin.
+
+What pins what:
+  brute_force      whole forward: scalar loops over the softmax definition
+                   exp(s)/ (sum exp(s) [+ exp(z)]) with no max shift (PR #2225
+                   sequence diagrams; codelab "How attention works")
+  finite_diff      dQ, dK, dV, d(alpha): central differences of sum(dO * O)
+  row_sums         sum_j P_ij = 1 (vanilla) or 1 - exp(z - LSE_i) (sink), via V = 1
+  gqa_repeat       GQA equals MHA on K/V heads repeated in contiguous groups
+                   (TE single-GPU page section 1; codelab section 9)
+  causal_rows      first causal row attends only to itself, last row equals the
+                   unmasked one (codelab section 7)
+  sink_augmented   sink softmax equals vanilla softmax over one extra key whose
+                   score is exactly z and whose value row is 0 (PR #2225 review
+                   thread: the offset is an extra logit)
+  sink_closed      closed form of the first causal row with a sink; off-by-one ==
+                   learnable with alpha = 0; alpha = -1e4 == vanilla
+  dalpha_forms     d(alpha) closed form == finite difference == augmented-key grad
+  padding          a padded batch equals the truncated unpadded problem; padded
+                   rows and keys are exactly zero
+  window_limits    left >= S-1 with causal == causal; left = 0 => O_i = V_i
+  scale            attn(Q, scale=c) == attn(cQ, scale=1), sink logit unscaled
+  torch_sdpa       torch.nn.functional.scaled_dot_product_attention (CPU float64)
+                   with autograd: O, dQ, dK, dV and, through an additive mask
+                   column, d(alpha)
+  golden           hand-derived closed forms stored under tests/golden/
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rand_case(seed, B=2, S=9, Hq=4, Hkv=2, dqk=5, dv=3, sink=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S, Hq, dqk))
+    k = rng.standard_normal((B, S, Hkv, dqk))
+    v = rng.standard_normal((B, S, Hkv, dv))
+    do = rng.standard_normal((B, S, Hq, dv))
+    alpha = rng.standard_normal(Hq)
+    return q, k, v, do, alpha
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(a - b))
+    bound = atol + rtol * np.maximum(np.abs(np.where(both_inf, 0, a)), np.abs(np.where(both_inf, 0, b)))
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: max err {np.nanmax(np.where(bad, err, 0))} at {np.argwhere(bad)[:3].tolist()}"
+
+
+def brute_forward(q, k, v, Hkv, causal, wl, wr, scale, stype, alpha, seqlens):
+    """Scalar loops over the definition, no max shift (inputs are small)."""
+    B, S, Hq, dqk = q.shape
+    dv = v.shape[3]
+    G = Hq // Hkv
+    o = np.zeros((B, S, Hq, dv))
+    lse = np.zeros((B, Hq, S))
+    for b in range(B):
+        L = S if seqlens is None else int(seqlens[b])
+        for h in range(Hq):
+            g = h // G
+            for i in range(S):
+                num = [0.0] * dv
+                den = 0.0
+                for j in range(S):
+                    vis = (i < L and j < L and (not causal or j <= i)
+                           and (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr))
+                    if not vis:
+                        continue
+                    s = scale * sum(float(q[b, i, h, d]) * float(k[b, j, g, d]) for d in range(dqk))
+                    e = math.exp(s)
+                    den += e
+                    for d in range(dv):
+                        num[d] += e * float(v[b, j, g, d])
+                if stype == "off_by_one":
+                    den += math.exp(0.0)
+                elif stype == "learnable":
+                    den += math.exp(float(alpha[h]))
+                for d in range(dv):
+                    o[b, i, h, d] = num[d] / den if den > 0 else 0.0
+                lse[b, h, i] = math.log(den) if den > 0 else -math.inf
+    return o, lse
+
+
+MASK_CASES = [
+    # causal, (left, right), seqlens
+    (True, (-1, -1), None),
+    (False, (-1, -1), None),
+    (True, (3, 0), [9, 5]),
+    (False, (2, 1), [6, 9]),
+    (True, (0, 0), None),
+    (False, (-1, 2), [0, 7]),
+    (True, (-1, -1), [1, 9]),
+]
+
+
+def pin_brute_force(orc):
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(100 + ci)
+            scale = 0.37
+            sl_np = None if sl is None else np.array(sl)
+            r = orc.attention(q, k, v, None, num_gqa_groups=2, causal=causal, window=win,
+                              scale_factor=scale, softmax_type=st, softmax_offset=alpha,
+                              seqlens=sl_np)
+            o, lse = brute_forward(q, k, v, 2, causal, win[0], win[1], scale, st, alpha, sl)
+            _close(r["o"], o, 1e-12, 1e-14, f"O case{ci} {st}")
+            _close(r["lse"], lse, 1e-12, 1e-14, f"LSE case{ci} {st}")
+
+
+def _loss(orc, q, k, v, do, alpha, **kw):
+    r = orc.attention(q, k, v, None, softmax_offset=alpha, **kw)
+    return float((r["o"] * do).sum())
+
+
+def pin_finite_diff(orc):
+    h = 1e-6
+    for ci, (causal, win, sl) in enumerate([(True, (-1, -1), None), (False, (2, 1), [5, 7]),
+                                            (True, (3, 0), [7, 4])]):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(200 + ci, B=2, S=7, Hq=4, Hkv=2, dqk=3, dv=2)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.6,
+                      softmax_type=st, seqlens=None if sl is None else np.array(sl))
+            r = orc.attention(q, k, v, do, softmax_offset=alpha, **kw)
+            for name, arr, grad in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+                fd = np.zeros_like(arr)
+                for idx in np.ndindex(arr.shape):
+                    a0 = arr[idx]
+                    arr[idx] = a0 + h
+                    lp = _loss(orc, q, k, v, do, alpha, **kw)
+                    arr[idx] = a0 - h
+                    lm = _loss(orc, q, k, v, do, alpha, **kw)
+                    arr[idx] = a0
+                    fd[idx] = (lp - lm) / (2 * h)
+                _close(grad, fd, 1e-6, 1e-8, f"d{name} case{ci} {st}")
+            if st != "vanilla":
+                fd = np.zeros(4)
+                for hh in range(4):
+                    a2 = alpha.copy()
+                    if st == "learnable":
+                        a2[hh] += h
+                        lp = _loss(orc, q, k, v, do, a2, **kw)
+                        a2[hh] -= 2 * h
+                        lm = _loss(orc, q, k, v, do, a2, **kw)
+                        fd[hh] = (lp - lm) / (2 * h)
+                if st == "learnable":
+                    _close(r["dalpha"], fd, 1e-6, 1e-8, f"dalpha case{ci}")
+            else:
+                assert r["dalpha"] is None
+
+
+def pin_row_sums(orc):
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(300 + ci, dv=1)
+            ones = np.ones_like(v)
+            r = orc.attention(q, k, ones, None, num_gqa_groups=2, causal=causal, window=win,
+                              softmax_type=st, softmax_offset=alpha,
+                              seqlens=None if sl is None else np.array(sl))
+            B, S = q.shape[:2]
+            for b in range(B):
+                L = S if sl is None else sl[b]
+                for h in range(4):
+                    rs = r["o"][b, :L, h, 0]
+                    if st == "vanilla":
+                        expect = np.ones(L)
+                    else:
+                        z = 0.0 if st == "off_by_one" else alpha[h]
+                        expect = 1.0 - np.exp(z - r["lse"][b, h, :L])
+                        assert (rs < 1).all()
+                    _close(rs, expect, 1e-12, 1e-13, f"rowsum case{ci} {st}")
+
+
+def pin_gqa_repeat(orc):
+    for Hq, Hkv in ((4, 2), (6, 3), (4, 1), (4, 4)):
+        G = Hq // Hkv
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(400 + Hq * 10 + Hkv, Hq=Hq, Hkv=Hkv)
+            alpha = np.random.default_rng(1).standard_normal(Hq)
+            kw = dict(causal=True, window=(4, 0), softmax_type=st, softmax_offset=alpha,
+                      seqlens=np.array([9, 6]))
+            r = orc.attention(q, k, v, do, num_gqa_groups=Hkv, **kw)
+            kr = np.repeat(k, G, axis=2)
+            vr = np.repeat(v, G, axis=2)
+            m = orc.attention(q, kr, vr, do, num_gqa_groups=Hq, **kw)
+            _close(r["o"], m["o"], 1e-13, 1e-14, "O")
+            _close(r["lse"], m["lse"], 1e-13, 1e-14, "LSE")
+            _close(r["dq"], m["dq"], 1e-12, 1e-13, "dQ")
+            B, S = q.shape[:2]
+            _close(r["dk"], m["dk"].reshape(B, S, Hkv, G, -1).sum(axis=3), 1e-12, 1e-13, "dK")
+            _close(r["dv"], m["dv"].reshape(B, S, Hkv, G, -1).sum(axis=3), 1e-12, 1e-13, "dV")
+            if st != "vanilla":
+                _close(r["dalpha"], m["dalpha"], 1e-12, 1e-13, "dalpha")
+
+
+def pin_causal_rows(orc):
+    q, k, v, do, alpha = rand_case(500, S=11)
+    c = orc.attention(q, k, v, None, num_gqa_groups=2, causal=True)
+    n = orc.attention(q, k, v, None, num_gqa_groups=2, causal=False)
+    _close(c["o"][:, -1], n["o"][:, -1], 1e-13, 1e-14, "last row")
+    _close(c["lse"][:, :, -1], n["lse"][:, :, -1], 1e-13, 1e-14, "last row lse")
+    G = 2
+    for h in range(4):
+        _close(c["o"][:, 0, h], v[:, 0, h // G], 1e-13, 1e-14, "row 0 = V_0")
+    assert np.abs(c["o"][:, 0] - n["o"][:, 0]).max() > 1e-3
+
+
+def pin_sink_augmented(orc):
+    """Sink softmax == vanilla over an extra key with score z and a zero value."""
+    B, S, Hq, Hkv, dqk, dv = 2, 8, 4, 2, 5, 3
+    q, k, v, do, alpha = rand_case(600, B, S, Hq, Hkv, dqk, dv)
+    scale = 0.45
+    G = Hq // Hkv
+    for st in ("off_by_one", "learnable"):
+        r = orc.attention(q, k, v, do, num_gqa_groups=Hkv, causal=False, scale_factor=scale,
+                          softmax_type=st, softmax_offset=alpha)
+        z = np.zeros(Hq) if st == "off_by_one" else alpha
+        # MHA over S+1 positions; Q gets a constant-1 extra feature, real keys a 0,
+        # the extra key (position S) has features (0.., z_h / scale) and value 0.
+        qa = np.zeros((B, S + 1, Hq, dqk + 1))
+        qa[:, :S, :, :dqk] = q
+        qa[:, :, :, dqk] = 1.0
+        ka = np.zeros((B, S + 1, Hq, dqk + 1))
+        ka[:, :S, :, :dqk] = np.repeat(k, G, axis=2)
+        ka[:, S, :, dqk] = z / scale
+        va = np.zeros((B, S + 1, Hq, dv))
+        va[:, :S] = np.repeat(v, G, axis=2)
+        doa = np.zeros((B, S + 1, Hq, dv))
+        doa[:, :S] = do
+        a = orc.attention(qa, ka, va, doa, num_gqa_groups=Hq, causal=False, scale_factor=scale)
+        _close(r["o"], a["o"][:, :S], 1e-12, 1e-14, f"O {st}")
+        _close(r["lse"], a["lse"][:, :, :S], 1e-12, 1e-14, f"LSE {st}")
+        _close(r["dq"], a["dq"][:, :S, :, :dqk], 1e-11, 1e-13, f"dQ {st}")
+        _close(r["dk"], a["dk"][:, :S, :, :dqk].reshape(B, S, Hkv, G, dqk).sum(3), 1e-11, 1e-13, f"dK {st}")
+        _close(r["dv"], a["dv"][:, :S].reshape(B, S, Hkv, G, dv).sum(3), 1e-11, 1e-13, f"dV {st}")
+        # d score(extra key) = d k_extra[last] / scale, summed over batches.
+        dz = a["dk"][:, S, :, dqk].sum(axis=0) / scale
+        _close(r["dalpha"], dz, 1e-10, 1e-13, f"dalpha {st}")
+
+
+def pin_sink_closed(orc):
+    q, k, v, do, alpha = rand_case(700, S=6)
+    scale = 0.5
+    G = 2
+    for st in ("off_by_one", "learnable"):
+        r = orc.attention(q, k, v, None, num_gqa_groups=2, causal=True, scale_factor=scale,
+                          softmax_type=st, softmax_offset=alpha)
+        for b in range(2):
+            for h in range(4):
+                z = 0.0 if st == "off_by_one" else alpha[h]
+                s00 = scale * float(q[b, 0, h] @ k[b, 0, h // G])
+                w = math.exp(s00) / (math.exp(z) + math.exp(s00))
+                _close(r["o"][b, 0, h], w * v[b, 0, h // G], 1e-13, 1e-15, f"row0 {st}")
+                _close(r["lse"][b, h, 0], math.log(math.exp(z) + math.exp(s00)), 1e-13, 0, "lse0")
+    kw = dict(num_gqa_groups=2, causal=True, window=(3, 0), seqlens=np.array([6, 4]))
+    a = orc.attention(q, k, v, do, softmax_type="off_by_one", **kw)
+    b_ = orc.attention(q, k, v, do, softmax_type="learnable", softmax_offset=np.zeros(4), **kw)
+    for key in ("o", "lse", "dq", "dk", "dv", "dalpha"):
+        _close(a[key], b_[key], 0, 0, f"obo==learnable(0) {key}")
+    c = orc.attention(q, k, v, do, softmax_type="learnable", softmax_offset=np.full(4, -1e4), **kw)
+    d = orc.attention(q, k, v, do, softmax_type="vanilla", **kw)
+    for key in ("o", "dq", "dk", "dv"):
+        _close(c[key], d[key], 1e-13, 1e-15, f"alpha=-1e4 == vanilla {key}")
+    _close(c["lse"][:, :, :4], d["lse"][:, :, :4], 1e-13, 1e-15, "lse")
+
+
+def pin_dalpha_forms(orc):
+    q, k, v, do, alpha = rand_case(800, B=3, S=8)
+    kw = dict(num_gqa_groups=2, causal=True, window=(4, 0), scale_factor=0.4,
+              seqlens=np.array([8, 5, 3]))
+    r = orc.attention(q, k, v, do, softmax_type="learnable", softmax_offset=alpha, **kw)
+    h = 1e-6
+    fd = np.zeros(4)
+    for hh in range(4):
+        ap = alpha.copy(); ap[hh] += h
+        am = alpha.copy(); am[hh] -= h
+        fd[hh] = (_loss(orc, q, k, v, do, ap, softmax_type="learnable", **kw)
+                  - _loss(orc, q, k, v, do, am, softmax_type="learnable", **kw)) / (2 * h)
+    _close(r["dalpha"], fd, 1e-6, 1e-9, "dalpha vs fd")
+    # closed form from the returned O and LSE
+    delta = (r["o"] * do).sum(axis=3)                    # [B,S,Hq]
+    cf = -(np.exp(alpha[None, :, None] - r["lse"]) * delta.transpose(0, 2, 1)).sum(axis=(0, 2))
+    _close(r["dalpha"], cf, 1e-12, 1e-14, "dalpha closed form")
+
+
+def pin_padding(orc):
+    q, k, v, do, alpha = rand_case(900, B=3, S=10)
+    sl = np.array([10, 6, 0])
+    for st in orc.SOFTMAX_TYPES:
+        for causal, win in ((True, (-1, -1)), (False, (3, 2)), (True, (2, 0))):
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, softmax_type=st,
+                      softmax_offset=alpha)
+            r = orc.attention(q, k, v, do, seqlens=sl, **kw)
+            for b in range(3):
+                L = sl[b]
+                if L > 0:
+                    # same arithmetic on a smaller matrix: equal up to BLAS summation order
+                    t = orc.attention(q[b:b + 1, :L], k[b:b + 1, :L], v[b:b + 1, :L],
+                                      do[b:b + 1, :L], **kw)
+                    _close(r["o"][b, :L], t["o"][0], 1e-13, 1e-15, "O")
+                    _close(r["lse"][b, :, :L], t["lse"][0], 1e-13, 1e-15, "LSE")
+                    _close(r["dq"][b, :L], t["dq"][0], 1e-13, 1e-15, "dQ")
+                    _close(r["dk"][b, :L], t["dk"][0], 1e-13, 1e-15, "dK")
+                    _close(r["dv"][b, :L], t["dv"][0], 1e-13, 1e-15, "dV")
+                assert (r["o"][b, L:] == 0).all() and (r["dq"][b, L:] == 0).all()
+                assert (r["dk"][b, L:] == 0).all() and (r["dv"][b, L:] == 0).all()
+                z = -np.inf if st == "vanilla" else (0.0 if st == "off_by_one" else alpha)
+                pad_lse = r["lse"][b, :, L:]
+                expect = np.broadcast_to(np.reshape(z, (-1, 1)) if st == "learnable" else z, pad_lse.shape)
+                _close(pad_lse, expect, 0, 0, "padded LSE")
+
+
+def pin_window_limits(orc):
+    S = 9
+    for L in (9, 5):
+        assert (orc.visible_mask(S, L, True, S - 1, 0) == orc.visible_mask(S, L, True, -1, -1)).all()
+        assert (orc.visible_mask(S, L, True, S + 5, 3) == orc.visible_mask(S, L, True, -1, -1)).all()
+    q, k, v, do, alpha = rand_case(1000, S=S)
+    r = orc.attention(q, k, v, None, num_gqa_groups=2, causal=True, window=(0, 0))
+    for h in range(4):
+        _close(r["o"][:, :, h], v[:, :, h // 2], 1e-13, 1e-15, "left=0 => O=V")
+    r = orc.attention(q, k, v, None, num_gqa_groups=2, causal=False, window=(0, 0))
+    for h in range(4):
+        _close(r["o"][:, :, h], v[:, :, h // 2], 1e-13, 1e-15, "(0,0) => O=V")
+    m = orc.visible_mask(6, 6, False, 1, 2)
+    expect = np.array([[abs(i - j) <= (1 if j < i else 2) for j in range(6)] for i in range(6)])
+    assert (m == expect).all()
+    assert orc.visible_pairs(S, S, True, -1, -1) == S * (S + 1) // 2
+    for causal in (True, False):
+        for wl in (-1, 0, 2, 7):
+            for wr in (-1, 0, 1, 4):
+                for L in (0, 3, 9):
+                    assert orc.visible_pairs(S, L, causal, wl, wr) == int(orc.visible_mask(S, L, causal, wl, wr).sum())
+
+
+def pin_scale(orc):
+    q, k, v, do, alpha = rand_case(1100)
+    c = 0.73
+    for st in orc.SOFTMAX_TYPES:
+        kw = dict(num_gqa_groups=2, causal=True, window=(5, 0), softmax_type=st,
+                  softmax_offset=alpha, seqlens=np.array([9, 7]))
+        a = orc.attention(q, k, v, do, scale_factor=c, **kw)
+        b = orc.attention(c * q, k, v, do, scale_factor=1.0, **kw)
+        _close(a["o"], b["o"], 1e-12, 1e-14, "O")
+        _close(a["lse"], b["lse"], 1e-12, 1e-14, "LSE")
+        _close(a["dq"], c * b["dq"], 1e-12, 1e-14, "dQ")
+        _close(a["dk"], b["dk"], 1e-12, 1e-14, "dK")
+        _close(a["dv"], b["dv"], 1e-12, 1e-14, "dV")
+    d = orc.attention(q[:, :, :, :4], k[:, :, :, :4], v, None, num_gqa_groups=2, causal=False)
+    e = orc.attention(0.5 * q[:, :, :, :4], k[:, :, :, :4], v, None, num_gqa_groups=2,
+                      causal=False, scale_factor=1.0)
+    _close(d["o"], e["o"], 1e-12, 1e-14, "default scale = 1/sqrt(d_qk)")
+
+
+def pin_torch_sdpa(orc):
+    import torch
+    F = torch.nn.functional
+    cases = [
+        (2, 33, 4, 2, 16, 8, True, (-1, -1), None),
+        (2, 40, 6, 3, 8, 12, True, (9, 0), [40, 23]),
+        (1, 37, 4, 1, 12, 12, False, (5, 3), [30]),
+        (2, 29, 2, 2, 8, 8, False, (-1, -1), [29, 1]),
+    ]
+    for ci, (B, S, Hq, Hkv, dqk, dv, causal, win, sl) in enumerate(cases):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(1200 + ci, B, S, Hq, Hkv, dqk, dv)
+            scale = 1.0 / math.sqrt(dqk)
+            sl_np = None if sl is None else np.array(sl)
+            r = orc.attention(q, k, v, do, num_gqa_groups=Hkv, causal=causal, window=win,
+                              softmax_type=st, softmax_offset=alpha, seqlens=sl_np)
+            G = Hq // Hkv
+            tq = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+            tk = torch.tensor(k.transpose(0, 2, 1, 3), requires_grad=True)
+            tv = torch.tensor(v.transpose(0, 2, 1, 3), requires_grad=True)
+            i = torch.arange(S)[:, None]
+            j = torch.arange(S)[None, :]
+            vis = torch.zeros(B, 1, S, S, dtype=torch.bool)
+            dmask = torch.ones(B, 1, S, 1, dtype=torch.float64)
+            for b in range(B):
+                L = S if sl is None else sl[b]
+                m = (i < L) & (j < L)
+                if causal:
+                    m &= j <= i
+                if win[0] >= 0:
+                    m &= j >= i - win[0]
+                if win[1] >= 0:
+                    m &= j <= i + win[1]
+                vis[b, 0] = m
+                dmask[b, 0, L:] = 0.0
+            tdo = torch.tensor(do.transpose(0, 2, 1, 3)) * dmask
+            kr = tk.repeat_interleave(G, dim=1)
+            vr = tv.repeat_interleave(G, dim=1)
+            if st == "vanilla":
+                # fully masked (padded) rows see key 0 with zero upstream gradient
+                vis2 = vis.clone()
+                vis2[:, :, :, 0] |= ~vis.any(dim=3)
+                madd = torch.where(vis2, 0.0, -torch.inf).to(torch.float64).expand(B, Hq, S, S)
+                madd = madd.clone().requires_grad_(True)
+                o = F.scaled_dot_product_attention(tq, kr, vr, attn_mask=madd, scale=scale)
+            else:
+                z = torch.zeros(Hq, dtype=torch.float64) if st == "off_by_one" else torch.tensor(alpha)
+                kz = torch.cat([kr, torch.zeros(B, Hq, 1, dqk, dtype=torch.float64)], dim=2)
+                vz = torch.cat([vr, torch.zeros(B, Hq, 1, dv, dtype=torch.float64)], dim=2)
+                base = torch.where(vis, 0.0, -torch.inf).to(torch.float64).expand(B, Hq, S, S)
+                col = z.view(1, Hq, 1, 1).expand(B, Hq, S, 1)
+                madd = torch.cat([base, col], dim=3).clone().requires_grad_(True)
+                o = F.scaled_dot_product_attention(tq, kz, vz, attn_mask=madd, scale=scale)
+            o.backward(tdo)
+            o_np = o.detach().numpy().transpose(0, 2, 1, 3)
+            for b in range(B):
+                L = S if sl is None else sl[b]
+                _close(r["o"][b, :L], o_np[b, :L], 1e-10, 1e-12, f"O case{ci} {st}")
+            _close(r["dq"], tq.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"dQ case{ci} {st}")
+            _close(r["dk"], tk.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"dK case{ci} {st}")
+            _close(r["dv"], tv.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"dV case{ci} {st}")
+            if st != "vanilla":
+                dz = madd.grad[:, :, :, S].sum(dim=(0, 2)).numpy()
+                _close(r["dalpha"], dz, 1e-10, 1e-12, f"dalpha case{ci} {st}")
+
+
+def pin_golden(orc):
+    with open(os.path.join(GOLDEN, "uniform_scores.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        S = len(case["v"])
+        v = np.array(case["v"], dtype=np.float64).reshape(1, S, 1, 1)
+        q = np.zeros((1, S, 1, 1))
+        k = np.zeros((1, S, 1, 1))
+        st = case["softmax_type"]
+        alpha = np.array([case.get("alpha", 0.0)])
+        r = orc.attention(q, k, v, None, num_gqa_groups=1, causal=case["causal"],
+                          window=tuple(case["window"]), softmax_type=st, softmax_offset=alpha)
+        _close(r["o"][0, :, 0, 0], np.array(case["o"]), 1e-15, 1e-15, case["name"])
+        _close(r["lse"][0, 0], np.log(np.array(case["lse_exp"], dtype=np.float64)), 1e-15, 1e-15,
+               case["name"] + " lse")
+
+
+ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
+            pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
+            pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden]

@@ -1,0 +1,73 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Every mutant is the oracle's source with one textual change, executed as a
+fresh module on the CPU; the real oracle module is never modified.  This shows
+the pins would notice a dropped term, a wrong sign, index or operand, or the
+off-by-one constant bug discussed in PR #2225 (offset 1.0 instead of 0.0).
+"""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "sdpa_oracle.py")
+
+MUTANTS = {
+    "off_by_one_logit_1": [("    if softmax_type == OFF_BY_ONE:\n        return 0.0",
+                            "    if softmax_type == OFF_BY_ONE:\n        return 1.0")],
+    "gqa_strided_heads": [("return h // (num_heads // num_kv_heads)", "return h % num_kv_heads"),
+                          ("h = g * G + gi", "h = gi * Hkv + g")],
+    "dk_missing_scale": [('out["dk"] += scale * (ds.T @ qh)', 'out["dk"] += (ds.T @ qh)')],
+    "dv_untransposed_p": [('out["dv"] += p.T @ doh', 'out["dv"] += p @ doh')],
+    "dq_wrong_operand": [('out["dq"][:, gi, :] = scale * (ds @ kb)', 'out["dq"][:, gi, :] = scale * (ds.T @ kb)')],
+    "ds_dropped_delta": [("ds = p * (dp - delta[:, None])", "ds = p * dp")],
+    "window_left_exclusive": [("m &= j >= i - window_left", "m &= j > i - window_left")],
+    "window_right_off_by_one": [("m &= j <= i + window_right", "m &= j <= i + window_right + 1")],
+    "causal_reversed": [("m &= j <= i\n", "m &= j >= i\n")],
+    "padding_rows_only": [("m = (i < L) & (j < L)", "m = (i < L)")],
+    "sink_not_in_denominator": [("l = l + np.exp(z - m_safe)", "l = l")],
+    "lse_missing_max": [("lse = np.where(l > 0, m_safe + np.log(l), -np.inf)",
+                         "lse = np.where(l > 0, np.log(l), -np.inf)")],
+    "dz_sign_flip": [('out["dz"][gi] = -(np.exp(z - lse_safe) * delta).sum()',
+                      'out["dz"][gi] = (np.exp(z - lse_safe) * delta).sum()')],
+    "default_scale_uses_dv": [("scale = (1.0 / math.sqrt(dqk))", "scale = (1.0 / math.sqrt(v.shape[3]))")],
+    "sink_logit_scaled": [("z = sink_logit(softmax_type, softmax_offset, h)",
+                           "z = sink_logit(softmax_type, softmax_offset, h)\n"
+                           "        z = None if z is None else z * scale")],
+}
+
+# cheap pins first: a mutant stops at its first failing pin
+ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_causal_rows,
+         oracle_pins.pin_window_limits, oracle_pins.pin_row_sums, oracle_pins.pin_sink_closed,
+         oracle_pins.pin_gqa_repeat, oracle_pins.pin_padding, oracle_pins.pin_scale,
+         oracle_pins.pin_dalpha_forms, oracle_pins.pin_sink_augmented,
+         oracle_pins.pin_torch_sdpa, oracle_pins.pin_finite_diff]
+
+
+def _mutant(edits):
+    with open(SRC) as f:
+        src = f.read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+def test_pin_order_covers_all():
+    assert set(ORDER) == set(oracle_pins.ALL_PINS)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(MUTANTS[name])
+    for pin in ORDER:
+        try:
+            pin(mod)
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            return
+    pytest.fail(f"no pin caught mutant {name}")
