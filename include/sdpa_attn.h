@@ -1,0 +1,170 @@
+/*
+ * sdpa_attn.h — C ABI of the MI355X (gfx950) fused scaled dot-product attention.
+ *
+ * The library computes, for every batch b, query head h and query row i,
+ *
+ *     O[b,i,h,:] = sum_j P_ij V[b,j,kv(h),:],
+ *     P_ij = exp(s_ij) / (sum_{j visible} exp(s_ij) + [sink] exp(z_h)),
+ *     s_ij = scale * Q[b,i,h,:] . K[b,j,kv(h),:],
+ *
+ * over visible keys j only, plus the row log-sum-exp, and the backward pass of
+ * that function.  Definitions followed:
+ *   - score/scale/softmax/attend steps: codelab "Speed up attention on GPU with
+ *     cuDNN and TransformerEngine", "How attention works";
+ *   - module arguments num_gqa_groups, attn_mask_type, window_size,
+ *     scale_factor (default 1/sqrt(head_dim)), separate BSHD Q/K/V with
+ *     different Q/K and V head dims, sequence lengths: TransformerEngine
+ *     "JAX: Single-GPU Attention with TransformerEngine", sections 1, 2, 4 and
+ *     "Other attention knobs";
+ *   - softmax_type vanilla / off-by-one / learnable, the softmax_offset
+ *     parameter of shape [1, num_heads, 1, 1], the forward outputs (output,
+ *     softmax_aux) and the backward outputs (grad_q, grad_k, grad_v,
+ *     grad_softmax_offset): PR "[JAX] Add support for sink attention in JAX"
+ *     #2225, review summaries and their sequence diagrams.
+ *
+ * Readings fixed by this ABI (the pages leave them open):
+ *   - kv(h) = floor(h / (num_heads / num_gqa_groups)): contiguous head groups;
+ *   - window (left, right) is inclusive, i-left <= j <= i+right, -1 unbounded,
+ *     intersected with the causal rule j <= i when mask_type is CAUSAL;
+ *   - seqlens[b] right-pads queries and keys alike; rows/keys >= seqlens[b]
+ *     are invisible;
+ *   - off-by-one = an extra logit z = 0; learnable = an extra logit z = alpha_h
+ *     (raw value of softmax_offset[h]); z is not multiplied by the scale;
+ *   - the LSE output ("softmax_aux") is the natural-log log-sum-exp of each
+ *     row including the sink term; empty rows get LSE = -inf (vanilla) or z_h.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays; the
+ *     library never allocates, never frees and keeps no state between calls.
+ *   - Layouts (BSHD): Q, dQ [B,S,Hq,Dqk]; K, dK [B,S,Hkv,Dqk]; V, dV [B,S,Hkv,Dv];
+ *     O, dO [B,S,Hq,Dv]; LSE [B,Hq,S] float32; softmax_offset and
+ *     d_softmax_offset [Hq] float32; seqlens [B] int32.
+ *   - Element type of Q,K,V,O,dO,dQ,dK,dV is params.dtype (bf16 or f32).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream); the
+ *     calls return without synchronising.  Inputs are read only.  Outputs are
+ *     fully overwritten, padded rows included (O = 0, dQ = dK = dV = 0 there).
+ *   - All argument checks run on the host before anything is enqueued; on a
+ *     non-zero return nothing was launched, except ATTN_ERR_HIP which reports
+ *     a launch failure.
+ *   - seqlens values live on the device and cannot be checked on the host;
+ *     kernels clamp them to [0, S].  The Python binding checks them.
+ */
+#ifndef SDPA_ATTN_H
+#define SDPA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* params.dtype */
+#define ATTN_F32 0
+#define ATTN_BF16 1
+/* params.mask_type (codelab section 7; TE single-GPU page section 2) */
+#define ATTN_MASK_NONE 0
+#define ATTN_MASK_CAUSAL 1
+/* params.softmax_type (PR #2225, AttnSoftmaxType) */
+#define ATTN_SOFTMAX_VANILLA 0
+#define ATTN_SOFTMAX_OFF_BY_ONE 1
+#define ATTN_SOFTMAX_LEARNABLE 2
+
+/* status codes */
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG (-1)   /* bad size, enum, window, pointer */
+#define ATTN_ERR_UNSUPPORTED (-2)   /* valid problem, no kernel for (dtype, Dqk, Dv) */
+#define ATTN_ERR_WORKSPACE (-3)     /* workspace_bytes below the required size */
+#define ATTN_ERR_HIP (-4)           /* a HIP launch failed */
+
+/* Problem description.  All fields are plain int32/float for a fixed ABI. */
+struct attn_params {
+  int32_t batch;          /* B >= 1 */
+  int32_t seqlen;         /* S >= 1, shared by queries and keys (self-attention) */
+  int32_t num_heads;      /* Hq >= 1 */
+  int32_t num_gqa_groups; /* Hkv >= 1, number of K/V heads; Hq % Hkv == 0 */
+  int32_t head_dim_qk;    /* Dqk */
+  int32_t head_dim_v;     /* Dv */
+  int32_t dtype;          /* ATTN_F32 | ATTN_BF16 */
+  int32_t mask_type;      /* ATTN_MASK_NONE | ATTN_MASK_CAUSAL */
+  int32_t window_left;    /* >= -1; -1 = unbounded */
+  int32_t window_right;   /* >= -1; -1 = unbounded */
+  float scale_factor;     /* finite; 0 => 1/sqrt(Dqk) */
+  int32_t softmax_type;   /* ATTN_SOFTMAX_* */
+};
+
+/* Host-only check of a problem description; no HIP call.  Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED.  Supported (dtype, Dqk, Dv):
+ * bf16 with (64,64), (128,128), (192,128); f32 with (64,64). */
+int attn_validate(const struct attn_params* p);
+
+/* Workspace bytes the forward / backward call needs (0 if p is invalid).
+ * The forward needs none; the backward needs room for the per-row
+ * delta = rowsum(dO * O) and the per-block partial sums of d(sink logit). */
+size_t attn_fwd_workspace_size(const struct attn_params* p);
+size_t attn_bwd_workspace_size(const struct attn_params* p);
+
+/* Forward.  Writes O [B,S,Hq,Dv] and LSE [B,Hq,S].
+ *   softmax_offset: [Hq] float32 sink logits; required for LEARNABLE,
+ *                   ignored otherwise (may be NULL).
+ *   seqlens:        [B] int32 valid lengths, or NULL for all S.
+ *   workspace:      may be NULL when workspace_bytes >= attn_fwd_workspace_size. */
+int attn_fwd(const struct attn_params* p, const void* q, const void* k, const void* v,
+             const float* softmax_offset, const int32_t* seqlens, void* o, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the forward above for upstream gradient d_o (PR #2225 backward:
+ * grad_q, grad_k, grad_v, grad_softmax_offset).  o and lse must be the
+ * forward's outputs for the same inputs.  Writes dQ, dK, dV.
+ *   d_softmax_offset: [Hq] float32, overwritten with d(loss)/d(z_h) summed
+ *     over batches and rows.  Required for LEARNABLE; optional for OFF_BY_ONE
+ *     (gradient w.r.t. the implicit zero logit); must be NULL for VANILLA.
+ *   workspace: at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
+ * dK/dV accumulate the query heads of a GQA group in a fixed order, and dQ and
+ * d_softmax_offset are reduced in a fixed order: results are bitwise
+ * reproducible run to run. */
+int attn_bwd(const struct attn_params* p, const void* q, const void* k, const void* v,
+             const void* o, const void* d_o, const float* lse, const float* softmax_offset,
+             const int32_t* seqlens, void* dq, void* dk, void* dv, float* d_softmax_offset,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Tile sizes (query rows x keys) the forward kernel uses for problem p.
+ * Returns ATTN_OK or the attn_validate error. */
+int attn_fwd_tile_shape(const struct attn_params* p, int32_t* block_m, int32_t* block_n);
+
+/* ---- mask engine exports (test and inspection) --------------------------
+ * Tile classes: 0 = SKIP (no visible pair), 1 = PARTIAL (per-element
+ * predicate), 2 = FULL (every pair visible).  The device variants run the
+ * same integer code the kernels run. */
+
+/* Device: out[b][qt][kt] (int8, device, B * ceil(S/block_m) * ceil(S/block_n)
+ * entries) = class of query tile qt x key tile kt for batch b. */
+int attn_debug_tile_map(const struct attn_params* p, const int32_t* seqlens, int32_t block_m,
+                        int32_t block_n, int8_t* out, void* stream);
+
+/* Device: out[b][i][j] (uint8, device, B*S*S entries) = 1 iff query i sees key j. */
+int attn_debug_mask_probe(const struct attn_params* p, const int32_t* seqlens, uint8_t* out,
+                          void* stream);
+
+/* Host: same tile map from host seqlens (NULL = all S) into host memory. */
+int attn_host_tile_map(const struct attn_params* p, const int32_t* seqlens, int32_t block_m,
+                       int32_t block_n, int8_t* out);
+
+/* Host: contiguous range [*lo, *hi] of keys visible from any of the query
+ * rows i0..i1 (inclusive), for valid length L; returns 1 if non-empty, else 0. */
+int attn_host_key_range(const struct attn_params* p, int32_t L, int32_t i0, int32_t i1,
+                        int32_t* lo, int32_t* hi);
+
+/* Host: contiguous range [*lo, *hi] of query rows that see any of the keys
+ * j0..j1 (inclusive); returns 1 if non-empty, else 0. */
+int attn_host_query_range(const struct attn_params* p, int32_t L, int32_t j0, int32_t j1,
+                          int32_t* lo, int32_t* hi);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_ATTN_H */

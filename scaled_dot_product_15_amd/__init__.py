@@ -8,7 +8,7 @@ raises if it is missing.
 _API = ("attn_fwd", "attn_bwd", "attn_validate", "attn_fwd_workspace_size",
         "attn_bwd_workspace_size", "attn_status_string", "debug_tile_map",
         "debug_mask_probe", "host_tile_map", "host_key_range", "host_query_range",
-        "load_library", "AttnError", "Params")
+        "load_library", "AttnError", "Params", "make_params", "fwd_tile_shape")
 
 
 def __getattr__(name):

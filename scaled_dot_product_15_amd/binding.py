@@ -1,0 +1,276 @@
+"""ctypes binding of libsdpa_mi355x.so (declared in include/sdpa_attn.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.  If
+the library is missing this module raises; it never falls back to another
+implementation.
+
+Names follow the pages' module arguments (TransformerEngine "JAX: Single-GPU
+Attention" sections 2 and 4 and "Other attention knobs"; PR #2225
+softmax_type / softmax_offset).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsdpa_mi355x.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+MASKS = {"no_mask": 0, "none": 0, "causal": 1}
+SOFTMAX = {"vanilla": 0, "off_by_one": 1, "learnable": 2}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error"}
+
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("seqlen", _c_i32), ("num_heads", _c_i32),
+                ("num_gqa_groups", _c_i32), ("head_dim_qk", _c_i32), ("head_dim_v", _c_i32),
+                ("dtype", _c_i32), ("mask_type", _c_i32), ("window_left", _c_i32),
+                ("window_right", _c_i32), ("scale_factor", ctypes.c_float),
+                ("softmax_type", _c_i32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({STATUS.get(status, 'unknown')})")
+
+
+EXPORTS = {
+    "attn_validate": (ctypes.c_int, [ctypes.POINTER(Params)]),
+    "attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]),
+    "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_fwd_tile_shape": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(_c_i32),
+                                           ctypes.POINTER(_c_i32)]),
+    "attn_debug_tile_map": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _c_i32, _c_i32, _vp, _vp]),
+    "attn_debug_mask_probe": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp]),
+    "attn_host_tile_map": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _c_i32, _c_i32, _vp]),
+    "attn_host_key_range": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32,
+                                           ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "attn_host_query_range": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32,
+                                             ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+}
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m scaled_dot_product_15_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def make_params(B, S, Hq, Hkv, d_qk, d_v, dtype="bf16", attn_mask_type="causal",
+                window_size=(-1, -1), scale_factor=None, softmax_type="vanilla") -> Params:
+    return Params(B, S, Hq, Hkv, d_qk, d_v, ATTN_BF16 if dtype == "bf16" else ATTN_F32,
+                  MASKS[attn_mask_type], int(window_size[0]), int(window_size[1]),
+                  float(scale_factor or 0.0), SOFTMAX[softmax_type])
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise AttnError(rc, where)
+
+
+def attn_validate(p: Params) -> int:
+    return load_library().attn_validate(ctypes.byref(p))
+
+
+def attn_fwd_workspace_size(p: Params) -> int:
+    return load_library().attn_fwd_workspace_size(ctypes.byref(p))
+
+
+def attn_bwd_workspace_size(p: Params) -> int:
+    return load_library().attn_bwd_workspace_size(ctypes.byref(p))
+
+
+def attn_status_string(rc: int) -> str:
+    return load_library().attn_status_string(rc).decode()
+
+
+def fwd_tile_shape(p: Params):
+    bm, bn = _c_i32(), _c_i32()
+    _check(load_library().attn_fwd_tile_shape(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn)),
+           "attn_fwd_tile_shape")
+    return bm.value, bn.value
+
+
+# --------------------------------------------------------------- torch level
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be BSHD tensors")
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    if tuple(k.shape) != (B, S, Hkv, dqk) or tuple(v.shape[:3]) != (B, S, Hkv):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be bfloat16 or float32")
+    dtype = "bf16" if q.dtype == torch.bfloat16 else "f32"
+    return make_params(B, S, Hq, Hkv, dqk, v.shape[3], dtype, attn_mask_type, window_size,
+                       scale_factor, softmax_type)
+
+
+def _check_seqlens(seqlens, B, S):
+    torch = _torch()
+    if seqlens is None:
+        return None
+    if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_cuda:
+        raise ValueError("seqlens must be an int32 device tensor of shape [B]")
+    host = seqlens.cpu()
+    if bool((host < 0).any()) or bool((host > S).any()):
+        raise ValueError(f"seqlens values must lie in [0, {S}]")
+    return seqlens
+
+
+def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_size=(-1, -1),
+             scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None,
+             out=None, lse=None, stream=None, check_seqlens=True):
+    """Forward attention on BSHD device tensors.  Returns (O [B,S,Hq,Dv], LSE [B,Hq,S])."""
+    torch = _torch()
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type)
+    B, S, Hq = p.batch, p.seqlen, p.num_heads
+    if check_seqlens:
+        _check_seqlens(seqlens, B, S)
+    if softmax_type == "learnable":
+        if softmax_offset is None:
+            raise ValueError("learnable softmax needs softmax_offset [Hq]")
+        softmax_offset = softmax_offset.reshape(-1).to(torch.float32).contiguous()
+        if softmax_offset.numel() != Hq:
+            raise ValueError("softmax_offset must hold num_heads values")
+    else:
+        softmax_offset = None
+    o = out if out is not None else torch.empty((B, S, Hq, p.head_dim_v), dtype=q.dtype, device=q.device)
+    l = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(softmax_offset),
+                        _ptr(seqlens), _ptr(o), _ptr(l), None, 0, _stream(stream)), "attn_fwd")
+    return o, l
+
+
+def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causal",
+             window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
+             seqlens=None, want_d_offset=None, workspace=None, outs=None, stream=None,
+             check_seqlens=True):
+    """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None).
+
+    d_softmax_offset is returned for learnable softmax (always) and for
+    off-by-one when want_d_offset is true; vanilla returns None.
+    """
+    torch = _torch()
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type)
+    B, S, Hq, Hkv = p.batch, p.seqlen, p.num_heads, p.num_gqa_groups
+    if check_seqlens:
+        _check_seqlens(seqlens, B, S)
+    for t in (o, d_o):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or tuple(t.shape) != (B, S, Hq, p.head_dim_v):
+            raise ValueError("o and d_o must be contiguous [B,S,Hq,Dv] tensors of q's dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq,S] tensor")
+    if softmax_type == "learnable":
+        if softmax_offset is None:
+            raise ValueError("learnable softmax needs softmax_offset [Hq]")
+        softmax_offset = softmax_offset.reshape(-1).to(torch.float32).contiguous()
+    else:
+        softmax_offset = None
+    want = softmax_type == "learnable" or (softmax_type == "off_by_one" and bool(want_d_offset))
+    if outs is not None:
+        dq, dk, dv, doff = outs
+    else:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        doff = torch.empty(Hq, dtype=torch.float32, device=q.device) if want else None
+    if not want:
+        doff = None
+    lib = load_library()
+    ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                        _ptr(softmax_offset), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(doff), _ptr(workspace), workspace.numel(), _stream(stream)), "attn_bwd")
+    return dq, dk, dv, doff
+
+
+def debug_tile_map(p: Params, seqlens, block_m, block_n, stream=None):
+    torch = _torch()
+    nqt = -(-p.seqlen // block_m)
+    nkt = -(-p.seqlen // block_n)
+    out = torch.empty((p.batch, nqt, nkt), dtype=torch.int8, device="cuda")
+    _check(load_library().attn_debug_tile_map(ctypes.byref(p), _ptr(seqlens), block_m, block_n,
+                                              _ptr(out), _stream(stream)), "attn_debug_tile_map")
+    return out
+
+
+def debug_mask_probe(p: Params, seqlens, stream=None):
+    torch = _torch()
+    out = torch.empty((p.batch, p.seqlen, p.seqlen), dtype=torch.uint8, device="cuda")
+    _check(load_library().attn_debug_mask_probe(ctypes.byref(p), _ptr(seqlens), _ptr(out),
+                                                _stream(stream)), "attn_debug_mask_probe")
+    return out
+
+
+def host_tile_map(p: Params, seqlens, block_m, block_n):
+    import numpy as np
+    nqt = -(-p.seqlen // block_m)
+    nkt = -(-p.seqlen // block_n)
+    out = np.zeros((p.batch, nqt, nkt), dtype=np.int8)
+    sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
+    _check(load_library().attn_host_tile_map(
+        ctypes.byref(p), None if sl is None else sl.ctypes.data_as(ctypes.c_void_p), block_m,
+        block_n, out.ctypes.data_as(ctypes.c_void_p)), "attn_host_tile_map")
+    return out
+
+
+def host_key_range(p: Params, L, i0, i1):
+    lo, hi = _c_i32(), _c_i32()
+    ok = load_library().attn_host_key_range(ctypes.byref(p), L, i0, i1, ctypes.byref(lo), ctypes.byref(hi))
+    return (lo.value, hi.value) if ok else None
+
+
+def host_query_range(p: Params, L, j0, j1):
+    lo, hi = _c_i32(), _c_i32()
+    ok = load_library().attn_host_query_range(ctypes.byref(p), L, j0, j1, ctypes.byref(lo), ctypes.byref(hi))
+    return (lo.value, hi.value) if ok else None

@@ -1,0 +1,218 @@
+// Host side of the C ABI declared in include/sdpa_attn.h: argument checks,
+// workspace layout, kernel choice and launches on the caller's stream.
+// Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "sdpa_attn.h"
+
+using namespace sdpa;
+
+namespace {
+
+bool supported(const attn_params* p) {
+  int bm, bn;
+  if (p->dtype == ATTN_BF16) return fwd_bf16_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
+  return fwd_f32_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
+}
+
+int check_fields(const attn_params* p) {
+  if (!p) return ATTN_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->seqlen < 1 || p->num_heads < 1 || p->num_gqa_groups < 1) return ATTN_ERR_INVALID_ARG;
+  if (p->num_heads % p->num_gqa_groups != 0) return ATTN_ERR_INVALID_ARG;
+  if (p->head_dim_qk < 1 || p->head_dim_v < 1) return ATTN_ERR_INVALID_ARG;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (p->mask_type != ATTN_MASK_NONE && p->mask_type != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
+  if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(p->scale_factor)) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type < ATTN_SOFTMAX_VANILLA || p->softmax_type > ATTN_SOFTMAX_LEARNABLE) return ATTN_ERR_INVALID_ARG;
+  // Kernels index rows with 32-bit (batch * S + i) and launch one-dimensional
+  // grids of B * heads * tiles workgroups.
+  const long long rows = (long long)p->batch * p->seqlen;
+  const long long grid = (long long)p->batch * p->num_heads * ((p->seqlen + 63) / 64);
+  if (rows > 0x7fffffffLL || grid > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int n_chunks(const attn_params* p) { return (p->seqlen + kPreRows - 1) / kPreRows; }
+size_t delta_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * p->seqlen * sizeof(float)); }
+size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * n_chunks(p) * sizeof(float)); }
+
+KArgs make_args(const attn_params* p) {
+  KArgs a = {};
+  a.B = p->batch;
+  a.S = p->seqlen;
+  a.Hq = p->num_heads;
+  a.Hkv = p->num_gqa_groups;
+  a.G = p->num_heads / p->num_gqa_groups;
+  a.causal = p->mask_type == ATTN_MASK_CAUSAL;
+  a.wl = normalise_window(p->window_left, p->seqlen);
+  a.wr = normalise_window(p->window_right, p->seqlen);
+  a.softmax_type = p->softmax_type;
+  a.scale = p->scale_factor != 0.0f ? p->scale_factor : (float)(1.0 / sqrt((double)p->head_dim_qk));
+  a.scale_log2 = a.scale * kLog2e;
+  a.n_chunks = n_chunks(p);
+  return a;
+}
+
+MaskSpec host_mask(const attn_params* p, int L) {
+  return make_mask(L, p->seqlen, p->mask_type == ATTN_MASK_CAUSAL, p->window_left, p->window_right);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_validate(const attn_params* p) {
+  const int rc = check_fields(p);
+  if (rc != ATTN_OK) return rc;
+  return supported(p) ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+size_t attn_fwd_workspace_size(const attn_params* p) {
+  (void)p;
+  return 0;
+}
+
+size_t attn_bwd_workspace_size(const attn_params* p) {
+  if (attn_validate(p) != ATTN_OK) return 0;
+  return delta_bytes(p) + dz_bytes(p);
+}
+
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
+             const int32_t* seqlens, void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const int rc = attn_validate(p);
+  if (rc != ATTN_OK) return rc;
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && !softmax_offset) return ATTN_ERR_INVALID_ARG;
+  KArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.softmax_offset = softmax_offset;
+  a.seqlens = seqlens;
+  a.out_o = o;
+  a.out_lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->dtype == ATTN_BF16) return hip_status(launch_fwd_bf16(a, p->head_dim_qk, p->head_dim_v, s));
+  return hip_status(launch_fwd_f32(a, p->head_dim_qk, p->head_dim_v, s));
+}
+
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+             const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq, void* dk, void* dv,
+             float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = attn_validate(p);
+  if (rc != ATTN_OK) return rc;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!softmax_offset || !d_softmax_offset)) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_VANILLA && d_softmax_offset) return ATTN_ERR_INVALID_ARG;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_bwd_workspace_size(p)) return ATTN_ERR_WORKSPACE;
+  KArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.softmax_offset = softmax_offset;
+  a.seqlens = seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.d_offset = d_softmax_offset;
+  a.delta = static_cast<float*>(workspace);
+  a.dz_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_bwd_pre(a, p->dtype, p->head_dim_v, s);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  e = p->dtype == ATTN_BF16 ? launch_bwd_bf16(a, p->head_dim_qk, p->head_dim_v, s)
+                            : launch_bwd_f32(a, p->head_dim_qk, p->head_dim_v, s);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  if (d_softmax_offset && p->softmax_type != ATTN_SOFTMAX_VANILLA) return hip_status(launch_dz_reduce(a, s));
+  return ATTN_OK;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported (dtype, head_dim_qk, head_dim_v) combination";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_tile_shape(const attn_params* p, int32_t* block_m, int32_t* block_n) {
+  const int rc = attn_validate(p);
+  if (rc != ATTN_OK) return rc;
+  if (!block_m || !block_n) return ATTN_ERR_INVALID_ARG;
+  int bm = 0, bn = 0;
+  if (p->dtype == ATTN_BF16) fwd_bf16_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
+  else fwd_f32_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
+  *block_m = bm;
+  *block_n = bn;
+  return ATTN_OK;
+}
+
+int attn_debug_tile_map(const attn_params* p, const int32_t* seqlens, int32_t block_m, int32_t block_n,
+                        int8_t* out, void* stream) {
+  const int rc = check_fields(p);
+  if (rc != ATTN_OK) return rc;
+  if (!out || block_m < 1 || block_n < 1) return ATTN_ERR_INVALID_ARG;
+  KArgs a = make_args(p);
+  a.seqlens = seqlens;
+  return hip_status(launch_debug_tile_map(a, block_m, block_n, out, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_mask_probe(const attn_params* p, const int32_t* seqlens, uint8_t* out, void* stream) {
+  const int rc = check_fields(p);
+  if (rc != ATTN_OK) return rc;
+  if (!out) return ATTN_ERR_INVALID_ARG;
+  KArgs a = make_args(p);
+  a.seqlens = seqlens;
+  return hip_status(launch_debug_mask_probe(a, out, static_cast<hipStream_t>(stream)));
+}
+
+int attn_host_tile_map(const attn_params* p, const int32_t* seqlens, int32_t block_m, int32_t block_n,
+                       int8_t* out) {
+  const int rc = check_fields(p);
+  if (rc != ATTN_OK) return rc;
+  if (!out || block_m < 1 || block_n < 1) return ATTN_ERR_INVALID_ARG;
+  const int S = p->seqlen, nqt = (S + block_m - 1) / block_m, nkt = (S + block_n - 1) / block_n;
+  for (int b = 0; b < p->batch; ++b) {
+    const MaskSpec m = host_mask(p, seqlens ? seqlens[b] : S);
+    for (int qt = 0; qt < nqt; ++qt)
+      for (int kt = 0; kt < nkt; ++kt)
+        out[((size_t)b * nqt + qt) * nkt + kt] = (int8_t)tile_class(m, qt * block_m, block_m, kt * block_n, block_n);
+  }
+  return ATTN_OK;
+}
+
+int attn_host_key_range(const attn_params* p, int32_t L, int32_t i0, int32_t i1, int32_t* lo, int32_t* hi) {
+  if (check_fields(p) != ATTN_OK || !lo || !hi) return 0;
+  int a = 0, b = -1;
+  const bool ok = key_range(host_mask(p, L), i0, i1, a, b);
+  *lo = a;
+  *hi = b;
+  return ok ? 1 : 0;
+}
+
+int attn_host_query_range(const attn_params* p, int32_t L, int32_t j0, int32_t j1, int32_t* lo, int32_t* hi) {
+  if (check_fields(p) != ATTN_OK || !lo || !hi) return 0;
+  int a = 0, b = -1;
+  const bool ok = query_range(host_mask(p, L), j0, j1, a, b);
+  *lo = a;
+  *hi = b;
+  return ok ? 1 : 0;
+}
+
+}  // extern "C"

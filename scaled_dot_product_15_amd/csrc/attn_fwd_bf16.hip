@@ -1,0 +1,277 @@
+// Forward attention, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
+//
+// Computes O = softmax(scale * Q K^T + mask [+ sink]) V and the row LSE
+// (codelab "Speed up attention on GPU with cuDNN and TransformerEngine",
+// "How attention works" steps 1-4, fused into one kernel as its sections 5-6
+// describe; sink softmax variants from PR #2225's sequence diagrams).
+//
+// Work decomposition: one workgroup of 4 waves owns BM = 128 query rows of one
+// (batch, query head); each wave owns 32 rows.  The workgroup walks the key
+// tiles (BN keys) that the mask engine says are visible from its rows.
+//
+// Per key tile and wave:
+//   S^T (keys x queries) = K Q^T with A = K from LDS (row-major, padded rows)
+//   and B = Q^T held in registers for the whole loop.  In the 32x32 MFMA
+//   accumulator a lane owns one query column, so the row max/sum of the
+//   online softmax need a single cross-lane step (lane <-> lane^32).
+//   O^T (d x queries) += V^T P^T with B = P^T taken directly from the S^T
+//   accumulator registers (after exp and bf16 rounding) and A = V^T read from
+//   LDS, where V is stored transposed with keys permuted to match the
+//   accumulator's row order (see perm16).
+//
+// Online softmax in base 2 with the scale folded into one multiply.  The
+// running max only moves (and O and the row sum are rescaled) when a tile's
+// max exceeds it by more than 8, so most tiles skip the rescale; P is then
+// bounded by 2^8, harmless in fp32/bf16, and the final O = acc / l and
+// LSE = m + log2(l) are exact regardless of which max was used.  A sink logit
+// z starts the running max at z with row sum 1 (its own exp term).
+#include "attn_common.h"
+#include "launch.h"
+
+namespace sdpa {
+
+template <int DQK, int DV, int BN>
+struct FwdBf16Cfg {
+  static constexpr int BM = 128;
+  static constexpr int NT = 256;
+  static constexpr int KP = DQK + 8;   // LDS pitch (bf16) of a K row
+  static constexpr int VP = BN + 8;    // LDS pitch (bf16) of a transposed V row
+  static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
+  static constexpr int KLOADS = BN * KCH / NT;
+  static constexpr int VBLK = (BN / 4) * (DV / 8);  // 4-key x 8-dim blocks of V
+  static constexpr int VLOADS = (VBLK + NT - 1) / NT;
+  static constexpr int LDS_ELEMS = BN * KP + DV * VP;
+  static_assert(BN * KCH % NT == 0, "K tile must split evenly over the workgroup");
+  static_assert(BN % 32 == 0 && DQK % 32 == 0 && DV % 32 == 0, "tile shape");
+};
+
+// Logical tile order for a linear workgroup id: heaviest query tiles first
+// (for causal masks the last tiles see the most keys), and the G query heads
+// sharing a KV head on consecutive ids, which are then kept on one XCD (the
+// hardware deals consecutive workgroups round-robin over the 8 XCDs, each with
+// its own L2) so the group reads its K/V tiles through a shared L2.
+__device__ __forceinline__ void fwd_tile_of(const KArgs& a, int bid, int& b, int& h, int& qt) {
+  const int N = a.B * a.Hq * a.n_tiles;
+  const int chunk = a.G;
+  const int full = (N / (8 * chunk)) * (8 * chunk);
+  int l = bid;
+  if (bid < full) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+  }
+  const int per_tile = a.B * a.Hq;
+  qt = a.n_tiles - 1 - l / per_tile;
+  const int r = l % per_tile;
+  b = r / a.Hq;
+  h = r % a.Hq;
+}
+
+template <int DQK, int DV, int BN, int OCC>
+__global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
+  using C = FwdBf16Cfg<DQK, DV, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  uint16_t* Ks = lds;
+  uint16_t* Vt = lds + BN * C::KP;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  int b, h, qt;
+  fwd_tile_of(a, blockIdx.x, b, h, qt);
+  const int g = h / a.G;
+  const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const int i0 = qt * C::BM;
+  const int row_w0 = i0 + w * 32;
+  const int qi = row_w0 + l32;
+
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
+  const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
+
+  // Q^T operand: lane holds query qi, dims [ks*16 + hf*8, +8).
+  bf16x8 qreg[DQK / 16];
+  {
+    const uint16_t* qp = Q + ((size_t)(b * a.S + (qi < a.S ? qi : 0)) * a.Hq + h) * DQK + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < DQK / 16; ++ks) {
+      u32x4 t = qi < a.S ? ldg16(qp + ks * 16) : u32x4{0, 0, 0, 0};
+      qreg[ks] = as_bf16x8(t);
+    }
+  }
+
+  const float z2 = sink_logit(a, h) * kLog2e;
+  const bool has_sink = a.softmax_type != 0;
+  float m_run = has_sink ? z2 : -__builtin_inff();
+  float l_run = (has_sink && hf == 0) ? 1.0f : 0.0f;
+  f32x16 o[DV / 32];
+#pragma unroll
+  for (int db = 0; db < DV / 32; ++db) o[db] = f32x16{};
+
+  int lo = 0, hi = -1;
+  const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
+  if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
+  const int kt0 = lo / BN, kt1 = hi < 0 ? -1 : hi / BN;
+
+  u32x4 kreg[C::KLOADS];
+  u32x4 vreg[C::VLOADS][4];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < C::KLOADS; ++r) {
+      const int c = tid + r * C::NT, row = c / C::KCH, cc = c % C::KCH, j = j0 + row;
+      kreg[r] = j < m.L ? ldg16(Kg + (size_t)j * kstride + cc * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < C::VLOADS; ++r) {
+      const int c = tid + r * C::NT;
+      const int dg = c % (DV / 8), kg = c / (DV / 8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = j0 + kg * 4 + t;
+        vreg[r][t] = (c < C::VBLK && j < m.L) ? ldg16(Vg + (size_t)j * vstride + dg * 8)
+                                              : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < C::KLOADS; ++r) {
+      const int c = tid + r * C::NT, row = c / C::KCH, cc = c % C::KCH;
+      *reinterpret_cast<u32x4*>(Ks + row * C::KP + cc * 8) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < C::VLOADS; ++r) {
+      const int c = tid + r * C::NT;
+      if (c < C::VBLK) {
+        const int dg = c % (DV / 8), kg = c / (DV / 8);
+        const int pos = perm16(kg * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x0 = vreg[r][0][e], x1 = vreg[r][1][e], x2 = vreg[r][2][e], x3 = vreg[r][3][e];
+          u32x2 even = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
+          u32x2 odd = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
+          *reinterpret_cast<u32x2*>(Vt + (dg * 8 + 2 * e) * C::VP + pos) = even;
+          *reinterpret_cast<u32x2*>(Vt + (dg * 8 + 2 * e + 1) * C::VP + pos) = odd;
+        }
+      }
+    }
+  };
+
+  if (kt0 <= kt1) load_tile(kt0 * BN);
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int j0 = kt * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt < kt1) load_tile(j0 + BN);
+
+    const int cls = tile_class(m, row_w0, 32, j0, BN);
+    if (cls == TILE_SKIP) continue;
+
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < DQK / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        const bf16x8 ka =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * C::KP + ks * 16 + hf * 8));
+        s[kb] = mfma32(ka, qreg[ks], s[kb]);
+      }
+    }
+
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = s[kb][i] * a.scale_log2;
+        if (cls == TILE_PARTIAL && !visible(m, qi, j0 + kb * 32 + acc_row(i, hf))) x = -__builtin_inff();
+        s[kb][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run + 8.0f)) {
+      const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
+    }
+    const float mu = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+    float ls = 0.0f;
+    bf16x8 pb[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(s[kb][half * 8 + 2 * e] - mu);
+          const float p1 = fast_exp2(s[kb][half * 8 + 2 * e + 1] - mu);
+          ls += p0 + p1;
+          t[e] = pack_bf16(p0, p1);
+        }
+        pb[kb * 2 + half] = as_bf16x8(t);
+      }
+    }
+    l_run += ls;
+
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; ++kk) {
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db) {
+        const bf16x8 va =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + (db * 32 + l32) * C::VP + kk * 16 + hf * 8));
+        o[db] = mfma32(va, pb[kk], o[db]);
+      }
+    }
+  }
+
+  // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (qi < a.S) {
+    uint16_t* op = static_cast<uint16_t*>(a.out_o) + ((size_t)(b * a.S + qi) * a.Hq + h) * DV + hf * 4;
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db) {
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        u32x2 val = {pack_bf16(o[db][ig * 4] * inv, o[db][ig * 4 + 1] * inv),
+                     pack_bf16(o[db][ig * 4 + 2] * inv, o[db][ig * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + db * 32 + ig * 8) = val;
+      }
+    }
+    if (hf == 0) {
+      const float lse2 = l_tot > 0.0f ? m_run + __log2f(l_tot) : -__builtin_inff();
+      a.out_lse[((size_t)b * a.Hq + h) * a.S + qi] = lse2 * kLn2;
+    }
+  }
+}
+
+template <int DQK, int DV, int BN, int OCC>
+static hipError_t launch_fwd_cfg(KArgs a, hipStream_t stream) {
+  using C = FwdBf16Cfg<DQK, DV, BN>;
+  a.n_tiles = (a.S + C::BM - 1) / C::BM;
+  const long long n = (long long)a.B * a.Hq * a.n_tiles;
+  hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, OCC>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn) {
+  if (dqk == 64 && dv == 64) { *bm = 128; *bn = 64; return true; }
+  if (dqk == 128 && dv == 128) { *bm = 128; *bn = 64; return true; }
+  if (dqk == 192 && dv == 128) { *bm = 128; *bn = 64; return true; }
+  return false;
+}
+
+hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 64 && dv == 64) return launch_fwd_cfg<64, 64, 64, 2>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_fwd_cfg<128, 128, 64, 2>(a, stream);
+  if (dqk == 192 && dv == 128) return launch_fwd_cfg<192, 128, 64, 1>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

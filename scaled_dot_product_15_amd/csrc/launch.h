@@ -1,0 +1,30 @@
+// Internal launcher declarations (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+
+namespace sdpa {
+
+// Rows per block of the backward pre-pass; also the chunk of the d(sink)
+// partial sums.
+constexpr int kPreRows = 64;
+
+bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn);
+hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+
+bool fwd_f32_tiles(int dqk, int dv, int* bm, int* bn);
+hipError_t launch_fwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
+
+// delta = rowsum(dO * O) and d(sink) partials; dtype 0 = f32, 1 = bf16.
+hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream);
+// d_softmax_offset[h] = sum over batches and chunks, fixed order.
+hipError_t launch_dz_reduce(const KArgs& a, hipStream_t stream);
+
+hipError_t launch_debug_tile_map(const KArgs& a, int bm, int bn, int8_t* out, hipStream_t stream);
+hipError_t launch_debug_mask_probe(const KArgs& a, uint8_t* out, hipStream_t stream);
+
+}  // namespace sdpa
