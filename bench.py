@@ -1,0 +1,200 @@
+"""Benchmark of the fused attention forward + backward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+attn_fwd, then the backward stages (pre-pass, dK/dV, dQ, sink-gradient
+reduce).  Inputs are resident in HBM before the timed region.  Prints one JSON
+line with whole-job effective TFLOP/s, counting only visible (query, key)
+pairs: forward 2 * pairs * (d_qk + d_v), backward 2 * pairs * (3 d_qk + 2 d_v).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--case 0]
+                       [--no-cpu-baseline] [--cpu-groups G]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_VALU_TFLOPS = 157.3
+METRIC = "fwd+bwd effective TFLOP/s (bf16 GQA+SWA, S=4096) and % of MFMA bf16 peak"
+
+
+def kernel_flops_per_pair(d_qk, d_v):
+    """Algorithmic MFMA FLOPs per visible pair of each kernel."""
+    return {
+        "fwd": 2 * (d_qk + d_v),                 # S = QK^T, O = PV
+        "bwd_dkdv": 2 * (2 * d_qk + 2 * d_v),    # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
+        "bwd_dq": 2 * (2 * d_qk + d_v),          # S, dP, dQ = dS K
+    }
+
+
+def cpu_baseline(p, arr, groups):
+    """Time the float64 oracle on `groups` (batch, kv-head) groups of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    from scaled_dot_product_15_amd import inputs
+    import torch
+    t = inputs.to_torch(arr, p.dtype, "cpu")
+    f64 = inputs.exact_f64
+    q, k, v, do = f64(t["q"][:1]), f64(t["k"][:1]), f64(t["v"][:1]), f64(t["do"][:1])
+    seq = None if arr["seqlens"] is None else arr["seqlens"][:1]
+    t0 = time.perf_counter()
+    for g in range(groups):
+        oracle.attention_group(q, k, v, do, b=0, g=g, num_gqa_groups=p.Hkv, causal=p.causal,
+                               window=p.window, scale_factor=p.scale_factor or None,
+                               softmax_type=p.softmax_type, softmax_offset=arr["alpha"],
+                               seqlens=seq)
+    dt = time.perf_counter() - t0
+    L = p.S if seq is None else int(seq[0])
+    pairs = oracle.visible_pairs(p.S, L, p.causal, p.window[0], p.window[1]) * (p.Hq // p.Hkv) * groups
+    ff, fb = oracle.effective_flops(pairs, p.d_qk, p.d_v)
+    return {"value": (ff + fb) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{groups} of {p.B * p.Hkv} (batch, kv-head) groups of the workload: "
+                      f"{groups * (p.Hq // p.Hkv)} query heads x S={p.S}, fwd+bwd, numpy float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--case", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=12)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the attention path here is single-GPU; no multi-GPU figure is produced.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from scaled_dot_product_15_amd import binding, inputs
+
+    p = inputs.workload_configs()[args.config][args.case]
+    seed = 1000 * args.config + args.case
+    arr = inputs.draw(p, seed)
+    t = inputs.to_torch(arr, p.dtype, "cuda")
+    dev = torch.cuda.get_device_properties(0)
+
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
+              window_size=p.window, scale_factor=p.scale_factor or None,
+              softmax_type=p.softmax_type, softmax_offset=t["alpha"], seqlens=t["seqlens"])
+    o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
+    want = p.softmax_type != "vanilla"
+    dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
+    outs = (dq, dk, dv, doff)
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"],
+                             p.window, kw["scale_factor"], p.softmax_type)
+    ws = torch.empty(binding.attn_bwd_workspace_size(pp), dtype=torch.uint8, device="cuda")
+    fast = dict(kw, check_seqlens=False)
+    stream = torch.cuda.current_stream()
+    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_offset"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
+        for s in range(1, 5):
+            if ev is not None:
+                ev[s].record(stream)
+            binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
+                             outs=outs, stage=s, **fast)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for s, n in enumerate(names):
+            per[n].append(ev[s].elapsed_time(ev[s + 1]))
+    avg_ms = {n: statistics.fmean(v) for n, v in per.items()}
+    med_ms = {n: statistics.median(v) for n, v in per.items()}
+
+    seq = arr["seqlens"]
+    pairs_per_head = [oracle.visible_pairs(p.S, p.S if seq is None else int(seq[b]), p.causal,
+                                           p.window[0], p.window[1]) for b in range(p.B)]
+    pairs = sum(pairs_per_head) * p.Hq
+    f_fwd, f_bwd = oracle.effective_flops(pairs, p.d_qk, p.d_v)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    t_fwd = med_ms["fwd"]
+    t_bwd = sum(med_ms[n] for n in names[1:])
+
+    kflops = kernel_flops_per_pair(p.d_qk, p.d_v)
+    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg_ms[n])
+    achieved = kflops[dominant] * pairs / (avg_ms[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "flops_per_launch": kflops[dominant] * pairs, "avg_launch_ms": round(avg_ms[dominant], 4)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": p.name, "batch": p.B, "seq_len": p.S, "num_heads": p.Hq,
+                   "num_gqa_groups": p.Hkv, "head_dim_qk": p.d_qk, "head_dim_v": p.d_v,
+                   "mask": "causal" if p.causal else "none", "window": list(p.window),
+                   "softmax_type": p.softmax_type, "seed": seed,
+                   "seqlens": None if seq is None else [int(x) for x in seq]},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "pairs": pairs,
+        "gflop_fwd": round(f_fwd / 1e9, 3),
+        "gflop_bwd": round(f_bwd / 1e9, 3),
+        "t_fwd_ms": round(t_fwd, 4),
+        "t_bwd_ms": round(t_bwd, 4),
+        "tflops_fwd": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+        "tflops_bwd": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "kernel_avg_ms": {n: round(v, 4) for n, v in avg_ms.items()},
+        "kernel_median_ms": {n: round(v, 4) for n, v in med_ms.items()},
+        "roofline": roofline,
+        "device": {"name": dev.name, "compute_units": dev.multi_processor_count,
+                   "gcn_arch": getattr(dev, "gcnArchName", "")},
+        "context": "pages report only a ~52x fwd+bwd speedup of a fused call over a score-materialising "
+                   "XLA baseline on one GB200 (no absolute figure)",
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(p, arr, args.cpu_groups)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -128,6 +128,25 @@ int attn_bwd(const struct attn_params* p, const void* q, const void* k, const vo
              const int32_t* seqlens, void* dq, void* dk, void* dv, float* d_softmax_offset,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* One stage of attn_bwd, same arguments and checks as attn_bwd.  attn_bwd
+ * runs the stages 1..4 in order on one stream; stage 1 must complete before
+ * stages 2 and 3, which are independent of each other (a caller may put them
+ * on two streams), and stage 4 needs only stage 1.
+ *   1 ATTN_BWD_STAGE_PREPROCESS  delta = rowsum(dO * O) and per-block partial
+ *                                sums of d(sink logit), into the workspace
+ *   2 ATTN_BWD_STAGE_DKDV        dK, dV
+ *   3 ATTN_BWD_STAGE_DQ          dQ
+ *   4 ATTN_BWD_STAGE_OFFSET_GRAD d_softmax_offset (no-op when it is NULL)
+ * Any other stage value returns ATTN_ERR_INVALID_ARG. */
+#define ATTN_BWD_STAGE_PREPROCESS 1
+#define ATTN_BWD_STAGE_DKDV 2
+#define ATTN_BWD_STAGE_DQ 3
+#define ATTN_BWD_STAGE_OFFSET_GRAD 4
+int attn_bwd_stage(int stage, const struct attn_params* p, const void* q, const void* k, const void* v,
+                   const void* o, const void* d_o, const float* lse, const float* softmax_offset,
+                   const int32_t* seqlens, void* dq, void* dk, void* dv, float* d_softmax_offset,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

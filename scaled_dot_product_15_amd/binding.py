@@ -48,6 +48,8 @@ EXPORTS = {
                                 ctypes.c_size_t, _vp]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_stage": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_tile_shape": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32)]),
@@ -192,7 +194,7 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
 def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causal",
              window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
              seqlens=None, want_d_offset=None, workspace=None, outs=None, stream=None,
-             check_seqlens=True):
+             check_seqlens=True, stage=0):
     """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None).
 
     d_softmax_offset is returned for learnable softmax (always) and for
@@ -228,9 +230,13 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
-                        _ptr(softmax_offset), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(doff), _ptr(workspace), workspace.numel(), _stream(stream)), "attn_bwd")
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+            _ptr(softmax_offset), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(doff), _ptr(workspace), workspace.numel(), _stream(stream))
+    if stage:
+        _check(lib.attn_bwd_stage(stage, *args), f"attn_bwd_stage({stage})")
+    else:
+        _check(lib.attn_bwd(*args), "attn_bwd")
     return dq, dk, dv, doff
 
 

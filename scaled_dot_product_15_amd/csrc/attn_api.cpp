@@ -104,9 +104,15 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   return hip_status(launch_fwd_f32(a, p->head_dim_qk, p->head_dim_v, s));
 }
 
-int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
-             const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq, void* dk, void* dv,
-             float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+               const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq,
+               void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (stage < 0 || stage > ATTN_BWD_STAGE_OFFSET_GRAD) return ATTN_ERR_INVALID_ARG;
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
@@ -131,13 +137,44 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.delta = static_cast<float*>(workspace);
   a.dz_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_bwd_pre(a, p->dtype, p->head_dim_v, s);
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  e = p->dtype == ATTN_BF16 ? launch_bwd_bf16(a, p->head_dim_qk, p->head_dim_v, s)
-                            : launch_bwd_f32(a, p->head_dim_qk, p->head_dim_v, s);
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  if (d_softmax_offset && p->softmax_type != ATTN_SOFTMAX_VANILLA) return hip_status(launch_dz_reduce(a, s));
+  const bool bf16 = p->dtype == ATTN_BF16;
+  const int dqk = p->head_dim_qk, dvd = p->head_dim_v;
+  if (stage == 0 || stage == ATTN_BWD_STAGE_PREPROCESS) {
+    if (launch_bwd_pre(a, p->dtype, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (stage == 0 || stage == ATTN_BWD_STAGE_DKDV) {
+    hipError_t e = bf16 ? launch_bwd_dkdv_bf16(a, dqk, dvd, s) : launch_bwd_dkdv_f32(a, dqk, dvd, s);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (stage == 0 || stage == ATTN_BWD_STAGE_DQ) {
+    hipError_t e = bf16 ? launch_bwd_dq_bf16(a, dqk, dvd, s) : launch_bwd_dq_f32(a, dqk, dvd, s);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&
+      p->softmax_type != ATTN_SOFTMAX_VANILLA) {
+    if (launch_dz_reduce(a, s) != hipSuccess) return ATTN_ERR_HIP;
+  }
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+             const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq, void* dk, void* dv,
+             float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, dq, dk, dv, d_softmax_offset, workspace,
+                    workspace_bytes, stream);
+}
+
+int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                   const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq,
+                   void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (stage < ATTN_BWD_STAGE_PREPROCESS) return ATTN_ERR_INVALID_ARG;
+  return bwd_common(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, dq, dk, dv, d_softmax_offset,
+                    workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_string(int status) {

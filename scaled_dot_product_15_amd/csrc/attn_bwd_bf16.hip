@@ -427,24 +427,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
 }
 
 template <int DQK, int DV>
-static hipError_t launch_bwd_cfg(KArgs a, hipStream_t stream) {
+static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   using D = DkdvCfg<DQK, DV>;
-  using Q = DqCfg<DQK, DV>;
   const int nkt = (a.S + D::BN - 1) / D::BN;
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(D::NT), 0,
                      stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t launch_dq_cfg(KArgs a, hipStream_t stream) {
+  using Q = DqCfg<DQK, DV>;
   a.n_tiles = (a.S + Q::BM - 1) / Q::BM;
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV>), dim3((unsigned)(a.n_tiles * a.B * a.Hq)), dim3(Q::NT), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
-  if (dqk == 64 && dv == 64) return launch_bwd_cfg<64, 64>(a, stream);
-  if (dqk == 128 && dv == 128) return launch_bwd_cfg<128, 128>(a, stream);
-  if (dqk == 192 && dv == 128) return launch_bwd_cfg<192, 128>(a, stream);
+hipError_t launch_bwd_dkdv_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 64 && dv == 64) return launch_dkdv_cfg<64, 64>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_dkdv_cfg<128, 128>(a, stream);
+  if (dqk == 192 && dv == 128) return launch_dkdv_cfg<192, 128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 64 && dv == 64) return launch_dq_cfg<64, 64>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_dq_cfg<128, 128>(a, stream);
+  if (dqk == 192 && dv == 128) return launch_dq_cfg<192, 128>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -189,13 +189,18 @@ hipError_t launch_fwd_f32(const KArgs& a0, int dqk, int dv, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const KArgs& a0, int dqk, int dv, hipStream_t stream) {
+hipError_t launch_bwd_dkdv_f32(const KArgs& a0, int dqk, int dv, hipStream_t stream) {
   if (!(dqk == 64 && dv == 64)) return hipErrorInvalidValue;
   KArgs a = a0;
   a.n_tiles = (a.S + kF32Tile - 1) / kF32Tile;
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<64, 64>), dim3((unsigned)(a.n_tiles * a.B * a.Hkv)), dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_f32(const KArgs& a0, int dqk, int dv, hipStream_t stream) {
+  if (!(dqk == 64 && dv == 64)) return hipErrorInvalidValue;
+  KArgs a = a0;
+  a.n_tiles = (a.S + kF32Tile - 1) / kF32Tile;
   hipLaunchKernelGGL((bwd_dq_f32_kernel<64, 64>), dim3((unsigned)(a.n_tiles * a.B * a.Hq)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

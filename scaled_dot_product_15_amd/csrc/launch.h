@@ -13,11 +13,13 @@ constexpr int kPreRows = 64;
 
 bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
-hipError_t launch_bwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 
 bool fwd_f32_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
-hipError_t launch_bwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_dkdv_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_bwd_dq_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
 
 // delta = rowsum(dO * O) and d(sink) partials; dtype 0 = f32, 1 = bf16.
 hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream);
