@@ -5,6 +5,7 @@ import this package.  It is independent of the HIP library: it imports nothing
 from it and shares none of its code.
 """
 from .sdpa_oracle import (  # noqa: F401
-    LEARNABLE, OFF_BY_ONE, SOFTMAX_TYPES, VANILLA, attention, attention_group,
+    LEARNABLE, OFF_BY_ONE, SOFTMAX_TYPES, VANILLA, attention, attention_group, attention_keys,
+    attention_rows, visible_rows,
     effective_flops, kv_head, sink_logit, visible_mask, visible_pairs,
 )

@@ -235,3 +235,92 @@ def effective_flops(pairs: int, d_qk: int, d_v: int):
     recompute, dP, dV, dK, dQ = 2 (3 d_qk + 2 d_v) per pair.
     """
     return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)
+
+
+def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_right: int) -> np.ndarray:
+    """Boolean [len(rows), S]: the visible_mask definition for selected query rows."""
+    i = np.asarray(rows)[:, None]
+    j = np.arange(S)[None, :]
+    m = (i < L) & (j < L)
+    if causal:
+        m = m & (j <= i)
+    if window_left >= 0:
+        m = m & (j >= i - window_left)
+    if window_right >= 0:
+        m = m & (j <= i + window_right)
+    return m
+
+
+def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True, window=(-1, -1),
+                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None):
+    """Outputs of selected query rows of one (batch b, query head h), in float64.
+
+    A row's output, LSE, delta and dQ depend only on that row's visible keys,
+    so rows can be computed one by one at any sequence length.  Columns where
+    the row mask is zero for every selected row are left out: they contribute
+    exactly zero.  Returns o [n, dv], lse [n], delta [n], dq [n, dqk] and
+    dz [n] = -exp(z - LSE_i) * delta_i (0 for vanilla).
+    """
+    B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
+    g = kv_head(h, Hq, Hkv)
+    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+    rows = np.asarray(rows, dtype=np.int64)
+    mask = visible_rows(rows, S, L, causal, int(window[0]), int(window[1]))
+    cols = np.nonzero(mask.any(axis=0))[0]
+    c0, c1 = (int(cols[0]), int(cols[-1]) + 1) if cols.size else (0, 1)  # one fully masked column
+    mask = mask[:, c0:c1]
+    kb = np.asarray(k[b, c0:c1, g, :], dtype=np.float64)
+    vb = np.asarray(v[b, c0:c1, g, :], dtype=np.float64)
+    qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    doh = np.asarray(d_o[b, rows, h, :], dtype=np.float64)
+    z = sink_logit(softmax_type, softmax_offset, h)
+    s = scale * (qh @ kb.T)
+    p, lse = _softmax_rows(s, mask, z)
+    o = p @ vb
+    delta = (doh * o).sum(axis=1)
+    ds = p * (doh @ vb.T - delta[:, None])
+    dq = scale * (ds @ kb)
+    if z is None:
+        dz = np.zeros(len(rows))
+    else:
+        dz = -np.exp(z - np.where(np.isfinite(lse), lse, z)) * delta
+    return {"o": o, "lse": lse, "delta": delta, "dq": dq, "dz": dz}
+
+
+def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True, window=(-1, -1),
+                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None,
+                   row_block=1024):
+    """dK, dV of selected keys of one (batch b, KV head g), in float64.
+
+    dK_j = scale * sum_h sum_i dS_ij Q_i and dV_j = sum_h sum_i P_ij dO_i over
+    the query heads h of the group and every row i that sees key j; each such
+    row's LSE and delta come from attention_rows.  Returns dk [n, dqk], dv [n, dv].
+    """
+    B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
+    G = Hq // Hkv
+    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+    keys = np.asarray(keys, dtype=np.int64)
+    # rows that see any selected key: the mask definition, transposed
+    sees = visible_rows(np.arange(S), S, L, causal, int(window[0]), int(window[1]))[:, keys]
+    rows_all = np.nonzero(sees.any(axis=1))[0]
+    kk = np.asarray(k[b, keys, g, :], dtype=np.float64)
+    vk = np.asarray(v[b, keys, g, :], dtype=np.float64)
+    dk = np.zeros((len(keys), dqk))
+    dvv = np.zeros((len(keys), dv_dim))
+    kw = dict(num_gqa_groups=Hkv, causal=causal, window=window, scale_factor=scale_factor,
+              softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens)
+    for gi in range(G):
+        h = g * G + gi
+        for r0 in range(0, len(rows_all), row_block):
+            rows = rows_all[r0:r0 + row_block]
+            rr = attention_rows(q, k, v, d_o, b=b, h=h, rows=rows, **kw)
+            m = sees[rows]
+            qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
+            doh = np.asarray(d_o[b, rows, h, :], dtype=np.float64)
+            s = scale * (qh @ kk.T)
+            lse = np.where(np.isfinite(rr["lse"]), rr["lse"], 0.0)
+            p = np.where(m, np.exp(np.where(m, s, 0.0) - lse[:, None]), 0.0)
+            ds = p * (doh @ vk.T - rr["delta"][:, None])
+            dk += scale * (ds.T @ qh)
+            dvv += p.T @ doh
+    return {"dk": dk, "dv": dvv}

@@ -449,6 +449,63 @@ def pin_golden(orc):
                case["name"] + " lse")
 
 
+def pin_sampled_rows(orc):
+    """Row-sampled outputs vs brute force (O, LSE), finite differences (dQ) and
+    the closed forms of delta and d(sink logit) from brute-force O and LSE."""
+    h_fd = 1e-6
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(1300 + ci)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.45, softmax_type=st,
+                      softmax_offset=alpha, seqlens=None if sl is None else np.array(sl))
+            o_bf, lse_bf = brute_forward(q, k, v, 2, causal, win[0], win[1], 0.45, st, alpha, sl)
+            for b in range(2):
+                for h in (0, 3):
+                    rows = [0, 4, 8, 2] if ci % 2 else [8, 1, 5]
+                    r = orc.attention_rows(q, k, v, do, b=b, h=h, rows=rows, **kw)
+                    _close(r["o"], o_bf[b, rows, h], 1e-12, 1e-14, f"rows O {ci} {st}")
+                    _close(r["lse"], lse_bf[b, h, rows], 1e-12, 1e-14, f"rows LSE {ci} {st}")
+                    delta = (o_bf[b, rows, h] * do[b, rows, h]).sum(axis=1)
+                    _close(r["delta"], delta, 1e-12, 1e-14, "rows delta")
+                    if st != "vanilla":
+                        z = 0.0 if st == "off_by_one" else alpha[h]
+                        lse_s = np.where(np.isfinite(lse_bf[b, h, rows]), lse_bf[b, h, rows], z)
+                        _close(r["dz"], -np.exp(z - lse_s) * delta, 1e-12, 1e-14, "rows dz")
+                    ri = rows[0]
+                    for d in range(q.shape[3]):
+                        q[b, ri, h, d] += h_fd
+                        lp = _loss(orc, q, k, v, do, alpha, **{x: y for x, y in kw.items() if x != "softmax_offset"})
+                        q[b, ri, h, d] -= 2 * h_fd
+                        lm = _loss(orc, q, k, v, do, alpha, **{x: y for x, y in kw.items() if x != "softmax_offset"})
+                        q[b, ri, h, d] += h_fd
+                        _close(r["dq"][0, d], (lp - lm) / (2 * h_fd), 1e-6, 1e-8, f"rows dQ fd {ci} {st}")
+
+
+def pin_sampled_keys(orc):
+    """Key-sampled dK, dV vs finite differences of sum(dO * O)."""
+    h_fd = 1e-6
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(1400 + ci, B=2, S=8, dqk=3, dv=2)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.55, softmax_type=st,
+                      seqlens=None if sl is None else np.array(sl))
+            for b in range(2):
+                g = (b + ci) % 2
+                keys = [7, 0, 3] if ci % 2 else [5, 2]
+                r = orc.attention_keys(q, k, v, do, b=b, g=g, keys=keys, softmax_offset=alpha,
+                                       row_block=3, **kw)
+                for n, j in enumerate(keys):
+                    for name, arr, got in (("k", k, r["dk"]), ("v", v, r["dv"])):
+                        for d in range(arr.shape[3]):
+                            arr[b, j, g, d] += h_fd
+                            lp = _loss(orc, q, k, v, do, alpha, **kw)
+                            arr[b, j, g, d] -= 2 * h_fd
+                            lm = _loss(orc, q, k, v, do, alpha, **kw)
+                            arr[b, j, g, d] += h_fd
+                            _close(got[n, d], (lp - lm) / (2 * h_fd), 1e-6, 1e-8, f"keys d{name} {ci} {st}")
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
-            pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden]
+            pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
+            pin_sampled_keys]

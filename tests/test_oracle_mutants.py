@@ -19,7 +19,7 @@ MUTANTS = {
     "off_by_one_logit_1": [("    if softmax_type == OFF_BY_ONE:\n        return 0.0",
                             "    if softmax_type == OFF_BY_ONE:\n        return 1.0")],
     "gqa_strided_heads": [("return h // (num_heads // num_kv_heads)", "return h % num_kv_heads"),
-                          ("h = g * G + gi", "h = gi * Hkv + g")],
+                          ("h = g * G + gi", "h = gi * Hkv + g", "all")],
     "dk_missing_scale": [('out["dk"] += scale * (ds.T @ qh)', 'out["dk"] += (ds.T @ qh)')],
     "dv_untransposed_p": [('out["dv"] += p.T @ doh', 'out["dv"] += p @ doh')],
     "dq_wrong_operand": [('out["dq"][:, gi, :] = scale * (ds @ kb)', 'out["dq"][:, gi, :] = scale * (ds.T @ kb)')],
@@ -27,16 +27,22 @@ MUTANTS = {
     "window_left_exclusive": [("m &= j >= i - window_left", "m &= j > i - window_left")],
     "window_right_off_by_one": [("m &= j <= i + window_right", "m &= j <= i + window_right + 1")],
     "causal_reversed": [("m &= j <= i\n", "m &= j >= i\n")],
-    "padding_rows_only": [("m = (i < L) & (j < L)", "m = (i < L)")],
+    "padding_rows_only": [("    m = (i < L) & (j < L)\n    if causal:\n        m &= j <= i",
+                           "    m = (i < L)\n    if causal:\n        m &= j <= i")],
     "sink_not_in_denominator": [("l = l + np.exp(z - m_safe)", "l = l")],
     "lse_missing_max": [("lse = np.where(l > 0, m_safe + np.log(l), -np.inf)",
                          "lse = np.where(l > 0, np.log(l), -np.inf)")],
     "dz_sign_flip": [('out["dz"][gi] = -(np.exp(z - lse_safe) * delta).sum()',
                       'out["dz"][gi] = (np.exp(z - lse_safe) * delta).sum()')],
     "default_scale_uses_dv": [("scale = (1.0 / math.sqrt(dqk))", "scale = (1.0 / math.sqrt(v.shape[3]))")],
-    "sink_logit_scaled": [("z = sink_logit(softmax_type, softmax_offset, h)",
+    "sink_logit_scaled": [("z = sink_logit(softmax_type, softmax_offset, h)\n        s = scale * (qh @ kb.T)",
                            "z = sink_logit(softmax_type, softmax_offset, h)\n"
-                           "        z = None if z is None else z * scale")],
+                           "        z = None if z is None else z * scale\n        s = scale * (qh @ kb.T)")],
+    "rows_dq_missing_scale": [("dq = scale * (ds @ kb)\n", "dq = ds @ kb\n")],
+    "rows_window_off_by_one": [("m = m & (j >= i - window_left)", "m = m & (j > i - window_left)")],
+    "keys_dk_missing_scale": [("dk += scale * (ds.T @ qh)", "dk += ds.T @ qh")],
+    "keys_rows_subset": [("rows_all = np.nonzero(sees.any(axis=1))[0]",
+                          "rows_all = np.nonzero(sees.any(axis=1))[0][1:]")],
 }
 
 # cheap pins first: a mutant stops at its first failing pin
@@ -44,14 +50,18 @@ ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_ca
          oracle_pins.pin_window_limits, oracle_pins.pin_row_sums, oracle_pins.pin_sink_closed,
          oracle_pins.pin_gqa_repeat, oracle_pins.pin_padding, oracle_pins.pin_scale,
          oracle_pins.pin_dalpha_forms, oracle_pins.pin_sink_augmented,
-         oracle_pins.pin_torch_sdpa, oracle_pins.pin_finite_diff]
+         oracle_pins.pin_torch_sdpa, oracle_pins.pin_finite_diff, oracle_pins.pin_sampled_rows,
+         oracle_pins.pin_sampled_keys]
 
 
 def _mutant(edits):
     with open(SRC) as f:
         src = f.read()
-    for old, new in edits:
-        assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    for edit in edits:
+        old, new = edit[0], edit[1]
+        every = len(edit) > 2 and edit[2] == "all"
+        n = src.count(old)
+        assert n >= 1 and (every or n == 1), f"mutation anchor not unique/present: {old!r}"
         src = src.replace(old, new)
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src, "oracle_mutant.py", "exec"), mod.__dict__)
