@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--case", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=12)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 launches) to "
+                         "calibrate the HBM byte counters, then exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -85,6 +88,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
+        return
 
     import oracle
     from scaled_dot_product_15_amd import binding, inputs

@@ -89,7 +89,7 @@ struct attn_params {
   int32_t mask_type;      /* ATTN_MASK_NONE | ATTN_MASK_CAUSAL */
   int32_t window_left;    /* >= -1; -1 = unbounded */
   int32_t window_right;   /* >= -1; -1 = unbounded */
-  float scale_factor;     /* finite; 0 => 1/sqrt(Dqk) */
+  float scale_factor;     /* finite, >= 0; 0 => 1/sqrt(Dqk) */
   int32_t softmax_type;   /* ATTN_SOFTMAX_* */
 };
 

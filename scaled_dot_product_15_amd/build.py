@@ -25,7 +25,10 @@ ARCH = "gfx950"
 # Packed-fp32 VALU instructions are disabled for every GPU source: hipcc still
 # emits plain fp32 instructions for float / float2 code.  The host pass warns
 # that it does not know the feature; that warning is harmless.
-GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # keep MFMA accumulators in ordinary VGPRs: the softmax reads
+             # them with VALU instructions, which cannot address AGPRs
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 

@@ -25,13 +25,16 @@ int check_fields(const attn_params* p) {
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (p->mask_type != ATTN_MASK_NONE && p->mask_type != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
-  if (!isfinite(p->scale_factor)) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(p->scale_factor) || p->scale_factor < 0.0f) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type < ATTN_SOFTMAX_VANILLA || p->softmax_type > ATTN_SOFTMAX_LEARNABLE) return ATTN_ERR_INVALID_ARG;
   // Kernels index rows with 32-bit (batch * S + i) and launch one-dimensional
   // grids of B * heads * tiles workgroups.
   const long long rows = (long long)p->batch * p->seqlen;
   const long long grid = (long long)p->batch * p->num_heads * ((p->seqlen + 63) / 64);
   if (rows > 0x7fffffffLL || grid > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  // Kernels address one batch of one tensor with 32-bit byte offsets.
+  const long long dmax = p->head_dim_qk > p->head_dim_v ? p->head_dim_qk : p->head_dim_v;
+  if ((long long)p->seqlen * p->num_heads * dmax * 4 > 0xffffffffLL) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }
 

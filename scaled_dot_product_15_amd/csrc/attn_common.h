@@ -97,4 +97,58 @@ __device__ __forceinline__ int perm16(int r) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return zero, so padded rows read as zeros without per-lane branches.
+// Word 3 (0x00020000) selects 32-bit data format for raw (untyped) access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand (rows = head dims, reduction = sequence positions) of a 32x32x16
+// MFMA, read with two LDS transpose loads from a row-major [position][dim]
+// bf16 tile.  Within each 16-lane group the transpose load treats the 8-byte
+// chunks of lanes 4s..4s+3 as row s of a 4x16 matrix and hands lane c
+// its column c.  Lane l (group G = l/16, half hf = G/2) therefore addresses
+// position pos0 + hf*4 + s at dims d0 + (G%2)*16 + 4q (s = (l/4)%4, q = l%4)
+// and receives dim d0 + l%32 of positions pos0 + hf*4 + {0..3}; the second
+// load adds 8 positions.  Those are exactly the rows acc_row(e, hf), e = 0..7,
+// that a lane of a 32x32 accumulator holds for the same 16 positions, so the
+// B operand can come straight from accumulator registers.
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int pitch, int pos0, int d0, int lane) {
+  const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+  const uint16_t* p = tile + (pos0 + (G >> 1) * 4 + s) * pitch + d0 + (G & 1) * 16 + q * 4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * pitch));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Keys visible from query row qi, as an inclusive interval [lo, hi]
+// (empty when lo > hi).  Same rule as visible(): row qi < L sees keys
+// max(0, qi-wl) .. min(L-1, qi [causal], qi+wr).
+__device__ __forceinline__ void row_key_bounds(const MaskSpec& m, int qi, int& lo, int& hi) {
+  lo = m.wl >= 0 ? (qi - m.wl > 0 ? qi - m.wl : 0) : 0;
+  hi = m.L - 1;
+  if (m.causal && qi < hi) hi = qi;
+  if (m.wr >= 0 && qi + m.wr < hi) hi = qi + m.wr;
+  if (qi >= m.L) { lo = 1; hi = 0; }
+}
+
+// Query rows that see key kj, as an inclusive interval [lo, hi]: the same
+// rule read by column, rows max(0, kj [causal], kj-wr) .. min(L-1, kj+wl).
+__device__ __forceinline__ void col_query_bounds(const MaskSpec& m, int kj, int& lo, int& hi) {
+  lo = 0;
+  if (m.causal) lo = kj;
+  if (m.wr >= 0 && kj - m.wr > lo) lo = kj - m.wr;
+  hi = m.L - 1;
+  if (m.wl >= 0 && kj + m.wl < hi) hi = kj + m.wl;
+  if (kj >= m.L) { lo = 1; hi = 0; }
+}
+
 }  // namespace sdpa

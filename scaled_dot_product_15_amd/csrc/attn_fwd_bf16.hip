@@ -7,24 +7,29 @@
 //
 // Work decomposition: one workgroup of 4 waves owns BM = 128 query rows of one
 // (batch, query head); each wave owns 32 rows.  The workgroup walks the key
-// tiles (BN keys) that the mask engine says are visible from its rows.
+// tiles (BN keys) that the mask engine says are visible from its rows; each
+// wave skips the tiles its own 32 rows cannot see and evaluates the mask per
+// element only on tiles its rows see partially.
 //
 // Per key tile and wave:
-//   S^T (keys x queries) = K Q^T with A = K from LDS (row-major, padded rows)
-//   and B = Q^T held in registers for the whole loop.  In the 32x32 MFMA
-//   accumulator a lane owns one query column, so the row max/sum of the
-//   online softmax need a single cross-lane step (lane <-> lane^32).
-//   O^T (d x queries) += V^T P^T with B = P^T taken directly from the S^T
-//   accumulator registers (after exp and bf16 rounding) and A = V^T read from
-//   LDS, where V is stored transposed with keys permuted to match the
-//   accumulator's row order (see perm16).
+//   S^T (keys x queries) = K Q^T with A = K rows read from LDS and B = Q^T
+//   held in registers for the whole loop.  In the 32x32 accumulator a lane
+//   owns one query column, so the row max/sum of the online softmax need a
+//   single cross-lane step (lane <-> lane^32).
+//   O^T (dims x queries) += V^T P^T with B = P^T taken straight from the S^T
+//   accumulator registers (after exp and bf16 rounding) and A = V^T read with
+//   LDS transpose loads from the row-major V tile (lds_tr_operand).
+// K and V tiles are staged global -> registers -> LDS as plain row copies;
+// the next tile's global loads are in flight while the current one computes.
 //
-// Online softmax in base 2 with the scale folded into one multiply.  The
-// running max only moves (and O and the row sum are rescaled) when a tile's
-// max exceeds it by more than 8, so most tiles skip the rescale; P is then
-// bounded by 2^8, harmless in fp32/bf16, and the final O = acc / l and
-// LSE = m + log2(l) are exact regardless of which max was used.  A sink logit
-// z starts the running max at z with row sum 1 (its own exp term).
+// Online softmax in base 2 with the scale folded into one FMA.  The running
+// max only moves (and O and the row sum are rescaled) when a tile's max
+// exceeds it by more than 8, so most tiles skip the rescale; P is then bounded
+// by 2^8, harmless in fp32/bf16, and the final O = acc / l and
+// LSE = m + log2(l) are exact whichever max was used.  A sink logit z starts
+// the running max at z with row sum 1 (its own exp term).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "launch.h"
 
@@ -34,14 +39,14 @@ template <int DQK, int DV, int BN>
 struct FwdBf16Cfg {
   static constexpr int BM = 128;
   static constexpr int NT = 256;
-  static constexpr int KP = DQK + 8;   // LDS pitch (bf16) of a K row
-  static constexpr int VP = BN + 8;    // LDS pitch (bf16) of a transposed V row
-  static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
+  static constexpr int KP = DQK + 8;    // LDS pitch (bf16) of a K row: rows 16 B apart mod 256 B
+  static constexpr int VP = DV + 32;    // LDS pitch (bf16) of a V row: 4 rows 64 B apart mod 256 B
+  static constexpr int KCH = DQK / 8;   // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;
   static constexpr int KLOADS = BN * KCH / NT;
-  static constexpr int VBLK = (BN / 4) * (DV / 8);  // 4-key x 8-dim blocks of V
-  static constexpr int VLOADS = (VBLK + NT - 1) / NT;
-  static constexpr int LDS_ELEMS = BN * KP + DV * VP;
-  static_assert(BN * KCH % NT == 0, "K tile must split evenly over the workgroup");
+  static constexpr int VLOADS = BN * VCH / NT;
+  static constexpr int LDS_ELEMS = BN * KP + BN * VP;
+  static_assert(BN * KCH % NT == 0 && BN * VCH % NT == 0, "tiles must split evenly over the workgroup");
   static_assert(BN % 32 == 0 && DQK % 32 == 0 && DV % 32 == 0, "tile shape");
 };
 
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   uint16_t* Ks = lds;
-  uint16_t* Vt = lds + BN * C::KP;
+  uint16_t* Vs = lds + BN * C::KP;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
@@ -81,23 +86,29 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   const int i0 = qt * C::BM;
   const int row_w0 = i0 + w * 32;
   const int qi = row_w0 + l32;
+  int klo, khi;  // keys visible from this lane's query row
+  row_key_bounds(m, qi, klo, khi);
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
   const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
 
+  // Buffer resources end at the valid length: rows >= L read as zeros.
+  const __amdgpu_buffer_rsrc_t kres = buf_rsrc(Kg, (uint32_t)(m.L * kstride * 2));
+  const __amdgpu_buffer_rsrc_t vres = buf_rsrc(Vg, (uint32_t)(m.L * vstride * 2));
+
   // Q^T operand: lane holds query qi, dims [ks*16 + hf*8, +8).
   bf16x8 qreg[DQK / 16];
   {
-    const uint16_t* qp = Q + ((size_t)(b * a.S + (qi < a.S ? qi : 0)) * a.Hq + h) * DQK + hf * 8;
+    const size_t qstride = (size_t)a.Hq * DQK;
+    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(Q + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(m.L * qstride * 2));
+    const uint32_t qoff = (uint32_t)(qi * qstride + hf * 8) * 2;
 #pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks) {
-      u32x4 t = qi < a.S ? ldg16(qp + ks * 16) : u32x4{0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(t);
-    }
+    for (int ks = 0; ks < DQK / 16; ++ks) qreg[ks] = as_bf16x8(buf_load16(qres, qoff + ks * 32));
   }
 
+  const float c = a.scale_log2;  // > 0
   const float z2 = sink_logit(a, h) * kLog2e;
   const bool has_sink = a.softmax_type != 0;
   float m_run = has_sink ? z2 : -__builtin_inff();
@@ -111,61 +122,36 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / BN, kt1 = hi < 0 ? -1 : hi / BN;
 
-  u32x4 kreg[C::KLOADS];
-  u32x4 vreg[C::VLOADS][4];
+  u32x4 kreg[C::KLOADS], vreg[C::VLOADS];
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < C::KLOADS; ++r) {
-      const int c = tid + r * C::NT, row = c / C::KCH, cc = c % C::KCH, j = j0 + row;
-      kreg[r] = j < m.L ? ldg16(Kg + (size_t)j * kstride + cc * 8) : u32x4{0, 0, 0, 0};
+      const int cidx = tid + r * C::NT, row = cidx / C::KCH, cc = cidx % C::KCH;
+      kreg[r] = buf_load16(kres, (uint32_t)((j0 + row) * kstride + cc * 8) * 2);
     }
 #pragma unroll
     for (int r = 0; r < C::VLOADS; ++r) {
-      const int c = tid + r * C::NT;
-      const int dg = c % (DV / 8), kg = c / (DV / 8);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = j0 + kg * 4 + t;
-        vreg[r][t] = (c < C::VBLK && j < m.L) ? ldg16(Vg + (size_t)j * vstride + dg * 8)
-                                              : u32x4{0, 0, 0, 0};
-      }
+      const int cidx = tid + r * C::NT, row = cidx / C::VCH, cc = cidx % C::VCH;
+      vreg[r] = buf_load16(vres, (uint32_t)((j0 + row) * vstride + cc * 8) * 2);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int r = 0; r < C::KLOADS; ++r) {
-      const int c = tid + r * C::NT, row = c / C::KCH, cc = c % C::KCH;
+      const int cidx = tid + r * C::NT, row = cidx / C::KCH, cc = cidx % C::KCH;
       *reinterpret_cast<u32x4*>(Ks + row * C::KP + cc * 8) = kreg[r];
     }
 #pragma unroll
     for (int r = 0; r < C::VLOADS; ++r) {
-      const int c = tid + r * C::NT;
-      if (c < C::VBLK) {
-        const int dg = c % (DV / 8), kg = c / (DV / 8);
-        const int pos = perm16(kg * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x0 = vreg[r][0][e], x1 = vreg[r][1][e], x2 = vreg[r][2][e], x3 = vreg[r][3][e];
-          u32x2 even = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-          u32x2 odd = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-          *reinterpret_cast<u32x2*>(Vt + (dg * 8 + 2 * e) * C::VP + pos) = even;
-          *reinterpret_cast<u32x2*>(Vt + (dg * 8 + 2 * e + 1) * C::VP + pos) = odd;
-        }
-      }
+      const int cidx = tid + r * C::NT, row = cidx / C::VCH, cc = cidx % C::VCH;
+      *reinterpret_cast<u32x4*>(Vs + row * C::VP + cc * 8) = vreg[r];
     }
   };
 
-  if (kt0 <= kt1) load_tile(kt0 * BN);
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int j0 = kt * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt < kt1) load_tile(j0 + BN);
-
-    const int cls = tile_class(m, row_w0, 32, j0, BN);
-    if (cls == TILE_SKIP) continue;
-
+  // One key tile for this wave.  MASKED selects the per-element predicate:
+  // element i of block kb is key j0 + hf*4 + kb*32 + acc_row(i, 0).
+  auto tile = [&](int j0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
@@ -178,19 +164,23 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
         s[kb] = mfma32(ka, qreg[ks], s[kb]);
       }
     }
-
     float mx = -__builtin_inff();
+    if constexpr (MASKED) {
+      const int base = j0 + hf * 4;
+      const int lo_r = klo - base, hi_r = khi - base;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * a.scale_log2;
-        if (cls == TILE_PARTIAL && !visible(m, qi, j0 + kb * 32 + acc_row(i, hf))) x = -__builtin_inff();
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
+          s[kb][i] = (off >= lo_r && off <= hi_r) ? s[kb][i] : -__builtin_inff();
+        }
     }
-    mx = halves_max(mx);
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = halves_max(mx) * c;
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run + 8.0f)) {
       const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
@@ -199,7 +189,7 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
     }
-    const float mu = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+    const float nmu = (m_run == -__builtin_inff()) ? 0.0f : -m_run;
     float ls = 0.0f;
     bf16x8 pb[BN / 16];
 #pragma unroll
@@ -209,8 +199,8 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
         u32x4 t;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(s[kb][half * 8 + 2 * e] - mu);
-          const float p1 = fast_exp2(s[kb][half * 8 + 2 * e + 1] - mu);
+          const float p0 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e], c, nmu));
+          const float p1 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e + 1], c, nmu));
           ls += p0 + p1;
           t[e] = pack_bf16(p0, p1);
         }
@@ -218,16 +208,26 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
       }
     }
     l_run += ls;
-
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) {
-        const bf16x8 va =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(Vt + (db * 32 + l32) * C::VP + kk * 16 + hf * 8));
+        const bf16x8 va = lds_tr_operand(Vs, C::VP, kk * 16, db * 32, lane);
         o[db] = mfma32(va, pb[kk], o[db]);
       }
     }
+  };
+
+  if (kt0 <= kt1) load_tile(kt0 * BN);
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int j0 = kt * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt < kt1) load_tile(j0 + BN);
+    const int cls = tile_class(m, row_w0, 32, j0, BN);
+    if (cls == TILE_FULL) tile(j0, std::false_type{});
+    else if (cls == TILE_PARTIAL) tile(j0, std::true_type{});
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.

@@ -47,7 +47,7 @@ def P(**kw):
 INVALID = [
     dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(Hq=8, Hkv=3), dict(d_qk=0), dict(d_v=-1),
     dict(window_size=(-2, 0)), dict(window_size=(0, -5)), dict(scale_factor=float("nan")),
-    dict(scale_factor=float("inf")), dict(B=70000, S=70000),
+    dict(scale_factor=float("inf")), dict(scale_factor=-0.5), dict(B=70000, S=70000),
 ]
 
 
