@@ -25,10 +25,13 @@ ARCH = "gfx950"
 # Packed-fp32 VALU instructions are disabled for every GPU source: hipcc still
 # emits plain fp32 instructions for float / float2 code.  The host pass warns
 # that it does not know the feature; that warning is harmless.
-GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             # keep MFMA accumulators in ordinary VGPRs: the softmax reads
-             # them with VALU instructions, which cannot address AGPRs
-             "-mllvm", "-amdgpu-mfma-vgpr-form"]
+GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Kernels whose MFMA results feed the softmax VALU directly keep accumulators
+# in ordinary VGPRs (VALU instructions cannot address AGPRs).  The dK/dV
+# kernel is left to the default allocation: its long-lived dK/dV
+# accumulators then sit in AGPRs and free VGPRs for in-flight LDS reads.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+VGPR_FORM_SOURCES = {"attn_fwd_bf16.hip", "attn_bwd_dq_bf16.hip"}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
@@ -47,6 +50,8 @@ def sources():
 def _compile(src, save_temps=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + GPU_FLAGS
+    if os.path.basename(src) in VGPR_FORM_SOURCES:
+        cmd += VGPR_FORM
     if save_temps:
         cmd.append("--save-temps")
     res = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)

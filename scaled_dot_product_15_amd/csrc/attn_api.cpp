@@ -83,7 +83,7 @@ size_t attn_fwd_workspace_size(const attn_params* p) {
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
   if (attn_validate(p) != ATTN_OK) return 0;
-  return delta_bytes(p) + dz_bytes(p);
+  return 2 * delta_bytes(p) + dz_bytes(p);
 }
 
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
@@ -138,7 +138,8 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   a.dv = dv;
   a.d_offset = d_softmax_offset;
   a.delta = static_cast<float*>(workspace);
-  a.dz_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
+  a.dz_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * delta_bytes(p));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == ATTN_BF16;
   const int dqk = p->head_dim_qk, dvd = p->head_dim_v;

@@ -1,7 +1,8 @@
 // Backward pre-pass and the sink-gradient reduction.
 //
 // delta_i = sum_e dO_ie O_ie equals sum_j P_ij dP_ij, the term the softmax
-// backward subtracts from dP (PR #2225: the backward takes dz = dO and returns
+// backward subtracts from dP; the pass also stores LSE_i * log2(e) for the
+// base-2 recomputation of P in the backward kernels (PR #2225: the backward takes dz = dO and returns
 // grad_q/k/v/softmax_offset).  For a sink logit z the gradient is
 // dL/dz = -sum_i exp(z - LSE_i) delta_i: the sink enters only the softmax
 // denominator and carries a zero value row.  Each block writes the partial
@@ -45,7 +46,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(KArgs a) {
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (part == 0) {
-      if (i < a.S) a.delta[((size_t)b * a.Hq + h) * a.S + i] = acc;
+      if (i < a.S) {
+        a.delta[((size_t)b * a.Hq + h) * a.S + i] = acc;
+        a.lse2[((size_t)b * a.Hq + h) * a.S + i] = i < L ? a.lse[((size_t)b * a.Hq + h) * a.S + i] * kLog2e : 0.0f;
+      }
       float dz = 0.0f;
       if (sink && i < L) dz = -expf(z - a.lse[((size_t)b * a.Hq + h) * a.S + i]) * acc;
       dzs[r0 + rr] = dz;

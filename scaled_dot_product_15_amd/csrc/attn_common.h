@@ -34,7 +34,8 @@ struct KArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;       // workspace [B,Hq,S]
+  float* delta;       // workspace [B,Hq,S]: rowsum(dO * O)
+  float* lse2;        // workspace [B,Hq,S]: LSE * log2(e), 0 past the valid length
   float* dz_partial;  // workspace [B,Hq,nchunk]
   float* d_offset;    // [Hq] or nullptr
   int B, S, Hq, Hkv, G;
@@ -128,6 +129,75 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int pitch
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
 }
+
+// ---- swizzled row-major bf16 tiles in LDS ---------------------------------
+//
+// A tile holds R rows of CH 16-byte chunks with no padding; logical chunk c
+// of row r is stored at physical chunk c ^ swz(r).  With 64 four-byte banks
+// (256 B per cycle) the two read patterns the kernels use are then free of
+// bank conflicts:
+//   row reads  (ds_read_b128): 16 lanes read one chunk of 16 consecutive rows;
+//   transpose loads (lds_tr): 32 lanes read 4 chunks of 4 consecutive rows.
+// 256-byte rows all start on bank 0, so swz must spread 16 consecutive rows
+// over 16 distinct chunks and 4 consecutive rows over 4 distinct chunk
+// quads; 128- and 384-byte rows alternate between the two 128-byte halves of
+// the bank array, so swz (kept below 8, which keeps c ^ swz inside the row)
+// must do the same for every other row.  swz is a bijection on the rows of
+// any aligned group of 16 in both cases.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int CH>
+__device__ __forceinline__ int swz_off(int r, int c) { return (r * CH + (c ^ swz<CH>(r))) * 16; }
+
+// 16-byte row read of logical chunk c of row r.
+template <int CH>
+__device__ __forceinline__ u32x4 tile_row16(const uint16_t* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) + swz_off<CH>(r, c));
+}
+
+// lds_tr_operand for a swizzled tile (dims d0 .. d0+31, positions pos0 .. pos0+15).
+template <int CH>
+__device__ __forceinline__ bf16x8 tile_tr_operand(const uint16_t* tile, int pos0, int d0, int lane) {
+  const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+  const int row = pos0 + (G >> 1) * 4 + s;
+  const int dim = d0 + (G & 1) * 16 + q * 4;
+  const char* base = reinterpret_cast<const char*>(tile) + (dim & 7) * 2;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<CH>(row, dim >> 3)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<CH>(row + 8, dim >> 3)));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Asynchronous copy of rows [row0, row0 + R) of a row-major bf16 tensor
+// (rows `stride_bytes` apart, starting at the buffer resource's base) into a
+// swizzled LDS tile, straight from memory to LDS (no registers).  Each
+// instruction moves 64 consecutive physical chunks: lane l of the wave fills
+// physical chunk idx = base + l, i.e. row idx / CH, logical chunk
+// (idx % CH) ^ swz(row).  Rows past the resource's end arrive as zeros.
+// Complete with lds_dma_wait() and a workgroup barrier before reading.
+template <int R, int CH, int NT>
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t res, uint32_t stride_bytes, int row0,
+                                         uint16_t* tile, int tid) {
+  static_assert((R * CH) % (NT) == 0, "tile must split into whole wave instructions");
+  constexpr int PER_WAVE = R * CH / NT;  // instructions per wave
+  const int w = tid >> 6, lane = tid & 63;
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int k = 0; k < PER_WAVE; ++k) {
+    const int base = (w * PER_WAVE + k) * 64;
+    const int idx = base + lane;
+    const int row = idx / CH, c = (idx % CH) ^ swz<CH>(row);
+    const uint32_t voff = (uint32_t)(row0 + row) * stride_bytes + (uint32_t)c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(reinterpret_cast<char*>(tile) + base * 16), 16, voff,
+                                             0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Keys visible from query row qi, as an inclusive interval [lo, hi]
 // (empty when lo > hi).  Same rule as visible(): row qi < L sees keys

@@ -39,14 +39,11 @@ template <int DQK, int DV, int BN>
 struct FwdBf16Cfg {
   static constexpr int BM = 128;
   static constexpr int NT = 256;
-  static constexpr int KP = DQK + 8;    // LDS pitch (bf16) of a K row: rows 16 B apart mod 256 B
-  static constexpr int VP = DV + 32;    // LDS pitch (bf16) of a V row: 4 rows 64 B apart mod 256 B
   static constexpr int KCH = DQK / 8;   // 16-byte chunks per K row
   static constexpr int VCH = DV / 8;
-  static constexpr int KLOADS = BN * KCH / NT;
-  static constexpr int VLOADS = BN * VCH / NT;
-  static constexpr int LDS_ELEMS = BN * KP + BN * VP;
-  static_assert(BN * KCH % NT == 0 && BN * VCH % NT == 0, "tiles must split evenly over the workgroup");
+  static constexpr int KT = BN * DQK;   // elements of one K tile
+  static constexpr int VT = BN * DV;
+  static constexpr int LDS_ELEMS = 2 * (KT + VT);  // double buffered
   static_assert(BN % 32 == 0 && DQK % 32 == 0 && DV % 32 == 0, "tile shape");
 };
 
@@ -75,8 +72,6 @@ template <int DQK, int DV, int BN, int OCC>
 __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  uint16_t* Ks = lds;
-  uint16_t* Vs = lds + BN * C::KP;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
@@ -122,35 +117,17 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / BN, kt1 = hi < 0 ? -1 : hi / BN;
 
-  u32x4 kreg[C::KLOADS], vreg[C::VLOADS];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int r = 0; r < C::KLOADS; ++r) {
-      const int cidx = tid + r * C::NT, row = cidx / C::KCH, cc = cidx % C::KCH;
-      kreg[r] = buf_load16(kres, (uint32_t)((j0 + row) * kstride + cc * 8) * 2);
-    }
-#pragma unroll
-    for (int r = 0; r < C::VLOADS; ++r) {
-      const int cidx = tid + r * C::NT, row = cidx / C::VCH, cc = cidx % C::VCH;
-      vreg[r] = buf_load16(vres, (uint32_t)((j0 + row) * vstride + cc * 8) * 2);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int r = 0; r < C::KLOADS; ++r) {
-      const int cidx = tid + r * C::NT, row = cidx / C::KCH, cc = cidx % C::KCH;
-      *reinterpret_cast<u32x4*>(Ks + row * C::KP + cc * 8) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::VLOADS; ++r) {
-      const int cidx = tid + r * C::NT, row = cidx / C::VCH, cc = cidx % C::VCH;
-      *reinterpret_cast<u32x4*>(Vs + row * C::VP + cc * 8) = vreg[r];
-    }
+  // K / V tiles of buffer `buf`: [BN][DQK] and [BN][DV], swizzled row-major.
+  auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
+  auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
+  auto issue_tile = [&](int j0, int buf) {
+    tile_dma<BN, C::KCH, C::NT>(kres, (uint32_t)(kstride * 2), j0, ktile(buf), tid);
+    tile_dma<BN, C::VCH, C::NT>(vres, (uint32_t)(vstride * 2), j0, vtile(buf), tid);
   };
 
   // One key tile for this wave.  MASKED selects the per-element predicate:
   // element i of block kb is key j0 + hf*4 + kb*32 + acc_row(i, 0).
-  auto tile = [&](int j0, auto masked) {
+  auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     f32x16 s[BN / 32];
 #pragma unroll
@@ -159,8 +136,7 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
     for (int ks = 0; ks < DQK / 16; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8 ka =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * C::KP + ks * 16 + hf * 8));
+        const bf16x8 ka = as_bf16x8(tile_row16<C::KCH>(Ks, kb * 32 + l32, ks * 2 + hf));
         s[kb] = mfma32(ka, qreg[ks], s[kb]);
       }
     }
@@ -212,22 +188,26 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
     for (int kk = 0; kk < BN / 16; ++kk) {
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) {
-        const bf16x8 va = lds_tr_operand(Vs, C::VP, kk * 16, db * 32, lane);
+        const bf16x8 va = tile_tr_operand<C::VCH>(Vs, kk * 16, db * 32, lane);
         o[db] = mfma32(va, pb[kk], o[db]);
       }
     }
   };
 
-  if (kt0 <= kt1) load_tile(kt0 * BN);
+  // Double-buffered pipeline, one barrier per tile: the copy of tile kt+1
+  // runs while tile kt computes; the barrier after the wait both publishes
+  // tile kt+1 and frees tile kt's buffer for the copy after it.
+  if (kt0 <= kt1) issue_tile(kt0 * BN, 0);
+  lds_dma_wait();
+  __syncthreads();
   for (int kt = kt0; kt <= kt1; ++kt) {
-    const int j0 = kt * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt < kt1) load_tile(j0 + BN);
+    const int j0 = kt * BN, buf = (kt - kt0) & 1;
+    if (kt < kt1) issue_tile(j0 + BN, buf ^ 1);
     const int cls = tile_class(m, row_w0, 32, j0, BN);
-    if (cls == TILE_FULL) tile(j0, std::false_type{});
-    else if (cls == TILE_PARTIAL) tile(j0, std::true_type{});
+    if (cls == TILE_FULL) tile(j0, ktile(buf), vtile(buf), std::false_type{});
+    else if (cls == TILE_PARTIAL) tile(j0, ktile(buf), vtile(buf), std::true_type{});
+    lds_dma_wait();
+    __syncthreads();
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
