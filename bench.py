@@ -26,6 +26,36 @@ PEAK_F32_VALU_TFLOPS = 157.3
 METRIC = "fwd+bwd effective TFLOP/s (bf16 GQA+SWA, S=4096) and % of MFMA bf16 peak"
 
 
+TRAFFIC_RECORDS = {2: os.path.join(ROOT, "profiles", "attn_gqa_swa_s4096_hbm_traffic.json")}
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources (names and bytes), to tie counter records to a build."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "scaled_dot_product_15_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    record (each counter scaled by its reading for a plain copy of known size),
+    or None when there is no record or the kernels changed since it was taken."""
+    path = TRAFFIC_RECORDS.get(config)
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
 def kernel_flops_per_pair(d_qk, d_v):
     """Algorithmic MFMA FLOPs per visible pair of each kernel."""
     return {
@@ -45,20 +75,25 @@ def cpu_baseline(p, arr, groups):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     from scaled_dot_product_15_amd import inputs
-    import torch
-    t = inputs.to_torch(arr, p.dtype, "cpu")
+    groups = min(groups, p.B * p.Hkv)
+    nb = -(-groups // p.Hkv)  # batches the sample touches
+    sub = {n: arr[n][:nb] for n in ("q", "k", "v", "do")}
+    sub.update(alpha=arr["alpha"], seqlens=None if arr["seqlens"] is None else arr["seqlens"][:nb])
+    t = inputs.to_torch(sub, p.dtype, "cpu")
     f64 = inputs.exact_f64
-    q, k, v, do = f64(t["q"][:1]), f64(t["k"][:1]), f64(t["v"][:1]), f64(t["do"][:1])
-    seq = None if arr["seqlens"] is None else arr["seqlens"][:1]
+    q, k, v, do = f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"])
+    seq = sub["seqlens"]
     t0 = time.perf_counter()
-    for g in range(groups):
-        oracle.attention_group(q, k, v, do, b=0, g=g, num_gqa_groups=p.Hkv, causal=p.causal,
+    pairs = 0
+    for n in range(groups):
+        b, g = n // p.Hkv, n % p.Hkv
+        oracle.attention_group(q, k, v, do, b=b, g=g, num_gqa_groups=p.Hkv, causal=p.causal,
                                window=p.window, scale_factor=p.scale_factor or None,
                                softmax_type=p.softmax_type, softmax_offset=arr["alpha"],
                                seqlens=seq)
+        L = p.S if seq is None else int(seq[b])
+        pairs += oracle.visible_pairs(p.S, L, p.causal, p.window[0], p.window[1]) * (p.Hq // p.Hkv)
     dt = time.perf_counter() - t0
-    L = p.S if seq is None else int(seq[0])
-    pairs = oracle.visible_pairs(p.S, L, p.causal, p.window[0], p.window[1]) * (p.Hq // p.Hkv) * groups
     ff, fb = oracle.effective_flops(pairs, p.d_qk, p.d_v)
     return {"value": (ff + fb) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
@@ -167,7 +202,7 @@ def main():
     achieved = kflops[dominant] * pairs / (avg_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(args.config, dominant) if args.case == 0 else None,
                 "flops_per_launch": kflops[dominant] * pairs, "avg_launch_ms": round(avg_ms[dominant], 4)}
 
     res = {
