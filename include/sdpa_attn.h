@@ -182,6 +182,13 @@ int attn_host_key_range(const struct attn_params* p, int32_t L, int32_t i0, int3
 int attn_host_query_range(const struct attn_params* p, int32_t L, int32_t j0, int32_t j1,
                           int32_t* lo, int32_t* hi);
 
+/* Host: key tiles [*f0, *f1] (tile t = keys t*block_n .. t*block_n+block_n-1)
+ * that every query row i0 .. i0+block_m-1 sees in full, for valid length L:
+ * the tiles attn_host_tile_map marks 2 for that row block.  Returns 1 if
+ * there are any, else 0 (also on invalid arguments). */
+int attn_host_full_key_tiles(const struct attn_params* p, int32_t L, int32_t i0, int32_t block_m,
+                             int32_t block_n, int32_t* f0, int32_t* f1);
+
 #ifdef __cplusplus
 }
 #endif

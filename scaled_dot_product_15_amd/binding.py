@@ -60,6 +60,8 @@ EXPORTS = {
                                            ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
     "attn_host_query_range": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32,
                                              ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "attn_host_full_key_tiles": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32, _c_i32,
+                                                ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
 }
 
 _lib = None
@@ -280,3 +282,10 @@ def host_query_range(p: Params, L, j0, j1):
     lo, hi = _c_i32(), _c_i32()
     ok = load_library().attn_host_query_range(ctypes.byref(p), L, j0, j1, ctypes.byref(lo), ctypes.byref(hi))
     return (lo.value, hi.value) if ok else None
+
+
+def host_full_key_tiles(p: Params, L, i0, block_m, block_n):
+    f0, f1 = _c_i32(), _c_i32()
+    ok = load_library().attn_host_full_key_tiles(ctypes.byref(p), L, i0, block_m, block_n, ctypes.byref(f0),
+                                                 ctypes.byref(f1))
+    return (f0.value, f1.value) if ok else None

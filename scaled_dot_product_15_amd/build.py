@@ -32,8 +32,12 @@ GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # accumulators then sit in AGPRs and free VGPRs for in-flight LDS reads.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 VGPR_FORM_SOURCES = {"attn_fwd_bf16.hip", "attn_bwd_dq_bf16.hip"}
+# The LDS-copy helper lists M0 as clobbered; M0 is a reserved register, so
+# the compiler warns on every use of it.  These kernels write M0 in that
+# helper only, so the warning is silenced (-Wno-inline-asm; asm errors stay).
+QUIET = ("packed-fp32-ops",)
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Wall", "-Wno-unused-function"]
+          "-Wall", "-Wno-unused-function", "-Wno-inline-asm"]
 
 
 def hipcc() -> str:
@@ -55,7 +59,7 @@ def _compile(src, save_temps=False):
     if save_temps:
         cmd.append("--save-temps")
     res = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in QUIET))
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
     return obj, err

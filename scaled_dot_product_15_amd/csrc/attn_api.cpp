@@ -256,4 +256,14 @@ int attn_host_query_range(const attn_params* p, int32_t L, int32_t j0, int32_t j
   return ok ? 1 : 0;
 }
 
+int attn_host_full_key_tiles(const attn_params* p, int32_t L, int32_t i0, int32_t block_m, int32_t block_n,
+                             int32_t* f0, int32_t* f1) {
+  if (check_fields(p) != ATTN_OK || !f0 || !f1 || block_m < 1 || block_n < 1 || i0 < 0) return 0;
+  int a = 0, b = -1;
+  const bool ok = full_key_tiles(host_mask(p, L), i0, block_m, block_n, a, b);
+  *f0 = a;
+  *f1 = b;
+  return ok ? 1 : 0;
+}
+
 }  // extern "C"

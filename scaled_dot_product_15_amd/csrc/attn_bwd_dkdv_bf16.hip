@@ -1,4 +1,4 @@
-// Backward attention (dK, dV), bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
+// Backward attention, dK and dV, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
 // Built without the VGPR-form MFMA option: dK and dV accumulate in AGPRs, which
 // leaves VGPRs free to keep several LDS reads in flight per MFMA chain.
 //
@@ -7,40 +7,44 @@
 // grad_q, grad_k, grad_v out):
 //     dP = dO V^T,  dS = P * (dP - delta),
 //     dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K.
-// Two kernels, both deterministic (no atomics):
-//   dkdv: a workgroup owns BN = 128 keys of one (batch, KV head); each wave
-//         owns 32 keys and keeps dK, dV in registers while the workgroup walks
-//         the G query heads of the group in ascending order and, for each, the
-//         visible query tiles in ascending order; the GQA sum is therefore a
-//         fixed-order register accumulation.
-//   dq:   a workgroup owns BM = 128 query rows of one (batch, query head) and
-//         walks the visible key tiles, keeping dQ in registers.
+// This kernel (deterministic, no atomics): a workgroup owns BN = 128 keys of
+// one (batch, KV head); each wave owns 32 keys and keeps dK, dV in registers
+// while the workgroup walks the G query heads of the group in ascending order
+// and, for each, the visible query steps in ascending order; the GQA sum is
+// therefore a fixed-order register accumulation.  dQ has its own kernel.
 // MFMA operand layouts: a lane of a 32x32 accumulator owns one column and 16
 // rows (acc_row).  Contractions over head dims read 16-byte row pieces of a
 // swizzled row-major LDS tile; contractions over the sequence take the
 // accumulator-side operand straight from registers and the other one with
-// LDS transpose loads from the same tile (tile_tr_operand).  Tiles arrive by
+// LDS transpose loads from the same tile (TrReads).  Tiles arrive by
 // direct memory-to-LDS copies, double buffered, one barrier per step.
 #include <type_traits>
 
 #include "launch.h"
 
-namespace sdpa {
+// Tile parameters (build-time overridable for tuning sweeps).
+#ifndef SDPA_DKDV_BMQ
+#define SDPA_DKDV_BMQ 64
+#endif
+#ifndef SDPA_DKDV_NQB
+#define SDPA_DKDV_NQB 1
+#endif
 
-// ---------------------------------------------------------------- dK, dV ---
+namespace sdpa {
 
 template <int DQK, int DV>
 struct DkdvCfg {
   static constexpr int BN = 128;      // keys per workgroup
-  static constexpr int BMQ = 64;      // queries per step
+  static constexpr int BMQ = SDPA_DKDV_BMQ;  // queries per step
   static constexpr int NT = 256;
   static constexpr int QCH = DQK / 8, OCH = DV / 8;  // 16-byte chunks per row
   static constexpr int QT = BMQ * DQK, OT = BMQ * DV;  // elements per tile
-  static constexpr int STAGE = QT + OT + 2 * BMQ * 2;  // Q, dO, lse2 and delta (f32)
+  static constexpr int LROWS = BMQ < 64 ? 64 : BMQ;    // lse2 / delta entries staged per step
+  static constexpr int STAGE = QT + OT + 2 * LROWS * 2;  // Q, dO, lse2 and delta (f32)
   static constexpr int LDS_ELEMS = 2 * STAGE;
   // 32-query blocks computed together; one at a time keeps registers free
   // for in-flight LDS reads.
-  static constexpr int NQB = 1;
+  static constexpr int NQB = DQK > 128 ? 1 : SDPA_DKDV_NQB;
 };
 
 template <int DQK, int DV>
@@ -51,8 +55,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   auto qtile = [&](int buf) { return lds + buf * C::STAGE; };
   auto otile = [&](int buf) { return lds + buf * C::STAGE + C::QT; };
   auto lse_s = [&](int buf) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT); };
-  auto delta_s = [&](int buf) { return lse_s(buf) + C::BMQ; };
+  auto delta_s = [&](int buf) { return lse_s(buf) + C::LROWS; };
 
+  // The wave index is left as a per-lane value here: treated as uniform,
+  // it turns the per-block class checks below into scalar branches, and the
+  // compiler then keeps far more values live (and spills for 192-dim heads).
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Workgroup id -> (key tile, batch, kv head): consecutive ids cover all
   // (batch, kv head) of one key tile, so with B*Hkv a multiple of 8 a given
@@ -100,20 +107,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* dOg = static_cast<const uint16_t*>(a.d_o);
   const size_t qstride = (size_t)a.Hq * DQK, ostride = (size_t)a.Hq * DV;
-  typedef __attribute__((address_space(3))) void lds_void;
+  const TileCopy<C::BMQ, C::QCH, C::NT> qcopy(tid, (uint32_t)(qstride * 2));
+  const TileCopy<C::BMQ, C::OCH, C::NT> ocopy(tid, (uint32_t)(ostride * 2));
+  const RowReads<C::QCH> qrd(lane);
+  const RowReads<C::OCH> ord(lane);
+  const TrReads<C::QCH> qtr(lane);
+  const TrReads<C::OCH> otr(lane);
   auto issue_step = [&](int t, int buf) {
     const int h = g * a.G + t / nsteps;
     const int q0 = (qs0 + t % nsteps) * C::BMQ;
-    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(Qg + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(m.L * qstride * 2));
-    const __amdgpu_buffer_rsrc_t ores = buf_rsrc(dOg + ((size_t)b * a.S * a.Hq + h) * DV, (uint32_t)(m.L * ostride * 2));
-    tile_dma<C::BMQ, C::QCH, C::NT>(qres, (uint32_t)(qstride * 2), q0, qtile(buf), tid);
-    tile_dma<C::BMQ, C::OCH, C::NT>(ores, (uint32_t)(ostride * 2), q0, otile(buf), tid);
-    // lse2 and delta rows q0 .. q0+63: one 4-byte copy per lane (waves 0, 1).
-    if (w < 2) {
-      const float* src = (w == 0 ? a.lse2 : a.delta) + ((size_t)b * a.Hq + h) * a.S;
-      const __amdgpu_buffer_rsrc_t res = buf_rsrc(src, (uint32_t)a.S * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(w == 0 ? lse_s(buf) : delta_s(buf)), 4,
-                                               (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+    qcopy.issue(Qg + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
+    ocopy.issue(dOg + ((size_t)b * a.S * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
+    // lse2 and delta rows q0 .. q0+LROWS-1: 64 rows per wave instruction,
+    // one 4-byte copy per lane; rows past S arrive as zeros.
+    constexpr int PARTS = C::LROWS / 64;
+    for (int chunk = w; chunk < 2 * PARTS; chunk += C::NT / 64) {
+      const int arr = chunk / PARTS, part = chunk % PARTS;
+      const float* src = (arr == 0 ? a.lse2 : a.delta) + ((size_t)b * a.Hq + h) * a.S;
+      float* dst = (arr == 0 ? lse_s(buf) : delta_s(buf)) + part * 64;
+      lds_dma4(buf_desc(src, (uint32_t)a.S * 4), lds_addr(dst), (uint32_t)(q0 + part * 64 + lane) * 4);
     }
   };
 
@@ -135,12 +147,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     for (int ks = 0; ks < DQK / 16; ++ks)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
-        s[qb] = mfma32(as_bf16x8(tile_row16<C::QCH>(Qs, (qb0 + qb) * 32 + l32, ks * 2 + hf)), kreg[ks], s[qb]);
+        s[qb] = mfma32(as_bf16x8(qrd.read(Qs, (qb0 + qb) * 32, ks)), kreg[ks], s[qb]);
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
-        dp[qb] = mfma32(as_bf16x8(tile_row16<C::OCH>(Os, (qb0 + qb) * 32 + l32, ks * 2 + hf)), vreg[ks], dp[qb]);
+        dp[qb] = mfma32(as_bf16x8(ord.read(Os, (qb0 + qb) * 32, ks)), vreg[ks], dp[qb]);
     const int lo_r = qlo_k - (q0 + hf * 4), hi_r = qhi_k - (q0 + hf * 4);
     u32x4 pw[2 * NQB], dw[2 * NQB];  // bf16 pairs of P and dS: B operands of the 16-query K-steps
 #pragma unroll
@@ -182,18 +194,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       const int pos0 = qb0 * 32 + kk * 16;
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
-        dv[db] = mfma32(tile_tr_operand<C::OCH>(Os, pos0, db * 32, lane), as_bf16x8(pw[kk]), dv[db]);
+        dv[db] = mfma32(otr.read(Os, pos0, db), as_bf16x8(pw[kk]), dv[db]);
 #pragma unroll
       for (int db = 0; db < DQK / 32; ++db)
-        dk[db] = mfma32(tile_tr_operand<C::QCH>(Qs, pos0, db * 32, lane), as_bf16x8(dw[kk]), dk[db]);
+        dk[db] = mfma32(qtr.read(Qs, pos0, db), as_bf16x8(dw[kk]), dk[db]);
     }
   };
 
-  if (total > 0) issue_step(0, 0);
-  lds_dma_wait();
-  __syncthreads();
-  for (int t = 0; t < total; ++t) {
-    const int q0 = (qs0 + t % nsteps) * C::BMQ, buf = t & 1;
+  // Unrolled by two: each stage's buffer, and so every LDS offset, is a
+  // compile-time constant.
+  auto stage = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int q0 = (qs0 + t % nsteps) * C::BMQ;
     if (t + 1 < total) issue_step(t + 1, buf ^ 1);
 #pragma unroll
     for (int qb0 = 0; qb0 < C::BMQ / 32; qb0 += C::NQB) {
@@ -209,6 +221,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     }
     lds_dma_wait();
     __syncthreads();
+  };
+  if (total > 0) issue_step(0, 0);
+  lds_dma_wait();
+  __syncthreads();
+  for (int t = 0; t < total; t += 2) {
+    stage(t, std::integral_constant<int, 0>{});
+    if (t + 1 < total) stage(t + 1, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
@@ -233,6 +252,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       }
   }
 }
+
+// Explicit instantiations: with only the implicit ones from the launchers
+// below, the host pass of this compiler drops the launch stub of the last
+// kernel instantiated in the file.
+template __global__ void bwd_dkdv_bf16_kernel<64, 64>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {

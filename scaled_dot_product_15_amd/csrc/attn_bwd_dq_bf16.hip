@@ -1,27 +1,31 @@
-// Backward attention (dQ), bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
+// Backward attention, dQ, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
 //
 // With P = exp(scale * Q K^T - LSE) recomputed from the forward's LSE and
 // delta_i = rowsum(dO * O) from the pre-pass (PR #2225 backward: dz = dO in,
 // grad_q, grad_k, grad_v out):
 //     dP = dO V^T,  dS = P * (dP - delta),
 //     dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K.
-// Two kernels, both deterministic (no atomics):
-//   dkdv: a workgroup owns BN = 128 keys of one (batch, KV head); each wave
-//         owns 32 keys and keeps dK, dV in registers while the workgroup walks
-//         the G query heads of the group in ascending order and, for each, the
-//         visible query tiles in ascending order; the GQA sum is therefore a
-//         fixed-order register accumulation.
-//   dq:   a workgroup owns BM = 128 query rows of one (batch, query head) and
-//         walks the visible key tiles, keeping dQ in registers.
+// This kernel (deterministic, no atomics): a workgroup owns BM = 128 query
+// rows of one (batch, query head) and walks the visible key tiles, keeping dQ
+// in registers; it recomputes S and dP instead of sharing them with the dK/dV
+// kernel, which would need atomics on dQ.
 // MFMA operand layouts: a lane of a 32x32 accumulator owns one column and 16
 // rows (acc_row).  Contractions over head dims read 16-byte row pieces of a
 // swizzled row-major LDS tile; contractions over the sequence take the
 // accumulator-side operand straight from registers and the other one with
-// LDS transpose loads from the same tile (tile_tr_operand).  Tiles arrive by
+// LDS transpose loads from the same tile (TrReads).  Tiles arrive by
 // direct memory-to-LDS copies, double buffered, one barrier per step.
 #include <type_traits>
 
 #include "launch.h"
+
+// Tile parameters (build-time overridable for tuning sweeps).
+#ifndef SDPA_DQ_BN
+#define SDPA_DQ_BN 64
+#endif
+#ifndef SDPA_DQ_WAVES
+#define SDPA_DQ_WAVES 4
+#endif
 
 namespace sdpa {
 
@@ -29,22 +33,22 @@ namespace sdpa {
 
 template <int DQK, int DV>
 struct DqCfg {
-  static constexpr int BM = 128;      // query rows per workgroup
-  static constexpr int BN = 64;       // keys per step
-  static constexpr int NT = 256;
+  static constexpr int BM = 32 * SDPA_DQ_WAVES;  // query rows per workgroup (32 per wave)
+  static constexpr int BN = SDPA_DQ_BN;  // keys per step
+  static constexpr int NT = 64 * SDPA_DQ_WAVES;
   static constexpr int KCH = DQK / 8, VCH = DV / 8;
   static constexpr int KT = BN * DQK, VT = BN * DV;
   static constexpr int LDS_ELEMS = 2 * (KT + VT);
 };
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArgs a) {
   using C = DqCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
   auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Same tile order as the forward: heavy query tiles first, the heads of a
   // GQA group on consecutive ids kept on one XCD.
   int b, h, qt;
@@ -97,11 +101,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
   const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
-  const __amdgpu_buffer_rsrc_t kres = buf_rsrc(Kg, (uint32_t)(m.L * kstride * 2));
-  const __amdgpu_buffer_rsrc_t vres = buf_rsrc(Vg, (uint32_t)(m.L * vstride * 2));
+  const TileCopy<C::BN, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
+  const TileCopy<C::BN, C::VCH, C::NT> vcopy(tid, (uint32_t)(vstride * 2));
+  const RowReads<C::KCH> krd(lane);
+  const RowReads<C::VCH> vrd(lane);
+  const TrReads<C::KCH> ktr(lane);
   auto issue_tile = [&](int j0, int buf) {
-    tile_dma<C::BN, C::KCH, C::NT>(kres, (uint32_t)(kstride * 2), j0, ktile(buf), tid);
-    tile_dma<C::BN, C::VCH, C::NT>(vres, (uint32_t)(vstride * 2), j0, vtile(buf), tid);
+    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
+    vcopy.issue(Vg, (uint32_t)(vstride * 2), j0, m.L, vtile(buf));
   };
 
   auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) {
@@ -109,16 +116,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
     f32x16 st[C::BN / 32], dpt[C::BN / 32];
 #pragma unroll
     for (int kb = 0; kb < C::BN / 32; ++kb) { st[kb] = f32x16{}; dpt[kb] = f32x16{}; }
+    prio_mfma();
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
-        st[kb] = mfma32(as_bf16x8(tile_row16<C::KCH>(Ks, kb * 32 + l32, ks * 2 + hf)), qreg[ks], st[kb]);
+        st[kb] = mfma32(as_bf16x8(krd.read(Ks, kb * 32, ks)), qreg[ks], st[kb]);
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
-        dpt[kb] = mfma32(as_bf16x8(tile_row16<C::VCH>(Vs, kb * 32 + l32, ks * 2 + hf)), oreg[ks], dpt[kb]);
+        dpt[kb] = mfma32(as_bf16x8(vrd.read(Vs, kb * 32, ks)), oreg[ks], dpt[kb]);
+    prio_valu();
     // Element i of block kb: key j0 + hf*4 + kb*32 + acc_row(i, 0), query qi.
     const int base = j0 + hf * 4;
     const int lo_r = klo - base, hi_r = khi - base;
@@ -146,24 +155,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
         dsb[kb * 2 + half] = as_bf16x8(t);
       }
     // dQ^T (dims x queries) += K^T dS^T
+    prio_mfma();
 #pragma unroll
     for (int kk = 0; kk < C::BN / 16; ++kk)
 #pragma unroll
       for (int db = 0; db < DQK / 32; ++db)
-        dq[db] = mfma32(tile_tr_operand<C::KCH>(Ks, kk * 16, db * 32, lane), dsb[kk], dq[db]);
+        dq[db] = mfma32(ktr.read(Ks, kk * 16, db), dsb[kk], dq[db]);
+    prio_valu();
   };
 
+  // Same walk as the forward: tiles in pairs (buffers 0, 1, so every LDS
+  // offset is a compile-time constant); key tiles every row of the
+  // workgroup sees in full run unmasked, the rest masked with per-wave
+  // skipping, each in a loop of its own so the dQ accumulators stay in
+  // place.
+  int fa = kt0, fb = kt0;  // unmasked tiles [fa, fb); fa - kt0, fb - fa even
+  {
+    int f0, f1;
+    if (kt0 <= kt1 && full_key_tiles(m, i0, C::BM, C::BN, f0, f1)) {
+      if (f0 < kt0) f0 = kt0;
+      if (f1 > kt1) f1 = kt1;
+      const int first = kt0 + ((f0 - kt0 + 1) & ~1);
+      const int n = (f1 + 1 - first) & ~1;
+      if (n > 0) {
+        fa = first;
+        fb = first + n;
+      }
+    }
+  }
+  auto step = [&](int kt, auto bufc, auto masked) {
+    constexpr int buf = decltype(bufc)::value;
+    const int j0 = kt * C::BN;
+    if (kt < kt1) issue_tile(j0 + C::BN, buf ^ 1);
+    if constexpr (decltype(masked)::value) {
+      if (tile_class(m, qw0, 32, j0, C::BN) != TILE_SKIP) tile(j0, ktile(buf), vtile(buf), std::true_type{});
+    } else {
+      tile(j0, ktile(buf), vtile(buf), std::false_type{});
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   if (kt0 <= kt1) issue_tile(kt0 * C::BN, 0);
   lds_dma_wait();
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int j0 = kt * C::BN, buf = (kt - kt0) & 1;
-    if (kt < kt1) issue_tile(j0 + C::BN, buf ^ 1);
-    const int cls = tile_class(m, qw0, 32, j0, C::BN);
-    if (cls == TILE_FULL) tile(j0, ktile(buf), vtile(buf), std::false_type{});
-    else if (cls == TILE_PARTIAL) tile(j0, ktile(buf), vtile(buf), std::true_type{});
-    lds_dma_wait();
-    __syncthreads();
+  for (int kt = kt0; kt < fa; kt += 2) {
+    step(kt, B0{}, std::true_type{});
+    step(kt + 1, B1{}, std::true_type{});
+  }
+  for (int kt = fa; kt < fb; kt += 2) {
+    step(kt, B0{}, std::false_type{});
+    step(kt + 1, B1{}, std::false_type{});
+  }
+  for (int kt = fb; kt <= kt1; kt += 2) {
+    step(kt, B0{}, std::true_type{});
+    if (kt + 1 <= kt1) step(kt + 1, B1{}, std::true_type{});
   }
 
   if (qi < a.S) {
@@ -178,6 +225,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(KArgs a) {
       }
   }
 }
+
+// Explicit instantiations: with only the implicit ones from the launchers
+// below, the host pass of this compiler drops the launch stub of the last
+// kernel instantiated in the file.
+template __global__ void bwd_dq_bf16_kernel<64, 64>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<192, 128>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dq_cfg(KArgs a, hipStream_t stream) {

@@ -86,16 +86,6 @@ __device__ __forceinline__ float halves_sum(float x) {
 // MFMA accumulator held by a lane in half hf (= lane / 32).
 __device__ __forceinline__ int acc_row(int i, int hf) { return (i >> 2) * 8 + hf * 4 + (i & 3); }
 
-// Position, inside a 16-wide step, where the operand that pairs with
-// accumulator-derived values stores physical offset r: the accumulator of
-// half hf holds rows {0-3, 8-11} (hf=0) or {4-7, 12-15} (hf=1) of each 16,
-// so groups of four rows 1 and 2 trade places.
-__device__ __forceinline__ int perm16(int r) {
-  const int g = (r >> 2) & 3;
-  const int pg = (g == 1) ? 2 : (g == 2 ? 1 : g);
-  return (r & ~15) + pg * 4 + (r & 3);
-}
-
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Raw buffer resource over [base, base + bytes): loads at or past the end
@@ -109,26 +99,6 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// A operand (rows = head dims, reduction = sequence positions) of a 32x32x16
-// MFMA, read with two LDS transpose loads from a row-major [position][dim]
-// bf16 tile.  Within each 16-lane group the transpose load treats the 8-byte
-// chunks of lanes 4s..4s+3 as row s of a 4x16 matrix and hands lane c
-// its column c.  Lane l (group G = l/16, half hf = G/2) therefore addresses
-// position pos0 + hf*4 + s at dims d0 + (G%2)*16 + 4q (s = (l/4)%4, q = l%4)
-// and receives dim d0 + l%32 of positions pos0 + hf*4 + {0..3}; the second
-// load adds 8 positions.  Those are exactly the rows acc_row(e, hf), e = 0..7,
-// that a lane of a 32x32 accumulator holds for the same 16 positions, so the
-// B operand can come straight from accumulator registers.
-__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int pitch, int pos0, int d0, int lane) {
-  const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
-  const uint16_t* p = tile + (pos0 + (G >> 1) * 4 + s) * pitch + d0 + (G & 1) * 16 + q * 4;
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * pitch));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
 
 // ---- swizzled row-major bf16 tiles in LDS ---------------------------------
 //
@@ -152,52 +122,163 @@ __device__ __forceinline__ int swz(int r) {
 template <int CH>
 __device__ __forceinline__ int swz_off(int r, int c) { return (r * CH + (c ^ swz<CH>(r))) * 16; }
 
-// 16-byte row read of logical chunk c of row r.
-template <int CH>
-__device__ __forceinline__ u32x4 tile_row16(const uint16_t* tile, int r, int c) {
-  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) + swz_off<CH>(r, c));
+// Wave index within the workgroup, marked wave-uniform so that everything
+// derived from it (row offsets, mask tile classes, LDS destinations) stays in
+// scalar registers.
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
+// ---- direct memory -> LDS copies -------------------------------------------
+//
+// buffer_load ... lds writes lane l's dwords to LDS address M0 + size * l
+// without touching registers.  The copies are issued from inline assembly:
+// the compiler then does not track them, and so does not put a wait for all
+// outstanding copies in front of every LDS transpose load (it cannot tell
+// that those read the other buffer).  Completion is therefore the caller's
+// job: lds_dma_wait() and a workgroup barrier before any wave reads the
+// destination.  The resource is a raw buffer over [base, base + bytes):
+// lanes whose offset reaches past the end receive zeros.
+struct BufDesc {
+  u32x4 w;  // base lo, base hi (stride 0), byte count, raw 32-bit format
+};
+__device__ __forceinline__ BufDesc buf_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return BufDesc{u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u}};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_char*)p);
+}
+// The resource and the LDS address are wave-uniform by construction;
+// readfirstlane states it, so they are always in scalar registers as the
+// instruction requires (it folds away where the compiler already knows).
+__device__ __forceinline__ u32x4 uniform4(u32x4 v) {
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[1]),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)v[2]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[3])};
+}
+// M0 is written here and nowhere else in these kernels; the hardware needs
+// one wait state between the M0 write and the copy that reads it.
+__device__ __forceinline__ void lds_dma16(const BufDesc& d, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_dst)), "v"(voff), "s"(uniform4(d.w))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const BufDesc& d, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_dst)), "v"(voff), "s"(uniform4(d.w))
+               : "memory", "m0");
 }
 
-// lds_tr_operand for a swizzled tile (dims d0 .. d0+31, positions pos0 .. pos0+15).
-template <int CH>
-__device__ __forceinline__ bf16x8 tile_tr_operand(const uint16_t* tile, int pos0, int d0, int lane) {
-  const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
-  const int row = pos0 + (G >> 1) * 4 + s;
-  const int dim = d0 + (G & 1) * 16 + q * 4;
-  const char* base = reinterpret_cast<const char*>(tile) + (dim & 7) * 2;
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<CH>(row, dim >> 3)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<CH>(row + 8, dim >> 3)));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their no-wait maxima),
+// issued through the builtin so the compiler sees it and counts every
+// earlier memory load of its own as complete from here on.
+__device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Asynchronous copy of rows [row0, row0 + R) of a row-major bf16 tensor
-// (rows `stride_bytes` apart, starting at the buffer resource's base) into a
-// swizzled LDS tile, straight from memory to LDS (no registers).  Each
-// instruction moves 64 consecutive physical chunks: lane l of the wave fills
-// physical chunk idx = base + l, i.e. row idx / CH, logical chunk
-// (idx % CH) ^ swz(row).  Rows past the resource's end arrive as zeros.
-// Complete with lds_dma_wait() and a workgroup barrier before reading.
-template <int R, int CH, int NT>
-__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t res, uint32_t stride_bytes, int row0,
-                                         uint16_t* tile, int tid) {
-  static_assert((R * CH) % (NT) == 0, "tile must split into whole wave instructions");
-  constexpr int PER_WAVE = R * CH / NT;  // instructions per wave
-  const int w = tid >> 6, lane = tid & 63;
-  typedef __attribute__((address_space(3))) void lds_void;
+// ---- reads of swizzled tiles -----------------------------------------------
+//
+// Loop-invariant per-lane byte offsets, so each LDS read in a hot loop is
+// "lane offset + immediate" with no address arithmetic.  swz depends on the
+// row modulo 16 only, so offsets computed for the first rows hold for every
+// row block that starts on a multiple of 16; only the immediate changes.
+
+// 16-byte row reads (B or A operand of a contraction over head dims): lane l
+// reads row rb + l%32, logical chunk 2*ks + l/32, i.e. dims [16 ks + 8 (l/32), +8).
+template <int CH>
+struct RowReads {
+  uint32_t off[CH / 2];
+  __device__ __forceinline__ explicit RowReads(int lane) {
+    const int r = lane & 31, hf = lane >> 5;
 #pragma unroll
-  for (int k = 0; k < PER_WAVE; ++k) {
-    const int base = (w * PER_WAVE + k) * 64;
-    const int idx = base + lane;
-    const int row = idx / CH, c = (idx % CH) ^ swz<CH>(row);
-    const uint32_t voff = (uint32_t)(row0 + row) * stride_bytes + (uint32_t)c * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)(reinterpret_cast<char*>(tile) + base * 16), 16, voff,
-                                             0, 0, 0);
+    for (int ks = 0; ks < CH / 2; ++ks) off[ks] = (uint32_t)(r * CH + ((2 * ks + hf) ^ swz<CH>(r))) * 16;
   }
-}
+  // rb: first row of the 32-row block (a multiple of 32).
+  __device__ __forceinline__ u32x4 read(const uint16_t* tile, int rb, int ks) const {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) + rb * CH * 16 + off[ks]);
+  }
+};
 
-__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A operand (rows = head dims, reduction = sequence positions) of a 32x32x16
+// MFMA, read with two LDS transpose loads from a row-major [position][dim]
+// tile.  Within each 16-lane group the transpose load treats the 8-byte
+// chunks of lanes 4s..4s+3 as row s of a 4x16 matrix and hands lane c its
+// column c.  Lane l (group G = l/16, half hf = G/2) therefore addresses
+// position pos0 + hf*4 + s at dims d0 + (G%2)*16 + 4q (s = (l/4)%4, q = l%4)
+// and receives dim d0 + l%32 of positions pos0 + hf*4 + {0..3}; the second
+// load adds 8 positions.  Those are exactly the rows acc_row(e, hf), e = 0..7,
+// that a lane of a 32x32 accumulator holds for the same 16 positions, so the
+// B operand can come straight from accumulator registers.  db selects the
+// 32-dim block d0 = 32 db.
+template <int CH>
+struct TrReads {
+  static constexpr int NDB = CH / 4;
+  uint32_t off[2][NDB];
+  __device__ __forceinline__ explicit TrReads(int lane) {
+    const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int row = (G >> 1) * 4 + s + 8 * h, dim = db * 32 + (G & 1) * 16 + q * 4;
+        off[h][db] = (uint32_t)(swz_off<CH>(row, dim >> 3) + (dim & 7) * 2);
+      }
+  }
+  // pos0: first of the 16 positions (a multiple of 16).
+  __device__ __forceinline__ bf16x8 read(const uint16_t* tile, int pos0, int db) const {
+    const char* t = reinterpret_cast<const char*>(tile) + pos0 * CH * 16;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off[0][db]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off[1][db]));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+  }
+};
+
+// Copy of rows [row0, row0 + R) of a row-major bf16 tensor (rows
+// stride_bytes apart) into a swizzled LDS tile.  Each wave instruction moves
+// 64 consecutive physical chunks: lane l fills physical chunk idx = base + l,
+// i.e. row idx / CH, logical chunk (idx % CH) ^ swz(row).  The resource of
+// each copy starts at row0 and ends at the valid length, so the per-lane
+// source offsets never change and rows past the end arrive as zeros.
+template <int R, int CH, int NT>
+struct TileCopy {
+  static_assert((R * CH) % NT == 0, "tile must split into whole wave instructions");
+  static constexpr int PER_WAVE = R * CH / NT;
+  uint32_t voff[PER_WAVE];
+  int chunk0;  // first physical chunk this wave fills
+  __device__ __forceinline__ TileCopy(int tid, uint32_t stride_bytes) {
+    const int w = wave_id(tid), lane = tid & 63;
+    chunk0 = w * PER_WAVE * 64;
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int idx = chunk0 + k * 64 + lane;
+      const int row = idx / CH, c = (idx % CH) ^ swz<CH>(row);
+      voff[k] = (uint32_t)row * stride_bytes + (uint32_t)c * 16;
+    }
+  }
+  // Rows past valid_rows arrive as zeros.
+  __device__ __forceinline__ void issue(const void* base, uint32_t stride_bytes, int row0, int valid_rows,
+                                        uint16_t* tile) const {
+    const int left = valid_rows - row0;
+    const BufDesc d = buf_desc(reinterpret_cast<const char*>(base) + (size_t)row0 * stride_bytes,
+                               left > 0 ? (uint32_t)left * stride_bytes : 0u);
+    const uint32_t dst = lds_addr(tile) + (uint32_t)chunk0 * 16;
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) lds_dma16(d, dst + k * 64 * 16, voff[k]);
+  }
+};
+
+// Wave priority around MFMA-heavy sections: a wave issuing matrix work runs
+// ahead of the co-resident wave, whose VALU work then fills the gaps.
+#ifndef SDPA_PRIO
+#define SDPA_PRIO 1
+#endif
+__device__ __forceinline__ void prio_mfma() {
+  if constexpr (SDPA_PRIO) __builtin_amdgcn_s_setprio(1);
+}
+__device__ __forceinline__ void prio_valu() {
+  if constexpr (SDPA_PRIO) __builtin_amdgcn_s_setprio(0);
+}
 
 // Keys visible from query row qi, as an inclusive interval [lo, hi]
 // (empty when lo > hi).  Same rule as visible(): row qi < L sees keys

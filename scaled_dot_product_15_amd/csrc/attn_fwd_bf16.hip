@@ -18,7 +18,7 @@
 //   single cross-lane step (lane <-> lane^32).
 //   O^T (dims x queries) += V^T P^T with B = P^T taken straight from the S^T
 //   accumulator registers (after exp and bf16 rounding) and A = V^T read with
-//   LDS transpose loads from the row-major V tile (lds_tr_operand).
+//   LDS transpose loads from the row-major V tile (TrReads).
 // K and V tiles are staged global -> registers -> LDS as plain row copies;
 // the next tile's global loads are in flight while the current one computes.
 //
@@ -33,12 +33,20 @@
 #include "attn_common.h"
 #include "launch.h"
 
+// Tile parameters (build-time overridable for tuning sweeps).
+#ifndef SDPA_FWD_BN
+#define SDPA_FWD_BN 64
+#endif
+#ifndef SDPA_FWD_WAVES
+#define SDPA_FWD_WAVES 4
+#endif
+
 namespace sdpa {
 
 template <int DQK, int DV, int BN>
 struct FwdBf16Cfg {
-  static constexpr int BM = 128;
-  static constexpr int NT = 256;
+  static constexpr int BM = 32 * SDPA_FWD_WAVES;  // query rows per workgroup (32 per wave)
+  static constexpr int NT = 64 * SDPA_FWD_WAVES;
   static constexpr int KCH = DQK / 8;   // 16-byte chunks per K row
   static constexpr int VCH = DV / 8;
   static constexpr int KT = BN * DQK;   // elements of one K tile
@@ -69,11 +77,11 @@ __device__ __forceinline__ void fwd_tile_of(const KArgs& a, int bid, int& b, int
 }
 
 template <int DQK, int DV, int BN, int OCC>
-__global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
   fwd_tile_of(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
@@ -89,9 +97,10 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
   const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
 
-  // Buffer resources end at the valid length: rows >= L read as zeros.
-  const __amdgpu_buffer_rsrc_t kres = buf_rsrc(Kg, (uint32_t)(m.L * kstride * 2));
-  const __amdgpu_buffer_rsrc_t vres = buf_rsrc(Vg, (uint32_t)(m.L * vstride * 2));
+  const TileCopy<BN, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
+  const TileCopy<BN, C::VCH, C::NT> vcopy(tid, (uint32_t)(vstride * 2));
+  const RowReads<C::KCH> krd(lane);
+  const TrReads<C::VCH> vrd(lane);
 
   // Q^T operand: lane holds query qi, dims [ks*16 + hf*8, +8).
   bf16x8 qreg[DQK / 16];
@@ -121,8 +130,8 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
   auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
   auto issue_tile = [&](int j0, int buf) {
-    tile_dma<BN, C::KCH, C::NT>(kres, (uint32_t)(kstride * 2), j0, ktile(buf), tid);
-    tile_dma<BN, C::VCH, C::NT>(vres, (uint32_t)(vstride * 2), j0, vtile(buf), tid);
+    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
+    vcopy.issue(Vg, (uint32_t)(vstride * 2), j0, m.L, vtile(buf));
   };
 
   // One key tile for this wave.  MASKED selects the per-element predicate:
@@ -132,14 +141,16 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+    prio_mfma();
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8 ka = as_bf16x8(tile_row16<C::KCH>(Ks, kb * 32 + l32, ks * 2 + hf));
+        const bf16x8 ka = as_bf16x8(krd.read(Ks, kb * 32, ks));
         s[kb] = mfma32(ka, qreg[ks], s[kb]);
       }
     }
+    prio_valu();
     float mx = -__builtin_inff();
     if constexpr (MASKED) {
       const int base = j0 + hf * 4;
@@ -158,12 +169,12 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = halves_max(mx) * c;
     const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run + 8.0f)) {
-      const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
+    const bool rescale = __any(m_new > m_run + 8.0f);
+    float alpha = 1.0f;
+    if (rescale) {
+      alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
     }
     const float nmu = (m_run == -__builtin_inff()) ? 0.0f : -m_run;
     float ls = 0.0f;
@@ -184,30 +195,75 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
       }
     }
     l_run += ls;
+    if (__builtin_expect(rescale, 0)) {
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
+    }
+    prio_mfma();
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) {
-        const bf16x8 va = tile_tr_operand<C::VCH>(Vs, kk * 16, db * 32, lane);
+        const bf16x8 va = vrd.read(Vs, kk * 16, db);
         o[db] = mfma32(va, pb[kk], o[db]);
       }
     }
+    prio_valu();
   };
 
   // Double-buffered pipeline, one barrier per tile: the copy of tile kt+1
   // runs while tile kt computes; the barrier after the wait both publishes
-  // tile kt+1 and frees tile kt's buffer for the copy after it.
+  // tile kt+1 and frees tile kt's buffer for the copy after it.  Tiles go in
+  // pairs (buffers 0, 1), so every LDS offset is a compile-time constant.
+  //
+  // Key tiles that every row of the workgroup sees in full run unmasked; the
+  // rest (window start, diagonal, padding) run masked, each wave skipping the
+  // tiles its own rows cannot see.  The unmasked range is trimmed to whole
+  // pairs, and each of the three loops has a single code path: choosing the
+  // masked or unmasked body per tile inside one loop made the compiler copy
+  // the O accumulators on every tile.
+  int fa = kt0, fb = kt0;  // unmasked tiles [fa, fb); fa - kt0, fb - fa even
+  {
+    int f0, f1;
+    if (kt0 <= kt1 && full_key_tiles(m, i0, C::BM, BN, f0, f1)) {
+      if (f0 < kt0) f0 = kt0;
+      if (f1 > kt1) f1 = kt1;
+      const int first = kt0 + ((f0 - kt0 + 1) & ~1);
+      const int n = (f1 + 1 - first) & ~1;
+      if (n > 0) {
+        fa = first;
+        fb = first + n;
+      }
+    }
+  }
+  auto step = [&](int kt, auto bufc, auto masked) {
+    constexpr int buf = decltype(bufc)::value;
+    const int j0 = kt * BN;
+    if (kt < kt1) issue_tile(j0 + BN, buf ^ 1);
+    if constexpr (decltype(masked)::value) {
+      if (tile_class(m, row_w0, 32, j0, BN) != TILE_SKIP) tile(j0, ktile(buf), vtile(buf), std::true_type{});
+    } else {
+      tile(j0, ktile(buf), vtile(buf), std::false_type{});
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   if (kt0 <= kt1) issue_tile(kt0 * BN, 0);
   lds_dma_wait();
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int j0 = kt * BN, buf = (kt - kt0) & 1;
-    if (kt < kt1) issue_tile(j0 + BN, buf ^ 1);
-    const int cls = tile_class(m, row_w0, 32, j0, BN);
-    if (cls == TILE_FULL) tile(j0, ktile(buf), vtile(buf), std::false_type{});
-    else if (cls == TILE_PARTIAL) tile(j0, ktile(buf), vtile(buf), std::true_type{});
-    lds_dma_wait();
-    __syncthreads();
+  for (int kt = kt0; kt < fa; kt += 2) {
+    step(kt, B0{}, std::true_type{});
+    step(kt + 1, B1{}, std::true_type{});
+  }
+  for (int kt = fa; kt < fb; kt += 2) {
+    step(kt, B0{}, std::false_type{});
+    step(kt + 1, B1{}, std::false_type{});
+  }
+  for (int kt = fb; kt <= kt1; kt += 2) {
+    step(kt, B0{}, std::true_type{});
+    if (kt + 1 <= kt1) step(kt + 1, B1{}, std::true_type{});
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
@@ -231,6 +287,18 @@ __global__ __launch_bounds__(256, OCC) void fwd_bf16_kernel(KArgs a) {
   }
 }
 
+// Occupancy (workgroups per CU) each head-dim configuration is built for.
+constexpr int kFwdOcc64 = SDPA_FWD_WAVES > 4 ? 1 : 2;
+constexpr int kFwdOcc128 = (SDPA_FWD_BN > 64 || SDPA_FWD_WAVES > 4) ? 1 : 2;
+constexpr int kFwdOcc192 = 1;
+
+// Explicit instantiations: with only the implicit ones from the launchers
+// below, the host pass of this compiler drops the launch stub of the last
+// kernel instantiated in the file.
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128>(KArgs);
+template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192>(KArgs);
+
 template <int DQK, int DV, int BN, int OCC>
 static hipError_t launch_fwd_cfg(KArgs a, hipStream_t stream) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
@@ -241,16 +309,19 @@ static hipError_t launch_fwd_cfg(KArgs a, hipStream_t stream) {
 }
 
 bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn) {
-  if (dqk == 64 && dv == 64) { *bm = 128; *bn = 64; return true; }
-  if (dqk == 128 && dv == 128) { *bm = 128; *bn = 64; return true; }
-  if (dqk == 192 && dv == 128) { *bm = 128; *bn = 64; return true; }
-  return false;
+  const bool ok = (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+  if (ok) {
+    *bm = 32 * SDPA_FWD_WAVES;
+    *bn = SDPA_FWD_BN;
+  }
+  return ok;
 }
 
 hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
-  if (dqk == 64 && dv == 64) return launch_fwd_cfg<64, 64, 64, 2>(a, stream);
-  if (dqk == 128 && dv == 128) return launch_fwd_cfg<128, 128, 64, 2>(a, stream);
-  if (dqk == 192 && dv == 128) return launch_fwd_cfg<192, 128, 64, 1>(a, stream);
+  constexpr int BN = SDPA_FWD_BN;
+  if (dqk == 64 && dv == 64) return launch_fwd_cfg<64, 64, BN, kFwdOcc64>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_fwd_cfg<128, 128, BN, kFwdOcc128>(a, stream);
+  if (dqk == 192 && dv == 128) return launch_fwd_cfg<192, 128, BN, kFwdOcc192>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -88,4 +88,21 @@ ME_HD int tile_class(const MaskSpec& m, int i0, int bm, int j0, int bn) {
   return full ? TILE_FULL : TILE_PARTIAL;
 }
 
+// Key tiles f0 .. f1 (tile t holds keys t*bn .. t*bn+bn-1) that every row of
+// [i0, i0+bm) sees in full, i.e. the tiles tile_class calls FULL for that row
+// block; false when there are none.  Rows see keys from max(0, row-wl) to
+// min(L-1, row [causal], row+wr); both bounds grow with the row, so the keys
+// all rows see run from the last row's lower bound to the first row's upper.
+ME_HD bool full_key_tiles(const MaskSpec& m, int i0, int bm, int bn, int& f0, int& f1) {
+  const int i1 = i0 + bm - 1;
+  if (i1 >= m.L) return false;
+  int jlo = 0, jhi = m.L - 1;
+  if (m.wl >= 0 && i1 - m.wl > jlo) jlo = i1 - m.wl;
+  if (m.causal && i0 < jhi) jhi = i0;
+  if (m.wr >= 0 && i0 + m.wr < jhi) jhi = i0 + m.wr;
+  f0 = (jlo + bn - 1) / bn;
+  f1 = (jhi + 1) / bn - 1;
+  return f0 <= f1;
+}
+
 }  // namespace sdpa

@@ -184,6 +184,30 @@ def test_host_ranges_match_oracle_mask(causal, wl, wr):
                 assert qr == (idx[0], idx[-1]) and cols[idx[0]:idx[-1] + 1].all()
 
 
+@pytest.mark.parametrize("causal,wl,wr", MASK_GRID[::2])
+def test_host_full_key_tiles_match_oracle_mask(causal, wl, wr):
+    S = 203
+    p = P(B=1, S=S, attn_mask_type="causal" if causal else "no_mask", window_size=(wl, wr))
+    for L in (0, 1, 97, 203):
+        M = oracle.visible_mask(S, L, causal, wl, wr)
+        for bm, bn in ((128, 64), (32, 64), (64, 32), (16, 48)):
+            nkt = -(-S // bn)
+            for i0 in range(0, S, bm // 2):
+                full = []
+                for t in range(nkt):
+                    blk = np.zeros((bm, bn), dtype=bool)
+                    sub = M[i0:i0 + bm, t * bn:(t + 1) * bn]
+                    blk[:sub.shape[0], :sub.shape[1]] = sub
+                    if blk.all():
+                        full.append(t)
+                got = binding.host_full_key_tiles(p, L, i0, bm, bn)
+                if not full:
+                    assert got is None, (L, bm, bn, i0, got)
+                else:
+                    assert full == list(range(full[0], full[-1] + 1))
+                    assert got == (full[0], full[-1]), (L, bm, bn, i0, got)
+
+
 def test_fwd_tile_shape():
     assert binding.fwd_tile_shape(P()) == (128, 64)
     assert binding.fwd_tile_shape(P(d_qk=64, d_v=64, dtype="f32")) == (64, 64)
