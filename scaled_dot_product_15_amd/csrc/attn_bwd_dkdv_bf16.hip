@@ -1,6 +1,6 @@
 // Backward attention, dK and dV, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
-// Built without the VGPR-form MFMA option: dK and dV accumulate in AGPRs, which
-// leaves VGPRs free to keep several LDS reads in flight per MFMA chain.
+// Built without the VGPR-form MFMA option: dK and dV (and the S / dP blocks in
+// flight) accumulate in AGPRs, leaving the VGPRs for operands and softmax work.
 //
 // With P = exp(scale * Q K^T - LSE) recomputed from the forward's LSE and
 // delta_i = rowsum(dO * O) from the pre-pass (PR #2225 backward: dz = dO in,
@@ -10,57 +10,77 @@
 // This kernel (deterministic, no atomics): a workgroup owns BN = 128 keys of
 // one (batch, KV head); each wave owns 32 keys and keeps dK, dV in registers
 // while the workgroup walks the G query heads of the group in ascending order
-// and, for each, the visible query steps in ascending order; the GQA sum is
-// therefore a fixed-order register accumulation.  dQ has its own kernel.
+// and, for each, the visible query rows in ascending order, 32 rows (one
+// block) at a time; the GQA sum is therefore a fixed-order register
+// accumulation.  dQ has its own kernel.
+//
+// Software pipeline.  Per block u a wave runs three dependent phases:
+//   A(u): S = Q K^T and dP = dO V^T for its 32 keys          (MFMA)
+//   B(u): P = exp2(S c - lse2), masked; dS = P (dP - delta)   (VALU)
+//   C(u): dV^T += dO^T P,  dK^T += Q^T dS                     (MFMA)
+// Iteration u issues A(u+1), B(u) and C(u-1): three independent groups in
+// one basic block, so the scheduler can fill the MFMA pipe with A and C
+// while B's exp / FMA work issues in between (one wave per SIMD has no other
+// wave to hide its softmax behind).  S/dP and P/dS each alternate between two
+// register sets.
+//
+// Query rows are staged 64 at a time (two blocks) in a ring of three LDS
+// buffers filled by direct memory-to-LDS copies: Q and dO tiles (swizzled
+// rows) plus the rows' lse2 and delta.  Iteration u touches the stages of
+// blocks u-1, u, u+1, so the copy of stage s+1 is issued after the barrier
+// that opens stage s (at iteration 2s-1), when stage s-2 is no longer read,
+// and has two iterations to land.  The loop is unrolled over the six phases
+// of (block parity, ring slot) so every register set and LDS offset is a
+// compile-time constant.
+//
+// Masks: every wave evaluates the visibility predicate per element (two
+// integer compares against the rows that see its key), on every block.  The
+// workgroup's blocks are computed by all four waves, also where a wave's own
+// keys see none of a block's rows (its P is then zero).
+//
 // MFMA operand layouts: a lane of a 32x32 accumulator owns one column and 16
 // rows (acc_row).  Contractions over head dims read 16-byte row pieces of a
-// swizzled row-major LDS tile; contractions over the sequence take the
-// accumulator-side operand straight from registers and the other one with
-// LDS transpose loads from the same tile (TrReads).  Tiles arrive by
-// direct memory-to-LDS copies, double buffered, one barrier per step.
+// swizzled row-major LDS tile (RowReads); contractions over the sequence take
+// the accumulator-side operand straight from registers and the other one
+// with LDS transpose loads from the same tile (TrReads).
 #include <type_traits>
 
 #include "launch.h"
 
-// Tile parameters (build-time overridable for tuning sweeps).
-#ifndef SDPA_DKDV_BMQ
-#define SDPA_DKDV_BMQ 64
+// Issue pattern inside a pipeline chunk (build-time overridable for tuning
+// sweeps): LDS reads and VALU instructions placed after each MFMA.
+#ifndef SDPA_DKDV_DS
+#define SDPA_DKDV_DS 2
 #endif
-#ifndef SDPA_DKDV_NQB
-#define SDPA_DKDV_NQB 1
+#ifndef SDPA_DKDV_VALU
+#define SDPA_DKDV_VALU 5
 #endif
 
 namespace sdpa {
 
 template <int DQK, int DV>
 struct DkdvCfg {
-  static constexpr int BN = 128;      // keys per workgroup
-  static constexpr int BMQ = SDPA_DKDV_BMQ;  // queries per step
+  static constexpr int BN = 128;  // keys per workgroup (32 per wave)
+  static constexpr int BMQ = 64;  // query rows per stage (two 32-row blocks)
+  static constexpr int NBUF = 3;  // stages resident in LDS
   static constexpr int NT = 256;
-  static constexpr int QCH = DQK / 8, OCH = DV / 8;  // 16-byte chunks per row
+  static constexpr int QCH = DQK / 8, OCH = DV / 8;    // 16-byte chunks per row
   static constexpr int QT = BMQ * DQK, OT = BMQ * DV;  // elements per tile
-  static constexpr int LROWS = BMQ < 64 ? 64 : BMQ;    // lse2 / delta entries staged per step
-  static constexpr int STAGE = QT + OT + 2 * LROWS * 2;  // Q, dO, lse2 and delta (f32)
-  static constexpr int LDS_ELEMS = 2 * STAGE;
-  // 32-query blocks computed together; one at a time keeps registers free
-  // for in-flight LDS reads.
-  static constexpr int NQB = DQK > 128 ? 1 : SDPA_DKDV_NQB;
+  static constexpr int STAGE = QT + OT + 2 * BMQ * 2;  // Q, dO, lse2 and delta (f32)
+  static constexpr int LDS_ELEMS = NBUF * STAGE;
 };
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   using C = DkdvCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  // Stage buffer `buf`: Q [BMQ][DQK], dO [BMQ][DV] (swizzled), lse2 [BMQ], delta [BMQ].
+  // Ring slot `buf`: Q [BMQ][DQK], dO [BMQ][DV] (swizzled), lse2 [BMQ], delta [BMQ].
   auto qtile = [&](int buf) { return lds + buf * C::STAGE; };
   auto otile = [&](int buf) { return lds + buf * C::STAGE + C::QT; };
   auto lse_s = [&](int buf) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT); };
-  auto delta_s = [&](int buf) { return lse_s(buf) + C::LROWS; };
+  auto delta_s = [&](int buf) { return lse_s(buf) + C::BMQ; };
 
-  // The wave index is left as a per-lane value here: treated as uniform,
-  // it turns the per-block class checks below into scalar branches, and the
-  // compiler then keeps far more values live (and spills for 192-dim heads).
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Workgroup id -> (key tile, batch, kv head): consecutive ids cover all
   // (batch, kv head) of one key tile, so with B*Hkv a multiple of 8 a given
   // (batch, kv head) always lands on the same XCD and its Q/dO tiles, read
@@ -71,10 +91,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const int b = r / a.Hkv, g = r % a.Hkv;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int j0 = kt * C::BN;
-  const int kw0 = j0 + w * 32;
-  const int kj = kw0 + l32;
+  const int kj = j0 + w * 32 + l32;
   int qlo_k, qhi_k;  // rows that see this lane's key
   col_query_bounds(m, kj, qlo_k, qhi_k);
+  // Rows that see all 32 keys of this wave: both bounds grow with the key,
+  // so they run from the last key's first row to the first key's last row
+  // (none if the wave holds keys past the valid length).  Blocks of such
+  // rows need no mask.
+  int all_lo, all_hi;
+  {
+    const int kw0 = j0 + w * 32;
+    int lo_a, hi_a, lo_b, hi_b;
+    col_query_bounds(m, kw0 + 31, lo_a, hi_a);
+    col_query_bounds(m, kw0, lo_b, hi_b);
+    all_lo = lo_a;
+    all_hi = hi_b;
+    if (kw0 + 31 >= m.L) { all_lo = 1; all_hi = 0; }
+  }
 
   // K^T / V^T operands: lane holds key kj, dims [ks*16 + hf*8, +8); buffer
   // resources end at the valid length, so keys >= L read as zeros.
@@ -98,11 +131,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < DV / 32; ++i) dv[i] = f32x16{};
 
+  // Stages: (head of the group, 64-row step) pairs in ascending order.
   int qlo = 0, qhi = -1;
   if (!query_range(m, j0, j0 + C::BN - 1, qlo, qhi)) { qlo = 0; qhi = -1; }
   const int qs0 = qlo / C::BMQ;
   const int nsteps = qhi < 0 ? 0 : qhi / C::BMQ - qs0 + 1;
-  const int total = nsteps * a.G;
+  const int T = nsteps * a.G;  // stages
+  const int NB = 2 * T;        // 32-row blocks
+  const int NI = NB > 0 ? (NB + 4) / 6 * 6 : 0;  // pipeline iterations after the first (multiple of 6, >= NB-1)
+  const int TP = ((NI + 1) >> 1) + 1;            // stages touched, the padding ones included
+  // Walk over the stages in order, kept incrementally (no divisions in the
+  // loop): head offset within the group and first row.  Padding stages
+  // start at row S: their copies read nothing and land zeros.
+  struct StageWalk {
+    int t, hh, q0;
+  };
+  const int q_first = qs0 * C::BMQ, q_last = (qs0 + nsteps - 1) * C::BMQ;
+  auto walk_next = [&](StageWalk& st) {
+    ++st.t;
+    st.q0 += C::BMQ;
+    if (st.q0 > q_last) {
+      st.q0 = q_first;
+      ++st.hh;
+    }
+    if (st.t >= T) {
+      st.q0 = a.S;
+      st.hh = 0;
+    }
+  };
 
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* dOg = static_cast<const uint16_t*>(a.d_o);
@@ -113,121 +169,241 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const RowReads<C::OCH> ord(lane);
   const TrReads<C::QCH> qtr(lane);
   const TrReads<C::OCH> otr(lane);
-  auto issue_step = [&](int t, int buf) {
-    const int h = g * a.G + t / nsteps;
-    const int q0 = (qs0 + t % nsteps) * C::BMQ;
+  auto issue_stage = [&](const StageWalk& st, int buf) {
+    const int h = g * a.G + st.hh;
+    const int q0 = st.q0;
     qcopy.issue(Qg + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
     ocopy.issue(dOg + ((size_t)b * a.S * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
-    // lse2 and delta rows q0 .. q0+LROWS-1: 64 rows per wave instruction,
-    // one 4-byte copy per lane; rows past S arrive as zeros.
-    constexpr int PARTS = C::LROWS / 64;
-    for (int chunk = w; chunk < 2 * PARTS; chunk += C::NT / 64) {
-      const int arr = chunk / PARTS, part = chunk % PARTS;
-      const float* src = (arr == 0 ? a.lse2 : a.delta) + ((size_t)b * a.Hq + h) * a.S;
-      float* dst = (arr == 0 ? lse_s(buf) : delta_s(buf)) + part * 64;
-      lds_dma4(buf_desc(src, (uint32_t)a.S * 4), lds_addr(dst), (uint32_t)(q0 + part * 64 + lane) * 4);
+    // lse2 (wave 0) and delta (wave 1) of rows q0 .. q0+63, one 4-byte copy
+    // per lane; rows past S arrive as zeros.
+    if (w < 2) {
+      const float* src = (w == 0 ? a.lse2 : a.delta) + ((size_t)b * a.Hq + h) * a.S;
+      float* dst = w == 0 ? lse_s(buf) : delta_s(buf);
+      lds_dma4(buf_desc(src, (uint32_t)a.S * 4), lds_addr(dst), (uint32_t)(q0 + lane) * 4);
     }
   };
 
-  // NQB consecutive 32-query blocks (from block qb0) of a staged step, for
-  // this wave's 32 keys.  Element i of an S / dP accumulator of block qb:
-  // query q0 + qb*32 + acc_row(i, hf), key kj.  MASKED evaluates the
-  // per-element predicate.
-  auto step = [&](int q0, int qb0, int buf, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    constexpr int NQB = C::NQB;
-    const uint16_t* Qs = qtile(buf);
-    const uint16_t* Os = otile(buf);
-    const float* ls = lse_s(buf);
-    const float* ds_ = delta_s(buf);
-    f32x16 s[NQB], dp[NQB];
+  const float c = a.scale_log2;
+  f32x16 S[2], DP[2];        // S / dP of the block in B and of the one in A
+  u32x4 PW[2][2], DW[2][2];  // bf16 P / dS pairs: B operands of the block's two 16-row K-steps
+
+  // A(u): S and dP of block u (rows rb .. rb+31 of a ring slot).
+  auto phase_a = [&](const uint16_t* Qs, const uint16_t* Os, int rb, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+    for (int ks = 0; ks < DQK / 16; ++ks) s = mfma32(as_bf16x8(qrd.read(Qs, rb, ks)), kreg[ks], s);
 #pragma unroll
-    for (int ks = 0; ks < DQK / 16; ++ks)
+    for (int ks = 0; ks < DV / 16; ++ks) dp = mfma32(as_bf16x8(ord.read(Os, rb, ks)), vreg[ks], dp);
+  };
+  // B(u): element i of the accumulators is query row qrow0 + acc_row(i, hf),
+  // key kj; lse2 / delta come from the stage at offset rb.
+  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, const f32x16& s, const f32x16& dp,
+                     u32x4(&pw)[2], u32x4(&dw)[2]) {
+    const int lo_r = qlo_k - (qrow0 + hf * 4), hi_r = qhi_k - (qrow0 + hf * 4);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-        s[qb] = mfma32(as_bf16x8(qrd.read(Qs, (qb0 + qb) * 32, ks)), kreg[ks], s[qb]);
+    for (int ig = 0; ig < 4; ++ig) {
+      const int qo = rb + ig * 8 + hf * 4;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qo);
+      u32x2 pp, dd;
 #pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
+      for (int u2 = 0; u2 < 2; ++u2) {
+        float p2[2], s2[2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-        dp[qb] = mfma32(as_bf16x8(ord.read(Os, (qb0 + qb) * 32, ks)), vreg[ks], dp[qb]);
-    const int lo_r = qlo_k - (q0 + hf * 4), hi_r = qhi_k - (q0 + hf * 4);
-    u32x4 pw[2 * NQB], dw[2 * NQB];  // bf16 pairs of P and dS: B operands of the 16-query K-steps
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const int qo = (qb0 + qb) * 32 + ig * 8 + hf * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds_ + qo);
-        u32x2 pp, dd;
-#pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
-          float p2[2], s2[2];
-#pragma unroll
-          for (int v = 0; v < 2; ++v) {
-            const int u = u2 * 2 + v, i = ig * 4 + u;
-            float pv = fast_exp2(fmaf(s[qb][i], a.scale_log2, -l4[u]));
-            if constexpr (MASKED) {
-              const int off = (qb0 + qb) * 32 + ig * 8 + u;
-              pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
-            }
-            p2[v] = pv;
-            s2[v] = pv * (dp[qb][i] - d4[u]);
-          }
-          pp[u2] = pack_bf16(p2[0], p2[1]);
-          dd[u2] = pack_bf16(s2[0], s2[1]);
+        for (int v = 0; v < 2; ++v) {
+          const int e = u2 * 2 + v, i = ig * 4 + e;
+          const int off = ig * 8 + e;
+          float pv = fast_exp2(fmaf(s[i], c, -l4[e]));
+          pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
+          p2[v] = pv;
+          s2[v] = pv * (dp[i] - d4[e]);
         }
-        // accumulator elements ig*4 .. ig*4+3 of block qb are B-operand
-        // elements (ig%2)*4 .. +3 of K-step qb*2 + ig/2
-        const int slot = qb * 2 + (ig >> 1), e0 = (ig & 1) * 2;
-        pw[slot][e0] = pp[0];
-        pw[slot][e0 + 1] = pp[1];
-        dw[slot][e0] = dd[0];
-        dw[slot][e0 + 1] = dd[1];
+        pp[u2] = pack_bf16(p2[0], p2[1]);
+        dd[u2] = pack_bf16(s2[0], s2[1]);
       }
-    // dV^T (dims x keys) += dO^T P ; dK^T (dims x keys) += Q^T dS.
+      // accumulator elements ig*4 .. ig*4+3 are B-operand elements
+      // (ig%2)*4 .. +3 of K-step ig/2
+      const int kstep = ig >> 1, e0 = (ig & 1) * 2;
+      pw[kstep][e0] = pp[0];
+      pw[kstep][e0 + 1] = pp[1];
+      dw[kstep][e0] = dd[0];
+      dw[kstep][e0 + 1] = dd[1];
+    }
+  };
+  // C(u): dV^T (dims x keys) += dO^T P ; dK^T (dims x keys) += Q^T dS.
+  auto phase_c = [&](const uint16_t* Qs, const uint16_t* Os, int rb, const u32x4(&pw)[2], const u32x4(&dw)[2]) {
 #pragma unroll
-    for (int kk = 0; kk < 2 * NQB; ++kk) {
-      const int pos0 = qb0 * 32 + kk * 16;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int pos0 = rb + kk * 16;
 #pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
-        dv[db] = mfma32(otr.read(Os, pos0, db), as_bf16x8(pw[kk]), dv[db]);
+      for (int db = 0; db < DV / 32; ++db) dv[db] = mfma32(otr.read(Os, pos0, db), as_bf16x8(pw[kk]), dv[db]);
 #pragma unroll
-      for (int db = 0; db < DQK / 32; ++db)
-        dk[db] = mfma32(qtr.read(Qs, pos0, db), as_bf16x8(dw[kk]), dk[db]);
+      for (int db = 0; db < DQK / 32; ++db) dk[db] = mfma32(qtr.read(Qs, pos0, db), as_bf16x8(dw[kk]), dk[db]);
     }
   };
 
-  // Unrolled by two: each stage's buffer, and so every LDS offset, is a
-  // compile-time constant.
-  auto stage = [&](int t, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const int q0 = (qs0 + t % nsteps) * C::BMQ;
-    if (t + 1 < total) issue_step(t + 1, buf ^ 1);
-#pragma unroll
-    for (int qb0 = 0; qb0 < C::BMQ / 32; qb0 += C::NQB) {
-      bool full = true, any = false;
-#pragma unroll
-      for (int qb = qb0; qb < qb0 + C::NQB; ++qb) {
-        const int cls = tile_class(m, q0 + qb * 32, 32, kw0, 32);
-        full = full && cls == TILE_FULL;
-        any = any || cls != TILE_SKIP;
+  StageWalk b_walk{0, 0, T > 0 ? q_first : a.S};  // stage of the block in B
+  StageWalk copy_walk = b_walk;                    // next stage to copy
+  // Iteration u, with P = u % 6 fixing the register sets and ring slots:
+  // block u sits in slot (u/2) % 3 = (P/2) % 3 at row offset (P%2)*32.
+  // The three phases are cut into four chunks, each holding a quarter of
+  // A(u+1)'s and of C(u-1)'s MFMAs and one 4-row group of B(u).  Chunk k's
+  // MFMA operands (and its rows' lse2 / delta) are read from LDS during
+  // chunk k-1, and a scheduling fence closes each chunk, so reads stay a
+  // chunk ahead of their use and register pressure stays bounded.
+  constexpr int NSK = DQK / 16, NPK = DV / 16, NA = NSK + NPK;  // A: S then dP k-steps
+  constexpr int NDV = DV / 32, NDK = DQK / 32, NC = 2 * (NDV + NDK);  // C: per K-step, dV then dK blocks
+  constexpr int NCH = 4, EA = NA / NCH, EC = NC / NCH;
+  static_assert(NA % NCH == 0 && NC % NCH == 0, "chunking");
+  auto iteration = [&](int u, auto phase) {
+    constexpr int P = decltype(phase)::value;
+    constexpr int cur = P & 1, nxt = cur ^ 1;
+    constexpr int slot_u = (P >> 1) % 3, slot_n = ((P + 1) >> 1) % 3, slot_p = ((P + 5) >> 1) % 3;
+    if constexpr ((P & 1) != 0) {
+      // Opens stage s = (u+1)/2: wait for its copy, then refill the slot of
+      // stage s-2 (last read by C(u-2) in the previous iteration) with s+1.
+      lds_dma_wait();
+      __syncthreads();
+      if (copy_walk.t < TP) {
+        issue_stage(copy_walk, (((P + 1) >> 1) + 1) % 3);
+        walk_next(copy_walk);
       }
-      if (full) step(q0, qb0, buf, std::false_type{});
-      else if (any) step(q0, qb0, buf, std::true_type{});
+    } else {
+      walk_next(b_walk);  // block u opens a new stage
     }
+    const uint16_t* Qa = qtile(slot_n);  // A(u+1): rows nxt*32 of its stage
+    const uint16_t* Oa = otile(slot_n);
+    const uint16_t* Qc = qtile(slot_p);  // C(u-1): rows nxt*32 of its stage
+    const uint16_t* Oc = otile(slot_p);
+    const float* ls = lse_s(slot_u);     // B(u): rows cur*32 of its stage
+    const float* dl = delta_s(slot_u);
+    const int q_u = b_walk.q0 + cur * 32;  // first row of block u
+
+    bf16x8 opa[2][EA], opc[2][EC];
+    f32x4 l4[2], d4[2];
+    auto read_chunk = [&](auto kc, auto setc) {
+      constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
+#pragma unroll
+      for (int e = 0; e < EA; ++e) {
+        const int i = k * EA + e;
+        opa[st][e] = as_bf16x8(i < NSK ? qrd.read(Qa, nxt * 32, i) : ord.read(Oa, nxt * 32, i - NSK));
+      }
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
+        opc[st][e] = j < NDV ? otr.read(Oc, nxt * 32 + kk * 16, j) : qtr.read(Qc, nxt * 32 + kk * 16, j - NDV);
+      }
+      const int qo = cur * 32 + k * 8 + hf * 4;
+      l4[st] = *reinterpret_cast<const f32x4*>(ls + qo);
+      d4[st] = *reinterpret_cast<const f32x4*>(dl + qo);
+    };
+    auto compute_chunk = [&](auto kc, auto setc) {
+      constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
+#pragma unroll
+      for (int e = 0; e < EA; ++e) {
+        const int i = k * EA + e;
+        if (i < NSK) S[nxt] = mfma32(opa[st][e], kreg[i], i == 0 ? f32x16{} : S[nxt]);
+        else DP[nxt] = mfma32(opa[st][e], vreg[i - NSK], i == NSK ? f32x16{} : DP[nxt]);
+      }
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
+        if (j < NDV) dv[j] = mfma32(opc[st][e], as_bf16x8(PW[nxt][kk]), dv[j]);
+        else dk[j - NDV] = mfma32(opc[st][e], as_bf16x8(DW[nxt][kk]), dk[j - NDV]);
+      }
+      // B(u) without the mask, rows k*8 + hf*4 + 0..3 of the block:
+      // accumulator elements 4k .. 4k+3, which are B-operand elements
+      // (k%2)*4 .. +3 of K-step k/2.  Blocks that need the mask redo B below.
+      u32x2 pp, dd;
+#pragma unroll
+      for (int u2 = 0; u2 < 2; ++u2) {
+        float p2[2], s2[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int e = u2 * 2 + v, i = k * 4 + e;
+          const float pv = fast_exp2(fmaf(S[cur][i], c, -l4[st][e]));
+          p2[v] = pv;
+          s2[v] = pv * (DP[cur][i] - d4[st][e]);
+        }
+        pp[u2] = pack_bf16(p2[0], p2[1]);
+        dd[u2] = pack_bf16(s2[0], s2[1]);
+      }
+      // Pin the results here: without it the compiler sinks this softmax
+      // work next to its consumer, C in the next iteration, which serialises
+      // it with those MFMAs again.
+      asm volatile("" : "+v"(pp), "+v"(dd));
+      constexpr int kstep = k >> 1, e0 = (k & 1) * 2;
+      PW[cur][kstep][e0] = pp[0];
+      PW[cur][kstep][e0 + 1] = pp[1];
+      DW[cur][kstep][e0] = dd[0];
+      DW[cur][kstep][e0 + 1] = dd[1];
+    };
+    // Within a chunk: each MFMA followed by LDS reads and VALU work, so the
+    // next MFMA is not issued while the matrix unit is still busy (a stalled
+    // MFMA would hold up every instruction behind it).
+    auto pattern = [&]() {
+#pragma unroll
+      for (int i = 0; i < EA + EC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, SDPA_DKDV_DS, 0);    // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, SDPA_DKDV_VALU, 0);  // VALU
+      }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    read_chunk(C0{}, C0{});
+    read_chunk(C1{}, C1{});
+    compute_chunk(C0{}, C0{});
+    pattern();
+    __builtin_amdgcn_sched_barrier(0);
+    read_chunk(C2{}, C0{});
+    compute_chunk(C1{}, C1{});
+    pattern();
+    __builtin_amdgcn_sched_barrier(0);
+    read_chunk(C3{}, C1{});
+    compute_chunk(C2{}, C0{});
+    pattern();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_chunk(C3{}, C1{});
+    pattern();
+    __builtin_amdgcn_sched_barrier(0);
+    // Blocks that some of this wave's (row, key) pairs cannot see (diagonal,
+    // window edge, padding): redo B with the mask.
+    if (!(q_u >= all_lo && q_u + 31 <= all_hi))
+      phase_b(ls, dl, cur * 32, q_u, S[cur], DP[cur], PW[cur], DW[cur]);
+  };
+
+  if (NB > 0) {
+    issue_stage(b_walk, 0);
+    StageWalk copy_walk_1 = b_walk;
+    walk_next(copy_walk_1);
+    issue_stage(copy_walk_1, 1);
+    copy_walk = copy_walk_1;
+    walk_next(copy_walk);
     lds_dma_wait();
     __syncthreads();
-  };
-  if (total > 0) issue_step(0, 0);
-  lds_dma_wait();
-  __syncthreads();
-  for (int t = 0; t < total; t += 2) {
-    stage(t, std::integral_constant<int, 0>{});
-    if (t + 1 < total) stage(t + 1, std::integral_constant<int, 1>{});
+    // Block 0 has no predecessor: A(0), then A(1) with B(0).
+    phase_a(qtile(0), otile(0), 0, S[0], DP[0]);
+    phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
+    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, S[0], DP[0], PW[0], DW[0]);
+    // Iterations 1 .. NI in trips of six (one per phase), padded past the
+    // last block NB-1 with empty blocks: their stages copy rows past the
+    // valid length, so Q, dO, lse2 and delta arrive as zeros, the mask
+    // zeroes P, and C adds exact zeros.  A single code path per trip keeps
+    // every register set in place.
+    for (int u = 1; u <= NI; u += 6) {
+      iteration(u, std::integral_constant<int, 1>{});
+      iteration(u + 1, std::integral_constant<int, 2>{});
+      iteration(u + 2, std::integral_constant<int, 3>{});
+      iteration(u + 3, std::integral_constant<int, 4>{});
+      iteration(u + 4, std::integral_constant<int, 5>{});
+      iteration(u + 5, std::integral_constant<int, 0>{});
+    }
+    // Block NI (even, first half of stage NI/2, ring slot 0) still owes C.
+    phase_c(qtile(0), otile(0), 0, PW[0], DW[0]);
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
