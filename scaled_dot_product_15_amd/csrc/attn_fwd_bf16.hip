@@ -129,19 +129,19 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   // K / V tiles of buffer `buf`: [BN][DQK] and [BN][DV], swizzled row-major.
   auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
   auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
-  auto issue_tile = [&](int j0, int buf) {
-    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
-    vcopy.issue(Vg, (uint32_t)(vstride * 2), j0, m.L, vtile(buf));
-  };
 
-  // One key tile for this wave.  MASKED selects the per-element predicate:
-  // element i of block kb is key j0 + hf*4 + kb*32 + acc_row(i, 0).
-  auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    f32x16 s[BN / 32];
+  // Software pipeline over key tiles: iteration k finishes tile k (mask,
+  // online softmax, P V) and computes the scores of tile k+1, so the score
+  // products of k+1 and the exp / pack work of k sit in one basic block and
+  // overlap.  K and V have separate double buffers: at the start of
+  // iteration k the copies of K(k+2) (into the slot S(k) was read from) and
+  // V(k+1) (into the slot P V(k-1) read) are issued; both land before the
+  // barrier that closes the iteration.  The scores of the tile after the
+  // last one are computed from whatever the slot holds and never used.
+  f32x16 sc[2][BN / 32];  // scores of tile k (slot k&1) and of tile k+1
+  auto scores = [&](const uint16_t* Ks, f32x16 (&s)[BN / 32]) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
-    prio_mfma();
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) {
 #pragma unroll
@@ -150,7 +150,16 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
         s[kb] = mfma32(ka, qreg[ks], s[kb]);
       }
     }
-    prio_valu();
+  };
+  // MASKED selects the per-element predicate: element i of block kb of tile
+  // k is key j0 + hf*4 + kb*32 + acc_row(i, 0).
+  auto iteration = [&](int kt, auto bufc, auto masked) {
+    constexpr int buf = decltype(bufc)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    const int j0 = kt * BN;
+    if (kt + 2 <= kt1) kcopy.issue(Kg, (uint32_t)(kstride * 2), j0 + 2 * BN, m.L, ktile(buf));
+    if (kt + 1 <= kt1) vcopy.issue(Vg, (uint32_t)(vstride * 2), j0 + BN, m.L, vtile(buf ^ 1));
+    f32x16 (&s)[BN / 32] = sc[buf];
     float mx = -__builtin_inff();
     if constexpr (MASKED) {
       const int base = j0 + hf * 4;
@@ -170,13 +179,18 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
     mx = halves_max(mx) * c;
     const float m_new = fmaxf(m_run, mx);
     const bool rescale = __any(m_new > m_run + 8.0f);
-    float alpha = 1.0f;
-    if (rescale) {
-      alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
+    if (__builtin_expect(rescale, 0)) {
+      const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
     }
     const float nmu = (m_run == -__builtin_inff()) ? 0.0f : -m_run;
+    // From here to the barrier one basic block: the scores of the next tile
+    // (issued first so the matrix unit starts while the exp work below
+    // runs), this tile's exp / pack, and its P V products.
+    scores(ktile(buf ^ 1), sc[buf ^ 1]);
     float ls = 0.0f;
     bf16x8 pb[BN / 16];
 #pragma unroll
@@ -195,11 +209,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
       }
     }
     l_run += ls;
-    if (__builtin_expect(rescale, 0)) {
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db) o[db] *= alpha;
-    }
-    prio_mfma();
+    const uint16_t* Vs = vtile(buf);
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
 #pragma unroll
@@ -208,20 +218,16 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
         o[db] = mfma32(va, pb[kk], o[db]);
       }
     }
-    prio_valu();
+    lds_dma_wait();
+    __syncthreads();
   };
 
-  // Double-buffered pipeline, one barrier per tile: the copy of tile kt+1
-  // runs while tile kt computes; the barrier after the wait both publishes
-  // tile kt+1 and frees tile kt's buffer for the copy after it.  Tiles go in
-  // pairs (buffers 0, 1), so every LDS offset is a compile-time constant.
-  //
   // Key tiles that every row of the workgroup sees in full run unmasked; the
-  // rest (window start, diagonal, padding) run masked, each wave skipping the
-  // tiles its own rows cannot see.  The unmasked range is trimmed to whole
-  // pairs, and each of the three loops has a single code path: choosing the
-  // masked or unmasked body per tile inside one loop made the compiler copy
-  // the O accumulators on every tile.
+  // rest (window start, diagonal, padding) run with the mask (a wave whose
+  // rows see none of a tile gets P = 0 there).  Tiles go in pairs (slots 0,
+  // 1) so every LDS offset is a compile-time constant; the unmasked range is
+  // trimmed to whole pairs, and each of the three loops has a single code
+  // path so the accumulators stay in place.
   int fa = kt0, fb = kt0;  // unmasked tiles [fa, fb); fa - kt0, fb - fa even
   {
     int f0, f1;
@@ -236,34 +242,30 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
       }
     }
   }
-  auto step = [&](int kt, auto bufc, auto masked) {
-    constexpr int buf = decltype(bufc)::value;
-    const int j0 = kt * BN;
-    if (kt < kt1) issue_tile(j0 + BN, buf ^ 1);
-    if constexpr (decltype(masked)::value) {
-      if (tile_class(m, row_w0, 32, j0, BN) != TILE_SKIP) tile(j0, ktile(buf), vtile(buf), std::true_type{});
-    } else {
-      tile(j0, ktile(buf), vtile(buf), std::false_type{});
-    }
-    lds_dma_wait();
-    __syncthreads();
-  };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  if (kt0 <= kt1) issue_tile(kt0 * BN, 0);
-  lds_dma_wait();
-  __syncthreads();
+  // Tile slots follow k - kt0; tile k0 = kt0 lands in slot 0.
+  if (kt0 <= kt1) {
+    kcopy.issue(Kg, (uint32_t)(kstride * 2), kt0 * BN, m.L, ktile(0));
+    vcopy.issue(Vg, (uint32_t)(vstride * 2), kt0 * BN, m.L, vtile(0));
+    if (kt0 + 1 <= kt1) kcopy.issue(Kg, (uint32_t)(kstride * 2), (kt0 + 1) * BN, m.L, ktile(1));
+    lds_dma_wait();
+    __syncthreads();
+    prio_mfma();
+    scores(ktile(0), sc[0]);
+    prio_valu();
+  }
   for (int kt = kt0; kt < fa; kt += 2) {
-    step(kt, B0{}, std::true_type{});
-    step(kt + 1, B1{}, std::true_type{});
+    iteration(kt, B0{}, std::true_type{});
+    iteration(kt + 1, B1{}, std::true_type{});
   }
   for (int kt = fa; kt < fb; kt += 2) {
-    step(kt, B0{}, std::false_type{});
-    step(kt + 1, B1{}, std::false_type{});
+    iteration(kt, B0{}, std::false_type{});
+    iteration(kt + 1, B1{}, std::false_type{});
   }
   for (int kt = fb; kt <= kt1; kt += 2) {
-    step(kt, B0{}, std::true_type{});
-    if (kt + 1 <= kt1) step(kt + 1, B1{}, std::true_type{});
+    iteration(kt, B0{}, std::true_type{});
+    if (kt + 1 <= kt1) iteration(kt + 1, B1{}, std::true_type{});
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
