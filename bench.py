@@ -1,8 +1,8 @@
 """Benchmark of the fused attention forward + backward on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-attn_fwd, then the backward stages (pre-pass, dK/dV, dQ, sink-gradient
-reduce).  Inputs are resident in HBM before the timed region.  Prints one JSON
+attn_fwd, then the backward stages (pre-pass (fp32 only; the bf16 dQ kernel
+does it), dQ, dK/dV, sink-gradient reduce).  Inputs are resident in HBM before the timed region.  Prints one JSON
 line with whole-job effective TFLOP/s, counting only visible (query, key)
 pairs: forward 2 * pairs * (d_qk + d_v), backward 2 * pairs * (3 d_qk + 2 d_v).
 
@@ -155,30 +155,45 @@ def main():
     ws = torch.empty(binding.attn_bwd_workspace_size(pp), dtype=torch.uint8, device="cuda")
     fast = dict(kw, check_seqlens=False)
     stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_offset"]
+    names = ["fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_offset"]  # stages 1..4 follow fwd
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
+        binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
+        binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
+                         outs=outs, **fast)
+
+    def staged_step(ev):
+        """The same work with HIP events between the kernels (per-kernel times)."""
+        ev[0].record(stream)
         binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
         for s in range(1, 5):
-            if ev is not None:
-                ev[s].record(stream)
+            ev[s].record(stream)
             binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
                              outs=outs, stage=s, **fast)
-        if ev is not None:
-            ev[5].record(stream)
+        ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Forward / backward split and per-kernel breakdown: separate passes of the
+    # same number of steps with HIP events on the launch stream.
+    split = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for ev in split:
+        ev[0].record(stream)
+        binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
+        ev[1].record(stream)
+        binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
+                         outs=outs, **fast)
+        ev[2].record(stream)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        staged_step(events[i])
+    torch.cuda.synchronize()
 
     per = {n: [] for n in names}
     for ev in events:
@@ -194,8 +209,8 @@ def main():
     f_fwd, f_bwd = oracle.effective_flops(pairs, p.d_qk, p.d_v)
     ms_per_step = elapsed / args.steps * 1e3
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
-    t_fwd = med_ms["fwd"]
-    t_bwd = sum(med_ms[n] for n in names[1:])
+    t_fwd = statistics.median(ev[0].elapsed_time(ev[1]) for ev in split)
+    t_bwd = statistics.median(ev[1].elapsed_time(ev[2]) for ev in split)
 
     kflops = kernel_flops_per_pair(p.d_qk, p.d_v)
     dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg_ms[n])

@@ -129,18 +129,19 @@ int attn_bwd(const struct attn_params* p, const void* q, const void* k, const vo
              void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of attn_bwd, same arguments and checks as attn_bwd.  attn_bwd
- * runs the stages 1..4 in order on one stream; stage 1 must complete before
- * stages 2 and 3, which are independent of each other (a caller may put them
- * on two streams), and stage 4 needs only stage 1.
- *   1 ATTN_BWD_STAGE_PREPROCESS  delta = rowsum(dO * O) and per-block partial
- *                                sums of d(sink logit), into the workspace
- *   2 ATTN_BWD_STAGE_DKDV        dK, dV
- *   3 ATTN_BWD_STAGE_DQ          dQ
+ * runs the stages 1..4 in order on one stream; each stage needs the ones
+ * before it (stage 4 needs only stages 1 and 2).
+ *   1 ATTN_BWD_STAGE_PREPROCESS  delta = rowsum(dO * O), LSE * log2(e) and
+ *                                per-block partials of the sink gradient
+ *                                (fp32; for bf16 stage 2 does this work and
+ *                                stage 1 launches nothing)
+ *   2 ATTN_BWD_STAGE_DQ          dQ
+ *   3 ATTN_BWD_STAGE_DKDV        dK, dV
  *   4 ATTN_BWD_STAGE_OFFSET_GRAD d_softmax_offset (no-op when it is NULL)
  * Any other stage value returns ATTN_ERR_INVALID_ARG. */
 #define ATTN_BWD_STAGE_PREPROCESS 1
-#define ATTN_BWD_STAGE_DKDV 2
-#define ATTN_BWD_STAGE_DQ 3
+#define ATTN_BWD_STAGE_DQ 2
+#define ATTN_BWD_STAGE_DKDV 3
 #define ATTN_BWD_STAGE_OFFSET_GRAD 4
 int attn_bwd_stage(int stage, const struct attn_params* p, const void* q, const void* k, const void* v,
                    const void* o, const void* d_o, const float* lse, const float* softmax_offset,

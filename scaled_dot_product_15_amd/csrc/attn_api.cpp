@@ -39,9 +39,14 @@ int check_fields(const attn_params* p) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-int n_chunks(const attn_params* p) { return (p->seqlen + kPreRows - 1) / kPreRows; }
+// Rows per sink-gradient partial: the bf16 dQ kernel writes one per wave
+// (32 rows), the fp32 pre-pass one per 64-row block; the workspace holds the
+// larger count.
+int chunk_rows(const attn_params* p) { return p->dtype == ATTN_BF16 ? kDqChunkRows : kPreRows; }
+int n_chunks(const attn_params* p) { return (p->seqlen + chunk_rows(p) - 1) / chunk_rows(p); }
+int max_chunks(const attn_params* p) { return (p->seqlen + kDqChunkRows - 1) / kDqChunkRows; }
 size_t delta_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * p->seqlen * sizeof(float)); }
-size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * n_chunks(p) * sizeof(float)); }
+size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * max_chunks(p) * sizeof(float)); }
 
 KArgs make_args(const attn_params* p) {
   KArgs a = {};
@@ -143,15 +148,16 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == ATTN_BF16;
   const int dqk = p->head_dim_qk, dvd = p->head_dim_v;
-  if (stage == 0 || stage == ATTN_BWD_STAGE_PREPROCESS) {
+  // bf16: the dQ kernel also runs the pre-pass, so stage 1 launches nothing.
+  if ((stage == 0 || stage == ATTN_BWD_STAGE_PREPROCESS) && !bf16) {
     if (launch_bwd_pre(a, p->dtype, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
-  }
-  if (stage == 0 || stage == ATTN_BWD_STAGE_DKDV) {
-    hipError_t e = bf16 ? launch_bwd_dkdv_bf16(a, dqk, dvd, s) : launch_bwd_dkdv_f32(a, dqk, dvd, s);
-    if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   if (stage == 0 || stage == ATTN_BWD_STAGE_DQ) {
     hipError_t e = bf16 ? launch_bwd_dq_bf16(a, dqk, dvd, s) : launch_bwd_dq_f32(a, dqk, dvd, s);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (stage == 0 || stage == ATTN_BWD_STAGE_DKDV) {
+    hipError_t e = bf16 ? launch_bwd_dkdv_bf16(a, dqk, dvd, s) : launch_bwd_dkdv_f32(a, dqk, dvd, s);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&

@@ -1,4 +1,5 @@
-// Backward attention, dQ, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
+// Backward attention, dQ, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16,
+// with the backward pre-pass (delta, lse2, sink-gradient partials) fused in.
 //
 // With P = exp(scale * Q K^T - LSE) recomputed from the forward's LSE and
 // delta_i = rowsum(dO * O) from the pre-pass (PR #2225 backward: dz = dO in,
@@ -84,9 +85,38 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks)
       oreg[ks] = as_bf16x8(buf_load16(ores, (uint32_t)(qi * ostride + ks * 16 + hf * 8) * 2));
-    if (qi < m.L) {
-      lse2 = a.lse2[((size_t)b * a.Hq + h) * a.S + qi];
-      dl = a.delta[((size_t)b * a.Hq + h) * a.S + qi];
+    // Backward pre-pass for this wave's 32 rows, fused here: delta =
+    // rowsum(dO * O) (each lane half holds half of the row's dims; rows
+    // >= L read zeros), lse2 = LSE * log2(e) (0 past L), both stored for the
+    // dK/dV kernel; for a sink logit z, the partial sum over the 32 rows of
+    // dL/dz_i = -exp(z - LSE_i) delta_i (the sink enters only the softmax
+    // denominator), added up over the rows' chunks in fixed order later.
+    const __amdgpu_buffer_rsrc_t outres = buf_rsrc(static_cast<const uint16_t*>(a.o) + ((size_t)b * a.S * a.Hq + h) * DV,
+                                                   (uint32_t)(m.L * ostride * 2));
+    float part = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      const u32x4 ov = buf_load16(outres, (uint32_t)(qi * ostride + ks * 16 + hf * 8) * 2);
+      const u32x4 dv4 = __builtin_bit_cast(u32x4, oreg[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part += __builtin_bit_cast(float, ov[e] << 16) * __builtin_bit_cast(float, dv4[e] << 16);
+        part += __builtin_bit_cast(float, ov[e] & 0xffff0000u) * __builtin_bit_cast(float, dv4[e] & 0xffff0000u);
+      }
+    }
+    dl = halves_sum(part);
+    const size_t row = ((size_t)b * a.Hq + h) * a.S + qi;
+    const float lse_nat = qi < m.L ? a.lse[row] : 0.0f;
+    lse2 = qi < m.L ? lse_nat * kLog2e : 0.0f;
+    if (hf == 0 && qi < a.S) {
+      a.delta[row] = dl;
+      a.lse2[row] = lse2;
+    }
+    if (a.softmax_type != 0) {
+      float dz = (hf == 0 && qi < m.L) ? -expf(sink_logit(a, h) - lse_nat) * dl : 0.0f;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) dz += __shfl_xor(dz, off);
+      if (lane == 0 && qw0 < a.S) a.dz_partial[((size_t)b * a.Hq + h) * a.n_chunks + qw0 / 32] = dz;
     }
   }
   f32x16 dq[DQK / 32];

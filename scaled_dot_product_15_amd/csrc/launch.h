@@ -9,7 +9,8 @@ namespace sdpa {
 
 // Rows per block of the backward pre-pass; also the chunk of the d(sink)
 // partial sums.
-constexpr int kPreRows = 64;
+constexpr int kPreRows = 64;      // rows per block of the fp32 pre-pass
+constexpr int kDqChunkRows = 32;  // rows per sink-gradient partial of the bf16 dQ kernel
 
 bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
