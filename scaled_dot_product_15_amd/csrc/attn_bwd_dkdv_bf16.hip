@@ -108,6 +108,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     all_hi = hi_b;
     if (kw0 + 31 >= m.L) { all_lo = 1; all_hi = 0; }
   }
+  // Rows that see at least one of them: from the first key's first row to
+  // the last valid key's last row.  Blocks outside see nothing here.
+  int any_lo = 1, any_hi = 0;
+  {
+    const int kw0 = j0 + w * 32;
+    if (kw0 < m.L) {
+      const int kl = kw0 + 31 < m.L ? kw0 + 31 : m.L - 1;
+      int lo_a, hi_a, lo_b, hi_b;
+      col_query_bounds(m, kw0, lo_a, hi_a);
+      col_query_bounds(m, kl, lo_b, hi_b);
+      any_lo = lo_a;
+      any_hi = hi_b;
+    }
+  }
+  auto block_seen = [&](int q0) { return q0 <= any_hi && q0 + 31 >= any_lo; };
 
   // K^T / V^T operands: lane holds key kj, dims [ks*16 + hf*8, +8); buffer
   // resources end at the valid length, so keys >= L read as zeros.
@@ -245,6 +260,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 
   StageWalk b_walk{0, 0, T > 0 ? q_first : a.S};  // stage of the block in B
   StageWalk copy_walk = b_walk;                    // next stage to copy
+  int prev_q0 = a.S;                               // first row of the stage before b_walk's
   // Iteration u, with P = u % 6 fixing the register sets and ring slots:
   // block u sits in slot (u/2) % 3 = (P/2) % 3 at row offset (P%2)*32.
   // The three phases are cut into four chunks, each holding a quarter of
@@ -270,6 +286,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         walk_next(copy_walk);
       }
     } else {
+      prev_q0 = b_walk.q0;
       walk_next(b_walk);  // block u opens a new stage
     }
     const uint16_t* Qa = qtile(slot_n);  // A(u+1): rows nxt*32 of its stage
@@ -279,6 +296,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     const float* ls = lse_s(slot_u);     // B(u): rows cur*32 of its stage
     const float* dl = delta_s(slot_u);
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
+    // A wave whose keys see none of blocks u-1, u, u+1 skips the iteration's
+    // work (it still takes part in the copies and barriers): C(u-1) would add
+    // zeros, and B(u) would produce zeros, set directly; A(u+1)'s scores are
+    // then never needed unmasked (B(u+1) masks them all).
+    int q_next = q_u + 32, q_prev = q_u - 32;
+    if constexpr (cur == 1) {
+      StageWalk nx = b_walk;
+      walk_next(nx);
+      q_next = nx.q0;
+    } else {
+      q_prev = prev_q0 + 32;
+    }
+    // (Not for 192-dim heads, whose register budget has no room left for it.)
+    const bool skip = DQK <= 128 && !block_seen(q_prev) && !block_seen(q_u) && !block_seen(q_next);
 
     bf16x8 opa[2][EA], opc[2][EC];
     f32x4 l4[2], d4[2];
@@ -354,6 +385,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
     using C3 = std::integral_constant<int, 3>;
+    if (skip) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        PW[cur][kk] = u32x4{};
+        DW[cur][kk] = u32x4{};
+      }
+      return;
+    }
     read_chunk(C0{}, C0{});
     read_chunk(C1{}, C1{});
     compute_chunk(C0{}, C0{});
