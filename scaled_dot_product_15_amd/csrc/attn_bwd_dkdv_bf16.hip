@@ -22,7 +22,9 @@
 // one basic block, so the scheduler can fill the MFMA pipe with A and C
 // while B's exp / FMA work issues in between (one wave per SIMD has no other
 // wave to hide its softmax behind).  S/dP and P/dS each alternate between two
-// register sets.
+// register sets.  An iteration runs in four chunks whose LDS operands are read
+// one chunk ahead, the first chunk's during the last chunk of the iteration
+// before (A's only where no barrier lies in between).
 //
 // Query rows are staged 64 at a time (two blocks) in a ring of three LDS
 // buffers filled by direct memory-to-LDS copies: Q and dO tiles (swizzled
@@ -108,21 +110,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     all_hi = hi_b;
     if (kw0 + 31 >= m.L) { all_lo = 1; all_hi = 0; }
   }
-  // Rows that see at least one of them: from the first key's first row to
-  // the last valid key's last row.  Blocks outside see nothing here.
-  int any_lo = 1, any_hi = 0;
-  {
-    const int kw0 = j0 + w * 32;
-    if (kw0 < m.L) {
-      const int kl = kw0 + 31 < m.L ? kw0 + 31 : m.L - 1;
-      int lo_a, hi_a, lo_b, hi_b;
-      col_query_bounds(m, kw0, lo_a, hi_a);
-      col_query_bounds(m, kl, lo_b, hi_b);
-      any_lo = lo_a;
-      any_hi = hi_b;
-    }
-  }
-  auto block_seen = [&](int q0) { return q0 <= any_hi && q0 + 31 >= any_lo; };
 
   // K^T / V^T operands: lane holds key kj, dims [ks*16 + hf*8, +8); buffer
   // resources end at the valid length, so keys >= L read as zeros.
@@ -260,7 +247,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 
   StageWalk b_walk{0, 0, T > 0 ? q_first : a.S};  // stage of the block in B
   StageWalk copy_walk = b_walk;                    // next stage to copy
-  int prev_q0 = a.S;                               // first row of the stage before b_walk's
   // Iteration u, with P = u % 6 fixing the register sets and ring slots:
   // block u sits in slot (u/2) % 3 = (P/2) % 3 at row offset (P%2)*32.
   // The three phases are cut into four chunks, each holding a quarter of
@@ -272,10 +258,57 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   constexpr int NDV = DV / 32, NDK = DQK / 32, NC = 2 * (NDV + NDK);  // C: per K-step, dV then dK blocks
   constexpr int NCH = 4, EA = NA / NCH, EC = NC / NCH;
   static_assert(NA % NCH == 0 && NC % NCH == 0, "chunking");
+  // Operand sets of two chunks; set 0 also carries the first chunk of the
+  // next iteration, read during the last chunk of the current one.
+  bf16x8 opa[2][EA], opc[2][EC];
+  f32x4 l4[2], d4[2];
+  // Chunk k's LDS reads for the iteration of phase P into set st: A(u+1)'s
+  // operands (RA), C(u-1)'s (RC), B(u)'s lse2 / delta (RL).
+  auto read_chunk = [&](auto phase, auto kc, auto setc, auto ra, auto rc, auto rl) {
+    constexpr int P = decltype(phase)::value, k = decltype(kc)::value, st = decltype(setc)::value;
+    constexpr int cur = P & 1, nxt = cur ^ 1;
+    constexpr int slot_u = (P >> 1) % 3, slot_n = ((P + 1) >> 1) % 3, slot_p = ((P + 5) >> 1) % 3;
+    if constexpr (decltype(ra)::value) {
+#pragma unroll
+      for (int e = 0; e < EA; ++e) {
+        const int i = k * EA + e;
+        opa[st][e] = as_bf16x8(i < NSK ? qrd.read(qtile(slot_n), nxt * 32, i)
+                                       : ord.read(otile(slot_n), nxt * 32, i - NSK));
+      }
+    }
+    if constexpr (decltype(rc)::value) {
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
+        opc[st][e] = j < NDV ? otr.read(otile(slot_p), nxt * 32 + kk * 16, j)
+                             : qtr.read(qtile(slot_p), nxt * 32 + kk * 16, j - NDV);
+      }
+    }
+    if constexpr (decltype(rl)::value) {
+      const int qo = cur * 32 + k * 8 + hf * 4;
+      l4[st] = *reinterpret_cast<const f32x4*>(lse_s(slot_u) + qo);
+      d4[st] = *reinterpret_cast<const f32x4*>(delta_s(slot_u) + qo);
+    }
+  };
+  using T0 = std::false_type;
+  using T1 = std::true_type;
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  // First chunk of the iteration after the one of phase P, read ahead.  When
+  // that iteration opens a stage (odd phase) its A operands are only there
+  // after its barrier, so they are read then.
+  auto read_ahead = [&](auto phase) {
+    constexpr int PN = (decltype(phase)::value + 1) % 6;
+    using PNC = std::integral_constant<int, PN>;
+    if constexpr ((PN & 1) != 0) read_chunk(PNC{}, C0{}, C0{}, T0{}, T1{}, T1{});
+    else read_chunk(PNC{}, C0{}, C0{}, T1{}, T1{}, T1{});
+  };
   auto iteration = [&](int u, auto phase) {
     constexpr int P = decltype(phase)::value;
     constexpr int cur = P & 1, nxt = cur ^ 1;
-    constexpr int slot_u = (P >> 1) % 3, slot_n = ((P + 1) >> 1) % 3, slot_p = ((P + 5) >> 1) % 3;
+    constexpr int slot_u = (P >> 1) % 3;
     if constexpr ((P & 1) != 0) {
       // Opens stage s = (u+1)/2: wait for its copy, then refill the slot of
       // stage s-2 (last read by C(u-2) in the previous iteration) with s+1.
@@ -286,62 +319,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         walk_next(copy_walk);
       }
     } else {
-      prev_q0 = b_walk.q0;
       walk_next(b_walk);  // block u opens a new stage
     }
-    const uint16_t* Qa = qtile(slot_n);  // A(u+1): rows nxt*32 of its stage
-    const uint16_t* Oa = otile(slot_n);
-    const uint16_t* Qc = qtile(slot_p);  // C(u-1): rows nxt*32 of its stage
-    const uint16_t* Oc = otile(slot_p);
-    const float* ls = lse_s(slot_u);     // B(u): rows cur*32 of its stage
+    const float* ls = lse_s(slot_u);  // B(u): rows cur*32 of its stage
     const float* dl = delta_s(slot_u);
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
-    // A wave whose keys see none of blocks u-1, u, u+1 skips the iteration's
-    // work (it still takes part in the copies and barriers): C(u-1) would add
-    // zeros, and B(u) would produce zeros, set directly; A(u+1)'s scores are
-    // then never needed unmasked (B(u+1) masks them all).
-    int q_next = q_u + 32, q_prev = q_u - 32;
-    if constexpr (cur == 1) {
-      StageWalk nx = b_walk;
-      walk_next(nx);
-      q_next = nx.q0;
-    } else {
-      q_prev = prev_q0 + 32;
-    }
-    // (Not for 192-dim heads, whose register budget has no room left for it.)
-    const bool skip = DQK <= 128 && !block_seen(q_prev) && !block_seen(q_u) && !block_seen(q_next);
 
-    bf16x8 opa[2][EA], opc[2][EC];
-    f32x4 l4[2], d4[2];
-    auto read_chunk = [&](auto kc, auto setc) {
-      constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
-#pragma unroll
-      for (int e = 0; e < EA; ++e) {
-        const int i = k * EA + e;
-        opa[st][e] = as_bf16x8(i < NSK ? qrd.read(Qa, nxt * 32, i) : ord.read(Oa, nxt * 32, i - NSK));
-      }
-#pragma unroll
-      for (int e = 0; e < EC; ++e) {
-        const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
-        opc[st][e] = j < NDV ? otr.read(Oc, nxt * 32 + kk * 16, j) : qtr.read(Qc, nxt * 32 + kk * 16, j - NDV);
-      }
-      const int qo = cur * 32 + k * 8 + hf * 4;
-      l4[st] = *reinterpret_cast<const f32x4*>(ls + qo);
-      d4[st] = *reinterpret_cast<const f32x4*>(dl + qo);
-    };
     auto compute_chunk = [&](auto kc, auto setc) {
       constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
-#pragma unroll
-      for (int e = 0; e < EA; ++e) {
-        const int i = k * EA + e;
-        if (i < NSK) S[nxt] = mfma32(opa[st][e], kreg[i], i == 0 ? f32x16{} : S[nxt]);
-        else DP[nxt] = mfma32(opa[st][e], vreg[i - NSK], i == NSK ? f32x16{} : DP[nxt]);
-      }
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
         const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
         if (j < NDV) dv[j] = mfma32(opc[st][e], as_bf16x8(PW[nxt][kk]), dv[j]);
         else dk[j - NDV] = mfma32(opc[st][e], as_bf16x8(DW[nxt][kk]), dk[j - NDV]);
+      }
+#pragma unroll
+      for (int e = 0; e < EA; ++e) {
+        const int i = k * EA + e;
+        if (i < NSK) S[nxt] = mfma32(opa[st][e], kreg[i], i == 0 ? f32x16{} : S[nxt]);
+        else DP[nxt] = mfma32(opa[st][e], vreg[i - NSK], i == NSK ? f32x16{} : DP[nxt]);
       }
       // B(u) without the mask, rows k*8 + hf*4 + 0..3 of the block:
       // accumulator elements 4k .. 4k+3, which are B-operand elements
@@ -381,31 +377,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, SDPA_DKDV_VALU, 0);  // VALU
       }
     };
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using C2 = std::integral_constant<int, 2>;
-    using C3 = std::integral_constant<int, 3>;
-    if (skip) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        PW[cur][kk] = u32x4{};
-        DW[cur][kk] = u32x4{};
-      }
-      return;
-    }
-    read_chunk(C0{}, C0{});
-    read_chunk(C1{}, C1{});
+    using PC = std::integral_constant<int, P>;
+    // Chunk 0's operands were read during the previous iteration, except A's
+    // after a barrier: C's MFMAs come first in each chunk and cover them.
+    if constexpr ((P & 1) != 0) read_chunk(PC{}, C0{}, C0{}, T1{}, T0{}, T0{});
+    read_chunk(PC{}, C1{}, C1{}, T1{}, T1{}, T1{});
     compute_chunk(C0{}, C0{});
     pattern();
     __builtin_amdgcn_sched_barrier(0);
-    read_chunk(C2{}, C0{});
+    read_chunk(PC{}, C2{}, C0{}, T1{}, T1{}, T1{});
     compute_chunk(C1{}, C1{});
     pattern();
     __builtin_amdgcn_sched_barrier(0);
-    read_chunk(C3{}, C1{});
+    read_chunk(PC{}, C3{}, C1{}, T1{}, T1{}, T1{});
     compute_chunk(C2{}, C0{});
     pattern();
     __builtin_amdgcn_sched_barrier(0);
+    read_ahead(PC{});
     compute_chunk(C3{}, C1{});
     pattern();
     __builtin_amdgcn_sched_barrier(0);
@@ -428,6 +416,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     phase_a(qtile(0), otile(0), 0, S[0], DP[0]);
     phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
     phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, S[0], DP[0], PW[0], DW[0]);
+    read_ahead(std::integral_constant<int, 0>{});  // first chunk of iteration 1
     // Iterations 1 .. NI in trips of six (one per phase), padded past the
     // last block NB-1 with empty blocks: their stages copy rows past the
     // valid length, so Q, dO, lse2 and delta arrive as zeros, the mask
