@@ -55,7 +55,7 @@
 #define SDPA_DKDV_DS 2
 #endif
 #ifndef SDPA_DKDV_VALU
-#define SDPA_DKDV_VALU 5
+#define SDPA_DKDV_VALU 2
 #endif
 
 namespace sdpa {
