@@ -100,7 +100,10 @@ int attn_validate(const struct attn_params* p);
 
 /* Workspace bytes the forward / backward call needs (0 if p is invalid).
  * The forward needs none; the backward needs room for the per-row
- * delta = rowsum(dO * O) and the per-block partial sums of d(sink logit). */
+ * delta = rowsum(dO * O) and LSE * log2(e), the per-block partial sums of
+ * d(sink logit), and, for bf16 problems whose dK/dV grid is small (few KV
+ * heads, short batches: attn_host_dkdv_splits > 1), fp32 partial dK and dV
+ * of each query-head split of a GQA group. */
 size_t attn_fwd_workspace_size(const struct attn_params* p);
 size_t attn_bwd_workspace_size(const struct attn_params* p);
 
@@ -182,6 +185,13 @@ int attn_host_key_range(const struct attn_params* p, int32_t L, int32_t i0, int3
  * j0..j1 (inclusive); returns 1 if non-empty, else 0. */
 int attn_host_query_range(const struct attn_params* p, int32_t L, int32_t j0, int32_t j1,
                           int32_t* lo, int32_t* hi);
+
+/* Host: number of query-head splits of a GQA group the bf16 dK/dV stage
+ * uses for this problem (1 = none; 0 if p is invalid).  With s > 1 splits,
+ * s workgroups per (128-key tile, batch, KV head) each walk G/s of the
+ * group's query heads and write fp32 partials, which a second kernel adds in
+ * split order, so dK and dV stay bitwise reproducible. */
+int attn_host_dkdv_splits(const struct attn_params* p);
 
 /* Host: key tiles [*f0, *f1] (tile t = keys t*block_n .. t*block_n+block_n-1)
  * that every query row i0 .. i0+block_m-1 sees in full, for valid length L:

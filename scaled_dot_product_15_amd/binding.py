@@ -62,6 +62,7 @@ EXPORTS = {
                                              ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
     "attn_host_full_key_tiles": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32, _c_i32,
                                                 ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "attn_host_dkdv_splits": (ctypes.c_int, [ctypes.POINTER(Params)]),
 }
 
 _lib = None
@@ -289,3 +290,8 @@ def host_full_key_tiles(p: Params, L, i0, block_m, block_n):
     ok = load_library().attn_host_full_key_tiles(ctypes.byref(p), L, i0, block_m, block_n, ctypes.byref(f0),
                                                  ctypes.byref(f1))
     return (f0.value, f1.value) if ok else None
+
+
+def host_dkdv_splits(p: Params) -> int:
+    """Query-head splits of a GQA group in the bf16 dK/dV stage (0 if p is invalid)."""
+    return load_library().attn_host_dkdv_splits(ctypes.byref(p))

@@ -47,6 +47,17 @@ int n_chunks(const attn_params* p) { return (p->seqlen + chunk_rows(p) - 1) / ch
 int max_chunks(const attn_params* p) { return (p->seqlen + kDqChunkRows - 1) / kDqChunkRows; }
 size_t delta_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * p->seqlen * sizeof(float)); }
 size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * max_chunks(p) * sizeof(float)); }
+// bf16 dK/dV: query-head splits of a GQA group (fp32 partials in the workspace when > 1).
+int kv_splits(const attn_params* p) {
+  if (p->dtype != ATTN_BF16) return 1;
+  return dkdv_head_splits(p->batch, p->seqlen, p->num_gqa_groups, p->num_heads / p->num_gqa_groups);
+}
+size_t kv_part_bytes(const attn_params* p) {
+  const int ns = kv_splits(p);
+  if (ns == 1) return 0;
+  return align256((size_t)ns * p->batch * p->seqlen * p->num_gqa_groups * (p->head_dim_qk + p->head_dim_v) *
+                  sizeof(float));
+}
 
 KArgs make_args(const attn_params* p) {
   KArgs a = {};
@@ -62,6 +73,7 @@ KArgs make_args(const attn_params* p) {
   a.scale = p->scale_factor != 0.0f ? p->scale_factor : (float)(1.0 / sqrt((double)p->head_dim_qk));
   a.scale_log2 = a.scale * kLog2e;
   a.n_chunks = n_chunks(p);
+  a.n_splits = kv_splits(p);
   return a;
 }
 
@@ -88,7 +100,7 @@ size_t attn_fwd_workspace_size(const attn_params* p) {
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
   if (attn_validate(p) != ATTN_OK) return 0;
-  return 2 * delta_bytes(p) + dz_bytes(p);
+  return 2 * delta_bytes(p) + dz_bytes(p) + kv_part_bytes(p);
 }
 
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
@@ -145,6 +157,7 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(p));
   a.dz_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * delta_bytes(p));
+  a.kv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * delta_bytes(p) + dz_bytes(p));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == ATTN_BF16;
   const int dqk = p->head_dim_qk, dvd = p->head_dim_v;
@@ -158,6 +171,7 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   }
   if (stage == 0 || stage == ATTN_BWD_STAGE_DKDV) {
     hipError_t e = bf16 ? launch_bwd_dkdv_bf16(a, dqk, dvd, s) : launch_bwd_dkdv_f32(a, dqk, dvd, s);
+    if (e == hipSuccess && a.n_splits > 1) e = launch_dkdv_split_reduce(a, dqk, dvd, s);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&
@@ -270,6 +284,11 @@ int attn_host_full_key_tiles(const attn_params* p, int32_t L, int32_t i0, int32_
   *f0 = a;
   *f1 = b;
   return ok ? 1 : 0;
+}
+
+int attn_host_dkdv_splits(const attn_params* p) {
+  if (attn_validate(p) != ATTN_OK) return 0;
+  return kv_splits(p);
 }
 
 }  // extern "C"

@@ -12,7 +12,10 @@
 // while the workgroup walks the G query heads of the group in ascending order
 // and, for each, the visible query rows in ascending order, 32 rows (one
 // block) at a time; the GQA sum is therefore a fixed-order register
-// accumulation.  dQ has its own kernel.
+// accumulation.  When the grid of key tiles would be too small to fill the
+// GPU (few KV heads, short batches), the G heads are split over n_splits
+// workgroups; each writes fp32 partial dK, dV and a second kernel adds the
+// partials in split order.  dQ has its own kernel.
 //
 // Software pipeline.  Per block u a wave runs three dependent phases:
 //   A(u): S = Q K^T and dP = dO V^T for its 32 keys          (MFMA)
@@ -83,13 +86,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   auto delta_s = [&](int buf) { return lse_s(buf) + C::BMQ; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  // Workgroup id -> (key tile, batch, kv head): consecutive ids cover all
-  // (batch, kv head) of one key tile, so with B*Hkv a multiple of 8 a given
-  // (batch, kv head) always lands on the same XCD and its Q/dO tiles, read
-  // again by the neighbouring key tiles, stay in that XCD's L2.  Key tiles in
+  // Workgroup id -> (key tile, batch, kv head, head split): consecutive ids
+  // cover all of one key tile, so with B*Hkv*n_splits a multiple of 8 a given
+  // (batch, kv head, split) always lands on the same XCD and its Q/dO tiles,
+  // read again by the neighbouring key tiles, stay in that XCD's L2.  Key tiles in
   // ascending order: under a causal mask the first ones see the most queries.
-  const int kt = blockIdx.x / (a.B * a.Hkv);
-  const int r = blockIdx.x % (a.B * a.Hkv);
+  // Head split hs of n_splits covers query heads hs*Gs .. hs*Gs+Gs-1 of the group.
+  const int nsp = a.n_splits, Gs = a.G / nsp;
+  const int kt = blockIdx.x / (a.B * a.Hkv * nsp);
+  int r = blockIdx.x % (a.B * a.Hkv * nsp);
+  const int hs = r % nsp;
+  r /= nsp;
   const int b = r / a.Hkv, g = r % a.Hkv;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int j0 = kt * C::BN;
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   if (!query_range(m, j0, j0 + C::BN - 1, qlo, qhi)) { qlo = 0; qhi = -1; }
   const int qs0 = qlo / C::BMQ;
   const int nsteps = qhi < 0 ? 0 : qhi / C::BMQ - qs0 + 1;
-  const int T = nsteps * a.G;  // stages
+  const int T = nsteps * Gs;   // stages
   const int NB = 2 * T;        // 32-row blocks
   const int NI = NB > 0 ? (NB + 4) / 6 * 6 : 0;  // pipeline iterations after the first (multiple of 6, >= NB-1)
   const int TP = ((NI + 1) >> 1) + 1;            // stages touched, the padding ones included
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const TrReads<C::QCH> qtr(lane);
   const TrReads<C::OCH> otr(lane);
   auto issue_stage = [&](const StageWalk& st, int buf) {
-    const int h = g * a.G + st.hh;
+    const int h = g * a.G + hs * Gs + st.hh;
     const int q0 = st.q0;
     qcopy.issue(Qg + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
     ocopy.issue(dOg + ((size_t)b * a.S * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
@@ -436,25 +443,55 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
   if (kj < a.S) {
-    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DQK + hf * 4;
-    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DV + hf * 4;
+    if (nsp == 1) {
+      uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DQK + hf * 4;
+      uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DV + hf * 4;
 #pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
+      for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        u32x2 val = {pack_bf16(dk[db][ig * 4] * a.scale, dk[db][ig * 4 + 1] * a.scale),
-                     pack_bf16(dk[db][ig * 4 + 2] * a.scale, dk[db][ig * 4 + 3] * a.scale)};
-        *reinterpret_cast<u32x2*>(dkp + db * 32 + ig * 8) = val;
-      }
+        for (int ig = 0; ig < 4; ++ig) {
+          u32x2 val = {pack_bf16(dk[db][ig * 4] * a.scale, dk[db][ig * 4 + 1] * a.scale),
+                       pack_bf16(dk[db][ig * 4 + 2] * a.scale, dk[db][ig * 4 + 3] * a.scale)};
+          *reinterpret_cast<u32x2*>(dkp + db * 32 + ig * 8) = val;
+        }
 #pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
+      for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        u32x2 val = {pack_bf16(dv[db][ig * 4], dv[db][ig * 4 + 1]),
-                     pack_bf16(dv[db][ig * 4 + 2], dv[db][ig * 4 + 3])};
-        *reinterpret_cast<u32x2*>(dvp + db * 32 + ig * 8) = val;
-      }
+        for (int ig = 0; ig < 4; ++ig) {
+          u32x2 val = {pack_bf16(dv[db][ig * 4], dv[db][ig * 4 + 1]),
+                       pack_bf16(dv[db][ig * 4 + 2], dv[db][ig * 4 + 3])};
+          *reinterpret_cast<u32x2*>(dvp + db * 32 + ig * 8) = val;
+        }
+    } else {
+      // fp32 partials of this split (dK unscaled), same element order as dK / dV.
+      const size_t row = ((size_t)(hs * a.B + b) * a.S + kj) * a.Hkv + g;
+      float* dkp = a.kv_part + row * DQK + hf * 4;
+      float* dvp = a.kv_part + (size_t)nsp * a.B * a.S * a.Hkv * DQK + row * DV + hf * 4;
+#pragma unroll
+      for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig)
+          *reinterpret_cast<f32x4*>(dkp + db * 32 + ig * 8) =
+              f32x4{dk[db][ig * 4], dk[db][ig * 4 + 1], dk[db][ig * 4 + 2], dk[db][ig * 4 + 3]};
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig)
+          *reinterpret_cast<f32x4*>(dvp + db * 32 + ig * 8) =
+              f32x4{dv[db][ig * 4], dv[db][ig * 4 + 1], dv[db][ig * 4 + 2], dv[db][ig * 4 + 3]};
+    }
   }
+}
+
+// dst[i] = bf16(mul * sum over splits s = 0 .. n_splits-1 of part[s*n + i]),
+// four consecutive elements per thread (n is a multiple of 4).
+__global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* part, uint16_t* dst, size_t n, int n_splits,
+                                                                float mul) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int sp = 1; sp < n_splits; ++sp) acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * n + i);
+  *reinterpret_cast<u32x2*>(dst + i) = u32x2{pack_bf16(acc[0] * mul, acc[1] * mul), pack_bf16(acc[2] * mul, acc[3] * mul)};
 }
 
 // Explicit instantiations: with only the implicit ones from the launchers
@@ -467,9 +504,32 @@ template __global__ void bwd_dkdv_bf16_kernel<192, 128>(KArgs);
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   using D = DkdvCfg<DQK, DV>;
+  static_assert(D::BN == kDkdvKeyTile, "split rule uses the kernel's key tile");
   const int nkt = (a.S + D::BN - 1) / D::BN;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(D::NT), 0,
-                     stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV>), dim3((unsigned)(nkt * a.B * a.Hkv * a.n_splits)), dim3(D::NT),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+int dkdv_head_splits(int B, int S, int Hkv, int G) {
+  const long long base = (long long)((S + kDkdvKeyTile - 1) / kDkdvKeyTile) * B * Hkv;
+  int splits = 1;
+  if (base < kDkdvMinGrid)
+    for (int d = 2; d <= G; ++d)
+      if (G % d == 0) {
+        splits = d;
+        if (base * d >= kDkdvMinGrid) break;
+      }
+  return splits;
+}
+
+hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  const size_t rows = (size_t)a.B * a.S * a.Hkv;
+  const size_t nk = rows * dqk, nv = rows * dv;
+  hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((nk / 4 + 255) / 256)), dim3(256), 0, stream,
+                     a.kv_part, static_cast<uint16_t*>(a.dk), nk, a.n_splits, a.scale);
+  hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((nv / 4 + 255) / 256)), dim3(256), 0, stream,
+                     a.kv_part + (size_t)a.n_splits * nk, static_cast<uint16_t*>(a.dv), nv, a.n_splits, 1.0f);
   return hipGetLastError();
 }
 

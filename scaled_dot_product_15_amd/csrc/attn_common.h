@@ -37,6 +37,7 @@ struct KArgs {
   float* delta;       // workspace [B,Hq,S]: rowsum(dO * O)
   float* lse2;        // workspace [B,Hq,S]: LSE * log2(e), 0 past the valid length
   float* dz_partial;  // workspace [B,Hq,nchunk]
+  float* kv_part;     // workspace [n_splits][B,S,Hkv,Dqk] then [n_splits][B,S,Hkv,Dv]: partial dK / dV
   float* d_offset;    // [Hq] or nullptr
   int B, S, Hq, Hkv, G;
   int causal, wl, wr;   // windows already normalised to -1 or < S
@@ -45,6 +46,7 @@ struct KArgs {
   float scale_log2;     // scale * log2(e)
   int n_tiles;          // tiles along the sequence for this kernel's grid
   int n_chunks;         // dz partial chunks per (b, h)
+  int n_splits;         // dK/dV workgroups per (key tile, batch, kv head), each over G / n_splits query heads
 };
 
 __device__ __forceinline__ int seq_len(const KArgs& a, int b) {

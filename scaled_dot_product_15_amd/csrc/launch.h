@@ -15,6 +15,14 @@ constexpr int kDqChunkRows = 32;  // rows per sink-gradient partial of the bf16 
 bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// Query-head splits of a GQA group in the bf16 dK/dV kernel: 1 while the
+// grid of key tiles x batches x kv heads holds at least kDkdvMinGrid
+// workgroups, else the smallest divisor of G that reaches it (or G).
+constexpr int kDkdvKeyTile = 128;
+constexpr int kDkdvMinGrid = 1024;
+int dkdv_head_splits(int B, int S, int Hkv, int G);
+// dK / dV = sum over the splits of the partials, in split order (bf16 out).
+hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 
 bool fwd_f32_tiles(int dqk, int dv, int* bm, int* bn);

@@ -89,6 +89,35 @@ def test_workspace_sizes():
     assert binding.attn_bwd_workspace_size(P(B=0)) == 0
 
 
+def _expected_splits(B, S, Hkv, G, key_tile=128, min_grid=1024):
+    """Split rule for the bf16 dK/dV grid, written out independently."""
+    base = -(-S // key_tile) * B * Hkv
+    if base >= min_grid:
+        return 1
+    divisors = [d for d in range(2, G + 1) if G % d == 0]
+    reaching = [d for d in divisors if base * d >= min_grid]
+    return reaching[0] if reaching else (divisors[-1] if divisors else 1)
+
+
+@pytest.mark.parametrize("B,S,Hkv,G", [(4, 4096, 8, 4), (1, 16384, 1, 16), (32, 512, 1, 16), (1, 16384, 4, 4),
+                                       (16, 1024, 4, 4), (1, 128, 2, 2), (2, 4096, 128, 1), (1, 300, 3, 6),
+                                       (1, 1000, 1, 7)])
+def test_dkdv_head_splits_and_workspace(B, S, Hkv, G):
+    p = P(B=B, S=S, Hq=Hkv * G, Hkv=Hkv, d_qk=64, d_v=64)
+    ns = binding.host_dkdv_splits(p)
+    assert ns == _expected_splits(B, S, Hkv, G)
+    assert G % ns == 0
+    ws = binding.attn_bwd_workspace_size(p)
+    rows = B * Hkv * G * S
+    need = 2 * rows * 4 + (B * Hkv * G * -(-S // 32)) * 4
+    if ns > 1:
+        need += ns * B * S * Hkv * (64 + 64) * 4
+    assert ws >= need and ws % 256 == 0
+    # fp32 problems never split (their dK/dV kernel has no split path)
+    assert binding.host_dkdv_splits(P(B=B, S=S, Hq=Hkv * G, Hkv=Hkv, d_qk=64, d_v=64, dtype="f32")) == 1
+    assert binding.host_dkdv_splits(P(B=0)) == 0
+
+
 def _fwd(p, q=1, k=1, v=1, off=None, sl=None, o=1, lse=1):
     vp = lambda x: None if x is None else ctypes.c_void_p(0x1000 * x)
     lib = binding.load_library()
