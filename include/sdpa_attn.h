@@ -102,8 +102,9 @@ int attn_validate(const struct attn_params* p);
  * The forward needs none; the backward needs room for the per-row
  * delta = rowsum(dO * O) and LSE * log2(e), the per-block partial sums of
  * d(sink logit), and, for bf16 problems whose dK/dV grid is small (few KV
- * heads, short batches: attn_host_dkdv_splits > 1), fp32 partial dK and dV
- * of each query-head split of a GQA group. */
+ * heads, short batches) or whose dK/dV workgroups would walk many rows (long
+ * windows, large GQA groups) -- attn_host_dkdv_splits > 1 -- fp32 partial dK
+ * and dV of each query-head split of a GQA group. */
 size_t attn_fwd_workspace_size(const struct attn_params* p);
 size_t attn_bwd_workspace_size(const struct attn_params* p);
 
@@ -187,7 +188,9 @@ int attn_host_query_range(const struct attn_params* p, int32_t L, int32_t j0, in
                           int32_t* lo, int32_t* hi);
 
 /* Host: number of query-head splits of a GQA group the bf16 dK/dV stage
- * uses for this problem (1 = none; 0 if p is invalid).  With s > 1 splits,
+ * uses for this problem (1 = none; 0 if p is invalid): the smallest divisor
+ * s of G for which ceil(S/128)*B*Hkv*s >= 1024 and one workgroup walks at
+ * most 512 blocks of 32 query rows over its G/s heads (else G).  With s > 1 splits,
  * s workgroups per (128-key tile, batch, KV head) each walk G/s of the
  * group's query heads and write fp32 partials, which a second kernel adds in
  * split order, so dK and dV stay bitwise reproducible. */

@@ -50,7 +50,9 @@ size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->nu
 // bf16 dK/dV: query-head splits of a GQA group (fp32 partials in the workspace when > 1).
 int kv_splits(const attn_params* p) {
   if (p->dtype != ATTN_BF16) return 1;
-  return dkdv_head_splits(p->batch, p->seqlen, p->num_gqa_groups, p->num_heads / p->num_gqa_groups);
+  return dkdv_head_splits(p->batch, p->seqlen, p->num_gqa_groups, p->num_heads / p->num_gqa_groups,
+                          p->mask_type == ATTN_MASK_CAUSAL, normalise_window(p->window_left, p->seqlen),
+                          normalise_window(p->window_right, p->seqlen));
 }
 size_t kv_part_bytes(const attn_params* p) {
   const int ns = kv_splits(p);

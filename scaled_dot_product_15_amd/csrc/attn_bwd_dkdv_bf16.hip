@@ -511,16 +511,19 @@ static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int dkdv_head_splits(int B, int S, int Hkv, int G) {
+int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr) {
   const long long base = (long long)((S + kDkdvKeyTile - 1) / kDkdvKeyTile) * B * Hkv;
-  int splits = 1;
-  if (base < kDkdvMinGrid)
-    for (int d = 2; d <= G; ++d)
-      if (G % d == 0) {
-        splits = d;
-        if (base * d >= kDkdvMinGrid) break;
-      }
-  return splits;
+  // Most 32-row blocks one workgroup walks per query head: rows j0-wr ..
+  // j0+127+wl of a key tile (causal: from j0), in 64-row stages.
+  const long long before = causal ? 0 : (wr < 0 ? S : wr), after = wl < 0 ? S : wl;
+  long long span = before + kDkdvKeyTile + after;
+  if (span > S) span = S;
+  long long stages = (span + 63) / 64 + 1;
+  if (stages > (S + 63) / 64) stages = (S + 63) / 64;
+  auto fits = [&](int d) { return base * d >= kDkdvMinGrid && 2 * stages * (G / d) <= kDkdvMaxBlocks; };
+  for (int d = 1; d <= G; ++d)
+    if (G % d == 0 && fits(d)) return d;
+  return G;
 }
 
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream) {

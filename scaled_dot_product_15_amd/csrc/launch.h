@@ -15,12 +15,21 @@ constexpr int kDqChunkRows = 32;  // rows per sink-gradient partial of the bf16 
 bool fwd_bf16_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
-// Query-head splits of a GQA group in the bf16 dK/dV kernel: 1 while the
-// grid of key tiles x batches x kv heads holds at least kDkdvMinGrid
-// workgroups, else the smallest divisor of G that reaches it (or G).
+// Query-head splits of a GQA group in the bf16 dK/dV kernel: the smallest
+// divisor d of G for which the grid of key tiles x batches x kv heads x d
+// holds at least kDkdvMinGrid workgroups and one workgroup walks at most
+// kDkdvMaxBlocks 32-row blocks (long workgroups leave a tail of idle CUs);
+// G if none does.  wl, wr: windows normalised to -1 or < S.
 constexpr int kDkdvKeyTile = 128;
-constexpr int kDkdvMinGrid = 1024;
-int dkdv_head_splits(int B, int S, int Hkv, int G);
+#ifndef SDPA_DKDV_MIN_GRID
+#define SDPA_DKDV_MIN_GRID 1024
+#endif
+#ifndef SDPA_DKDV_MAX_BLOCKS
+#define SDPA_DKDV_MAX_BLOCKS 512
+#endif
+constexpr int kDkdvMinGrid = SDPA_DKDV_MIN_GRID;
+constexpr long long kDkdvMaxBlocks = SDPA_DKDV_MAX_BLOCKS;
+int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr);
 // dK / dV = sum over the splits of the partials, in split order (bf16 out).
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);

@@ -54,7 +54,9 @@ def test_tile_map_bitexact_at_kernel_tiles(causal, wl, wr, S):
     gc.log(f"S={S} mask={causal, wl, wr}: {visited} non-skipped tiles")
 
 
-@pytest.mark.parametrize("cfg,case", [(2, 0), (5, 1), (4, 0)])
+# (5, 1), (3, 11) and (3, 17) split each GQA group's query heads over 2, 4 and
+# 16 dK/dV workgroups (fp32 partials added in split order).
+@pytest.mark.parametrize("cfg,case", [(2, 0), (5, 1), (4, 0), (3, 11), (3, 17)])
 def test_backward_bitwise_reproducible(cfg, case):
     import torch
     p = inputs.workload_configs()[cfg][case]
