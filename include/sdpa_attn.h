@@ -190,7 +190,8 @@ int attn_host_query_range(const struct attn_params* p, int32_t L, int32_t j0, in
 /* Host: number of query-head splits of a GQA group the bf16 dK/dV stage
  * uses for this problem (1 = none; 0 if p is invalid): the smallest divisor
  * s of G for which ceil(S/128)*B*Hkv*s >= 1024 and one workgroup walks at
- * most 512 blocks of 32 query rows over its G/s heads (else G).  With s > 1 splits,
+ * most 512 blocks of 32 query rows over its G/s heads (else G), lowered to
+ * the largest divisor whose fp32 partials take at most 1 GiB.  With s > 1 splits,
  * s workgroups per (128-key tile, batch, KV head) each walk G/s of the
  * group's query heads and write fp32 partials, which a second kernel adds in
  * split order, so dK and dV stay bitwise reproducible. */

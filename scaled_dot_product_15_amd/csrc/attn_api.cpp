@@ -52,7 +52,7 @@ int kv_splits(const attn_params* p) {
   if (p->dtype != ATTN_BF16) return 1;
   return dkdv_head_splits(p->batch, p->seqlen, p->num_gqa_groups, p->num_heads / p->num_gqa_groups,
                           p->mask_type == ATTN_MASK_CAUSAL, normalise_window(p->window_left, p->seqlen),
-                          normalise_window(p->window_right, p->seqlen));
+                          normalise_window(p->window_right, p->seqlen), p->head_dim_qk, p->head_dim_v);
 }
 size_t kv_part_bytes(const attn_params* p) {
   const int ns = kv_splits(p);

@@ -511,7 +511,7 @@ static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr) {
+int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, int dqk, int dv) {
   const long long base = (long long)((S + kDkdvKeyTile - 1) / kDkdvKeyTile) * B * Hkv;
   // Most 32-row blocks one workgroup walks per query head: rows j0-wr ..
   // j0+127+wl of a key tile (causal: from j0), in 64-row stages.
@@ -521,9 +521,18 @@ int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr) 
   long long stages = (span + 63) / 64 + 1;
   if (stages > (S + 63) / 64) stages = (S + 63) / 64;
   auto fits = [&](int d) { return base * d >= kDkdvMinGrid && 2 * stages * (G / d) <= kDkdvMaxBlocks; };
+  int want = G;
   for (int d = 1; d <= G; ++d)
-    if (G % d == 0 && fits(d)) return d;
-  return G;
+    if (G % d == 0 && fits(d)) {
+      want = d;
+      break;
+    }
+  // The fp32 partials must stay within kDkdvMaxPartialBytes: else the
+  // largest divisor below the wanted count that does.
+  const long long per_split = (long long)B * S * Hkv * (dqk + dv) * 4;
+  for (int d = want; d > 1; --d)
+    if (G % d == 0 && per_split * d <= kDkdvMaxPartialBytes) return d;
+  return 1;
 }
 
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream) {

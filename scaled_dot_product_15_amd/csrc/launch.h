@@ -19,7 +19,9 @@ hipError_t launch_bwd_dkdv_bf16(const KArgs& a, int dqk, int dv, hipStream_t str
 // divisor d of G for which the grid of key tiles x batches x kv heads x d
 // holds at least kDkdvMinGrid workgroups and one workgroup walks at most
 // kDkdvMaxBlocks 32-row blocks (long workgroups leave a tail of idle CUs);
-// G if none does.  wl, wr: windows normalised to -1 or < S.
+// G if none does; then lowered to the largest divisor whose fp32 partials
+// fit in kDkdvMaxPartialBytes (1 if none).  wl, wr: windows normalised to
+// -1 or < S.
 constexpr int kDkdvKeyTile = 128;
 #ifndef SDPA_DKDV_MIN_GRID
 #define SDPA_DKDV_MIN_GRID 1024
@@ -29,7 +31,8 @@ constexpr int kDkdvKeyTile = 128;
 #endif
 constexpr int kDkdvMinGrid = SDPA_DKDV_MIN_GRID;
 constexpr long long kDkdvMaxBlocks = SDPA_DKDV_MAX_BLOCKS;
-int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr);
+constexpr long long kDkdvMaxPartialBytes = 1ll << 30;
+int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, int dqk, int dv);
 // dK / dV = sum over the splits of the partials, in split order (bf16 out).
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);

@@ -89,26 +89,29 @@ def test_workspace_sizes():
     assert binding.attn_bwd_workspace_size(P(B=0)) == 0
 
 
-def _expected_splits(B, S, Hkv, G, causal=True, wl=-1, wr=-1, key_tile=128, min_grid=1024, max_blocks=512):
+def _expected_splits(B, S, Hkv, G, causal=True, wl=-1, wr=-1, key_tile=128, min_grid=1024, max_blocks=512,
+                     dims=128, max_partial=1 << 30):
     """Split rule for the bf16 dK/dV grid, written out independently: the
     smallest divisor d of G giving at least min_grid workgroups whose longest
-    walk (32-row blocks over G/d heads) is at most max_blocks; else G."""
+    walk (32-row blocks over G/d heads) is at most max_blocks (else G), then
+    the largest divisor not above it whose fp32 partials fit max_partial."""
     wl = -1 if (wl < 0 or wl >= S) else wl
     wr = -1 if (wr < 0 or wr >= S) else wr
     base = -(-S // key_tile) * B * Hkv
     rows = min(S, (0 if causal else (S if wr < 0 else wr)) + key_tile + (S if wl < 0 else wl))
     stages = min(-(-rows // 64) + 1, -(-S // 64))
-    for d in range(1, G + 1):
-        if G % d == 0 and base * d >= min_grid and 2 * stages * (G // d) <= max_blocks:
-            return d
-    return G
+    want = next((d for d in range(1, G + 1)
+                 if G % d == 0 and base * d >= min_grid and 2 * stages * (G // d) <= max_blocks), G)
+    per_split = B * S * Hkv * dims * 4
+    return next((d for d in range(want, 1, -1) if G % d == 0 and per_split * d <= max_partial), 1)
 
 
 @pytest.mark.parametrize("B,S,Hkv,G,causal,win", [
     (4, 4096, 8, 4, True, (1024, 0)), (1, 16384, 1, 16, True, (-1, -1)), (32, 512, 1, 16, True, (-1, -1)),
     (1, 16384, 4, 4, True, (-1, -1)), (16, 1024, 4, 4, True, (-1, -1)), (1, 128, 2, 2, True, (-1, -1)),
     (2, 4096, 128, 1, True, (-1, -1)), (1, 300, 3, 6, False, (-1, -1)), (1, 1000, 1, 7, False, (100, 50)),
-    (4, 8192, 8, 4, True, (4096, 0)), (2, 4096, 4, 8, False, (-1, 0))])
+    (4, 8192, 8, 4, True, (4096, 0)), (2, 4096, 4, 8, False, (-1, 0)), (8, 65536, 8, 8, True, (-1, -1)),
+    (2, 65536, 2, 8, True, (-1, -1))])
 def test_dkdv_head_splits_and_workspace(B, S, Hkv, G, causal, win):
     p = P(B=B, S=S, Hq=Hkv * G, Hkv=Hkv, d_qk=64, d_v=64, attn_mask_type="causal" if causal else "no_mask",
           window_size=win)
