@@ -11,7 +11,7 @@ import numpy as np
 import oracle
 from scaled_dot_product_15_amd import binding, inputs
 
-# Tolerances (per the stated spec bar): fp32 max-abs 1e-4 on O and
+# Tolerances (the accuracy bar this path is held to): fp32 max-abs 1e-4 on O and
 # 1e-3 on gradients; bf16 (fp32 accumulation) max-abs 2e-2 on O and
 # relative L2 3e-2 on dQ, dK, dV and d(softmax offset).
 TOL = {
