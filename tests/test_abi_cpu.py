@@ -169,6 +169,18 @@ def test_bwd_argument_errors():
     assert _bwd(P(), ws=0x100010) == -1  # workspace must be 256-byte aligned
 
 
+def test_bwd_stage_rejects_unknown_stages():
+    # Checked before anything else: no launch is reached with these stage values.
+    lib = binding.load_library()
+    p = P()
+    vp = ctypes.c_void_p
+    for stage in (0, -1, 5, 99):
+        rc = lib.attn_bwd_stage(stage, ctypes.byref(p), *(vp(0x1000) for _ in range(6)), None, None,
+                                *(vp(0x1000) for _ in range(3)), None, vp(0x100000),
+                                binding.attn_bwd_workspace_size(p), None)
+        assert rc == -1, stage
+
+
 def test_status_strings():
     for rc in (0, -1, -2, -3, -4, 7):
         assert isinstance(binding.attn_status_string(rc), str)
