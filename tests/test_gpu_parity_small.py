@@ -59,3 +59,24 @@ def test_config1_tiny_fp32():
     g = gc.run_gpu(p, t)
     stats = gc.compare_full(p, t, g, gc.oracle_full(p, t), tag="config1")
     gc.log(f"  {stats}")
+
+
+# Degenerate shapes: one token, a diagonal-only window (every row sees only
+# itself, so O = V row and P = 1), a (0, 0) window without the causal mask, and
+# lengths that end one row into a new tile.
+DEGENERATE = list(itertools.product((1, 2, 65), ("diag", "diag_nc", "causal"), SOFTMAX,
+                                    ("bf16_128", "f32_64")))
+DEG_MASKS = {"diag": (True, (0, 0)), "diag_nc": (False, (0, 0)), "causal": (True, (-1, -1))}
+
+
+@pytest.mark.parametrize("S,mask,st,dims", DEGENERATE, ids=lambda x: str(x))
+def test_degenerate_shapes(S, mask, st, dims):
+    dtype, dqk, dv = DIMS[dims]
+    causal, win = DEG_MASKS[mask]
+    p = inputs.Problem(B=2, S=S, Hq=4, Hkv=2, d_qk=dqk, d_v=dv, dtype=dtype, causal=causal, window=win,
+                       softmax_type=st)
+    seed = 40_000 + DEGENERATE.index((S, mask, st, dims))
+    t = inputs.to_torch(inputs.draw(p, seed), dtype, "cuda")
+    gc.log(f"degenerate S={S} {mask} {st} {dims} seed={seed}")
+    g = gc.run_gpu(p, t)
+    gc.compare_full(p, t, g, gc.oracle_full(p, t), tag=f"S={S}/{mask}/{st}/{dims}")
