@@ -6,6 +6,6 @@ from it and shares none of its code.
 """
 from .sdpa_oracle import (  # noqa: F401
     LEARNABLE, OFF_BY_ONE, SOFTMAX_TYPES, VANILLA, attention, attention_group, attention_keys,
-    attention_rows, visible_rows,
+    attention_packed, attention_rows, packed_visible_mask, visible_rows,
     effective_flops, kv_head, sink_logit, visible_mask, visible_pairs,
 )

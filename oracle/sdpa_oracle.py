@@ -324,3 +324,99 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
             dk += scale * (ds.T @ qh)
             dvv += p.T @ doh
     return {"dk": dk, "dv": dvv}
+
+
+def packed_visible_mask(seq_offsets, seqlens, T: int, causal: bool, window_left: int,
+                        window_right: int) -> np.ndarray:
+    """Boolean [T, T] over the packed token axis: True where token t may attend to token u.
+
+    Packed (THD) inputs: the TE single-GPU page, section 1, lets the sequence
+    descriptor carry segment boundaries and padding metadata for packed
+    sequences.  Reading taken: segment b holds tokens seq_offsets[b] ..
+    seq_offsets[b+1]-1, of which the first seqlens[b] are valid (all of them
+    when seqlens is None) and the rest padding.  Token t may attend to token u
+    iff both lie in the same segment, both are valid, and their positions
+    inside the segment satisfy the causal and window rules.  Tokens outside
+    every segment see nothing and are seen by nothing.
+    """
+    off = np.asarray(seq_offsets, dtype=np.int64).reshape(-1)
+    B = off.size - 1
+    seg = np.full(T, -1, dtype=np.int64)
+    pos = np.zeros(T, dtype=np.int64)
+    valid = np.zeros(T, dtype=bool)
+    for b in range(B):
+        n = int(off[b + 1] - off[b])
+        L = n if seqlens is None else min(int(np.asarray(seqlens).reshape(-1)[b]), n)
+        seg[off[b]:off[b + 1]] = b
+        pos[off[b]:off[b + 1]] = np.arange(n)
+        valid[off[b]:off[b] + L] = True
+    same = (seg[:, None] == seg[None, :]) & (seg[:, None] >= 0)
+    m = same & valid[:, None] & valid[None, :]
+    pi, pj = pos[:, None], pos[None, :]
+    if causal:
+        m &= pj <= pi
+    if window_left >= 0:
+        m &= pj >= pi - window_left
+    if window_right >= 0:
+        m &= pj <= pi + window_right
+    return m
+
+
+def attention_packed(q, k, v, d_o=None, *, seq_offsets, max_seqlen, seqlens=None,
+                     num_gqa_groups=None, causal=True, window=(-1, -1), scale_factor=None,
+                     softmax_type=VANILLA, softmax_offset=None):
+    """Oracle for packed (THD) inputs: one attention over the whole token axis.
+
+    q [T,Hq,dqk], k [T,Hkv,dqk], v [T,Hkv,dv], d_o [T,Hq,dv]; the segments
+    and their valid lengths come from seq_offsets [B+1] and seqlens [B] (see
+    packed_visible_mask).  The T x T score matrix of each head is masked
+    block-diagonally, then softmax (+ sink), attend and the gradients follow
+    the same definitions as attention_group.  Returns o [T,Hq,dv],
+    lse [B,Hq,max_seqlen] (row i of segment b; rows past the segment or its
+    valid length are empty: -inf for vanilla, the sink logit otherwise), and
+    with d_o: dq, dk, dv on the token axis and dalpha [Hq] (None for vanilla).
+    Tokens outside every segment get zeros.
+    """
+    T, Hq, dqk = q.shape
+    Hkv = k.shape[1] if num_gqa_groups is None else int(num_gqa_groups)
+    if k.shape != (T, Hkv, dqk) or v.shape[:2] != (T, Hkv) or Hq % Hkv:
+        raise ValueError("K/V shapes do not match Q and num_gqa_groups")
+    dv_dim = v.shape[2]
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    off = np.asarray(seq_offsets, dtype=np.int64).reshape(-1)
+    B = off.size - 1
+    mask = packed_visible_mask(off, seqlens, T, causal, int(window[0]), int(window[1]))
+    grads = d_o is not None
+    res = {"o": np.zeros((T, Hq, dv_dim)), "lse": np.zeros((B, Hq, max_seqlen))}
+    if grads:
+        res.update(dq=np.zeros((T, Hq, dqk)), dk=np.zeros((T, Hkv, dqk)),
+                   dv=np.zeros((T, Hkv, dv_dim)), dalpha=np.zeros(Hq))
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        z = sink_logit(softmax_type, softmax_offset, h)
+        qh = np.asarray(q[:, h, :], dtype=np.float64)
+        kg = np.asarray(k[:, g, :], dtype=np.float64)
+        vg = np.asarray(v[:, g, :], dtype=np.float64)
+        s = scale * (qh @ kg.T)
+        p, lse_t = _softmax_rows(s, mask, z)
+        o = p @ vg
+        res["o"][:, h, :] = o
+        empty = -np.inf if z is None else z
+        res["lse"][:, h, :] = empty
+        for b in range(B):
+            n = min(int(off[b + 1] - off[b]), max_seqlen)
+            res["lse"][b, h, :n] = lse_t[off[b]:off[b] + n]
+        if not grads:
+            continue
+        doh = np.asarray(d_o[:, h, :], dtype=np.float64)
+        delta = (doh * o).sum(axis=1)
+        ds = p * (doh @ vg.T - delta[:, None])
+        res["dq"][:, h, :] = scale * (ds @ kg)
+        res["dk"][:, g, :] += scale * (ds.T @ qh)
+        res["dv"][:, g, :] += p.T @ doh
+        if z is not None:
+            lse_safe = np.where(np.isfinite(lse_t), lse_t, z)
+            res["dalpha"][h] = -(np.exp(z - lse_safe) * delta).sum()
+    if grads and softmax_type == VANILLA:
+        res["dalpha"] = None
+    return res

@@ -28,6 +28,10 @@ What pins what:
                    with autograd: O, dQ, dK, dV and, through an additive mask
                    column, d(alpha)
   golden           hand-derived closed forms stored under tests/golden/
+  packed_*         packed (THD) oracle: scalar loops over each segment's
+                   tokens; equality with the padded per-batch oracle (a
+                   different formulation: block-diagonal mask over the token
+                   axis vs one S x S problem per batch); finite differences
 """
 from __future__ import annotations
 
@@ -505,7 +509,137 @@ def pin_sampled_keys(orc):
                             _close(got[n, d], (lp - lm) / (2 * h_fd), 1e-6, 1e-8, f"keys d{name} {ci} {st}")
 
 
+# ---- packed (THD) inputs ---------------------------------------------------
+#
+# Segments b = 0 .. B-1 occupy tokens off[b] .. off[b+1]-1 of the packed axis;
+# the first seqlens[b] of them are valid.  Cases: segments of unequal size,
+# one with padding inside, one empty, and tokens past the last segment.
+PACKED_CASES = [
+    # offsets, seqlens, T, causal, window
+    ([0, 5, 12, 12, 16], [5, 4, 0, 4], 18, True, (-1, -1)),
+    ([0, 7, 9], None, 9, False, (2, 1)),
+    ([0, 3, 11], [3, 6], 11, True, (2, 0)),
+]
+
+
+def _packed_case(seed, T, B, Hq=4, Hkv=2, dqk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, Hq, dqk)), rng.standard_normal((T, Hkv, dqk)),
+            rng.standard_normal((T, Hkv, dv)), rng.standard_normal((T, Hq, dv)), rng.standard_normal(Hq))
+
+
+def pin_packed_brute_force(orc):
+    """Packed forward vs scalar loops that walk each segment's tokens directly."""
+    for ci, (off, sl, T, causal, (wl, wr)) in enumerate(PACKED_CASES):
+        B = len(off) - 1
+        S = max(off[b + 1] - off[b] for b in range(B))
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = _packed_case(1500 + ci, T, B)
+            Hq, Hkv, dv = q.shape[1], k.shape[1], v.shape[2]
+            r = orc.attention_packed(q, k, v, None, seq_offsets=np.array(off), max_seqlen=S,
+                                     seqlens=None if sl is None else np.array(sl), num_gqa_groups=Hkv,
+                                     causal=causal, window=(wl, wr), scale_factor=0.45, softmax_type=st,
+                                     softmax_offset=alpha)
+            o = np.zeros((T, Hq, dv))
+            lse = np.zeros((B, Hq, S))
+            for b in range(B):
+                n = off[b + 1] - off[b]
+                L = n if sl is None else min(sl[b], n)
+                for h in range(Hq):
+                    g = h // (Hq // Hkv)
+                    for i in range(S):
+                        den, num = 0.0, [0.0] * dv
+                        for j in range(L if i < L else 0):
+                            if (causal and j > i) or (wl >= 0 and j < i - wl) or (wr >= 0 and j > i + wr):
+                                continue
+                            e = math.exp(0.45 * sum(q[off[b] + i, h, d] * k[off[b] + j, g, d] for d in range(q.shape[2])))
+                            den += e
+                            for d in range(dv):
+                                num[d] += e * v[off[b] + j, g, d]
+                        if st == "off_by_one":
+                            den += 1.0
+                        elif st == "learnable":
+                            den += math.exp(alpha[h])
+                        lse[b, h, i] = math.log(den) if den > 0 else -math.inf
+                        if i < n:
+                            o[off[b] + i, h, :] = [x / den if den > 0 else 0.0 for x in num]
+            _close(r["o"], o, 1e-12, 1e-14, f"packed O case{ci} {st}")
+            _close(r["lse"], lse, 1e-12, 1e-14, f"packed LSE case{ci} {st}")
+
+
+def pin_packed_equals_padded(orc):
+    """Packed (block-diagonal mask over the token axis) == padded BSHD per batch.
+
+    The two oracle paths are different formulations of the same function:
+    scattering each segment into row b of a [B, S, ...] tensor with
+    seqlens[b] valid rows must give identical outputs and gradients."""
+    for ci, (off, sl, T, causal, win) in enumerate(PACKED_CASES):
+        B = len(off) - 1
+        S = max(off[b + 1] - off[b] for b in range(B))
+        lens = [min(off[b + 1] - off[b], S if sl is None else sl[b]) for b in range(B)]
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = _packed_case(1600 + ci, T, B)
+
+            def pad(x):
+                y = np.zeros((B, S) + x.shape[1:])
+                for b in range(B):
+                    y[b, :off[b + 1] - off[b]] = x[off[b]:off[b + 1]]
+                return y
+
+            kw = dict(num_gqa_groups=k.shape[1], causal=causal, window=win, scale_factor=0.7,
+                      softmax_type=st, softmax_offset=alpha)
+            rp = orc.attention_packed(q, k, v, do, seq_offsets=np.array(off), max_seqlen=S,
+                                      seqlens=None if sl is None else np.array(sl), **kw)
+            rb = orc.attention(pad(q), pad(k), pad(v), pad(do), seqlens=np.array(lens), **kw)
+            for name in ("o", "dq", "dk", "dv"):
+                _close(pad(rp[name]), rb[name], 1e-12, 1e-14, f"packed vs padded {name} case{ci} {st}")
+                outside = np.ones(T, dtype=bool)
+                outside[off[0]:off[-1]] = False
+                assert not rp[name][outside].any(), f"tokens outside segments written: {name}"
+            _close(rp["lse"], rb["lse"], 1e-12, 1e-14, f"packed vs padded lse case{ci} {st}")
+            if st == "vanilla":
+                assert rp["dalpha"] is None
+            else:
+                _close(rp["dalpha"], rb["dalpha"], 1e-12, 1e-14, f"packed vs padded dalpha case{ci} {st}")
+
+
+def pin_packed_finite_diff(orc):
+    """Packed dQ, dK, dV, d(alpha) vs central differences of sum(dO * O)."""
+    hstep = 1e-6
+    off, sl, T = [0, 3, 7], [3, 3], 8
+    for st in orc.SOFTMAX_TYPES:
+        q, k, v, do, alpha = _packed_case(1700, T, 2, dqk=2, dv=2)
+        kw = dict(seq_offsets=np.array(off), max_seqlen=4, seqlens=np.array(sl), num_gqa_groups=2,
+                  causal=True, window=(1, 0), scale_factor=0.8, softmax_type=st)
+
+        def loss(qq, kk, vv, al):
+            return float((orc.attention_packed(qq, kk, vv, None, softmax_offset=al, **kw)["o"] * do).sum())
+
+        r = orc.attention_packed(q, k, v, do, softmax_offset=alpha, **kw)
+        for name, arr, grad in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                a0 = arr[idx]
+                arr[idx] = a0 + hstep
+                lp = loss(q, k, v, alpha)
+                arr[idx] = a0 - hstep
+                lm = loss(q, k, v, alpha)
+                arr[idx] = a0
+                fd[idx] = (lp - lm) / (2 * hstep)
+            _close(grad, fd, 1e-6, 1e-8, f"packed d{name} {st}")
+        if st == "learnable":
+            fd = np.zeros(alpha.size)
+            for hh in range(alpha.size):
+                a2 = alpha.copy()
+                a2[hh] += hstep
+                lp = loss(q, k, v, a2)
+                a2[hh] -= 2 * hstep
+                lm = loss(q, k, v, a2)
+                fd[hh] = (lp - lm) / (2 * hstep)
+            _close(r["dalpha"], fd, 1e-6, 1e-8, "packed dalpha")
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
             pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
-            pin_sampled_keys]
+            pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff]

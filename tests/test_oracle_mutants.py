@@ -34,13 +34,18 @@ MUTANTS = {
                          "lse = np.where(l > 0, np.log(l), -np.inf)")],
     "dz_sign_flip": [('out["dz"][gi] = -(np.exp(z - lse_safe) * delta).sum()',
                       'out["dz"][gi] = (np.exp(z - lse_safe) * delta).sum()')],
-    "default_scale_uses_dv": [("scale = (1.0 / math.sqrt(dqk))", "scale = (1.0 / math.sqrt(v.shape[3]))")],
+    "default_scale_uses_dv": [("scale = (1.0 / math.sqrt(dqk))", "scale = (1.0 / math.sqrt(v.shape[-1]))", "all")],
     "sink_logit_scaled": [("z = sink_logit(softmax_type, softmax_offset, h)\n        s = scale * (qh @ kb.T)",
                            "z = sink_logit(softmax_type, softmax_offset, h)\n"
                            "        z = None if z is None else z * scale\n        s = scale * (qh @ kb.T)")],
     "rows_dq_missing_scale": [("dq = scale * (ds @ kb)\n", "dq = ds @ kb\n")],
     "rows_window_off_by_one": [("m = m & (j >= i - window_left)", "m = m & (j > i - window_left)")],
     "keys_dk_missing_scale": [("dk += scale * (ds.T @ qh)", "dk += ds.T @ qh")],
+    "packed_segments_leak": [("same = (seg[:, None] == seg[None, :]) & (seg[:, None] >= 0)",
+                              "same = (seg[:, None] >= 0) & (seg[None, :] >= 0)")],
+    "packed_padding_ignored": [("valid[off[b]:off[b] + L] = True", "valid[off[b]:off[b + 1]] = True")],
+    "packed_lse_shifted_rows": [('res["lse"][b, h, :n] = lse_t[off[b]:off[b] + n]',
+                                 'res["lse"][b, h, :n] = lse_t[b:b + n]')],
     "keys_rows_subset": [("rows_all = np.nonzero(sees.any(axis=1))[0]",
                           "rows_all = np.nonzero(sees.any(axis=1))[0][1:]")],
 }
@@ -51,7 +56,8 @@ ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_ca
          oracle_pins.pin_gqa_repeat, oracle_pins.pin_padding, oracle_pins.pin_scale,
          oracle_pins.pin_dalpha_forms, oracle_pins.pin_sink_augmented,
          oracle_pins.pin_torch_sdpa, oracle_pins.pin_finite_diff, oracle_pins.pin_sampled_rows,
-         oracle_pins.pin_sampled_keys]
+         oracle_pins.pin_sampled_keys, oracle_pins.pin_packed_brute_force,
+         oracle_pins.pin_packed_equals_padded, oracle_pins.pin_packed_finite_diff]
 
 
 def _mutant(edits):
