@@ -39,6 +39,18 @@
  *   - Layouts (BSHD): Q, dQ [B,S,Hq,Dqk]; K, dK [B,S,Hkv,Dqk]; V, dV [B,S,Hkv,Dv];
  *     O, dO [B,S,Hq,Dv]; LSE [B,Hq,S] float32; softmax_offset and
  *     d_softmax_offset [Hq] float32; seqlens [B] int32.
+ *   - Packed layout (THD), selected by a non-NULL seq_offsets [B+1] int32:
+ *     the sequences lie back to back along one token axis, Q, dQ [T,Hq,Dqk];
+ *     K, dK [T,Hkv,Dqk]; V, dV [T,Hkv,Dv]; O, dO [T,Hq,Dv] with
+ *     T >= seq_offsets[B].  Segment b holds tokens seq_offsets[b] ..
+ *     seq_offsets[b+1]-1 (0 = seq_offsets[0] <= seq_offsets[1] <= ..., each
+ *     segment at most S = params.seqlen tokens); the first seqlens[b] of them
+ *     are valid (all of them when seqlens is NULL) and the rest are padding.
+ *     Attention never crosses a segment; positions for the causal and window
+ *     rules count from the segment start.  LSE keeps the [B,Hq,S] layout
+ *     (row i of segment b).  Tokens at or past seq_offsets[B] are not
+ *     touched.  This follows the sequence descriptor of the TE single-GPU
+ *     page, section 1: lengths plus, for packed inputs, segment boundaries.
  *   - Element type of Q,K,V,O,dO,dQ,dK,dV is params.dtype (bf16 or f32).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream); the
  *     calls return without synchronising.  Inputs are read only.  Outputs are
@@ -46,8 +58,9 @@
  *   - All argument checks run on the host before anything is enqueued; on a
  *     non-zero return nothing was launched, except ATTN_ERR_HIP which reports
  *     a launch failure.
- *   - seqlens values live on the device and cannot be checked on the host;
- *     kernels clamp them to [0, S].  The Python binding checks them.
+ *   - seqlens and seq_offsets values live on the device and cannot be
+ *     checked on the host; kernels clamp lengths and segment sizes to [0, S].
+ *     The Python binding checks them.
  */
 #ifndef SDPA_ATTN_H
 #define SDPA_ATTN_H
@@ -108,14 +121,17 @@ int attn_validate(const struct attn_params* p);
 size_t attn_fwd_workspace_size(const struct attn_params* p);
 size_t attn_bwd_workspace_size(const struct attn_params* p);
 
-/* Forward.  Writes O [B,S,Hq,Dv] and LSE [B,Hq,S].
+/* Forward.  Writes O [B,S,Hq,Dv] (packed: [T,Hq,Dv]) and LSE [B,Hq,S].
  *   softmax_offset: [Hq] float32 sink logits; required for LEARNABLE,
  *                   ignored otherwise (may be NULL).
- *   seqlens:        [B] int32 valid lengths, or NULL for all S.
+ *   seqlens:        [B] int32 valid lengths, or NULL for all S (packed: the
+ *                   whole segment).
+ *   seq_offsets:    [B+1] int32 segment starts of packed (THD) tensors, or
+ *                   NULL for BSHD.
  *   workspace:      may be NULL when workspace_bytes >= attn_fwd_workspace_size. */
 int attn_fwd(const struct attn_params* p, const void* q, const void* k, const void* v,
-             const float* softmax_offset, const int32_t* seqlens, void* o, float* lse,
-             void* workspace, size_t workspace_bytes, void* stream);
+             const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets,
+             void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of the forward above for upstream gradient d_o (PR #2225 backward:
  * grad_q, grad_k, grad_v, grad_softmax_offset).  o and lse must be the
@@ -124,13 +140,14 @@ int attn_fwd(const struct attn_params* p, const void* q, const void* k, const vo
  *     over batches and rows.  Required for LEARNABLE; optional for OFF_BY_ONE
  *     (gradient w.r.t. the implicit zero logit); must be NULL for VANILLA.
  *   workspace: at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
+ *   seqlens, seq_offsets: as for attn_fwd, and the same values.
  * dK/dV accumulate the query heads of a GQA group in a fixed order, and dQ and
  * d_softmax_offset are reduced in a fixed order: results are bitwise
  * reproducible run to run. */
 int attn_bwd(const struct attn_params* p, const void* q, const void* k, const void* v,
              const void* o, const void* d_o, const float* lse, const float* softmax_offset,
-             const int32_t* seqlens, void* dq, void* dk, void* dv, float* d_softmax_offset,
-             void* workspace, size_t workspace_bytes, void* stream);
+             const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
+             float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of attn_bwd, same arguments and checks as attn_bwd.  attn_bwd
  * runs the stages 1..4 in order on one stream; each stage needs the ones
@@ -149,8 +166,8 @@ int attn_bwd(const struct attn_params* p, const void* q, const void* k, const vo
 #define ATTN_BWD_STAGE_OFFSET_GRAD 4
 int attn_bwd_stage(int stage, const struct attn_params* p, const void* q, const void* k, const void* v,
                    const void* o, const void* d_o, const float* lse, const float* softmax_offset,
-                   const int32_t* seqlens, void* dq, void* dk, void* dv, float* d_softmax_offset,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
+                   float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

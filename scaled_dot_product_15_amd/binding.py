@@ -44,12 +44,12 @@ EXPORTS = {
     "attn_validate": (ctypes.c_int, [ctypes.POINTER(Params)]),
     "attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
-    "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]),
-    "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_bwd_stage": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp,
-                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_tile_shape": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32)]),
@@ -139,13 +139,53 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type):
+def _packed_layout(q, seq_offsets, seqlens, max_seqlen):
+    """Host checks of packed (THD) segment metadata; returns (B, S).
+
+    seq_offsets [B+1] int32 on the device: 0 = off[0] <= off[1] <= ... <=
+    off[B] <= T.  S = max_seqlen, or the largest segment when None; every
+    segment must fit in S tokens and every seqlens[b] in its segment.
+    """
     torch = _torch()
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be BSHD tensors")
-    B, S, Hq, dqk = q.shape
-    Hkv = k.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
-    if tuple(k.shape) != (B, S, Hkv, dqk) or tuple(v.shape[:3]) != (B, S, Hkv):
+    if seq_offsets.dtype != torch.int32 or seq_offsets.dim() != 1 or seq_offsets.numel() < 2 \
+            or not seq_offsets.is_cuda:
+        raise ValueError("seq_offsets must be an int32 device tensor of shape [B+1]")
+    off = seq_offsets.cpu().to(torch.int64)
+    sizes = off[1:] - off[:-1]
+    if int(off[0]) != 0 or bool((sizes < 0).any()) or int(off[-1]) > q.shape[0]:
+        raise ValueError("seq_offsets must start at 0, not decrease and end at or below T")
+    S = int(sizes.max()) if max_seqlen is None else int(max_seqlen)
+    S = max(S, 1)
+    if bool((sizes > S).any()):
+        raise ValueError(f"a segment holds more than max_seqlen = {S} tokens")
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or seqlens.numel() != sizes.numel() or not seqlens.is_cuda:
+            raise ValueError("seqlens must be an int32 device tensor of shape [B]")
+        sl = seqlens.cpu().to(torch.int64)
+        if bool((sl < 0).any()) or bool((sl > sizes).any()):
+            raise ValueError("seqlens values must lie in [0, segment size]")
+    return int(sizes.numel()), S
+
+
+def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
+             packed=None):
+    """Params for BSHD tensors, or for packed [T, H, D] tensors when
+    packed = (B, S) comes from _packed_layout."""
+    torch = _torch()
+    if packed is None:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("q, k, v must be BSHD tensors (or pass seq_offsets for packed THD)")
+        B, S, Hq, dqk = q.shape
+        Hkv = k.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+        lead = (B, S)
+    else:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("packed q, k, v must be [T, heads, dim] tensors")
+        B, S = packed
+        T, Hq, dqk = q.shape
+        Hkv = k.shape[1] if num_gqa_groups is None else int(num_gqa_groups)
+        lead = (T,)
+    if tuple(k.shape) != lead + (Hkv, dqk) or tuple(v.shape[:-1]) != lead + (Hkv,):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
@@ -153,7 +193,7 @@ def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor,
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("dtype must be bfloat16 or float32")
     dtype = "bf16" if q.dtype == torch.bfloat16 else "f32"
-    return make_params(B, S, Hq, Hkv, dqk, v.shape[3], dtype, attn_mask_type, window_size,
+    return make_params(B, S, Hq, Hkv, dqk, v.shape[-1], dtype, attn_mask_type, window_size,
                        scale_factor, softmax_type)
 
 
@@ -169,14 +209,29 @@ def _check_seqlens(seqlens, B, S):
     return seqlens
 
 
+def _layout(q, seq_offsets, seqlens, max_seqlen):
+    """(B, S) of packed inputs (host-checked), or None for BSHD."""
+    if seq_offsets is None:
+        if max_seqlen is not None:
+            raise ValueError("max_seqlen applies to packed inputs (seq_offsets) only")
+        return None
+    return _packed_layout(q, seq_offsets, seqlens, max_seqlen)
+
+
 def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_size=(-1, -1),
              scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None,
-             out=None, lse=None, stream=None, check_seqlens=True):
-    """Forward attention on BSHD device tensors.  Returns (O [B,S,Hq,Dv], LSE [B,Hq,S])."""
+             seq_offsets=None, max_seqlen=None, out=None, lse=None, stream=None, check_seqlens=True):
+    """Forward attention.  Returns (O, LSE [B,Hq,S]).
+
+    BSHD: q [B,S,Hq,Dqk], k/v [B,S,Hkv,D], O [B,S,Hq,Dv].  Packed (THD, when
+    seq_offsets [B+1] is given): q [T,Hq,Dqk], k/v [T,Hkv,D], O [T,Hq,Dv];
+    S = max_seqlen or the largest segment.
+    """
     torch = _torch()
-    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type)
+    packed = _layout(q, seq_offsets, seqlens, max_seqlen)
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
     B, S, Hq = p.batch, p.seqlen, p.num_heads
-    if check_seqlens:
+    if check_seqlens and packed is None:
         _check_seqlens(seqlens, B, S)
     if softmax_type == "learnable":
         if softmax_offset is None:
@@ -186,31 +241,36 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
             raise ValueError("softmax_offset must hold num_heads values")
     else:
         softmax_offset = None
-    o = out if out is not None else torch.empty((B, S, Hq, p.head_dim_v), dtype=q.dtype, device=q.device)
+    o = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (p.head_dim_v,), dtype=q.dtype,
+                                                device=q.device)
     l = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     lib = load_library()
     _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(softmax_offset),
-                        _ptr(seqlens), _ptr(o), _ptr(l), None, 0, _stream(stream)), "attn_fwd")
+                        _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), None, 0, _stream(stream)),
+           "attn_fwd")
     return o, l
 
 
 def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causal",
              window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
-             seqlens=None, want_d_offset=None, workspace=None, outs=None, stream=None,
-             check_seqlens=True, stage=0):
+             seqlens=None, seq_offsets=None, max_seqlen=None, want_d_offset=None, workspace=None,
+             outs=None, stream=None, check_seqlens=True, stage=0):
     """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None).
 
     d_softmax_offset is returned for learnable softmax (always) and for
-    off-by-one when want_d_offset is true; vanilla returns None.
+    off-by-one when want_d_offset is true; vanilla returns None.  Layouts as
+    for attn_fwd (packed THD when seq_offsets is given).
     """
     torch = _torch()
-    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type)
+    packed = _layout(q, seq_offsets, seqlens, max_seqlen)
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
     B, S, Hq, Hkv = p.batch, p.seqlen, p.num_heads, p.num_gqa_groups
-    if check_seqlens:
+    if check_seqlens and packed is None:
         _check_seqlens(seqlens, B, S)
+    o_shape = tuple(q.shape[:-1]) + (p.head_dim_v,)
     for t in (o, d_o):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or tuple(t.shape) != (B, S, Hq, p.head_dim_v):
-            raise ValueError("o and d_o must be contiguous [B,S,Hq,Dv] tensors of q's dtype")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or tuple(t.shape) != o_shape:
+            raise ValueError(f"o and d_o must be contiguous {list(o_shape)} tensors of q's dtype")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,Hq,S] tensor")
     if softmax_type == "learnable":
@@ -234,7 +294,7 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
-            _ptr(softmax_offset), _ptr(seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(softmax_offset), _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(doff), _ptr(workspace), workspace.numel(), _stream(stream))
     if stage:
         _check(lib.attn_bwd_stage(stage, *args), f"attn_bwd_stage({stage})")

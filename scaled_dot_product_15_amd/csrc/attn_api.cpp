@@ -106,7 +106,8 @@ size_t attn_bwd_workspace_size(const attn_params* p) {
 }
 
 int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
-             const int32_t* seqlens, void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+             const int32_t* seqlens, const int32_t* seq_offsets, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   const int rc = attn_validate(p);
@@ -119,6 +120,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.v = v;
   a.softmax_offset = softmax_offset;
   a.seqlens = seqlens;
+  a.seq_offsets = seq_offsets;
   a.out_o = o;
   a.out_lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -131,9 +133,9 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
 namespace {
 
 int bwd_common(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
-               const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq,
-               void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
+               const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace,
+               size_t workspace_bytes, void* stream) {
   if (stage < 0 || stage > ATTN_BWD_STAGE_OFFSET_GRAD) return ATTN_ERR_INVALID_ARG;
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
@@ -152,6 +154,7 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   a.lse = lse;
   a.softmax_offset = softmax_offset;
   a.seqlens = seqlens;
+  a.seq_offsets = seq_offsets;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -188,19 +191,20 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
 extern "C" {
 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
-             const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq, void* dk, void* dv,
-             float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_common(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, dq, dk, dv, d_softmax_offset, workspace,
-                    workspace_bytes, stream);
+             const float* lse, const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets,
+             void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return bwd_common(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv, d_softmax_offset,
+                    workspace, workspace_bytes, stream);
 }
 
 int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
-                   const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens, void* dq,
-                   void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
+                   const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < ATTN_BWD_STAGE_PREPROCESS) return ATTN_ERR_INVALID_ARG;
-  return bwd_common(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, dq, dk, dv, d_softmax_offset,
-                    workspace, workspace_bytes, stream);
+  return bwd_common(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
+                    d_softmax_offset, workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -123,9 +123,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   bf16x8 kreg[DQK / 16], vreg[DV / 16];
   {
     const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
-    const __amdgpu_buffer_rsrc_t kres = buf_rsrc(static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK,
+    const __amdgpu_buffer_rsrc_t kres = buf_rsrc(static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK,
                                                  (uint32_t)(m.L * kstride * 2));
-    const __amdgpu_buffer_rsrc_t vres = buf_rsrc(static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV,
+    const __amdgpu_buffer_rsrc_t vres = buf_rsrc(static_cast<const uint16_t*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV,
                                                  (uint32_t)(m.L * vstride * 2));
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks)
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const uint16_t* Qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* dOg = static_cast<const uint16_t*>(a.d_o);
   const size_t qstride = (size_t)a.Hq * DQK, ostride = (size_t)a.Hq * DV;
+  const size_t row0 = seq_row0(a, b);
   const TileCopy<C::BMQ, C::QCH, C::NT> qcopy(tid, (uint32_t)(qstride * 2));
   const TileCopy<C::BMQ, C::OCH, C::NT> ocopy(tid, (uint32_t)(ostride * 2));
   const RowReads<C::QCH> qrd(lane);
@@ -181,8 +182,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   auto issue_stage = [&](const StageWalk& st, int buf) {
     const int h = g * a.G + hs * Gs + st.hh;
     const int q0 = st.q0;
-    qcopy.issue(Qg + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
-    ocopy.issue(dOg + ((size_t)b * a.S * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
+    qcopy.issue(Qg + (row0 * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
+    ocopy.issue(dOg + (row0 * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
     // lse2 (wave 0) and delta (wave 1) of rows q0 .. q0+63, one 4-byte copy
     // per lane; rows past S arrive as zeros.
     if (w < 2) {
@@ -442,10 +443,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
-  if (kj < a.S) {
+  // dK / dV rows exist up to the batch's row count (S, or the segment size
+  // of packed tensors); the fp32 partials always use the padded layout.
+  if (kj < seq_rows(a, b)) {
     if (nsp == 1) {
-      uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DQK + hf * 4;
-      uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ((size_t)(b * a.S + kj) * a.Hkv + g) * DV + hf * 4;
+      uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ((seq_row0(a, b) + kj) * a.Hkv + g) * DQK + hf * 4;
+      uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ((seq_row0(a, b) + kj) * a.Hkv + g) * DV + hf * 4;
 #pragma unroll
       for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
@@ -484,14 +487,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 }
 
 // dst[i] = bf16(mul * sum over splits s = 0 .. n_splits-1 of part[s*n + i]),
-// four consecutive elements per thread (n is a multiple of 4).
+// four consecutive elements per thread (n and row_elems are multiples of 4).
+// The partials use the padded layout, row b*S + j of row_elems elements; for
+// packed (THD) tensors that row goes to row seq_offsets[b] + j of dst, and
+// rows past the segment size are not written.
 __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* part, uint16_t* dst, size_t n, int n_splits,
-                                                                float mul) {
+                                                                float mul, const int32_t* seq_offsets, int S,
+                                                                int row_elems) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
+  size_t out = i;
+  if (seq_offsets) {
+    const size_t r = i / (size_t)row_elems;
+    const int b = (int)(r / (size_t)S), j = (int)(r % (size_t)S);
+    const int rows = seq_offsets[b + 1] - seq_offsets[b];
+    if (j >= rows) return;
+    out = ((size_t)seq_offsets[b] + j) * row_elems + (i - r * row_elems);
+  }
   f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
   for (int sp = 1; sp < n_splits; ++sp) acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * n + i);
-  *reinterpret_cast<u32x2*>(dst + i) = u32x2{pack_bf16(acc[0] * mul, acc[1] * mul), pack_bf16(acc[2] * mul, acc[3] * mul)};
+  *reinterpret_cast<u32x2*>(dst + out) = u32x2{pack_bf16(acc[0] * mul, acc[1] * mul), pack_bf16(acc[2] * mul, acc[3] * mul)};
 }
 
 // Explicit instantiations: with only the implicit ones from the launchers
@@ -539,9 +554,11 @@ hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t
   const size_t rows = (size_t)a.B * a.S * a.Hkv;
   const size_t nk = rows * dqk, nv = rows * dv;
   hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((nk / 4 + 255) / 256)), dim3(256), 0, stream,
-                     a.kv_part, static_cast<uint16_t*>(a.dk), nk, a.n_splits, a.scale);
+                     a.kv_part, static_cast<uint16_t*>(a.dk), nk, a.n_splits, a.scale, a.seq_offsets, a.S,
+                     a.Hkv * dqk);
   hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((nv / 4 + 255) / 256)), dim3(256), 0, stream,
-                     a.kv_part + (size_t)a.n_splits * nk, static_cast<uint16_t*>(a.dv), nv, a.n_splits, 1.0f);
+                     a.kv_part + (size_t)a.n_splits * nk, static_cast<uint16_t*>(a.dv), nv, a.n_splits, 1.0f,
+                     a.seq_offsets, a.S, a.Hkv * dv);
   return hipGetLastError();
 }
 

@@ -75,9 +75,9 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
   float lse2 = 0.0f, dl = 0.0f;
   {
     const size_t qstride = (size_t)a.Hq * DQK, ostride = (size_t)a.Hq * DV;
-    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(static_cast<const uint16_t*>(a.q) + ((size_t)b * a.S * a.Hq + h) * DQK,
+    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(static_cast<const uint16_t*>(a.q) + (seq_row0(a, b) * a.Hq + h) * DQK,
                                                  (uint32_t)(m.L * qstride * 2));
-    const __amdgpu_buffer_rsrc_t ores = buf_rsrc(static_cast<const uint16_t*>(a.d_o) + ((size_t)b * a.S * a.Hq + h) * DV,
+    const __amdgpu_buffer_rsrc_t ores = buf_rsrc(static_cast<const uint16_t*>(a.d_o) + (seq_row0(a, b) * a.Hq + h) * DV,
                                                  (uint32_t)(m.L * ostride * 2));
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks)
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
     // dK/dV kernel; for a sink logit z, the partial sum over the 32 rows of
     // dL/dz_i = -exp(z - LSE_i) delta_i (the sink enters only the softmax
     // denominator), added up over the rows' chunks in fixed order later.
-    const __amdgpu_buffer_rsrc_t outres = buf_rsrc(static_cast<const uint16_t*>(a.o) + ((size_t)b * a.S * a.Hq + h) * DV,
+    const __amdgpu_buffer_rsrc_t outres = buf_rsrc(static_cast<const uint16_t*>(a.o) + (seq_row0(a, b) * a.Hq + h) * DV,
                                                    (uint32_t)(m.L * ostride * 2));
     float part = 0.0f;
 #pragma unroll
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / C::BN, kt1 = hi < 0 ? -1 : hi / C::BN;
 
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV;
   const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
   const TileCopy<C::BN, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
   const TileCopy<C::BN, C::VCH, C::NT> vcopy(tid, (uint32_t)(vstride * 2));
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
     if (kt + 1 <= kt1) step(kt + 1, B1{}, std::true_type{});
   }
 
-  if (qi < a.S) {
-    uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((size_t)(b * a.S + qi) * a.Hq + h) * DQK + hf * 4;
+  if (qi < seq_rows(a, b)) {
+    uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK + hf * 4;
 #pragma unroll
     for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll

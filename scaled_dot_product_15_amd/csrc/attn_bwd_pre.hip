@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(KArgs a) {
     const int i = chunk * kPreRows + r0 + rr;
     float acc = 0.0f;
     if (i < L) {
-      const size_t off = ((size_t)(b * a.S + i) * a.Hq + h) * DV + part * EPC;
+      const size_t off = ((seq_row0(a, b) + i) * a.Hq + h) * DV + part * EPC;
       const u32x4 ov = ldg16(O + off), dv = ldg16(dO + off);
       if constexpr (sizeof(T) == 2) {
 #pragma unroll

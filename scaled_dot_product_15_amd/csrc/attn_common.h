@@ -29,6 +29,7 @@ struct KArgs {
   const float* lse;
   const float* softmax_offset;  // [Hq] raw sink logits (learnable)
   const int32_t* seqlens;       // [B] or nullptr
+  const int32_t* seq_offsets;   // [B+1] segment starts of packed (THD) tensors, or nullptr (BSHD)
   void* out_o;                  // forward output O
   float* out_lse;               // forward output LSE
   void* dq;
@@ -49,9 +50,25 @@ struct KArgs {
   int n_splits;         // dK/dV workgroups per (key tile, batch, kv head), each over G / n_splits query heads
 };
 
+// First row of batch b along the token axis of Q, K, V, O and the gradients:
+// b * S for BSHD tensors; the start of segment b for packed (THD) tensors.
+__device__ __forceinline__ size_t seq_row0(const KArgs& a, int b) {
+  return a.seq_offsets ? (size_t)a.seq_offsets[b] : (size_t)b * a.S;
+}
+
+// Rows batch b owns along that axis: S (BSHD) or the size of segment b
+// (THD), clamped to [0, S].  Kernels write output rows below this count only.
+__device__ __forceinline__ int seq_rows(const KArgs& a, int b) {
+  if (!a.seq_offsets) return a.S;
+  const int n = a.seq_offsets[b + 1] - a.seq_offsets[b];
+  return n < 0 ? 0 : (n > a.S ? a.S : n);
+}
+
+// Valid (unpadded) length of batch b, clamped to [0, seq_rows(a, b)].
 __device__ __forceinline__ int seq_len(const KArgs& a, int b) {
-  int L = a.seqlens ? a.seqlens[b] : a.S;
-  return L < 0 ? 0 : (L > a.S ? a.S : L);
+  const int R = seq_rows(a, b);
+  const int L = a.seqlens ? a.seqlens[b] : R;
+  return L < 0 ? 0 : (L > R ? R : L);
 }
 
 // Sink logit z_h in natural-log units, or -inf when there is none.

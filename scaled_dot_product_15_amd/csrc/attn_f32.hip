@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
   const float* Q = static_cast<const float*>(a.q);
 
   float q[DQK], o[DV];
-  for (int d = 0; d < DQK; ++d) q[d] = qi < m.L ? Q[((size_t)(b * a.S + qi) * a.Hq + h) * DQK + d] * a.scale : 0.0f;
+  for (int d = 0; d < DQK; ++d) q[d] = qi < m.L ? Q[((seq_row0(a, b) + qi) * a.Hq + h) * DQK + d] * a.scale : 0.0f;
   for (int d = 0; d < DV; ++d) o[d] = 0.0f;
   // The sink enters once: as wave 0's initial state.
   const bool sink = a.softmax_type != 0 && w == 0;
@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
   const int nrow = (i0 + kF32Tile < m.L ? i0 + kF32Tile : m.L) - 1;
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const size_t kvrow = (size_t)a.Hkv;
-  const float* Kb = static_cast<const float*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
-  const float* Vb = static_cast<const float*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
+  const float* Kb = static_cast<const float*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
+  const float* Vb = static_cast<const float*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV;
   for (int j0 = (lo / kF32Tile) * kF32Tile; hi >= 0 && j0 <= hi; j0 += kF32Tile) {
     __syncthreads();
     load_tile_f32<DQK>(Ks, Kb, kvrow * DQK, j0, m.L, tid);
@@ -93,10 +93,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
       for (int d = 0; d < DV; ++d) o[d] = o[d] * c1 + part[k][lane][d] * c2;
       mrun = mn;
     }
-    if (qi < a.S) {
+    if (qi < seq_rows(a, b)) {
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float* O = static_cast<float*>(a.out_o) + ((size_t)(b * a.S + qi) * a.Hq + h) * DV;
+      float* O = static_cast<float*>(a.out_o) + ((seq_row0(a, b) + qi) * a.Hq + h) * DV;
       for (int d = 0; d < DV; ++d) O[d] = o[d] * inv;
+    }
+    if (qi < a.S) {
       a.out_lse[((size_t)b * a.Hq + h) * a.S + qi] = l > 0.0f ? mrun + logf(l) : -__builtin_inff();
     }
   }
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
   const int j0 = kt * kF32Tile, kj = j0 + lane;
   float kk[DQK], vv[DV], dk[DQK], dv[DV];
   {
-    const size_t row = (size_t)(b * a.S + kj) * a.Hkv + g;
+    const size_t row = (seq_row0(a, b) + kj) * a.Hkv + g;
     for (int d = 0; d < DQK; ++d) { kk[d] = kj < m.L ? static_cast<const float*>(a.k)[row * DQK + d] : 0.0f; dk[d] = 0.0f; }
     for (int d = 0; d < DV; ++d) { vv[d] = kj < m.L ? static_cast<const float*>(a.v)[row * DV + d] : 0.0f; dv[d] = 0.0f; }
   }
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
   const size_t qrow = (size_t)a.Hq;
   for (int hi_ = 0; hi_ < a.G; ++hi_) {
     const int h = g * a.G + hi_;
-    const float* Qb = static_cast<const float*>(a.q) + ((size_t)b * a.S * a.Hq + h) * DQK;
-    const float* dOb = static_cast<const float*>(a.d_o) + ((size_t)b * a.S * a.Hq + h) * DV;
+    const float* Qb = static_cast<const float*>(a.q) + (seq_row0(a, b) * a.Hq + h) * DQK;
+    const float* dOb = static_cast<const float*>(a.d_o) + (seq_row0(a, b) * a.Hq + h) * DV;
     for (int q0 = (lo / kF32Tile) * kF32Tile; hi >= 0 && q0 <= hi; q0 += kF32Tile) {
       __syncthreads();
       load_tile_f32<DQK>(Qs, Qb, qrow * DQK, q0, m.L, tid);
@@ -155,12 +157,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
     for (int d = 0; d < DV; ++d) part[w - 1][lane][DQK + d] = dv[d];
   }
   __syncthreads();
-  if (w == 0 && kj < a.S) {
+  if (w == 0 && kj < seq_rows(a, b)) {
     for (int k = 0; k < kF32Waves - 1; ++k) {
       for (int d = 0; d < DQK; ++d) dk[d] += part[k][lane][d];
       for (int d = 0; d < DV; ++d) dv[d] += part[k][lane][DQK + d];
     }
-    const size_t row = (size_t)(b * a.S + kj) * a.Hkv + g;
+    const size_t row = (seq_row0(a, b) + kj) * a.Hkv + g;
     for (int d = 0; d < DQK; ++d) static_cast<float*>(a.dk)[row * DQK + d] = dk[d] * a.scale;
     for (int d = 0; d < DV; ++d) static_cast<float*>(a.dv)[row * DV + d] = dv[d];
   }
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(KArgs a) {
   float q[DQK], dov[DV], dq[DQK];
   float lse = 0.0f, dl = 0.0f;
   {
-    const size_t row = (size_t)(b * a.S + qi) * a.Hq + h;
+    const size_t row = (seq_row0(a, b) + qi) * a.Hq + h;
     for (int d = 0; d < DQK; ++d) { q[d] = qi < m.L ? static_cast<const float*>(a.q)[row * DQK + d] : 0.0f; dq[d] = 0.0f; }
     for (int d = 0; d < DV; ++d) dov[d] = qi < m.L ? static_cast<const float*>(a.d_o)[row * DV + d] : 0.0f;
     if (qi < m.L) {
@@ -192,8 +194,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(KArgs a) {
   const int nrow = (i0 + kF32Tile < m.L ? i0 + kF32Tile : m.L) - 1;
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const size_t kvrow = (size_t)a.Hkv;
-  const float* Kb = static_cast<const float*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
-  const float* Vb = static_cast<const float*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
+  const float* Kb = static_cast<const float*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
+  const float* Vb = static_cast<const float*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV;
   for (int j0 = (lo / kF32Tile) * kF32Tile; hi >= 0 && j0 <= hi; j0 += kF32Tile) {
     __syncthreads();
     load_tile_f32<DQK>(Ks, Kb, kvrow * DQK, j0, m.L, tid);
@@ -212,10 +214,10 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(KArgs a) {
   if (w > 0)
     for (int d = 0; d < DQK; ++d) part[w - 1][lane][d] = dq[d];
   __syncthreads();
-  if (w == 0 && qi < a.S) {
+  if (w == 0 && qi < seq_rows(a, b)) {
     for (int k = 0; k < kF32Waves - 1; ++k)
       for (int d = 0; d < DQK; ++d) dq[d] += part[k][lane][d];
-    float* dQ = static_cast<float*>(a.dq) + ((size_t)(b * a.S + qi) * a.Hq + h) * DQK;
+    float* dQ = static_cast<float*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK;
     for (int d = 0; d < DQK; ++d) dQ[d] = dq[d] * a.scale;
   }
 }

@@ -93,8 +93,8 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   row_key_bounds(m, qi, klo, khi);
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * DQK;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * DV;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV;
   const size_t kstride = (size_t)a.Hkv * DQK, vstride = (size_t)a.Hkv * DV;
 
   const TileCopy<BN, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   bf16x8 qreg[DQK / 16];
   {
     const size_t qstride = (size_t)a.Hq * DQK;
-    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(Q + ((size_t)b * a.S * a.Hq + h) * DQK, (uint32_t)(m.L * qstride * 2));
+    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(Q + (seq_row0(a, b) * a.Hq + h) * DQK, (uint32_t)(m.L * qstride * 2));
     const uint32_t qoff = (uint32_t)(qi * qstride + hf * 8) * 2;
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) qreg[ks] = as_bf16x8(buf_load16(qres, qoff + ks * 32));
@@ -271,8 +271,10 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qi < a.S) {
-    uint16_t* op = static_cast<uint16_t*>(a.out_o) + ((size_t)(b * a.S + qi) * a.Hq + h) * DV + hf * 4;
+  // O rows exist up to the batch's row count (S, or the segment size of
+  // packed tensors); LSE rows up to S.
+  if (qi < seq_rows(a, b)) {
+    uint16_t* op = static_cast<uint16_t*>(a.out_o) + ((seq_row0(a, b) + qi) * a.Hq + h) * DV + hf * 4;
 #pragma unroll
     for (int db = 0; db < DV / 32; ++db) {
 #pragma unroll
@@ -282,6 +284,8 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
         *reinterpret_cast<u32x2*>(op + db * 32 + ig * 8) = val;
       }
     }
+  }
+  if (qi < a.S) {
     if (hf == 0) {
       const float lse2 = l_tot > 0.0f ? m_run + __log2f(l_tot) : -__builtin_inff();
       a.out_lse[((size_t)b * a.Hq + h) * a.S + qi] = lse2 * kLn2;

@@ -98,3 +98,30 @@ def exact_f64(t) -> np.ndarray:
     """Exact float64 copy of a (bf16 or f32) torch tensor's values."""
     import torch
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def pack(arrays: dict, seg_sizes) -> dict:
+    """Packed (THD) copy of BSHD draws: segment b is the first seg_sizes[b]
+    token rows of batch b; segments lie back to back along one token axis,
+    followed by `tail` extra rows (zeros) that belong to no segment when
+    arrays holds a "tail" entry.  Adds seq_offsets [B+1] (int32).  Pure data
+    movement: no attention arithmetic."""
+    sizes = [int(n) for n in seg_sizes]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    tail = int(arrays.get("tail", 0))
+    out = dict(arrays)
+    for name in ("q", "k", "v", "do"):
+        x = arrays[name]
+        parts = [x[b, :n] for b, n in enumerate(sizes)]
+        parts.append(np.zeros((tail,) + x.shape[2:], dtype=x.dtype))
+        out[name] = np.concatenate(parts, axis=0)
+    out["seq_offsets"] = off
+    return out
+
+
+def to_torch_packed(arrays: dict, dtype: str, device="cpu") -> dict:
+    """to_torch for packed arrays (adds seq_offsets)."""
+    import torch
+    out = to_torch(arrays, dtype, device)
+    out["seq_offsets"] = torch.from_numpy(arrays["seq_offsets"]).to(device)
+    return out

@@ -132,7 +132,8 @@ def test_dkdv_head_splits_and_workspace(B, S, Hkv, G, causal, win):
 def _fwd(p, q=1, k=1, v=1, off=None, sl=None, o=1, lse=1):
     vp = lambda x: None if x is None else ctypes.c_void_p(0x1000 * x)
     lib = binding.load_library()
-    return lib.attn_fwd(ctypes.byref(p), vp(q), vp(k), vp(v), vp(off), vp(sl), vp(o), vp(lse), None, 0, None)
+    return lib.attn_fwd(ctypes.byref(p), vp(q), vp(k), vp(v), vp(off), vp(sl), None, vp(o), vp(lse), None, 0,
+                        None)
 
 
 def _bwd(p, ptrs=None, off=None, doff=None, ws=0x100000, ws_bytes=None):
@@ -141,7 +142,7 @@ def _bwd(p, ptrs=None, off=None, doff=None, ws=0x100000, ws_bytes=None):
     lib = binding.load_library()
     wsb = binding.attn_bwd_workspace_size(p) if ws_bytes is None else ws_bytes
     q, k, v, o, do, lse, dq, dk, dv = (vp(x) for x in ptrs)
-    return lib.attn_bwd(ctypes.byref(p), q, k, v, o, do, lse, vp(off), None, dq, dk, dv, vp(doff),
+    return lib.attn_bwd(ctypes.byref(p), q, k, v, o, do, lse, vp(off), None, None, dq, dk, dv, vp(doff),
                         vp(ws), wsb, None)
 
 
@@ -175,7 +176,7 @@ def test_bwd_stage_rejects_unknown_stages():
     p = P()
     vp = ctypes.c_void_p
     for stage in (0, -1, 5, 99):
-        rc = lib.attn_bwd_stage(stage, ctypes.byref(p), *(vp(0x1000) for _ in range(6)), None, None,
+        rc = lib.attn_bwd_stage(stage, ctypes.byref(p), *(vp(0x1000) for _ in range(6)), None, None, None,
                                 *(vp(0x1000) for _ in range(3)), None, vp(0x100000),
                                 binding.attn_bwd_workspace_size(p), None)
         assert rc == -1, stage

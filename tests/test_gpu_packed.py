@@ -1,0 +1,154 @@
+"""GPU parity for packed (THD) inputs: sequences back to back on one token axis.
+
+Each case packs segments of unequal size (one empty, one with padding inside,
+one ending in a ragged tail tile) followed by tokens that belong to no
+segment, and checks, element by element:
+  * the HIP path against the float64 packed oracle (block-diagonal mask over
+    the token axis) within the accuracy bar of the padded tests;
+  * that tokens outside every segment are never written (outputs are
+    pre-filled with a sentinel);
+  * that packed results equal, bit for bit, the padded BSHD results on the
+    same segments (the kernels differ only in where a batch's rows start),
+    which also shows no segment reads another's rows.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from scaled_dot_product_15_amd import binding, inputs
+from tests import gpu_cases as gc
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gc.gpu_available(), reason="needs a GPU and the built library")]
+
+DIMS = {"bf16_64": ("bf16", 64, 64), "bf16_128": ("bf16", 128, 128), "bf16_192_128": ("bf16", 192, 128),
+        "f32_64": ("f32", 64, 64)}
+MASKS = {"causal": (True, (-1, -1)), "causal_swa": (True, (37, 0)), "window": (False, (20, 9))}
+SOFTMAX = ("vanilla", "off_by_one", "learnable")
+SEG_SIZES = [333, 150, 0, 97]   # S = 333: several 128-row tiles and a ragged tail
+SEQLENS = [333, 120, 0, 97]     # segment 1 ends in 30 padding tokens
+TAIL = 7                        # tokens past the last segment
+SENTINEL = 1232.0  # exact in bf16 and fp32
+
+CASES = list(itertools.product(DIMS, MASKS, SOFTMAX))
+
+
+def _run(p, t, seq_offsets, seqlens, T, packed):
+    import torch
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
+              window_size=p.window, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
+              seqlens=seqlens)
+    if packed:
+        kw.update(seq_offsets=seq_offsets, max_seqlen=p.S)
+    dt = t["q"].dtype
+    o = torch.full(tuple(t["q"].shape[:-1]) + (p.d_v,), SENTINEL, dtype=dt, device="cuda")
+    o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], out=o, **kw)
+    outs = (torch.full_like(t["q"], SENTINEL), torch.full_like(t["k"], SENTINEL),
+            torch.full_like(t["v"], SENTINEL),
+            None if p.softmax_type == "vanilla" else torch.empty(p.Hq, dtype=torch.float32, device="cuda"))
+    dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=True, outs=outs,
+                                        **kw)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv, doff
+
+
+def _problem(dims, mask, st, Hq=4, Hkv=2):
+    dtype, dqk, dv = DIMS[dims]
+    causal, win = MASKS[mask]
+    return inputs.Problem(B=len(SEG_SIZES), S=max(SEG_SIZES), Hq=Hq, Hkv=Hkv, d_qk=dqk, d_v=dv, dtype=dtype,
+                          causal=causal, window=win, softmax_type=st)
+
+
+def _check_packed(p, t, g, tag):
+    o, lse, dq, dk, dv, doff = (None if x is None else inputs.exact_f64(x) for x in g)
+    off = t["seq_offsets"].cpu().numpy()
+    T = t["q"].shape[0]
+    f64 = inputs.exact_f64
+    r = oracle.attention_packed(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), seq_offsets=off,
+                                max_seqlen=p.S, seqlens=np.array(SEQLENS), num_gqa_groups=p.Hkv,
+                                causal=p.causal, window=p.window, softmax_type=p.softmax_type,
+                                softmax_offset=f64(t["alpha"]))
+    inside = slice(0, int(off[-1]))
+    for name, a in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert (a[int(off[-1]):] == SENTINEL).all(), f"{tag}: {name} written past the last segment"
+    # padding tokens inside a segment are exact zeros
+    for b in range(len(SEG_SIZES)):
+        pad = slice(int(off[b]) + SEQLENS[b], int(off[b + 1]))
+        for name, a in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+            assert (a[pad] == 0).all(), f"{tag}: {name} padding of segment {b} not zero"
+    fin = np.isfinite(r["lse"])
+    assert (np.isfinite(lse) == fin).all(), f"{tag}: LSE finiteness differs"
+    assert (lse[~fin] == r["lse"][~fin]).all(), f"{tag}: empty-row LSE differs"
+    stats = {"lse_maxabs": float(np.abs(lse[fin] - r["lse"][fin]).max()) if fin.any() else 0.0,
+             "o_maxabs": float(np.abs(o[inside] - r["o"][inside]).max())}
+    for name, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+        stats[f"{name}_maxabs"] = float(np.abs(a[inside] - r[name][inside]).max())
+        stats[f"{name}_rel_l2"] = gc.rel_l2(a[inside], r[name][inside])
+    if p.softmax_type != "vanilla":
+        stats["doff_rel_l2"] = gc.rel_l2(doff, r["dalpha"])
+        stats["doff_maxabs"] = float(np.abs(doff - r["dalpha"]).max())
+    gc.check(p, stats, tag)
+    return stats
+
+
+def _inputs(p, seed):
+    arr = inputs.draw(p, seed)
+    arr["tail"] = TAIL
+    packed = inputs.pack(arr, SEG_SIZES)
+    tp = inputs.to_torch_packed(packed, p.dtype, "cuda")
+    import torch
+    tp["seqlens"] = torch.tensor(SEQLENS, dtype=torch.int32, device="cuda")
+    return arr, tp
+
+
+@pytest.mark.parametrize("dims,mask,st", CASES, ids=lambda x: str(x))
+def test_packed_parity(dims, mask, st):
+    p = _problem(dims, mask, st)
+    seed = 50_000 + CASES.index((dims, mask, st))
+    gc.log(f"packed {dims} {mask} {st} seed={seed}")
+    _, tp = _inputs(p, seed)
+    g = _run(p, tp, tp["seq_offsets"], tp["seqlens"], tp["q"].shape[0], packed=True)
+    stats = _check_packed(p, tp, g, f"packed/{dims}/{mask}/{st}")
+    gc.log(f"  {stats}")
+
+
+@pytest.mark.parametrize("dims,st,hkv", [("bf16_128", "learnable", 2), ("bf16_64", "off_by_one", 1),
+                                         ("bf16_192_128", "vanilla", 4), ("f32_64", "learnable", 2)],
+                         ids=lambda x: str(x))
+def test_packed_equals_padded_bitwise(dims, st, hkv):
+    """Packed and padded BSHD runs of the same segments agree bit for bit.
+
+    Hkv = 1 with 8 query heads makes the bf16 dK/dV stage split the group's
+    heads over workgroups (fp32 partials reduced into the packed rows)."""
+    import torch
+    p = _problem(dims, "causal_swa", st, Hq=8, Hkv=hkv)
+    seed = 51_000 + hkv
+    gc.log(f"packed==padded {dims} {st} Hkv={hkv} seed={seed} splits={binding.host_dkdv_splits(_params(p))}")
+    arr, tp = _inputs(p, seed)
+    gp = _run(p, tp, tp["seq_offsets"], tp["seqlens"], tp["q"].shape[0], packed=True)
+    tb = inputs.to_torch(arr, p.dtype, "cuda")
+    tb["seqlens"] = torch.tensor(SEQLENS, dtype=torch.int32, device="cuda")
+    gb = _run(p, tb, None, tb["seqlens"], None, packed=False)
+    off = tp["seq_offsets"].cpu().numpy()
+    for name, i in (("o", 0), ("dq", 2), ("dk", 3), ("dv", 4)):
+        a, b = gp[i].cpu(), gb[i].cpu()
+        for s in range(len(SEG_SIZES)):
+            n = SEG_SIZES[s]
+            assert torch.equal(a[int(off[s]):int(off[s]) + n], b[s, :n]), f"{name} segment {s} differs"
+    assert torch.equal(gp[1].cpu(), gb[1].cpu()), "lse differs"
+    if st != "vanilla":
+        assert torch.equal(gp[5].cpu(), gb[5].cpu()), "d_softmax_offset differs"
+    _check_packed(p, tp, gp, f"packed==padded/{dims}/{st}/Hkv={hkv}")
+
+
+def _params(p):
+    return binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype,
+                               "causal" if p.causal else "no_mask", p.window, None, p.softmax_type)
+
+
+def test_packed_head_split_is_used():
+    """The MQA bitwise case above exercises the split-reduce path."""
+    p = _problem("bf16_64", "causal_swa", "off_by_one", Hq=8, Hkv=1)
+    assert binding.host_dkdv_splits(_params(p)) > 1
