@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--case", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=12)
+    ap.add_argument("--layout", choices=("bshd", "thd"), default="bshd",
+                    help="thd: the batch's sequences packed back to back at their valid lengths "
+                         "(seq_offsets), no padding tokens stored")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) to "
                          "calibrate the HBM byte counters, then exit")
@@ -140,12 +143,20 @@ def main():
     p = inputs.workload_configs()[args.config][args.case]
     seed = 1000 * args.config + args.case
     arr = inputs.draw(p, seed)
-    t = inputs.to_torch(arr, p.dtype, "cuda")
     dev = torch.cuda.get_device_properties(0)
+    packed = args.layout == "thd"
+    if packed:
+        sizes = [p.S] * p.B if arr["seqlens"] is None else [int(x) for x in arr["seqlens"]]
+        t = inputs.to_torch_packed(inputs.pack(arr, sizes), p.dtype, "cuda")
+        t["seqlens"] = None  # every segment is exactly its valid tokens
+    else:
+        t = inputs.to_torch(arr, p.dtype, "cuda")
 
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
               window_size=p.window, scale_factor=p.scale_factor or None,
               softmax_type=p.softmax_type, softmax_offset=t["alpha"], seqlens=t["seqlens"])
+    if packed:
+        kw.update(seq_offsets=t["seq_offsets"], max_seqlen=p.S)
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     want = p.softmax_type != "vanilla"
     dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
@@ -222,7 +233,7 @@ def main():
     achieved = kflops[dominant] * pairs / (avg_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, dominant) if args.case == 0 else None,
+                "traffic": measured_traffic(args.config, dominant) if args.case == 0 and not packed else None,
                 "flops_per_launch": kflops[dominant] * pairs, "avg_launch_ms": round(avg_ms[dominant], 4)}
 
     res = {
@@ -242,7 +253,8 @@ def main():
                    "num_gqa_groups": p.Hkv, "head_dim_qk": p.d_qk, "head_dim_v": p.d_v,
                    "mask": "causal" if p.causal else "none", "window": list(p.window),
                    "softmax_type": p.softmax_type, "seed": seed,
-                   "seqlens": None if seq is None else [int(x) for x in seq]},
+                   "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout,
+                   "tokens": int(t["q"].shape[0]) if packed else p.B * p.S},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "pairs": pairs,
         "gflop_fwd": round(f_fwd / 1e9, 3),

@@ -209,12 +209,18 @@ def _check_seqlens(seqlens, B, S):
     return seqlens
 
 
-def _layout(q, seq_offsets, seqlens, max_seqlen):
-    """(B, S) of packed inputs (host-checked), or None for BSHD."""
+def _layout(q, seq_offsets, seqlens, max_seqlen, check):
+    """(B, S) of packed inputs, or None for BSHD.  With check, the offsets and
+    lengths are copied to the host and checked; without (timed loops), S must
+    be given as max_seqlen and the caller vouches for the values."""
     if seq_offsets is None:
         if max_seqlen is not None:
             raise ValueError("max_seqlen applies to packed inputs (seq_offsets) only")
         return None
+    if not check:
+        if max_seqlen is None:
+            raise ValueError("packed inputs without host checks need max_seqlen")
+        return seq_offsets.numel() - 1, int(max_seqlen)
     return _packed_layout(q, seq_offsets, seqlens, max_seqlen)
 
 
@@ -228,7 +234,7 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
     S = max_seqlen or the largest segment.
     """
     torch = _torch()
-    packed = _layout(q, seq_offsets, seqlens, max_seqlen)
+    packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
     B, S, Hq = p.batch, p.seqlen, p.num_heads
     if check_seqlens and packed is None:
@@ -262,7 +268,7 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     for attn_fwd (packed THD when seq_offsets is given).
     """
     torch = _torch()
-    packed = _layout(q, seq_offsets, seqlens, max_seqlen)
+    packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
     B, S, Hq, Hkv = p.batch, p.seqlen, p.num_heads, p.num_gqa_groups
     if check_seqlens and packed is None:

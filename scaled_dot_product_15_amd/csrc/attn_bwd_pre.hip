@@ -65,13 +65,27 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(KArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void dz_reduce_kernel(KArgs a) {
-  const int h = blockIdx.x * 64 + threadIdx.x;
-  if (h >= a.Hq) return;
+// d_offset[h] = sum of head h's B * n_chunks partials, one workgroup per
+// head, in a fixed order: thread t adds partials t, t + 256, ... of the
+// batch-major sequence (consecutive threads read consecutive chunks), then
+// the 256 thread sums meet in a fixed pairwise tree.
+constexpr int kDzThreads = 256;
+__global__ __launch_bounds__(kDzThreads) void dz_reduce_kernel(KArgs a) {
+  __shared__ float red[kDzThreads];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int n = a.B * a.n_chunks;
   float s = 0.0f;
-  for (int b = 0; b < a.B; ++b)
-    for (int c = 0; c < a.n_chunks; ++c) s += a.dz_partial[((size_t)b * a.Hq + h) * a.n_chunks + c];
-  a.d_offset[h] = s;
+  for (int i = t; i < n; i += kDzThreads) {
+    const int b = i / a.n_chunks, c = i - b * a.n_chunks;
+    s += a.dz_partial[((size_t)b * a.Hq + h) * a.n_chunks + c];
+  }
+  red[t] = s;
+  __syncthreads();
+  for (int w = kDzThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) a.d_offset[h] = red[0];
 }
 
 hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream) {
@@ -84,7 +98,7 @@ hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream)
 }
 
 hipError_t launch_dz_reduce(const KArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(dz_reduce_kernel, dim3((a.Hq + 63) / 64), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(dz_reduce_kernel, dim3(a.Hq), dim3(kDzThreads), 0, stream, a);
   return hipGetLastError();
 }
 
