@@ -49,8 +49,9 @@
  *     Attention never crosses a segment; positions for the causal and window
  *     rules count from the segment start.  LSE keeps the [B,Hq,S] layout
  *     (row i of segment b).  Tokens at or past seq_offsets[B] are not
- *     touched.  This follows the sequence descriptor of the TE single-GPU
- *     page, section 1: lengths plus, for packed inputs, segment boundaries.
+ *     touched.  Reading of the TE single-GPU page, section 1, where the
+ *     sequence descriptor gives, besides lengths, the start of each packed
+ *     sequence and its padding.
  *   - Element type of Q,K,V,O,dO,dQ,dK,dV is params.dtype (bf16 or f32).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream); the
  *     calls return without synchronising.  Inputs are read only.  Outputs are

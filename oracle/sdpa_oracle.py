@@ -330,9 +330,9 @@ def packed_visible_mask(seq_offsets, seqlens, T: int, causal: bool, window_left:
                         window_right: int) -> np.ndarray:
     """Boolean [T, T] over the packed token axis: True where token t may attend to token u.
 
-    Packed (THD) inputs: the TE single-GPU page, section 1, lets the sequence
-    descriptor carry segment boundaries and padding metadata for packed
-    sequences.  Reading taken: segment b holds tokens seq_offsets[b] ..
+    Packed (THD) inputs: in the TE single-GPU page, section 1, the sequence
+    descriptor tells the library, besides lengths, where packed sequences
+    start and which of their tokens pad them.  Reading taken: segment b holds tokens seq_offsets[b] ..
     seq_offsets[b+1]-1, of which the first seqlens[b] are valid (all of them
     when seqlens is None) and the rest padding.  Token t may attend to token u
     iff both lie in the same segment, both are valid, and their positions
