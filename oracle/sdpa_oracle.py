@@ -420,3 +420,128 @@ def attention_packed(q, k, v, d_o=None, *, seq_offsets, max_seqlen, seqlens=None
     if grads and softmax_type == VANILLA:
         res["dalpha"] = None
     return res
+
+
+# ---- attention dropout ------------------------------------------------------
+#
+# The TE single-GPU page ("Other attention knobs") enables attention dropout
+# with a rate and an RNG, and the PR #2225 sequence diagrams show the fused
+# forward returning an rng_state next to the output and softmax_aux.  The
+# pages fix neither the generator nor where the rate applies; readings taken:
+#   * inverted dropout on the softmax probabilities: O = (P * Z) V with
+#     Z_ij = keep_ij / (1 - p_eff); the LSE and the softmax normalisation use
+#     the undropped P;
+#   * keep_ij comes from the counter-based generator Philox4x32-10 (Salmon,
+#     Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+#     SC 2011), with the 64-bit seed as key and the 32-bit offset (the rng
+#     state advanced between calls) in the counter.  One generator call
+#     covers a 4 x 4 block of (query row, key) pairs of one (batch, query
+#     head): counter = (j >> 2, i >> 2, b * Hq + h, offset); the 16 output
+#     bytes (word w, byte k = bits 8k .. 8k+7) are the pairs' random bytes,
+#     byte (i & 3) * 4 + (j & 3);
+#   * a pair is kept iff its byte >= t with t = round(256 p), so the drop
+#     rate is p_eff = t / 256 (the rate is quantised to 1/256).
+
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
+MASK32 = 0xFFFFFFFF
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds on arrays of counter words and a key.
+
+    One round multiplies counter words 0 and 2 by the round constants, keeps
+    each 64-bit product's high and low halves, and mixes the high halves with
+    counter words 1 and 3 and the round key; the key grows by the Weyl
+    constants between rounds.  All words are uint32 (held in uint64 arrays).
+    """
+    c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) & MASK32 for x in (c0, c1, c2, c3))
+    k0 = np.uint64(int(k0) & MASK32)
+    k1 = np.uint64(int(k1) & MASK32)
+    m0, m1 = np.uint64(PHILOX_M0), np.uint64(PHILOX_M1)
+    for r in range(10):
+        if r:
+            k0 = np.uint64((int(k0) + PHILOX_W0) & MASK32)
+            k1 = np.uint64((int(k1) + PHILOX_W1) & MASK32)
+        p0 = m0 * c0
+        p1 = m1 * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & np.uint64(MASK32)
+        hi1, lo1 = p1 >> np.uint64(32), p1 & np.uint64(MASK32)
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return c0, c1, c2, c3
+
+
+def dropout_threshold(p: float) -> int:
+    """Byte threshold t = round(256 p), clamped to [0, 255]."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout probability must lie in [0, 1)")
+    return min(255, int(math.floor(256.0 * p + 0.5)))
+
+
+def dropout_keep(b: int, h: int, rows, keys, *, num_heads: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Boolean [len(rows), len(keys)]: True where pair (row, key) of batch b,
+    query head h is kept."""
+    t = dropout_threshold(p)
+    i = np.asarray(rows, dtype=np.uint64)[:, None]
+    j = np.asarray(keys, dtype=np.uint64)[None, :]
+    i, j = np.broadcast_arrays(i, j)
+    out = philox4x32_10(j >> np.uint64(2), i >> np.uint64(2), np.full(i.shape, b * num_heads + h, np.uint64),
+                        np.full(i.shape, offset, np.uint64), seed & MASK32, (seed >> 32) & MASK32)
+    byte_idx = (i & np.uint64(3)) * np.uint64(4) + (j & np.uint64(3))
+    words = np.stack(out)                                         # [4, rows, keys]
+    w = np.take_along_axis(words, (byte_idx >> np.uint64(2)).astype(np.int64)[None], axis=0)[0]
+    byte = (w >> ((byte_idx & np.uint64(3)) * np.uint64(8))) & np.uint64(0xFF)
+    return byte >= np.uint64(t)
+
+
+def attention_dropout(q, k, v, d_o=None, *, p: float, seed: int, offset: int, num_gqa_groups=None,
+                      causal=True, window=(-1, -1), scale_factor=None, softmax_type=VANILLA,
+                      softmax_offset=None, seqlens=None):
+    """attention() with inverted dropout on the probabilities (readings above).
+
+    Per (batch, query head): P and LSE as without dropout; Z = keep / (1 - p_eff);
+    O = (P Z) V;  dV = (P Z)^T dO;  dP = Z (dO V^T);  delta = rowsum(dO O);
+    dS = P (dP - delta);  dQ = scale dS K;  dK = scale dS^T Q;  dz = -p_sink delta.
+    Returns the same dict as attention() plus keep [B, Hq, S, S].
+    """
+    B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
+    G = Hq // Hkv
+    zscale = 1.0 / (1.0 - dropout_threshold(p) / 256.0)
+    grads = d_o is not None
+    res = {"o": np.zeros((B, S, Hq, dv_dim)), "lse": np.zeros((B, Hq, S)),
+           "keep": np.zeros((B, Hq, S, S), dtype=bool)}
+    if grads:
+        res.update(dq=np.zeros((B, S, Hq, dqk)), dk=np.zeros((B, S, Hkv, dqk)),
+                   dv=np.zeros((B, S, Hkv, dv_dim)), dalpha=np.zeros(Hq))
+    for b in range(B):
+        L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+        mask = visible_mask(S, L, causal, int(window[0]), int(window[1]))
+        for h in range(Hq):
+            g = h // G
+            keep = dropout_keep(b, h, np.arange(S), np.arange(S), num_heads=Hq, p=p, seed=seed, offset=offset)
+            res["keep"][b, h] = keep
+            z = sink_logit(softmax_type, softmax_offset, h)
+            qh = np.asarray(q[b, :, h, :], dtype=np.float64)
+            kg = np.asarray(k[b, :, g, :], dtype=np.float64)
+            vg = np.asarray(v[b, :, g, :], dtype=np.float64)
+            s = scale * (qh @ kg.T)
+            pr, lse = _softmax_rows(s, mask, z)
+            zmat = np.where(keep, zscale, 0.0)
+            o = (pr * zmat) @ vg
+            res["o"][b, :, h, :] = o
+            res["lse"][b, h] = lse
+            if not grads:
+                continue
+            doh = np.asarray(d_o[b, :, h, :], dtype=np.float64)
+            dp = zmat * (doh @ vg.T)
+            delta = (doh * o).sum(axis=1)
+            ds = pr * (dp - delta[:, None])
+            res["dq"][b, :, h, :] = scale * (ds @ kg)
+            res["dk"][b, :, g, :] += scale * (ds.T @ qh)
+            res["dv"][b, :, g, :] += (pr * zmat).T @ doh
+            if z is not None:
+                lse_safe = np.where(np.isfinite(lse), lse, z)
+                res["dalpha"][h] += -(np.exp(z - lse_safe) * delta).sum()
+    if grads and softmax_type == VANILLA:
+        res["dalpha"] = None
+    return res

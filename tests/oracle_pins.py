@@ -32,6 +32,11 @@ What pins what:
                    tokens; equality with the padded per-batch oracle (a
                    different formulation: block-diagonal mask over the token
                    axis vs one S x S problem per batch); finite differences
+  philox_kat       the dropout generator (Philox4x32-10) against its published
+                   known-answer vectors (tests/golden/philox4x32_10_kat.json)
+  dropout_*        keep rate and stream independence; scalar loops with the
+                   keep mask applied by hand; p = 0 == no dropout; finite
+                   differences; unbiasedness over many offsets
 """
 from __future__ import annotations
 
@@ -639,7 +644,150 @@ def pin_packed_finite_diff(orc):
             _close(r["dalpha"], fd, 1e-6, 1e-8, "packed dalpha")
 
 
+# ---- attention dropout -----------------------------------------------------
+
+def pin_philox_kat(orc):
+    """Philox4x32-10 against the generator's published known-answer vectors."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for vec in kat["vectors"]:
+        c = [int(x, 16) for x in vec["counter"]]
+        k = [int(x, 16) for x in vec["key"]]
+        got = [int(x) for x in orc.philox4x32_10(*c, *k)]
+        assert got == [int(x, 16) for x in vec["output"]], (vec, [hex(x) for x in got])
+
+
+def pin_dropout_rate(orc):
+    """Kept fraction within 5 sigma of 1 - t/256; rows, keys, heads and
+    offsets draw different bytes (no repeated 4 x 4 block)."""
+    for p in (0.1, 0.5, 0.9):
+        t = orc.dropout_threshold(p)
+        keeps = [orc.dropout_keep(b, h, np.arange(64), np.arange(64), num_heads=3, p=p, seed=0x1234567890,
+                                  offset=off) for b in range(2) for h in range(3) for off in (0, 7)]
+        frac = float(np.mean(keeps))
+        n = sum(x.size for x in keeps)
+        q = 1.0 - t / 256.0
+        assert abs(frac - q) <= 5 * math.sqrt(q * (1 - q) / n), (p, frac, q)
+        flat = [x.tobytes() for x in keeps]
+        assert len(set(flat)) == len(flat), "two (batch, head, offset) streams coincide"
+        if p == 0.5:  # 256 blocks of 16 fair bits: a few repeats at most
+            blocks = {keeps[0][r:r + 4, c:c + 4].tobytes() for r in range(0, 64, 4) for c in range(0, 64, 4)}
+            assert len(blocks) > 245, "4 x 4 blocks repeat"
+    assert orc.dropout_threshold(0.0) == 0 and orc.dropout_threshold(0.5) == 128
+    assert orc.dropout_keep(0, 0, np.arange(8), np.arange(8), num_heads=1, p=0.0, seed=5, offset=0).all()
+
+
+def pin_dropout_brute(orc):
+    """Dropout forward vs scalar loops over the definition with the keep mask
+    applied by hand (inverted dropout on the probabilities)."""
+    for ci, (causal, win, sl) in enumerate(MASK_CASES[:4]):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(1800 + ci)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.41, softmax_type=st,
+                      softmax_offset=alpha, seqlens=None if sl is None else np.array(sl))
+            r = orc.attention_dropout(q, k, v, None, p=0.3, seed=99, offset=3, **kw)
+            base = orc.attention(q, k, v, None, **kw)
+            zs = 1.0 / (1.0 - orc.dropout_threshold(0.3) / 256.0)
+            B, S, Hq = q.shape[:3]
+            o = np.zeros_like(r["o"])
+            for b in range(B):
+                for h in range(Hq):
+                    keep = orc.dropout_keep(b, h, np.arange(S), np.arange(S), num_heads=Hq, p=0.3, seed=99,
+                                            offset=3)
+                    for i in range(S):
+                        for j in range(S):
+                            if not np.isfinite(base["lse"][b, h, i]):
+                                continue
+                            pij = math.exp(0.41 * float(q[b, i, h] @ k[b, j, h // 2]) - base["lse"][b, h, i])
+                            vis = (sl is None or (i < sl[b] and j < sl[b])) and (not causal or j <= i) and \
+                                (win[0] < 0 or j >= i - win[0]) and (win[1] < 0 or j <= i + win[1])
+                            if vis and keep[i, j]:
+                                o[b, i, h] += pij * zs * v[b, j, h // 2]
+            _close(r["o"], o, 1e-12, 1e-14, f"dropout O case{ci} {st}")
+            _close(r["lse"], base["lse"], 0, 0, "dropout leaves the LSE unchanged")
+
+
+def pin_dropout_p0(orc):
+    """p = 0 keeps every pair: identical to attention() in every output."""
+    q, k, v, do, alpha = rand_case(1900)
+    kw = dict(num_gqa_groups=2, causal=True, window=(3, 0), scale_factor=0.5, softmax_type="learnable",
+              softmax_offset=alpha, seqlens=np.array([9, 6]))
+    r = orc.attention_dropout(q, k, v, do, p=0.0, seed=1, offset=0, **kw)
+    base = orc.attention(q, k, v, do, **kw)
+    for n in ("o", "lse", "dq", "dk", "dv", "dalpha"):
+        _close(r[n], base[n], 0, 0, f"p=0 {n}")
+
+
+def pin_dropout_finite_diff(orc):
+    """Dropout dQ, dK, dV, d(alpha) vs central differences (the mask is a
+    fixed function of the seed, so the loss is differentiable)."""
+    hstep = 1e-6
+    for st in orc.SOFTMAX_TYPES:
+        q, k, v, do, alpha = rand_case(2000, B=1, S=6, Hq=2, Hkv=1, dqk=2, dv=2)
+        kw = dict(p=0.45, seed=0xABCDEF12345, offset=11, num_gqa_groups=1, causal=False, window=(3, 1),
+                  scale_factor=0.7, softmax_type=st, seqlens=np.array([5]))
+
+        def loss(qq, kk, vv, al):
+            return float((orc.attention_dropout(qq, kk, vv, None, softmax_offset=al, **kw)["o"] * do).sum())
+
+        r = orc.attention_dropout(q, k, v, do, softmax_offset=alpha, **kw)
+        assert 0 < r["keep"].mean() < 1
+        for name, arr, grad in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                a0 = arr[idx]
+                arr[idx] = a0 + hstep
+                lp = loss(q, k, v, alpha)
+                arr[idx] = a0 - hstep
+                lm = loss(q, k, v, alpha)
+                arr[idx] = a0
+                fd[idx] = (lp - lm) / (2 * hstep)
+            _close(grad, fd, 1e-6, 1e-8, f"dropout d{name} {st}")
+        if st == "learnable":
+            fd = np.zeros(alpha.size)
+            for hh in range(alpha.size):
+                a2 = alpha.copy()
+                a2[hh] += hstep
+                lp = loss(q, k, v, a2)
+                a2[hh] -= 2 * hstep
+                lm = loss(q, k, v, a2)
+                fd[hh] = (lp - lm) / (2 * hstep)
+            _close(r["dalpha"], fd, 1e-6, 1e-8, "dropout dalpha")
+
+
+def pin_dropout_mean(orc):
+    """Inverted dropout is unbiased: O averaged over many offsets approaches
+    the undropped O (200 draws; loose bound)."""
+    q, k, v, do, alpha = rand_case(2100, B=1, S=8, Hq=2, Hkv=1)
+    kw = dict(num_gqa_groups=1, causal=True, scale_factor=0.5)
+    base = orc.attention(q, k, v, None, **kw)["o"]
+    acc = np.zeros_like(base)
+    n = 200
+    for off in range(n):
+        acc += orc.attention_dropout(q, k, v, None, p=0.25, seed=3, offset=off, **kw)["o"]
+    err = np.abs(acc / n - base).max()
+    assert err < 0.15 * np.abs(base).max() + 0.05, err
+
+
+def pin_dropout_layout(orc):
+    """The documented pair -> generator-byte layout, spelled out: pair (i, j)
+    of (b, h) takes byte (i % 4) * 4 + j % 4 (word byte // 4, bits 8 (byte % 4)
+    up) of the call with counter (j // 4, i // 4, b * Hq + h, offset) and the
+    seed as key (low word first)."""
+    seed, offset, Hq, p = 0x0123456789ABCDEF, 77, 3, 0.5
+    t = orc.dropout_threshold(p)
+    keep = orc.dropout_keep(1, 2, np.arange(12), np.arange(20), num_heads=Hq, p=p, seed=seed, offset=offset)
+    for i in range(12):
+        for j in range(20):
+            words = orc.philox4x32_10(j // 4, i // 4, 1 * Hq + 2, offset, seed & 0xFFFFFFFF, seed >> 32)
+            byte_no = (i % 4) * 4 + j % 4
+            byte = (int(words[byte_no // 4]) >> (8 * (byte_no % 4))) & 0xFF
+            assert keep[i, j] == (byte >= t), (i, j)
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
             pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
-            pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff]
+            pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff,
+            pin_philox_kat, pin_dropout_rate, pin_dropout_brute, pin_dropout_p0, pin_dropout_finite_diff,
+            pin_dropout_mean, pin_dropout_layout]

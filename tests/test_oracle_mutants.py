@@ -46,6 +46,15 @@ MUTANTS = {
     "packed_padding_ignored": [("valid[off[b]:off[b] + L] = True", "valid[off[b]:off[b + 1]] = True")],
     "packed_lse_shifted_rows": [('res["lse"][b, h, :n] = lse_t[off[b]:off[b] + n]',
                                  'res["lse"][b, h, :n] = lse_t[b:b + n]')],
+    "philox_round_constant": [("PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57",
+                               "PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D59")],
+    "dropout_rows_keys_swapped": [("out = philox4x32_10(j >> np.uint64(2), i >> np.uint64(2),",
+                                   "out = philox4x32_10(i >> np.uint64(2), j >> np.uint64(2),")],
+    "dropout_byte_order": [("byte_idx = (i & np.uint64(3)) * np.uint64(4) + (j & np.uint64(3))",
+                            "byte_idx = (j & np.uint64(3)) * np.uint64(4) + (i & np.uint64(3))")],
+    "dropout_no_rescale": [("zmat = np.where(keep, zscale, 0.0)", "zmat = np.where(keep, 1.0, 0.0)")],
+    "dropout_dp_unmasked": [("dp = zmat * (doh @ vg.T)", "dp = doh @ vg.T")],
+    "dropout_dv_unmasked": [('res["dv"][b, :, g, :] += (pr * zmat).T @ doh', 'res["dv"][b, :, g, :] += pr.T @ doh')],
     "keys_rows_subset": [("rows_all = np.nonzero(sees.any(axis=1))[0]",
                           "rows_all = np.nonzero(sees.any(axis=1))[0][1:]")],
 }
@@ -57,7 +66,10 @@ ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_ca
          oracle_pins.pin_dalpha_forms, oracle_pins.pin_sink_augmented,
          oracle_pins.pin_torch_sdpa, oracle_pins.pin_finite_diff, oracle_pins.pin_sampled_rows,
          oracle_pins.pin_sampled_keys, oracle_pins.pin_packed_brute_force,
-         oracle_pins.pin_packed_equals_padded, oracle_pins.pin_packed_finite_diff]
+         oracle_pins.pin_packed_equals_padded, oracle_pins.pin_packed_finite_diff,
+         oracle_pins.pin_philox_kat, oracle_pins.pin_dropout_rate, oracle_pins.pin_dropout_p0,
+         oracle_pins.pin_dropout_brute, oracle_pins.pin_dropout_finite_diff, oracle_pins.pin_dropout_mean,
+         oracle_pins.pin_dropout_layout]
 
 
 def _mutant(edits):
