@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--layout", choices=("bshd", "thd"), default="bshd",
                     help="thd: the batch's sequences packed back to back at their valid lengths "
                          "(seq_offsets), no padding tokens stored")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="attention dropout rate (Philox keep mask regenerated in forward and backward)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) to "
                          "calibrate the HBM byte counters, then exit")
@@ -157,12 +159,14 @@ def main():
               softmax_type=p.softmax_type, softmax_offset=t["alpha"], seqlens=t["seqlens"])
     if packed:
         kw.update(seq_offsets=t["seq_offsets"], max_seqlen=p.S)
+    if args.dropout:
+        kw.update(dropout_p=args.dropout, rng_state=(seed, 0))
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     want = p.softmax_type != "vanilla"
     dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
     outs = (dq, dk, dv, doff)
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"],
-                             p.window, kw["scale_factor"], p.softmax_type)
+                             p.window, kw["scale_factor"], p.softmax_type, args.dropout)
     ws = torch.empty(binding.attn_bwd_workspace_size(pp), dtype=torch.uint8, device="cuda")
     fast = dict(kw, check_seqlens=False)
     stream = torch.cuda.current_stream()
@@ -233,7 +237,8 @@ def main():
     achieved = kflops[dominant] * pairs / (avg_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, dominant) if args.case == 0 and not packed else None,
+                "traffic": (measured_traffic(args.config, dominant)
+                            if args.case == 0 and not packed and not args.dropout else None),
                 "flops_per_launch": kflops[dominant] * pairs, "avg_launch_ms": round(avg_ms[dominant], 4)}
 
     res = {
@@ -253,7 +258,7 @@ def main():
                    "num_gqa_groups": p.Hkv, "head_dim_qk": p.d_qk, "head_dim_v": p.d_v,
                    "mask": "causal" if p.causal else "none", "window": list(p.window),
                    "softmax_type": p.softmax_type, "seed": seed,
-                   "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout,
+                   "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout, "dropout": args.dropout,
                    "tokens": int(t["q"].shape[0]) if packed else p.B * p.S},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "pairs": pairs,

@@ -91,7 +91,8 @@ extern "C" {
 #define ATTN_ERR_WORKSPACE (-3)     /* workspace_bytes below the required size */
 #define ATTN_ERR_HIP (-4)           /* a HIP launch failed */
 
-/* Problem description.  All fields are plain int32/float for a fixed ABI. */
+/* Problem description.  All fields are plain 32-bit integers or floats for a
+ * fixed ABI. */
 struct attn_params {
   int32_t batch;          /* B >= 1 */
   int32_t seqlen;         /* S >= 1, shared by queries and keys (self-attention) */
@@ -105,6 +106,23 @@ struct attn_params {
   int32_t window_right;   /* >= -1; -1 = unbounded */
   float scale_factor;     /* finite, >= 0; 0 => 1/sqrt(Dqk) */
   int32_t softmax_type;   /* ATTN_SOFTMAX_* */
+  /* Attention dropout (TE single-GPU page, "Other attention knobs": a rate
+   * and an RNG; PR #2225's forward returns an rng_state).  Reading: inverted
+   * dropout on the softmax probabilities, O = (P * Z) V with
+   * Z = keep / (1 - t/256), t = round(256 * dropout_p) (the rate is
+   * quantised to 1/256; t = 0 disables dropout); the LSE is unchanged.  keep
+   * comes from Philox4x32-10 (Salmon et al., SC 2011): one call per 4 x 4
+   * block of (query row i, key j) pairs of batch b, query head h, counter
+   * (j >> 2, i >> 2, b * num_heads + h, dropout_offset), key (seed_lo,
+   * seed_hi); pair (i, j) takes byte (i & 3) * 4 + (j & 3) of the output
+   * (word byte / 4, bits 8 * (byte % 4) up) and is kept iff that byte >= t.
+   * The (seed, offset) pair is the rng state: pass the same values to the
+   * forward and the backward of one step, and advance the offset between
+   * steps. */
+  float dropout_p;           /* in [0, 1) */
+  uint32_t dropout_seed_lo;  /* generator key, low word */
+  uint32_t dropout_seed_hi;  /* generator key, high word */
+  uint32_t dropout_offset;   /* counter word 3 */
 };
 
 /* Host-only check of a problem description; no HIP call.  Returns ATTN_OK,
@@ -190,6 +208,11 @@ int attn_debug_tile_map(const struct attn_params* p, const int32_t* seqlens, int
 /* Device: out[b][i][j] (uint8, device, B*S*S entries) = 1 iff query i sees key j. */
 int attn_debug_mask_probe(const struct attn_params* p, const int32_t* seqlens, uint8_t* out,
                           void* stream);
+
+/* Device: out[b][h][i][j] (uint8, device, B*Hq*S*S entries) = 1 iff pair
+ * (i, j) of batch b, query head h is kept by dropout (every pair, visible or
+ * not), from the same device generator the kernels use. */
+int attn_debug_dropout_mask(const struct attn_params* p, uint8_t* out, void* stream);
 
 /* Host: same tile map from host seqlens (NULL = all S) into host memory. */
 int attn_host_tile_map(const struct attn_params* p, const int32_t* seqlens, int32_t block_m,

@@ -31,7 +31,9 @@ class Params(ctypes.Structure):
                 ("num_gqa_groups", _c_i32), ("head_dim_qk", _c_i32), ("head_dim_v", _c_i32),
                 ("dtype", _c_i32), ("mask_type", _c_i32), ("window_left", _c_i32),
                 ("window_right", _c_i32), ("scale_factor", ctypes.c_float),
-                ("softmax_type", _c_i32)]
+                ("softmax_type", _c_i32), ("dropout_p", ctypes.c_float),
+                ("dropout_seed_lo", ctypes.c_uint32), ("dropout_seed_hi", ctypes.c_uint32),
+                ("dropout_offset", ctypes.c_uint32)]
 
 
 class AttnError(RuntimeError):
@@ -55,6 +57,7 @@ EXPORTS = {
                                            ctypes.POINTER(_c_i32)]),
     "attn_debug_tile_map": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _c_i32, _c_i32, _vp, _vp]),
     "attn_debug_mask_probe": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp]),
+    "attn_debug_dropout_mask": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp]),
     "attn_host_tile_map": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _c_i32, _c_i32, _vp]),
     "attn_host_key_range": (ctypes.c_int, [ctypes.POINTER(Params), _c_i32, _c_i32, _c_i32,
                                            ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
@@ -88,10 +91,15 @@ def load_library(path: str | None = None):
 
 
 def make_params(B, S, Hq, Hkv, d_qk, d_v, dtype="bf16", attn_mask_type="causal",
-                window_size=(-1, -1), scale_factor=None, softmax_type="vanilla") -> Params:
+                window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", dropout_p=0.0,
+                rng_state=(0, 0)) -> Params:
+    """rng_state = (seed, offset): the 64-bit generator key and the 32-bit
+    counter word of attention dropout (same values for forward and backward)."""
+    seed, offset = (int(x) for x in rng_state)
     return Params(B, S, Hq, Hkv, d_qk, d_v, ATTN_BF16 if dtype == "bf16" else ATTN_F32,
                   MASKS[attn_mask_type], int(window_size[0]), int(window_size[1]),
-                  float(scale_factor or 0.0), SOFTMAX[softmax_type])
+                  float(scale_factor or 0.0), SOFTMAX[softmax_type], float(dropout_p),
+                  seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF, offset & 0xFFFFFFFF)
 
 
 def _check(rc, where):
@@ -168,7 +176,7 @@ def _packed_layout(q, seq_offsets, seqlens, max_seqlen):
 
 
 def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
-             packed=None):
+             packed=None, dropout_p=0.0, rng_state=(0, 0)):
     """Params for BSHD tensors, or for packed [T, H, D] tensors when
     packed = (B, S) comes from _packed_layout."""
     torch = _torch()
@@ -194,7 +202,7 @@ def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor,
         raise ValueError("dtype must be bfloat16 or float32")
     dtype = "bf16" if q.dtype == torch.bfloat16 else "f32"
     return make_params(B, S, Hq, Hkv, dqk, v.shape[-1], dtype, attn_mask_type, window_size,
-                       scale_factor, softmax_type)
+                       scale_factor, softmax_type, dropout_p, rng_state)
 
 
 def _check_seqlens(seqlens, B, S):
@@ -226,16 +234,20 @@ def _layout(q, seq_offsets, seqlens, max_seqlen, check):
 
 def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_size=(-1, -1),
              scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None,
-             seq_offsets=None, max_seqlen=None, out=None, lse=None, stream=None, check_seqlens=True):
+             seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0), out=None, lse=None,
+             stream=None, check_seqlens=True):
     """Forward attention.  Returns (O, LSE [B,Hq,S]).
 
     BSHD: q [B,S,Hq,Dqk], k/v [B,S,Hkv,D], O [B,S,Hq,Dv].  Packed (THD, when
     seq_offsets [B+1] is given): q [T,Hq,Dqk], k/v [T,Hkv,D], O [T,Hq,Dv];
-    S = max_seqlen or the largest segment.
+    S = max_seqlen or the largest segment.  dropout_p > 0 applies attention
+    dropout with the generator state rng_state = (seed, offset); pass the
+    same values to attn_bwd.
     """
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
-    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
+                 dropout_p, rng_state)
     B, S, Hq = p.batch, p.seqlen, p.num_heads
     if check_seqlens and packed is None:
         _check_seqlens(seqlens, B, S)
@@ -259,17 +271,19 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
 
 def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causal",
              window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
-             seqlens=None, seq_offsets=None, max_seqlen=None, want_d_offset=None, workspace=None,
-             outs=None, stream=None, check_seqlens=True, stage=0):
+             seqlens=None, seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0),
+             want_d_offset=None, workspace=None, outs=None, stream=None, check_seqlens=True, stage=0):
     """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None).
 
     d_softmax_offset is returned for learnable softmax (always) and for
     off-by-one when want_d_offset is true; vanilla returns None.  Layouts as
-    for attn_fwd (packed THD when seq_offsets is given).
+    for attn_fwd (packed THD when seq_offsets is given); dropout_p and
+    rng_state must match the forward's.
     """
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
-    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed)
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
+                 dropout_p, rng_state)
     B, S, Hq, Hkv = p.batch, p.seqlen, p.num_heads, p.num_gqa_groups
     if check_seqlens and packed is None:
         _check_seqlens(seqlens, B, S)
@@ -324,6 +338,15 @@ def debug_mask_probe(p: Params, seqlens, stream=None):
     out = torch.empty((p.batch, p.seqlen, p.seqlen), dtype=torch.uint8, device="cuda")
     _check(load_library().attn_debug_mask_probe(ctypes.byref(p), _ptr(seqlens), _ptr(out),
                                                 _stream(stream)), "attn_debug_mask_probe")
+    return out
+
+
+def debug_dropout_mask(p: Params, stream=None):
+    """Device keep decisions of attention dropout, uint8 [B, Hq, S, S]."""
+    torch = _torch()
+    out = torch.empty((p.batch, p.num_heads, p.seqlen, p.seqlen), dtype=torch.uint8, device="cuda")
+    _check(load_library().attn_debug_dropout_mask(ctypes.byref(p), _ptr(out), _stream(stream)),
+           "attn_debug_dropout_mask")
     return out
 
 

@@ -27,6 +27,7 @@ int check_fields(const attn_params* p) {
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(p->scale_factor) || p->scale_factor < 0.0f) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type < ATTN_SOFTMAX_VANILLA || p->softmax_type > ATTN_SOFTMAX_LEARNABLE) return ATTN_ERR_INVALID_ARG;
+  if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return ATTN_ERR_INVALID_ARG;  // also rejects NaN
   // Kernels index rows with 32-bit (batch * S + i) and launch one-dimensional
   // grids of B * heads * tiles workgroups.
   const long long rows = (long long)p->batch * p->seqlen;
@@ -76,6 +77,14 @@ KArgs make_args(const attn_params* p) {
   a.scale_log2 = a.scale * kLog2e;
   a.n_chunks = n_chunks(p);
   a.n_splits = kv_splits(p);
+  // Dropout: byte threshold round(256 p), kept probabilities scaled by
+  // 1 / (1 - t / 256); t = 0 (p < 1/512) means no dropout.
+  const double t = floor(256.0 * (double)p->dropout_p + 0.5);
+  a.drop_t = t > 255.0 ? 255 : (int)t;
+  a.drop_scale = (float)(1.0 / (1.0 - a.drop_t / 256.0));
+  a.drop_seed_lo = p->dropout_seed_lo;
+  a.drop_seed_hi = p->dropout_seed_hi;
+  a.drop_offset = p->dropout_offset;
   return a;
 }
 
@@ -238,6 +247,13 @@ int attn_debug_tile_map(const attn_params* p, const int32_t* seqlens, int32_t bl
   KArgs a = make_args(p);
   a.seqlens = seqlens;
   return hip_status(launch_debug_tile_map(a, block_m, block_n, out, static_cast<hipStream_t>(stream)));
+}
+
+int attn_debug_dropout_mask(const attn_params* p, uint8_t* out, void* stream) {
+  const int rc = check_fields(p);
+  if (rc != ATTN_OK) return rc;
+  if (!out) return ATTN_ERR_INVALID_ARG;
+  return hip_status(launch_debug_dropout_mask(make_args(p), out, static_cast<hipStream_t>(stream)));
 }
 
 int attn_debug_mask_probe(const attn_params* p, const int32_t* seqlens, uint8_t* out, void* stream) {

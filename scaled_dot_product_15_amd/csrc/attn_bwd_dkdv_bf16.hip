@@ -48,8 +48,15 @@
 // swizzled row-major LDS tile (RowReads); contractions over the sequence take
 // the accumulator-side operand straight from registers and the other one
 // with LDS transpose loads from the same tile (TrReads).
+//
+// DROP (attention dropout, dropout.h): with Z = keep / (1 - p), dV = (P Z)^T
+// dO and dS = P (Z dP - delta).  B keeps P * keep for dV (the 1 / (1 - p)
+// factor is applied once, to dV at the end) and P (Z dP - delta) for dK; the
+// random bytes of a lane's key and one 4-row group come from one generator
+// call, which is exactly one pipeline chunk's share of B.
 #include <type_traits>
 
+#include "dropout.h"
 #include "launch.h"
 
 // Issue pattern inside a pipeline chunk (build-time overridable for tuning
@@ -75,15 +82,15 @@ struct DkdvCfg {
   static constexpr int LDS_ELEMS = NBUF * STAGE;
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   using C = DkdvCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   // Ring slot `buf`: Q [BMQ][DQK], dO [BMQ][DV] (swizzled), lse2 [BMQ], delta [BMQ].
-  auto qtile = [&](int buf) { return lds + buf * C::STAGE; };
-  auto otile = [&](int buf) { return lds + buf * C::STAGE + C::QT; };
-  auto lse_s = [&](int buf) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT); };
-  auto delta_s = [&](int buf) { return lse_s(buf) + C::BMQ; };
+  auto qtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE; };
+  auto otile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::QT; };
+  auto lse_s = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT); };
+  auto delta_s = [&](int buf) __attribute__((always_inline)) { return lse_s(buf) + C::BMQ; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Workgroup id -> (key tile, batch, kv head, head split): consecutive ids
@@ -99,6 +106,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   r /= nsp;
   const int b = r / a.Hkv, g = r % a.Hkv;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const DropGen dg = drop_gen(a);
   const int j0 = kt * C::BN;
   const int kj = j0 + w * 32 + l32;
   int qlo_k, qhi_k;  // rows that see this lane's key
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     int t, hh, q0;
   };
   const int q_first = qs0 * C::BMQ, q_last = (qs0 + nsteps - 1) * C::BMQ;
-  auto walk_next = [&](StageWalk& st) {
+  auto walk_next = [&](StageWalk& st) __attribute__((always_inline)) {
     ++st.t;
     st.q0 += C::BMQ;
     if (st.q0 > q_last) {
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const RowReads<C::OCH> ord(lane);
   const TrReads<C::QCH> qtr(lane);
   const TrReads<C::OCH> otr(lane);
-  auto issue_stage = [&](const StageWalk& st, int buf) {
+  auto issue_stage = [&](const StageWalk& st, int buf) __attribute__((always_inline)) {
     const int h = g * a.G + hs * Gs + st.hh;
     const int q0 = st.q0;
     qcopy.issue(Qg + (row0 * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   u32x4 PW[2][2], DW[2][2];  // bf16 P / dS pairs: B operands of the block's two 16-row K-steps
 
   // A(u): S and dP of block u (rows rb .. rb+31 of a ring slot).
-  auto phase_a = [&](const uint16_t* Qs, const uint16_t* Os, int rb, f32x16& s, f32x16& dp) {
+  auto phase_a = [&](const uint16_t* Qs, const uint16_t* Os, int rb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     s = f32x16{};
     dp = f32x16{};
 #pragma unroll
@@ -208,14 +216,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   };
   // B(u): element i of the accumulators is query row qrow0 + acc_row(i, hf),
   // key kj; lse2 / delta come from the stage at offset rb.
-  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, const f32x16& s, const f32x16& dp,
-                     u32x4(&pw)[2], u32x4(&dw)[2]) {
+  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, int bh, const f32x16& s, const f32x16& dp,
+                     u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
     const int lo_r = qlo_k - (qrow0 + hf * 4), hi_r = qhi_k - (qrow0 + hf * 4);
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
       const int qo = rb + ig * 8 + hf * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qo);
+      uint32_t rnd = 0;  // dropout bytes of rows qrow0 + ig*8 + hf*4 + 0..3, key kj
+      if constexpr (DROP) rnd = drop_bytes_col(dg, bh, qrow0 + ig * 8 + hf * 4, kj);
       u32x2 pp, dd;
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
@@ -226,8 +236,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
           const int off = ig * 8 + e;
           float pv = fast_exp2(fmaf(s[i], c, -l4[e]));
           pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
-          p2[v] = pv;
-          s2[v] = pv * (dp[i] - d4[e]);
+          float pk = pv, dpz = dp[i];
+          if constexpr (DROP) {
+            const bool kp = drop_keep(rnd, e, dg.t);
+            pk = kp ? pv : 0.0f;
+            dpz = kp ? dpz * dg.scale : 0.0f;
+          }
+          p2[v] = pk;
+          s2[v] = pv * (dpz - d4[e]);
         }
         pp[u2] = pack_bf16(p2[0], p2[1]);
         dd[u2] = pack_bf16(s2[0], s2[1]);
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     }
   };
   // C(u): dV^T (dims x keys) += dO^T P ; dK^T (dims x keys) += Q^T dS.
-  auto phase_c = [&](const uint16_t* Qs, const uint16_t* Os, int rb, const u32x4(&pw)[2], const u32x4(&dw)[2]) {
+  auto phase_c = [&](const uint16_t* Qs, const uint16_t* Os, int rb, const u32x4(&pw)[2], const u32x4(&dw)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int pos0 = rb + kk * 16;
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   f32x4 l4[2], d4[2];
   // Chunk k's LDS reads for the iteration of phase P into set st: A(u+1)'s
   // operands (RA), C(u-1)'s (RC), B(u)'s lse2 / delta (RL).
-  auto read_chunk = [&](auto phase, auto kc, auto setc, auto ra, auto rc, auto rl) {
+  auto read_chunk = [&](auto phase, auto kc, auto setc, auto ra, auto rc, auto rl) __attribute__((always_inline)) {
     constexpr int P = decltype(phase)::value, k = decltype(kc)::value, st = decltype(setc)::value;
     constexpr int cur = P & 1, nxt = cur ^ 1;
     constexpr int slot_u = (P >> 1) % 3, slot_n = ((P + 1) >> 1) % 3, slot_p = ((P + 5) >> 1) % 3;
@@ -307,13 +323,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // First chunk of the iteration after the one of phase P, read ahead.  When
   // that iteration opens a stage (odd phase) its A operands are only there
   // after its barrier, so they are read then.
-  auto read_ahead = [&](auto phase) {
+  auto read_ahead = [&](auto phase) __attribute__((always_inline)) {
     constexpr int PN = (decltype(phase)::value + 1) % 6;
     using PNC = std::integral_constant<int, PN>;
     if constexpr ((PN & 1) != 0) read_chunk(PNC{}, C0{}, C0{}, T0{}, T1{}, T1{});
     else read_chunk(PNC{}, C0{}, C0{}, T1{}, T1{}, T1{});
   };
-  auto iteration = [&](int u, auto phase) {
+  auto iteration = [&](int u, auto phase) __attribute__((always_inline)) {
     constexpr int P = decltype(phase)::value;
     constexpr int cur = P & 1, nxt = cur ^ 1;
     constexpr int slot_u = (P >> 1) % 3;
@@ -332,8 +348,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     const float* ls = lse_s(slot_u);  // B(u): rows cur*32 of its stage
     const float* dl = delta_s(slot_u);
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
+    const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
 
-    auto compute_chunk = [&](auto kc, auto setc) {
+    auto compute_chunk = [&](auto kc, auto setc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
@@ -351,6 +368,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       // accumulator elements 4k .. 4k+3, which are B-operand elements
       // (k%2)*4 .. +3 of K-step k/2.  Blocks that need the mask redo B below.
       u32x2 pp, dd;
+      uint32_t rnd = 0;  // dropout bytes of rows q_u + k*8 + hf*4 + 0..3, key kj
+      if constexpr (DROP) rnd = drop_bytes_col(dg, bh_u, q_u + k * 8 + hf * 4, kj);
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         float p2[2], s2[2];
@@ -358,8 +377,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         for (int v = 0; v < 2; ++v) {
           const int e = u2 * 2 + v, i = k * 4 + e;
           const float pv = fast_exp2(fmaf(S[cur][i], c, -l4[st][e]));
-          p2[v] = pv;
-          s2[v] = pv * (DP[cur][i] - d4[st][e]);
+          float pk = pv, dpz = DP[cur][i];
+          if constexpr (DROP) {
+            const bool kp = drop_keep(rnd, e, dg.t);
+            pk = kp ? pv : 0.0f;
+            dpz = kp ? dpz * dg.scale : 0.0f;
+          }
+          p2[v] = pk;
+          s2[v] = pv * (dpz - d4[st][e]);
         }
         pp[u2] = pack_bf16(p2[0], p2[1]);
         dd[u2] = pack_bf16(s2[0], s2[1]);
@@ -377,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Within a chunk: each MFMA followed by LDS reads and VALU work, so the
     // next MFMA is not issued while the matrix unit is still busy (a stalled
     // MFMA would hold up every instruction behind it).
-    auto pattern = [&]() {
+    auto pattern = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < EA + EC; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
@@ -408,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Blocks that some of this wave's (row, key) pairs cannot see (diagonal,
     // window edge, padding): redo B with the mask.
     if (!(q_u >= all_lo && q_u + 31 <= all_hi))
-      phase_b(ls, dl, cur * 32, q_u, S[cur], DP[cur], PW[cur], DW[cur]);
+      phase_b(ls, dl, cur * 32, q_u, bh_u, S[cur], DP[cur], PW[cur], DW[cur]);
   };
 
   if (NB > 0) {
@@ -423,7 +448,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Block 0 has no predecessor: A(0), then A(1) with B(0).
     phase_a(qtile(0), otile(0), 0, S[0], DP[0]);
     phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
-    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, S[0], DP[0], PW[0], DW[0]);
+    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, b * a.Hq + g * a.G + hs * Gs + b_walk.hh, S[0], DP[0], PW[0],
+            DW[0]);
     read_ahead(std::integral_constant<int, 0>{});  // first chunk of iteration 1
     // Iterations 1 .. NI in trips of six (one per phase), padded past the
     // last block NB-1 with empty blocks: their stages copy rows past the
@@ -461,12 +487,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
-          u32x2 val = {pack_bf16(dv[db][ig * 4], dv[db][ig * 4 + 1]),
-                       pack_bf16(dv[db][ig * 4 + 2], dv[db][ig * 4 + 3])};
+          const float zs = DROP ? dg.scale : 1.0f;
+          u32x2 val = {pack_bf16(dv[db][ig * 4] * zs, dv[db][ig * 4 + 1] * zs),
+                       pack_bf16(dv[db][ig * 4 + 2] * zs, dv[db][ig * 4 + 3] * zs)};
           *reinterpret_cast<u32x2*>(dvp + db * 32 + ig * 8) = val;
         }
     } else {
-      // fp32 partials of this split (dK unscaled), same element order as dK / dV.
+      // fp32 partials of this split (dK without the softmax scale, dV without
+      // the dropout scale), same element order as dK / dV.
       const size_t row = ((size_t)(hs * a.B + b) * a.S + kj) * a.Hkv + g;
       float* dkp = a.kv_part + row * DQK + hf * 4;
       float* dvp = a.kv_part + (size_t)nsp * a.B * a.S * a.Hkv * DQK + row * DV + hf * 4;
@@ -512,17 +540,21 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* par
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void bwd_dkdv_bf16_kernel<64, 64>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<192, 128>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, true>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   using D = DkdvCfg<DQK, DV>;
   static_assert(D::BN == kDkdvKeyTile, "split rule uses the kernel's key tile");
   const int nkt = (a.S + D::BN - 1) / D::BN;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV>), dim3((unsigned)(nkt * a.B * a.Hkv * a.n_splits)), dim3(D::NT),
-                     0, stream, a);
+  const dim3 grid((unsigned)(nkt * a.B * a.Hkv * a.n_splits));
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true>), grid, dim3(D::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false>), grid, dim3(D::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -535,7 +567,7 @@ int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, 
   if (span > S) span = S;
   long long stages = (span + 63) / 64 + 1;
   if (stages > (S + 63) / 64) stages = (S + 63) / 64;
-  auto fits = [&](int d) { return base * d >= kDkdvMinGrid && 2 * stages * (G / d) <= kDkdvMaxBlocks; };
+  auto fits = [&](int d) __attribute__((always_inline)) { return base * d >= kDkdvMinGrid && 2 * stages * (G / d) <= kDkdvMaxBlocks; };
   int want = G;
   for (int d = 1; d <= G; ++d)
     if (G % d == 0 && fits(d)) {
@@ -557,7 +589,8 @@ hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t
                      a.kv_part, static_cast<uint16_t*>(a.dk), nk, a.n_splits, a.scale, a.seq_offsets, a.S,
                      a.Hkv * dqk);
   hipLaunchKernelGGL(dkdv_split_reduce_kernel, dim3((unsigned)((nv / 4 + 255) / 256)), dim3(256), 0, stream,
-                     a.kv_part + (size_t)a.n_splits * nk, static_cast<uint16_t*>(a.dv), nv, a.n_splits, 1.0f,
+                     a.kv_part + (size_t)a.n_splits * nk, static_cast<uint16_t*>(a.dv), nv, a.n_splits,
+                     a.drop_t > 0 ? a.drop_scale : 1.0f,
                      a.seq_offsets, a.S, a.Hkv * dv);
   return hipGetLastError();
 }

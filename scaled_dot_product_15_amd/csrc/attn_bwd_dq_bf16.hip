@@ -16,8 +16,12 @@
 // accumulator-side operand straight from registers and the other one with
 // LDS transpose loads from the same tile (TrReads).  Tiles arrive by
 // direct memory-to-LDS copies, double buffered, one barrier per step.
+//
+// DROP (attention dropout, dropout.h): with Z = keep / (1 - p),
+// dS = P * (Z dP - delta); delta = rowsum(dO * O) already holds the dropped O.
 #include <type_traits>
 
+#include "dropout.h"
 #include "launch.h"
 
 // Tile parameters (build-time overridable for tuning sweeps).
@@ -42,12 +46,12 @@ struct DqCfg {
   static constexpr int LDS_ELEMS = 2 * (KT + VT);
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArgs a) {
   using C = DqCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
-  auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
+  auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
+  auto vtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT) + C::KT; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Same tile order as the forward: heavy query tiles first, the heads of a
@@ -67,6 +71,8 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
   }
   const int g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const int bh = b * a.Hq + h;
+  const DropGen dg = drop_gen(a);
   const int i0 = qt * C::BM, qw0 = i0 + w * 32, qi = qw0 + l32;
   int klo, khi;
   row_key_bounds(m, qi, klo, khi);
@@ -136,12 +142,12 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
   const RowReads<C::KCH> krd(lane);
   const RowReads<C::VCH> vrd(lane);
   const TrReads<C::KCH> ktr(lane);
-  auto issue_tile = [&](int j0, int buf) {
+  auto issue_tile = [&](int j0, int buf) __attribute__((always_inline)) {
     kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
     vcopy.issue(Vg, (uint32_t)(vstride * 2), j0, m.L, vtile(buf));
   };
 
-  auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) {
+  auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     f32x16 st[C::BN / 32], dpt[C::BN / 32];
 #pragma unroll
@@ -160,6 +166,13 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
     prio_valu();
     // Element i of block kb: key j0 + hf*4 + kb*32 + acc_row(i, 0), query qi.
     const int base = j0 + hf * 4;
+    uint32_t rnd[C::BN / 32][4];  // dropout bytes of keys base + kb*32 + g*8 + 0..3
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, base + kb * 32 + g4 * 8);
+    }
     const int lo_r = klo - base, hi_r = khi - base;
     bf16x8 dsb[C::BN / 16];
 #pragma unroll
@@ -178,7 +191,9 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
               const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
               pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
             }
-            v2[u] = pv * (dpt[kb][i] - dl);
+            float dpz = dpt[kb][i];
+            if constexpr (DROP) dpz = drop_keep(rnd[kb][i >> 2], i & 3, dg.t) ? dpz * dg.scale : 0.0f;
+            v2[u] = pv * (dpz - dl);
           }
           t[e] = pack_bf16(v2[0], v2[1]);
         }
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
       }
     }
   }
-  auto step = [&](int kt, auto bufc, auto masked) {
+  auto step = [&](int kt, auto bufc, auto masked) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int j0 = kt * C::BN;
     if (kt < kt1) issue_tile(j0 + C::BN, buf ^ 1);
@@ -259,16 +274,20 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void bwd_dq_bf16_kernel<64, 64>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<128, 128>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<192, 128>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<192, 128, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<192, 128, true>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dq_cfg(KArgs a, hipStream_t stream) {
   using Q = DqCfg<DQK, DV>;
   a.n_tiles = (a.S + Q::BM - 1) / Q::BM;
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV>), dim3((unsigned)(a.n_tiles * a.B * a.Hq)), dim3(Q::NT), 0,
-                     stream, a);
+  const dim3 grid((unsigned)(a.n_tiles * a.B * a.Hq));
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, true>), grid, dim3(Q::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, false>), grid, dim3(Q::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,9 @@ struct KArgs {
   int n_tiles;          // tiles along the sequence for this kernel's grid
   int n_chunks;         // dz partial chunks per (b, h)
   int n_splits;         // dK/dV workgroups per (key tile, batch, kv head), each over G / n_splits query heads
+  int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
+  float drop_scale;     // 1 / (1 - drop_t / 256)
+  uint32_t drop_seed_lo, drop_seed_hi, drop_offset;  // generator key and counter word 3
 };
 
 // First row of batch b along the token axis of Q, K, V, O and the gradients:

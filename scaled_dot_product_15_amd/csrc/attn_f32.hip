@@ -9,6 +9,11 @@
 // (16 keys, or 16 query rows), staged in LDS and read as broadcasts.  The four
 // waves' partial results are combined at the end in wave order (a fixed
 // order, so results are reproducible).
+//
+// Attention dropout (dropout.h) draws one generator call per pair here: O
+// accumulates kept probabilities only and is scaled by 1 / (1 - p) at the
+// end; dV takes P * keep, dS = P (Z dP - delta) with Z = keep / (1 - p).
+#include "dropout.h"
 #include "launch.h"
 
 namespace sdpa {
@@ -38,6 +43,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
   const int qt = a.n_tiles - 1 - blockIdx.x / per;
   const int b = (blockIdx.x % per) / a.Hq, h = (blockIdx.x % per) % a.Hq, g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const DropGen dg = drop_gen(a);
   const int i0 = qt * kF32Tile, qi = i0 + lane;
   const float* Q = static_cast<const float*>(a.q);
 
@@ -64,15 +70,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
       if (!visible(m, qi, j0 + r)) continue;
       float s = 0.0f;
       for (int d = 0; d < DQK; ++d) s = fmaf(q[d], Ks[r][d], s);
+      const float kp = (dg.t > 0 && !drop_keep_pair(dg, b * a.Hq + h, qi, j0 + r)) ? 0.0f : 1.0f;
       if (s > mrun) {
         const float c = expf(mrun - s);
         l = l * c + 1.0f;
-        for (int d = 0; d < DV; ++d) o[d] = fmaf(o[d], c, Vs[r][d]);
+        for (int d = 0; d < DV; ++d) o[d] = fmaf(o[d], c, kp * Vs[r][d]);
         mrun = s;
       } else {
         const float p = expf(s - mrun);
         l += p;
-        for (int d = 0; d < DV; ++d) o[d] = fmaf(p, Vs[r][d], o[d]);
+        for (int d = 0; d < DV; ++d) o[d] = fmaf(kp * p, Vs[r][d], o[d]);
       }
     }
   }
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(KArgs a) {
       mrun = mn;
     }
     if (qi < seq_rows(a, b)) {
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const float inv = l > 0.0f ? (dg.t > 0 ? dg.scale : 1.0f) / l : 0.0f;
       float* O = static_cast<float*>(a.out_o) + ((seq_row0(a, b) + qi) * a.Hq + h) * DV;
       for (int d = 0; d < DV; ++d) O[d] = o[d] * inv;
     }
@@ -115,6 +122,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
   const int kt = blockIdx.x / per;
   const int b = (blockIdx.x % per) / a.Hkv, g = (blockIdx.x % per) % a.Hkv;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const DropGen dg = drop_gen(a);
   const int j0 = kt * kF32Tile, kj = j0 + lane;
   float kk[DQK], vv[DV], dk[DQK], dv[DV];
   {
@@ -145,8 +153,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
         for (int d = 0; d < DQK; ++d) s = fmaf(Qs[r][d], kk[d], s);
         for (int d = 0; d < DV; ++d) dp = fmaf(dOs[r][d], vv[d], dp);
         const float p = expf(s * a.scale - lse_s[r]);
+        float pk = p;
+        if (dg.t > 0) {
+          const bool kp = drop_keep_pair(dg, b * a.Hq + h, q0 + r, kj);
+          pk = kp ? p : 0.0f;
+          dp = kp ? dp * dg.scale : 0.0f;
+        }
         const float ds = p * (dp - delta_s[r]);
-        for (int d = 0; d < DV; ++d) dv[d] = fmaf(p, dOs[r][d], dv[d]);
+        for (int d = 0; d < DV; ++d) dv[d] = fmaf(pk, dOs[r][d], dv[d]);
         for (int d = 0; d < DQK; ++d) dk[d] = fmaf(ds, Qs[r][d], dk[d]);
       }
     }
@@ -164,7 +178,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(KArgs a) {
     }
     const size_t row = (seq_row0(a, b) + kj) * a.Hkv + g;
     for (int d = 0; d < DQK; ++d) static_cast<float*>(a.dk)[row * DQK + d] = dk[d] * a.scale;
-    for (int d = 0; d < DV; ++d) static_cast<float*>(a.dv)[row * DV + d] = dv[d];
+    const float zs = dg.t > 0 ? dg.scale : 1.0f;
+    for (int d = 0; d < DV; ++d) static_cast<float*>(a.dv)[row * DV + d] = dv[d] * zs;
   }
 }
 
@@ -178,6 +193,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(KArgs a) {
   const int qt = a.n_tiles - 1 - blockIdx.x / per;
   const int b = (blockIdx.x % per) / a.Hq, h = (blockIdx.x % per) % a.Hq, g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const DropGen dg = drop_gen(a);
   const int i0 = qt * kF32Tile, qi = i0 + lane;
   float q[DQK], dov[DV], dq[DQK];
   float lse = 0.0f, dl = 0.0f;
@@ -207,6 +223,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(KArgs a) {
       for (int d = 0; d < DQK; ++d) s = fmaf(q[d], Ks[r][d], s);
       for (int d = 0; d < DV; ++d) dp = fmaf(dov[d], Vs[r][d], dp);
       const float p = expf(s * a.scale - lse);
+      if (dg.t > 0) dp = drop_keep_pair(dg, b * a.Hq + h, qi, j0 + r) ? dp * dg.scale : 0.0f;
       const float ds = p * (dp - dl);
       for (int d = 0; d < DQK; ++d) dq[d] = fmaf(ds, Ks[r][d], dq[d]);
     }

@@ -28,9 +28,14 @@
 // by 2^8, harmless in fp32/bf16, and the final O = acc / l and
 // LSE = m + log2(l) are exact whichever max was used.  A sink logit z starts
 // the running max at z with row sum 1 (its own exp term).
+//
+// DROP (attention dropout): the P tile fed to P V keeps a probability only
+// where the pair's random byte passes the threshold (dropout.h); the row sum
+// takes every probability, and O is scaled by 1 / (1 - p) in the epilogue.
 #include <type_traits>
 
 #include "attn_common.h"
+#include "dropout.h"
 #include "launch.h"
 
 // Tile parameters (build-time overridable for tuning sweeps).
@@ -76,7 +81,7 @@ __device__ __forceinline__ void fwd_tile_of(const KArgs& a, int bid, int& b, int
   h = r % a.Hq;
 }
 
-template <int DQK, int DV, int BN, int OCC>
+template <int DQK, int DV, int BN, int OCC, bool DROP>
 __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
@@ -85,6 +90,8 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   int b, h, qt;
   fwd_tile_of(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
+  const int bh = b * a.Hq + h;
+  const DropGen dg = drop_gen(a);
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int i0 = qt * C::BM;
   const int row_w0 = i0 + w * 32;
@@ -127,8 +134,8 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   const int kt0 = lo / BN, kt1 = hi < 0 ? -1 : hi / BN;
 
   // K / V tiles of buffer `buf`: [BN][DQK] and [BN][DV], swizzled row-major.
-  auto ktile = [&](int buf) { return lds + buf * (C::KT + C::VT); };
-  auto vtile = [&](int buf) { return lds + buf * (C::KT + C::VT) + C::KT; };
+  auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
+  auto vtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT) + C::KT; };
 
   // Software pipeline over key tiles: iteration k finishes tile k (mask,
   // online softmax, P V) and computes the scores of tile k+1, so the score
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   // barrier that closes the iteration.  The scores of the tile after the
   // last one are computed from whatever the slot holds and never used.
   f32x16 sc[2][BN / 32];  // scores of tile k (slot k&1) and of tile k+1
-  auto scores = [&](const uint16_t* Ks, f32x16 (&s)[BN / 32]) {
+  auto scores = [&](const uint16_t* Ks, f32x16 (&s)[BN / 32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   };
   // MASKED selects the per-element predicate: element i of block kb of tile
   // k is key j0 + hf*4 + kb*32 + acc_row(i, 0).
-  auto iteration = [&](int kt, auto bufc, auto masked) {
+  auto iteration = [&](int kt, auto bufc, auto masked) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     constexpr bool MASKED = decltype(masked)::value;
     const int j0 = kt * BN;
@@ -191,6 +198,15 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
     // (issued first so the matrix unit starts while the exp work below
     // runs), this tile's exp / pack, and its P V products.
     scores(ktile(buf ^ 1), sc[buf ^ 1]);
+    // Dropout: random bytes of keys j0 + kb*32 + g*8 + hf*4 + 0..3 (the
+    // accumulator elements 4g .. 4g+3 of block kb) for this lane's row.
+    uint32_t rnd[BN / 32][4];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, j0 + kb * 32 + g4 * 8 + hf * 4);
+    }
     float ls = 0.0f;
     bf16x8 pb[BN / 16];
 #pragma unroll
@@ -200,9 +216,15 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
         u32x4 t;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e], c, nmu));
-          const float p1 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e + 1], c, nmu));
+          float p0 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e], c, nmu));
+          float p1 = fast_exp2(fmaf(s[kb][half * 8 + 2 * e + 1], c, nmu));
           ls += p0 + p1;
+          if constexpr (DROP) {
+            // elements half*8 + 2e, +1: group half*2 + e/2, bytes (2e) % 4, +1
+            const uint32_t r4 = rnd[kb][half * 2 + (e >> 1)];
+            p0 = drop_keep(r4, (2 * e) & 3, dg.t) ? p0 : 0.0f;
+            p1 = drop_keep(r4, ((2 * e) & 3) + 1, dg.t) ? p1 : 0.0f;
+          }
           t[e] = pack_bf16(p0, p1);
         }
         pb[kb * 2 + half] = as_bf16x8(t);
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = halves_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float inv = l_tot > 0.0f ? (DROP ? dg.scale : 1.0f) / l_tot : 0.0f;
   // O rows exist up to the batch's row count (S, or the segment size of
   // packed tensors); LSE rows up to S.
   if (qi < seq_rows(a, b)) {
@@ -301,16 +323,24 @@ constexpr int kFwdOcc192 = 1;
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64>(KArgs);
-template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128>(KArgs);
-template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192>(KArgs);
+// The dropout variants run one workgroup per CU: the generator's state
+// needs registers the two-workgroup budget does not have.
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64, false>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128, false>(KArgs);
+template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192, false>(KArgs);
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, 1, true>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, 1, true>(KArgs);
+template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, 1, true>(KArgs);
 
 template <int DQK, int DV, int BN, int OCC>
 static hipError_t launch_fwd_cfg(KArgs a, hipStream_t stream) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   a.n_tiles = (a.S + C::BM - 1) / C::BM;
   const long long n = (long long)a.B * a.Hq * a.n_tiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, OCC>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
+  if (a.drop_t > 0)
+    hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, 1, true>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, OCC, false>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 

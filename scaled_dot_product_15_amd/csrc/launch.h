@@ -49,5 +49,6 @@ hipError_t launch_dz_reduce(const KArgs& a, hipStream_t stream);
 
 hipError_t launch_debug_tile_map(const KArgs& a, int bm, int bn, int8_t* out, hipStream_t stream);
 hipError_t launch_debug_mask_probe(const KArgs& a, uint8_t* out, hipStream_t stream);
+hipError_t launch_debug_dropout_mask(const KArgs& a, uint8_t* out, hipStream_t stream);
 
 }  // namespace sdpa

@@ -56,6 +56,17 @@ def test_validate_invalid(kw):
     assert binding.attn_validate(P(**kw)) == -1
 
 
+def test_validate_dropout_rate():
+    # dropout_p must lie in [0, 1); NaN is rejected
+    for bad in (1.0, 1.5, -0.1, float("nan"), float("inf")):
+        p = binding.make_params(1, 8, 1, 1, 64, 64, "bf16", "causal", (-1, -1), None, "vanilla", bad)
+        assert binding.attn_validate(p) == -1, bad
+    for ok in (0.0, 0.001, 0.5, 0.999):
+        p = binding.make_params(1, 8, 1, 1, 64, 64, "bf16", "causal", (-1, -1), None, "vanilla", ok, (2**64 - 1, 7))
+        assert binding.attn_validate(p) == 0, ok
+        assert (p.dropout_seed_lo, p.dropout_seed_hi, p.dropout_offset) == (2**32 - 1, 2**32 - 1, 7)
+
+
 def test_validate_bad_enums():
     for field, bad in (("dtype", 2), ("mask_type", 3), ("softmax_type", 3), ("softmax_type", -1)):
         p = P()
