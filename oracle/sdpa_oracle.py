@@ -252,14 +252,15 @@ def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_ri
 
 
 def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True, window=(-1, -1),
-                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None):
+                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None, dropout=None):
     """Outputs of selected query rows of one (batch b, query head h), in float64.
 
     A row's output, LSE, delta and dQ depend only on that row's visible keys,
     so rows can be computed one by one at any sequence length.  Columns where
     the row mask is zero for every selected row are left out: they contribute
     exactly zero.  Returns o [n, dv], lse [n], delta [n], dq [n, dqk] and
-    dz [n] = -exp(z - LSE_i) * delta_i (0 for vanilla).
+    dz [n] = -exp(z - LSE_i) * delta_i (0 for vanilla).  dropout = (p, seed,
+    offset) applies attention dropout as attention_dropout does.
     """
     B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
     g = kv_head(h, Hq, Hkv)
@@ -276,9 +277,10 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
     z = sink_logit(softmax_type, softmax_offset, h)
     s = scale * (qh @ kb.T)
     p, lse = _softmax_rows(s, mask, z)
-    o = p @ vb
+    zmat = _dropout_factors(dropout, b, h, Hq, rows, np.arange(c0, c1))
+    o = (p * zmat) @ vb
     delta = (doh * o).sum(axis=1)
-    ds = p * (doh @ vb.T - delta[:, None])
+    ds = p * (zmat * (doh @ vb.T) - delta[:, None])
     dq = scale * (ds @ kb)
     if z is None:
         dz = np.zeros(len(rows))
@@ -289,7 +291,7 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
 
 def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True, window=(-1, -1),
                    scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None,
-                   row_block=1024):
+                   row_block=1024, dropout=None):
     """dK, dV of selected keys of one (batch b, KV head g), in float64.
 
     dK_j = scale * sum_h sum_i dS_ij Q_i and dV_j = sum_h sum_i P_ij dO_i over
@@ -308,7 +310,7 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
     dk = np.zeros((len(keys), dqk))
     dvv = np.zeros((len(keys), dv_dim))
     kw = dict(num_gqa_groups=Hkv, causal=causal, window=window, scale_factor=scale_factor,
-              softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens)
+              softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens, dropout=dropout)
     for gi in range(G):
         h = g * G + gi
         for r0 in range(0, len(rows_all), row_block):
@@ -320,9 +322,10 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
             s = scale * (qh @ kk.T)
             lse = np.where(np.isfinite(rr["lse"]), rr["lse"], 0.0)
             p = np.where(m, np.exp(np.where(m, s, 0.0) - lse[:, None]), 0.0)
-            ds = p * (doh @ vk.T - rr["delta"][:, None])
+            zmat = _dropout_factors(dropout, b, h, Hq, rows, keys)
+            ds = p * (zmat * (doh @ vk.T) - rr["delta"][:, None])
             dk += scale * (ds.T @ qh)
-            dvv += p.T @ doh
+            dvv += (p * zmat).T @ doh
     return {"dk": dk, "dv": dvv}
 
 
@@ -492,6 +495,15 @@ def dropout_keep(b: int, h: int, rows, keys, *, num_heads: int, p: float, seed: 
     w = np.take_along_axis(words, (byte_idx >> np.uint64(2)).astype(np.int64)[None], axis=0)[0]
     byte = (w >> ((byte_idx & np.uint64(3)) * np.uint64(8))) & np.uint64(0xFF)
     return byte >= np.uint64(t)
+
+
+def _dropout_factors(dropout, b, h, num_heads, rows, keys):
+    """Z = keep / (1 - p_eff) for the pairs rows x keys, or 1 without dropout."""
+    if dropout is None:
+        return np.ones((len(rows), len(keys)))
+    p, seed, offset = dropout
+    keep = dropout_keep(b, h, rows, keys, num_heads=num_heads, p=p, seed=seed, offset=offset)
+    return np.where(keep, 1.0 / (1.0 - dropout_threshold(p) / 256.0), 0.0)
 
 
 def attention_dropout(q, k, v, d_o=None, *, p: float, seed: int, offset: int, num_gqa_groups=None,

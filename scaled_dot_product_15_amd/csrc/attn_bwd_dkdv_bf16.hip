@@ -216,16 +216,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   };
   // B(u): element i of the accumulators is query row qrow0 + acc_row(i, hf),
   // key kj; lse2 / delta come from the stage at offset rb.
-  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, int bh, const f32x16& s, const f32x16& dp,
-                     u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
+  // Dropout bytes of key kj and rows q0 + g*8 + hf*4 + 0..3, g = 0..3 (the
+  // accumulator elements 4g .. 4g+3 of a block starting at row q0): four
+  // independent generator calls, computed together so their round chains
+  // overlap.
+  auto drop_rows = [&](int bh, int q0, uint32_t(&rnd4)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) rnd4[g4] = drop_bytes_col(dg, bh, q0 + g4 * 8 + hf * 4, kj);
+  };
+  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, const uint32_t(&rnd4)[4], const f32x16& s,
+                     const f32x16& dp, u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
     const int lo_r = qlo_k - (qrow0 + hf * 4), hi_r = qhi_k - (qrow0 + hf * 4);
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
       const int qo = rb + ig * 8 + hf * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qo);
-      uint32_t rnd = 0;  // dropout bytes of rows qrow0 + ig*8 + hf*4 + 0..3, key kj
-      if constexpr (DROP) rnd = drop_bytes_col(dg, bh, qrow0 + ig * 8 + hf * 4, kj);
+      const uint32_t rnd = rnd4[ig];  // dropout bytes of rows qrow0 + ig*8 + hf*4 + 0..3, key kj
       u32x2 pp, dd;
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
@@ -349,6 +356,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     const float* dl = delta_s(slot_u);
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
     const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
+    uint32_t rnd_u[4] = {0u, 0u, 0u, 0u};
+    if constexpr (DROP) drop_rows(bh_u, q_u, rnd_u);
 
     auto compute_chunk = [&](auto kc, auto setc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value, st = decltype(setc)::value;
@@ -368,8 +377,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       // accumulator elements 4k .. 4k+3, which are B-operand elements
       // (k%2)*4 .. +3 of K-step k/2.  Blocks that need the mask redo B below.
       u32x2 pp, dd;
-      uint32_t rnd = 0;  // dropout bytes of rows q_u + k*8 + hf*4 + 0..3, key kj
-      if constexpr (DROP) rnd = drop_bytes_col(dg, bh_u, q_u + k * 8 + hf * 4, kj);
+      const uint32_t rnd = rnd_u[k];  // dropout bytes of rows q_u + k*8 + hf*4 + 0..3, key kj
 #pragma unroll
       for (int u2 = 0; u2 < 2; ++u2) {
         float p2[2], s2[2];
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Blocks that some of this wave's (row, key) pairs cannot see (diagonal,
     // window edge, padding): redo B with the mask.
     if (!(q_u >= all_lo && q_u + 31 <= all_hi))
-      phase_b(ls, dl, cur * 32, q_u, bh_u, S[cur], DP[cur], PW[cur], DW[cur]);
+      phase_b(ls, dl, cur * 32, q_u, rnd_u, S[cur], DP[cur], PW[cur], DW[cur]);
   };
 
   if (NB > 0) {
@@ -448,8 +456,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Block 0 has no predecessor: A(0), then A(1) with B(0).
     phase_a(qtile(0), otile(0), 0, S[0], DP[0]);
     phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
-    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, b * a.Hq + g * a.G + hs * Gs + b_walk.hh, S[0], DP[0], PW[0],
-            DW[0]);
+    uint32_t rnd_0[4] = {0u, 0u, 0u, 0u};
+    if constexpr (DROP) drop_rows(b * a.Hq + g * a.G + hs * Gs + b_walk.hh, b_walk.q0, rnd_0);
+    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, rnd_0, S[0], DP[0], PW[0], DW[0]);
     read_ahead(std::integral_constant<int, 0>{});  // first chunk of iteration 1
     // Iterations 1 .. NI in trips of six (one per phase), padded past the
     // last block NB-1 with empty blocks: their stages copy rows past the

@@ -46,8 +46,10 @@ struct DqCfg {
   static constexpr int LDS_ELEMS = 2 * (KT + VT);
 };
 
+// The dropout variant is held to two workgroups per CU (head dims up to 128)
+// so two waves share each SIMD as in the plain kernel.
 template <int DQK, int DV, bool DROP>
-__global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) void bwd_dq_bf16_kernel(KArgs a) {
   using C = DqCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
@@ -149,6 +151,17 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
 
   auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
+    // Element i of block kb: key j0 + hf*4 + kb*32 + acc_row(i, 0), query qi.
+    const int base = j0 + hf * 4;
+    // Dropout bytes of keys base + kb*32 + g*8 + 0..3, drawn before the score
+    // products so the generator's temporaries are dead while S and dP live.
+    uint32_t rnd[C::BN / 32][4];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, base + kb * 32 + g4 * 8);
+    }
     f32x16 st[C::BN / 32], dpt[C::BN / 32];
 #pragma unroll
     for (int kb = 0; kb < C::BN / 32; ++kb) { st[kb] = f32x16{}; dpt[kb] = f32x16{}; }
@@ -164,15 +177,6 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, 1) void bwd_dq_bf16_kernel(KArg
       for (int kb = 0; kb < C::BN / 32; ++kb)
         dpt[kb] = mfma32(as_bf16x8(vrd.read(Vs, kb * 32, ks)), oreg[ks], dpt[kb]);
     prio_valu();
-    // Element i of block kb: key j0 + hf*4 + kb*32 + acc_row(i, 0), query qi.
-    const int base = j0 + hf * 4;
-    uint32_t rnd[C::BN / 32][4];  // dropout bytes of keys base + kb*32 + g*8 + 0..3
-    if constexpr (DROP) {
-#pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, base + kb * 32 + g4 * 8);
-    }
     const int lo_r = klo - base, hi_r = khi - base;
     bf16x8 dsb[C::BN / 16];
 #pragma unroll

@@ -54,10 +54,14 @@ __device__ __forceinline__ u32x4 drop_block(const DropGen& d, int bh, int i, int
 
 // Random bytes of pairs (i, j4 + c), c = 0..3, as byte c of the result
 // (j4 % 4 == 0): lanes that own a query row (forward, dQ).
+// Word i & 3 is picked with AND / OR masks: a chain of selects on the
+// lane-varying row would be turned into divergent branches.
 __device__ __forceinline__ uint32_t drop_bytes_row(const DropGen& d, int bh, int i, int j4) {
   const u32x4 w = drop_block(d, bh, i, j4);
   const int r = i & 3;
-  return r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+  const uint32_t m0 = 0u - (uint32_t)(r == 0), m1 = 0u - (uint32_t)(r == 1), m2 = 0u - (uint32_t)(r == 2),
+                 m3 = 0u - (uint32_t)(r == 3);
+  return (w[0] & m0) | (w[1] & m1) | (w[2] & m2) | (w[3] & m3);
 }
 
 // Random bytes of pairs (i4 + r, j), r = 0..3, as byte r of the result

@@ -785,9 +785,34 @@ def pin_dropout_layout(orc):
             assert keep[i, j] == (byte >= t), (i, j)
 
 
+def pin_dropout_sampled(orc):
+    """Row- and key-sampled functions with dropout equal the whole-problem
+    dropout oracle on those rows and keys (different code paths: masked
+    column ranges and row blocks vs full S x S matrices)."""
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(2200 + ci, B=2, S=9)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.6, softmax_type=st,
+                      softmax_offset=alpha, seqlens=None if sl is None else np.array(sl))
+            drop = (0.35, 0xFEED + ci, 4)
+            full = orc.attention_dropout(q, k, v, do, p=drop[0], seed=drop[1], offset=drop[2], **kw)
+            for b in range(2):
+                h = (b + ci) % 4
+                rows = np.array([0, 3, 8])
+                r = orc.attention_rows(q, k, v, do, b=b, h=h, rows=rows, dropout=drop, **kw)
+                _close(r["o"], full["o"][b, rows, h], 1e-12, 1e-14, f"rows O {ci} {st}")
+                _close(r["dq"], full["dq"][b, rows, h], 1e-12, 1e-14, f"rows dQ {ci} {st}")
+                g = h // 2
+                keys = np.array([0, 4, 8])
+                rk = orc.attention_keys(q, k, v, do, b=b, g=g, keys=keys, dropout=drop, row_block=2, **kw)
+                _close(rk["dk"], full["dk"][b, keys, g], 1e-12, 1e-14, f"keys dK {ci} {st}")
+                _close(rk["dv"], full["dv"][b, keys, g], 1e-12, 1e-14, f"keys dV {ci} {st}")
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
             pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
             pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff,
             pin_philox_kat, pin_dropout_rate, pin_dropout_brute, pin_dropout_p0, pin_dropout_finite_diff,
-            pin_dropout_mean, pin_dropout_layout]
+            pin_dropout_mean, pin_dropout_layout,
+            pin_dropout_sampled]

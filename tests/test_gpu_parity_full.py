@@ -42,15 +42,20 @@ def _sample_keys(rng, p, L):
     return np.array(sorted(picks))
 
 
-@pytest.mark.parametrize("cfg,case", CASES, ids=lambda x: str(x))
-def test_full_size(cfg, case):
+# (config, case, dropout rate): the last two run attention dropout at full size.
+RUNS = [(c, k, 0.0) for c, k in CASES] + [(2, 0, 0.1), (5, 1, 0.1)]
+
+
+@pytest.mark.parametrize("cfg,case,drop", RUNS, ids=lambda x: str(x))
+def test_full_size(cfg, case, drop):
     import torch
     p = inputs.workload_configs()[cfg][case]
     seed = 1000 * cfg + case
-    gc.log(f"config {cfg} case {case}: {p.name} seed={seed}")
+    gc.log(f"config {cfg} case {case}: {p.name} seed={seed} dropout={drop}")
     arr = inputs.draw(p, seed)
     t = inputs.to_torch(arr, p.dtype, "cuda")
-    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t)
+    dropout = (drop, seed, 77) if drop else None
+    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout)
     B, S = p.B, p.S
     L = np.full(B, S) if arr["seqlens"] is None else arr["seqlens"]
     for b in range(B):
@@ -64,7 +69,7 @@ def test_full_size(cfg, case):
     alpha = t["alpha"].cpu().numpy().astype(np.float64)
     kw = dict(num_gqa_groups=p.Hkv, causal=p.causal, window=p.window,
               scale_factor=p.scale_factor or None, softmax_type=p.softmax_type,
-              softmax_offset=alpha, seqlens=arr["seqlens"])
+              softmax_offset=alpha, seqlens=arr["seqlens"], dropout=dropout)
     rng = np.random.default_rng(seed)
     G = p.Hq // p.Hkv
     got = {"o": [], "dq": [], "dk": [], "dv": []}

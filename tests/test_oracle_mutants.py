@@ -55,6 +55,9 @@ MUTANTS = {
     "dropout_no_rescale": [("zmat = np.where(keep, zscale, 0.0)", "zmat = np.where(keep, 1.0, 0.0)")],
     "dropout_dp_unmasked": [("dp = zmat * (doh @ vg.T)", "dp = doh @ vg.T")],
     "dropout_dv_unmasked": [('res["dv"][b, :, g, :] += (pr * zmat).T @ doh', 'res["dv"][b, :, g, :] += pr.T @ doh')],
+    "rows_dropout_dp_unmasked": [("ds = p * (zmat * (doh @ vb.T) - delta[:, None])",
+                                  "ds = p * (doh @ vb.T - delta[:, None])")],
+    "keys_dropout_dv_unmasked": [("dvv += (p * zmat).T @ doh", "dvv += p.T @ doh")],
     "keys_rows_subset": [("rows_all = np.nonzero(sees.any(axis=1))[0]",
                           "rows_all = np.nonzero(sees.any(axis=1))[0][1:]")],
 }
@@ -69,7 +72,7 @@ ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_ca
          oracle_pins.pin_packed_equals_padded, oracle_pins.pin_packed_finite_diff,
          oracle_pins.pin_philox_kat, oracle_pins.pin_dropout_rate, oracle_pins.pin_dropout_p0,
          oracle_pins.pin_dropout_brute, oracle_pins.pin_dropout_finite_diff, oracle_pins.pin_dropout_mean,
-         oracle_pins.pin_dropout_layout]
+         oracle_pins.pin_dropout_layout, oracle_pins.pin_dropout_sampled]
 
 
 def _mutant(edits):
