@@ -323,8 +323,9 @@ constexpr int kFwdOcc192 = 1;
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-// The dropout variants run one workgroup per CU: the generator's state
-// needs registers the two-workgroup budget does not have.
+// The dropout variants are built with a one-workgroup bound so the
+// generator's state can never force spills; at head dims up to 128 they still
+// fit the two-workgroup register budget and run two per CU.
 template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64, false>(KArgs);
 template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128, false>(KArgs);
 template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192, false>(KArgs);
