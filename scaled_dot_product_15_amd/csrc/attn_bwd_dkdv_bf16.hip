@@ -217,12 +217,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // B(u): element i of the accumulators is query row qrow0 + acc_row(i, hf),
   // key kj; lse2 / delta come from the stage at offset rb.
   // Dropout bytes of key kj and rows q0 + g*8 + hf*4 + 0..3, g = 0..3 (the
-  // accumulator elements 4g .. 4g+3 of a block starting at row q0): four
-  // independent generator calls, computed together so their round chains
-  // overlap.
+  // accumulator elements 4g .. 4g+3 of a block starting at row q0): one
+  // generator call per lane, shared across the lane quad.
   auto drop_rows = [&](int bh, int q0, uint32_t(&rnd4)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) rnd4[g4] = drop_bytes_col(dg, bh, q0 + g4 * 8 + hf * 4, kj);
+    drop_cols_quad(dg, bh, q0 + hf * 4, kj, rnd4);
   };
   auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, const uint32_t(&rnd4)[4], const f32x16& s,
                      const f32x16& dp, u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {

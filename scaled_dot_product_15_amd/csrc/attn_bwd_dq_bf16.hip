@@ -158,9 +158,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) v
     uint32_t rnd[C::BN / 32][4];
     if constexpr (DROP) {
 #pragma unroll
-      for (int kb = 0; kb < C::BN / 32; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, base + kb * 32 + g4 * 8);
+      for (int kb = 0; kb < C::BN / 32; ++kb) drop_rows_quad(dg, bh, qi, base + kb * 32, rnd[kb]);
     }
     f32x16 st[C::BN / 32], dpt[C::BN / 32];
 #pragma unroll

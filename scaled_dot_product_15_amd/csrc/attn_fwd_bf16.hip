@@ -203,9 +203,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
     uint32_t rnd[BN / 32][4];
     if constexpr (DROP) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) rnd[kb][g4] = drop_bytes_row(dg, bh, qi, j0 + kb * 32 + g4 * 8 + hf * 4);
+      for (int kb = 0; kb < BN / 32; ++kb) drop_rows_quad(dg, bh, qi, j0 + kb * 32 + hf * 4, rnd[kb]);
     }
     float ls = 0.0f;
     bf16x8 pb[BN / 16];

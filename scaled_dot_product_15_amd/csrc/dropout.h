@@ -73,6 +73,71 @@ __device__ __forceinline__ uint32_t drop_bytes_col(const DropGen& d, int bh, int
          (((w[3] >> sh) & 0xFFu) << 24);
 }
 
+// ---- one generator call per lane, shared across a lane quad ------------------
+//
+// In the kernels the four lanes of a quad (lanes 4m .. 4m+3) hold the four
+// rows (forward, dQ) or the four keys (dK / dV) of the same 4 x 4 blocks, so
+// they need the same calls.  Lane r of the quad makes only the call of group
+// r and the quad exchanges the results: a 4 x 4 transpose across the quad
+// (lane r holding row r of A ends up with column r), done as two butterfly
+// stages of DPP quad permutes (partners r ^ 2, then r ^ 1), each stage
+// swapping the two words whose index bit differs from the lane's.
+
+// DPP quad_perm controls: lane r reads lane r ^ 2, resp. r ^ 1.
+constexpr int kQuadSwap2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+constexpr int kQuadSwap1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+
+__device__ __forceinline__ uint32_t quad_read(uint32_t v, int ctrl_selector) {
+  return ctrl_selector == 2
+             ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false)
+             : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false);
+}
+
+// a[c] = A[r][c] on lane r (r = lane % 4) -> a[c] = A[c][r].
+__device__ __forceinline__ void quad_transpose(uint32_t (&a)[4], int r) {
+  const bool hi = (r & 2) != 0, lo = (r & 1) != 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {  // words p and p + 2 with lanes r ^ 2
+    const uint32_t recv = quad_read(hi ? a[p] : a[p + 2], 2);
+    a[p] = hi ? recv : a[p];
+    a[p + 2] = hi ? a[p + 2] : recv;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; p += 2) {  // words p and p + 1 with lanes r ^ 1
+    const uint32_t recv = quad_read(lo ? a[p] : a[p + 1], 1);
+    a[p] = lo ? recv : a[p];
+    a[p + 1] = lo ? a[p + 1] : recv;
+  }
+}
+
+// Row lanes (query row i, i % 4 == lane % 4): out[g] = random bytes of pairs
+// (i, jb + 8g + c), c = 0..3, for g = 0..3 (jb % 4 == 0); same as
+// drop_bytes_row(d, bh, i, jb + 8g).
+__device__ __forceinline__ void drop_rows_quad(const DropGen& d, int bh, int i, int jb, uint32_t (&out)[4]) {
+  const int r = i & 3;
+  const u32x4 w = drop_block(d, bh, i, jb + 8 * r);
+  out[0] = w[0];
+  out[1] = w[1];
+  out[2] = w[2];
+  out[3] = w[3];
+  quad_transpose(out, r);
+}
+
+// Column lanes (key j, j % 4 == lane % 4): out[g] = random bytes of pairs
+// (ib + 8g + r, j), r = 0..3, for g = 0..3 (ib % 4 == 0); same as
+// drop_bytes_col(d, bh, ib + 8g, j).
+__device__ __forceinline__ void drop_cols_quad(const DropGen& d, int bh, int ib, int j, uint32_t (&out)[4]) {
+  const int c = j & 3;
+  const u32x4 w = drop_block(d, bh, ib + 8 * c, j);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {  // column x of the call's 4 x 4 bytes
+    const uint32_t sh = 8u * x;
+    out[x] = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) | (((w[2] >> sh) & 0xFFu) << 16) |
+             (((w[3] >> sh) & 0xFFu) << 24);
+  }
+  quad_transpose(out, c);
+}
+
 // Byte n of a random word against the threshold.
 __device__ __forceinline__ bool drop_keep(uint32_t bytes, int n, int t) {
   return (int)((bytes >> (8 * n)) & 0xFFu) >= t;
