@@ -35,11 +35,11 @@ SENTINEL = 1232.0  # exact in bf16 and fp32
 CASES = list(itertools.product(DIMS, MASKS, SOFTMAX))
 
 
-def _run(p, t, seq_offsets, seqlens, T, packed):
+def _run(p, t, seq_offsets, seqlens, T, packed, dropout_p=0.0):
     import torch
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
               window_size=p.window, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
-              seqlens=seqlens)
+              seqlens=seqlens, dropout_p=dropout_p, rng_state=(0xC0FFEE, 3))
     if packed:
         kw.update(seq_offsets=seq_offsets, max_seqlen=p.S)
     dt = t["q"].dtype
@@ -114,23 +114,28 @@ def test_packed_parity(dims, mask, st):
     gc.log(f"  {stats}")
 
 
-@pytest.mark.parametrize("dims,st,hkv", [("bf16_128", "learnable", 2), ("bf16_64", "off_by_one", 1),
-                                         ("bf16_192_128", "vanilla", 4), ("f32_64", "learnable", 2)],
+@pytest.mark.parametrize("dims,st,hkv,drop", [("bf16_128", "learnable", 2, 0.0), ("bf16_64", "off_by_one", 1, 0.0),
+                                              ("bf16_192_128", "vanilla", 4, 0.0), ("f32_64", "learnable", 2, 0.0),
+                                              ("bf16_128", "off_by_one", 2, 0.2), ("bf16_64", "vanilla", 1, 0.3),
+                                              ("f32_64", "vanilla", 2, 0.2)],
                          ids=lambda x: str(x))
-def test_packed_equals_padded_bitwise(dims, st, hkv):
-    """Packed and padded BSHD runs of the same segments agree bit for bit.
+def test_packed_equals_padded_bitwise(dims, st, hkv, drop):
+    """Packed and padded BSHD runs of the same segments agree bit for bit,
+    with and without attention dropout (the keep mask is a function of the
+    position inside the segment, so both layouts draw the same one).
 
     Hkv = 1 with 8 query heads makes the bf16 dK/dV stage split the group's
     heads over workgroups (fp32 partials reduced into the packed rows)."""
     import torch
     p = _problem(dims, "causal_swa", st, Hq=8, Hkv=hkv)
     seed = 51_000 + hkv
-    gc.log(f"packed==padded {dims} {st} Hkv={hkv} seed={seed} splits={binding.host_dkdv_splits(_params(p))}")
+    gc.log(f"packed==padded {dims} {st} Hkv={hkv} dropout={drop} seed={seed} "
+           f"splits={binding.host_dkdv_splits(_params(p))}")
     arr, tp = _inputs(p, seed)
-    gp = _run(p, tp, tp["seq_offsets"], tp["seqlens"], tp["q"].shape[0], packed=True)
+    gp = _run(p, tp, tp["seq_offsets"], tp["seqlens"], tp["q"].shape[0], packed=True, dropout_p=drop)
     tb = inputs.to_torch(arr, p.dtype, "cuda")
     tb["seqlens"] = torch.tensor(SEQLENS, dtype=torch.int32, device="cuda")
-    gb = _run(p, tb, None, tb["seqlens"], None, packed=False)
+    gb = _run(p, tb, None, tb["seqlens"], None, packed=False, dropout_p=drop)
     off = tp["seq_offsets"].cpu().numpy()
     for name, i in (("o", 0), ("dq", 2), ("dk", 3), ("dv", 4)):
         a, b = gp[i].cpu(), gb[i].cpu()
@@ -140,7 +145,8 @@ def test_packed_equals_padded_bitwise(dims, st, hkv):
     assert torch.equal(gp[1].cpu(), gb[1].cpu()), "lse differs"
     if st != "vanilla":
         assert torch.equal(gp[5].cpu(), gb[5].cpu()), "d_softmax_offset differs"
-    _check_packed(p, tp, gp, f"packed==padded/{dims}/{st}/Hkv={hkv}")
+    if not drop:
+        _check_packed(p, tp, gp, f"packed==padded/{dims}/{st}/Hkv={hkv}")
 
 
 def _params(p):
