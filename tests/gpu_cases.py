@@ -68,8 +68,12 @@ def oracle_full(p: inputs.Problem, t: dict):
                             seqlens=None if t["seqlens"] is None else t["seqlens"].cpu().numpy())
 
 
-def compare_full(p: inputs.Problem, t: dict, g: tuple, r: dict, tag=""):
-    """Element-by-element comparison of GPU outputs g with oracle result r."""
+def compare_full(p: inputs.Problem, t: dict, g: tuple, r: dict, tag="", o_scale=1.0):
+    """Element-by-element comparison of GPU outputs g with oracle result r.
+
+    o_scale: factor by which O's magnitude exceeds plain attention's (with
+    attention dropout, kept probabilities are multiplied by 1 / (1 - p), and
+    bf16 output rounding is relative); the O bound applies to O / o_scale."""
     o, lse, dq, dk, dv, doff = (None if x is None else to64(x) for x in g)
     B, S = p.B, p.S
     L = np.full(B, S) if t["seqlens"] is None else t["seqlens"].cpu().numpy()
@@ -93,7 +97,7 @@ def compare_full(p: inputs.Problem, t: dict, g: tuple, r: dict, tag=""):
     fin = np.isfinite(r["lse"])
     assert (np.isfinite(lse) == fin).all(), f"{tag} LSE finiteness differs"
     stats["lse_maxabs"] = float(np.abs(lse[fin] - r["lse"][fin]).max()) if fin.any() else 0.0
-    stats["o_maxabs"] = float(np.abs(o - r["o"]).max())
+    stats["o_maxabs"] = float(np.abs(o - r["o"]).max()) / o_scale
     for name, a, ref in (("dq", dq, r["dq"]), ("dk", dk, r["dk"]), ("dv", dv, r["dv"])):
         stats[f"{name}_maxabs"] = float(np.abs(a - ref).max())
         stats[f"{name}_rel_l2"] = rel_l2(a, ref)

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sdpa_attn.h")
 
 lib_missing = not os.path.exists(binding.LIB_PATH)
-pytestmark = pytest.mark.skipif(lib_missing, reason="library not built (run __graft_entry__.build())")
+pytestmark = pytest.mark.skipif(lib_missing, reason="library not built (python -m scaled_dot_product_15_amd.build)")
 
 
 def header_functions():

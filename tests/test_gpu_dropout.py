@@ -23,6 +23,11 @@ pytestmark = [pytest.mark.gpu,
 SEED, OFFSET = 0x9E3779B97F4A7C15, 12345
 
 
+def _zscale(rate):
+    """1 / (1 - p_eff): how much larger O's values are than without dropout."""
+    return 1.0 / (1.0 - oracle.dropout_threshold(rate) / 256.0)
+
+
 def _params(p, dropout_p, rng_state=(SEED, OFFSET)):
     return binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype,
                                "causal" if p.causal else "no_mask", p.window, p.scale_factor or None,
@@ -114,7 +119,7 @@ def test_dropout_parity(dims, mask, st):
     r = oracle.attention_dropout(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), p=0.2, seed=SEED + seed,
                                  offset=OFFSET, num_gqa_groups=p.Hkv, causal=causal, window=win, softmax_type=st,
                                  softmax_offset=f64(t["alpha"]), seqlens=arr["seqlens"])
-    stats = gc.compare_full(p, t, g, r, tag=f"dropout/{dims}/{mask}/{st}")
+    stats = gc.compare_full(p, t, g, r, tag=f"dropout/{dims}/{mask}/{st}", o_scale=_zscale(0.2))
     gc.log(f"  {stats}")
 
 
@@ -136,3 +141,23 @@ def test_dropout_reproducible_and_p0(dims):
     n = _run(p, t, 0.0, (0, 0))
     for x, y in zip(z, n):
         assert torch.equal(x, y), "p = 0 must ignore the rng state"
+
+
+@pytest.mark.parametrize("dims,rate", [("bf16_128", 0.9), ("bf16_64", 0.6), ("f32_64", 0.9)], ids=str)
+def test_dropout_edge_cases(dims, rate):
+    """High rates (large 1 / (1 - p)), an empty batch and a one-token batch."""
+    dtype, dqk, dv = DIMS[dims]
+    p = inputs.Problem(B=3, S=150, Hq=4, Hkv=1, d_qk=dqk, d_v=dv, dtype=dtype, causal=True, window=(40, 0),
+                       softmax_type="learnable")
+    seed = 62_000 + int(rate * 10) + dqk
+    arr = inputs.draw(p, seed)
+    arr["seqlens"] = np.array([150, 0, 1], dtype=np.int32)
+    t = inputs.to_torch(arr, dtype, "cuda")
+    gc.log(f"dropout edge {dims} p={rate} seed={seed}")
+    g = _run(p, t, rate, (seed, 9))
+    f64 = inputs.exact_f64
+    r = oracle.attention_dropout(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), p=rate, seed=seed, offset=9,
+                                 num_gqa_groups=p.Hkv, causal=True, window=(40, 0), softmax_type="learnable",
+                                 softmax_offset=f64(t["alpha"]), seqlens=arr["seqlens"])
+    stats = gc.compare_full(p, t, g, r, tag=f"dropout edge/{dims}/{rate}", o_scale=_zscale(rate))
+    gc.log(f"  {stats}")

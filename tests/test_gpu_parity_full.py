@@ -95,8 +95,10 @@ def test_full_size(cfg, case, drop):
         ref["dk"].append(rk["dk"])
         got["dv"].append(dv[b, keys, g].float().cpu().numpy())
         ref["dv"].append(rk["dv"])
+    # with dropout, O is 1 / (1 - p) times larger and bf16 rounding relative: bound O / that factor
+    zs = 1.0 / (1.0 - oracle.dropout_threshold(drop) / 256.0)
     stats = {"lse_maxabs": lse_err,
-             "o_maxabs": float(max(np.abs(a - r).max() for a, r in zip(got["o"], ref["o"])))}
+             "o_maxabs": float(max(np.abs(a - r).max() for a, r in zip(got["o"], ref["o"]))) / zs}
     for n in ("dq", "dk", "dv"):
         a = np.concatenate([x.reshape(-1) for x in got[n]])
         r = np.concatenate([x.reshape(-1) for x in ref[n]])
