@@ -237,10 +237,12 @@ def effective_flops(pairs: int, d_qk: int, d_v: int):
     return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)
 
 
-def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_right: int) -> np.ndarray:
-    """Boolean [len(rows), S]: the visible_mask definition for selected query rows."""
+def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_right: int,
+                 cols=None) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: the visible_mask definition for selected
+    query rows and keys (all S keys when cols is None)."""
     i = np.asarray(rows)[:, None]
-    j = np.arange(S)[None, :]
+    j = (np.arange(S) if cols is None else np.asarray(cols))[None, :]
     m = (i < L) & (j < L)
     if causal:
         m = m & (j <= i)
@@ -266,10 +268,16 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
     g = kv_head(h, Hq, Hkv)
     L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
     rows = np.asarray(rows, dtype=np.int64)
-    mask = visible_rows(rows, S, L, causal, int(window[0]), int(window[1]))
+    # keys outside [min row - left, max row + right] fail the window rule for
+    # every selected row; the mask definition is evaluated on the rest
+    lo = max(0, int(rows.min()) - int(window[0])) if window[0] >= 0 and rows.size else 0
+    hi = min(S, int(rows.max()) + int(window[1]) + 1) if window[1] >= 0 and rows.size else S
+    lo, hi = (lo, hi) if lo < hi else (0, 1)
+    mask = visible_rows(rows, S, L, causal, int(window[0]), int(window[1]), cols=np.arange(lo, hi))
     cols = np.nonzero(mask.any(axis=0))[0]
     c0, c1 = (int(cols[0]), int(cols[-1]) + 1) if cols.size else (0, 1)  # one fully masked column
     mask = mask[:, c0:c1]
+    c0, c1 = c0 + lo, c1 + lo
     kb = np.asarray(k[b, c0:c1, g, :], dtype=np.float64)
     vb = np.asarray(v[b, c0:c1, g, :], dtype=np.float64)
     qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
@@ -302,8 +310,8 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
     G = Hq // Hkv
     L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
     keys = np.asarray(keys, dtype=np.int64)
-    # rows that see any selected key: the mask definition, transposed
-    sees = visible_rows(np.arange(S), S, L, causal, int(window[0]), int(window[1]))[:, keys]
+    # rows that see any selected key: the mask definition on those key columns
+    sees = visible_rows(np.arange(S), S, L, causal, int(window[0]), int(window[1]), cols=keys)
     rows_all = np.nonzero(sees.any(axis=1))[0]
     kk = np.asarray(k[b, keys, g, :], dtype=np.float64)
     vk = np.asarray(v[b, keys, g, :], dtype=np.float64)
@@ -311,10 +319,13 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
     dvv = np.zeros((len(keys), dv_dim))
     kw = dict(num_gqa_groups=Hkv, causal=causal, window=window, scale_factor=scale_factor,
               softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens, dropout=dropout)
+    # row blocks never straddle a gap in rows_all, so each block's key range
+    # stays as narrow as the mask allows
+    cuts = np.nonzero(np.diff(rows_all) > 1)[0] + 1
+    blocks = [run[r0:r0 + row_block] for run in np.split(rows_all, cuts) for r0 in range(0, len(run), row_block)]
     for gi in range(G):
         h = g * G + gi
-        for r0 in range(0, len(rows_all), row_block):
-            rows = rows_all[r0:r0 + row_block]
+        for rows in blocks:
             rr = attention_rows(q, k, v, d_o, b=b, h=h, rows=rows, **kw)
             m = sees[rows]
             qh = np.asarray(q[b, rows, h, :], dtype=np.float64)

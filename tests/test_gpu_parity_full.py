@@ -115,3 +115,48 @@ def test_full_size(cfg, case, drop):
         stats["doff_rel_l2"] = gc.rel_l2(doff.cpu().numpy()[heads], ref_dz)
     gc.log(f"  {stats}")
     gc.check(p, stats, f"config {cfg} case {case}")
+
+
+@pytest.mark.parametrize("st,drop", [("vanilla", 0.0), ("learnable", 0.1)], ids=str)
+def test_long_sequence(st, drop):
+    """S = 131072 tokens (sliding window 1024, causal, GQA 4:1, d = 128): row and
+    byte offsets far past every listed workload, checked on sampled rows and
+    keys (start, middle, end) against the row/key-sampled oracle."""
+    import torch
+    p = inputs.Problem(B=1, S=131072, Hq=4, Hkv=1, d_qk=128, d_v=128, dtype="bf16", causal=True,
+                       window=(1024, 0), softmax_type=st)
+    seed = 70_000 + int(drop * 10)
+    gc.log(f"long sequence S={p.S} {st} dropout={drop} seed={seed}")
+    arr = inputs.draw(p, seed)
+    t = inputs.to_torch(arr, "bf16", "cuda")
+    dropout = (drop, seed, 5) if drop else None
+    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
+    assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
+    host = {n: t[n].float().cpu().numpy() for n in ("q", "k", "v", "do")}
+    kw = dict(num_gqa_groups=1, causal=True, window=(1024, 0), softmax_type=st,
+              softmax_offset=t["alpha"].cpu().numpy().astype(np.float64), dropout=dropout)
+    rows = np.array([0, 1, 1023, 1024, 1025, 65536, 100000, p.S - 2, p.S - 1])
+    keys = np.array([0, 5, 70000, p.S - 1030, p.S - 1])
+    got, ref = {"o": [], "dq": [], "dk": [], "dv": []}, {"o": [], "dq": [], "dk": [], "dv": []}
+    zs = 1.0 / (1.0 - oracle.dropout_threshold(drop) / 256.0)
+    lse_err = 0.0
+    for h in (0, 3):
+        r = oracle.attention_rows(host["q"], host["k"], host["v"], host["do"], b=0, h=h, rows=rows, **kw)
+        got["o"].append(o[0, rows, h].float().cpu().numpy())
+        ref["o"].append(r["o"])
+        got["dq"].append(dq[0, rows, h].float().cpu().numpy())
+        ref["dq"].append(r["dq"])
+        lse_err = max(lse_err, float(np.abs(lse[0, h, rows].cpu().numpy() - r["lse"]).max()))
+    rk = oracle.attention_keys(host["q"], host["k"], host["v"], host["do"], b=0, g=0, keys=keys, **kw)
+    got["dk"].append(dk[0, keys, 0].float().cpu().numpy())
+    ref["dk"].append(rk["dk"])
+    got["dv"].append(dv[0, keys, 0].float().cpu().numpy())
+    ref["dv"].append(rk["dv"])
+    stats = {"lse_maxabs": lse_err,
+             "o_maxabs": float(max(np.abs(a - b).max() for a, b in zip(got["o"], ref["o"]))) / zs}
+    for n in ("dq", "dk", "dv"):
+        stats[f"{n}_rel_l2"] = gc.rel_l2(np.concatenate([x.reshape(-1) for x in got[n]]),
+                                         np.concatenate([x.reshape(-1) for x in ref[n]]))
+    gc.log(f"  {stats}")
+    gc.check(p, stats, f"long sequence {st}")
