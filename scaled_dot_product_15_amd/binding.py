@@ -205,6 +205,14 @@ def _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor,
                        scale_factor, softmax_type, dropout_p, rng_state)
 
 
+def _check_buffer(t, shape, dtype, name):
+    """Caller-supplied output / workspace buffers: the library sees only their
+    pointers, so their size, dtype and layout are checked here."""
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {list(shape)}, "
+                         f"got {t.dtype} {list(t.shape)}")
+
+
 def _check_seqlens(seqlens, B, S):
     torch = _torch()
     if seqlens is None:
@@ -259,9 +267,11 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
             raise ValueError("softmax_offset must hold num_heads values")
     else:
         softmax_offset = None
-    o = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (p.head_dim_v,), dtype=q.dtype,
-                                                device=q.device)
+    o_shape = tuple(q.shape[:-1]) + (p.head_dim_v,)
+    o = out if out is not None else torch.empty(o_shape, dtype=q.dtype, device=q.device)
     l = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check_buffer(o, o_shape, q.dtype, "out")
+    _check_buffer(l, (B, Hq, S), torch.float32, "lse")
     lib = load_library()
     _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(softmax_offset),
                         _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), None, 0, _stream(stream)),
@@ -302,6 +312,11 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     want = softmax_type == "learnable" or (softmax_type == "off_by_one" and bool(want_d_offset))
     if outs is not None:
         dq, dk, dv, doff = outs
+        _check_buffer(dq, q.shape, q.dtype, "dq")
+        _check_buffer(dk, k.shape, q.dtype, "dk")
+        _check_buffer(dv, v.shape, q.dtype, "dv")
+        if want and doff is not None:
+            _check_buffer(doff, (Hq,), torch.float32, "d_softmax_offset")
     else:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)
@@ -311,11 +326,13 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
         doff = None
     lib = load_library()
     ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    if workspace is not None and (not workspace.is_cuda or workspace.numel() * workspace.element_size() < ws_bytes):
+        raise ValueError(f"workspace must be a device tensor of at least {ws_bytes} bytes")
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
             _ptr(softmax_offset), _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv),
-            _ptr(doff), _ptr(workspace), workspace.numel(), _stream(stream))
+            _ptr(doff), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if stage:
         _check(lib.attn_bwd_stage(stage, *args), f"attn_bwd_stage({stage})")
     else:
