@@ -27,6 +27,11 @@ section 4 "Implement attention from scratch", does):
   * grads   dQ, dK, dV of L = sum(dO * O), and the gradient of the sink logit
             (PR #2225: the backward returns grad_q, grad_k, grad_v and
             grad_softmax_offset)
+  * packed  sequences back to back on one token axis (attention_packed: one
+            block-diagonal mask over the axis; TE single-GPU page, section 1)
+  * dropout inverted dropout on the probabilities with a Philox4x32-10 keep
+            mask (attention_dropout; TE single-GPU page, "Other attention
+            knobs"; the generator and its layout are readings, stated below)
 
 Readings taken where the pages are silent or disagree (each also listed in the
 design notes):
