@@ -86,6 +86,27 @@ def build(jobs: int = 8, save_temps: bool = False, verbose: bool = True) -> str:
     return LIB
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "abi_gpu_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c", "abi_gpu_client")
+
+
+def build_c_client(verbose: bool = True) -> str:
+    """The test client that drives the library from C (gcc; HIP runtime API for
+    memory, the C ABI for attention).  It finds the library relative to itself."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    rel = os.path.relpath(PKG, os.path.dirname(C_CLIENT))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, C_CLIENT_SRC, "-o", C_CLIENT, "-L", PKG,
+           "-l:" + os.path.basename(LIB), "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/" + rel, "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{res.stderr}")
+    if verbose:
+        print(f"built {C_CLIENT}")
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=8)
