@@ -134,16 +134,24 @@ def _resolve(q, k, v, num_gqa_groups, scale_factor):
     return B, S, Hq, Hkv, dqk, v.shape[3], scale
 
 
+def _bias_index(bias, b, h):
+    """Indices of batch b, query head h into a [Bb, Hb, S, S] bias (Bb, Hb = 1 broadcast)."""
+    return (b if bias.shape[0] > 1 else 0), (h if bias.shape[1] > 1 else 0)
+
+
 def attention_group(q, k, v, d_o, *, b, g, num_gqa_groups=None, causal=True,
                     window=(-1, -1), scale_factor=None, softmax_type=VANILLA,
-                    softmax_offset=None, seqlens=None, want_grads=True):
+                    softmax_offset=None, seqlens=None, want_grads=True, bias=None):
     """Forward (and backward) for one batch b and one KV head g, in float64.
 
     Computes every query head of the group.  Returns a dict with
       o    [S, G, dv]   lse [G, S]   (forward)
       dq   [S, G, dqk]  dk  [S, dqk]  dv [S, dv]
       dz   [G]          this batch's share of d(sink logit) per query head
-    Inputs may be any float dtype; they are upcast to float64 exactly.
+      ds   [G, S, S]    dS per query head (with bias, for its gradient)
+    Inputs may be any float dtype; they are upcast to float64 exactly.  bias:
+    an additive post-scale bias [Bb, Hb, S, S] (Bb in {1, B}, Hb in {1, Hq};
+    see attention()).
     """
     B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
     G = Hq // Hkv
@@ -161,6 +169,8 @@ def attention_group(q, k, v, d_o, *, b, g, num_gqa_groups=None, causal=True,
         qh = np.asarray(q[b, :, h, :], dtype=np.float64)
         z = sink_logit(softmax_type, softmax_offset, h)
         s = scale * (qh @ kb.T)                       # score + scale
+        if bias is not None:
+            s = s + np.asarray(bias[_bias_index(bias, b, h)], dtype=np.float64)
         p, lse = _softmax_rows(s, mask, z)            # softmax (+ sink)
         o = p @ vb                                    # attend
         out["o"][:, gi, :] = o
@@ -171,6 +181,8 @@ def attention_group(q, k, v, d_o, *, b, g, num_gqa_groups=None, causal=True,
         dp = doh @ vb.T                               # dL/dP
         delta = (doh * o).sum(axis=1)                 # rowsum(dO * O) = sum_j P_ij dP_ij
         ds = p * (dp - delta[:, None])                # softmax Jacobian applied to dP
+        if bias is not None:
+            out.setdefault("ds", np.zeros((G, S, S)))[gi] = ds
         out["dq"][:, gi, :] = scale * (ds @ kb)
         out["dk"] += scale * (ds.T @ qh)
         out["dv"] += p.T @ doh
@@ -183,12 +195,20 @@ def attention_group(q, k, v, d_o, *, b, g, num_gqa_groups=None, causal=True,
 
 
 def attention(q, k, v, d_o=None, *, num_gqa_groups=None, causal=True, window=(-1, -1),
-              scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None):
+              scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None, bias=None):
     """Whole-problem oracle (small shapes): assembles every (batch, kv head) group.
 
     Returns dict o [B,S,Hq,dv], lse [B,Hq,S] and, when d_o is given,
     dq [B,S,Hq,dqk], dk [B,S,Hkv,dqk], dv [B,S,Hkv,dv], dalpha [Hq]
-    (dalpha is None for vanilla softmax).
+    (dalpha is None for vanilla softmax) and dbias (None without bias).
+
+    bias: attention bias, read as an additive post-scale bias on the visible
+    scores, s_ij = scale q_i.k_j + bias[b, h, i, j], of shape [Bb, Hb, S, S]
+    with Bb in {1, B} and Hb in {1, Hq} (1 = shared, broadcast).  The TE
+    single-GPU page ("Other attention knobs") passes a bias with a bias type,
+    and the PR #2225 backward returns grad_bias; the reading: the gradient is
+    dS = P (dP - delta), summed over the dimensions the bias is shared along,
+    and zero on pairs the mask hides.
     """
     B, S, Hq, Hkv, dqk, dv_dim, _ = _resolve(q, k, v, num_gqa_groups, scale_factor)
     G = Hq // Hkv
@@ -196,13 +216,17 @@ def attention(q, k, v, d_o=None, *, num_gqa_groups=None, causal=True, window=(-1
     res = {"o": np.zeros((B, S, Hq, dv_dim)), "lse": np.zeros((B, Hq, S))}
     if grads:
         res.update(dq=np.zeros((B, S, Hq, dqk)), dk=np.zeros((B, S, Hkv, dqk)),
-                   dv=np.zeros((B, S, Hkv, dv_dim)), dalpha=np.zeros(Hq))
+                   dv=np.zeros((B, S, Hkv, dv_dim)), dalpha=np.zeros(Hq),
+                   dbias=None if bias is None else np.zeros(np.shape(bias)))
+    if bias is not None and (np.ndim(bias) != 4 or np.shape(bias)[0] not in (1, B) or
+                             np.shape(bias)[1] not in (1, Hq) or np.shape(bias)[2:] != (S, S)):
+        raise ValueError("bias must have shape [1 or B, 1 or Hq, S, S]")
     for b in range(B):
         for g in range(Hkv):
             r = attention_group(q, k, v, d_o, b=b, g=g, num_gqa_groups=Hkv, causal=causal,
                                 window=window, scale_factor=scale_factor,
                                 softmax_type=softmax_type, softmax_offset=softmax_offset,
-                                seqlens=seqlens, want_grads=grads)
+                                seqlens=seqlens, want_grads=grads, bias=bias)
             hs = slice(g * G, (g + 1) * G)
             res["o"][b, :, hs, :] = r["o"]
             res["lse"][b, hs, :] = r["lse"]
@@ -211,6 +235,9 @@ def attention(q, k, v, d_o=None, *, num_gqa_groups=None, causal=True, window=(-1
                 res["dk"][b, :, g, :] = r["dk"]
                 res["dv"][b, :, g, :] = r["dv"]
                 res["dalpha"][hs] += r["dz"]
+                if bias is not None:
+                    for gi in range(G):
+                        res["dbias"][_bias_index(bias, b, g * G + gi)] += r["ds"][gi]
     if grads and softmax_type == VANILLA:
         res["dalpha"] = None
     return res

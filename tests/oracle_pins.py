@@ -34,6 +34,9 @@ What pins what:
                    axis vs one S x S problem per batch); finite differences
   philox_kat       the dropout generator (Philox4x32-10) against its published
                    known-answer vectors (tests/golden/philox4x32_10_kat.json)
+  bias_*           additive post-scale bias: torch SDPA with the bias as a float
+                   mask (autograd gives the bias gradient), zero / row-constant
+                   bias invariants, finite differences
   dropout_*        keep rate and stream independence; scalar loops with the
                    keep mask applied by hand; p = 0 == no dropout; finite
                    differences; unbiasedness over many offsets
@@ -809,10 +812,105 @@ def pin_dropout_sampled(orc):
                 _close(rk["dv"], full["dv"][b, keys, g], 1e-12, 1e-14, f"keys dV {ci} {st}")
 
 
+# ---- attention bias ---------------------------------------------------------
+
+BIAS_SHAPES = [(2, 4), (1, 4), (2, 1), (1, 1)]  # [Bb, Hb] of a [Bb, Hb, S, S] bias, B = 2, Hq = 4
+
+
+def pin_bias_torch(orc):
+    """Bias forward and backward, every broadcast shape and softmax type, vs
+    torch.nn.functional.scaled_dot_product_attention in float64 with the bias
+    (plus the mask as -inf) as its additive float mask; the bias gradient is
+    that mask's autograd gradient summed over the shared dimensions."""
+    import torch
+    F = torch.nn.functional
+    B, S, Hq, Hkv, dqk, dv = 2, 21, 4, 2, 8, 6
+    win, sl = (7, 0), [21, 13]
+    for si, (Bb, Hb) in enumerate(BIAS_SHAPES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(2300 + si, B, S, Hq, Hkv, dqk, dv)
+            bias = np.random.default_rng(2400 + si).standard_normal((Bb, Hb, S, S))
+            r = orc.attention(q, k, v, do, num_gqa_groups=Hkv, causal=True, window=win, softmax_type=st,
+                              softmax_offset=alpha, seqlens=np.array(sl), bias=bias)
+            G = Hq // Hkv
+            tq = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+            tk = torch.tensor(k.transpose(0, 2, 1, 3), requires_grad=True)
+            tv = torch.tensor(v.transpose(0, 2, 1, 3), requires_grad=True)
+            i, j = torch.arange(S)[:, None], torch.arange(S)[None, :]
+            vis = torch.zeros(B, 1, S, S, dtype=torch.bool)
+            dmask = torch.ones(B, 1, S, 1, dtype=torch.float64)
+            for b in range(B):
+                L = sl[b]
+                vis[b, 0] = (i < L) & (j < L) & (j <= i) & (j >= i - win[0])
+                dmask[b, 0, L:] = 0.0
+            vis2 = vis.clone()
+            vis2[:, :, :, 0] |= ~vis.any(dim=3)  # padded rows: one dummy key, zero upstream gradient
+            tb = torch.tensor(bias, requires_grad=True)
+            madd = torch.where(vis2, tb.expand(B, Hq, S, S), torch.tensor(-torch.inf, dtype=torch.float64))
+            kr, vr = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+            if st != "vanilla":
+                z = torch.zeros(Hq, dtype=torch.float64) if st == "off_by_one" else torch.tensor(alpha)
+                kr = torch.cat([kr, torch.zeros(B, Hq, 1, dqk, dtype=torch.float64)], dim=2)
+                vr = torch.cat([vr, torch.zeros(B, Hq, 1, dv, dtype=torch.float64)], dim=2)
+                madd = torch.cat([madd, z.view(1, Hq, 1, 1).expand(B, Hq, S, 1)], dim=3)
+            o = F.scaled_dot_product_attention(tq, kr, vr, attn_mask=madd, scale=1.0 / math.sqrt(dqk))
+            o.backward(torch.tensor(do.transpose(0, 2, 1, 3)) * dmask)
+            o_np = o.detach().numpy().transpose(0, 2, 1, 3)
+            for b in range(B):
+                _close(r["o"][b, :sl[b]], o_np[b, :sl[b]], 1e-10, 1e-12, f"bias O {Bb}x{Hb} {st}")
+            _close(r["dq"], tq.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"bias dQ {Bb}x{Hb} {st}")
+            _close(r["dk"], tk.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"bias dK {Bb}x{Hb} {st}")
+            _close(r["dv"], tv.grad.numpy().transpose(0, 2, 1, 3), 1e-10, 1e-12, f"bias dV {Bb}x{Hb} {st}")
+            _close(r["dbias"], tb.grad.numpy(), 1e-10, 1e-12, f"dbias {Bb}x{Hb} {st}")
+
+
+def pin_bias_invariants(orc):
+    """Zero bias == no bias; a bias constant along each row changes nothing
+    for vanilla softmax (shift invariance) and its gradient's rows sum to 0;
+    the bias gradient vanishes on pairs the mask hides."""
+    q, k, v, do, alpha = rand_case(2500)
+    kw = dict(num_gqa_groups=2, causal=True, window=(4, 0), scale_factor=0.5, seqlens=np.array([9, 6]))
+    for st in orc.SOFTMAX_TYPES:
+        base = orc.attention(q, k, v, do, softmax_type=st, softmax_offset=alpha, **kw)
+        r0 = orc.attention(q, k, v, do, softmax_type=st, softmax_offset=alpha, bias=np.zeros((1, 1, 9, 9)), **kw)
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            _close(r0[n], base[n], 0, 0, f"zero bias {n} {st}")
+    base = orc.attention(q, k, v, do, **kw)
+    rowc = np.random.default_rng(2501).standard_normal((2, 4, 9, 1)) * np.ones((1, 1, 1, 9))
+    r = orc.attention(q, k, v, do, bias=rowc, **kw)
+    for n in ("o", "dq", "dk", "dv"):
+        _close(r[n], base[n], 1e-12, 1e-14, f"row-constant bias {n}")
+    _close(r["dbias"].sum(axis=3), np.zeros((2, 4, 9)), 0, 1e-12, "dbias row sums")
+    for b, L in enumerate([9, 6]):
+        vis = orc.visible_mask(9, L, True, 4, 0)
+        assert not r["dbias"][b][:, ~vis].any(), "dbias on hidden pairs"
+
+
+def pin_bias_finite_diff(orc):
+    """The bias gradient (shared over the batch) vs central differences."""
+    hstep = 1e-6
+    for st in orc.SOFTMAX_TYPES:
+        q, k, v, do, alpha = rand_case(2600, B=2, S=5, Hq=2, Hkv=1, dqk=3, dv=2)
+        bias = np.random.default_rng(2601).standard_normal((1, 2, 5, 5))
+        kw = dict(num_gqa_groups=1, causal=False, window=(2, 1), scale_factor=0.7, softmax_type=st,
+                  softmax_offset=alpha, seqlens=np.array([5, 4]))
+        r = orc.attention(q, k, v, do, bias=bias, **kw)
+        fd = np.zeros_like(bias)
+        for idx in np.ndindex(bias.shape):
+            b0 = bias[idx]
+            bias[idx] = b0 + hstep
+            lp = float((orc.attention(q, k, v, None, bias=bias, **kw)["o"] * do).sum())
+            bias[idx] = b0 - hstep
+            lm = float((orc.attention(q, k, v, None, bias=bias, **kw)["o"] * do).sum())
+            bias[idx] = b0
+            fd[idx] = (lp - lm) / (2 * hstep)
+        _close(r["dbias"], fd, 1e-6, 1e-8, f"dbias finite differences {st}")
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
             pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
             pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff,
             pin_philox_kat, pin_dropout_rate, pin_dropout_brute, pin_dropout_p0, pin_dropout_finite_diff,
             pin_dropout_mean, pin_dropout_layout,
-            pin_dropout_sampled]
+            pin_dropout_sampled, pin_bias_torch, pin_bias_invariants, pin_bias_finite_diff]
