@@ -31,7 +31,10 @@
  *   - off-by-one = an extra logit z = 0; learnable = an extra logit z = alpha_h
  *     (raw value of softmax_offset[h]); z is not multiplied by the scale;
  *   - the LSE output ("softmax_aux") is the natural-log log-sum-exp of each
- *     row including the sink term; empty rows get LSE = -inf (vanilla) or z_h.
+ *     row including the sink term; empty rows get LSE = -inf (vanilla) or z_h;
+ *   - attention dropout, when params.dropout_p > 0, multiplies P_ij in O (and
+ *     in the backward) by keep_ij / (1 - p); keep comes from a counter-based
+ *     generator keyed by the caller's rng state (see struct attn_params).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays; the
