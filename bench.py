@@ -30,11 +30,15 @@ TRAFFIC_RECORDS = {2: os.path.join(ROOT, "profiles", "attn_gqa_swa_s4096_hbm_tra
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources (names and bytes), to tie counter records to a build."""
+    """sha256 over the HIP sources and the build script (names and bytes): the
+    build script holds the compile flags, which change register allocation and
+    so the kernels' traffic; counter records are tied to this hash."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "scaled_dot_product_15_amd", "csrc", "*"))):
+    files = sorted(glob.glob(os.path.join(ROOT, "scaled_dot_product_15_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "scaled_dot_product_15_amd", "build.py"))
+    for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
@@ -56,6 +60,30 @@ def measured_traffic(config, kernel):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
+def visible_pairs(S, L, causal, window_left, window_right):
+    """Visible (query, key) pairs of one (batch, query head), in closed form:
+    row i < L sees keys max(0, i - left) .. min(L - 1, i [causal], i + right)
+    (windows inclusive, -1 unbounded), i.e. max(0, hi - lo + 1) keys."""
+    import numpy as np
+    L = max(0, min(int(L), int(S)))
+    i = np.arange(L, dtype=np.int64)
+    hi = np.full(L, L - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, i)
+    if window_right >= 0:
+        hi = np.minimum(hi, i + window_right)
+    lo = np.maximum(0, i - window_left) if window_left >= 0 else np.zeros(L, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def effective_flops(pairs, d_qk, d_v):
+    """Effective FLOPs of the metric, counted on visible pairs only: forward
+    2 * pairs * (d_qk + d_v) (S = QK^T, O = PV); backward
+    2 * pairs * (3 d_qk + 2 d_v) (S recomputed, dP = dO V^T, dV = P^T dO,
+    dK = dS^T Q, dQ = dS K)."""
+    return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)
+
+
 def kernel_flops_per_pair(d_qk, d_v):
     """Algorithmic MFMA FLOPs per visible pair of each kernel."""
     return {
@@ -63,6 +91,12 @@ def kernel_flops_per_pair(d_qk, d_v):
         "bwd_dkdv": 2 * (2 * d_qk + 2 * d_v),    # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
         "bwd_dq": 2 * (2 * d_qk + d_v),          # S, dP, dQ = dS K
     }
+
+
+def workload_pairs(p, seqlens):
+    """Visible pairs over all batches and query heads of workload p."""
+    return sum(visible_pairs(p.S, p.S if seqlens is None else int(seqlens[b]), p.causal,
+                             p.window[0], p.window[1]) for b in range(p.B)) * p.Hq
 
 
 def cpu_baseline(p, arr, groups):
@@ -91,10 +125,12 @@ def cpu_baseline(p, arr, groups):
                                window=p.window, scale_factor=p.scale_factor or None,
                                softmax_type=p.softmax_type, softmax_offset=arr["alpha"],
                                seqlens=seq)
-        L = p.S if seq is None else int(seq[b])
-        pairs += oracle.visible_pairs(p.S, L, p.causal, p.window[0], p.window[1]) * (p.Hq // p.Hkv)
     dt = time.perf_counter() - t0
-    ff, fb = oracle.effective_flops(pairs, p.d_qk, p.d_v)
+    for n in range(groups):
+        b = n // p.Hkv
+        L = p.S if seq is None else int(seq[b])
+        pairs += visible_pairs(p.S, L, p.causal, p.window[0], p.window[1]) * (p.Hq // p.Hkv)
+    ff, fb = effective_flops(pairs, p.d_qk, p.d_v)
     return {"value": (ff + fb) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
             "sample": f"{groups} of {p.B * p.Hkv} (batch, kv-head) groups of the workload: "
@@ -139,7 +175,6 @@ def main():
         print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}), flush=True)
         return
 
-    import oracle
     from scaled_dot_product_15_amd import binding, inputs
 
     p = inputs.workload_configs()[args.config][args.case]
@@ -195,13 +230,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # Forward / backward split and per-kernel breakdown: separate passes of the
-    # same number of steps with HIP events on the launch stream.
+    # Forward / backward split and per-kernel breakdown first: passes of the
+    # same number of steps with HIP events on the launch stream.  They also
+    # bring the GPU to its steady clock before the event-free timed loop.
     split = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for ev in split:
         ev[0].record(stream)
@@ -214,6 +245,12 @@ def main():
     for i in range(args.steps):
         staged_step(events[i])
     torch.cuda.synchronize()
+    # The timed region: exactly K steps, no events, synchronised on both sides.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
 
     per = {n: [] for n in names}
     for ev in events:
@@ -223,10 +260,8 @@ def main():
     med_ms = {n: statistics.median(v) for n, v in per.items()}
 
     seq = arr["seqlens"]
-    pairs_per_head = [oracle.visible_pairs(p.S, p.S if seq is None else int(seq[b]), p.causal,
-                                           p.window[0], p.window[1]) for b in range(p.B)]
-    pairs = sum(pairs_per_head) * p.Hq
-    f_fwd, f_bwd = oracle.effective_flops(pairs, p.d_qk, p.d_v)
+    pairs = workload_pairs(p, seq)
+    f_fwd, f_bwd = effective_flops(pairs, p.d_qk, p.d_v)
     ms_per_step = elapsed / args.steps * 1e3
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     t_fwd = statistics.median(ev[0].elapsed_time(ev[1]) for ev in split)

@@ -90,7 +90,7 @@ extern "C" {
 /* status codes */
 #define ATTN_OK 0
 #define ATTN_ERR_INVALID_ARG (-1)   /* bad size, enum, window, pointer */
-#define ATTN_ERR_UNSUPPORTED (-2)   /* valid problem, no kernel for (dtype, Dqk, Dv) */
+#define ATTN_ERR_UNSUPPORTED (-2)   /* valid problem, no kernel: (dtype, Dqk, Dv) or scale < 0 */
 #define ATTN_ERR_WORKSPACE (-3)     /* workspace_bytes below the required size */
 #define ATTN_ERR_HIP (-4)           /* a HIP launch failed */
 
@@ -107,7 +107,7 @@ struct attn_params {
   int32_t mask_type;      /* ATTN_MASK_NONE | ATTN_MASK_CAUSAL */
   int32_t window_left;    /* >= -1; -1 = unbounded */
   int32_t window_right;   /* >= -1; -1 = unbounded */
-  float scale_factor;     /* finite, >= 0; 0 => 1/sqrt(Dqk) */
+  float scale_factor;     /* finite; 0 => 1/sqrt(Dqk); < 0 is ATTN_ERR_UNSUPPORTED */
   int32_t softmax_type;   /* ATTN_SOFTMAX_* */
   /* Attention dropout (TE single-GPU page, "Other attention knobs": a rate
    * and an RNG; PR #2225's forward returns an rng_state).  Reading: inverted

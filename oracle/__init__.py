@@ -8,5 +8,5 @@ from .sdpa_oracle import (  # noqa: F401
     LEARNABLE, OFF_BY_ONE, SOFTMAX_TYPES, VANILLA, attention, attention_group, attention_keys,
     attention_dropout, attention_packed, attention_rows, dropout_keep, dropout_threshold,
     packed_visible_mask, philox4x32_10, visible_rows,
-    effective_flops, kv_head, sink_logit, visible_mask, visible_pairs,
+    kv_head, sink_logit, visible_mask, visible_pairs,
 )

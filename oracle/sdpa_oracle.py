@@ -260,15 +260,6 @@ def visible_pairs(S: int, L: int, causal: bool, window_left: int, window_right: 
     return total
 
 
-def effective_flops(pairs: int, d_qk: int, d_v: int):
-    """Effective FLOPs of forward and backward over the visible pairs.
-
-    forward: score (2 d_qk) and attend (2 d_v) per pair; backward: score
-    recompute, dP, dV, dK, dQ = 2 (3 d_qk + 2 d_v) per pair.
-    """
-    return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)
-
-
 def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_right: int,
                  cols=None) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: the visible_mask definition for selected

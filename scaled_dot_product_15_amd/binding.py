@@ -11,6 +11,7 @@ softmax_type / softmax_offset).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -213,6 +214,30 @@ def _check_buffer(t, shape, dtype, name):
                          f"got {t.dtype} {list(t.shape)}")
 
 
+def _sink_offsets(softmax_offset, Hq, q):
+    """The learnable sink logits as a contiguous float32 [Hq] device tensor on
+    q's device (a copy when the caller's tensor has another dtype or layout).
+    The kernels read softmax_offset[h] for every query head h, so a host
+    tensor or a short one is refused here."""
+    torch = _torch()
+    if softmax_offset is None:
+        raise ValueError("learnable softmax needs softmax_offset [Hq]")
+    if not isinstance(softmax_offset, torch.Tensor) or not softmax_offset.is_cuda \
+            or softmax_offset.device != q.device:
+        raise ValueError("softmax_offset must be a device tensor on q's device")
+    if softmax_offset.numel() != Hq:
+        raise ValueError(f"softmax_offset must hold num_heads = {Hq} values, got {softmax_offset.numel()}")
+    return softmax_offset.reshape(-1).to(torch.float32).contiguous()
+
+
+def _on_stream(stream):
+    """Context for the call's torch work (allocations, dtype copies): on the
+    launch stream, so that memory freed when the call returns is reused only
+    after the kernels queued on that stream, and copies precede the kernels."""
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _check_seqlens(seqlens, B, S):
     torch = _torch()
     if seqlens is None:
@@ -252,6 +277,15 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
     dropout with the generator state rng_state = (seed, offset); pass the
     same values to attn_bwd.
     """
+    with _on_stream(stream):
+        return _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
+                         softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state, out, lse,
+                         stream, check_seqlens)
+
+
+def _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
+              softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state, out, lse, stream,
+              check_seqlens):
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
@@ -259,14 +293,7 @@ def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_si
     B, S, Hq = p.batch, p.seqlen, p.num_heads
     if check_seqlens and packed is None:
         _check_seqlens(seqlens, B, S)
-    if softmax_type == "learnable":
-        if softmax_offset is None:
-            raise ValueError("learnable softmax needs softmax_offset [Hq]")
-        softmax_offset = softmax_offset.reshape(-1).to(torch.float32).contiguous()
-        if softmax_offset.numel() != Hq:
-            raise ValueError("softmax_offset must hold num_heads values")
-    else:
-        softmax_offset = None
+    softmax_offset = _sink_offsets(softmax_offset, Hq, q) if softmax_type == "learnable" else None
     o_shape = tuple(q.shape[:-1]) + (p.head_dim_v,)
     o = out if out is not None else torch.empty(o_shape, dtype=q.dtype, device=q.device)
     l = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
@@ -290,6 +317,15 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     for attn_fwd (packed THD when seq_offsets is given); dropout_p and
     rng_state must match the forward's.
     """
+    with _on_stream(stream):
+        return _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
+                         softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p,
+                         rng_state, want_d_offset, workspace, outs, stream, check_seqlens, stage)
+
+
+def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
+              softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state,
+              want_d_offset, workspace, outs, stream, check_seqlens, stage):
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
@@ -301,14 +337,10 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     for t in (o, d_o):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or tuple(t.shape) != o_shape:
             raise ValueError(f"o and d_o must be contiguous {list(o_shape)} tensors of q's dtype")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B,Hq,S] tensor")
-    if softmax_type == "learnable":
-        if softmax_offset is None:
-            raise ValueError("learnable softmax needs softmax_offset [Hq]")
-        softmax_offset = softmax_offset.reshape(-1).to(torch.float32).contiguous()
-    else:
-        softmax_offset = None
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous() \
+            or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 [B,Hq,S] device tensor")
+    softmax_offset = _sink_offsets(softmax_offset, Hq, q) if softmax_type == "learnable" else None
     want = softmax_type == "learnable" or (softmax_type == "off_by_one" and bool(want_d_offset))
     if outs is not None:
         dq, dk, dv, doff = outs
@@ -317,6 +349,8 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
         _check_buffer(dv, v.shape, q.dtype, "dv")
         if want and doff is not None:
             _check_buffer(doff, (Hq,), torch.float32, "d_softmax_offset")
+        if want and doff is None:
+            doff = torch.empty(Hq, dtype=torch.float32, device=q.device)
     else:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)

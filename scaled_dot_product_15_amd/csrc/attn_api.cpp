@@ -12,6 +12,9 @@ using namespace sdpa;
 namespace {
 
 bool supported(const attn_params* p) {
+  // A negative scale is a valid problem; the kernels take each row's running
+  // max on unscaled scores and multiply it by the scale, which needs scale >= 0.
+  if (p->scale_factor < 0.0f) return false;
   int bm, bn;
   if (p->dtype == ATTN_BF16) return fwd_bf16_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
   return fwd_f32_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
@@ -25,7 +28,7 @@ int check_fields(const attn_params* p) {
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (p->mask_type != ATTN_MASK_NONE && p->mask_type != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
-  if (!isfinite(p->scale_factor) || p->scale_factor < 0.0f) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(p->scale_factor)) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type < ATTN_SOFTMAX_VANILLA || p->softmax_type > ATTN_SOFTMAX_LEARNABLE) return ATTN_ERR_INVALID_ARG;
   if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return ATTN_ERR_INVALID_ARG;  // also rejects NaN
   // Kernels index rows with 32-bit (batch * S + i) and launch one-dimensional
@@ -220,7 +223,7 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported (dtype, head_dim_qk, head_dim_v) combination";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported: no kernel for this (dtype, head_dim_qk, head_dim_v) or a negative scale";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";

@@ -7,9 +7,12 @@
 //
 // Work decomposition: one workgroup of 4 waves owns BM = 128 query rows of one
 // (batch, query head); each wave owns 32 rows.  The workgroup walks the key
-// tiles (BN keys) that the mask engine says are visible from its rows; each
-// wave skips the tiles its own 32 rows cannot see and evaluates the mask per
-// element only on tiles its rows see partially.
+// tiles (BN keys) that the mask engine says are visible from any of its rows,
+// all four waves together (one barrier per tile).  Tiles that every row of
+// the workgroup sees in full run in an unmasked loop; the others (window
+// start, diagonal, padding) run in masked loops that evaluate the predicate
+// per element, where a wave whose rows see none of a tile computes it with
+// P = 0.
 //
 // Per key tile and wave:
 //   S^T (keys x queries) = K Q^T with A = K rows read from LDS and B = Q^T
@@ -19,8 +22,9 @@
 //   O^T (dims x queries) += V^T P^T with B = P^T taken straight from the S^T
 //   accumulator registers (after exp and bf16 rounding) and A = V^T read with
 //   LDS transpose loads from the row-major V tile (TrReads).
-// K and V tiles are staged global -> registers -> LDS as plain row copies;
-// the next tile's global loads are in flight while the current one computes.
+// K and V tiles reach LDS by direct memory-to-LDS copies into double
+// buffers (swizzled rows); K runs two tiles ahead, V one, so the copies are in
+// flight while the current tile computes.
 //
 // Online softmax in base 2 with the scale folded into one FMA.  The running
 // max only moves (and O and the row sum are rescaled) when a tile's max

@@ -47,13 +47,22 @@ def P(**kw):
 INVALID = [
     dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(Hq=8, Hkv=3), dict(d_qk=0), dict(d_v=-1),
     dict(window_size=(-2, 0)), dict(window_size=(0, -5)), dict(scale_factor=float("nan")),
-    dict(scale_factor=float("inf")), dict(scale_factor=-0.5), dict(B=70000, S=70000),
+    dict(scale_factor=float("inf")), dict(B=70000, S=70000),
 ]
 
 
 @pytest.mark.parametrize("kw", INVALID, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_validate_invalid(kw):
     assert binding.attn_validate(P(**kw)) == -1
+
+
+def test_validate_negative_scale_unsupported():
+    # A negative scale is a well-formed problem the kernels do not handle (they
+    # take the running max on unscaled scores): unsupported, not invalid.
+    assert binding.attn_validate(P(scale_factor=-0.5)) == -2
+    assert binding.attn_validate(P(scale_factor=-1e-30)) == -2
+    assert binding.attn_validate(P(dtype="f32", d_qk=64, d_v=64, scale_factor=-2.0)) == -2
+    assert binding.attn_validate(P(scale_factor=0.25)) == 0
 
 
 def test_validate_dropout_rate():

@@ -44,3 +44,52 @@ def test_backward_buffers_checked_and_workspace_in_bytes():
     r2 = binding.attn_bwd(q, k, v, o, lse, do)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(r1[:3], r2[:3]))
+
+
+def test_softmax_offset_checked_on_host():
+    """A host tensor, one on another device or one of the wrong length would
+    be read out of bounds (or from host memory) by the kernels: refused before
+    any launch."""
+    import torch
+    q, k, v = _qkv()
+    o, lse = binding.attn_fwd(q, k, v)
+    do = torch.randn_like(o)
+    good = torch.zeros(2, device="cuda")
+    for bad in (torch.zeros(2), torch.zeros(1, device="cuda"), torch.zeros(3, device="cuda"), None):
+        with pytest.raises(ValueError):
+            binding.attn_fwd(q, k, v, softmax_type="learnable", softmax_offset=bad)
+        with pytest.raises(ValueError):
+            binding.attn_bwd(q, k, v, o, lse, do, softmax_type="learnable", softmax_offset=bad)
+    # the accepted form: [Hq] (or [1, Hq, 1, 1]) on q's device, any float dtype
+    binding.attn_fwd(q, k, v, softmax_type="learnable", softmax_offset=good.reshape(1, 2, 1, 1).half())
+    torch.cuda.synchronize()
+
+
+def test_side_stream_matches_default_stream():
+    """stream= runs the call's allocations, the sink-logit copy and the kernels
+    on that stream; the results equal a default-stream run bitwise."""
+    import torch
+    torch.manual_seed(3)
+    B, S, Hq, Hkv, D = 2, 300, 4, 2, 128
+    q = torch.randn(B, S, Hq, D, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(B, S, Hkv, D, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(B, S, Hkv, D, device="cuda", dtype=torch.bfloat16)
+    do = torch.randn(B, S, Hq, D, device="cuda", dtype=torch.bfloat16)
+    alpha = torch.randn(Hq, device="cuda", dtype=torch.float64)  # forces a float32 copy in the call
+    kw = dict(num_gqa_groups=Hkv, window_size=(100, 0), softmax_type="learnable", softmax_offset=alpha)
+    ref_o, ref_lse = binding.attn_fwd(q, k, v, **kw)
+    ref = binding.attn_bwd(q, k, v, ref_o, ref_lse, do, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):  # repeated calls reuse the freed workspace memory
+        o, lse = binding.attn_fwd(q, k, v, stream=side, **kw)
+        got = binding.attn_bwd(q, k, v, o, lse, do, stream=side, **kw)
+        # unrelated work on the default stream that may reuse freed blocks
+        junk = torch.full((1 << 20,), 7.0, device="cuda")
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
