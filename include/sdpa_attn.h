@@ -93,6 +93,7 @@ extern "C" {
 #define ATTN_ERR_UNSUPPORTED (-2)   /* valid problem, no kernel: (dtype, Dqk, Dv) or scale < 0 */
 #define ATTN_ERR_WORKSPACE (-3)     /* workspace_bytes below the required size */
 #define ATTN_ERR_HIP (-4)           /* a HIP launch failed */
+#define ATTN_ERR_TOO_LARGE (-5)     /* attn_bwd_noalloc: the problem needs more than its scratch */
 
 /* Problem description.  All fields are plain 32-bit integers or floats for a
  * fixed ABI. */
@@ -190,6 +191,29 @@ int attn_bwd_stage(int stage, const struct attn_params* p, const void* q, const 
                    const void* o, const void* d_o, const float* lse, const float* softmax_offset,
                    const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
                    float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, kernels and results as attn_bwd, minus
+ * the workspace: the backward runs in a scratch array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that the library holds in device memory on each
+ * GPU it runs on, from the first call on that GPU until the process ends.
+ * Nothing is allocated or freed per call (no hipMalloc, hipFree or
+ * allocating library routine).
+ *   - A problem whose attn_bwd_workspace_size exceeds the scratch returns
+ *     ATTN_ERR_TOO_LARGE before anything is enqueued; use attn_bwd then.
+ *   - Work is enqueued on `stream`, which must belong to the current device
+ *     (the scratch used is the current device's).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *     one GPU (other streams, other threads, without ordering between them)
+ *     race and give wrong results.  Calls on one stream are ordered.  Every
+ *     value a call reads from the scratch it has written first, so nothing
+ *     needs clearing between calls. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int attn_bwd_noalloc(const struct attn_params* p, const void* q, const void* k, const void* v,
+                     const void* o, const void* d_o, const float* lse, const float* softmax_offset,
+                     const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
+                     float* d_softmax_offset, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

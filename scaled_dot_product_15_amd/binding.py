@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libsdpa_mi355x.so")
 ATTN_F32, ATTN_BF16 = 0, 1
 MASKS = {"no_mask": 0, "none": 0, "causal": 1}
 SOFTMAX = {"vanilla": 0, "off_by_one": 1, "learnable": 2}
-STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error"}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error",
+          -5: "too large for the allocation-free scratch"}
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # ATTN_NOALLOC_SCRATCH_BYTES
 
 _c_i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -53,6 +55,8 @@ EXPORTS = {
                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_bwd_stage": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_tile_shape": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32)]),
@@ -371,6 +375,52 @@ def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size,
         _check(lib.attn_bwd_stage(stage, *args), f"attn_bwd_stage({stage})")
     else:
         _check(lib.attn_bwd(*args), "attn_bwd")
+    return dq, dk, dv, doff
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, d_o, *, outs, num_gqa_groups=None, attn_mask_type="causal",
+                     window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
+                     seqlens=None, seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0),
+                     stream=None, check_seqlens=True):
+    """The allocation-free backward: attn_bwd's result in the caller's
+    outs = (dq, dk, dv, d_softmax_offset or None), with the library's static
+    per-GPU scratch as workspace.  Allocates nothing: every output must be
+    given, and a learnable softmax_offset must already be a contiguous float32
+    [Hq] device tensor.  Calls that overlap on one GPU race (they share the
+    scratch); calls on one stream are ordered."""
+    torch = _torch()
+    packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
+    p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
+                 dropout_p, rng_state)
+    B, S, Hq = p.batch, p.seqlen, p.num_heads
+    if check_seqlens and packed is None:
+        _check_seqlens(seqlens, B, S)
+    o_shape = tuple(q.shape[:-1]) + (p.head_dim_v,)
+    for t in (o, d_o):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or tuple(t.shape) != o_shape:
+            raise ValueError(f"o and d_o must be contiguous {list(o_shape)} tensors of q's dtype")
+    _check_buffer(lse, (B, Hq, S), torch.float32, "lse")
+    if softmax_type == "learnable":
+        if not isinstance(softmax_offset, torch.Tensor) or not softmax_offset.is_cuda \
+                or softmax_offset.device != q.device or softmax_offset.dtype != torch.float32 \
+                or not softmax_offset.is_contiguous() or softmax_offset.numel() != Hq:
+            raise ValueError(f"softmax_offset must be a contiguous float32 tensor of {Hq} values on q's "
+                             "device (no copy is made)")
+        softmax_offset = softmax_offset.reshape(-1)
+    else:
+        softmax_offset = None
+    dq, dk, dv, doff = outs
+    _check_buffer(dq, q.shape, q.dtype, "dq")
+    _check_buffer(dk, k.shape, q.dtype, "dk")
+    _check_buffer(dv, v.shape, q.dtype, "dv")
+    if softmax_type == "vanilla":
+        doff = None
+    elif doff is not None:
+        _check_buffer(doff, (Hq,), torch.float32, "d_softmax_offset")
+    _check(load_library().attn_bwd_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(softmax_offset),
+        _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doff), _stream(stream)),
+        "attn_bwd_noalloc")
     return dq, dk, dv, doff
 
 

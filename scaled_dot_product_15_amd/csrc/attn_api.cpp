@@ -142,9 +142,9 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
 
 }  // extern "C"
 
-namespace {
+namespace sdpa {
 
-int bwd_common(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
                const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
                const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace,
                size_t workspace_bytes, void* stream) {
@@ -198,7 +198,7 @@ int bwd_common(int stage, const attn_params* p, const void* q, const void* k, co
   return ATTN_OK;
 }
 
-}  // namespace
+}  // namespace sdpa
 
 extern "C" {
 
@@ -206,7 +206,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
              const float* lse, const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets,
              void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
              void* stream) {
-  return bwd_common(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv, d_softmax_offset,
+  return bwd_run(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv, d_softmax_offset,
                     workspace, workspace_bytes, stream);
 }
 
@@ -215,7 +215,7 @@ int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k
                    const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset,
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < ATTN_BWD_STAGE_PREPROCESS) return ATTN_ERR_INVALID_ARG;
-  return bwd_common(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
+  return bwd_run(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
                     d_softmax_offset, workspace, workspace_bytes, stream);
 }
 
@@ -226,6 +226,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported: no kernel for this (dtype, head_dim_qk, head_dim_v) or a negative scale";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_TOO_LARGE: return "backward workspace exceeds the allocation-free scratch (64 MiB)";
     default: return "unknown status";
   }
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "attn_common.h"
+#include "sdpa_attn.h"
 
 namespace sdpa {
 
@@ -46,6 +47,13 @@ hipError_t launch_bwd_dq_f32(const KArgs& a, int dqk, int dv, hipStream_t stream
 hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream);
 // d_softmax_offset[h] = sum over batches and chunks, fixed order.
 hipError_t launch_dz_reduce(const KArgs& a, hipStream_t stream);
+
+// The backward of attn_bwd / attn_bwd_stage (stage 0 = all stages) with the
+// workspace at `workspace`: host checks, then launches on `stream`.
+int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+            const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
+            const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace,
+            size_t workspace_bytes, void* stream);
 
 hipError_t launch_debug_tile_map(const KArgs& a, int bm, int bn, int8_t* out, hipStream_t stream);
 hipError_t launch_debug_mask_probe(const KArgs& a, uint8_t* out, hipStream_t stream);

@@ -284,3 +284,24 @@ def test_host_full_key_tiles_match_oracle_mask(causal, wl, wr):
 def test_fwd_tile_shape():
     assert binding.fwd_tile_shape(P()) == (128, 64)
     assert binding.fwd_tile_shape(P(d_qk=64, d_v=64, dtype="f32")) == (64, 64)
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """attn_bwd_noalloc checks the problem, its pointers and its size on the
+    host before touching the device: invalid arguments give -1 and a backward
+    whose workspace exceeds the static scratch gives ATTN_ERR_TOO_LARGE (-5).
+    The pointers below are never dereferenced (nothing is launched)."""
+    lib = binding.load_library()
+    fake = ctypes.c_void_p(256)
+    ptrs = [fake] * 6 + [None, None, None] + [fake] * 3 + [None, None]
+    # delta and LSE * log2(e) alone take 2 * 4 bytes per (batch, head, row): 128 MiB here
+    big = binding.make_params(8, 16384, 64, 64, 64, 64, "bf16", "causal")
+    assert binding.attn_bwd_workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_noalloc(ctypes.byref(big), *ptrs) == -5
+    assert "scratch" in binding.attn_status_string(-5)
+    small = binding.make_params(1, 64, 2, 1, 64, 64, "bf16", "causal")
+    bad = list(ptrs)
+    bad[0] = None  # q
+    assert lib.attn_bwd_noalloc(ctypes.byref(small), *bad) == -1
+    assert lib.attn_bwd_noalloc(ctypes.byref(P(B=0)), *ptrs) == -1
+    assert lib.attn_bwd_noalloc(ctypes.byref(P(d_qk=96, d_v=96)), *ptrs) == -2
