@@ -192,6 +192,36 @@ int attn_bwd_stage(int stage, const struct attn_params* p, const void* q, const 
                    const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
                    float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention with an additive bias.  TE single-GPU page, "Other attention
+ * knobs": the module takes a bias tensor with a bias type; PR #2225's backward
+ * returns grad_bias next to grad_q, grad_k, grad_v.  Neither gives the formula
+ * or the shapes; reading: a post-scale bias added to the scores of visible
+ * pairs,
+ *     s_ij = scale * Q[b,i,h,:] . K[b,j,kv(h),:] + bias[b', h', i, j],
+ * with bias [bias_batch, bias_heads, S, S] in params.dtype, bias_batch in
+ * {1, B} and bias_heads in {1, Hq} (a size-1 dim is shared: b' = 0 or b,
+ * h' = 0 or h).  Rows and keys are positions within the sequence (within
+ * the segment for packed inputs).  Masked pairs ignore the bias.
+ * Supported: bf16 with (Dqk, Dv) = (64, 64) or (128, 128), S a multiple of
+ * 8 and S <= 46336 (one bias matrix within 4 GiB); anything else with a bias
+ * is ATTN_ERR_UNSUPPORTED (pad S and pass seqlens for other lengths).  bias
+ * and d_bias must be 16-byte aligned (else ATTN_ERR_INVALID_ARG).  Otherwise
+ * as attn_fwd / attn_bwd (same checks, layouts, stream and ownership rules). */
+int attn_fwd_bias(const struct attn_params* p, const void* q, const void* k, const void* v,
+                  const void* bias, int32_t bias_batch, int32_t bias_heads,
+                  const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets,
+                  void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+/* Backward with the same bias.  d_bias: NULL (not computed) or a device
+ * array of the bias's shape, overwritten with d(loss)/d(bias): dS = P * (dP -
+ * delta) on the pairs each sharing (batch, head) sees, zero elsewhere,
+ * summed over the batches and heads that share a bias matrix in ascending
+ * order (bitwise reproducible). */
+int attn_bwd_bias(const struct attn_params* p, const void* q, const void* k, const void* v,
+                  const void* o, const void* d_o, const float* lse, const void* bias,
+                  int32_t bias_batch, int32_t bias_heads, void* d_bias, const float* softmax_offset,
+                  const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
+                  float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Allocation-free backward, for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, checks, kernels and results as attn_bwd, minus

@@ -277,7 +277,8 @@ def visible_rows(rows, S: int, L: int, causal: bool, window_left: int, window_ri
 
 
 def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True, window=(-1, -1),
-                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None, dropout=None):
+                   scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None, dropout=None,
+                   bias=None):
     """Outputs of selected query rows of one (batch b, query head h), in float64.
 
     A row's output, LSE, delta and dQ depend only on that row's visible keys,
@@ -285,7 +286,10 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
     the row mask is zero for every selected row are left out: they contribute
     exactly zero.  Returns o [n, dv], lse [n], delta [n], dq [n, dqk] and
     dz [n] = -exp(z - LSE_i) * delta_i (0 for vanilla).  dropout = (p, seed,
-    offset) applies attention dropout as attention_dropout does.
+    offset) applies attention dropout as attention_dropout does.  bias: the
+    additive post-scale bias of attention() ([Bb, Hb, S, S]); with it, ds
+    [n, c1 - c0] holds the rows' dS on keys c0 .. c1-1 (cols = (c0, c1)), zero
+    on every other key.
     """
     B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
     g = kv_head(h, Hq, Hkv)
@@ -307,6 +311,8 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
     doh = np.asarray(d_o[b, rows, h, :], dtype=np.float64)
     z = sink_logit(softmax_type, softmax_offset, h)
     s = scale * (qh @ kb.T)
+    if bias is not None:
+        s = s + np.asarray(bias[_bias_index(bias, b, h)][rows][:, c0:c1], dtype=np.float64)
     p, lse = _softmax_rows(s, mask, z)
     zmat = _dropout_factors(dropout, b, h, Hq, rows, np.arange(c0, c1))
     o = (p * zmat) @ vb
@@ -317,17 +323,18 @@ def attention_rows(q, k, v, d_o, *, b, h, rows, num_gqa_groups=None, causal=True
         dz = np.zeros(len(rows))
     else:
         dz = -np.exp(z - np.where(np.isfinite(lse), lse, z)) * delta
-    return {"o": o, "lse": lse, "delta": delta, "dq": dq, "dz": dz}
+    return {"o": o, "lse": lse, "delta": delta, "dq": dq, "dz": dz, "ds": ds, "cols": (c0, c1)}
 
 
 def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True, window=(-1, -1),
                    scale_factor=None, softmax_type=VANILLA, softmax_offset=None, seqlens=None,
-                   row_block=1024, dropout=None):
+                   row_block=1024, dropout=None, bias=None):
     """dK, dV of selected keys of one (batch b, KV head g), in float64.
 
     dK_j = scale * sum_h sum_i dS_ij Q_i and dV_j = sum_h sum_i P_ij dO_i over
     the query heads h of the group and every row i that sees key j; each such
     row's LSE and delta come from attention_rows.  Returns dk [n, dqk], dv [n, dv].
+    bias: the additive post-scale bias of attention().
     """
     B, S, Hq, Hkv, dqk, dv_dim, scale = _resolve(q, k, v, num_gqa_groups, scale_factor)
     G = Hq // Hkv
@@ -341,7 +348,8 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
     dk = np.zeros((len(keys), dqk))
     dvv = np.zeros((len(keys), dv_dim))
     kw = dict(num_gqa_groups=Hkv, causal=causal, window=window, scale_factor=scale_factor,
-              softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens, dropout=dropout)
+              softmax_type=softmax_type, softmax_offset=softmax_offset, seqlens=seqlens, dropout=dropout,
+              bias=bias)
     # row blocks never straddle a gap in rows_all, so each block's key range
     # stays as narrow as the mask allows
     cuts = np.nonzero(np.diff(rows_all) > 1)[0] + 1
@@ -354,6 +362,8 @@ def attention_keys(q, k, v, d_o, *, b, g, keys, num_gqa_groups=None, causal=True
             qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
             doh = np.asarray(d_o[b, rows, h, :], dtype=np.float64)
             s = scale * (qh @ kk.T)
+            if bias is not None:
+                s = s + np.asarray(bias[_bias_index(bias, b, h)][rows][:, keys], dtype=np.float64)
             lse = np.where(np.isfinite(rr["lse"]), rr["lse"], 0.0)
             p = np.where(m, np.exp(np.where(m, s, 0.0) - lse[:, None]), 0.0)
             zmat = _dropout_factors(dropout, b, h, Hq, rows, keys)

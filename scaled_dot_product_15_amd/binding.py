@@ -55,6 +55,10 @@ EXPORTS = {
                                 _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_bwd_stage": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "attn_fwd_bias": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _c_i32, _c_i32, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "attn_bwd_bias": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -234,6 +238,18 @@ def _sink_offsets(softmax_offset, Hq, q):
     return softmax_offset.reshape(-1).to(torch.float32).contiguous()
 
 
+def _check_bias(bias, q, B, Hq, S):
+    """An additive bias [1 or B, 1 or Hq, S, S] of q's dtype on q's device;
+    returns (bias_batch, bias_heads)."""
+    torch = _torch()
+    if not isinstance(bias, torch.Tensor) or not bias.is_cuda or bias.device != q.device \
+            or bias.dtype != q.dtype or not bias.is_contiguous() or bias.dim() != 4 \
+            or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq) or tuple(bias.shape[2:]) != (S, S):
+        raise ValueError(f"bias must be a contiguous {q.dtype} device tensor of shape [1 or {B}, 1 or {Hq}, "
+                         f"{S}, {S}]")
+    return int(bias.shape[0]), int(bias.shape[1])
+
+
 def _on_stream(stream):
     """Context for the call's torch work (allocations, dtype copies): on the
     launch stream, so that memory freed when the call returns is reused only
@@ -272,24 +288,25 @@ def _layout(q, seq_offsets, seqlens, max_seqlen, check):
 def attn_fwd(q, k, v, *, num_gqa_groups=None, attn_mask_type="causal", window_size=(-1, -1),
              scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None,
              seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0), out=None, lse=None,
-             stream=None, check_seqlens=True):
+             stream=None, check_seqlens=True, bias=None):
     """Forward attention.  Returns (O, LSE [B,Hq,S]).
 
     BSHD: q [B,S,Hq,Dqk], k/v [B,S,Hkv,D], O [B,S,Hq,Dv].  Packed (THD, when
     seq_offsets [B+1] is given): q [T,Hq,Dqk], k/v [T,Hkv,D], O [T,Hq,Dv];
     S = max_seqlen or the largest segment.  dropout_p > 0 applies attention
     dropout with the generator state rng_state = (seed, offset); pass the
-    same values to attn_bwd.
+    same values to attn_bwd.  bias: an additive post-scale bias
+    [1 or B, 1 or Hq, S, S] of q's dtype (attn_fwd_bias).
     """
     with _on_stream(stream):
         return _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
                          softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state, out, lse,
-                         stream, check_seqlens)
+                         stream, check_seqlens, bias)
 
 
 def _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type,
               softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state, out, lse, stream,
-              check_seqlens):
+              check_seqlens, bias):
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
@@ -304,6 +321,12 @@ def _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor
     _check_buffer(o, o_shape, q.dtype, "out")
     _check_buffer(l, (B, Hq, S), torch.float32, "lse")
     lib = load_library()
+    if bias is not None:
+        bb, bh = _check_bias(bias, q, B, Hq, S)
+        _check(lib.attn_fwd_bias(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), bb, bh,
+                                 _ptr(softmax_offset), _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), None, 0,
+                                 _stream(stream)), "attn_fwd_bias")
+        return o, l
     _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(softmax_offset),
                         _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), None, 0, _stream(stream)),
            "attn_fwd")
@@ -313,8 +336,10 @@ def _attn_fwd(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor
 def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causal",
              window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
              seqlens=None, seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0),
-             want_d_offset=None, workspace=None, outs=None, stream=None, check_seqlens=True, stage=0):
-    """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None).
+             want_d_offset=None, workspace=None, outs=None, stream=None, check_seqlens=True, stage=0,
+             bias=None, d_bias=None, want_d_bias=True):
+    """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None),
+    and with a bias (dQ, dK, dV, d_softmax_offset or None, d_bias or None).
 
     d_softmax_offset is returned for learnable softmax (always) and for
     off-by-one when want_d_offset is true; vanilla returns None.  Layouts as
@@ -324,12 +349,13 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
     with _on_stream(stream):
         return _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
                          softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p,
-                         rng_state, want_d_offset, workspace, outs, stream, check_seqlens, stage)
+                         rng_state, want_d_offset, workspace, outs, stream, check_seqlens, stage, bias, d_bias,
+                         want_d_bias)
 
 
 def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
               softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state,
-              want_d_offset, workspace, outs, stream, check_seqlens, stage):
+              want_d_offset, workspace, outs, stream, check_seqlens, stage, bias, d_bias, want_d_bias):
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
@@ -344,6 +370,14 @@ def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size,
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous() \
             or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 [B,Hq,S] device tensor")
+    if bias is not None:
+        bias_dims = _check_bias(bias, q, B, Hq, S)
+        if stage:
+            raise ValueError("the staged backward takes no bias")
+        if d_bias is not None:
+            _check_buffer(d_bias, bias.shape, bias.dtype, "d_bias")
+        elif want_d_bias:
+            d_bias = torch.empty_like(bias)
     softmax_offset = _sink_offsets(softmax_offset, Hq, q) if softmax_type == "learnable" else None
     want = softmax_type == "learnable" or (softmax_type == "off_by_one" and bool(want_d_offset))
     if outs is not None:
@@ -371,6 +405,13 @@ def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size,
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
             _ptr(softmax_offset), _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(doff), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if bias is not None:
+        _check(lib.attn_bwd_bias(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                 _ptr(bias), bias_dims[0], bias_dims[1], _ptr(d_bias), _ptr(softmax_offset),
+                                 _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doff),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+               "attn_bwd_bias")
+        return dq, dk, dv, doff, d_bias
     if stage:
         _check(lib.attn_bwd_stage(stage, *args), f"attn_bwd_stage({stage})")
     else:

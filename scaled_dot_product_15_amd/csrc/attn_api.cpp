@@ -78,6 +78,7 @@ KArgs make_args(const attn_params* p) {
   a.softmax_type = p->softmax_type;
   a.scale = p->scale_factor != 0.0f ? p->scale_factor : (float)(1.0 / sqrt((double)p->head_dim_qk));
   a.scale_log2 = a.scale * kLog2e;
+  a.inv_scale = 1.0f / a.scale;
   a.n_chunks = n_chunks(p);
   a.n_splits = kv_splits(p);
   // Dropout: byte threshold round(256 p), kept probabilities scaled by
@@ -89,6 +90,33 @@ KArgs make_args(const attn_params* p) {
   a.drop_seed_hi = p->dropout_seed_hi;
   a.drop_offset = p->dropout_offset;
   return a;
+}
+
+// Bias arguments (attn_fwd_bias / attn_bwd_bias): an additive post-scale bias
+// of shape [bias_batch, bias_heads, S, S] in the input dtype.
+int check_bias(const attn_params* p, const void* bias, int32_t bias_batch, int32_t bias_heads) {
+  if (!bias) return ATTN_ERR_INVALID_ARG;
+  if (bias_batch != 1 && bias_batch != p->batch) return ATTN_ERR_INVALID_ARG;
+  if (bias_heads != 1 && bias_heads != p->num_heads) return ATTN_ERR_INVALID_ARG;
+  if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const bool dims = (p->head_dim_qk == 64 && p->head_dim_v == 64) || (p->head_dim_qk == 128 && p->head_dim_v == 128);
+  if (!dims) return ATTN_ERR_UNSUPPORTED;
+  // Kernels address one [S, S] bias matrix with 32-bit byte offsets, copy
+  // 16-byte pieces of its rows (rows of S * 2 bytes, S a multiple of 8, on a
+  // 16-byte aligned base) and add bias / scale to the unscaled scores.
+  if ((long long)p->seqlen * p->seqlen * 2 > 0xffffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (p->seqlen % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(bias) & 15) != 0) return ATTN_ERR_INVALID_ARG;
+  const KArgs a = make_args(p);
+  if (!isfinite(a.inv_scale)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+void set_bias(KArgs& a, const void* bias, void* d_bias, int32_t bias_batch, int32_t bias_heads) {
+  a.bias = bias;
+  a.d_bias = d_bias;
+  a.bias_b = bias_batch;
+  a.bias_h = bias_heads;
 }
 
 MaskSpec host_mask(const attn_params* p, int L) {
@@ -117,16 +145,23 @@ size_t attn_bwd_workspace_size(const attn_params* p) {
   return 2 * delta_bytes(p) + dz_bytes(p) + kv_part_bytes(p);
 }
 
-int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
-             const int32_t* seqlens, const int32_t* seq_offsets, void* o, float* lse, void* workspace,
-             size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+int fwd_run(const attn_params* p, const void* q, const void* k, const void* v, const void* bias, int32_t bias_batch,
+            int32_t bias_heads, const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets,
+            void* o, float* lse, void* stream) {
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && !softmax_offset) return ATTN_ERR_INVALID_ARG;
+  if (bias) {
+    const int rb = check_bias(p, bias, bias_batch, bias_heads);
+    if (rb != ATTN_OK) return rb;
+  }
   KArgs a = make_args(p);
+  if (bias) set_bias(a, bias, nullptr, bias_batch, bias_heads);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -140,6 +175,28 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   return hip_status(launch_fwd_f32(a, p->head_dim_qk, p->head_dim_v, s));
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const float* softmax_offset,
+             const int32_t* seqlens, const int32_t* seq_offsets, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return fwd_run(p, q, k, v, nullptr, 0, 0, softmax_offset, seqlens, seq_offsets, o, lse, stream);
+}
+
+int attn_fwd_bias(const attn_params* p, const void* q, const void* k, const void* v, const void* bias,
+                  int32_t bias_batch, int32_t bias_heads, const float* softmax_offset, const int32_t* seqlens,
+                  const int32_t* seq_offsets, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!bias) return ATTN_ERR_INVALID_ARG;
+  return fwd_run(p, q, k, v, bias, bias_batch, bias_heads, softmax_offset, seqlens, seq_offsets, o, lse, stream);
+}
+
 }  // extern "C"
 
 namespace sdpa {
@@ -147,7 +204,7 @@ namespace sdpa {
 int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
                const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
                const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream, const BiasArgs* bias) {
   if (stage < 0 || stage > ATTN_BWD_STAGE_OFFSET_GRAD) return ATTN_ERR_INVALID_ARG;
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
@@ -157,7 +214,14 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   if (!workspace) return ATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_ERR_INVALID_ARG;
   if (workspace_bytes < attn_bwd_workspace_size(p)) return ATTN_ERR_WORKSPACE;
+  if (bias) {
+    if (stage != 0) return ATTN_ERR_INVALID_ARG;
+    const int rb = check_bias(p, bias->bias, bias->batch, bias->heads);
+    if (rb != ATTN_OK) return rb;
+    if ((reinterpret_cast<uintptr_t>(bias->d_bias) & 15) != 0) return ATTN_ERR_INVALID_ARG;
+  }
   KArgs a = make_args(p);
+  if (bias) set_bias(a, bias->bias, bias->d_bias, bias->batch, bias->heads);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -191,6 +255,9 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
     if (e == hipSuccess && a.n_splits > 1) e = launch_dkdv_split_reduce(a, dqk, dvd, s);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
+  if (stage == 0 && a.bias && a.d_bias) {
+    if (launch_bwd_dbias_bf16(a, dqk, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
+  }
   if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&
       p->softmax_type != ATTN_SOFTMAX_VANILLA) {
     if (launch_dz_reduce(a, s) != hipSuccess) return ATTN_ERR_HIP;
@@ -207,7 +274,17 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
              void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes,
              void* stream) {
   return bwd_run(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv, d_softmax_offset,
-                    workspace, workspace_bytes, stream);
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+int attn_bwd_bias(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                  const float* lse, const void* bias, int32_t bias_batch, int32_t bias_heads, void* d_bias,
+                  const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk,
+                  void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bias) return ATTN_ERR_INVALID_ARG;
+  const BiasArgs ba = {bias, d_bias, bias_batch, bias_heads};
+  return bwd_run(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv, d_softmax_offset,
+                 workspace, workspace_bytes, stream, &ba);
 }
 
 int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
@@ -216,7 +293,7 @@ int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < ATTN_BWD_STAGE_PREPROCESS) return ATTN_ERR_INVALID_ARG;
   return bwd_run(stage, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
-                    d_softmax_offset, workspace, workspace_bytes, stream);
+                    d_softmax_offset, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* attn_status_string(int status) {

@@ -1,0 +1,198 @@
+// Gradient of the attention bias, bf16 inputs, fp32 accumulation, gfx950 MFMA 32x32x16.
+//
+// With the bias read as an additive post-scale bias on the scores
+// (s = scale q.k + bias; TE single-GPU page "Other attention knobs" passes a
+// bias, PR #2225's backward returns grad_bias), its gradient for a bias matrix
+// (b', h') is the sum, over the (batch, query head) pairs (b, h) that share it,
+// of dS = P (dP - delta) on the pairs each of them sees (zero elsewhere):
+//     P = exp(scale q.k + bias - LSE),  dP = dO V^T.
+// Deterministic: a workgroup owns one block of the output and sums the
+// sharing pairs in ascending order in registers; nothing is accumulated in
+// memory.
+//
+// Work decomposition: 4 waves x 32 query rows (128 rows) of one bias matrix,
+// over a range of key tiles of 64 keys.  Per key tile, for each sharing pair
+// that sees any of it: K and V tiles of that pair's KV head are copied to LDS,
+// the pair's Q and dO rows are loaded as register operands (as in the dQ
+// kernel), S^T = K Q^T and dP^T = V dO^T are recomputed by MFMA (a lane owns
+// a query row), and dS is added to the tile's fp32 accumulators.  delta and
+// LSE * log2(e) come from the backward pre-pass in the workspace.  The tile is
+// then written whole (zeros where no sharing pair sees it), so the output
+// needs no clearing.
+#include "dropout.h"
+#include "launch.h"
+
+namespace sdpa {
+
+template <int DQK, int DV>
+struct DbiasCfg {
+  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int KCH = DQK / 8, VCH = DV / 8;
+  static constexpr int KT = BN * DQK, VT = BN * DV;
+  static constexpr int LDS_ELEMS = KT + VT;
+};
+
+template <int DQK, int DV, bool DROP>
+__global__ __launch_bounds__(256, 2) void bwd_dbias_bf16_kernel(KArgs a) {
+  using C = DbiasCfg<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  uint16_t* Ks = lds;
+  uint16_t* Vs = lds + C::KT;
+
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  // Workgroup id -> (bias matrix, query tile, key-tile chunk).
+  const int n_qt = a.n_tiles, n_kc = a.n_chunks;
+  const int kc = blockIdx.x % n_kc;
+  const int qt = (blockIdx.x / n_kc) % n_qt;
+  const int mat = blockIdx.x / (n_kc * n_qt);
+  const int bb = mat / a.bias_h, hh = mat % a.bias_h;  // the bias matrix (b', h')
+  const int n_kt = (a.S + C::BN - 1) / C::BN;
+  const int per_chunk = (n_kt + n_kc - 1) / n_kc;
+  const int kt_lo = kc * per_chunk, kt_hi = kt_lo + per_chunk < n_kt ? kt_lo + per_chunk : n_kt;
+  // Sharing pairs: all batches when bias_b == 1, all query heads when bias_h == 1.
+  const int nb = a.bias_b == 1 ? a.B : 1, nh = a.bias_h == 1 ? a.Hq : 1;
+
+  const int i0 = qt * C::BM, qw0 = i0 + w * 32, qi = qw0 + l32;
+  const DropGen dg = drop_gen(a);
+  const TileCopy<C::BN, C::KCH, C::NT> kcopy(tid, (uint32_t)(a.Hkv * DQK * 2));
+  const TileCopy<C::BN, C::VCH, C::NT> vcopy(tid, (uint32_t)(a.Hkv * DV * 2));
+  const RowReads<C::KCH> krd(lane);
+  const RowReads<C::VCH> vrd(lane);
+  RowBias<C::BN / 32> bias;
+  bias.init(a, bb, hh, qi, hf);  // (b', h') is the matrix of every sharing pair
+  const float c = a.scale_log2;
+  const size_t qstride = (size_t)a.Hq * DQK, ostride = (size_t)a.Hq * DV;
+
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
+    const int j0 = kt * C::BN;
+    f32x16 acc[C::BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < C::BN / 32; ++kb) acc[kb] = f32x16{};
+    bias.load(j0);
+    for (int pb = 0; pb < nb; ++pb) {
+      const int b = a.bias_b == 1 ? pb : bb;
+      const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+      if (tile_class(m, i0, C::BM, j0, C::BN) == TILE_SKIP) continue;  // no row of the block sees it
+      const size_t row0 = seq_row0(a, b);
+      int klo, khi;
+      row_key_bounds(m, qi, klo, khi);
+      for (int ph = 0; ph < nh; ++ph) {
+        const int h = a.bias_h == 1 ? ph : hh;
+        const int g = h / a.G, bh = b * a.Hq + h;
+        // K / V tiles of the pair's KV head; the previous pair's reads are
+        // done (barrier at the end of the pair).
+        kcopy.issue(static_cast<const uint16_t*>(a.k) + (row0 * a.Hkv + g) * DQK, (uint32_t)(a.Hkv * DQK * 2), j0,
+                    m.L, Ks);
+        vcopy.issue(static_cast<const uint16_t*>(a.v) + (row0 * a.Hkv + g) * DV, (uint32_t)(a.Hkv * DV * 2), j0, m.L,
+                    Vs);
+        // Q and dO rows of the pair (rows past the valid length read zeros),
+        // and the rows' LSE * log2(e) and delta.
+        bf16x8 qreg[DQK / 16], oreg[DV / 16];
+        const __amdgpu_buffer_rsrc_t qres =
+            buf_rsrc(static_cast<const uint16_t*>(a.q) + (row0 * a.Hq + h) * DQK, (uint32_t)(m.L * qstride * 2));
+        const __amdgpu_buffer_rsrc_t ores =
+            buf_rsrc(static_cast<const uint16_t*>(a.d_o) + (row0 * a.Hq + h) * DV, (uint32_t)(m.L * ostride * 2));
+#pragma unroll
+        for (int ks = 0; ks < DQK / 16; ++ks)
+          qreg[ks] = as_bf16x8(buf_load16(qres, (uint32_t)(qi * qstride + ks * 16 + hf * 8) * 2));
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks)
+          oreg[ks] = as_bf16x8(buf_load16(ores, (uint32_t)(qi * ostride + ks * 16 + hf * 8) * 2));
+        const size_t row = ((size_t)b * a.Hq + h) * a.S + (qi < a.S ? qi : a.S - 1);
+        const float lse2 = qi < m.L ? a.lse2[row] : 0.0f;
+        const float dl = qi < m.L ? a.delta[row] : 0.0f;
+        uint32_t rnd[C::BN / 32][4];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int kb = 0; kb < C::BN / 32; ++kb) drop_rows_quad(dg, bh, qi, j0 + hf * 4 + kb * 32, rnd[kb]);
+        }
+        lds_dma_wait();
+        __syncthreads();
+        f32x16 st[C::BN / 32], dpt[C::BN / 32];
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb) {
+          st[kb] = f32x16{};
+          dpt[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < DQK / 16; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < C::BN / 32; ++kb)
+            st[kb] = mfma32(as_bf16x8(krd.read(Ks, kb * 32, ks)), qreg[ks], st[kb]);
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < C::BN / 32; ++kb)
+            dpt[kb] = mfma32(as_bf16x8(vrd.read(Vs, kb * 32, ks)), oreg[ks], dpt[kb]);
+        bias.add(st, a.inv_scale);
+        // Element i of block kb: key j0 + kb*32 + acc_row(i, hf), query qi.
+        const int lo_r = klo - (j0 + hf * 4), hi_r = khi - (j0 + hf * 4);
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
+            float pv = fast_exp2(fmaf(st[kb][i], c, -lse2));
+            pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
+            float dpz = dpt[kb][i];
+            if constexpr (DROP) dpz = drop_keep(rnd[kb][i >> 2], i & 3, dg.t) ? dpz * dg.scale : 0.0f;
+            acc[kb][i] += pv * (dpz - dl);
+          }
+        __syncthreads();  // every wave is done with this pair's K / V tiles
+      }
+    }
+    // Write the tile: rows below S, keys below S (four consecutive keys per
+    // group of accumulator elements).
+    if (qi < a.S) {
+      uint16_t* out = static_cast<uint16_t*>(a.d_bias) + (((size_t)bb * a.bias_h + hh) * a.S + qi) * a.S;
+#pragma unroll
+      for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int j = j0 + kb * 32 + gq * 8 + hf * 4;
+          const float v[4] = {acc[kb][4 * gq], acc[kb][4 * gq + 1], acc[kb][4 * gq + 2], acc[kb][4 * gq + 3]};
+          if (j + 3 < a.S) {
+            *reinterpret_cast<u32x2*>(out + j) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < a.S) out[j + e] = (uint16_t)(pack_bf16(v[e], 0.0f) & 0xffffu);
+          }
+        }
+    }
+  }
+}
+
+template __global__ void bwd_dbias_bf16_kernel<64, 64, false>(KArgs);
+template __global__ void bwd_dbias_bf16_kernel<128, 128, false>(KArgs);
+template __global__ void bwd_dbias_bf16_kernel<64, 64, true>(KArgs);
+template __global__ void bwd_dbias_bf16_kernel<128, 128, true>(KArgs);
+
+// Key-tile chunks per (bias matrix, query tile) so that the grid holds about
+// 2048 workgroups (broadcast biases have few matrices, each summing many pairs).
+int dbias_key_chunks(int n_mats, int n_qt, int n_kt) {
+  const long long base = (long long)n_mats * n_qt;
+  long long want = (2048 + base - 1) / base;
+  if (want > n_kt) want = n_kt;
+  return want < 1 ? 1 : (int)want;
+}
+
+template <int DQK, int DV>
+static hipError_t launch_dbias_cfg(KArgs a, hipStream_t stream) {
+  using C = DbiasCfg<DQK, DV>;
+  a.n_tiles = (a.S + C::BM - 1) / C::BM;
+  const int n_kt = (a.S + C::BN - 1) / C::BN;
+  a.n_chunks = dbias_key_chunks(a.bias_b * a.bias_h, a.n_tiles, n_kt);
+  const dim3 grid((unsigned)(a.bias_b * a.bias_h * a.n_tiles * a.n_chunks));
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dbias_bf16_kernel<DQK, DV, true>), grid, dim3(C::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dbias_bf16_kernel<DQK, DV, false>), grid, dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 64 && dv == 64) return launch_dbias_cfg<64, 64>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_dbias_cfg<128, 128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -54,6 +54,12 @@
 // factor is applied once, to dV at the end) and P (Z dP - delta) for dK; the
 // random bytes of a lane's key and one 4-row group come from one generator
 // call, which is exactly one pipeline chunk's share of B.
+//
+// BIAS (additive post-scale attention bias, P = exp(scale q.k + bias - LSE)):
+// each stage also holds the bias tile of its 64 rows x the workgroup's 128
+// keys (swizzled rows, copied with Q and dO).  A lane needs its key's values
+// for the rows of its accumulator elements; one LDS transpose load hands it
+// the four rows of one B chunk, in accumulator order (TrReads).
 #include <type_traits>
 
 #include "dropout.h"
@@ -70,7 +76,7 @@
 
 namespace sdpa {
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool BIAS>
 struct DkdvCfg {
   static constexpr int BN = 128;  // keys per workgroup (32 per wave)
   static constexpr int BMQ = 64;  // query rows per stage (two 32-row blocks)
@@ -78,18 +84,21 @@ struct DkdvCfg {
   static constexpr int NT = 256;
   static constexpr int QCH = DQK / 8, OCH = DV / 8;    // 16-byte chunks per row
   static constexpr int QT = BMQ * DQK, OT = BMQ * DV;  // elements per tile
-  static constexpr int STAGE = QT + OT + 2 * BMQ * 2;  // Q, dO, lse2 and delta (f32)
+  static constexpr int BT = BIAS ? BMQ * BN : 0;       // bias tile [BMQ][BN]
+  static constexpr int STAGE = QT + OT + BT + 2 * BMQ * 2;  // Q, dO, bias, lse2 and delta (f32)
   static constexpr int LDS_ELEMS = NBUF * STAGE;
 };
 
-template <int DQK, int DV, bool DROP>
+template <int DQK, int DV, bool DROP, bool BIAS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
-  using C = DkdvCfg<DQK, DV>;
+  using C = DkdvCfg<DQK, DV, BIAS>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  // Ring slot `buf`: Q [BMQ][DQK], dO [BMQ][DV] (swizzled), lse2 [BMQ], delta [BMQ].
+  // Ring slot `buf`: Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN] (swizzled),
+  // lse2 [BMQ], delta [BMQ].
   auto qtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE; };
   auto otile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::QT; };
-  auto lse_s = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT); };
+  auto btile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::QT + C::OT; };
+  auto lse_s = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT + C::BT); };
   auto delta_s = [&](int buf) __attribute__((always_inline)) { return lse_s(buf) + C::BMQ; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -187,11 +196,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const RowReads<C::OCH> ord(lane);
   const TrReads<C::QCH> qtr(lane);
   const TrReads<C::OCH> otr(lane);
+  const TileCopy<C::BMQ, C::BN / 8, C::NT> bcopy(tid, (uint32_t)a.S * 2);
+  const TrReads<C::BN / 8> btr(lane);
   auto issue_stage = [&](const StageWalk& st, int buf) __attribute__((always_inline)) {
     const int h = g * a.G + hs * Gs + st.hh;
     const int q0 = st.q0;
     qcopy.issue(Qg + (row0 * a.Hq + h) * DQK, (uint32_t)(qstride * 2), q0, m.L, qtile(buf));
     ocopy.issue(dOg + (row0 * a.Hq + h) * DV, (uint32_t)(ostride * 2), q0, m.L, otile(buf));
+    if constexpr (BIAS) {
+      // Bias rows q0 .. q0+63, keys j0 .. j0+127 of head h: the resource ends
+      // where row L starts, so rows past the valid length (and keys past S
+      // on the last valid row) arrive as zeros and nothing past the [S, S]
+      // matrix is read; keys past S on earlier rows read the next row (pairs
+      // the mask hides).
+      const long long left = (long long)(m.L - q0) * a.S - j0;
+      bcopy.issue_bytes(bias_matrix(a, b, h) + (size_t)q0 * a.S + j0, left > 0 ? (uint32_t)(left * 2) : 0u,
+                        btile(buf));
+    }
     // lse2 (wave 0) and delta (wave 1) of rows q0 .. q0+63, one 4-byte copy
     // per lane; rows past S arrive as zeros.
     if (w < 2) {
@@ -222,14 +243,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   auto drop_rows = [&](int bh, int q0, uint32_t(&rnd4)[4]) __attribute__((always_inline)) {
     drop_cols_quad(dg, bh, q0 + hf * 4, kj, rnd4);
   };
-  auto phase_b = [&](const float* ls, const float* dl, int rb, int qrow0, const uint32_t(&rnd4)[4], const f32x16& s,
-                     const f32x16& dp, u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
+  // Bias of rows rb + k*8 + hf*4 + 0..3 (B chunk k of the block at rb) for
+  // this lane's key: the k%2 half of the transpose read at rb + (k/2)*16.
+  auto bias_chunk = [&](const uint16_t* bt, int rb, int k) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* t = reinterpret_cast<const char*>(bt) + (rb + (k >> 1) * 16) * (C::BN / 8) * 16;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + btr.off[k & 1][w])));
+  };
+  // Score of element e of a B chunk with its bias added (unscaled units).
+  auto biased = [&](float sv, const u32x2& bw, int e) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      const uint32_t word = bw[e >> 1];
+      return fmaf((e & 1) ? bf16_hi(word) : bf16_lo(word), a.inv_scale, sv);
+    } else {
+      return sv;
+    }
+  };
+  auto phase_b = [&](const float* ls, const float* dl, const uint16_t* bt, int rb, int qrow0, const uint32_t(&rnd4)[4],
+                     const f32x16& s, const f32x16& dp, u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
     const int lo_r = qlo_k - (qrow0 + hf * 4), hi_r = qhi_k - (qrow0 + hf * 4);
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
       const int qo = rb + ig * 8 + hf * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qo);
+      u32x2 bw = {0u, 0u};
+      if constexpr (BIAS) bw = bias_chunk(bt, rb, ig);
       const uint32_t rnd = rnd4[ig];  // dropout bytes of rows qrow0 + ig*8 + hf*4 + 0..3, key kj
       u32x2 pp, dd;
 #pragma unroll
@@ -239,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         for (int v = 0; v < 2; ++v) {
           const int e = u2 * 2 + v, i = ig * 4 + e;
           const int off = ig * 8 + e;
-          float pv = fast_exp2(fmaf(s[i], c, -l4[e]));
+          float pv = fast_exp2(fmaf(biased(s[i], bw, e), c, -l4[e]));
           pv = (off >= lo_r && off <= hi_r) ? pv : 0.0f;
           float pk = pv, dpz = dp[i];
           if constexpr (DROP) {
@@ -291,6 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // next iteration, read during the last chunk of the current one.
   bf16x8 opa[2][EA], opc[2][EC];
   f32x4 l4[2], d4[2];
+  u32x2 b4[2] = {{0u, 0u}, {0u, 0u}};  // bias of the chunk's four rows (BIAS)
   // Chunk k's LDS reads for the iteration of phase P into set st: A(u+1)'s
   // operands (RA), C(u-1)'s (RC), B(u)'s lse2 / delta (RL).
   auto read_chunk = [&](auto phase, auto kc, auto setc, auto ra, auto rc, auto rl) __attribute__((always_inline)) {
@@ -317,6 +357,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       const int qo = cur * 32 + k * 8 + hf * 4;
       l4[st] = *reinterpret_cast<const f32x4*>(lse_s(slot_u) + qo);
       d4[st] = *reinterpret_cast<const f32x4*>(delta_s(slot_u) + qo);
+      if constexpr (BIAS) b4[st] = bias_chunk(btile(slot_u), cur * 32, k);
     }
   };
   using T0 = std::false_type;
@@ -382,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
           const int e = u2 * 2 + v, i = k * 4 + e;
-          const float pv = fast_exp2(fmaf(S[cur][i], c, -l4[st][e]));
+          const float pv = fast_exp2(fmaf(biased(S[cur][i], b4[st], e), c, -l4[st][e]));
           float pk = pv, dpz = DP[cur][i];
           if constexpr (DROP) {
             const bool kp = drop_keep(rnd, e, dg.t);
@@ -439,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Blocks that some of this wave's (row, key) pairs cannot see (diagonal,
     // window edge, padding): redo B with the mask.
     if (!(q_u >= all_lo && q_u + 31 <= all_hi))
-      phase_b(ls, dl, cur * 32, q_u, rnd_u, S[cur], DP[cur], PW[cur], DW[cur]);
+      phase_b(ls, dl, btile(slot_u), cur * 32, q_u, rnd_u, S[cur], DP[cur], PW[cur], DW[cur]);
   };
 
   if (NB > 0) {
@@ -456,7 +497,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
     uint32_t rnd_0[4] = {0u, 0u, 0u, 0u};
     if constexpr (DROP) drop_rows(b * a.Hq + g * a.G + hs * Gs + b_walk.hh, b_walk.q0, rnd_0);
-    phase_b(lse_s(0), delta_s(0), 0, b_walk.q0, rnd_0, S[0], DP[0], PW[0], DW[0]);
+    phase_b(lse_s(0), delta_s(0), btile(0), 0, b_walk.q0, rnd_0, S[0], DP[0], PW[0], DW[0]);
     read_ahead(std::integral_constant<int, 0>{});  // first chunk of iteration 1
     // Iterations 1 .. NI in trips of six (one per phase), padded past the
     // last block NB-1 with empty blocks: their stages copy rows past the
@@ -547,21 +588,37 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* par
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<192, 128, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, true>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, true>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<192, 128, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false>(KArgs);
+// Bias variants: a stage grows by a 64 x 128 bf16 tile (147 KB of LDS in all
+// at head dim 128; the 192-dim stages would not fit).
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, true>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
-  using D = DkdvCfg<DQK, DV>;
+  using D = DkdvCfg<DQK, DV, false>;
   static_assert(D::BN == kDkdvKeyTile, "split rule uses the kernel's key tile");
   const int nkt = (a.S + D::BN - 1) / D::BN;
   const dim3 grid((unsigned)(nkt * a.B * a.Hkv * a.n_splits));
-  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true>), grid, dim3(D::NT), 0, stream, a);
-  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false>), grid, dim3(D::NT), 0, stream, a);
+  if constexpr (DQK <= 128) {
+    static_assert(DkdvCfg<DQK, DV, true>::LDS_ELEMS * 2 <= 160 * 1024, "bias stages fit the LDS");
+    if (a.bias) {
+      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, true>), grid, dim3(D::NT), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true>), grid, dim3(D::NT), 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.bias) {
+    return hipErrorInvalidValue;  // no bias variant for these head dims
+  }
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, false>), grid, dim3(D::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false>), grid, dim3(D::NT), 0, stream, a);
   return hipGetLastError();
 }
 

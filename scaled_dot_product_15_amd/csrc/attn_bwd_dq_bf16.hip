@@ -19,6 +19,10 @@
 //
 // DROP (attention dropout, dropout.h): with Z = keep / (1 - p),
 // dS = P * (Z dP - delta); delta = rowsum(dO * O) already holds the dropped O.
+//
+// BIAS (additive post-scale attention bias): P = exp(scale q.k + bias - LSE);
+// bias / scale is added to the recomputed scores; each lane loads its row's
+// bias values of a key tile at the start of that tile's step (RowBias).
 #include <type_traits>
 
 #include "dropout.h"
@@ -46,10 +50,11 @@ struct DqCfg {
   static constexpr int LDS_ELEMS = 2 * (KT + VT);
 };
 
-// The dropout variant is held to two workgroups per CU (head dims up to 128)
-// so two waves share each SIMD as in the plain kernel.
-template <int DQK, int DV, bool DROP>
-__global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) void bwd_dq_bf16_kernel(KArgs a) {
+// The dropout and the bias variants are held to two workgroups per CU (head
+// dims up to 128) so two waves share each SIMD as in the plain kernel; with
+// both, the register budget of two does not hold and the bound is one.
+template <int DQK, int DV, bool DROP, bool BIAS>
+__global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) ? 2 : 1) void bwd_dq_bf16_kernel(KArgs a) {
   using C = DqCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
@@ -135,6 +140,8 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) v
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / C::BN, kt1 = hi < 0 ? -1 : hi / C::BN;
+  RowBias<C::BN / 32> bias;
+  if constexpr (BIAS) bias.init(a, b, h, qi, hf);
 
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * DV;
@@ -169,6 +176,9 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) v
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
         st[kb] = mfma32(as_bf16x8(krd.read(Ks, kb * 32, ks)), qreg[ks], st[kb]);
+    // This tile's bias (requested at the start of the step) joins the scores
+    // while the dP products run.
+    if constexpr (BIAS) bias.add(st, a.inv_scale);
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks)
 #pragma unroll
@@ -233,6 +243,9 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) v
   auto step = [&](int kt, auto bufc, auto masked) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int j0 = kt * C::BN;
+    // The bias loads go out before the next tile's copies: the compiler's
+    // wait for them then counts only the copies issued after them.
+    if constexpr (BIAS) bias.load(j0);
     if (kt < kt1) issue_tile(j0 + C::BN, buf ^ 1);
     if constexpr (decltype(masked)::value) {
       if (tile_class(m, qw0, 32, j0, C::BN) != TILE_SKIP) tile(j0, ktile(buf), vtile(buf), std::true_type{});
@@ -276,20 +289,33 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, (DROP && DQK <= 128) ? 2 : 1) v
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void bwd_dq_bf16_kernel<64, 64, false>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<128, 128, false>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<192, 128, false>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<64, 64, true>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<128, 128, true>(KArgs);
-template __global__ void bwd_dq_bf16_kernel<192, 128, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, false, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, false, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<192, 128, false, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, true, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, true, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<192, 128, true, false>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, false, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, false, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<64, 64, true, true>(KArgs);
+template __global__ void bwd_dq_bf16_kernel<128, 128, true, true>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dq_cfg(KArgs a, hipStream_t stream) {
   using Q = DqCfg<DQK, DV>;
   a.n_tiles = (a.S + Q::BM - 1) / Q::BM;
   const dim3 grid((unsigned)(a.n_tiles * a.B * a.Hq));
-  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, true>), grid, dim3(Q::NT), 0, stream, a);
-  else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, false>), grid, dim3(Q::NT), 0, stream, a);
+  if constexpr (DQK <= 128) {
+    if (a.bias) {
+      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, true, true>), grid, dim3(Q::NT), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, false, true>), grid, dim3(Q::NT), 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.bias) {
+    return hipErrorInvalidValue;  // no bias variant for these head dims
+  }
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, true, false>), grid, dim3(Q::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dq_bf16_kernel<DQK, DV, false, false>), grid, dim3(Q::NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,10 @@ struct KArgs {
   int n_tiles;          // tiles along the sequence for this kernel's grid
   int n_chunks;         // dz partial chunks per (b, h)
   int n_splits;         // dK/dV workgroups per (key tile, batch, kv head), each over G / n_splits query heads
+  const void* bias;     // additive post-scale bias [bias_b, bias_h, S, S] (bf16), or nullptr
+  void* d_bias;         // its gradient, same shape, or nullptr
+  int bias_b, bias_h;   // 1 (shared) or B / Hq
+  float inv_scale;      // 1 / scale: the kernels add bias / scale to the unscaled scores
   int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
   float drop_scale;     // 1 / (1 - drop_t / 256)
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;  // generator key and counter word 3
@@ -72,6 +76,13 @@ __device__ __forceinline__ int seq_len(const KArgs& a, int b) {
   const int R = seq_rows(a, b);
   const int L = a.seqlens ? a.seqlens[b] : R;
   return L < 0 ? 0 : (L > R ? R : L);
+}
+
+// The [S, S] bias matrix of batch b, query head h: the [bias_b, bias_h, S, S]
+// tensor with its size-1 dims broadcast.
+__device__ __forceinline__ const uint16_t* bias_matrix(const KArgs& a, int b, int h) {
+  const int bb = a.bias_b == 1 ? 0 : b, hh = a.bias_h == 1 ? 0 : h;
+  return static_cast<const uint16_t*>(a.bias) + ((size_t)bb * a.bias_h + hh) * a.S * a.S;
 }
 
 // Sink logit z_h in natural-log units, or -inf when there is none.
@@ -119,6 +130,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// The two bf16 halves of a 32-bit word as floats (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Bias of one query row for the keys a lane holds in a 32x32 accumulator
+// whose column is that row (forward, dQ: lane = query): element 4g + e of
+// block kb is key j0 + kb*32 + g*8 + hf*4 + e, i.e. four runs of four
+// consecutive keys, one 8-byte load each.  The resource spans the row's
+// [S, S] matrix: keys past the row end read the next row (masked pairs) and
+// nothing past the matrix is read.
+template <int NKB>
+struct RowBias {
+  __amdgpu_buffer_rsrc_t res;
+  uint32_t off;  // byte offset of (row, hf*4)
+  u32x2 w[NKB][4];
+  __device__ __forceinline__ void init(const KArgs& a, int b, int h, int qi, int hf) {
+    res = buf_rsrc(bias_matrix(a, b, h), (uint32_t)((size_t)a.S * a.S * 2));
+    const int row = qi < a.S ? qi : a.S - 1;  // rows past S are masked
+    off = (uint32_t)((size_t)row * a.S + hf * 4) * 2;
+  }
+  __device__ __forceinline__ void load(int j0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) w[kb][g] = buf_load8(res, off + (uint32_t)(j0 + kb * 32 + g * 8) * 2);
+  }
+  // s += bias * inv_scale on element 4g + e of block kb.
+  __device__ __forceinline__ void add(f32x16 (&s)[NKB], float inv_scale) const {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        s[kb][4 * g + 0] = fmaf(bf16_lo(w[kb][g][0]), inv_scale, s[kb][4 * g + 0]);
+        s[kb][4 * g + 1] = fmaf(bf16_hi(w[kb][g][0]), inv_scale, s[kb][4 * g + 1]);
+        s[kb][4 * g + 2] = fmaf(bf16_lo(w[kb][g][1]), inv_scale, s[kb][4 * g + 2]);
+        s[kb][4 * g + 3] = fmaf(bf16_hi(w[kb][g][1]), inv_scale, s[kb][4 * g + 3]);
+      }
+  }
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -277,6 +331,14 @@ struct TileCopy {
       const int row = idx / CH, c = (idx % CH) ^ swz<CH>(row);
       voff[k] = (uint32_t)row * stride_bytes + (uint32_t)c * 16;
     }
+  }
+  // Rows [row0, row0 + R) from a resource of `bytes` starting at row0's
+  // first element: whatever lies past `bytes` arrives as zeros.
+  __device__ __forceinline__ void issue_bytes(const void* row0_base, uint32_t bytes, uint16_t* tile) const {
+    const BufDesc d = buf_desc(row0_base, bytes);
+    const uint32_t dst = lds_addr(tile) + (uint32_t)chunk0 * 16;
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) lds_dma16(d, dst + k * 64 * 16, voff[k]);
   }
   // Rows past valid_rows arrive as zeros.
   __device__ __forceinline__ void issue(const void* base, uint32_t stride_bytes, int row0, int valid_rows,

@@ -36,6 +36,11 @@
 // DROP (attention dropout): the P tile fed to P V keeps a probability only
 // where the pair's random byte passes the threshold (dropout.h); the row sum
 // takes every probability, and O is scaled by 1 / (1 - p) in the epilogue.
+//
+// BIAS (additive post-scale attention bias, s = scale q.k + bias): bias / scale
+// is added to the unscaled scores of each tile before its max; each lane
+// loads its row's 64 bias values of the next tile while the current one
+// computes (RowBias).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -85,7 +90,7 @@ __device__ __forceinline__ void fwd_tile_of(const KArgs& a, int bid, int& b, int
   h = r % a.Hq;
 }
 
-template <int DQK, int DV, int BN, int OCC, bool DROP>
+template <int DQK, int DV, int BN, int OCC, bool DROP, bool BIAS>
 __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
@@ -136,6 +141,8 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / BN, kt1 = hi < 0 ? -1 : hi / BN;
+  RowBias<BN / 32> bias;
+  if constexpr (BIAS) bias.init(a, b, h, qi, hf);
 
   // K / V tiles of buffer `buf`: [BN][DQK] and [BN][DV], swizzled row-major.
   auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
@@ -171,6 +178,10 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
     if (kt + 2 <= kt1) kcopy.issue(Kg, (uint32_t)(kstride * 2), j0 + 2 * BN, m.L, ktile(buf));
     if (kt + 1 <= kt1) vcopy.issue(Vg, (uint32_t)(vstride * 2), j0 + BN, m.L, vtile(buf ^ 1));
     f32x16 (&s)[BN / 32] = sc[buf];
+    if constexpr (BIAS) {
+      bias.add(s, a.inv_scale);            // tile kt's bias, loaded one iteration ago
+      if (kt + 1 <= kt1) bias.load(j0 + BN);  // lands by the barrier closing this iteration
+    }
     float mx = -__builtin_inff();
     if constexpr (MASKED) {
       const int base = j0 + hf * 4;
@@ -273,6 +284,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
     kcopy.issue(Kg, (uint32_t)(kstride * 2), kt0 * BN, m.L, ktile(0));
     vcopy.issue(Vg, (uint32_t)(vstride * 2), kt0 * BN, m.L, vtile(0));
     if (kt0 + 1 <= kt1) kcopy.issue(Kg, (uint32_t)(kstride * 2), (kt0 + 1) * BN, m.L, ktile(1));
+    if constexpr (BIAS) bias.load(kt0 * BN);
     lds_dma_wait();
     __syncthreads();
     prio_mfma();
@@ -328,22 +340,35 @@ constexpr int kFwdOcc192 = 1;
 // The dropout variants are built with a one-workgroup bound so the
 // generator's state can never force spills; at head dims up to 128 they still
 // fit the two-workgroup register budget and run two per CU.
-template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64, false>(KArgs);
-template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128, false>(KArgs);
-template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192, false>(KArgs);
-template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, 1, true>(KArgs);
-template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, 1, true>(KArgs);
-template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, 1, true>(KArgs);
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, kFwdOcc64, false, false>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, kFwdOcc128, false, false>(KArgs);
+template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, kFwdOcc192, false, false>(KArgs);
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, 1, true, false>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, 1, true, false>(KArgs);
+template __global__ void fwd_bf16_kernel<192, 128, SDPA_FWD_BN, 1, true, false>(KArgs);
+// Bias variants (head dims 64 and 128), with the same one-workgroup bound.
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, 1, false, true>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, 1, false, true>(KArgs);
+template __global__ void fwd_bf16_kernel<64, 64, SDPA_FWD_BN, 1, true, true>(KArgs);
+template __global__ void fwd_bf16_kernel<128, 128, SDPA_FWD_BN, 1, true, true>(KArgs);
 
 template <int DQK, int DV, int BN, int OCC>
 static hipError_t launch_fwd_cfg(KArgs a, hipStream_t stream) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
   a.n_tiles = (a.S + C::BM - 1) / C::BM;
   const long long n = (long long)a.B * a.Hq * a.n_tiles;
-  if (a.drop_t > 0)
-    hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, 1, true>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, OCC, false>), dim3((unsigned)n), dim3(C::NT), 0, stream, a);
+  const dim3 grid((unsigned)n), block(C::NT);
+  if constexpr (DQK <= 128) {
+    if (a.bias) {
+      if (a.drop_t > 0) hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, 1, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, 1, false, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.bias) {
+    return hipErrorInvalidValue;  // no bias variant for these head dims
+  }
+  if (a.drop_t > 0) hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, 1, true, false>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, BN, OCC, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -50,5 +50,5 @@ extern "C" int attn_bwd_noalloc(const attn_params* p, const void* q, const void*
   const int e = scratch_ptr(&ws);
   if (e != ATTN_OK) return e;
   return sdpa::bwd_run(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
-                       d_softmax_offset, ws, (size_t)ATTN_NOALLOC_SCRATCH_BYTES, stream);
+                       d_softmax_offset, ws, (size_t)ATTN_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }

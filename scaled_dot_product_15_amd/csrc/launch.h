@@ -37,6 +37,9 @@ int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, 
 // dK / dV = sum over the splits of the partials, in split order (bf16 out).
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// Gradient of the attention bias (needs the pre-pass's delta and LSE * log2 e).
+int dbias_key_chunks(int n_mats, int n_qt, int n_kt);
+hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 
 bool fwd_f32_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
@@ -48,12 +51,20 @@ hipError_t launch_bwd_pre(const KArgs& a, int dtype, int dv, hipStream_t stream)
 // d_softmax_offset[h] = sum over batches and chunks, fixed order.
 hipError_t launch_dz_reduce(const KArgs& a, hipStream_t stream);
 
-// The backward of attn_bwd / attn_bwd_stage (stage 0 = all stages) with the
-// workspace at `workspace`: host checks, then launches on `stream`.
+// Attention bias of attn_bwd_bias: [batch, heads, S, S] and its gradient
+// (d_bias may be NULL).
+struct BiasArgs {
+  const void* bias;
+  void* d_bias;
+  int32_t batch, heads;
+};
+// The backward of attn_bwd / attn_bwd_stage / attn_bwd_bias (stage 0 = all
+// stages; bias only with stage 0, else NULL) with the workspace at
+// `workspace`: host checks, then launches on `stream`.
 int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const void* v, const void* o,
             const void* d_o, const float* lse, const float* softmax_offset, const int32_t* seqlens,
             const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset, void* workspace,
-            size_t workspace_bytes, void* stream);
+            size_t workspace_bytes, void* stream, const BiasArgs* bias);
 
 hipError_t launch_debug_tile_map(const KArgs& a, int bm, int bn, int8_t* out, hipStream_t stream);
 hipError_t launch_debug_mask_probe(const KArgs& a, uint8_t* out, hipStream_t stream);

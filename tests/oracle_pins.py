@@ -907,10 +907,40 @@ def pin_bias_finite_diff(orc):
         _close(r["dbias"], fd, 1e-6, 1e-8, f"dbias finite differences {st}")
 
 
+def pin_bias_sampled(orc):
+    """Row- and key-sampled functions with a bias equal the whole-problem bias
+    oracle (itself pinned against torch SDPA above): O, LSE, dQ and the rows'
+    dS (the bias gradient of a full-shape bias) per row; dK, dV per key."""
+    for ci, (causal, win, sl) in enumerate(MASK_CASES):
+        for st in orc.SOFTMAX_TYPES:
+            q, k, v, do, alpha = rand_case(2700 + ci)
+            for si, (Bb, Hb) in enumerate(BIAS_SHAPES):
+                bias = np.random.default_rng(2750 + 4 * ci + si).standard_normal((Bb, Hb, 9, 9))
+                kw = dict(num_gqa_groups=2, causal=causal, window=win, scale_factor=0.45, softmax_type=st,
+                          softmax_offset=alpha, seqlens=None if sl is None else np.array(sl), bias=bias)
+                full = orc.attention(q, k, v, do, **kw)
+                for b in range(2):
+                    for h in (1, 2):
+                        rows = [0, 4, 8, 2] if ci % 2 else [8, 1, 5]
+                        r = orc.attention_rows(q, k, v, do, b=b, h=h, rows=rows, **kw)
+                        _close(r["o"], full["o"][b, rows, h], 1e-12, 1e-14, f"bias rows O {ci} {st}")
+                        _close(r["lse"], full["lse"][b, h, rows], 1e-12, 1e-14, f"bias rows LSE {ci} {st}")
+                        _close(r["dq"], full["dq"][b, rows, h], 1e-12, 1e-14, f"bias rows dQ {ci} {st}")
+                        if (Bb, Hb) == (2, 4):
+                            ds = np.zeros((len(rows), 9))
+                            ds[:, r["cols"][0]:r["cols"][1]] = r["ds"]
+                            _close(ds, full["dbias"][b, h, rows], 1e-12, 1e-14, f"bias rows dS {ci} {st}")
+                    g = (b + ci) % 2
+                    keys = [7, 0, 3] if ci % 2 else [5, 2]
+                    rk = orc.attention_keys(q, k, v, do, b=b, g=g, keys=keys, row_block=2, **kw)
+                    _close(rk["dk"], full["dk"][b, keys, g], 1e-12, 1e-14, f"bias keys dK {ci} {st}")
+                    _close(rk["dv"], full["dv"][b, keys, g], 1e-12, 1e-14, f"bias keys dV {ci} {st}")
+
+
 ALL_PINS = [pin_brute_force, pin_finite_diff, pin_row_sums, pin_gqa_repeat, pin_causal_rows,
             pin_sink_augmented, pin_sink_closed, pin_dalpha_forms, pin_padding,
             pin_window_limits, pin_scale, pin_torch_sdpa, pin_golden, pin_sampled_rows,
             pin_sampled_keys, pin_packed_brute_force, pin_packed_equals_padded, pin_packed_finite_diff,
             pin_philox_kat, pin_dropout_rate, pin_dropout_brute, pin_dropout_p0, pin_dropout_finite_diff,
             pin_dropout_mean, pin_dropout_layout,
-            pin_dropout_sampled, pin_bias_torch, pin_bias_invariants, pin_bias_finite_diff]
+            pin_dropout_sampled, pin_bias_torch, pin_bias_invariants, pin_bias_finite_diff, pin_bias_sampled]

@@ -305,3 +305,30 @@ def test_noalloc_rejects_before_any_hip_call():
     assert lib.attn_bwd_noalloc(ctypes.byref(small), *bad) == -1
     assert lib.attn_bwd_noalloc(ctypes.byref(P(B=0)), *ptrs) == -1
     assert lib.attn_bwd_noalloc(ctypes.byref(P(d_qk=96, d_v=96)), *ptrs) == -2
+
+
+def test_bias_arguments_checked_before_any_hip_call():
+    """attn_fwd_bias / attn_bwd_bias: a missing or misaligned bias or one
+    whose batch or head count is neither 1 nor the problem's is an invalid
+    argument; fp32, the (192, 128) head dims, S not a multiple of 8 and S above
+    46336 (one bias matrix within 4 GiB) are unsupported.  Nothing is launched
+    (the pointers are never read)."""
+    lib = binding.load_library()
+    f = ctypes.c_void_p(256)
+
+    def fwd(p, bias, bb, bh):
+        return lib.attn_fwd_bias(ctypes.byref(p), f, f, f, bias, bb, bh, None, None, None, f, f, None, 0, None)
+
+    def bwd(p, bias, bb, bh):
+        return lib.attn_bwd_bias(ctypes.byref(p), f, f, f, f, f, f, bias, bb, bh, None, None, None, None,
+                                 f, f, f, None, f, 1 << 30, None)
+
+    for call in (fwd, bwd):
+        assert call(P(), None, 1, 1) == -1
+        assert call(P(B=2), f, 3, 1) == -1
+        assert call(P(Hq=8), f, 1, 2) == -1
+        assert call(P(d_qk=192, d_v=128), f, 1, 1) == -2
+        assert call(P(dtype="f32", d_qk=64, d_v=64), f, 1, 1) == -2
+        assert call(P(S=50000, B=1, Hq=2, Hkv=1), f, 1, 1) == -2
+        assert call(P(S=100), f, 1, 1) == -2                 # S not a multiple of 8
+        assert call(P(), ctypes.c_void_p(264), 1, 1) == -1   # bias not 16-byte aligned

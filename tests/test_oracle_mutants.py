@@ -58,6 +58,9 @@ MUTANTS = {
     "rows_dropout_dp_unmasked": [("ds = p * (zmat * (doh @ vb.T) - delta[:, None])",
                                   "ds = p * (doh @ vb.T - delta[:, None])")],
     "keys_dropout_dv_unmasked": [("dvv += (p * zmat).T @ doh", "dvv += p.T @ doh")],
+    "rows_bias_transposed": [("bias[_bias_index(bias, b, h)][rows][:, c0:c1]", "bias[_bias_index(bias, b, h)].T[rows][:, c0:c1]")],
+    "keys_bias_wrong_head": [("s = s + np.asarray(bias[_bias_index(bias, b, h)][rows][:, keys], dtype=np.float64)",
+                              "s = s + np.asarray(bias[_bias_index(bias, b, g)][rows][:, keys], dtype=np.float64)")],
     "bias_pre_scale": [("            s = s + np.asarray(bias[_bias_index(bias, b, h)], dtype=np.float64)",
                         "            s = s + scale * np.asarray(bias[_bias_index(bias, b, h)], dtype=np.float64)")],
     "bias_transposed": [("            s = s + np.asarray(bias[_bias_index(bias, b, h)], dtype=np.float64)",
@@ -79,7 +82,8 @@ ORDER = [oracle_pins.pin_golden, oracle_pins.pin_brute_force, oracle_pins.pin_ca
          oracle_pins.pin_philox_kat, oracle_pins.pin_dropout_rate, oracle_pins.pin_dropout_p0,
          oracle_pins.pin_dropout_brute, oracle_pins.pin_dropout_finite_diff, oracle_pins.pin_dropout_mean,
          oracle_pins.pin_dropout_layout, oracle_pins.pin_dropout_sampled,
-         oracle_pins.pin_bias_invariants, oracle_pins.pin_bias_torch, oracle_pins.pin_bias_finite_diff]
+         oracle_pins.pin_bias_invariants, oracle_pins.pin_bias_torch, oracle_pins.pin_bias_finite_diff,
+         oracle_pins.pin_bias_sampled]
 
 
 def _mutant(edits):
