@@ -1,0 +1,154 @@
+"""Float64 CPU oracle for FP8 attention (forward) and FP8 per-tensor scaling.
+
+TEST INFRASTRUCTURE ONLY, like sdpa_oracle: only the test suite, the smoke
+entry point and the benchmark's CPU-baseline leg may import it.  It shares no
+code with the HIP path.
+
+The codelab "Speed up attention on GPU with cuDNN and TransformerEngine",
+section 10, runs attention under FP8 autocast with a DelayedScaling recipe:
+HYBRID format (E4M3 for forward tensors, E5M2 for backward ones), an amax
+history of 1024 steps and the "max" rule over that history.  The page shows
+neither the formats' bit layouts nor the attention arithmetic under FP8, so
+this module takes these readings (each also listed in the design notes):
+
+  * formats: the two 8-bit formats of the OCP 8-bit floating point
+    specification (OFP8): E4M3 (bias 7, no infinities, one NaN pattern per
+    sign, largest finite 448) and E5M2 (bias 15, IEEE-like infinities and
+    NaNs, largest finite 57344), both with subnormals.
+  * rounding: a real value is encoded by round-to-nearest, ties to the even
+    code; magnitudes beyond the largest finite value saturate to it
+    (NaN stays NaN).
+  * per-tensor scaling: a tensor x is stored as codes encode(x * scale) with a
+    float32 scale; its real value is decode(code) * descale, descale = 1/scale.
+  * delayed scaling: each step's amax = max |x| enters an amax history of a
+    fixed length (newest first); the next scale is fmt_max / max(history) /
+    2^margin while that max is positive and finite, else the old scale.
+  * FP8 attention forward: Q, K, V are E4M3 codes with descales; scores
+    s = scale * (dq Q8) . (dk K8); row max m_i and sum l_i of exp(s - m_i)
+    over visible keys (plus the sink) as in sdpa_oracle; the probabilities
+    relative to the row max are quantized to E4M3 as P8 = encode(256 exp(s -
+    m_i)) (every value at most 256, below the E4M3 maximum; 256 a power of
+    two, so the scaling adds no rounding); O_i = dv / (256 l_i) * sum_j P8_ij
+    V8_j, LSE_i = m_i + ln l_i.  The normalisation uses the unquantized sum,
+    so O is not exactly a convex combination: the quantization of P is part
+    of the definition.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .sdpa_oracle import kv_head, sink_logit, visible_mask
+
+E4M3, E5M2 = "e4m3", "e5m2"
+# (exponent bits, mantissa bits, exponent bias)
+_FORMATS = {E4M3: (4, 3, 7), E5M2: (5, 2, 15)}
+
+
+def fp8_decode(codes, fmt: str) -> np.ndarray:
+    """Real value of each 8-bit code (float64), from the bit layout:
+    sign | exponent | mantissa; exponent 0 = subnormal m * 2^(1 - bias - M).
+    E4M3: exponent and mantissa all ones is NaN (no infinities).  E5M2:
+    exponent all ones is infinity (mantissa 0) or NaN."""
+    eb, mb, bias = _FORMATS[fmt]
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> mb) & ((1 << eb) - 1)
+    m = c & ((1 << mb) - 1)
+    frac = m / float(1 << mb)
+    val = np.where(e == 0, frac * 2.0 ** (1 - bias), (1.0 + frac) * 2.0 ** (e - bias))
+    emax = (1 << eb) - 1
+    if fmt == E4M3:
+        val = np.where((e == emax) & (m == (1 << mb) - 1), np.nan, val)
+    else:
+        val = np.where(e == emax, np.where(m == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def fp8_max(fmt: str) -> float:
+    """Largest finite value of the format."""
+    return {E4M3: 448.0, E5M2: 57344.0}[fmt]
+
+
+def _positive_table(fmt: str):
+    codes = np.arange(128)
+    vals = fp8_decode(codes, fmt)
+    ok = np.isfinite(vals)
+    return codes[ok], vals[ok]  # ascending, 0 first
+
+
+def fp8_encode(x, fmt: str) -> np.ndarray:
+    """uint8 codes of x: saturating round-to-nearest, ties to the even code."""
+    x = np.asarray(x, dtype=np.float64)
+    codes, vals = _positive_table(fmt)
+    a = np.minimum(np.abs(x), fp8_max(fmt))
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    out = np.where(pick_hi, codes[hi], codes[lo])
+    out = np.where(a == vals[hi], codes[hi], out)
+    out = out | np.where(np.signbit(x), 0x80, 0)
+    out = np.where(np.isnan(x), 0x7F, out)  # a NaN code of either format
+    return out.astype(np.uint8)
+
+
+def quantize(x, scale: float, fmt: str):
+    """Per-tensor quantization: (codes of x * scale, amax = max |x|)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    return fp8_encode(x * float(scale), fmt), amax
+
+
+def delayed_scaling_update(history, new_amax: float, scale: float, fmt: str, margin: int = 0):
+    """One step of the delayed-scaling recipe: the new amax enters the history
+    (newest first, oldest dropped); the next scale is fmt_max / max(history) /
+    2^margin when that max is positive and finite, else the old scale.
+    Returns (history, scale, descale)."""
+    h = np.concatenate([[float(new_amax)], np.asarray(history, dtype=np.float64)[:-1]])
+    amax = float(h.max())
+    if amax > 0.0 and math.isfinite(amax):
+        scale = fp8_max(fmt) / amax / (2.0 ** margin)
+    return h, float(scale), 1.0 / float(scale)
+
+
+def attention_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, *, num_gqa_groups=None,
+                  causal=True, window=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
+                  seqlens=None):
+    """FP8 attention forward (readings above).  q8 [B,S,Hq,Dqk], k8 [B,S,Hkv,Dqk],
+    v8 [B,S,Hkv,Dv]: E4M3 codes (uint8).  Returns o [B,S,Hq,Dv], lse [B,Hq,S]
+    (natural log) and p8 (the quantized probability codes, [B,Hq,S,S])."""
+    q8, k8, v8 = (np.asarray(x, dtype=np.uint8) for x in (q8, k8, v8))
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    dv = v8.shape[3]
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    q = fp8_decode(q8, E4M3) * float(descale_q)
+    k = fp8_decode(k8, E4M3) * float(descale_k)
+    v = fp8_decode(v8, E4M3) * float(descale_v)
+    o = np.zeros((B, S, Hq, dv))
+    lse = np.zeros((B, Hq, S))
+    p8 = np.zeros((B, Hq, S, S), dtype=np.uint8)
+    for b in range(B):
+        L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+        mask = visible_mask(S, L, causal, int(window[0]), int(window[1]))
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            s = scale * (q[b, :, h, :] @ k[b, :, g, :].T)
+            z = sink_logit(softmax_type, softmax_offset, h)
+            neg = np.where(mask, s, -np.inf)
+            m = neg.max(axis=1)
+            if z is not None:
+                m = np.maximum(m, z)
+            m_safe = np.where(np.isfinite(m), m, 0.0)
+            e = np.where(mask, np.exp(neg - m_safe[:, None]), 0.0)
+            l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - m_safe))
+            with np.errstate(divide="ignore"):
+                lse[b, h] = np.where(l > 0, m_safe + np.log(l), -np.inf)
+            codes = np.where(mask, fp8_encode(256.0 * e, E4M3), 0).astype(np.uint8)
+            p8[b, h] = codes
+            pq = fp8_decode(codes, E4M3) / 256.0
+            with np.errstate(invalid="ignore", divide="ignore"):
+                o[b, :, h, :] = np.where(l[:, None] > 0, (pq @ v[b, :, g, :]) / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return {"o": o, "lse": lse, "p8": p8}

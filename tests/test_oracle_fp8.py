@@ -1,0 +1,197 @@
+"""Pins of the FP8 oracle (oracle/fp8.py), on the CPU.
+
+  codec       every code decodes as torch's float8_e4m3fn / float8_e5m2 (a
+              library implementation of the OFP8 formats); encoding equals
+              torch's round-to-nearest-even cast on in-range values, exact ties
+              included; saturation and NaN by definition; encode(decode(c)) = c
+  recipe      delayed scaling on hand-worked histories
+  attention   LSE equals the unquantized oracle's; O lies within the bound the
+              E4M3 rounding of P allows around the unquantized oracle's O;
+              scalar loops over a tiny case reproduce O and the P codes
+  mutants     planted mistakes in copies of the module each fail a pin
+"""
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fp8.py")
+TDT = {fp8.E4M3: torch.float8_e4m3fn, fp8.E5M2: torch.float8_e5m2}
+
+
+def _torch_codes(x, fmt):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(TDT[fmt]).view(torch.uint8).numpy()
+
+
+def pin_decode(m):
+    for fmt in (m.E4M3, m.E5M2):
+        codes = np.arange(256, dtype=np.uint8)
+        ref = torch.tensor(codes).view(TDT[fmt]).to(torch.float64).numpy()
+        got = m.fp8_decode(codes, fmt)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), fmt
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok], ref[ok]), fmt
+        assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok])), fmt
+
+
+def pin_encode(m):
+    rng = np.random.default_rng(5)
+    for fmt in (m.E4M3, m.E5M2):
+        mx = m.fp8_max(fmt)
+        vals = np.sort(np.unique(np.abs(m.fp8_decode(np.arange(128), fmt)[:-1 if fmt == m.E4M3 else 124])))
+        vals = vals[np.isfinite(vals)]
+        mids = (vals[1:] + vals[:-1]) / 2  # exact ties
+        x = np.concatenate([rng.uniform(-mx, mx, 4000), rng.standard_normal(4000) * 0.05,
+                            rng.standard_normal(2000) * 1e-3, mids, -mids, vals, -vals])
+        x = x.astype(np.float32).astype(np.float64)  # values torch sees exactly
+        got = m.fp8_encode(x, fmt)
+        ref = _torch_codes(x, fmt)
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, (fmt, x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def pin_saturation_and_nan(m):
+    for fmt, top in ((m.E4M3, 0x7E), (m.E5M2, 0x7B)):
+        mx = m.fp8_max(fmt)
+        assert m.fp8_decode([top], fmt)[0] == mx
+        big = np.array([mx * 1.01, mx * 4, 1e30, np.inf])
+        assert (m.fp8_encode(big, fmt) == top).all(), fmt
+        assert (m.fp8_encode(-big, fmt) == (top | 0x80)).all(), fmt
+        assert np.isnan(m.fp8_decode(m.fp8_encode([np.nan], fmt), fmt)[0])
+        finite = np.nonzero(np.isfinite(m.fp8_decode(np.arange(256), fmt)))[0]
+        assert np.array_equal(m.fp8_encode(m.fp8_decode(finite, fmt), fmt), finite.astype(np.uint8)), fmt
+
+
+def pin_recipe(m):
+    h = np.array([3.0, 9.0, 2.0, 0.0])
+    h2, s, d = m.delayed_scaling_update(h, 5.0, 1.0, m.E4M3)
+    assert np.array_equal(h2, [5.0, 3.0, 9.0, 2.0])       # newest first, oldest dropped
+    assert s == 448.0 / 9.0 and d == 1.0 / s
+    _, s, _ = m.delayed_scaling_update(h, 5.0, 1.0, m.E5M2, margin=2)
+    assert s == 57344.0 / 9.0 / 4.0
+    _, s, _ = m.delayed_scaling_update(np.zeros(4), 0.0, 0.75, m.E4M3)
+    assert s == 0.75                                       # no amax yet: keep the scale
+    _, s, _ = m.delayed_scaling_update(np.zeros(4), np.inf, 0.5, m.E4M3)
+    assert s == 0.5
+    codes, amax = m.quantize(np.array([0.5, -3.0, 2.0]), 2.0, m.E4M3)
+    assert amax == 3.0 and list(m.fp8_decode(codes, m.E4M3)) == [1.0, -6.0, 4.0]
+
+
+def _case(seed, B=2, S=11, Hq=4, Hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    q8 = fp8.fp8_encode(rng.standard_normal((B, S, Hq, d)) * 8, fp8.E4M3)
+    k8 = fp8.fp8_encode(rng.standard_normal((B, S, Hkv, d)) * 8, fp8.E4M3)
+    v8 = fp8.fp8_encode(rng.standard_normal((B, S, Hkv, d)) * 8, fp8.E4M3)
+    alpha = rng.standard_normal(Hq)
+    return q8, k8, v8, alpha
+
+
+MASKS = [(True, (-1, -1), None), (True, (3, 0), [11, 6]), (False, (2, 4), [0, 9]), (False, (-1, -1), None)]
+
+
+def pin_attention_bound(m):
+    """LSE is the unquantized oracle's; |O - O_exact| per element stays within
+    sum_j max(2^-4 e_ij, 2^-18) |v_j| / l_i, the E4M3 rounding of 256 e_ij
+    (half a unit in the last place: 2^-4 relative for normals, 2^-10 / 256
+    absolute for subnormals) carried through O = sum_j e_ij v_j / l_i."""
+    dq, dk, dv = 0.125, 0.25, 0.0625
+    for ci, (causal, win, sl) in enumerate(MASKS):
+        for st in oracle.SOFTMAX_TYPES:
+            q8, k8, v8, alpha = _case(3100 + ci)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, softmax_type=st, softmax_offset=alpha,
+                      seqlens=None if sl is None else np.array(sl))
+            r = m.attention_fp8(q8, k8, v8, dq, dk, dv, **kw)
+            q, k, v = (m.fp8_decode(x, m.E4M3) * s for x, s in ((q8, dq), (k8, dk), (v8, dv)))
+            ex = oracle.attention(q, k, v, None, **kw)
+            fin = np.isfinite(ex["lse"])
+            assert np.array_equal(np.isfinite(r["lse"]), fin)
+            assert np.abs(r["lse"][fin] - ex["lse"][fin]).max() <= 1e-12
+            B, S, Hq = q8.shape[:3]
+            for b in range(B):
+                L = S if sl is None else sl[b]
+                mask = oracle.visible_mask(S, L, causal, win[0], win[1])
+                for h in range(Hq):
+                    g = h // 2
+                    s = (q[b, :, h] @ k[b, :, g].T) / math.sqrt(q.shape[3])
+                    z = oracle.sink_logit(st, alpha, h)
+                    mrow = np.where(mask, s, -np.inf).max(axis=1)
+                    if z is not None:
+                        mrow = np.maximum(mrow, z)
+                    mrow = np.where(np.isfinite(mrow), mrow, 0.0)
+                    e = np.where(mask, np.exp(s - mrow[:, None]), 0.0)
+                    l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - mrow))
+                    bound = (np.maximum(2.0 ** -4 * e, 2.0 ** -18) * mask) @ np.abs(v[b, :, g])
+                    bound = np.where(l[:, None] > 0, bound / np.where(l > 0, l, 1)[:, None], 0.0)
+                    err = np.abs(r["o"][b, :, h] - ex["o"][b, :, h])
+                    assert (err <= bound * (1 + 1e-9) + 1e-15).all(), (ci, st, b, h, float((err - bound).max()))
+
+
+def pin_attention_loops(m):
+    """Scalar loops on a tiny case: scores, row max, sum, each P code and O."""
+    q8, k8, v8, alpha = _case(3200, B=1, S=5, Hq=2, Hkv=1, d=4)
+    dq, dk, dv = 0.5, 0.25, 2.0
+    r = m.attention_fp8(q8, k8, v8, dq, dk, dv, num_gqa_groups=1, causal=True, softmax_type="off_by_one")
+    S, scale = 5, 0.5  # 1/sqrt(4)
+    for h in range(2):
+        for i in range(S):
+            s = [scale * sum(float(m.fp8_decode([q8[0, i, h, d]], m.E4M3)[0]) * dq *
+                             float(m.fp8_decode([k8[0, j, 0, d]], m.E4M3)[0]) * dk for d in range(4))
+                 for j in range(i + 1)]
+            mx = max(max(s), 0.0)
+            l = sum(math.exp(x - mx) for x in s) + math.exp(0.0 - mx)
+            assert abs(r["lse"][0, h, i] - (mx + math.log(l))) <= 1e-12
+            for d in range(4):
+                acc = 0.0
+                for j in range(i + 1):
+                    c = int(m.fp8_encode([256.0 * math.exp(s[j] - mx)], m.E4M3)[0])
+                    assert c == r["p8"][0, h, i, j]
+                    acc += float(m.fp8_decode([c], m.E4M3)[0]) / 256.0 * float(
+                        m.fp8_decode([v8[0, j, 0, d]], m.E4M3)[0]) * dv
+                assert abs(r["o"][0, i, h, d] - acc / l) <= 1e-12 * (1 + abs(acc / l))
+
+
+PINS = [pin_decode, pin_encode, pin_saturation_and_nan, pin_recipe, pin_attention_bound, pin_attention_loops]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_fp8_pin(pin):
+    pin(fp8)
+
+
+MUTANTS = {
+    "e4m3_bias_8": ("E4M3: (4, 3, 7)", "E4M3: (4, 3, 8)"),
+    "ties_to_odd": ("(codes[hi] % 2 == 0)", "(codes[hi] % 2 == 1)"),
+    "overflow_to_nan": ("out = np.where(np.isnan(x), 0x7F, out)",
+                        "out = np.where(np.isnan(x) | (np.abs(x) > fp8_max(fmt)), 0x7F, out)"),
+    "e5m2_inf_as_nan": ("val = np.where(e == emax, np.where(m == 0, np.inf, np.nan), val)",
+                        "val = np.where(e == emax, np.nan, val)"),
+    "p_scale_448": ("codes = np.where(mask, fp8_encode(256.0 * e, E4M3), 0).astype(np.uint8)",
+                    "codes = np.where(mask, fp8_encode(448.0 * e, E4M3), 0).astype(np.uint8)"),
+    "v_descale_dropped": ("v = fp8_decode(v8, E4M3) * float(descale_v)", "v = fp8_decode(v8, E4M3)"),
+    "history_oldest_first": ("h = np.concatenate([[float(new_amax)], np.asarray(history, dtype=np.float64)[:-1]])",
+                             "h = np.concatenate([np.asarray(history, dtype=np.float64)[1:], [float(new_amax)]])"),
+    "margin_ignored": ("scale = fp8_max(fmt) / amax / (2.0 ** margin)", "scale = fp8_max(fmt) / amax"),
+    "sink_missing_in_sum": ("l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - m_safe))", "l = e.sum(axis=1)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_fp8_mutant_is_caught(name):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("fp8_mutant")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), "fp8_mutant.py", "exec"), mod.__dict__)
+    for pin in PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            return
+    pytest.fail(f"mutant {name} passed every pin")
