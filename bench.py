@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_F32_VALU_TFLOPS = 157.3
 METRIC = "fwd+bwd effective TFLOP/s (bf16 GQA+SWA, S=4096) and % of MFMA bf16 peak"
 
@@ -137,6 +138,119 @@ def cpu_baseline(p, arr, groups):
                       f"{groups * (p.Hq // p.Hkv)} query heads x S={p.S}, fwd+bwd, numpy float64"}
 
 
+def cpu_baseline_fp8(p, q8, k8, v8, descales, offsets, heads):
+    """Time the float64 FP8 oracle on every row of `heads` (batch, query head)
+    pairs of the workload."""
+    from oracle import fp8
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = list(range(p.S))
+    heads = min(heads, p.B * p.Hq)
+    t0 = time.perf_counter()
+    for n in range(heads):
+        fp8.attention_fp8_rows(q8, k8, v8, *descales, b=n // p.Hq, h=n % p.Hq, rows=rows, num_gqa_groups=p.Hkv,
+                               causal=p.causal, window=p.window, scale_factor=p.scale_factor or None,
+                               softmax_type=p.softmax_type, softmax_offset=offsets)
+    dt = time.perf_counter() - t0
+    pairs = visible_pairs(p.S, p.S, p.causal, p.window[0], p.window[1]) * heads
+    return {"value": effective_flops(pairs, p.d_qk, p.d_v)[0] / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{heads} of {p.B * p.Hq} (batch, query head) pairs of the workload, all {p.S} rows each, "
+                      f"FP8 forward, numpy float64"}
+
+
+def bench_fp8(args, p, arr, t, seed, dev, packed):
+    """FP8 forward line: Q, K, V quantized to E4M3 on the device (one delayed-
+    scaling step sets the scales from their amax), then attn_fwd_fp8 timed
+    with those codes resident in HBM.  Effective FLOPs as the forward's:
+    2 * pairs * (d_qk + d_v)."""
+    import numpy as np
+    import torch
+    from scaled_dot_product_15_amd import binding
+    if p.d_qk != p.d_v or p.d_qk not in (64, 128) or args.dropout or args.bias != "none" or packed:
+        print("the FP8 forward line runs head dims 64/128, bshd, without dropout or bias", file=sys.stderr)
+        sys.exit(2)
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask", window_size=p.window,
+              scale_factor=p.scale_factor or None, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
+              seqlens=t["seqlens"])
+    codes, descale, scales = [], [], []
+    for name in ("q", "k", "v"):
+        hist = torch.zeros(1024, dtype=torch.float32, device="cuda")
+        scale = torch.ones(1, dtype=torch.float32, device="cuda")
+        dsc = torch.ones(1, dtype=torch.float32, device="cuda")
+        _, amax = binding.fp8_quantize(t[name], scale, "e4m3")
+        binding.fp8_update_scale(hist, amax, scale, dsc, "e4m3", margin=0)
+        c, _ = binding.fp8_quantize(t[name], scale, "e4m3")
+        codes.append(c)
+        descale.append(dsc)
+        scales.append(scale)
+    desc = torch.cat(descale)
+    o, lse = binding.attn_fwd_fp8(*codes, desc, **kw)
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, "fp8", kw["attn_mask_type"], p.window,
+                             kw["scale_factor"], p.softmax_type)
+    ws = torch.empty(max(binding.attn_fwd_workspace_size(pp), 1), dtype=torch.uint8, device="cuda")
+    fast = dict(kw, check_seqlens=False, out=o, lse=lse, workspace=ws)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.attn_fwd_fp8(*codes, desc, **fast)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    qev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    qev[0].record(stream)
+    for name, c, sc in zip(("q", "k", "v"), codes, scales):
+        binding.fp8_quantize(t[name], sc, "e4m3", out=c)  # same scales: the codes are unchanged
+    qev[1].record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    avg = statistics.fmean(call_ms)
+    seq = arr["seqlens"]
+    pairs = workload_pairs(p, seq)
+    f_fwd = effective_flops(pairs, p.d_qk, p.d_v)[0]
+    ms = elapsed / args.steps * 1e3
+    value = f_fwd / (ms * 1e-3) / 1e12
+    achieved = f_fwd / (avg * 1e-3) / 1e12
+    res = {
+        "metric": "fwd effective TFLOP/s (FP8 E4M3 GQA+SWA, S=4096) and % of MFMA fp8 peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": p.name, "batch": p.B, "seq_len": p.S, "num_heads": p.Hq, "num_gqa_groups": p.Hkv,
+                   "head_dim_qk": p.d_qk, "head_dim_v": p.d_v, "mask": "causal" if p.causal else "none",
+                   "window": list(p.window), "softmax_type": p.softmax_type, "seed": seed, "fp8": "e4m3",
+                   "seqlens": None if seq is None else [int(x) for x in seq], "tokens": p.B * p.S},
+        "pct_of_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "pairs": pairs, "gflop_fwd": round(f_fwd / 1e9, 3),
+        "t_quantize_qkv_ms": round(qev[0].elapsed_time(qev[1]), 4),
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": f_fwd, "avg_launch_ms": round(avg, 4),
+                     "note": "avg_launch_ms brackets the call: the V transpose kernel and the forward kernel"},
+        "device": {"name": dev.name, "compute_units": dev.multi_processor_count,
+                   "gcn_arch": getattr(dev, "gcnArchName", "")},
+    }
+    if not args.no_cpu_baseline:
+        qc, kc, vc = (c.cpu().numpy() for c in codes)
+        res["cpu_baseline"] = cpu_baseline_fp8(p, qc, kc, vc, [float(x) for x in desc.cpu()],
+                                               arr["alpha"].astype(np.float64), args.cpu_groups // 3 or 1)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +265,12 @@ def main():
                          "(seq_offsets), no padding tokens stored")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="attention dropout rate (Philox keep mask regenerated in forward and backward)")
+    ap.add_argument("--bias", choices=("none", "full", "heads", "batch", "shared"), default="none",
+                    help="additive post-scale attention bias [B|1, Hq|1, S, S] (bf16, N(0,1)) in forward and "
+                         "backward, with its gradient")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 (E4M3) forward instead: Q, K, V quantized on the device with "
+                         "delayed-scaling scales, then attn_fwd_fp8")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) to "
                          "calibrate the HBM byte counters, then exit")
@@ -188,6 +308,8 @@ def main():
         t["seqlens"] = None  # every segment is exactly its valid tokens
     else:
         t = inputs.to_torch(arr, p.dtype, "cuda")
+    if args.fp8:
+        return bench_fp8(args, p, arr, t, seed, dev, packed)
 
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
               window_size=p.window, scale_factor=p.scale_factor or None,
@@ -196,9 +318,19 @@ def main():
         kw.update(seq_offsets=t["seq_offsets"], max_seqlen=p.S)
     if args.dropout:
         kw.update(dropout_p=args.dropout, rng_state=(seed, 0))
+    bias_kw = {}
+    if args.bias != "none":
+        per_b, per_h = {"full": (1, 1), "heads": (0, 1), "batch": (1, 0), "shared": (0, 0)}[args.bias]
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        bias = torch.randn((p.B if per_b else 1, p.Hq if per_h else 1, p.S, p.S), generator=gen, device="cuda",
+                           dtype=torch.float32).to(torch.bfloat16)
+        kw.update(bias=bias)
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     want = p.softmax_type != "vanilla"
-    dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
+    res = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
+    dq, dk, dv, doff = res[:4]
+    if args.bias != "none":
+        bias_kw = dict(d_bias=res[4])
     outs = (dq, dk, dv, doff)
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"],
                              p.window, kw["scale_factor"], p.softmax_type, args.dropout)
@@ -210,12 +342,14 @@ def main():
     # runs only when a softmax-offset gradient is requested.
     stages = [(s, n) for s, n in ((1, "bwd_pre"), (2, "bwd_dq"), (3, "bwd_dkdv"), (4, "bwd_offset"))
               if not (s == 1 and p.dtype == "bf16") and not (s == 4 and not want)]
+    if args.bias != "none":
+        stages = [(0, "bwd")]  # the biased backward runs as one call (dQ, dK/dV, dBias)
     names = ["fwd"] + [n for _, n in stages]
 
     def step():
         binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
         binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
-                         outs=outs, **fast)
+                         outs=outs, **fast, **bias_kw)
 
     def staged_step(ev):
         """The same work with HIP events between the kernels (per-kernel times)."""
@@ -224,7 +358,7 @@ def main():
         for i, (s, _) in enumerate(stages):
             ev[i + 1].record(stream)
             binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
-                             outs=outs, stage=s, **fast)
+                             outs=outs, stage=s, **fast, **bias_kw)
         ev[len(stages) + 1].record(stream)
 
     for _ in range(args.warmup):
@@ -239,7 +373,7 @@ def main():
         binding.attn_fwd(t["q"], t["k"], t["v"], out=o, lse=lse, **fast)
         ev[1].record(stream)
         binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws,
-                         outs=outs, **fast)
+                         outs=outs, **fast, **bias_kw)
         ev[2].record(stream)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -268,12 +402,15 @@ def main():
     t_bwd = statistics.median(ev[1].elapsed_time(ev[2]) for ev in split)
 
     kflops = kernel_flops_per_pair(p.d_qk, p.d_v)
-    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg_ms[n])
+    # With a bias the backward is timed as one call; the roofline then covers
+    # the forward, the one kernel its events bracket alone.
+    dominant = max((n for n in ("fwd", "bwd_dkdv", "bwd_dq") if n in avg_ms), key=lambda n: avg_ms[n])
     achieved = kflops[dominant] * pairs / (avg_ms[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (measured_traffic(args.config, dominant)
-                            if args.case == 0 and not packed and not args.dropout else None),
+                            if args.case == 0 and not packed and not args.dropout and args.bias == "none"
+                            else None),
                 "flops_per_launch": kflops[dominant] * pairs, "avg_launch_ms": round(avg_ms[dominant], 4)}
 
     res = {
@@ -293,7 +430,8 @@ def main():
                    "num_gqa_groups": p.Hkv, "head_dim_qk": p.d_qk, "head_dim_v": p.d_v,
                    "mask": "causal" if p.causal else "none", "window": list(p.window),
                    "softmax_type": p.softmax_type, "seed": seed,
-                   "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout, "dropout": args.dropout,
+                   "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout,
+                   "dropout": args.dropout, "bias": args.bias,
                    "tokens": int(t["q"].shape[0]) if packed else p.B * p.S},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "pairs": pairs,

@@ -79,6 +79,10 @@ extern "C" {
 /* params.dtype */
 #define ATTN_F32 0
 #define ATTN_BF16 1
+#define ATTN_FP8 2  /* attn_fwd_fp8 only: E4M3 Q, K, V with descales; O is bf16 */
+/* 8-bit formats (OCP 8-bit floating point spec) */
+#define ATTN_FP8_E4M3 0
+#define ATTN_FP8_E5M2 1
 /* params.mask_type (codelab section 7; TE single-GPU page section 2) */
 #define ATTN_MASK_NONE 0
 #define ATTN_MASK_CAUSAL 1
@@ -104,7 +108,7 @@ struct attn_params {
   int32_t num_gqa_groups; /* Hkv >= 1, number of K/V heads; Hq % Hkv == 0 */
   int32_t head_dim_qk;    /* Dqk */
   int32_t head_dim_v;     /* Dv */
-  int32_t dtype;          /* ATTN_F32 | ATTN_BF16 */
+  int32_t dtype;          /* ATTN_F32 | ATTN_BF16 | ATTN_FP8 (attn_fwd_fp8) */
   int32_t mask_type;      /* ATTN_MASK_NONE | ATTN_MASK_CAUSAL */
   int32_t window_left;    /* >= -1; -1 = unbounded */
   int32_t window_right;   /* >= -1; -1 = unbounded */
@@ -244,6 +248,49 @@ int attn_bwd_noalloc(const struct attn_params* p, const void* q, const void* k, 
                      const void* o, const void* d_o, const float* lse, const float* softmax_offset,
                      const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk, void* dv,
                      float* d_softmax_offset, void* stream);
+
+/* ---- FP8 (codelab "Speed up attention on GPU with cuDNN and
+ * TransformerEngine", section 10: attention under FP8 autocast with a
+ * DelayedScaling recipe, HYBRID format = E4M3 forward / E5M2 backward tensors,
+ * an amax history and the "max" rule).  The page fixes neither the formats'
+ * encodings nor the arithmetic; readings:
+ *   - formats E4M3 and E5M2 of the OCP 8-bit floating point spec, encoded by
+ *     round-to-nearest-even with saturation to the largest finite value;
+ *   - per-tensor scaling: codes = encode(x * scale), value = code * descale;
+ *   - the forward quantizes P relative to the exact row max,
+ *     P8 = E4M3(256 exp(s - m_i)), and normalises by the unquantized sum:
+ *     O_i = descale_v / (256 l_i) sum_j P8_ij V8_j.
+ * Built: the forward (E4M3 Q, K, V; bf16 O; fp32 LSE), the quantization with
+ * amax and the delayed-scaling scale update.  Not built: an FP8 backward
+ * (attn_bwd with ATTN_FP8 returns ATTN_ERR_UNSUPPORTED). */
+
+/* FP8 forward.  p->dtype = ATTN_FP8; Dqk = Dv in {64, 128}; dropout_p = 0.
+ * q, k, v: E4M3 codes (1 byte each) in the layouts of attn_fwd, 16-byte
+ * aligned.  descale_qkv: device float[3] = the descales of q, k, v (kept on
+ * the device so a recipe can update them without a host round trip).  o:
+ * bf16 [B,S,Hq,Dv] (packed: [T,Hq,Dv]); lse: float32 [B,Hq,S] (natural log,
+ * sink included).  workspace: attn_fwd_workspace_size(p) bytes, 256-byte
+ * aligned (V transposed per KV head).  Other arguments as attn_fwd. */
+int attn_fwd_fp8(const struct attn_params* p, const void* q, const void* k, const void* v,
+                 const float* descale_qkv, const float* softmax_offset, const int32_t* seqlens,
+                 const int32_t* seq_offsets, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Per-tensor quantization: out[i] = encode(clamp(x[i] * scale[0], -max,
+ * max)) in format fmt (ATTN_FP8_E4M3 / ATTN_FP8_E5M2), and amax[0] = max |x|
+ * (NaN elements excluded).  x: n elements of x_dtype (ATTN_F32 32-byte or
+ * ATTN_BF16 16-byte aligned); out: n bytes, 8-byte aligned; scale, amax:
+ * device float[1].  All on `stream`; amax is overwritten. */
+int attn_fp8_quantize(const void* x, int32_t x_dtype, size_t n, int32_t fmt, const float* scale,
+                      uint8_t* out, float* amax, void* stream);
+
+/* One delayed-scaling step, on the device: amax_history[0 .. history_len)
+ * (1 <= history_len <= 4096, newest first) becomes {amax[0], previous
+ * history without its oldest entry}; then scale[0] = fmt_max / max(history) /
+ * 2^margin when that max is positive and finite (else scale[0] is kept), and
+ * descale[0] = 1 / scale[0]. */
+int attn_fp8_update_scale(float* amax_history, int32_t history_len, const float* amax, int32_t fmt,
+                          int32_t margin, float* scale, float* descale, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

@@ -39,7 +39,7 @@ import math
 
 import numpy as np
 
-from .sdpa_oracle import kv_head, sink_logit, visible_mask
+from .sdpa_oracle import kv_head, sink_logit, visible_mask, visible_rows
 
 E4M3, E5M2 = "e4m3", "e5m2"
 # (exponent bits, mantissa bits, exponent bias)
@@ -118,7 +118,8 @@ def attention_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: flo
                   seqlens=None):
     """FP8 attention forward (readings above).  q8 [B,S,Hq,Dqk], k8 [B,S,Hkv,Dqk],
     v8 [B,S,Hkv,Dv]: E4M3 codes (uint8).  Returns o [B,S,Hq,Dv], lse [B,Hq,S]
-    (natural log) and p8 (the quantized probability codes, [B,Hq,S,S])."""
+    (natural log), p8 (the quantized probability codes, [B,Hq,S,S]) and the
+    unquantized e = exp(s - m) [B,Hq,S,S] and l [B,Hq,S] they come from."""
     q8, k8, v8 = (np.asarray(x, dtype=np.uint8) for x in (q8, k8, v8))
     B, S, Hq, dqk = q8.shape
     Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
@@ -130,6 +131,8 @@ def attention_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: flo
     o = np.zeros((B, S, Hq, dv))
     lse = np.zeros((B, Hq, S))
     p8 = np.zeros((B, Hq, S, S), dtype=np.uint8)
+    e_all = np.zeros((B, Hq, S, S))
+    l_all = np.zeros((B, Hq, S))
     for b in range(B):
         L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
         mask = visible_mask(S, L, causal, int(window[0]), int(window[1]))
@@ -148,7 +151,42 @@ def attention_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: flo
                 lse[b, h] = np.where(l > 0, m_safe + np.log(l), -np.inf)
             codes = np.where(mask, fp8_encode(256.0 * e, E4M3), 0).astype(np.uint8)
             p8[b, h] = codes
+            e_all[b, h] = e
+            l_all[b, h] = l
             pq = fp8_decode(codes, E4M3) / 256.0
             with np.errstate(invalid="ignore", divide="ignore"):
                 o[b, :, h, :] = np.where(l[:, None] > 0, (pq @ v[b, :, g, :]) / np.where(l > 0, l, 1.0)[:, None], 0.0)
-    return {"o": o, "lse": lse, "p8": p8}
+    return {"o": o, "lse": lse, "p8": p8, "e": e_all, "l": l_all}
+
+
+def attention_fp8_rows(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, *, b, h, rows,
+                       num_gqa_groups=None, causal=True, window=(-1, -1), scale_factor=None, softmax_type="vanilla",
+                       softmax_offset=None, seqlens=None):
+    """attention_fp8 for selected query rows of one (batch b, query head h):
+    a row's output depends only on its own visible keys, so rows can be
+    computed one by one at any length.  Returns o [n, Dv], lse [n]."""
+    q8, k8, v8 = (np.asarray(x, dtype=np.uint8) for x in (q8, k8, v8))
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    g = kv_head(h, Hq, Hkv)
+    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+    rows = np.asarray(rows, dtype=np.int64)
+    mask = visible_rows(rows, S, L, causal, int(window[0]), int(window[1]))
+    q = fp8_decode(q8[b, rows, h, :], E4M3) * float(descale_q)
+    k = fp8_decode(k8[b, :, g, :], E4M3) * float(descale_k)
+    v = fp8_decode(v8[b, :, g, :], E4M3) * float(descale_v)
+    s = scale * (q @ k.T)
+    z = sink_logit(softmax_type, softmax_offset, h)
+    neg = np.where(mask, s, -np.inf)
+    m = neg.max(axis=1)
+    if z is not None:
+        m = np.maximum(m, z)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(mask, np.exp(neg - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - m_safe))
+    with np.errstate(divide="ignore"):
+        lse = np.where(l > 0, m_safe + np.log(l), -np.inf)
+    pq = fp8_decode(np.where(mask, fp8_encode(256.0 * e, E4M3), 0), E4M3) / 256.0
+    o = np.where(l[:, None] > 0, (pq @ v) / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return {"o": o, "lse": lse}

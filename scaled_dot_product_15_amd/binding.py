@@ -18,7 +18,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdpa_mi355x.so")
 
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_FP8 = 0, 1, 2
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 MASKS = {"no_mask": 0, "none": 0, "causal": 1}
 SOFTMAX = {"vanilla": 0, "off_by_one": 1, "learnable": 2}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error",
@@ -61,6 +62,10 @@ EXPORTS = {
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp]),
+    "attn_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]),
+    "attn_fp8_quantize": (ctypes.c_int, [_vp, _c_i32, ctypes.c_size_t, _c_i32, _vp, _vp, _vp, _vp]),
+    "attn_fp8_update_scale": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_fwd_tile_shape": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(_c_i32),
                                            ctypes.POINTER(_c_i32)]),
@@ -105,7 +110,7 @@ def make_params(B, S, Hq, Hkv, d_qk, d_v, dtype="bf16", attn_mask_type="causal",
     """rng_state = (seed, offset): the 64-bit generator key and the 32-bit
     counter word of attention dropout (same values for forward and backward)."""
     seed, offset = (int(x) for x in rng_state)
-    return Params(B, S, Hq, Hkv, d_qk, d_v, ATTN_BF16 if dtype == "bf16" else ATTN_F32,
+    return Params(B, S, Hq, Hkv, d_qk, d_v, {"bf16": ATTN_BF16, "f32": ATTN_F32, "fp8": ATTN_FP8}[dtype],
                   MASKS[attn_mask_type], int(window_size[0]), int(window_size[1]),
                   float(scale_factor or 0.0), SOFTMAX[softmax_type], float(dropout_p),
                   seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF, offset & 0xFFFFFFFF)
@@ -463,6 +468,88 @@ def attn_bwd_noalloc(q, k, v, o, lse, d_o, *, outs, num_gqa_groups=None, attn_ma
         _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doff), _stream(stream)),
         "attn_bwd_noalloc")
     return dq, dk, dv, doff
+
+
+# ------------------------------------------------------------------- FP8
+
+def fp8_quantize(x, scale, fmt="e4m3", out=None, amax=None, stream=None):
+    """Per-tensor quantization on the device: codes (uint8, x's shape) of
+    clamp(x * scale, -max, max) in fmt ("e4m3" / "e5m2"), and amax = max |x|
+    (float32 [1]).  x: contiguous bf16 or float32 device tensor; scale: float32
+    device tensor of one element."""
+    torch = _torch()
+    if not x.is_cuda or not x.is_contiguous() or x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be a contiguous bf16 or float32 device tensor")
+    if not isinstance(scale, torch.Tensor) or not scale.is_cuda or scale.dtype != torch.float32 or scale.numel() != 1:
+        raise ValueError("scale must be a float32 device tensor of one element")
+    with _on_stream(stream):
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+        amax = torch.empty(1, dtype=torch.float32, device=x.device) if amax is None else amax
+    _check_buffer(out, x.shape, torch.uint8, "out")
+    _check_buffer(amax, (1,), torch.float32, "amax")
+    _check(load_library().attn_fp8_quantize(_ptr(x), ATTN_BF16 if x.dtype == torch.bfloat16 else ATTN_F32,
+                                            x.numel(), FP8_FORMATS[fmt], _ptr(scale), _ptr(out), _ptr(amax),
+                                            _stream(stream)), "attn_fp8_quantize")
+    return out, amax
+
+
+def fp8_update_scale(amax_history, amax, scale, descale, fmt="e4m3", margin=0, stream=None):
+    """One delayed-scaling step on the device (updates amax_history, scale and
+    descale in place): the new amax enters the history newest first; scale =
+    fmt_max / max(history) / 2^margin while that max is positive and finite."""
+    torch = _torch()
+    for name, t in (("amax_history", amax_history), ("amax", amax), ("scale", scale), ("descale", descale)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    _check(load_library().attn_fp8_update_scale(_ptr(amax_history), amax_history.numel(), _ptr(amax),
+                                                FP8_FORMATS[fmt], int(margin), _ptr(scale), _ptr(descale),
+                                                _stream(stream)), "attn_fp8_update_scale")
+
+
+def attn_fwd_fp8(q8, k8, v8, descale_qkv, *, num_gqa_groups=None, attn_mask_type="causal", window_size=(-1, -1),
+                 scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None, seq_offsets=None,
+                 max_seqlen=None, out=None, lse=None, workspace=None, stream=None, check_seqlens=True):
+    """FP8 forward: q8, k8, v8 are E4M3 codes (uint8, the layouts of attn_fwd),
+    descale_qkv a float32 device tensor [3] (descales of q, k, v).  Returns
+    (O bf16, LSE [B,Hq,S])."""
+    torch = _torch()
+    for t in (q8, k8, v8):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("q8, k8, v8 must be contiguous uint8 device tensors (E4M3 codes)")
+    if not descale_qkv.is_cuda or descale_qkv.dtype != torch.float32 or descale_qkv.numel() != 3:
+        raise ValueError("descale_qkv must be a float32 device tensor of 3 elements")
+    with _on_stream(stream):
+        packed = _layout(q8, seq_offsets, seqlens, max_seqlen, check_seqlens)
+        if packed is None:
+            B, S, Hq, dqk = q8.shape
+            Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+        else:
+            B, S = packed
+            Hq, dqk = q8.shape[1], q8.shape[2]
+            Hkv = k8.shape[1] if num_gqa_groups is None else int(num_gqa_groups)
+        lead = tuple(q8.shape[:-2])
+        if tuple(k8.shape) != lead + (Hkv, dqk) or tuple(v8.shape[:-1]) != lead + (Hkv,):
+            raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v8.shape)}")
+        p = make_params(B, S, Hq, Hkv, dqk, v8.shape[-1], "fp8", attn_mask_type, window_size, scale_factor,
+                        softmax_type)
+        if check_seqlens and packed is None:
+            _check_seqlens(seqlens, B, S)
+        offs = _sink_offsets(softmax_offset, Hq, q8) if softmax_type == "learnable" else None
+        o_shape = tuple(q8.shape[:-1]) + (p.head_dim_v,)
+        o = out if out is not None else torch.empty(o_shape, dtype=torch.bfloat16, device=q8.device)
+        l = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q8.device)
+        _check_buffer(o, o_shape, torch.bfloat16, "out")
+        _check_buffer(l, (B, Hq, S), torch.float32, "lse")
+        lib = load_library()
+        ws_bytes = lib.attn_fwd_workspace_size(ctypes.byref(p))
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q8.device)
+        elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must be a device tensor of at least {ws_bytes} bytes")
+        _check(lib.attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_qkv), _ptr(offs),
+                                _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)), "attn_fwd_fp8")
+    return o, l
 
 
 def debug_tile_map(p: Params, seqlens, block_m, block_n, stream=None):

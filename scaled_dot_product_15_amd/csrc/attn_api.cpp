@@ -15,6 +15,11 @@ bool supported(const attn_params* p) {
   // A negative scale is a valid problem; the kernels take each row's running
   // max on unscaled scores and multiply it by the scale, which needs scale >= 0.
   if (p->scale_factor < 0.0f) return false;
+  if (p->dtype == ATTN_FP8) {
+    // E4M3 forward: head dims 64 or 128, no dropout.
+    return p->head_dim_qk == p->head_dim_v && (p->head_dim_qk == 64 || p->head_dim_qk == 128) &&
+           p->dropout_p == 0.0f;
+  }
   int bm, bn;
   if (p->dtype == ATTN_BF16) return fwd_bf16_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
   return fwd_f32_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
@@ -25,7 +30,7 @@ int check_fields(const attn_params* p) {
   if (p->batch < 1 || p->seqlen < 1 || p->num_heads < 1 || p->num_gqa_groups < 1) return ATTN_ERR_INVALID_ARG;
   if (p->num_heads % p->num_gqa_groups != 0) return ATTN_ERR_INVALID_ARG;
   if (p->head_dim_qk < 1 || p->head_dim_v < 1) return ATTN_ERR_INVALID_ARG;
-  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16 && p->dtype != ATTN_FP8) return ATTN_ERR_INVALID_ARG;
   if (p->mask_type != ATTN_MASK_NONE && p->mask_type != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(p->scale_factor)) return ATTN_ERR_INVALID_ARG;
@@ -136,12 +141,13 @@ int attn_validate(const attn_params* p) {
 }
 
 size_t attn_fwd_workspace_size(const attn_params* p) {
-  (void)p;
-  return 0;
+  if (attn_validate(p) != ATTN_OK) return 0;
+  if (p->dtype != ATTN_FP8) return 0;
+  return align256(fp8_vt_bytes(p->batch, p->seqlen, p->num_gqa_groups, p->head_dim_v));
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
-  if (attn_validate(p) != ATTN_OK) return 0;
+  if (attn_validate(p) != ATTN_OK || p->dtype == ATTN_FP8) return 0;
   return 2 * delta_bytes(p) + dz_bytes(p) + kv_part_bytes(p);
 }
 
@@ -162,6 +168,7 @@ int fwd_run(const attn_params* p, const void* q, const void* k, const void* v, c
   }
   KArgs a = make_args(p);
   if (bias) set_bias(a, bias, nullptr, bias_batch, bias_heads);
+  if (p->dtype == ATTN_FP8) return ATTN_ERR_UNSUPPORTED;  // through attn_fwd_fp8 only
   a.q = q;
   a.k = k;
   a.v = v;
@@ -184,6 +191,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
              size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
+  if (p && p->dtype == ATTN_FP8) return check_fields(p) == ATTN_OK ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG;
   return fwd_run(p, q, k, v, nullptr, 0, 0, softmax_offset, seqlens, seq_offsets, o, lse, stream);
 }
 
@@ -208,6 +216,7 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   if (stage < 0 || stage > ATTN_BWD_STAGE_OFFSET_GRAD) return ATTN_ERR_INVALID_ARG;
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
+  if (p->dtype == ATTN_FP8) return ATTN_ERR_UNSUPPORTED;  // FP8: forward only
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!softmax_offset || !d_softmax_offset)) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type == ATTN_SOFTMAX_VANILLA && d_softmax_offset) return ATTN_ERR_INVALID_ARG;
@@ -296,6 +305,58 @@ int attn_bwd_stage(int stage, const attn_params* p, const void* q, const void* k
                     d_softmax_offset, workspace, workspace_bytes, stream, nullptr);
 }
 
+int attn_fwd_fp8(const attn_params* p, const void* q, const void* k, const void* v, const float* descale_qkv,
+                 const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = attn_validate(p);
+  if (rc != ATTN_OK) return rc;
+  if (p->dtype != ATTN_FP8) return ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !descale_qkv || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && !softmax_offset) return ATTN_ERR_INVALID_ARG;
+  // 16-byte row pieces of Q, K, V are read directly.
+  if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15) != 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_fwd_workspace_size(p)) return ATTN_ERR_WORKSPACE;
+  KArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.fp8_descale = descale_qkv;
+  a.softmax_offset = softmax_offset;
+  a.seqlens = seqlens;
+  a.seq_offsets = seq_offsets;
+  a.out_o = o;
+  a.out_lse = lse;
+  a.vt = static_cast<uint8_t*>(workspace);
+  return hip_status(launch_fwd_fp8(a, p->head_dim_qk, p->head_dim_v, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fp8_quantize(const void* x, int32_t x_dtype, size_t n, int32_t fmt, const float* scale, uint8_t* out,
+                      float* amax, void* stream) {
+  if (x_dtype != ATTN_F32 && x_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (fmt != ATTN_FP8_E4M3 && fmt != ATTN_FP8_E5M2) return ATTN_ERR_INVALID_ARG;
+  if ((n > 0 && (!x || !out)) || !scale || !amax) return ATTN_ERR_INVALID_ARG;
+  // whole 8-element groups are read and written as vectors
+  const uintptr_t align = x_dtype == ATTN_BF16 ? 15 : 31;
+  if ((reinterpret_cast<uintptr_t>(x) & align) != 0 || (reinterpret_cast<uintptr_t>(out) & 7) != 0)
+    return ATTN_ERR_INVALID_ARG;
+  return hip_status(launch_fp8_quantize(x, x_dtype == ATTN_BF16, n, fmt == ATTN_FP8_E5M2, scale, out, amax,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int attn_fp8_update_scale(float* amax_history, int32_t history_len, const float* amax, int32_t fmt, int32_t margin,
+                          float* scale, float* descale, void* stream) {
+  if (!amax_history || !amax || !scale || !descale) return ATTN_ERR_INVALID_ARG;
+  if (history_len < 1 || history_len > kFp8MaxHistory) return ATTN_ERR_INVALID_ARG;
+  if (fmt != ATTN_FP8_E4M3 && fmt != ATTN_FP8_E5M2) return ATTN_ERR_INVALID_ARG;
+  if (margin < 0 || margin > 64) return ATTN_ERR_INVALID_ARG;
+  const float fmt_max = fmt == ATTN_FP8_E4M3 ? 448.0f : 57344.0f;
+  return hip_status(launch_fp8_update_scale(amax_history, history_len, amax, fmt_max, margin, scale, descale,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -314,6 +375,7 @@ int attn_fwd_tile_shape(const attn_params* p, int32_t* block_m, int32_t* block_n
   if (!block_m || !block_n) return ATTN_ERR_INVALID_ARG;
   int bm = 0, bn = 0;
   if (p->dtype == ATTN_BF16) fwd_bf16_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
+  else if (p->dtype == ATTN_FP8) bm = 128, bn = 64;
   else fwd_f32_tiles(p->head_dim_qk, p->head_dim_v, &bm, &bn);
   *block_m = bm;
   *block_n = bn;

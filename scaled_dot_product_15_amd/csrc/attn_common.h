@@ -52,6 +52,9 @@ struct KArgs {
   void* d_bias;         // its gradient, same shape, or nullptr
   int bias_b, bias_h;   // 1 (shared) or B / Hq
   float inv_scale;      // 1 / scale: the kernels add bias / scale to the unscaled scores
+  const float* fp8_descale;  // FP8 forward: [3] descales of Q, K, V (device)
+  uint8_t* vt;          // FP8 forward workspace: V^T [B, Hkv, Dv, S_pad] with permuted key order
+  int s_pad;            // S rounded up to the FP8 key tile (64)
   int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
   float drop_scale;     // 1 / (1 - drop_t / 256)
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;  // generator key and counter word 3
@@ -190,9 +193,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // the bank array, so swz (kept below 8, which keeps c ^ swz inside the row)
 // must do the same for every other row.  swz is a bijection on the rows of
 // any aligned group of 16 in both cases.
+// 64-byte rows (CH == 4, the FP8 tiles) put four rows on the bank array, so
+// swz spreads the four rows of each group of 16 that share a bank quarter
+// over the four chunks.
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CH == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+  else if constexpr (CH == 4) return (r >> 2) & 3;
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 template <int CH>

@@ -1,0 +1,301 @@
+// FP8 attention forward: E4M3 Q, K, V with per-tensor descales, gfx950 MFMA
+// 32x32x64 f8f6f4 (twice the bf16 matrix rate), fp32 softmax, bf16 O.
+//
+// Computes, for each row i (codelab "Speed up attention on GPU with cuDNN and
+// TransformerEngine", section 10: FP8 with E4M3 for the forward tensors; the
+// arithmetic is this build's reading, see the header):
+//     s_ij = scale dq dk (Q8_i . K8_j),  m_i = row max (with the sink),
+//     l_i  = sum_j exp(s_ij - m_i) (+ exp(z - m_i)),  LSE_i = m_i + ln l_i,
+//     P8_ij = E4M3(256 exp(s_ij - m_i)),  O_i = dv / (256 l_i) sum_j P8_ij V8_j.
+// Quantizing P relative to the exact row max needs the max first, so the
+// kernel walks the key tiles twice: pass 1 computes S and the row max, pass 2
+// computes S again, exp, the row sum, P8 and O += P8 V.  With the max known,
+// no accumulator rescale is ever needed.
+//
+// Work decomposition as the bf16 forward: 4 waves x 32 query rows of one
+// (batch, head), key tiles of 64 in LDS (direct-to-LDS copies, double
+// buffered), heavy query tiles first, the G heads of a GQA group on one XCD.
+//
+// MFMA operands (K = 64 per instruction, 32 bytes per lane, lane l = row or
+// column l % 32 and half l / 32; an A lane and a B lane of the same half
+// pair their bytes one to one):
+//   S^T = K Q^T: A = K rows (LDS, 16-byte chunks 4k + hf and 4k + 2 + hf of
+//     a 128-byte row for k-step k), B = Q^T (registers, same chunks of the
+//     lane's query row).  The 32x32 accumulator puts a query in each lane
+//     column and 16 keys per lane (acc_row).
+//   O^T = V^T P^T: B = P8 straight from the S^T accumulators of the tile's
+//     two 32-key blocks (byte 16 kb + e = key 32 kb + acc_row(e, hf)), A = the
+//     V^T row of the lane's dim holding the same keys in the same order: the
+//     pre-pass stores V^T with the keys of each 64-key group permuted so that
+//     those 32 keys are the contiguous half hf of the row.
+#include <type_traits>
+
+#include "launch.h"
+
+namespace sdpa {
+
+// Position of key k (0..63) of a 64-key group in the permuted V^T row: half
+// hf of the row holds the keys a lane of half hf holds in two 32x32
+// accumulator blocks, byte 16 kb + e for key 32 kb + acc_row(e, hf).
+__host__ __device__ __forceinline__ int fp8_key_slot(int k) {
+  const int kb = k >> 5, r = k & 31;
+  const int hf = (r >> 2) & 1, e = (r >> 3) * 4 + (r & 3);
+  return hf * 32 + kb * 16 + e;
+}
+
+// V (E4M3 codes, [rows, Hkv, Dv] per batch) -> V^T [B, Hkv, Dv, S_pad] with
+// the key slots above; keys at or past the batch's row count are zero.  One
+// thread per (batch, kv head, 16 dims, key), keys fastest, so a wave writes
+// each of its 16 dim rows in one 64-byte run.
+template <int DV>
+__global__ __launch_bounds__(256) void fp8_vt_kernel(KArgs a) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int j = (int)(t % a.s_pad);
+  long long r = t / a.s_pad;
+  const int dc = (int)(r % (DV / 16));
+  r /= DV / 16;
+  const int g = (int)(r % a.Hkv), b = (int)(r / a.Hkv);
+  if (b >= a.B) return;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (j < seq_rows(a, b))
+    v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) +
+                                        ((seq_row0(a, b) + j) * a.Hkv + g) * DV + dc * 16);
+  uint8_t* dst = a.vt + (((size_t)b * a.Hkv + g) * DV + dc * 16) * a.s_pad + (j & ~63) + fp8_key_slot(j & 63);
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int byte = 0; byte < 4; ++byte) dst[(size_t)(w * 4 + byte) * a.s_pad] = (uint8_t)(v[w] >> (8 * byte));
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);  // E4M3 x E4M3
+}
+__device__ __forceinline__ i32x8 cat16(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int D>
+struct Fp8Cfg {
+  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int KCH = D / 16;      // 16-byte chunks per K row (D bytes)
+  static constexpr int KT = BN * D;       // bytes of a K tile [64 keys][D]
+  static constexpr int VT = D * BN;       // bytes of a V^T tile [D dims][64 keys]
+  static constexpr int NKS = D / 64;      // k-steps of S
+  static constexpr int LDS_BYTES = 2 * (KT + VT);
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
+  using C = Fp8Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+  auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
+  auto vtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT) + C::KT; };
+
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  int b, h, qt;
+  {
+    const int N = a.B * a.Hq * a.n_tiles, chunk = a.G, full = (N / (8 * chunk)) * (8 * chunk);
+    int l = blockIdx.x;
+    if (l < full) {
+      const int xcd = l & 7, slot = l >> 3;
+      l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+    }
+    const int per_tile = a.B * a.Hq;
+    qt = a.n_tiles - 1 - l / per_tile;
+    b = (l % per_tile) / a.Hq;
+    h = (l % per_tile) % a.Hq;
+  }
+  const int g = h / a.G;
+  const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const int i0 = qt * C::BM, qi = i0 + w * 32 + l32;
+  int klo, khi;
+  row_key_bounds(m, qi, klo, khi);
+
+  // Q^T operand: lane holds query qi, chunks 4k + hf and 4k + 2 + hf of its row.
+  i32x8 qreg[C::NKS];
+  {
+    const size_t qstride = (size_t)a.Hq * D;
+    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(static_cast<const uint8_t*>(a.q) + (seq_row0(a, b) * a.Hq + h) * D,
+                                                 (uint32_t)(m.L * qstride));
+#pragma unroll
+    for (int k = 0; k < C::NKS; ++k)
+      qreg[k] = cat16(buf_load16(qres, (uint32_t)(qi * qstride + (4 * k + hf) * 16)),
+                      buf_load16(qres, (uint32_t)(qi * qstride + (4 * k + 2 + hf) * 16)));
+  }
+  const uint8_t* Kg = static_cast<const uint8_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * D;
+  const uint8_t* VTg = a.vt + ((size_t)b * a.Hkv + g) * D * a.s_pad;
+  const uint32_t kstride = (uint32_t)(a.Hkv * D);
+  const TileCopy<C::BN, C::KCH, C::NT> kcopy(tid, kstride);
+  const TileCopy<D, 4, C::NT> vcopy(tid, (uint32_t)a.s_pad);
+  const RowReads<C::KCH> krd(lane);
+  // V^T rows: chunks 2 hf and 2 hf + 1 (the keys of this lane's half).
+  uint32_t voff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) voff[c] = (uint32_t)swz_off<4>(l32, 2 * hf + c);
+
+  const float descale_q = a.fp8_descale[0], descale_k = a.fp8_descale[1], descale_v = a.fp8_descale[2];
+  const float c8 = a.scale_log2 * descale_q * descale_k;  // s_raw -> log2 units
+  const float z2 = sink_logit(a, h) * kLog2e;
+  const bool has_sink = a.softmax_type != 0;
+
+  int lo = 0, hi = -1;
+  const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
+  if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
+  const int kt0 = lo / C::BN, kt1 = hi < 0 ? -1 : hi / C::BN;
+  int fa = kt0, fb = kt0;  // tiles every row of the workgroup sees in full: [fa, fb)
+  {
+    int f0, f1;
+    if (kt0 <= kt1 && full_key_tiles(m, i0, C::BM, C::BN, f0, f1)) {
+      fa = f0 < kt0 ? kt0 : f0;
+      fb = (f1 > kt1 ? kt1 : f1) + 1;
+      if (fb < fa) fb = fa;
+    }
+  }
+
+  // S^T of the tile in buffer buf: two 32-key blocks, raw products of codes.
+  auto scores = [&](const uint8_t* Ks, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::NKS; ++k)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const i32x8 ka = cat16(krd.read(reinterpret_cast<const uint16_t*>(Ks), kb * 32, 2 * k),
+                               krd.read(reinterpret_cast<const uint16_t*>(Ks), kb * 32, 2 * k + 1));
+        s[kb] = mfma_fp8(ka, qreg[k], s[kb]);
+      }
+  };
+  // Element i of block kb is key j0 + kb*32 + acc_row(i, hf).
+  auto mask = [&](f32x16 (&s)[2], int j0) __attribute__((always_inline)) {
+    const int lo_r = klo - (j0 + hf * 4), hi_r = khi - (j0 + hf * 4);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
+        s[kb][i] = (off >= lo_r && off <= hi_r) ? s[kb][i] : -__builtin_inff();
+      }
+  };
+
+  // ---- pass 1: row max -----------------------------------------------------
+  float mx = -__builtin_inff();
+  auto pass1 = [&](int kt, int buf, bool masked) __attribute__((always_inline)) {
+    if (kt < kt1) kcopy.issue(Kg, kstride, (kt + 1) * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(buf ^ 1)));
+    f32x16 s[2];
+    scores(ktile(buf), s);
+    if (masked) mask(s, kt * C::BN);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    lds_dma_wait();
+    __syncthreads();
+  };
+  if (kt0 <= kt1) kcopy.issue(Kg, kstride, kt0 * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(0)));
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) pass1(kt, (kt - kt0) & 1, kt < fa || kt >= fb);
+  float m2 = halves_max(mx) * c8;  // row max in log2 units
+  if (has_sink) m2 = fmaxf(m2, z2);
+  const float nm = m2 == -__builtin_inff() ? 0.0f : -m2;
+
+  // ---- pass 2: P8 and O ----------------------------------------------------
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float lsum = 0.0f;
+  auto pass2 = [&](int kt, int buf, bool masked) __attribute__((always_inline)) {
+    if (kt < kt1) {
+      kcopy.issue(Kg, kstride, (kt + 1) * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(buf ^ 1)));
+      vcopy.issue_bytes(VTg + (kt + 1) * C::BN, (uint32_t)(D * a.s_pad - (kt + 1) * C::BN),
+                        reinterpret_cast<uint16_t*>(vtile(buf ^ 1)));
+    }
+    f32x16 s[2];
+    scores(ktile(buf), s);
+    if (masked) mask(s, kt * C::BN);
+    // p = 2^(s c8 - m2) <= 1, masked -> 0; P8 = E4M3(256 p) (never above 256)
+    uint32_t pw[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(fmaf(s[kb][4 * q + e], c8, nm));
+          lsum += p[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.0f, p[1] * 256.0f, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.0f, p[3] * 256.0f, word, true);
+        pw[kb * 4 + q] = (uint32_t)word;
+      }
+    const i32x8 pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    const uint8_t* Vs = vtile(buf);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const char* row = reinterpret_cast<const char*>(Vs) + db * 32 * 64;
+      const i32x8 va = cat16(*reinterpret_cast<const u32x4*>(row + voff[0]), *reinterpret_cast<const u32x4*>(row + voff[1]));
+      o[db] = mfma_fp8(va, pb, o[db]);
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  if (kt0 <= kt1) {
+    kcopy.issue(Kg, kstride, kt0 * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(0)));
+    vcopy.issue_bytes(VTg + kt0 * C::BN, (uint32_t)(D * a.s_pad - kt0 * C::BN), reinterpret_cast<uint16_t*>(vtile(0)));
+  }
+  lds_dma_wait();
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) pass2(kt, (kt - kt0) & 1, kt < fa || kt >= fb);
+
+  float l_tot = halves_sum(lsum);
+  if (has_sink) l_tot += fast_exp2(z2 - m2);
+  const float inv = l_tot > 0.0f ? descale_v / (256.0f * l_tot) : 0.0f;
+  if (qi < seq_rows(a, b)) {
+    uint16_t* op = static_cast<uint16_t*>(a.out_o) + ((seq_row0(a, b) + qi) * a.Hq + h) * D + hf * 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        u32x2 val = {pack_bf16(o[db][ig * 4] * inv, o[db][ig * 4 + 1] * inv),
+                     pack_bf16(o[db][ig * 4 + 2] * inv, o[db][ig * 4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + db * 32 + ig * 8) = val;
+      }
+  }
+  if (qi < a.S && hf == 0) {
+    const float lse2 = l_tot > 0.0f ? m2 + __log2f(l_tot) : -__builtin_inff();
+    a.out_lse[((size_t)b * a.Hq + h) * a.S + qi] = lse2 * kLn2;
+  }
+}
+
+template __global__ void fp8_vt_kernel<64>(KArgs);
+template __global__ void fp8_vt_kernel<128>(KArgs);
+template __global__ void fwd_fp8_kernel<64>(KArgs);
+template __global__ void fwd_fp8_kernel<128>(KArgs);
+
+size_t fp8_vt_bytes(int B, int S, int Hkv, int dv) {
+  const size_t s_pad = (size_t)((S + 63) / 64) * 64;
+  return (size_t)B * Hkv * dv * s_pad;
+}
+
+template <int D>
+static hipError_t launch_fp8_cfg(KArgs a, hipStream_t stream) {
+  using C = Fp8Cfg<D>;
+  a.s_pad = (a.S + 63) / 64 * 64;
+  const long long nv = (long long)a.B * a.Hkv * a.s_pad * (D / 16);
+  hipLaunchKernelGGL(fp8_vt_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, stream, a);
+  a.n_tiles = (a.S + C::BM - 1) / C::BM;
+  const long long n = (long long)a.B * a.Hq * a.n_tiles;
+  hipLaunchKernelGGL(fwd_fp8_kernel<D>, dim3((unsigned)n), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const KArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 64 && dv == 64) return launch_fp8_cfg<64>(a, stream);
+  if (dqk == 128 && dv == 128) return launch_fp8_cfg<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -41,6 +41,16 @@ hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t strea
 int dbias_key_chunks(int n_mats, int n_qt, int n_kt);
 hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 
+// FP8 forward (E4M3 Q, K, V): V^T pre-pass into a.vt, then the two-pass kernel.
+size_t fp8_vt_bytes(int B, int S, int Hkv, int dv);
+hipError_t launch_fwd_fp8(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// FP8 per-tensor scaling.
+hipError_t launch_fp8_quantize(const void* x, int bf16_in, size_t n, int e5m2, const float* scale, uint8_t* out,
+                               float* amax, hipStream_t stream);
+constexpr int kFp8MaxHistory = 4096;
+hipError_t launch_fp8_update_scale(float* history, int len, const float* amax, float fmt_max, int margin,
+                                   float* scale, float* descale, hipStream_t stream);
+
 bool fwd_f32_tiles(int dqk, int dv, int* bm, int* bn);
 hipError_t launch_fwd_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dkdv_f32(const KArgs& a, int dqk, int dv, hipStream_t stream);

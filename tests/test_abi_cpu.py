@@ -77,7 +77,7 @@ def test_validate_dropout_rate():
 
 
 def test_validate_bad_enums():
-    for field, bad in (("dtype", 2), ("mask_type", 3), ("softmax_type", 3), ("softmax_type", -1)):
+    for field, bad in (("dtype", 3), ("dtype", -1), ("mask_type", 3), ("softmax_type", 3), ("softmax_type", -1)):
         p = P()
         setattr(p, field, bad)
         assert binding.attn_validate(p) == -1
@@ -332,3 +332,33 @@ def test_bias_arguments_checked_before_any_hip_call():
         assert call(P(S=50000, B=1, Hq=2, Hkv=1), f, 1, 1) == -2
         assert call(P(S=100), f, 1, 1) == -2                 # S not a multiple of 8
         assert call(P(), ctypes.c_void_p(264), 1, 1) == -1   # bias not 16-byte aligned
+
+
+def test_fp8_validation_before_any_hip_call():
+    """ATTN_FP8 is a forward-only dtype: head dims 64 or 128 without dropout;
+    attn_fwd / attn_bwd refuse it (unsupported), attn_fwd_fp8 refuses other
+    dtypes; its workspace holds V transposed.  The scaling entry points check
+    formats, history lengths and pointers.  Nothing is launched."""
+    lib = binding.load_library()
+    f = ctypes.c_void_p(256)
+    p8 = binding.make_params(2, 100, 4, 2, 128, 128, "fp8", "causal")
+    assert binding.attn_validate(p8) == 0
+    assert binding.attn_fwd_workspace_size(p8) == 2 * 2 * 128 * 128  # B Hkv Dv S_pad(128)
+    assert binding.attn_bwd_workspace_size(p8) == 0
+    assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 192, 128, "fp8")) == -2
+    assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 64, 64, "fp8", dropout_p=0.1)) == -2
+    assert lib.attn_fwd(ctypes.byref(p8), f, f, f, None, None, None, f, f, None, 0, None) == -2
+    assert lib.attn_bwd(ctypes.byref(p8), f, f, f, f, f, f, None, None, None, f, f, f, None, f, 1 << 20, None) == -2
+    pb = binding.make_params(2, 100, 4, 2, 128, 128, "bf16", "causal")
+    assert lib.attn_fwd_fp8(ctypes.byref(pb), f, f, f, f, None, None, None, f, f, f, 1 << 20, None) == -1
+    assert lib.attn_fwd_fp8(ctypes.byref(p8), f, f, f, None, None, None, None, f, f, f, 1 << 20, None) == -1
+    assert lib.attn_fwd_fp8(ctypes.byref(p8), f, f, f, f, None, None, None, f, f, None, 0, None) == -3
+    assert lib.attn_fwd_fp8(ctypes.byref(p8), f, f, f, f, None, None, None, f, f, f, 16, None) == -3
+    assert lib.attn_fwd_fp8(ctypes.byref(p8), ctypes.c_void_p(264), f, f, f, None, None, None, f, f, f, 1 << 20,
+                            None) == -1  # q not 16-byte aligned
+    assert lib.attn_fp8_quantize(f, 1, 10, 2, f, f, f, None) == -1      # no such format
+    assert lib.attn_fp8_quantize(f, 2, 10, 0, f, f, f, None) == -1      # x dtype
+    assert lib.attn_fp8_quantize(f, 1, 10, 0, None, f, f, None) == -1   # no scale
+    assert lib.attn_fp8_update_scale(f, 0, f, 0, 0, f, f, None) == -1
+    assert lib.attn_fp8_update_scale(f, 4097, f, 0, 0, f, f, None) == -1
+    assert lib.attn_fp8_update_scale(f, 16, f, 3, 0, f, f, None) == -1

@@ -1,0 +1,193 @@
+"""GPU parity of the FP8 path against the FP8 oracle (oracle/fp8.py).
+
+  quantize     device codes equal the oracle's encoder bit for bit (E4M3 and
+               E5M2, bf16 and float32 inputs, saturated values, a ragged
+               tail); amax exact
+  recipe       a sequence of delayed-scaling steps: history exact, scale and
+               descale to float32 rounding
+  forward      E4M3 attention vs attention_fp8 on small shapes (every element
+               within a derived bound: bf16 output rounding plus one E4M3 step
+               for P elements whose score sits within the device's float32
+               accuracy of a rounding midpoint; masks, softmax types, GQA,
+               padding, head dims 64 and 128), the GQA+SWA S=4096 workload on
+               sampled rows, packed == padded
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import fp8
+from scaled_dot_product_15_amd import binding, inputs
+from tests import gpu_cases as gc
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gc.gpu_available(), reason="needs a GPU and the built library")]
+
+
+def _dev(x, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t if dtype is None else t.to(dtype)
+
+
+@pytest.mark.parametrize("fmt,src", list(itertools.product(("e4m3", "e5m2"), ("bf16", "f32"))))
+def test_quantize_bit_exact(fmt, src):
+    import torch
+    rng = np.random.default_rng(81)
+    ofmt = fp8.E4M3 if fmt == "e4m3" else fp8.E5M2
+    mx = fp8.fp8_max(ofmt)
+    n = 100_003  # not a multiple of the 8-element groups
+    x = np.concatenate([rng.standard_normal(n - 6) * 3, [1e4, -1e4, 5e5, -5e5, 0.0, -0.0]]).astype(np.float32)
+    tx = _dev(x, torch.bfloat16 if src == "bf16" else torch.float32)
+    xv = inputs.exact_f64(tx)
+    scale = np.float32(mx / 16.0)  # values up to 16 map to the format's top; larger ones saturate
+    gc.log(f"quantize {fmt} from {src}, n={n}")
+    codes, amax = binding.fp8_quantize(tx, _dev(np.array([scale], np.float32)), fmt)
+    import torch as _t
+    _t.cuda.synchronize()
+    # the device scales in float32: x * scale rounded to float32, then encoded
+    want = fp8.fp8_encode((xv * np.float64(scale)).astype(np.float32).astype(np.float64), ofmt)
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (fmt, src, xv[bad[:5]], got[bad[:5]], want[bad[:5]])
+    assert float(amax.cpu()[0]) == float(np.abs(xv).max())
+
+
+def test_delayed_scaling_steps():
+    import torch
+    rng = np.random.default_rng(82)
+    L = 1024
+    hist = _dev(np.zeros(L, np.float32))
+    scale = _dev(np.array([1.0], np.float32))
+    descale = _dev(np.array([1.0], np.float32))
+    h_ref, s_ref = np.zeros(L), 1.0
+    for step in range(40):
+        amax_v = float(np.float32(abs(rng.standard_normal()) * 10.0 ** int(rng.integers(-2, 3)))) if step else 0.0
+        amax = _dev(np.array([amax_v], np.float32))
+        binding.fp8_update_scale(hist, amax, scale, descale, "e4m3", margin=1)
+        h_ref, s_ref, d_ref = fp8.delayed_scaling_update(h_ref, amax_v, s_ref, fp8.E4M3, margin=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(hist.cpu().numpy().astype(np.float64), h_ref)
+        assert abs(float(scale.cpu()[0]) - s_ref) <= 4e-7 * s_ref
+        assert abs(float(descale.cpu()[0]) - d_ref) <= 4e-7 * d_ref
+        s_ref = float(scale.cpu()[0])  # carry the device's float32 scale forward
+
+
+def _fp8_inputs(p, seed, sc=16.0):
+    """E4M3 codes of the N(0,1) draws scaled by sc; descales 1/sc."""
+    arr = inputs.draw(p, seed)
+    q8, k8, v8 = (fp8.fp8_encode(arr[n].astype(np.float64) * sc, fp8.E4M3) for n in ("q", "k", "v"))
+    return arr, q8, k8, v8, 1.0 / sc
+
+
+MASKS = {"causal": (True, (-1, -1)), "causal_swa": (True, (37, 0)), "window": (False, (20, 9)),
+         "full": (False, (-1, -1))}
+CASES = list(itertools.product((64, 128), MASKS, ("vanilla", "off_by_one", "learnable"), (False, True)))
+
+
+@pytest.mark.parametrize("d,mask,st,padded", CASES, ids=lambda x: str(x))
+def test_fp8_forward_small(d, mask, st, padded):
+    import torch
+    causal, win = MASKS[mask]
+    p = inputs.Problem(B=3, S=333, Hq=4, Hkv=2, d_qk=d, d_v=d, dtype="bf16", causal=causal, window=win,
+                       softmax_type=st)
+    seed = 80_000 + CASES.index((d, mask, st, padded))
+    arr, q8, k8, v8, ds = _fp8_inputs(p, seed)
+    sl = np.array([333, 150, 0], np.int32) if padded else None
+    gc.log(f"fp8 fwd d={d} {mask} {st} padded={padded} seed={seed}")
+    desc = _dev(np.array([ds, ds, ds], np.float32))
+    o, lse = binding.attn_fwd_fp8(_dev(q8), _dev(k8), _dev(v8), desc, num_gqa_groups=p.Hkv,
+                                  attn_mask_type="causal" if causal else "no_mask", window_size=win, softmax_type=st,
+                                  softmax_offset=_dev(arr["alpha"]), seqlens=None if sl is None else _dev(sl))
+    torch.cuda.synchronize()
+    r = fp8.attention_fp8(q8, k8, v8, ds, ds, ds, num_gqa_groups=p.Hkv, causal=causal, window=win, softmax_type=st,
+                          softmax_offset=arr["alpha"].astype(np.float64), seqlens=sl)
+    o64, l64 = inputs.exact_f64(o), inputs.exact_f64(lse)
+    fin = np.isfinite(r["lse"])
+    assert np.array_equal(np.isfinite(l64), fin)
+    lse_err = float(np.abs(l64[fin] - r["lse"][fin]).max()) if fin.any() else 0.0
+    o_err = np.abs(o64 - r["o"])
+    bound = _o_bound(r, v8, ds, p)
+    rel = gc.rel_l2(o64, r["o"])
+    worst = float((o_err - bound).max())
+    gc.log(f"  lse {lse_err:.3g} o max-abs {float(o_err.max()):.3g} rel-l2 {rel:.3g} worst over bound {worst:.3g}")
+    assert lse_err <= 1e-3 and rel <= 1e-2
+    assert (o_err <= bound).all(), worst
+    if sl is not None:
+        for b in range(p.B):
+            assert (o64[b, sl[b]:] == 0).all()
+
+
+def _o_bound(r, v8, ds, p, near_rel=1e-3):
+    """Per-element bound on |O_gpu - O_oracle|: bf16 output rounding (2^-9,
+    doubled) relative to O; the device's accumulation (the FP8 MFMA sums
+    products to about 3e-5 relative, float32 row sums) as 2e-4 of
+    sum_j P8_ij |V_j| / (256 l_i), the sum of the magnitudes O adds up; and,
+    for every P element whose 256 e lies within near_rel (relative) of an E4M3
+    rounding midpoint, one E4M3 step of that element times |V| / (256 l): the
+    device's float32 scores can put such an element on the neighbouring code."""
+    vals = fp8.fp8_decode(np.arange(127), fp8.E4M3)          # finite non-negative values, ascending
+    mids = (vals[1:] + vals[:-1]) / 2
+    gaps = np.diff(vals)
+    x = 256.0 * r["e"]                                       # [B, Hq, S, S]
+    k = np.clip(np.searchsorted(mids, x), 1, len(mids) - 1)  # nearest midpoints mids[k-1], mids[k]
+    near = np.zeros_like(x, dtype=bool)
+    step = np.zeros_like(x)
+    for kk in (k - 1, k):
+        close = np.abs(x - mids[kk]) <= near_rel * np.maximum(x, 1e-30)
+        near |= close
+        step = np.where(close, np.maximum(step, gaps[kk]), step)
+    near &= r["p8"] > 0
+    v = fp8.fp8_decode(v8, fp8.E4M3) * ds                    # [B, S, Hkv, Dv]
+    G = p.Hq // p.Hkv
+    bound = 2.0 ** -8 * np.abs(r["o"]) + 1e-6
+    pq = fp8.fp8_decode(r["p8"], fp8.E4M3) / 256.0
+    for b in range(p.B):
+        for h in range(p.Hq):
+            w = np.where(near[b, h], step[b, h], 0.0) / 256.0
+            l = np.where(r["l"][b, h] > 0, r["l"][b, h], 1.0)
+            av = np.abs(v[b, :, h // G, :])
+            bound[b, :, h, :] += (w @ av + 2e-4 * (pq[b, h] @ av)) / l[:, None]
+    return bound
+
+
+def test_fp8_forward_full_length_sampled():
+    """GQA+SWA S=4096 (B=4, Hq=32, Hkv=8, d=128, window (1024, 0)), sampled rows."""
+    import torch
+    p = inputs.workload_configs()[2][0]
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 83_000)
+    desc = _dev(np.array([ds, ds, ds], np.float32))
+    gc.log("fp8 fwd full length")
+    o, lse = binding.attn_fwd_fp8(_dev(q8), _dev(k8), _dev(v8), desc, num_gqa_groups=p.Hkv,
+                                  window_size=p.window)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 1023, 1024, 1025, 2047, 3333, 4095])
+    for b, h in ((0, 0), (1, 9), (3, 31)):
+        r = fp8.attention_fp8_rows(q8, k8, v8, ds, ds, ds, b=b, h=h, rows=rows, num_gqa_groups=p.Hkv,
+                                   causal=True, window=p.window)
+        o64 = inputs.exact_f64(o[b, rows, h])
+        assert np.abs(inputs.exact_f64(lse[b, h, rows]) - r["lse"]).max() <= 1e-3
+        assert np.abs(o64 - r["o"]).max() <= gc.TOL["bf16"]["o_maxabs"], (b, h)
+        assert gc.rel_l2(o64, r["o"]) <= 1e-2
+
+
+def test_fp8_packed_equals_padded():
+    import torch
+    p = inputs.Problem(B=3, S=256, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16", causal=True, window=(60, 0),
+                       softmax_type="off_by_one")
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 84_000)
+    sizes = [256, 100, 1]
+    desc = _dev(np.array([ds, ds, ds], np.float32))
+    o, lse = binding.attn_fwd_fp8(_dev(q8), _dev(k8), _dev(v8), desc, num_gqa_groups=p.Hkv, window_size=p.window,
+                                  softmax_type=p.softmax_type, seqlens=_dev(np.array(sizes, np.int32)))
+    cat = lambda x: np.ascontiguousarray(np.concatenate([x[b, :n] for b, n in enumerate(sizes)]))  # noqa: E731
+    off = _dev(np.array([0, 256, 356, 357], np.int32))
+    po, plse = binding.attn_fwd_fp8(_dev(cat(q8)), _dev(cat(k8)), _dev(cat(v8)), desc, num_gqa_groups=p.Hkv,
+                                    window_size=p.window, softmax_type=p.softmax_type, seq_offsets=off,
+                                    max_seqlen=p.S)
+    torch.cuda.synchronize()
+    start = [0, 256, 356]
+    for b, n in enumerate(sizes):
+        assert torch.equal(po[start[b]:start[b] + n], o[b, :n])
+        assert torch.equal(plse[b, :, :n], lse[b, :, :n])

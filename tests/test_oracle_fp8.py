@@ -156,7 +156,26 @@ def pin_attention_loops(m):
                 assert abs(r["o"][0, i, h, d] - acc / l) <= 1e-12 * (1 + abs(acc / l))
 
 
-PINS = [pin_decode, pin_encode, pin_saturation_and_nan, pin_recipe, pin_attention_bound, pin_attention_loops]
+def pin_attention_rows(m):
+    """The row-sampled function equals the whole-problem one."""
+    for ci, (causal, win, sl) in enumerate(MASKS):
+        for st in oracle.SOFTMAX_TYPES:
+            q8, k8, v8, alpha = _case(3300 + ci)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, softmax_type=st, softmax_offset=alpha,
+                      seqlens=None if sl is None else np.array(sl))
+            full = m.attention_fp8(q8, k8, v8, 0.5, 0.25, 0.125, **kw)
+            for b in range(2):
+                for h in (0, 1, 3):
+                    rows = [10, 0, 4, 7]
+                    r = m.attention_fp8_rows(q8, k8, v8, 0.5, 0.25, 0.125, b=b, h=h, rows=rows, **kw)
+                    assert np.array_equal(np.isfinite(r["lse"]), np.isfinite(full["lse"][b, h, rows]))
+                    fin = np.isfinite(r["lse"])
+                    assert np.abs(r["lse"][fin] - full["lse"][b, h, rows][fin]).max(initial=0) <= 1e-12
+                    assert np.abs(r["o"] - full["o"][b, rows, h]).max() <= 1e-12
+
+
+PINS = [pin_decode, pin_encode, pin_saturation_and_nan, pin_recipe, pin_attention_bound, pin_attention_loops,
+        pin_attention_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -177,15 +196,19 @@ MUTANTS = {
     "history_oldest_first": ("h = np.concatenate([[float(new_amax)], np.asarray(history, dtype=np.float64)[:-1]])",
                              "h = np.concatenate([np.asarray(history, dtype=np.float64)[1:], [float(new_amax)]])"),
     "margin_ignored": ("scale = fp8_max(fmt) / amax / (2.0 ** margin)", "scale = fp8_max(fmt) / amax"),
-    "sink_missing_in_sum": ("l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - m_safe))", "l = e.sum(axis=1)"),
+    "sink_missing_in_sum": ("l = e.sum(axis=1) + (0.0 if z is None else np.exp(z - m_safe))", "l = e.sum(axis=1)",
+                            "all"),
+    "rows_wrong_kv_head": ("k = fp8_decode(k8[b, :, g, :], E4M3) * float(descale_k)",
+                           "k = fp8_decode(k8[b, :, h % k8.shape[2], :], E4M3) * float(descale_k)"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_fp8_mutant_is_caught(name):
     src = open(SRC).read()
-    old, new = MUTANTS[name]
-    assert src.count(old) == 1, name
+    old, new = MUTANTS[name][:2]
+    every = len(MUTANTS[name]) > 2
+    assert src.count(old) >= 1 and (every or src.count(old) == 1), name
     mod = types.ModuleType("fp8_mutant")
     mod.__package__ = "oracle"
     exec(compile(src.replace(old, new), "fp8_mutant.py", "exec"), mod.__dict__)
