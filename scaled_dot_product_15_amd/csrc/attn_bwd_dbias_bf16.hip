@@ -8,7 +8,8 @@
 //     P = exp(scale q.k + bias - LSE),  dP = dO V^T.
 // Deterministic: a workgroup owns one block of the output and sums the
 // sharing pairs in ascending order in registers; nothing is accumulated in
-// memory.
+// memory.  Key tiles no sharing pair sees are written as zeros without
+// reading the bias or recomputing anything.
 //
 // Work decomposition: 4 waves x 32 query rows (128 rows) of one bias matrix,
 // over a range of key tiles of 64 keys.  Per key tile, for each sharing pair
@@ -65,6 +66,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dbias_bf16_kernel(KArgs a) {
 
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     const int j0 = kt * C::BN;
+    bool seen = false;  // does any sharing pair see a (row, key) of the tile?
+    for (int pb = 0; pb < nb && !seen; ++pb) {
+      const MaskSpec m = make_mask(seq_len(a, a.bias_b == 1 ? pb : bb), a.S, a.causal, a.wl, a.wr);
+      seen = tile_class(m, i0, C::BM, j0, C::BN) != TILE_SKIP;
+    }
+    if (!seen) {
+      // The gradient is zero on the whole tile: 16-byte stores of zeros, eight
+      // threads per row (S is a multiple of 8 and rows are 16-byte aligned, so
+      // a chunk that starts below S lies wholly below it).
+      uint16_t* out = static_cast<uint16_t*>(a.d_bias) + ((size_t)bb * a.bias_h + hh) * a.S * a.S;
+#pragma unroll
+      for (int r = 0; r < C::BM * C::BN / 8 / C::NT; ++r) {
+        const int c = tid + r * C::NT, row = i0 + (c >> 3), key = j0 + (c & 7) * 8;
+        if (row < a.S && key < a.S) *reinterpret_cast<u32x4*>(out + (size_t)row * a.S + key) = u32x4{0, 0, 0, 0};
+      }
+      continue;
+    }
     f32x16 acc[C::BN / 32];
 #pragma unroll
     for (int kb = 0; kb < C::BN / 32; ++kb) acc[kb] = f32x16{};

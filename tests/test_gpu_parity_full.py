@@ -3,7 +3,8 @@
 Each workload runs through the same entry points and launch configuration the
 benchmark times.  The oracle then computes sampled query rows (O, LSE, dQ)
 and sampled keys (dK, dV, summed over every row and head that sees them) in
-float64; the sink gradient is checked for two heads over all batches and rows.
+float64, for the first, the last and a seeded middle query head (and their KV
+heads); the sink gradient is checked for three heads over all batches and rows.
 Padded rows and keys are checked to be exactly zero over the whole tensor.
 """
 import numpy as np
@@ -75,7 +76,9 @@ def test_full_size(cfg, case, drop):
     got = {"o": [], "dq": [], "dk": [], "dv": []}
     ref = {"o": [], "dq": [], "dk": [], "dv": []}
     lse_err = 0.0
-    for h in sorted({0, p.Hq - 1}):
+    # first and last query heads (first and last KV heads) and a seeded middle one
+    heads = sorted({0, int(rng.integers(1, p.Hq - 1)) if p.Hq > 2 else 0, p.Hq - 1})
+    for h in heads:
         b = int(rng.integers(0, B))
         rows = _sample_rows(rng, int(L[b]), S)
         r = oracle.attention_rows(host["q"], host["k"], host["v"], host["do"], b=b, h=h, rows=rows, **kw)
@@ -104,7 +107,7 @@ def test_full_size(cfg, case, drop):
         r = np.concatenate([x.reshape(-1) for x in ref[n]])
         stats[f"{n}_rel_l2"] = gc.rel_l2(a, r)
     if p.softmax_type != "vanilla":
-        heads = sorted({1, p.Hq - 2})
+        heads = sorted({1, int(rng.integers(2, p.Hq - 2)) if p.Hq > 4 else 1, p.Hq - 2})
         ref_dz = np.zeros(len(heads))
         for n, h in enumerate(heads):
             for b in range(B):
