@@ -32,6 +32,18 @@ this module takes these readings (each also listed in the design notes):
     V8_j, LSE_i = m_i + ln l_i.  The normalisation uses the unquantized sum,
     so O is not exactly a convex combination: the quantization of P is part
     of the definition.
+  * FP8 attention backward (HYBRID: the gradient entering the backward, dO,
+    is E5M2): inputs Q8, K8, V8 (E4M3) with descales, dO8 (E5M2) with its
+    descale, the forward's O (bf16 values) and LSE.  With P = exp(s - LSE) on
+    visible pairs, delta_i = dO_i . O_i, dP = dO V^T and dS = P (dP - delta)
+    computed from the dequantized values, the three gradient products take
+    FP8 operands: dV = sum_i E4M3(256 P_ij) / 256 dO_i, and with dS quantized
+    as dS8 = E5M2(s_ds dS) under a caller-given per-tensor scale s_ds (the
+    recipe's delayed scale for dS; the call also returns this step's amax of
+    dS), dK_j = scale / s_ds sum_i dS8_ij Q_i and dQ_i = scale / s_ds sum_j
+    dS8_ij K_j (dK and dV summed over the query heads of the KV head's
+    group).  The sink gradient is the bf16 path's, -sum_i exp(z - LSE_i)
+    delta_i, per head over batches and rows.
 """
 from __future__ import annotations
 
@@ -190,3 +202,61 @@ def attention_fp8_rows(q8, k8, v8, descale_q: float, descale_k: float, descale_v
     pq = fp8_decode(np.where(mask, fp8_encode(256.0 * e, E4M3), 0), E4M3) / 256.0
     o = np.where(l[:, None] > 0, (pq @ v) / np.where(l > 0, l, 1.0)[:, None], 0.0)
     return {"o": o, "lse": lse}
+
+
+def attention_fp8_bwd(q8, k8, v8, o, do8, lse, descale_q: float, descale_k: float, descale_v: float,
+                      descale_do: float, scale_ds: float, *, num_gqa_groups=None, causal=True, window=(-1, -1),
+                      scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None):
+    """FP8 attention backward (reading above).  q8 [B,S,Hq,D], k8 / v8
+    [B,S,Hkv,D] E4M3 codes; do8 [B,S,Hq,Dv] E5M2 codes; o [B,S,Hq,Dv] and lse
+    [B,Hq,S] from the forward (real values).  Returns dq, dk, dv (float64),
+    dalpha [Hq] (None for vanilla), amax_ds, and per (b, h) the intermediates
+    the tolerance bounds use: p [B,Hq,S,S], ds (unquantized dS), p8, ds8 codes,
+    dp_abs (sum_d |dO_id V_jd|, the magnitude dP sums) and delta [B,Hq,S]."""
+    q8, k8, v8, do8 = (np.asarray(x, dtype=np.uint8) for x in (q8, k8, v8, do8))
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    dv_dim = v8.shape[3]
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    q = fp8_decode(q8, E4M3) * float(descale_q)
+    k = fp8_decode(k8, E4M3) * float(descale_k)
+    v = fp8_decode(v8, E4M3) * float(descale_v)
+    do = fp8_decode(do8, E5M2) * float(descale_do)
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    dq = np.zeros((B, S, Hq, dqk))
+    dk = np.zeros((B, S, Hkv, dqk))
+    dv = np.zeros((B, S, Hkv, dv_dim))
+    dalpha = np.zeros(Hq)
+    shape4 = (B, Hq, S, S)
+    out = {"p": np.zeros(shape4), "ds": np.zeros(shape4), "p8": np.zeros(shape4, dtype=np.uint8),
+           "ds8": np.zeros(shape4, dtype=np.uint8), "dp_abs": np.zeros(shape4), "delta": np.zeros((B, Hq, S))}
+    amax = 0.0
+    for b in range(B):
+        L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+        mask = visible_mask(S, L, causal, int(window[0]), int(window[1]))
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            s = scale * (q[b, :, h, :] @ k[b, :, g, :].T)
+            with np.errstate(invalid="ignore", over="ignore"):
+                p = np.where(mask & np.isfinite(lse[b, h])[:, None], np.exp(s - lse[b, h][:, None]), 0.0)
+            delta = np.where(np.arange(S) < L, (do[b, :, h, :] * o[b, :, h, :]).sum(axis=1), 0.0)
+            dp = do[b, :, h, :] @ v[b, :, g, :].T
+            ds = p * (dp - delta[:, None])
+            amax = max(amax, float(np.abs(ds).max()))
+            p8 = np.where(mask, fp8_encode(256.0 * p, E4M3), 0).astype(np.uint8)
+            ds8 = np.where(mask, fp8_encode(float(scale_ds) * ds, E5M2), 0).astype(np.uint8)
+            pq = fp8_decode(p8, E4M3) / 256.0
+            dsq = fp8_decode(ds8, E5M2)
+            dv[b, :, g, :] += pq.T @ do[b, :, h, :]
+            dk[b, :, g, :] += scale / float(scale_ds) * (dsq.T @ q[b, :, h, :])
+            dq[b, :, h, :] = scale / float(scale_ds) * (dsq @ k[b, :, g, :])
+            z = sink_logit(softmax_type, softmax_offset, h)
+            if z is not None:
+                rows = np.isfinite(lse[b, h]) & (np.arange(S) < L)
+                dalpha[h] += -float(np.sum(np.where(rows, np.exp(z - np.where(rows, lse[b, h], 0.0)) * delta, 0.0)))
+            out["p"][b, h], out["ds"][b, h], out["p8"][b, h], out["ds8"][b, h] = p, ds, p8, ds8
+            out["dp_abs"][b, h] = np.abs(do[b, :, h, :]) @ np.abs(v[b, :, g, :]).T
+            out["delta"][b, h] = delta
+    out.update(dq=dq, dk=dk, dv=dv, dalpha=None if softmax_type == "vanilla" else dalpha, amax_ds=amax)
+    return out

@@ -8,6 +8,11 @@
   attention   LSE equals the unquantized oracle's; O lies within the bound the
               E4M3 rounding of P allows around the unquantized oracle's O;
               scalar loops over a tiny case reproduce O and the P codes
+  backward    equal to the unquantized oracle where no quantization rounds;
+              the hand-worked example of tests/golden/fp8_bwd_hand.json;
+              codes are nearest values (brute force) and the gradients lie
+              within the E4M3 / E5M2 rounding bounds around the unquantized
+              ones; the sink gradient equals the unquantized one; scalar loops
   mutants     planted mistakes in copies of the module each fail a pin
 """
 import math
@@ -174,8 +179,171 @@ def pin_attention_rows(m):
                     assert np.abs(r["o"] - full["o"][b, rows, h]).max() <= 1e-12
 
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_bwd_hand.json")
+
+
+def _bwd_exact_case(m, kind, seed):
+    """GQA (Hq 4, Hkv 2), S 16, d 8, no mask, where every quantization is
+    exact: all scores of a row are equal (kind "q0": Q = 0; kind "krow": the
+    16 keys of a KV head are one vector), so P = 1/16 and 256 P = 16; each V
+    column holds eight 0s and eight 2s (mean 1); dO rows are one-hot with
+    values +-1, +-2, so dS = P (dP - delta) = +-dO / 16 and with s_ds = 16 the
+    E5M2 codes are exact.  Descales differ from 1 (the codes hold 2 Q, 2 K,
+    2 V, 4 dO)."""
+    rng = np.random.default_rng(seed)
+    B, S, Hq, Hkv, d = 1, 16, 4, 2, 8
+    q = np.zeros((B, S, Hq, d)) if kind == "q0" else rng.integers(-3, 4, (B, S, Hq, d)).astype(float)
+    if kind == "q0":
+        k = rng.integers(-3, 4, (B, S, Hkv, d)).astype(float)
+    else:
+        k = np.broadcast_to(rng.integers(-3, 4, (B, 1, Hkv, d)).astype(float), (B, S, Hkv, d)).copy()
+    v = np.zeros((B, S, Hkv, d))
+    for g in range(Hkv):
+        for c in range(d):
+            v[0, rng.permutation(S)[:8], g, c] = 2.0
+    do = np.zeros((B, S, Hq, d))
+    for i in range(S):
+        for h in range(Hq):
+            do[0, i, h, rng.integers(0, d)] = rng.choice([-2.0, -1.0, 1.0, 2.0])
+    codes = [m.fp8_encode(2 * q, m.E4M3), m.fp8_encode(2 * k, m.E4M3), m.fp8_encode(2 * v, m.E4M3),
+             m.fp8_encode(4 * do, m.E5M2)]
+    return (q, k, v, do), codes
+
+
+def pin_bwd_exact(m):
+    """Where no quantization rounds, the FP8 backward equals the unquantized
+    float64 backward (oracle.attention) on the same values."""
+    for kind, seed in (("q0", 3400), ("krow", 3401)):
+        (q, k, v, do), (q8, k8, v8, do8) = _bwd_exact_case(m, kind, seed)
+        ex = oracle.attention(q, k, v, do, num_gqa_groups=2, causal=False)
+        r = m.attention_fp8_bwd(q8, k8, v8, ex["o"], do8, ex["lse"], 0.5, 0.5, 0.5, 0.25, 16.0, num_gqa_groups=2,
+                                causal=False)
+        for n in ("dq", "dk", "dv"):
+            err = np.abs(r[n] - ex[n]).max()
+            assert err <= 1e-12 * (1 + np.abs(ex[n]).max()), (kind, n, err)
+        assert np.abs(r["dq" if kind == "q0" else "dk"]).max() > 0.1  # the case exercises the product
+        assert abs(r["amax_ds"] - 2.0 / 16) <= 1e-12
+
+
+def pin_bwd_hand(m):
+    """The hand-worked example of tests/golden/fp8_bwd_hand.json: dS rounded
+    to E5M2 (1/3 -> 0.3125) and P to E4M3 (256/3 -> 88) where they enter dQ
+    and dV."""
+    import json
+    gold = json.load(open(GOLDEN))
+    S, d = 4, 4
+    q8 = np.zeros((1, S, 1, d), dtype=np.uint8)
+    k8 = m.fp8_encode(np.eye(S).reshape(1, S, 1, d), m.E4M3)
+    v = np.zeros((1, S, 1, d))
+    v[0, :, 0, 0] = np.arange(S)
+    do = np.zeros((1, S, 1, d))
+    do[0, :, 0, 0] = 1.0
+    o = np.zeros((1, S, 1, d))
+    o[0, :, 0, 0] = [0.0, 0.5, 1.0, 1.5]
+    lse = np.log(np.arange(1, S + 1, dtype=float)).reshape(1, 1, S)
+    r = m.attention_fp8_bwd(q8, k8, m.fp8_encode(v, m.E4M3), o, m.fp8_encode(do, m.E5M2), lse, 1.0, 1.0, 1.0, 1.0,
+                            1.0, num_gqa_groups=1, causal=True)
+    assert np.abs(r["dq"][0, :, 0, :] - np.array(gold["dq"])).max() <= 1e-12
+    assert np.abs(r["dv"][0, :, 0, 0] - np.array(gold["dv_first_component"])).max() <= 1e-12
+    assert np.abs(r["dv"][0, :, 0, 1:]).max() == 0 and np.abs(r["dk"]).max() == 0
+
+
+def _nearest_ok(m, codes, x, fmt):
+    """Each code's value is a nearest finite value of the format to x (brute
+    force over all codes; x within the finite range)."""
+    vals = m.fp8_decode(np.arange(256), fmt)
+    vals = vals[np.isfinite(vals)]
+    best = np.abs(x.reshape(-1, 1) - vals.reshape(1, -1)).min(axis=1)
+    got = np.abs(m.fp8_decode(codes.reshape(-1), fmt) - x.reshape(-1))
+    return np.all(got <= best * (1 + 1e-12) + 1e-300)
+
+
+def pin_bwd_bound(m):
+    """Random inputs: d_softmax_offset equals the unquantized oracle's; the P
+    and dS codes are nearest values of E4M3 / E5M2 (brute force); dV, dK, dQ
+    lie within the rounding bounds around the unquantized gradients:
+    |P8/256 - P| <= max(2^-4 P, 2^-18) and |dS8/s - dS| <= max(2^-3 |dS|,
+    2^-17 / s), carried through dV = sum P dO, dK = scale sum dS Q,
+    dQ = scale sum dS K."""
+    dq_, dk_, dv_, ddo = 0.125, 0.25, 0.0625, 1.0 / 64
+    for ci, (causal, win, sl) in enumerate(MASKS):
+        for st in oracle.SOFTMAX_TYPES:
+            q8, k8, v8, alpha = _case(3500 + ci)
+            rng = np.random.default_rng(3600 + ci)
+            do8 = m.fp8_encode(rng.standard_normal(q8.shape) * 64, m.E5M2)
+            kw = dict(num_gqa_groups=2, causal=causal, window=win, softmax_type=st, softmax_offset=alpha,
+                      seqlens=None if sl is None else np.array(sl))
+            q, k, v = (m.fp8_decode(x, m.E4M3) * s for x, s in ((q8, dq_), (k8, dk_), (v8, dv_)))
+            do = m.fp8_decode(do8, m.E5M2) * ddo
+            ex = oracle.attention(q, k, v, do, **kw)
+            s_ds = 64.0
+            r = m.attention_fp8_bwd(q8, k8, v8, ex["o"], do8, ex["lse"], dq_, dk_, dv_, ddo, s_ds, **kw)
+            if st == "vanilla":
+                assert r["dalpha"] is None
+            else:
+                assert np.abs(r["dalpha"] - ex["dalpha"]).max() <= 1e-12 * (1 + np.abs(ex["dalpha"]).max())
+            vis = r["p"] > 0
+            assert _nearest_ok(m, r["p8"][vis], 256.0 * r["p"][vis], m.E4M3)
+            assert _nearest_ok(m, r["ds8"][vis], s_ds * r["ds"][vis], m.E5M2)
+            scale = 1.0 / math.sqrt(q.shape[3])
+            ep = np.maximum(2.0 ** -4 * r["p"], 2.0 ** -18) * vis
+            eds = np.maximum(2.0 ** -3 * np.abs(r["ds"]), 2.0 ** -17 / s_ds) * vis
+            B, S, Hq = q8.shape[:3]
+            bdv, bdk, bdq = np.zeros(ex["dv"].shape), np.zeros(ex["dk"].shape), np.zeros(ex["dq"].shape)
+            for b in range(B):
+                for h in range(Hq):
+                    g = h // 2
+                    bdv[b, :, g] += ep[b, h].T @ np.abs(do[b, :, h])
+                    bdk[b, :, g] += scale * eds[b, h].T @ np.abs(q[b, :, h])
+                    bdq[b, :, h] = scale * eds[b, h] @ np.abs(k[b, :, g])
+            for n, bound in (("dv", bdv), ("dk", bdk), ("dq", bdq)):
+                err = np.abs(r[n] - ex[n])
+                assert (err <= bound * (1 + 1e-9) + 1e-13).all(), (ci, st, n, float((err - bound).max()))
+            assert abs(r["amax_ds"] - float(np.abs(r["ds"]).max())) == 0
+
+
+def pin_bwd_loops(m):
+    """Scalar loops on a tiny case (off-by-one sink, causal): P, delta, dP,
+    dS, the codes and the three gradients element by element."""
+    q8, k8, v8, alpha = _case(3700, B=1, S=4, Hq=2, Hkv=1, d=2)
+    rng = np.random.default_rng(3701)
+    do8 = m.fp8_encode(rng.standard_normal(q8.shape) * 8, m.E5M2)
+    o = rng.standard_normal((1, 4, 2, 2))
+    lse = rng.standard_normal((1, 2, 4)) + 2.0
+    dq_, dk_, dv_, ddo, s_ds = 0.5, 0.25, 2.0, 0.125, 8.0
+    r = m.attention_fp8_bwd(q8, k8, v8, o, do8, lse, dq_, dk_, dv_, ddo, s_ds, num_gqa_groups=1, causal=True,
+                            softmax_type="off_by_one")
+    e4 = lambda c: float(m.fp8_decode([c], m.E4M3)[0])  # noqa: E731
+    e5 = lambda c: float(m.fp8_decode([c], m.E5M2)[0])  # noqa: E731
+    S, D, scale = 4, 2, 1.0 / math.sqrt(2)
+    dq = np.zeros((S, 2, D))
+    dk = np.zeros((S, D))
+    dv = np.zeros((S, D))
+    dz = [0.0, 0.0]
+    for h in range(2):
+        for i in range(S):
+            delta = sum(e5(do8[0, i, h, d]) * ddo * o[0, i, h, d] for d in range(D))
+            dz[h] -= math.exp(0.0 - lse[0, h, i]) * delta
+            for j in range(i + 1):
+                s = scale * sum(e4(q8[0, i, h, d]) * dq_ * e4(k8[0, j, 0, d]) * dk_ for d in range(D))
+                p = math.exp(s - lse[0, h, i])
+                dp = sum(e5(do8[0, i, h, d]) * ddo * e4(v8[0, j, 0, d]) * dv_ for d in range(D))
+                ds = p * (dp - delta)
+                c_p = int(m.fp8_encode([256.0 * p], m.E4M3)[0])
+                c_ds = int(m.fp8_encode([s_ds * ds], m.E5M2)[0])
+                assert c_p == r["p8"][0, h, i, j] and c_ds == r["ds8"][0, h, i, j]
+                for d in range(D):
+                    dv[j, d] += e4(c_p) / 256.0 * e5(do8[0, i, h, d]) * ddo
+                    dk[j, d] += scale / s_ds * e5(c_ds) * e4(q8[0, i, h, d]) * dq_
+                    dq[i, h, d] += scale / s_ds * e5(c_ds) * e4(k8[0, j, 0, d]) * dk_
+    assert np.abs(r["dv"][0, :, 0] - dv).max() <= 1e-12 * (1 + np.abs(dv).max())
+    assert np.abs(r["dk"][0, :, 0] - dk).max() <= 1e-12 * (1 + np.abs(dk).max())
+    assert np.abs(r["dq"][0] - dq).max() <= 1e-12 * (1 + np.abs(dq).max())
+    assert np.abs(r["dalpha"] - np.array(dz)).max() <= 1e-12 * (1 + np.abs(dz).max())
+
+
 PINS = [pin_decode, pin_encode, pin_saturation_and_nan, pin_recipe, pin_attention_bound, pin_attention_loops,
-        pin_attention_rows]
+        pin_attention_rows, pin_bwd_exact, pin_bwd_hand, pin_bwd_bound, pin_bwd_loops]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -192,7 +360,7 @@ MUTANTS = {
                         "val = np.where(e == emax, np.nan, val)"),
     "p_scale_448": ("codes = np.where(mask, fp8_encode(256.0 * e, E4M3), 0).astype(np.uint8)",
                     "codes = np.where(mask, fp8_encode(448.0 * e, E4M3), 0).astype(np.uint8)"),
-    "v_descale_dropped": ("v = fp8_decode(v8, E4M3) * float(descale_v)", "v = fp8_decode(v8, E4M3)"),
+    "v_descale_dropped": ("v = fp8_decode(v8, E4M3) * float(descale_v)", "v = fp8_decode(v8, E4M3)", "all"),
     "history_oldest_first": ("h = np.concatenate([[float(new_amax)], np.asarray(history, dtype=np.float64)[:-1]])",
                              "h = np.concatenate([np.asarray(history, dtype=np.float64)[1:], [float(new_amax)]])"),
     "margin_ignored": ("scale = fp8_max(fmt) / amax / (2.0 ** margin)", "scale = fp8_max(fmt) / amax"),
@@ -200,18 +368,36 @@ MUTANTS = {
                             "all"),
     "rows_wrong_kv_head": ("k = fp8_decode(k8[b, :, g, :], E4M3) * float(descale_k)",
                            "k = fp8_decode(k8[b, :, h % k8.shape[2], :], E4M3) * float(descale_k)"),
+    "bwd_ds_scale_kept": ("dq[b, :, h, :] = scale / float(scale_ds) * (dsq @ k[b, :, g, :])",
+                          "dq[b, :, h, :] = scale * (dsq @ k[b, :, g, :])"),
+    "bwd_ds_as_e4m3": [("ds8 = np.where(mask, fp8_encode(float(scale_ds) * ds, E5M2), 0)",
+                        "ds8 = np.where(mask, fp8_encode(float(scale_ds) * ds, E4M3), 0)"),
+                       ("dsq = fp8_decode(ds8, E5M2)", "dsq = fp8_decode(ds8, E4M3)")],
+    "bwd_p_unquantized": ("dv[b, :, g, :] += pq.T @ do[b, :, h, :]", "dv[b, :, g, :] += p.T @ do[b, :, h, :]"),
+    "bwd_delta_dropped": ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
+    "bwd_p_row_max": ("np.exp(s - lse[b, h][:, None])",
+                      "np.exp(s - np.where(mask, s, -np.inf).max(axis=1)[:, None])"),
+    "bwd_dk_no_group_sum": ("dk[b, :, g, :] += scale", "dk[b, :, g, :] = scale"),
+    "bwd_dq_wrong_kv_head": ("dq[b, :, h, :] = scale / float(scale_ds) * (dsq @ k[b, :, g, :])",
+                             "dq[b, :, h, :] = scale / float(scale_ds) * (dsq @ k[b, :, (g + 1) % Hkv, :])"),
+    "bwd_do_descale_dropped": ("do = fp8_decode(do8, E5M2) * float(descale_do)", "do = fp8_decode(do8, E5M2)"),
+    "bwd_dalpha_sign": ("dalpha[h] += -float(", "dalpha[h] += float("),
+    "bwd_dk_takes_k": ("(dsq.T @ q[b, :, h, :])", "(dsq.T @ k[b, :, g, :])"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_fp8_mutant_is_caught(name):
     src = open(SRC).read()
-    old, new = MUTANTS[name][:2]
-    every = len(MUTANTS[name]) > 2
-    assert src.count(old) >= 1 and (every or src.count(old) == 1), name
+    edits = MUTANTS[name] if isinstance(MUTANTS[name], list) else [MUTANTS[name]]
+    for edit in edits:
+        old, new = edit[:2]
+        every = len(edit) > 2
+        assert src.count(old) >= 1 and (every or src.count(old) == 1), name
+        src = src.replace(old, new)
     mod = types.ModuleType("fp8_mutant")
     mod.__package__ = "oracle"
-    exec(compile(src.replace(old, new), "fp8_mutant.py", "exec"), mod.__dict__)
+    exec(compile(src, "fp8_mutant.py", "exec"), mod.__dict__)
     for pin in PINS:
         try:
             pin(mod)
