@@ -79,7 +79,7 @@ extern "C" {
 /* params.dtype */
 #define ATTN_F32 0
 #define ATTN_BF16 1
-#define ATTN_FP8 2  /* attn_fwd_fp8 only: E4M3 Q, K, V with descales; O is bf16 */
+#define ATTN_FP8 2  /* attn_fwd_fp8 / attn_bwd_fp8 only: E4M3 Q, K, V (E5M2 dO) with descales */
 /* 8-bit formats (OCP 8-bit floating point spec) */
 #define ATTN_FP8_E4M3 0
 #define ATTN_FP8_E5M2 1
@@ -259,10 +259,17 @@ int attn_bwd_noalloc(const struct attn_params* p, const void* q, const void* k, 
  *   - per-tensor scaling: codes = encode(x * scale), value = code * descale;
  *   - the forward quantizes P relative to the exact row max,
  *     P8 = E4M3(256 exp(s - m_i)), and normalises by the unquantized sum:
- *     O_i = descale_v / (256 l_i) sum_j P8_ij V8_j.
- * Built: the forward (E4M3 Q, K, V; bf16 O; fp32 LSE), the quantization with
- * amax and the delayed-scaling scale update.  Not built: an FP8 backward
- * (attn_bwd with ATTN_FP8 returns ATTN_ERR_UNSUPPORTED). */
+ *     O_i = descale_v / (256 l_i) sum_j P8_ij V8_j;
+ *   - the backward (HYBRID: dO arrives as E5M2 codes) recomputes
+ *     P = exp(s - LSE), delta_i = dO_i . O_i, dP = dO V^T, dS = P (dP - delta)
+ *     in fp32 and feeds FP8 operands to the gradient products:
+ *     dV = sum_i E4M3(256 P_ij) / 256 dO_i, and with a per-tensor dS scale
+ *     s_ds (the recipe's delayed scale; the call returns this step's amax of
+ *     dS) dK = scale / s_ds sum_i E5M2(s_ds dS_ij) Q_i,
+ *     dQ = scale / s_ds sum_j E5M2(s_ds dS_ij) K_j.
+ * Built: forward, backward, the quantization with amax and the
+ * delayed-scaling scale update.  attn_fwd / attn_bwd with ATTN_FP8 return
+ * ATTN_ERR_UNSUPPORTED (use the entry points below). */
 
 /* FP8 forward.  p->dtype = ATTN_FP8; Dqk = Dv in {64, 128}; dropout_p = 0.
  * q, k, v: E4M3 codes (1 byte each) in the layouts of attn_fwd, 16-byte
@@ -275,6 +282,22 @@ int attn_fwd_fp8(const struct attn_params* p, const void* q, const void* k, cons
                  const float* descale_qkv, const float* softmax_offset, const int32_t* seqlens,
                  const int32_t* seq_offsets, void* o, float* lse, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/* FP8 backward.  p as attn_fwd_fp8.  q, k, v: the forward's E4M3 codes; o:
+ * the forward's bf16 output; d_o: E5M2 codes of dO ([B,S,Hq,Dv] / [T,Hq,Dv]);
+ * all 16-byte aligned.  lse: the forward's [B,Hq,S].  descale_qkvdo: device
+ * float[4], the descales of q, k, v, d_o.  ds_scale: device float[1], the
+ * scale of dS before its E5M2 encoding.  amax_ds: device float[1], receives
+ * max |dS| over the visible pairs (overwritten).  dq, dk, dv: bf16 outputs in
+ * the layouts of q, k, v (padded rows and keys written as zeros).
+ * d_softmax_offset as attn_bwd.  workspace: attn_bwd_workspace_size(p) bytes,
+ * 256-byte aligned (delta, LSE log2 e, sink partials, and K, Q, dO transposed
+ * per head).  Deterministic: no atomics on the gradients. */
+int attn_bwd_fp8(const struct attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                 const void* d_o, const float* lse, const float* descale_qkvdo, const float* ds_scale,
+                 float* amax_ds, const float* softmax_offset, const int32_t* seqlens,
+                 const int32_t* seq_offsets, void* dq, void* dk, void* dv, float* d_softmax_offset,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-tensor quantization: out[i] = encode(clamp(x[i] * scale[0], -max,
  * max)) in format fmt (ATTN_FP8_E4M3 / ATTN_FP8_E5M2), and amax[0] = max |x|

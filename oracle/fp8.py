@@ -260,3 +260,74 @@ def attention_fp8_bwd(q8, k8, v8, o, do8, lse, descale_q: float, descale_k: floa
             out["delta"][b, h] = delta
     out.update(dq=dq, dk=dk, dv=dv, dalpha=None if softmax_type == "vanilla" else dalpha, amax_ds=amax)
     return out
+
+
+def _bwd_rows_common(q8, k8, v8, o, do8, lse, descales, *, b, h, rows, keys, num_gqa_groups, causal, window,
+                     scale_factor, seqlens):
+    """Scores and gradient pieces of the FP8 backward for rows x keys of one
+    (batch b, query head h): p, dp, delta of the rows, ds and the masks."""
+    from .sdpa_oracle import visible_rows
+    q8, k8, v8, do8 = (np.asarray(x, dtype=np.uint8) for x in (q8, k8, v8, do8))
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    scale = (1.0 / math.sqrt(dqk)) if not scale_factor else float(scale_factor)
+    dq_, dk_, dv_, ddo = (float(x) for x in descales)
+    g = kv_head(h, Hq, Hkv)
+    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    mask = visible_rows(rows, S, L, causal, int(window[0]), int(window[1]))[:, keys]
+    q = fp8_decode(q8[b, rows, h, :], E4M3) * dq_
+    k = fp8_decode(k8[b, keys, g, :], E4M3) * dk_
+    v = fp8_decode(v8[b, keys, g, :], E4M3) * dv_
+    do = fp8_decode(do8[b, rows, h, :], E5M2) * ddo
+    lse_r = np.asarray(lse, dtype=np.float64)[b, h, rows]
+    s = scale * (q @ k.T)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(mask & np.isfinite(lse_r)[:, None], np.exp(s - lse_r[:, None]), 0.0)
+    delta = np.where(rows < L, (do * np.asarray(o, dtype=np.float64)[b, rows, h, :]).sum(axis=1), 0.0)
+    dp = do @ v.T
+    ds = p * (dp - delta[:, None])
+    return dict(q=q, k=k, do=do, p=p, ds=ds, mask=mask, scale=scale, dp_abs=np.abs(do) @ np.abs(v).T, delta=delta)
+
+
+def attention_fp8_bwd_rows(q8, k8, v8, o, do8, lse, descale_q, descale_k, descale_v, descale_do, scale_ds, *, b, h,
+                           rows, num_gqa_groups=None, causal=True, window=(-1, -1), scale_factor=None, seqlens=None):
+    """dQ of attention_fp8_bwd for selected query rows of one (batch b, query
+    head h), at any length: a row's dQ needs only its own scores against all
+    keys.  Returns dq [n, D] and the row pieces p, ds, ds8, dp_abs, delta."""
+    S = np.asarray(q8).shape[1]
+    c = _bwd_rows_common(q8, k8, v8, o, do8, lse, (descale_q, descale_k, descale_v, descale_do), b=b, h=h,
+                         rows=rows, keys=np.arange(S), num_gqa_groups=num_gqa_groups, causal=causal, window=window,
+                         scale_factor=scale_factor, seqlens=seqlens)
+    ds8 = np.where(c["mask"], fp8_encode(float(scale_ds) * c["ds"], E5M2), 0).astype(np.uint8)
+    dq = c["scale"] / float(scale_ds) * (fp8_decode(ds8, E5M2) @ c["k"])
+    return {"dq": dq, "p": c["p"], "ds": c["ds"], "ds8": ds8, "dp_abs": c["dp_abs"], "delta": c["delta"]}
+
+
+def attention_fp8_bwd_keys(q8, k8, v8, o, do8, lse, descale_q, descale_k, descale_v, descale_do, scale_ds, *, b, g,
+                           keys, num_gqa_groups=None, causal=True, window=(-1, -1), scale_factor=None, seqlens=None):
+    """dK, dV of attention_fp8_bwd for selected keys of one (batch b, KV head
+    g), summed over every row and query head of the group that sees them.
+    Returns dk, dv [n, D] and, per query head of the group, the pieces
+    (p, ds, p8, ds8, dp_abs, delta) as lists."""
+    q8 = np.asarray(q8, dtype=np.uint8)
+    B, S, Hq, dqk = q8.shape
+    Hkv = np.asarray(k8).shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+    G = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    dk = np.zeros((len(keys), dqk))
+    dv = np.zeros((len(keys), np.asarray(v8).shape[3]))
+    parts = {n: [] for n in ("p", "ds", "p8", "ds8", "dp_abs", "delta")}
+    for h in range(g * G, (g + 1) * G):
+        c = _bwd_rows_common(q8, k8, v8, o, do8, lse, (descale_q, descale_k, descale_v, descale_do), b=b, h=h,
+                             rows=np.arange(S), keys=keys, num_gqa_groups=Hkv, causal=causal, window=window,
+                             scale_factor=scale_factor, seqlens=seqlens)
+        p8 = np.where(c["mask"], fp8_encode(256.0 * c["p"], E4M3), 0).astype(np.uint8)
+        ds8 = np.where(c["mask"], fp8_encode(float(scale_ds) * c["ds"], E5M2), 0).astype(np.uint8)
+        dv += (fp8_decode(p8, E4M3) / 256.0).T @ c["do"]
+        dk += c["scale"] / float(scale_ds) * (fp8_decode(ds8, E5M2).T @ c["q"])
+        for n, x in (("p", c["p"]), ("ds", c["ds"]), ("p8", p8), ("ds8", ds8), ("dp_abs", c["dp_abs"]),
+                     ("delta", c["delta"])):
+            parts[n].append(x)
+    return {"dk": dk, "dv": dv, **parts}

@@ -64,6 +64,8 @@ EXPORTS = {
                                         _vp, _vp, _vp, _vp, _vp, _vp]),
     "attn_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]),
+    "attn_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "attn_fp8_quantize": (ctypes.c_int, [_vp, _c_i32, ctypes.c_size_t, _c_i32, _vp, _vp, _vp, _vp]),
     "attn_fp8_update_scale": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, _vp]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -550,6 +552,78 @@ def attn_fwd_fp8(q8, k8, v8, descale_qkv, *, num_gqa_groups=None, attn_mask_type
                                 _ptr(seqlens), _ptr(seq_offsets), _ptr(o), _ptr(l), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)), "attn_fwd_fp8")
     return o, l
+
+
+def attn_bwd_fp8(q8, k8, v8, o, do8, lse, descale_qkvdo, ds_scale, *, num_gqa_groups=None, attn_mask_type="causal",
+                 window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None, seqlens=None,
+                 seq_offsets=None, max_seqlen=None, want_d_offset=None, outs=None, amax=None, workspace=None,
+                 stream=None, check_seqlens=True):
+    """FP8 backward: q8, k8, v8 the forward's E4M3 codes, o its bf16 output,
+    do8 E5M2 codes of dO (q's layout with Dv), lse the forward's LSE;
+    descale_qkvdo float32 device [4]; ds_scale float32 device [1] (the scale
+    of dS before its E5M2 encoding).  Returns (dQ, dK, dV bf16,
+    d_softmax_offset or None, amax of dS float32 [1])."""
+    torch = _torch()
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8), ("do8", do8)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor (FP8 codes)")
+    for name, t, n in (("descale_qkvdo", descale_qkvdo, 4), ("ds_scale", ds_scale, 1)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or t.numel() != n:
+            raise ValueError(f"{name} must be a float32 device tensor of {n} element(s)")
+    with _on_stream(stream):
+        packed = _layout(q8, seq_offsets, seqlens, max_seqlen, check_seqlens)
+        if packed is None:
+            B, S, Hq, dqk = q8.shape
+            Hkv = k8.shape[2] if num_gqa_groups is None else int(num_gqa_groups)
+        else:
+            B, S = packed
+            Hq, dqk = q8.shape[1], q8.shape[2]
+            Hkv = k8.shape[1] if num_gqa_groups is None else int(num_gqa_groups)
+        lead = tuple(q8.shape[:-2])
+        if tuple(k8.shape) != lead + (Hkv, dqk) or tuple(v8.shape[:-1]) != lead + (Hkv,):
+            raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v8.shape)}")
+        p = make_params(B, S, Hq, Hkv, dqk, v8.shape[-1], "fp8", attn_mask_type, window_size, scale_factor,
+                        softmax_type)
+        if check_seqlens and packed is None:
+            _check_seqlens(seqlens, B, S)
+        o_shape = tuple(q8.shape[:-1]) + (p.head_dim_v,)
+        if tuple(do8.shape) != o_shape:
+            raise ValueError(f"do8 must have shape {list(o_shape)}")
+        if not o.is_cuda or not o.is_contiguous() or o.dtype != torch.bfloat16 or tuple(o.shape) != o_shape:
+            raise ValueError(f"o must be a contiguous bf16 {list(o_shape)} device tensor")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous() \
+                or not lse.is_cuda:
+            raise ValueError("lse must be a contiguous float32 [B,Hq,S] device tensor")
+        offs = _sink_offsets(softmax_offset, Hq, q8) if softmax_type == "learnable" else None
+        want = softmax_type == "learnable" or (softmax_type == "off_by_one" and bool(want_d_offset))
+        if outs is not None:
+            dq, dk, dv, doff = outs
+            for name, t, shape in (("dq", dq, q8.shape), ("dk", dk, k8.shape), ("dv", dv, v8.shape)):
+                _check_buffer(t, shape, torch.bfloat16, name)
+            if want and doff is None:
+                doff = torch.empty(Hq, dtype=torch.float32, device=q8.device)
+            elif want:
+                _check_buffer(doff, (Hq,), torch.float32, "d_softmax_offset")
+        else:
+            dq = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+            dk = torch.empty(k8.shape, dtype=torch.bfloat16, device=q8.device)
+            dv = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device)
+            doff = torch.empty(Hq, dtype=torch.float32, device=q8.device) if want else None
+        if not want:
+            doff = None
+        amax = torch.empty(1, dtype=torch.float32, device=q8.device) if amax is None else amax
+        _check_buffer(amax, (1,), torch.float32, "amax")
+        lib = load_library()
+        ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(p))
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q8.device)
+        elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must be a device tensor of at least {ws_bytes} bytes")
+        _check(lib.attn_bwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(do8), _ptr(lse),
+                                _ptr(descale_qkvdo), _ptr(ds_scale), _ptr(amax), _ptr(offs), _ptr(seqlens),
+                                _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doff), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)), "attn_bwd_fp8")
+    return dq, dk, dv, doff, amax
 
 
 def debug_tile_map(p: Params, seqlens, block_m, block_n, stream=None):

@@ -51,7 +51,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Rows per sink-gradient partial: the bf16 dQ kernel writes one per wave
 // (32 rows), the fp32 pre-pass one per 64-row block; the workspace holds the
 // larger count.
-int chunk_rows(const attn_params* p) { return p->dtype == ATTN_BF16 ? kDqChunkRows : kPreRows; }
+int chunk_rows(const attn_params* p) { return p->dtype == ATTN_F32 ? kPreRows : kDqChunkRows; }
 int n_chunks(const attn_params* p) { return (p->seqlen + chunk_rows(p) - 1) / chunk_rows(p); }
 int max_chunks(const attn_params* p) { return (p->seqlen + kDqChunkRows - 1) / kDqChunkRows; }
 size_t delta_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * p->seqlen * sizeof(float)); }
@@ -147,7 +147,10 @@ size_t attn_fwd_workspace_size(const attn_params* p) {
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
-  if (attn_validate(p) != ATTN_OK || p->dtype == ATTN_FP8) return 0;
+  if (attn_validate(p) != ATTN_OK) return 0;
+  if (p->dtype == ATTN_FP8)
+    return 2 * delta_bytes(p) + dz_bytes(p) +
+           align256(fp8_bwd_transposed_bytes(p->batch, p->seqlen, p->num_heads, p->num_gqa_groups, p->head_dim_qk));
   return 2 * delta_bytes(p) + dz_bytes(p) + kv_part_bytes(p);
 }
 
@@ -216,7 +219,7 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   if (stage < 0 || stage > ATTN_BWD_STAGE_OFFSET_GRAD) return ATTN_ERR_INVALID_ARG;
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
-  if (p->dtype == ATTN_FP8) return ATTN_ERR_UNSUPPORTED;  // FP8: forward only
+  if (p->dtype == ATTN_FP8) return ATTN_ERR_UNSUPPORTED;  // FP8: through attn_bwd_fp8 only
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!softmax_offset || !d_softmax_offset)) return ATTN_ERR_INVALID_ARG;
   if (p->softmax_type == ATTN_SOFTMAX_VANILLA && d_softmax_offset) return ATTN_ERR_INVALID_ARG;
@@ -331,6 +334,54 @@ int attn_fwd_fp8(const attn_params* p, const void* q, const void* k, const void*
   a.out_lse = lse;
   a.vt = static_cast<uint8_t*>(workspace);
   return hip_status(launch_fwd_fp8(a, p->head_dim_qk, p->head_dim_v, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_fp8(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                 const float* lse, const float* descale_qkvdo, const float* ds_scale, float* amax_ds,
+                 const float* softmax_offset, const int32_t* seqlens, const int32_t* seq_offsets, void* dq, void* dk,
+                 void* dv, float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = attn_validate(p);
+  if (rc != ATTN_OK) return rc;
+  if (p->dtype != ATTN_FP8) return ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !d_o || !lse || !descale_qkvdo || !ds_scale || !amax_ds || !dq || !dk || !dv)
+    return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_LEARNABLE && (!softmax_offset || !d_softmax_offset)) return ATTN_ERR_INVALID_ARG;
+  if (p->softmax_type == ATTN_SOFTMAX_VANILLA && d_softmax_offset) return ATTN_ERR_INVALID_ARG;
+  // 16-byte row pieces of Q, K, V, dO are read directly; O rows in 8- or 16-byte pieces.
+  const uintptr_t in = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(d_o) |
+                       reinterpret_cast<uintptr_t>(o);
+  if ((in & 15) != 0) return ATTN_ERR_INVALID_ARG;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_bwd_workspace_size(p)) return ATTN_ERR_WORKSPACE;
+  KArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.fp8_descale = descale_qkvdo;
+  a.ds_scale = ds_scale;
+  a.amax_out = amax_ds;
+  a.softmax_offset = softmax_offset;
+  a.seqlens = seqlens;
+  a.seq_offsets = seq_offsets;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.d_offset = d_softmax_offset;
+  char* ws = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(ws + delta_bytes(p));
+  a.dz_partial = reinterpret_cast<float*>(ws + 2 * delta_bytes(p));
+  // K^T, Q^T, dO^T: [B, heads, D, S_pad] codes each
+  const size_t s_pad = (size_t)((p->seqlen + 63) / 64) * 64, d = (size_t)p->head_dim_qk;
+  a.kt_t = reinterpret_cast<uint8_t*>(ws + 2 * delta_bytes(p) + dz_bytes(p));
+  a.qt_t = a.kt_t + (size_t)p->batch * p->num_gqa_groups * d * s_pad;
+  a.dot_t = a.qt_t + (size_t)p->batch * p->num_heads * d * s_pad;
+  return hip_status(launch_bwd_fp8(a, p->head_dim_qk, p->head_dim_v, static_cast<hipStream_t>(stream)));
 }
 
 int attn_fp8_quantize(const void* x, int32_t x_dtype, size_t n, int32_t fmt, const float* scale, uint8_t* out,

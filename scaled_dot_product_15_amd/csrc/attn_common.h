@@ -52,8 +52,13 @@ struct KArgs {
   void* d_bias;         // its gradient, same shape, or nullptr
   int bias_b, bias_h;   // 1 (shared) or B / Hq
   float inv_scale;      // 1 / scale: the kernels add bias / scale to the unscaled scores
-  const float* fp8_descale;  // FP8 forward: [3] descales of Q, K, V (device)
+  const float* fp8_descale;  // FP8: descales of Q, K, V (and dO in the backward), device
   uint8_t* vt;          // FP8 forward workspace: V^T [B, Hkv, Dv, S_pad] with permuted key order
+  uint8_t* kt_t;        // FP8 backward workspace: K^T [B, Hkv, D, S_pad], permuted key order
+  uint8_t* qt_t;        //   Q^T [B, Hq, D, S_pad], permuted row order
+  uint8_t* dot_t;       //   dO^T [B, Hq, Dv, S_pad], permuted row order
+  const float* ds_scale;  // FP8 backward: per-tensor scale of dS before its E5M2 encoding (device, [1])
+  float* amax_out;      // FP8 backward: max |dS| (device, [1]; cleared by the launcher)
   int s_pad;            // S rounded up to the FP8 key tile (64)
   int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
   float drop_scale;     // 1 / (1 - drop_t / 256)
@@ -121,6 +126,18 @@ __device__ __forceinline__ float halves_sum(float x) {
 // Key (or query) offset, inside a 32-wide block, of element i of a 32x32
 // MFMA accumulator held by a lane in half hf (= lane / 32).
 __device__ __forceinline__ int acc_row(int i, int hf) { return (i >> 2) * 8 + hf * 4 + (i & 3); }
+
+// FP8 transposed tiles ([dims][positions], 64 positions per group): slot of
+// position k (0..63) of a group.  Half hf of a 64-byte row holds the
+// positions a lane of half hf holds in two 32x32 accumulator blocks, byte
+// 16 kb + e for position 32 kb + acc_row(e, hf), so an accumulator-side
+// operand of the 32x32x64 FP8 MFMA (one byte per element, packed in element
+// order) pairs byte for byte with a 32-byte read of that half.
+__host__ __device__ __forceinline__ int fp8_key_slot(int k) {
+  const int kb = k >> 5, r = k & 31;
+  const int hf = (r >> 2) & 1, e = (r >> 3) * 4 + (r & 3);
+  return hf * 32 + kb * 16 + e;
+}
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 

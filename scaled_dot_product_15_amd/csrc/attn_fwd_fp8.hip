@@ -34,17 +34,9 @@
 
 namespace sdpa {
 
-// Position of key k (0..63) of a 64-key group in the permuted V^T row: half
-// hf of the row holds the keys a lane of half hf holds in two 32x32
-// accumulator blocks, byte 16 kb + e for key 32 kb + acc_row(e, hf).
-__host__ __device__ __forceinline__ int fp8_key_slot(int k) {
-  const int kb = k >> 5, r = k & 31;
-  const int hf = (r >> 2) & 1, e = (r >> 3) * 4 + (r & 3);
-  return hf * 32 + kb * 16 + e;
-}
-
 // V (E4M3 codes, [rows, Hkv, Dv] per batch) -> V^T [B, Hkv, Dv, S_pad] with
-// the key slots above; keys at or past the batch's row count are zero.  One
+// the key slots of fp8_key_slot; keys at or past the batch's valid length are
+// zero (padding codes are never read, so a NaN code there cannot reach O).  One
 // thread per (batch, kv head, 16 dims, key), keys fastest, so a wave writes
 // each of its 16 dim rows in one 64-byte run.
 template <int DV>
@@ -57,7 +49,7 @@ __global__ __launch_bounds__(256) void fp8_vt_kernel(KArgs a) {
   const int g = (int)(r % a.Hkv), b = (int)(r / a.Hkv);
   if (b >= a.B) return;
   u32x4 v = {0u, 0u, 0u, 0u};
-  if (j < seq_rows(a, b))
+  if (j < seq_len(a, b))
     v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) +
                                         ((seq_row0(a, b) + j) * a.Hkv + g) * DV + dc * 16);
   uint8_t* dst = a.vt + (((size_t)b * a.Hkv + g) * DV + dc * 16) * a.s_pad + (j & ~63) + fp8_key_slot(j & 63);

@@ -44,6 +44,10 @@ hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t st
 // FP8 forward (E4M3 Q, K, V): V^T pre-pass into a.vt, then the two-pass kernel.
 size_t fp8_vt_bytes(int B, int S, int Hkv, int dv);
 hipError_t launch_fwd_fp8(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// FP8 backward (E4M3 Q, K, V, E5M2 dO): pre-pass, transposes of K, Q, dO into
+// a.kt_t / a.qt_t / a.dot_t, dQ and dK/dV kernels, sink-gradient reduce.
+size_t fp8_bwd_transposed_bytes(int B, int S, int Hq, int Hkv, int d);
+hipError_t launch_bwd_fp8(const KArgs& a, int dqk, int dv, hipStream_t stream);
 // FP8 per-tensor scaling.
 hipError_t launch_fp8_quantize(const void* x, int bf16_in, size_t n, int e5m2, const float* scale, uint8_t* out,
                                float* amax, hipStream_t stream);

@@ -335,16 +335,19 @@ def test_bias_arguments_checked_before_any_hip_call():
 
 
 def test_fp8_validation_before_any_hip_call():
-    """ATTN_FP8 is a forward-only dtype: head dims 64 or 128 without dropout;
-    attn_fwd / attn_bwd refuse it (unsupported), attn_fwd_fp8 refuses other
-    dtypes; its workspace holds V transposed.  The scaling entry points check
-    formats, history lengths and pointers.  Nothing is launched."""
+    """ATTN_FP8 runs through attn_fwd_fp8 / attn_bwd_fp8 only: head dims 64
+    or 128 without dropout; attn_fwd / attn_bwd refuse it (unsupported), the
+    FP8 entry points refuse other dtypes; the forward workspace holds V
+    transposed, the backward's delta, LSE log2 e, sink partials and K, Q, dO
+    transposed.  The scaling entry points check formats, history lengths and
+    pointers.  Nothing is launched."""
     lib = binding.load_library()
     f = ctypes.c_void_p(256)
     p8 = binding.make_params(2, 100, 4, 2, 128, 128, "fp8", "causal")
     assert binding.attn_validate(p8) == 0
     assert binding.attn_fwd_workspace_size(p8) == 2 * 2 * 128 * 128  # B Hkv Dv S_pad(128)
-    assert binding.attn_bwd_workspace_size(p8) == 0
+    # 2 x align256(B Hq S 4) + align256(B Hq ceil(S/32) 4) + B D S_pad (Hkv + 2 Hq)
+    assert binding.attn_bwd_workspace_size(p8) == 2 * 3328 + 256 + 2 * 128 * 128 * (2 + 2 * 4)
     assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 192, 128, "fp8")) == -2
     assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 64, 64, "fp8", dropout_p=0.1)) == -2
     assert lib.attn_fwd(ctypes.byref(p8), f, f, f, None, None, None, f, f, None, 0, None) == -2
@@ -356,6 +359,17 @@ def test_fp8_validation_before_any_hip_call():
     assert lib.attn_fwd_fp8(ctypes.byref(p8), f, f, f, f, None, None, None, f, f, f, 16, None) == -3
     assert lib.attn_fwd_fp8(ctypes.byref(p8), ctypes.c_void_p(264), f, f, f, None, None, None, f, f, f, 1 << 20,
                             None) == -1  # q not 16-byte aligned
+    ws = 1 << 20
+    bwd = lambda pp, q=f, d=f, s=f, am=f, off=None, doff=None, w=f, wb=ws: lib.attn_bwd_fp8(  # noqa: E731
+        ctypes.byref(pp), q, f, f, f, f, f, d, s, am, off, None, None, f, f, f, doff, w, wb, None)
+    assert bwd(pb) == -1                                   # not an FP8 problem
+    assert bwd(p8, d=None) == -1 and bwd(p8, s=None) == -1 and bwd(p8, am=None) == -1
+    assert bwd(p8, w=None) == -3 and bwd(p8, wb=1024) == -3
+    assert bwd(p8, w=ctypes.c_void_p(512 + 16)) == -1       # workspace not 256-byte aligned
+    assert bwd(p8, q=ctypes.c_void_p(264)) == -1            # q not 16-byte aligned
+    assert bwd(p8, doff=f) == -1                            # vanilla takes no offset gradient
+    pl = binding.make_params(2, 100, 4, 2, 128, 128, "fp8", "causal", softmax_type="learnable")
+    assert bwd(pl) == -1 and bwd(pl, off=f) == -1           # learnable needs offsets and their gradient
     assert lib.attn_fp8_quantize(f, 1, 10, 2, f, f, f, None) == -1      # no such format
     assert lib.attn_fp8_quantize(f, 2, 10, 0, f, f, f, None) == -1      # x dtype
     assert lib.attn_fp8_quantize(f, 1, 10, 0, None, f, f, None) == -1   # no scale

@@ -11,6 +11,13 @@
                accuracy of a rounding midpoint; masks, softmax types, GQA,
                padding, head dims 64 and 128), the GQA+SWA S=4096 workload on
                sampled rows, packed == padded
+  backward     E5M2 dO; dQ, dK, dV vs attention_fp8_bwd within a derived
+               per-element bound (bf16 output rounding, float32 accumulation,
+               and for every P and dS element the largest code change a
+               float32 error of the stated size can cause: one step at a
+               rounding midpoint, several near zero where codes are dense);
+               amax of dS and the sink gradient; padded rows zero; the S=4096
+               workload on sampled rows and keys; packed == padded, reproducible
 """
 import itertools
 
@@ -191,3 +198,170 @@ def test_fp8_packed_equals_padded():
     for b, n in enumerate(sizes):
         assert torch.equal(po[start[b]:start[b] + n], o[b, :n])
         assert torch.equal(plse[b, :, :n], lse[b, :, :n])
+
+
+# ---- backward -------------------------------------------------------------------
+
+def _spread(x, fmt, tol):
+    """How far the code of a value within tol of x can lie from the code of x:
+    max(|q(x + tol) - q(x)|, |q(x) - q(x - tol)|) with q = decode(encode(.))
+    (monotone).  Near a rounding midpoint that is one code step; near zero,
+    where codes are dense, float32 noise of size tol can move several steps."""
+    def q(y):
+        return fp8.fp8_decode(fp8.fp8_encode(y, fmt), fmt)
+    qx = q(x)
+    return np.maximum(np.abs(q(x + tol) - qx), np.abs(qx - q(x - tol)))
+
+
+def _p_steps(p):
+    """E4M3 code changes of 256 P: the device's P is within 1e-3 (relative) of
+    the oracle's."""
+    x = 256.0 * p
+    return _spread(x, fp8.E4M3, 1e-3 * x) / 256.0
+
+
+def _ds_steps(p, ds, dp_abs, delta, s_ds):
+    """E5M2 code changes of s_ds dS: the device's dS differs by P's error (1e-3
+    relative, doubled) and by float32 sums in dP and delta (4e-5 of the
+    magnitudes they add up)."""
+    tol = s_ds * (2e-3 * np.abs(ds) + p * 4e-5 * (dp_abs + np.abs(delta)[:, None]))
+    return _spread(s_ds * ds, fp8.E5M2, tol) / s_ds
+
+
+BWD_CASES = list(itertools.product((64, 128), MASKS, ("vanilla", "off_by_one", "learnable"), (False, True)))
+S_DO, S_DS = 256.0, 1024.0  # dO codes hold 256 dO; dS is encoded as E5M2(1024 dS)
+
+
+def _bwd_run(p, arr, q8, k8, v8, ds, seed, sl, causal, win, st):
+    import torch
+    do8 = fp8.fp8_encode(arr["do"].astype(np.float64) * S_DO, fp8.E5M2)
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if causal else "no_mask", window_size=win,
+              softmax_type=st, softmax_offset=_dev(arr["alpha"]), seqlens=None if sl is None else _dev(sl))
+    q8d, k8d, v8d = _dev(q8), _dev(k8), _dev(v8)
+    o, lse = binding.attn_fwd_fp8(q8d, k8d, v8d, _dev(np.array([ds, ds, ds], np.float32)), **kw)
+    desc4 = _dev(np.array([ds, ds, ds, 1.0 / S_DO], np.float32))
+    dq, dk, dv, doff, amax = binding.attn_bwd_fp8(q8d, k8d, v8d, o, _dev(do8), lse, desc4,
+                                                  _dev(np.array([S_DS], np.float32)), want_d_offset=True, **kw)
+    torch.cuda.synchronize()
+    return do8, o, lse, dq, dk, dv, doff, amax
+
+
+@pytest.mark.parametrize("d,mask,st,padded", BWD_CASES, ids=lambda x: str(x))
+def test_fp8_backward_small(d, mask, st, padded):
+    causal, win = MASKS[mask]
+    p = inputs.Problem(B=3, S=333, Hq=4, Hkv=2, d_qk=d, d_v=d, dtype="bf16", causal=causal, window=win,
+                       softmax_type=st)
+    seed = 85_000 + BWD_CASES.index((d, mask, st, padded))
+    arr, q8, k8, v8, ds = _fp8_inputs(p, seed)
+    sl = np.array([333, 150, 0], np.int32) if padded else None
+    gc.log(f"fp8 bwd d={d} {mask} {st} padded={padded} seed={seed}")
+    do8, o, lse, dq, dk, dv, doff, amax = _bwd_run(p, arr, q8, k8, v8, ds, seed, sl, causal, win, st)
+    o64, lse64 = inputs.exact_f64(o), inputs.exact_f64(lse)
+    r = fp8.attention_fp8_bwd(q8, k8, v8, o64, do8, lse64, ds, ds, ds, 1.0 / S_DO, S_DS, num_gqa_groups=p.Hkv,
+                              causal=causal, window=win, softmax_type=st,
+                              softmax_offset=arr["alpha"].astype(np.float64), seqlens=sl)
+    Q = fp8.fp8_decode(q8, fp8.E4M3) * ds
+    K = fp8.fp8_decode(k8, fp8.E4M3) * ds
+    dO = fp8.fp8_decode(do8, fp8.E5M2) / S_DO
+    scale = 1.0 / np.sqrt(d)
+    G = p.Hq // p.Hkv
+    bdq, bdk, bdv = np.zeros(r["dq"].shape), np.zeros(r["dk"].shape), np.zeros(r["dv"].shape)
+    for b in range(p.B):
+        for h in range(p.Hq):
+            g = h // G
+            sds = _ds_steps(r["p"][b, h], r["ds"][b, h], r["dp_abs"][b, h], r["delta"][b, h], S_DS)
+            dsa = np.abs(fp8.fp8_decode(r["ds8"][b, h], fp8.E5M2)) / S_DS
+            pa = fp8.fp8_decode(r["p8"][b, h], fp8.E4M3) / 256.0
+            sp = _p_steps(r["p"][b, h])
+            bdq[b, :, h] = scale * (sds + 2e-4 * dsa) @ np.abs(K[b, :, g])
+            bdk[b, :, g] += scale * (sds + 2e-4 * dsa).T @ np.abs(Q[b, :, h])
+            bdv[b, :, g] += (sp + 2e-4 * pa).T @ np.abs(dO[b, :, h])
+    worst = {}
+    for n, got, bound in (("dq", dq, bdq), ("dk", dk, bdk), ("dv", dv, bdv)):
+        g64 = inputs.exact_f64(got)
+        bound = bound + 2.0 ** -8 * (np.abs(r[n]) + bound) + 1e-6  # bf16 rounding of the device's value
+        err = np.abs(g64 - r[n])
+        worst[n] = float((err - bound).max())
+        assert gc.rel_l2(g64, r[n]) <= 1e-2, (n, gc.rel_l2(g64, r[n]))
+        assert (err <= bound).all(), (n, worst[n], float(err.max()))
+    gc.log(f"  worst over bound {worst}; amax {float(amax.cpu()[0]):.6g} vs {r['amax_ds']:.6g}")
+    assert abs(float(amax.cpu()[0]) - r["amax_ds"]) <= 1e-3 * r["amax_ds"] + 1e-12
+    if st == "vanilla":
+        assert doff is None
+    else:
+        assert np.abs(doff.cpu().numpy() - r["dalpha"]).max() <= 1e-3 * (1 + np.abs(r["dalpha"]).max())
+    if sl is not None:
+        for b in range(p.B):
+            assert not bool(dq[b, sl[b]:].any()) and not bool(dk[b, sl[b]:].any()) and not bool(dv[b, sl[b]:].any())
+
+
+def test_fp8_backward_full_length_sampled():
+    """GQA+SWA S=4096 (B=4, Hq=32, Hkv=8, d=128, window (1024, 0)): dQ on
+    sampled rows and dK, dV on sampled keys (summed over their group's four
+    heads and every row) against the sampled FP8 oracle."""
+    import torch
+    p = inputs.workload_configs()[2][0]
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 86_000)
+    gc.log("fp8 bwd full length")
+    do8, o, lse, dq, dk, dv, doff, amax = _bwd_run(p, arr, q8, k8, v8, ds, 86_000, None, True, p.window, "vanilla")
+    assert bool(torch.isfinite(dq).all()) and bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
+    o64, lse64 = inputs.exact_f64(o), inputs.exact_f64(lse)
+    args = (q8, k8, v8, o64, do8, lse64, ds, ds, ds, 1.0 / S_DO, S_DS)
+    kw = dict(num_gqa_groups=p.Hkv, causal=True, window=p.window)
+    K = fp8.fp8_decode(k8, fp8.E4M3) * ds
+    Q = fp8.fp8_decode(q8, fp8.E4M3) * ds
+    dO = fp8.fp8_decode(do8, fp8.E5M2) / S_DO
+    scale = 1.0 / np.sqrt(p.d_qk)
+    rows = np.array([0, 1, 63, 64, 1023, 1024, 1025, 2047, 3333, 4095])
+    for b, h in ((0, 0), (1, 9), (3, 31), (2, 17)):
+        r = fp8.attention_fp8_bwd_rows(*args, b=b, h=h, rows=rows, **kw)
+        sds = _ds_steps(r["p"], r["ds"], r["dp_abs"], r["delta"], S_DS)
+        dsa = np.abs(fp8.fp8_decode(r["ds8"], fp8.E5M2)) / S_DS
+        bound = scale * (sds + 2e-4 * dsa) @ np.abs(K[b, :, h // 4])
+        bound = bound + 2.0 ** -8 * (np.abs(r["dq"]) + bound) + 1e-6
+        got = inputs.exact_f64(dq[b, rows, h])
+        assert (np.abs(got - r["dq"]) <= bound).all(), (b, h, float((np.abs(got - r["dq"]) - bound).max()))
+    keys = np.array([0, 5, 127, 128, 2000, 4000, 4095])
+    for b, g in ((0, 0), (2, 3), (3, 7)):
+        r = fp8.attention_fp8_bwd_keys(*args, b=b, g=g, keys=keys, **kw)
+        bdk = np.zeros(r["dk"].shape)
+        bdv = np.zeros(r["dv"].shape)
+        for n, h in enumerate(range(g * 4, g * 4 + 4)):
+            sds = _ds_steps(r["p"][n], r["ds"][n], r["dp_abs"][n], r["delta"][n], S_DS)
+            dsa = np.abs(fp8.fp8_decode(r["ds8"][n], fp8.E5M2)) / S_DS
+            pa = fp8.fp8_decode(r["p8"][n], fp8.E4M3) / 256.0
+            bdk += scale * (sds + 2e-4 * dsa).T @ np.abs(Q[b, :, h])
+            bdv += (_p_steps(r["p"][n]) + 2e-4 * pa).T @ np.abs(dO[b, :, h])
+        for n, got, bound in (("dk", dk[b, keys, g], bdk), ("dv", dv[b, keys, g], bdv)):
+            g64 = inputs.exact_f64(got)
+            bound = bound + 2.0 ** -8 * (np.abs(r[n]) + bound) + 1e-6
+            assert (np.abs(g64 - r[n]) <= bound).all(), (n, b, g, float((np.abs(g64 - r[n]) - bound).max()))
+
+
+def test_fp8_backward_packed_equals_padded_and_reproducible():
+    import torch
+    p = inputs.Problem(B=3, S=256, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16", causal=True, window=(60, 0),
+                       softmax_type="learnable")
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 87_000)
+    sizes = [256, 100, 1]
+    do8, o, lse, dq, dk, dv, doff, amax = _bwd_run(p, arr, q8, k8, v8, ds, 87_000, np.array(sizes, np.int32), True,
+                                                   p.window, p.softmax_type)
+    again = _bwd_run(p, arr, q8, k8, v8, ds, 87_000, np.array(sizes, np.int32), True, p.window, p.softmax_type)
+    for a_, b_ in zip((dq, dk, dv, doff, amax), again[3:]):
+        assert torch.equal(a_, b_)
+    cat = lambda x: np.ascontiguousarray(np.concatenate([x[b, :n] for b, n in enumerate(sizes)]))  # noqa: E731
+    off = _dev(np.array([0, 256, 356, 357], np.int32))
+    desc4 = _dev(np.array([ds, ds, ds, 1.0 / S_DO], np.float32))
+    po = torch.cat([o[b, :n] for b, n in enumerate(sizes)]).contiguous()
+    plse = lse.clone()
+    pdq, pdk, pdv, pdoff, pamax = binding.attn_bwd_fp8(
+        _dev(cat(q8)), _dev(cat(k8)), _dev(cat(v8)), po, _dev(cat(do8)), plse, desc4,
+        _dev(np.array([S_DS], np.float32)), num_gqa_groups=p.Hkv, window_size=p.window, softmax_type=p.softmax_type,
+        softmax_offset=_dev(arr["alpha"]), seq_offsets=off, max_seqlen=p.S)
+    torch.cuda.synchronize()
+    start = [0, 256, 356]
+    for b, n in enumerate(sizes):
+        assert torch.equal(pdq[start[b]:start[b] + n], dq[b, :n])
+        assert torch.equal(pdk[start[b]:start[b] + n], dk[b, :n])
+        assert torch.equal(pdv[start[b]:start[b] + n], dv[b, :n])
+    assert torch.equal(pdoff, doff) and torch.equal(pamax, amax)

@@ -342,8 +342,32 @@ def pin_bwd_loops(m):
     assert np.abs(r["dalpha"] - np.array(dz)).max() <= 1e-12 * (1 + np.abs(dz).max())
 
 
+def pin_bwd_sampled(m):
+    """The row- and key-sampled backward functions equal the whole-problem one."""
+    for ci, (causal, win, sl) in enumerate(MASKS):
+        q8, k8, v8, alpha = _case(3800 + ci)
+        rng = np.random.default_rng(3900 + ci)
+        do8 = m.fp8_encode(rng.standard_normal(q8.shape) * 64, m.E5M2)
+        o = rng.standard_normal(q8.shape)
+        lse = rng.standard_normal((2, 4, 11)) + 3.0
+        kw = dict(num_gqa_groups=2, causal=causal, window=win, seqlens=None if sl is None else np.array(sl))
+        args = (q8, k8, v8, o, do8, lse, 0.125, 0.25, 0.0625, 1.0 / 64, 32.0)
+        full = m.attention_fp8_bwd(*args, **kw)
+        for b in range(2):
+            for h in (0, 1, 3):
+                rows = [10, 0, 4, 7]
+                r = m.attention_fp8_bwd_rows(*args, b=b, h=h, rows=rows, **kw)
+                assert np.abs(r["dq"] - full["dq"][b, rows, h]).max() <= 1e-12
+                assert np.array_equal(r["ds8"], full["ds8"][b, h][rows])
+            for g in (0, 1):
+                keys = [9, 0, 5]
+                r = m.attention_fp8_bwd_keys(*args, b=b, g=g, keys=keys, **kw)
+                assert np.abs(r["dk"] - full["dk"][b, keys, g]).max() <= 1e-12
+                assert np.abs(r["dv"] - full["dv"][b, keys, g]).max() <= 1e-12
+
+
 PINS = [pin_decode, pin_encode, pin_saturation_and_nan, pin_recipe, pin_attention_bound, pin_attention_loops,
-        pin_attention_rows, pin_bwd_exact, pin_bwd_hand, pin_bwd_bound, pin_bwd_loops]
+        pin_attention_rows, pin_bwd_exact, pin_bwd_hand, pin_bwd_bound, pin_bwd_loops, pin_bwd_sampled]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -374,7 +398,7 @@ MUTANTS = {
                         "ds8 = np.where(mask, fp8_encode(float(scale_ds) * ds, E4M3), 0)"),
                        ("dsq = fp8_decode(ds8, E5M2)", "dsq = fp8_decode(ds8, E4M3)")],
     "bwd_p_unquantized": ("dv[b, :, g, :] += pq.T @ do[b, :, h, :]", "dv[b, :, g, :] += p.T @ do[b, :, h, :]"),
-    "bwd_delta_dropped": ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
+    "bwd_delta_dropped": ("ds = p * (dp - delta[:, None])", "ds = p * dp", "all"),
     "bwd_p_row_max": ("np.exp(s - lse[b, h][:, None])",
                       "np.exp(s - np.where(mask, s, -np.inf).max(axis=1)[:, None])"),
     "bwd_dk_no_group_sum": ("dk[b, :, g, :] += scale", "dk[b, :, g, :] = scale"),
@@ -383,6 +407,9 @@ MUTANTS = {
     "bwd_do_descale_dropped": ("do = fp8_decode(do8, E5M2) * float(descale_do)", "do = fp8_decode(do8, E5M2)"),
     "bwd_dalpha_sign": ("dalpha[h] += -float(", "dalpha[h] += float("),
     "bwd_dk_takes_k": ("(dsq.T @ q[b, :, h, :])", "(dsq.T @ k[b, :, g, :])"),
+    "bwd_rows_wrong_kv_head": ("    g = kv_head(h, Hq, Hkv)\n    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])\n    rows = np.asarray(rows, dtype=np.int64)\n    keys",
+                               "    g = (h + 1) % Hkv\n    L = S if seqlens is None else int(np.asarray(seqlens).reshape(-1)[b])\n    rows = np.asarray(rows, dtype=np.int64)\n    keys"),
+    "bwd_keys_group_off_by_one": ("for h in range(g * G, (g + 1) * G):", "for h in range(g * G, (g + 1) * G - 1):"),
 }
 
 
