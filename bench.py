@@ -138,35 +138,45 @@ def cpu_baseline(p, arr, groups):
                       f"{groups * (p.Hq // p.Hkv)} query heads x S={p.S}, fwd+bwd, numpy float64"}
 
 
-def cpu_baseline_fp8(p, q8, k8, v8, descales, offsets, heads):
-    """Time the float64 FP8 oracle on every row of `heads` (batch, query head)
-    pairs of the workload."""
+def cpu_baseline_fp8(p, q8, k8, v8, do8, descales, s_ds, offsets, heads):
+    """Time the float64 FP8 oracle, forward then backward, on `heads` query
+    heads of the workload (each a sub-problem of that head and its K/V head)."""
     from oracle import fp8
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    rows = list(range(p.S))
+    G = p.Hq // p.Hkv
     heads = min(heads, p.B * p.Hq)
+    kw = dict(num_gqa_groups=1, causal=p.causal, window=p.window, scale_factor=p.scale_factor or None,
+              softmax_type=p.softmax_type)
     t0 = time.perf_counter()
     for n in range(heads):
-        fp8.attention_fp8_rows(q8, k8, v8, *descales, b=n // p.Hq, h=n % p.Hq, rows=rows, num_gqa_groups=p.Hkv,
-                               causal=p.causal, window=p.window, scale_factor=p.scale_factor or None,
-                               softmax_type=p.softmax_type, softmax_offset=offsets)
+        b, h = n // p.Hq, n % p.Hq
+        g = h // G
+        sub = dict(q8=q8[b:b + 1, :, h:h + 1], k8=k8[b:b + 1, :, g:g + 1], v8=v8[b:b + 1, :, g:g + 1],
+                   do8=do8[b:b + 1, :, h:h + 1])
+        off = None if offsets is None else offsets[h:h + 1]
+        f = fp8.attention_fp8(sub["q8"], sub["k8"], sub["v8"], *descales[:3], softmax_offset=off, **kw)
+        fp8.attention_fp8_bwd(sub["q8"], sub["k8"], sub["v8"], f["o"], sub["do8"], f["lse"], *descales, s_ds,
+                              softmax_offset=off, **kw)
     dt = time.perf_counter() - t0
     pairs = visible_pairs(p.S, p.S, p.causal, p.window[0], p.window[1]) * heads
-    return {"value": effective_flops(pairs, p.d_qk, p.d_v)[0] / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"{heads} of {p.B * p.Hq} (batch, query head) pairs of the workload, all {p.S} rows each, "
-                      f"FP8 forward, numpy float64"}
+    ff, fb = effective_flops(pairs, p.d_qk, p.d_v)
+    return {"value": (ff + fb) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{heads} of {p.B * p.Hq} (batch, query head) pairs of the workload (S={p.S}), FP8 forward "
+                      f"+ backward, numpy float64"}
 
 
 def bench_fp8(args, p, arr, t, seed, dev, packed):
-    """FP8 forward line: Q, K, V quantized to E4M3 on the device (one delayed-
-    scaling step sets the scales from their amax), then attn_fwd_fp8 timed
-    with those codes resident in HBM.  Effective FLOPs as the forward's:
-    2 * pairs * (d_qk + d_v)."""
+    """FP8 line: Q, K, V quantized to E4M3 and dO to E5M2 on the device (one
+    delayed-scaling step sets each scale from its amax; the dS scale is the
+    recipe's for E5M2 after one step on dS's amax), then a step of
+    attn_fwd_fp8 + attn_bwd_fp8 timed with the codes resident in HBM.
+    Effective FLOPs as the bf16 line's: forward 2 * pairs * (d_qk + d_v),
+    backward 2 * pairs * (3 d_qk + 2 d_v)."""
     import numpy as np
     import torch
     from scaled_dot_product_15_amd import binding
@@ -177,39 +187,53 @@ def bench_fp8(args, p, arr, t, seed, dev, packed):
               scale_factor=p.scale_factor or None, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
               seqlens=t["seqlens"])
     codes, descale, scales = [], [], []
-    for name in ("q", "k", "v"):
+    for name, fmt in (("q", "e4m3"), ("k", "e4m3"), ("v", "e4m3"), ("do", "e5m2")):
         hist = torch.zeros(1024, dtype=torch.float32, device="cuda")
         scale = torch.ones(1, dtype=torch.float32, device="cuda")
         dsc = torch.ones(1, dtype=torch.float32, device="cuda")
-        _, amax = binding.fp8_quantize(t[name], scale, "e4m3")
-        binding.fp8_update_scale(hist, amax, scale, dsc, "e4m3", margin=0)
-        c, _ = binding.fp8_quantize(t[name], scale, "e4m3")
+        _, amax = binding.fp8_quantize(t[name], scale, fmt)
+        binding.fp8_update_scale(hist, amax, scale, dsc, fmt, margin=0)
+        c, _ = binding.fp8_quantize(t[name], scale, fmt)
         codes.append(c)
         descale.append(dsc)
         scales.append(scale)
-    desc = torch.cat(descale)
-    o, lse = binding.attn_fwd_fp8(*codes, desc, **kw)
+    q8, k8, v8, do8 = codes
+    desc = torch.cat(descale[:3])
+    desc4 = torch.cat(descale)
+    o, lse = binding.attn_fwd_fp8(q8, k8, v8, desc, **kw)
+    # dS scale: one recipe step on the amax of dS a first backward reports
+    ds_scale = torch.ones(1, dtype=torch.float32, device="cuda")
+    want = p.softmax_type != "vanilla"
+    dq, dk, dv, doff, amax_ds = binding.attn_bwd_fp8(q8, k8, v8, o, do8, lse, desc4, ds_scale, want_d_offset=want,
+                                                     **kw)
+    binding.fp8_update_scale(torch.zeros(1024, dtype=torch.float32, device="cuda"), amax_ds, ds_scale,
+                             torch.ones(1, dtype=torch.float32, device="cuda"), "e5m2", margin=0)
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, "fp8", kw["attn_mask_type"], p.window,
                              kw["scale_factor"], p.softmax_type)
     ws = torch.empty(max(binding.attn_fwd_workspace_size(pp), 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(binding.attn_bwd_workspace_size(pp), 1), dtype=torch.uint8, device="cuda")
     fast = dict(kw, check_seqlens=False, out=o, lse=lse, workspace=ws)
+    fastb = dict(kw, check_seqlens=False, outs=(dq, dk, dv, doff), amax=amax_ds, workspace=wsb, want_d_offset=want)
     stream = torch.cuda.current_stream()
 
     def step():
-        binding.attn_fwd_fp8(*codes, desc, **fast)
+        binding.attn_fwd_fp8(q8, k8, v8, desc, **fast)
+        binding.attn_bwd_fp8(q8, k8, v8, o, do8, lse, desc4, ds_scale, **fastb)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in ev:
         e[0].record(stream)
-        step()
+        binding.attn_fwd_fp8(q8, k8, v8, desc, **fast)
         e[1].record(stream)
+        binding.attn_bwd_fp8(q8, k8, v8, o, do8, lse, desc4, ds_scale, **fastb)
+        e[2].record(stream)
     qev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     qev[0].record(stream)
-    for name, c, sc in zip(("q", "k", "v"), codes, scales):
-        binding.fp8_quantize(t[name], sc, "e4m3", out=c)  # same scales: the codes are unchanged
+    for name, c, sc, fmt in zip(("q", "k", "v", "do"), codes, scales, ("e4m3", "e4m3", "e4m3", "e5m2")):
+        binding.fp8_quantize(t[name], sc, fmt, out=c)  # same scales: the codes are unchanged
     qev[1].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -217,26 +241,32 @@ def bench_fp8(args, p, arr, t, seed, dev, packed):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    call_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    avg = statistics.fmean(call_ms)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    avg = statistics.fmean(fwd_ms)
     seq = arr["seqlens"]
     pairs = workload_pairs(p, seq)
-    f_fwd = effective_flops(pairs, p.d_qk, p.d_v)[0]
+    f_fwd, f_bwd = effective_flops(pairs, p.d_qk, p.d_v)
     ms = elapsed / args.steps * 1e3
-    value = f_fwd / (ms * 1e-3) / 1e12
+    value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     achieved = f_fwd / (avg * 1e-3) / 1e12
+    t_bwd = statistics.median(bwd_ms)
     res = {
-        "metric": "fwd effective TFLOP/s (FP8 E4M3 GQA+SWA, S=4096) and % of MFMA fp8 peak",
+        "metric": "fwd+bwd effective TFLOP/s (FP8 E4M3/E5M2 GQA+SWA, S=4096) and % of MFMA fp8 peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3", "data": "synthetic",
+        "dtype": "fp8_e4m3/e5m2", "data": "synthetic",
         "config": {"workload": p.name, "batch": p.B, "seq_len": p.S, "num_heads": p.Hq, "num_gqa_groups": p.Hkv,
                    "head_dim_qk": p.d_qk, "head_dim_v": p.d_v, "mask": "causal" if p.causal else "none",
-                   "window": list(p.window), "softmax_type": p.softmax_type, "seed": seed, "fp8": "e4m3",
+                   "window": list(p.window), "softmax_type": p.softmax_type, "seed": seed,
+                   "fp8": "E4M3 Q, K, V, P; E5M2 dO, dS",
                    "seqlens": None if seq is None else [int(x) for x in seq], "tokens": p.B * p.S},
         "pct_of_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
-        "pairs": pairs, "gflop_fwd": round(f_fwd / 1e9, 3),
-        "t_quantize_qkv_ms": round(qev[0].elapsed_time(qev[1]), 4),
+        "pairs": pairs, "gflop_fwd": round(f_fwd / 1e9, 3), "gflop_bwd": round(f_bwd / 1e9, 3),
+        "t_fwd_ms": round(statistics.median(fwd_ms), 4), "t_bwd_ms": round(t_bwd, 4),
+        "tflops_fwd": round(f_fwd / (statistics.median(fwd_ms) * 1e-3) / 1e12, 2),
+        "tflops_bwd": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "t_quantize_qkvdo_ms": round(qev[0].elapsed_time(qev[1]), 4),
         "roofline": {"bound": "mfma", "kernel": "fwd_fp8", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": f_fwd, "avg_launch_ms": round(avg, 4),
@@ -245,9 +275,10 @@ def bench_fp8(args, p, arr, t, seed, dev, packed):
                    "gcn_arch": getattr(dev, "gcnArchName", "")},
     }
     if not args.no_cpu_baseline:
-        qc, kc, vc = (c.cpu().numpy() for c in codes)
-        res["cpu_baseline"] = cpu_baseline_fp8(p, qc, kc, vc, [float(x) for x in desc.cpu()],
-                                               arr["alpha"].astype(np.float64), args.cpu_groups // 3 or 1)
+        qc, kc, vc, dc = (c.cpu().numpy() for c in codes)
+        res["cpu_baseline"] = cpu_baseline_fp8(p, qc, kc, vc, dc, [float(x) for x in desc4.cpu()],
+                                               float(ds_scale.cpu()[0]), arr["alpha"].astype(np.float64),
+                                               max(1, args.cpu_groups // 12))  # one head at the default
     print(json.dumps(res), flush=True)
 
 

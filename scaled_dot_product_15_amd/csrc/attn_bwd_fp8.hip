@@ -30,6 +30,11 @@
 //     dP   = dO V^T    A dO rows (LDS)       B V row (registers)   E5M2 x E4M3
 //     dV^T += dO^T P8  A dO^T rows (LDS)     B P8 (accumulators)   E5M2 x E4M3
 //     dK^T += Q^T dS8  A Q^T rows (LDS)      B dS8 (accumulators)  E4M3 x E5M2
+// The pre-pass stores the per-row terms already scaled for the element work:
+// l8 = LSE log2 e - 8, so exp2(s c8 - l8) = 256 P is the E4M3 input, and
+// delta' = delta s_ds / 256, so 256 P (dP' - delta') with dP' = dP s_ds / 256
+// is s_ds dS, the E5M2 input: per element one FMA, one exp, one FMA, one
+// multiply and one clamp, plus the mask where a step needs it.
 // A 32x32x64 operand is 32 bytes per lane: row (or column) l % 32, half l / 32;
 // an A lane and a B lane of the same half pair their bytes one to one.
 // Row-major tiles are read as chunks 4k + hf and 4k + 2 + hf of a row for
@@ -67,7 +72,7 @@ __device__ __forceinline__ uint32_t pack_e4m3(float x0, float x1, float x2, floa
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }
-__device__ __forceinline__ float clamp_e5m2(float x) { return fminf(fmaxf(x, -57344.0f), 57344.0f); }
+__device__ __forceinline__ float clamp_e5m2(float x) { return __builtin_amdgcn_fmed3f(x, -57344.0f, 57344.0f); }
 __device__ __forceinline__ uint32_t pack_e5m2(float x0, float x1, float x2, float x3) {
   int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(x0), clamp_e5m2(x1), 0, false);
   w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(x2), clamp_e5m2(x3), w, true);
@@ -92,30 +97,51 @@ __global__ void fp8_amax_zero_kernel(float* amax) {
 
 // codes [rows, heads, D] per batch -> [B, heads, D, s_pad] with the positions
 // of each 64-group in fp8_key_slot order; positions at or past the batch's
-// valid length are zero.  One thread per (batch, head, 16 dims, position),
-// positions fastest, so a wave writes each of its 16 dim rows in one run.
+// valid length are zero.  One workgroup per (batch, head, 64 positions): the
+// 64 rows arrive in LDS with 16-byte loads (D / 16 consecutive threads per
+// row), then each thread writes 16-byte pieces of the [D][64] output, slot
+// t of a row holding position 32 (t / 16 % 2) + acc_row(t % 16, t / 32).
 template <int D>
 __global__ __launch_bounds__(256) void fp8_transpose_kernel(KArgs a, const uint8_t* src, int heads, uint8_t* dst) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int j = (int)(t % a.s_pad);
-  long long r = t / a.s_pad;
-  const int dc = (int)(r % (D / 16));
-  r /= D / 16;
-  const int hh = (int)(r % heads), b = (int)(r / heads);
-  if (b >= a.B) return;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (j < seq_len(a, b)) v = *reinterpret_cast<const u32x4*>(src + ((seq_row0(a, b) + j) * heads + hh) * D + dc * 16);
-  uint8_t* out = dst + (((size_t)b * heads + hh) * D + dc * 16) * a.s_pad + (j & ~63) + fp8_key_slot(j & 63);
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * D];
+  const int groups = a.s_pad / 64;
+  const int grp = blockIdx.x % groups;
+  const int hh = (blockIdx.x / groups) % heads, b = blockIdx.x / (groups * heads);
+  const int tid = threadIdx.x;
+  const int L = seq_len(a, b), j0 = grp * 64;
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
+  for (int c = tid; c < 64 * D / 16; c += 256) {
+    const int row = c / (D / 16), ch = c % (D / 16);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j0 + row < L) v = *reinterpret_cast<const u32x4*>(src + ((seq_row0(a, b) + j0 + row) * heads + hh) * D + ch * 16);
+    *reinterpret_cast<u32x4*>(tile + row * D + ch * 16) = v;
+  }
+  __syncthreads();
+  uint8_t* out = dst + ((size_t)b * heads + hh) * D * a.s_pad + j0;
 #pragma unroll
-    for (int byte = 0; byte < 4; ++byte) out[(size_t)(w * 4 + byte) * a.s_pad] = (uint8_t)(v[w] >> (8 * byte));
+  for (int c = tid; c < D * 4; c += 256) {
+    const int d = c / 4, t0 = (c % 4) * 16;  // dim row d, slots t0 .. t0+15
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + q * 4 + e;
+        const int k = ((t >> 4) & 1) * 32 + acc_row(t & 15, t >> 5);
+        word |= (uint32_t)tile[k * D + d] << (8 * e);
+      }
+      w[q] = word;
+    }
+    *reinterpret_cast<u32x4*>(out + (size_t)d * a.s_pad + t0) = u32x4{w[0], w[1], w[2], w[3]};
+  }
 }
 
-// Pre-pass: delta = ddo (dO8 . O), lse2 = LSE log2 e (both 0 past the valid
-// length), and the sink-gradient partial -sum exp(z - LSE_i) delta_i of the
-// block's 32 rows.  Grid (32-row chunks, Hq, B); 16 lanes per row, each 8
-// (D = 128) or 4 (D = 64) dims; the lane sums meet in a fixed butterfly.
+// Pre-pass: delta' = ddo (dO8 . O) s_ds / 256 and l8 = LSE log2 e - 8 (both 0
+// past the valid length), and the sink-gradient partial -sum exp(z - LSE_i)
+// delta_i of the block's 32 rows (unscaled delta).  Grid (32-row chunks, Hq,
+// B); 16 lanes per row, each 8 (D = 128) or 4 (D = 64) dims; the lane sums
+// meet in a fixed butterfly.
 template <int DV>
 __global__ __launch_bounds__(256) void fp8_bwd_pre_kernel(KArgs a) {
   constexpr int PER = DV / 16;
@@ -124,6 +150,7 @@ __global__ __launch_bounds__(256) void fp8_bwd_pre_kernel(KArgs a) {
   const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
   const int L = seq_len(a, b);
   const float ddo = a.fp8_descale[3];
+  const float dsc = a.ds_scale[0] * (1.0f / 256.0f);
   const float z = sink_logit(a, h);
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
@@ -153,8 +180,8 @@ __global__ __launch_bounds__(256) void fp8_bwd_pre_kernel(KArgs a) {
       if (i < a.S) {
         const size_t idx = ((size_t)b * a.Hq + h) * a.S + i;
         const float lse = i < L ? a.lse[idx] : 0.0f;
-        a.delta[idx] = delta;
-        a.lse2[idx] = i < L ? lse * kLog2e : 0.0f;
+        a.delta[idx] = delta * dsc;
+        a.lse2[idx] = i < L ? lse * kLog2e - 8.0f : 0.0f;
         if (a.softmax_type != 0 && i < L && lse > -__builtin_inff()) dz = -expf(z - lse) * delta;
       }
       dzs[r] = dz;
@@ -228,17 +255,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
     }
   }
   const size_t rowx = ((size_t)b * a.Hq + h) * a.S + (qi < a.S ? qi : a.S - 1);
-  const float lse2 = qi < m.L ? a.lse2[rowx] : 0.0f;
-  const float dl = qi < m.L ? a.delta[rowx] : 0.0f;
-  const float dsq = a.fp8_descale[0], dsk = a.fp8_descale[1], dsv = a.fp8_descale[2], dso = a.fp8_descale[3];
+  const float l8 = qi < m.L ? a.lse2[rowx] : 0.0f;  // LSE log2 e - 8
+  const float dl = qi < m.L ? a.delta[rowx] : 0.0f;  // delta s_ds / 256
+  const float dsk = a.fp8_descale[1];
   const float s_ds = a.ds_scale[0];
-  const float c8 = a.scale_log2 * dsq * dsk;  // raw score -> log2 units
-  const float cdp = dso * dsv;                // raw dP -> dP
+  const float c8 = a.scale_log2 * a.fp8_descale[0] * dsk;                      // raw score -> log2 units
+  const float cdp = a.fp8_descale[3] * a.fp8_descale[2] * s_ds * (1.0f / 256.0f);  // raw dP -> dP s_ds / 256
 
   int lo = 0, hi = -1;
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
   if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
   const int kt0 = lo / C::BN, kt1 = hi < 0 ? -1 : hi / C::BN;
+  int fa = kt0, fb = kt0;  // tiles every row of the workgroup sees in full: [fa, fb)
+  {
+    int f0, f1;
+    if (kt0 <= kt1 && full_key_tiles(m, i0, C::BM, C::BN, f0, f1)) {
+      fa = f0 < kt0 ? kt0 : f0;
+      fb = (f1 > kt1 ? kt1 : f1) + 1;
+      if (fb < fa) fb = fa;
+    }
+  }
 
   const uint8_t* Kg = static_cast<const uint8_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * D;
   const uint8_t* Vg = static_cast<const uint8_t*>(a.v) + (seq_row0(a, b) * a.Hkv + g) * D;
@@ -283,8 +319,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
         s[kb] = mfma_f8<kE4, kE4>(cat16(rrd.read(Ks, kb * 32, 2 * k), rrd.read(Ks, kb * 32, 2 * k + 1)), qreg[k], s[kb]);
         dp[kb] = mfma_f8<kE4, kE5>(cat16(rrd.read(Vs, kb * 32, 2 * k), rrd.read(Vs, kb * 32, 2 * k + 1)), oreg[k], dp[kb]);
       }
-    // Element i of block kb: key j0 + kb*32 + acc_row(i, hf), query qi.
+    // Element i of block kb: key j0 + kb*32 + acc_row(i, hf), query qi;
+    // x = 256 P (dP' - delta') = s_ds dS.
     const int j0 = kt * C::BN;
+    const bool masked = kt < fa || kt >= fb;
     const int lo_r = klo - (j0 + hf * 4), hi_r = khi - (j0 + hf * 4);
     uint32_t dw[8];
 #pragma unroll
@@ -295,11 +333,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q + e, off = kb * 32 + q * 8 + e;
-          float p = fast_exp2(fmaf(s[kb][i], c8, -lse2));
-          p = (off >= lo_r && off <= hi_r) ? p : 0.0f;
-          const float ds = p * fmaf(dp[kb][i], cdp, -dl);
-          amax = fmaxf(amax, fabsf(ds));
-          x[e] = ds * s_ds;
+          float pp = fast_exp2(fmaf(s[kb][i], c8, -l8));
+          if (masked) pp = (off >= lo_r && off <= hi_r) ? pp : 0.0f;
+          x[e] = pp * fmaf(dp[kb][i], cdp, -dl);
+          amax = fmaxf(amax, fabsf(x[e]));
         }
         dw[kb * 4 + q] = pack_e5m2(x[0], x[1], x[2], x[3]);
       }
@@ -328,12 +365,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
         *reinterpret_cast<u32x2*>(dqp + db * 32 + ig * 8) = val;
       }
   }
-  amax_atomic(amax, red4, a.amax_out, tid);
+  amax_atomic(amax / s_ds, red4, a.amax_out, tid);
 }
 
 // ---- dK, dV ------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_fp8_kernel(KArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
   using C = Fp8BwdCfg<D>;
   // Stage (64 query rows of one head): Q rows, dO rows, Q^T, dO^T, lse2, delta.
   constexpr int STAGE = 4 * C::T + 2 * 64 * 4;
@@ -372,10 +409,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_fp8_kernel(KArgs a) {
                       buf_load16(vres, (uint32_t)(kj * stride + (4 * k + 2 + hf) * 16)));
     }
   }
-  const float dsq = a.fp8_descale[0], dsk = a.fp8_descale[1], dsv = a.fp8_descale[2], dso = a.fp8_descale[3];
+  const float dsq = a.fp8_descale[0], dso = a.fp8_descale[3];
   const float s_ds = a.ds_scale[0];
-  const float c8 = a.scale_log2 * dsq * dsk;
-  const float cdp = dso * dsv;
+  const float c8 = a.scale_log2 * dsq * a.fp8_descale[1];
+  const float cdp = dso * a.fp8_descale[2] * s_ds * (1.0f / 256.0f);
+  // Rows that see all 32 keys of this wave (none if it holds keys past the
+  // valid length): steps inside them need no mask.
+  int all_lo, all_hi;
+  {
+    const int kw0 = j0 + w * 32;
+    int lo_a, hi_a, lo_b, hi_b;
+    col_query_bounds(m, kw0 + 31, lo_a, hi_a);
+    col_query_bounds(m, kw0, lo_b, hi_b);
+    all_lo = lo_a;
+    all_hi = hi_b;
+    if (kw0 + 31 >= m.L) {
+      all_lo = 1;
+      all_hi = 0;
+    }
+  }
 
   // Steps: (head of the group, 64-row block) pairs, heads outer, rows ascending.
   int qlo = 0, qhi = -1;
@@ -443,6 +495,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_fp8_kernel(KArgs a) {
     // transposed tiles' slots.
     const float* ls = lse_s(buf);
     const float* dl = del_s(buf);
+    const bool masked = !(q0 >= all_lo && q0 + 63 <= all_hi);
     const int lo_r = qlo_k - (q0 + hf * 4), hi_r = qhi_k - (q0 + hf * 4);
     uint32_t pw[8], dw[8];
 #pragma unroll
@@ -456,10 +509,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_fp8_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q + e, off = rb * 32 + q * 8 + e;
-          float p = fast_exp2(fmaf(s[rb][i], c8, -l4[e]));
-          p = (off >= lo_r && off <= hi_r) ? p : 0.0f;
-          pp[e] = p * 256.0f;
-          xx[e] = p * fmaf(dp[rb][i], cdp, -d4[e]) * s_ds;
+          pp[e] = fast_exp2(fmaf(s[rb][i], c8, -l4[e]));  // 256 P
+          if (masked) pp[e] = (off >= lo_r && off <= hi_r) ? pp[e] : 0.0f;
+          xx[e] = pp[e] * fmaf(dp[rb][i], cdp, -d4[e]);    // s_ds dS
         }
         pw[rb * 4 + q] = pack_e4m3(pp[0], pp[1], pp[2], pp[3]);
         dw[rb * 4 + q] = pack_e5m2(xx[0], xx[1], xx[2], xx[3]);
@@ -515,6 +567,16 @@ size_t fp8_bwd_transposed_bytes(int B, int S, int Hq, int Hkv, int d) {
   return (size_t)B * d * s_pad * (size_t)(Hkv + 2 * Hq);
 }
 
+hipError_t launch_fp8_transpose(const KArgs& a, const void* src, int heads, uint8_t* dst, int d, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)a.B * heads * (a.s_pad / 64)));
+  if (d == 64) hipLaunchKernelGGL(fp8_transpose_kernel<64>, grid, dim3(256), 0, stream, a, static_cast<const uint8_t*>(src),
+                                  heads, dst);
+  else if (d == 128) hipLaunchKernelGGL(fp8_transpose_kernel<128>, grid, dim3(256), 0, stream, a,
+                                        static_cast<const uint8_t*>(src), heads, dst);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
   using C = Fp8BwdCfg<D>;
@@ -522,14 +584,9 @@ static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
   a.n_chunks = (a.S + 31) / 32;
   hipLaunchKernelGGL(fp8_amax_zero_kernel, dim3(1), dim3(64), 0, stream, a.amax_out);
   hipLaunchKernelGGL(fp8_bwd_pre_kernel<D>, dim3(a.n_chunks, a.Hq, a.B), dim3(256), 0, stream, a);
-  auto transpose = [&](const void* src, int heads, uint8_t* dst) {
-    const long long n = (long long)a.B * heads * a.s_pad * (D / 16);
-    hipLaunchKernelGGL(fp8_transpose_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a,
-                       static_cast<const uint8_t*>(src), heads, dst);
-  };
-  transpose(a.k, a.Hkv, a.kt_t);
-  transpose(a.q, a.Hq, a.qt_t);
-  transpose(a.d_o, a.Hq, a.dot_t);
+  launch_fp8_transpose(a, a.k, a.Hkv, a.kt_t, D, stream);
+  launch_fp8_transpose(a, a.q, a.Hq, a.qt_t, D, stream);
+  launch_fp8_transpose(a, a.d_o, a.Hq, a.dot_t, D, stream);
   a.n_tiles = (a.S + C::BM - 1) / C::BM;
   hipLaunchKernelGGL(bwd_dq_fp8_kernel<D>, dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)), dim3(C::NT), 0,
                      stream, a);

@@ -34,31 +34,6 @@
 
 namespace sdpa {
 
-// V (E4M3 codes, [rows, Hkv, Dv] per batch) -> V^T [B, Hkv, Dv, S_pad] with
-// the key slots of fp8_key_slot; keys at or past the batch's valid length are
-// zero (padding codes are never read, so a NaN code there cannot reach O).  One
-// thread per (batch, kv head, 16 dims, key), keys fastest, so a wave writes
-// each of its 16 dim rows in one 64-byte run.
-template <int DV>
-__global__ __launch_bounds__(256) void fp8_vt_kernel(KArgs a) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int j = (int)(t % a.s_pad);
-  long long r = t / a.s_pad;
-  const int dc = (int)(r % (DV / 16));
-  r /= DV / 16;
-  const int g = (int)(r % a.Hkv), b = (int)(r / a.Hkv);
-  if (b >= a.B) return;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (j < seq_len(a, b))
-    v = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.v) +
-                                        ((seq_row0(a, b) + j) * a.Hkv + g) * DV + dc * 16);
-  uint8_t* dst = a.vt + (((size_t)b * a.Hkv + g) * DV + dc * 16) * a.s_pad + (j & ~63) + fp8_key_slot(j & 63);
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-#pragma unroll
-    for (int byte = 0; byte < 4; ++byte) dst[(size_t)(w * 4 + byte) * a.s_pad] = (uint8_t)(v[w] >> (8 * byte));
-}
-
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
@@ -262,8 +237,6 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
   }
 }
 
-template __global__ void fp8_vt_kernel<64>(KArgs);
-template __global__ void fp8_vt_kernel<128>(KArgs);
 template __global__ void fwd_fp8_kernel<64>(KArgs);
 template __global__ void fwd_fp8_kernel<128>(KArgs);
 
@@ -276,8 +249,8 @@ template <int D>
 static hipError_t launch_fp8_cfg(KArgs a, hipStream_t stream) {
   using C = Fp8Cfg<D>;
   a.s_pad = (a.S + 63) / 64 * 64;
-  const long long nv = (long long)a.B * a.Hkv * a.s_pad * (D / 16);
-  hipLaunchKernelGGL(fp8_vt_kernel<D>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, stream, a);
+  const hipError_t e = launch_fp8_transpose(a, a.v, a.Hkv, a.vt, D, stream);  // V^T, keys zero past L
+  if (e != hipSuccess) return e;
   a.n_tiles = (a.S + C::BM - 1) / C::BM;
   const long long n = (long long)a.B * a.Hq * a.n_tiles;
   hipLaunchKernelGGL(fwd_fp8_kernel<D>, dim3((unsigned)n), dim3(C::NT), 0, stream, a);

@@ -44,6 +44,9 @@ hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t st
 // FP8 forward (E4M3 Q, K, V): V^T pre-pass into a.vt, then the two-pass kernel.
 size_t fp8_vt_bytes(int B, int S, int Hkv, int dv);
 hipError_t launch_fwd_fp8(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// FP8 codes [rows, heads, d] per batch -> [B, heads, d, a.s_pad] (positions of
+// each 64-group in fp8_key_slot order, zero past the valid length).
+hipError_t launch_fp8_transpose(const KArgs& a, const void* src, int heads, uint8_t* dst, int d, hipStream_t stream);
 // FP8 backward (E4M3 Q, K, V, E5M2 dO): pre-pass, transposes of K, Q, dO into
 // a.kt_t / a.qt_t / a.dot_t, dQ and dK/dV kernels, sink-gradient reduce.
 size_t fp8_bwd_transposed_bytes(int B, int S, int Hq, int Hkv, int d);
