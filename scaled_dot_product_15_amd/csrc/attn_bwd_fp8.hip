@@ -41,6 +41,8 @@
 // k-step k (both operands alike); the accumulator-side operand packs its 32
 // elements of two 32-wide blocks in element order, matched by the permuted
 // transposed tiles.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace sdpa {
@@ -301,7 +303,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
   if (kt0 <= kt1) issue(kt0, 0);
   lds_dma_wait();
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) {
+  // One key tile; MASKED applies the per-element visibility (tiles outside
+  // [fa, fb)), a separate instantiation so full tiles carry no mask work.
+  auto step = [&](int kt, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int buf = (kt - kt0) & 1;
     if (kt < kt1) issue(kt + 1, buf ^ 1);
     const uint16_t* Ks = reinterpret_cast<const uint16_t*>(krows(buf));
@@ -322,7 +327,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
     // Element i of block kb: key j0 + kb*32 + acc_row(i, hf), query qi;
     // x = 256 P (dP' - delta') = s_ds dS.
     const int j0 = kt * C::BN;
-    const bool masked = kt < fa || kt >= fb;
     const int lo_r = klo - (j0 + hf * 4), hi_r = khi - (j0 + hf * 4);
     uint32_t dw[8];
 #pragma unroll
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q + e, off = kb * 32 + q * 8 + e;
           float pp = fast_exp2(fmaf(s[kb][i], c8, -l8));
-          if (masked) pp = (off >= lo_r && off <= hi_r) ? pp : 0.0f;
+          if constexpr (MASKED) pp = (off >= lo_r && off <= hi_r) ? pp : 0.0f;
           x[e] = pp * fmaf(dp[kb][i], cdp, -dl);
           amax = fmaxf(amax, fabsf(x[e]));
         }
@@ -351,7 +355,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
     }
     lds_dma_wait();
     __syncthreads();
-  }
+  };
+  for (int kt = kt0; kt < fa; ++kt) step(kt, std::true_type{});
+  for (int kt = fa; kt < fb; ++kt) step(kt, std::false_type{});
+  for (int kt = fb; kt <= kt1; ++kt) step(kt, std::true_type{});
 
   const float mul = a.scale * dsk / s_ds;
   if (qi < seq_rows(a, b)) {
@@ -471,10 +478,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
   if (T > 0) issue(0, 0);
   lds_dma_wait();
   __syncthreads();
-  for (int t = 0; t < T; ++t) {
+  // Step t = (head hh, rows q0 .. q0+63).  Steps whose 64 rows all see this
+  // wave's 32 keys run without the mask: per head, steps [m0, m1) (per wave;
+  // every wave still passes one barrier per step, in step order).
+  auto step = [&](int t, int hh, int q0, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int buf = t & 1;
     if (t + 1 < T) issue(t + 1, buf ^ 1);
-    const int hh = t / nsteps, q0 = q_first + (t - hh * nsteps) * 64;
     const uint16_t* Qs = reinterpret_cast<const uint16_t*>(qrows(buf));
     const uint16_t* Os = reinterpret_cast<const uint16_t*>(orows(buf));
     f32x16 s[2], dp[2];
@@ -495,7 +505,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
     // transposed tiles' slots.
     const float* ls = lse_s(buf);
     const float* dl = del_s(buf);
-    const bool masked = !(q0 >= all_lo && q0 + 63 <= all_hi);
     const int lo_r = qlo_k - (q0 + hf * 4), hi_r = qhi_k - (q0 + hf * 4);
     uint32_t pw[8], dw[8];
 #pragma unroll
@@ -510,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q + e, off = rb * 32 + q * 8 + e;
           pp[e] = fast_exp2(fmaf(s[rb][i], c8, -l4[e]));  // 256 P
-          if (masked) pp[e] = (off >= lo_r && off <= hi_r) ? pp[e] : 0.0f;
+          if constexpr (MASKED) pp[e] = (off >= lo_r && off <= hi_r) ? pp[e] : 0.0f;
           xx[e] = pp[e] * fmaf(dp[rb][i], cdp, -d4[e]);    // s_ds dS
         }
         pw[rb * 4 + q] = pack_e4m3(pp[0], pp[1], pp[2], pp[3]);
@@ -532,6 +541,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
     }
     lds_dma_wait();
     __syncthreads();
+  };
+  int m0 = nsteps, m1 = nsteps;
+  if (all_lo <= all_hi) {
+    m0 = all_lo <= q_first ? 0 : (all_lo - q_first + 63) / 64;
+    const int last = all_hi - 63 - q_first;  // q0 + 63 <= all_hi  <=>  s <= last / 64
+    m1 = last < 0 ? 0 : last / 64 + 1;
+    m0 = m0 < nsteps ? m0 : nsteps;
+    m1 = m1 < m0 ? m0 : (m1 < nsteps ? m1 : nsteps);
+  }
+  for (int hh = 0, t = 0; hh < a.G; ++hh) {
+    for (int st = 0; st < m0; ++st, ++t) step(t, hh, q_first + st * 64, std::true_type{});
+    for (int st = m0; st < m1; ++st, ++t) step(t, hh, q_first + st * 64, std::false_type{});
+    for (int st = m1; st < nsteps; ++st, ++t) step(t, hh, q_first + st * 64, std::true_type{});
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).

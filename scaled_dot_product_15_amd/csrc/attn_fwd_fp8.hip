@@ -148,11 +148,14 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
 
   // ---- pass 1: row max -----------------------------------------------------
   float mx = -__builtin_inff();
-  auto pass1 = [&](int kt, int buf, bool masked) __attribute__((always_inline)) {
+  // Key tiles outside [fa, fb) need the mask: a separate instantiation
+  // (MASKED) in loops of their own, so full tiles carry no mask work.
+  auto pass1 = [&](int kt, int buf, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     if (kt < kt1) kcopy.issue(Kg, kstride, (kt + 1) * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(buf ^ 1)));
     f32x16 s[2];
     scores(ktile(buf), s);
-    if (masked) mask(s, kt * C::BN);
+    if constexpr (MASKED) mask(s, kt * C::BN);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -163,17 +166,20 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
   if (kt0 <= kt1) kcopy.issue(Kg, kstride, kt0 * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(0)));
   lds_dma_wait();
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) pass1(kt, (kt - kt0) & 1, kt < fa || kt >= fb);
+  for (int kt = kt0; kt < fa; ++kt) pass1(kt, (kt - kt0) & 1, std::true_type{});
+  for (int kt = fa; kt < fb; ++kt) pass1(kt, (kt - kt0) & 1, std::false_type{});
+  for (int kt = fb; kt <= kt1; ++kt) pass1(kt, (kt - kt0) & 1, std::true_type{});
   float m2 = halves_max(mx) * c8;  // row max in log2 units
   if (has_sink) m2 = fmaxf(m2, z2);
-  const float nm = m2 == -__builtin_inff() ? 0.0f : -m2;
+  const float nm8 = (m2 == -__builtin_inff() ? 0.0f : -m2) + 8.0f;  // exp2(s c8 + nm8) = 256 p
 
   // ---- pass 2: P8 and O ----------------------------------------------------
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float lsum = 0.0f;
-  auto pass2 = [&](int kt, int buf, bool masked) __attribute__((always_inline)) {
+  auto pass2 = [&](int kt, int buf, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     if (kt < kt1) {
       kcopy.issue(Kg, kstride, (kt + 1) * C::BN, m.L, reinterpret_cast<uint16_t*>(ktile(buf ^ 1)));
       vcopy.issue_bytes(VTg + (kt + 1) * C::BN, (uint32_t)(D * a.s_pad - (kt + 1) * C::BN),
@@ -181,8 +187,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
     }
     f32x16 s[2];
     scores(ktile(buf), s);
-    if (masked) mask(s, kt * C::BN);
-    // p = 2^(s c8 - m2) <= 1, masked -> 0; P8 = E4M3(256 p) (never above 256)
+    if constexpr (MASKED) mask(s, kt * C::BN);
+    // 256 p = 2^(s c8 - m2 + 8) <= 256, masked -> 0; P8 = E4M3(256 p); the row
+    // sum collects 256 p (scaled back, exactly, at the end)
     uint32_t pw[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -191,11 +198,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(fmaf(s[kb][4 * q + e], c8, nm));
+          p[e] = fast_exp2(fmaf(s[kb][4 * q + e], c8, nm8));
           lsum += p[e];
         }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.0f, p[1] * 256.0f, 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.0f, p[3] * 256.0f, word, true);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
         pw[kb * 4 + q] = (uint32_t)word;
       }
     const i32x8 pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
@@ -215,9 +222,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(KArgs a) {
   }
   lds_dma_wait();
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) pass2(kt, (kt - kt0) & 1, kt < fa || kt >= fb);
+  for (int kt = kt0; kt < fa; ++kt) pass2(kt, (kt - kt0) & 1, std::true_type{});
+  for (int kt = fa; kt < fb; ++kt) pass2(kt, (kt - kt0) & 1, std::false_type{});
+  for (int kt = fb; kt <= kt1; ++kt) pass2(kt, (kt - kt0) & 1, std::true_type{});
 
-  float l_tot = halves_sum(lsum);
+  float l_tot = halves_sum(lsum) * (1.0f / 256.0f);
   if (has_sink) l_tot += fast_exp2(z2 - m2);
   const float inv = l_tot > 0.0f ? descale_v / (256.0f * l_tot) : 0.0f;
   if (qi < seq_rows(a, b)) {
