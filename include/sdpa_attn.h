@@ -144,7 +144,9 @@ int attn_validate(const struct attn_params* p);
  * d(sink logit), and, for bf16 problems whose dK/dV grid is small (few KV
  * heads, short batches) or whose dK/dV workgroups would walk many rows (long
  * windows, large GQA groups) -- attn_host_dkdv_splits > 1 -- fp32 partial dK
- * and dV of each query-head split of a GQA group. */
+ * and dV of each query-head split of a GQA group.  FP8 problems: the forward
+ * needs V transposed per KV head, the backward (attn_bwd_fp8) the per-row
+ * terms and K, Q, dO transposed per head (codes). */
 size_t attn_fwd_workspace_size(const struct attn_params* p);
 size_t attn_bwd_workspace_size(const struct attn_params* p);
 
