@@ -295,6 +295,44 @@ def test_fp8_backward_small(d, mask, st, padded):
             assert not bool(dq[b, sl[b]:].any()) and not bool(dk[b, sl[b]:].any()) and not bool(dv[b, sl[b]:].any())
 
 
+def test_fp8_backward_mqa_custom_scale():
+    """MQA (4 query heads on one KV head), a non-default scale, a two-sided
+    window, head dim 64: gradients within the derived bound."""
+    import torch
+    p = inputs.Problem(B=2, S=200, Hq=4, Hkv=1, d_qk=64, d_v=64, dtype="bf16", causal=False, window=(30, 17),
+                       softmax_type="off_by_one", scale_factor=0.2)
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 88_000)
+    do8 = fp8.fp8_encode(arr["do"].astype(np.float64) * S_DO, fp8.E5M2)
+    kw = dict(num_gqa_groups=1, attn_mask_type="no_mask", window_size=p.window, scale_factor=0.2,
+              softmax_type=p.softmax_type)
+    q8d, k8d, v8d = _dev(q8), _dev(k8), _dev(v8)
+    o, lse = binding.attn_fwd_fp8(q8d, k8d, v8d, _dev(np.array([ds, ds, ds], np.float32)), **kw)
+    dq, dk, dv, doff, amax = binding.attn_bwd_fp8(q8d, k8d, v8d, o, _dev(do8), lse,
+                                                  _dev(np.array([ds, ds, ds, 1.0 / S_DO], np.float32)),
+                                                  _dev(np.array([S_DS], np.float32)), want_d_offset=True, **kw)
+    torch.cuda.synchronize()
+    r = fp8.attention_fp8_bwd(q8, k8, v8, inputs.exact_f64(o), do8, inputs.exact_f64(lse), ds, ds, ds, 1.0 / S_DO,
+                              S_DS, num_gqa_groups=1, causal=False, window=p.window, scale_factor=0.2,
+                              softmax_type=p.softmax_type)
+    Q = fp8.fp8_decode(q8, fp8.E4M3) * ds
+    K = fp8.fp8_decode(k8, fp8.E4M3) * ds
+    dO = fp8.fp8_decode(do8, fp8.E5M2) / S_DO
+    bdq, bdk, bdv = np.zeros(r["dq"].shape), np.zeros(r["dk"].shape), np.zeros(r["dv"].shape)
+    for b in range(p.B):
+        for h in range(p.Hq):
+            sds = _ds_steps(r["p"][b, h], r["ds"][b, h], r["dp_abs"][b, h], r["delta"][b, h], S_DS)
+            dsa = np.abs(fp8.fp8_decode(r["ds8"][b, h], fp8.E5M2)) / S_DS
+            pa = fp8.fp8_decode(r["p8"][b, h], fp8.E4M3) / 256.0
+            bdq[b, :, h] = 0.2 * (sds + 2e-4 * dsa) @ np.abs(K[b, :, 0])
+            bdk[b, :, 0] += 0.2 * (sds + 2e-4 * dsa).T @ np.abs(Q[b, :, h])
+            bdv[b, :, 0] += (_p_steps(r["p"][b, h]) + 2e-4 * pa).T @ np.abs(dO[b, :, h])
+    for n, got, bound in (("dq", dq, bdq), ("dk", dk, bdk), ("dv", dv, bdv)):
+        g64 = inputs.exact_f64(got)
+        bound = bound + 2.0 ** -8 * (np.abs(r[n]) + bound) + 1e-6
+        assert (np.abs(g64 - r[n]) <= bound).all(), (n, float((np.abs(g64 - r[n]) - bound).max()))
+    assert np.abs(doff.cpu().numpy() - r["dalpha"]).max() <= 1e-3 * (1 + np.abs(r["dalpha"]).max())
+
+
 def test_fp8_backward_full_length_sampled():
     """GQA+SWA S=4096 (B=4, Hq=32, Hkv=8, d=128, window (1024, 0)): dQ on
     sampled rows and dK, dV on sampled keys (summed over their group's four
