@@ -234,6 +234,9 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   }
   KArgs a = make_args(p);
   if (bias) set_bias(a, bias->bias, bias->d_bias, bias->batch, bias->heads);
+  // A bias with one matrix per (batch, head) has dBias = dS: the dQ kernel
+  // writes it (its dS values, zeros elsewhere) and no separate pass runs.
+  a.dbias_direct = bias && bias->d_bias && bias->batch == p->batch && bias->heads == p->num_heads;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -267,7 +270,7 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
     if (e == hipSuccess && a.n_splits > 1) e = launch_dkdv_split_reduce(a, dqk, dvd, s);
     if (e != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (stage == 0 && a.bias && a.d_bias) {
+  if (stage == 0 && a.bias && a.d_bias && !a.dbias_direct) {
     if (launch_bwd_dbias_bf16(a, dqk, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
   }
   if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&

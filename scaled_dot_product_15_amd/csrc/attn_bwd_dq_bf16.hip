@@ -22,7 +22,10 @@
 //
 // BIAS (additive post-scale attention bias): P = exp(scale q.k + bias - LSE);
 // bias / scale is added to the recomputed scores; each lane loads its row's
-// bias values of a key tile at the start of that tile's step (RowBias).
+// bias values of a key tile at the start of that tile's step (RowBias).  For
+// a bias that is not shared (one matrix per batch and head) dBias = dS: the
+// kernel writes each tile's bf16 dS (the values the dQ products take) to its
+// rows of dBias, and zeros for the keys its rows do not reach.
 #include <type_traits>
 
 #include "dropout.h"
@@ -156,6 +159,26 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     vcopy.issue(Vg, (uint32_t)(vstride * 2), j0, m.L, vtile(buf));
   };
 
+  // Unshared bias (dBias written here): this lane's row of dBias, and zeros
+  // for keys [k0, k1) of the wave's 32 rows (16-byte stores, lanes across
+  // keys; S is a multiple of 8, so every 8-key piece below S is whole).
+  // (a null base and size when there is no such bias: nothing is stored then)
+  const __amdgpu_buffer_rsrc_t dbias_res =
+      buf_rsrc(BIAS && a.dbias_direct ? static_cast<uint16_t*>(a.d_bias) + (size_t)bh * a.S * a.S : nullptr,
+               BIAS && a.dbias_direct ? (uint32_t)((size_t)a.S * a.S * 2) : 0u);
+  // byte offset of (row qi, key hf*4) in this (b, h)'s matrix; rows past S store nothing
+  const uint32_t dbias_off = qi < a.S ? (uint32_t)((qi * a.S + hf * 4) * 2) : 0u;
+  auto dbias_zero = [&](int k0, int k1) __attribute__((always_inline)) {
+    if (!a.dbias_direct) return;
+    k1 = k1 < a.S ? k1 : a.S;
+    uint16_t* base = static_cast<uint16_t*>(a.d_bias) + (size_t)bh * a.S * a.S;
+    for (int r = 0; r < 32; ++r) {
+      const int row = qw0 + r;
+      if (row >= a.S) break;
+      for (int k = k0 + lane * 8; k < k1; k += 64 * 8)
+        *reinterpret_cast<u32x4*>(base + (size_t)row * a.S + k) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   auto tile = [&](int j0, const uint16_t* Ks, const uint16_t* Vs, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     // Element i of block kb: key j0 + hf*4 + kb*32 + acc_row(i, 0), query qi.
@@ -211,6 +234,23 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
         }
         dsb[kb * 2 + half] = as_bf16x8(t);
       }
+    if constexpr (BIAS) {
+      // Unshared bias: dBias = dS, row qi, keys j0 + kb*32 + hf*4 + 16 half
+      // + {0..3} and + 8 + {0..3} (words 0-1 and 2-3 of dsb[kb*2 + half]).
+      if (a.dbias_direct && qi < a.S) {
+#pragma unroll
+        for (int kb = 0; kb < C::BN / 32; ++kb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x4 wds = __builtin_bit_cast(u32x4, dsb[kb * 2 + half]);
+            const int k0 = j0 + kb * 32 + half * 16;  // (+ hf * 4, in dbias_off)
+            if (k0 < a.S)
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{wds[0], wds[1]}, dbias_res, dbias_off + k0 * 2, 0, 0);
+            if (k0 + 8 < a.S)
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{wds[2], wds[3]}, dbias_res, dbias_off + (k0 + 8) * 2, 0, 0);
+          }
+      }
+    }
     // dQ^T (dims x queries) += K^T dS^T
     prio_mfma();
 #pragma unroll
@@ -249,6 +289,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     if (kt < kt1) issue_tile(j0 + C::BN, buf ^ 1);
     if constexpr (decltype(masked)::value) {
       if (tile_class(m, qw0, 32, j0, C::BN) != TILE_SKIP) tile(j0, ktile(buf), vtile(buf), std::true_type{});
+      else if constexpr (BIAS) dbias_zero(j0, j0 + C::BN);  // no row of this wave sees the tile
     } else {
       tile(j0, ktile(buf), vtile(buf), std::false_type{});
     }
@@ -273,6 +314,15 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     if (kt + 1 <= kt1) step(kt + 1, B1{}, std::true_type{});
   }
 
+  if constexpr (BIAS) {
+    // keys outside the visited tiles [kt0, kt1]
+    if (kt0 <= kt1) {
+      dbias_zero(0, kt0 * C::BN);
+      dbias_zero((kt1 + 1) * C::BN, a.S);
+    } else {
+      dbias_zero(0, a.S);
+    }
+  }
   if (qi < seq_rows(a, b)) {
     uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK + hf * 4;
 #pragma unroll

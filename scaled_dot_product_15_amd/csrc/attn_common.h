@@ -60,6 +60,7 @@ struct KArgs {
   const float* ds_scale;  // FP8 backward: per-tensor scale of dS before its E5M2 encoding (device, [1])
   float* amax_out;      // FP8 backward: max |dS| (device, [1]; cleared by the launcher)
   int s_pad;            // S rounded up to the FP8 key tile (64)
+  int dbias_direct;     // bias not shared (B x Hq matrices): the dQ kernel writes dBias = dS itself
   int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
   float drop_scale;     // 1 / (1 - drop_t / 256)
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;  // generator key and counter word 3
