@@ -252,7 +252,7 @@ def bench_fp8(args, p, arr, t, seed, dev, packed):
     achieved = f_fwd / (avg * 1e-3) / 1e12
     t_bwd = statistics.median(bwd_ms)
     res = {
-        "metric": "fwd+bwd effective TFLOP/s (FP8 E4M3/E5M2 GQA+SWA, S=4096) and % of MFMA fp8 peak",
+        "metric": "fwd+bwd effective TFLOP/s (FP8: E4M3 Q, K, V, P; E5M2 dO, dS) and % of MFMA fp8 peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3/e5m2", "data": "synthetic",

@@ -58,7 +58,7 @@ size_t delta_bytes(const attn_params* p) { return align256((size_t)p->batch * p-
 size_t dz_bytes(const attn_params* p) { return align256((size_t)p->batch * p->num_heads * max_chunks(p) * sizeof(float)); }
 // bf16 dK/dV: query-head splits of a GQA group (fp32 partials in the workspace when > 1).
 int kv_splits(const attn_params* p) {
-  if (p->dtype != ATTN_BF16) return 1;
+  if (p->dtype == ATTN_F32) return 1;  // bf16 and FP8 dK/dV kernels split a GQA group's heads
   return dkdv_head_splits(p->batch, p->seqlen, p->num_gqa_groups, p->num_heads / p->num_gqa_groups,
                           p->mask_type == ATTN_MASK_CAUSAL, normalise_window(p->window_left, p->seqlen),
                           normalise_window(p->window_right, p->seqlen), p->head_dim_qk, p->head_dim_v);
@@ -150,7 +150,8 @@ size_t attn_bwd_workspace_size(const attn_params* p) {
   if (attn_validate(p) != ATTN_OK) return 0;
   if (p->dtype == ATTN_FP8)
     return 2 * delta_bytes(p) + dz_bytes(p) +
-           align256(fp8_bwd_transposed_bytes(p->batch, p->seqlen, p->num_heads, p->num_gqa_groups, p->head_dim_qk));
+           align256(fp8_bwd_transposed_bytes(p->batch, p->seqlen, p->num_heads, p->num_gqa_groups, p->head_dim_qk)) +
+           kv_part_bytes(p);
   return 2 * delta_bytes(p) + dz_bytes(p) + kv_part_bytes(p);
 }
 
@@ -384,6 +385,10 @@ int attn_bwd_fp8(const attn_params* p, const void* q, const void* k, const void*
   a.kt_t = reinterpret_cast<uint8_t*>(ws + 2 * delta_bytes(p) + dz_bytes(p));
   a.qt_t = a.kt_t + (size_t)p->batch * p->num_gqa_groups * d * s_pad;
   a.dot_t = a.qt_t + (size_t)p->batch * p->num_heads * d * s_pad;
+  // fp32 partial dK, dV of the query-head splits (when the split rule asks for them)
+  a.kv_part = reinterpret_cast<float*>(ws + 2 * delta_bytes(p) + dz_bytes(p) +
+                                       align256(fp8_bwd_transposed_bytes(p->batch, p->seqlen, p->num_heads,
+                                                                         p->num_gqa_groups, p->head_dim_qk)));
   return hip_status(launch_bwd_fp8(a, p->head_dim_qk, p->head_dim_v, static_cast<hipStream_t>(stream)));
 }
 

@@ -392,8 +392,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   // Workgroup id -> (key tile, batch, kv head): consecutive ids cover one key
   // tile, so a (batch, kv head) keeps to one XCD when B * Hkv is a multiple of 8.
-  const int kt = blockIdx.x / (a.B * a.Hkv);
-  const int r0 = blockIdx.x % (a.B * a.Hkv);
+  // Head split hs of n_splits covers query heads hs*Gs .. hs*Gs+Gs-1 of the
+  // group (small grids: few KV heads or batches); each split then writes
+  // fp32 partials that a second kernel adds in split order.
+  const int nsp = a.n_splits, Gs = a.G / nsp;
+  const int kt = blockIdx.x / (a.B * a.Hkv * nsp);
+  int r0 = blockIdx.x % (a.B * a.Hkv * nsp);
+  const int hs = r0 % nsp;
+  r0 /= nsp;
   const int b = r0 / a.Hkv, g = r0 % a.Hkv;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int j0 = kt * C::BK, kj = j0 + w * 32 + l32;
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
   if (!query_range(m, j0, j0 + C::BK - 1, qlo, qhi)) { qlo = 0; qhi = -1; }
   const int q_first = (qlo / 64) * 64;
   const int nsteps = qhi < 0 ? 0 : qhi / 64 - qlo / 64 + 1;
-  const int T = nsteps * a.G;
+  const int T = nsteps * Gs;
 
   const size_t stride = (size_t)a.Hq * D;
   const TileCopy<64, C::KCH, C::NT> rcopy(tid, (uint32_t)stride);
@@ -452,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
   for (int c = 0; c < 2; ++c) toff[c] = (uint32_t)swz_off<4>(l32, 2 * hf + c);
   auto issue = [&](int t, int buf) __attribute__((always_inline)) {
     const int hh = t / nsteps, q0 = q_first + (t - hh * nsteps) * 64;
-    const int h = g * a.G + hh;
+    const int h = g * a.G + hs * Gs + hh;
     const uint8_t* Qg = static_cast<const uint8_t*>(a.q) + (seq_row0(a, b) * a.Hq + h) * D;
     const uint8_t* Og = static_cast<const uint8_t*>(a.d_o) + (seq_row0(a, b) * a.Hq + h) * D;
     rcopy.issue(Qg, (uint32_t)stride, q0, m.L, reinterpret_cast<uint16_t*>(qrows(buf)));
@@ -550,15 +556,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
     m0 = m0 < nsteps ? m0 : nsteps;
     m1 = m1 < m0 ? m0 : (m1 < nsteps ? m1 : nsteps);
   }
-  for (int hh = 0, t = 0; hh < a.G; ++hh) {
+  for (int hh = 0, t = 0; hh < Gs; ++hh) {
     for (int st = 0; st < m0; ++st, ++t) step(t, hh, q_first + st * 64, std::true_type{});
     for (int st = m0; st < m1; ++st, ++t) step(t, hh, q_first + st * 64, std::false_type{});
     for (int st = m1; st < nsteps; ++st, ++t) step(t, hh, q_first + st * 64, std::true_type{});
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
-  if (kj < seq_rows(a, b)) {
-    const float mk = a.scale * dsq / s_ds, mv = dso / 256.0f;
+  const float mk = a.scale * dsq / s_ds, mv = dso / 256.0f;
+  if (nsp > 1) {
+    // fp32 partials of this split, already scaled, in the padded layout
+    // (row (hs*B + b)*S + kj of [.., Hkv, D]) the split-reduce kernel reads
+    if (kj < seq_rows(a, b)) {
+      const size_t row = ((size_t)(hs * a.B + b) * a.S + kj) * a.Hkv + g;
+      float* dkp = a.kv_part + row * D + hf * 4;
+      float* dvp = a.kv_part + (size_t)nsp * a.B * a.S * a.Hkv * D + row * D + hf * 4;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          *reinterpret_cast<f32x4*>(dkp + db * 32 + ig * 8) =
+              f32x4{dk[db][ig * 4] * mk, dk[db][ig * 4 + 1] * mk, dk[db][ig * 4 + 2] * mk, dk[db][ig * 4 + 3] * mk};
+          *reinterpret_cast<f32x4*>(dvp + db * 32 + ig * 8) =
+              f32x4{dv[db][ig * 4] * mv, dv[db][ig * 4 + 1] * mv, dv[db][ig * 4 + 2] * mv, dv[db][ig * 4 + 3] * mv};
+        }
+    }
+  } else if (kj < seq_rows(a, b)) {
     uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ((seq_row0(a, b) + kj) * a.Hkv + g) * D + hf * 4;
     uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ((seq_row0(a, b) + kj) * a.Hkv + g) * D + hf * 4;
 #pragma unroll
@@ -613,8 +636,16 @@ static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dq_fp8_kernel<D>, dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)), dim3(C::NT), 0,
                      stream, a);
   const int nkt = (a.S + C::BK - 1) / C::BK;
-  hipLaunchKernelGGL(bwd_dkdv_fp8_kernel<D>, dim3((unsigned)((long long)nkt * a.B * a.Hkv)), dim3(C::NT), 0, stream,
-                     a);
+  hipLaunchKernelGGL(bwd_dkdv_fp8_kernel<D>, dim3((unsigned)((long long)nkt * a.B * a.Hkv * a.n_splits)), dim3(C::NT),
+                     0, stream, a);
+  if (a.n_splits > 1) {
+    // the partials are scaled already: add them with multiplier 1
+    KArgs r = a;
+    r.scale = 1.0f;
+    r.drop_t = 0;
+    const hipError_t e = launch_dkdv_split_reduce(r, D, D, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.d_offset && a.softmax_type != 0) return launch_dz_reduce(a, stream);
   return hipGetLastError();
 }

@@ -346,8 +346,11 @@ def test_fp8_validation_before_any_hip_call():
     p8 = binding.make_params(2, 100, 4, 2, 128, 128, "fp8", "causal")
     assert binding.attn_validate(p8) == 0
     assert binding.attn_fwd_workspace_size(p8) == 2 * 2 * 128 * 128  # B Hkv Dv S_pad(128)
-    # 2 x align256(B Hq S 4) + align256(B Hq ceil(S/32) 4) + B D S_pad (Hkv + 2 Hq)
-    assert binding.attn_bwd_workspace_size(p8) == 2 * 3328 + 256 + 2 * 128 * 128 * (2 + 2 * 4)
+    # 2 x align256(B Hq S 4) + align256(B Hq ceil(S/32) 4) + B D S_pad (Hkv + 2 Hq), plus the fp32
+    # partial dK, dV of the query-head splits when the split rule asks for them (as for bf16)
+    ns = binding.host_dkdv_splits(p8)
+    part = -(-ns * 2 * 100 * 2 * 256 * 4 // 256) * 256 if ns > 1 else 0
+    assert binding.attn_bwd_workspace_size(p8) == 2 * 3328 + 256 + 2 * 128 * 128 * (2 + 2 * 4) + part
     assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 192, 128, "fp8")) == -2
     assert binding.attn_validate(binding.make_params(1, 64, 2, 1, 64, 64, "fp8", dropout_p=0.1)) == -2
     assert lib.attn_fwd(ctypes.byref(p8), f, f, f, None, None, None, f, f, None, 0, None) == -2
