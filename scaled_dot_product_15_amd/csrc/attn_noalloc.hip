@@ -44,6 +44,7 @@ extern "C" int attn_bwd_noalloc(const attn_params* p, const void* q, const void*
   // Host checks before any HIP call: the problem, the pointers, the size.
   const int rc = attn_validate(p);
   if (rc != ATTN_OK) return rc;
+  if (p->dtype == ATTN_FP8) return ATTN_ERR_UNSUPPORTED;  // the bf16 / fp32 backward only
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (attn_bwd_workspace_size(p) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
   void* ws = nullptr;

@@ -305,6 +305,10 @@ def test_noalloc_rejects_before_any_hip_call():
     assert lib.attn_bwd_noalloc(ctypes.byref(small), *bad) == -1
     assert lib.attn_bwd_noalloc(ctypes.byref(P(B=0)), *ptrs) == -1
     assert lib.attn_bwd_noalloc(ctypes.byref(P(d_qk=96, d_v=96)), *ptrs) == -2
+    # FP8 problems have their own backward (attn_bwd_fp8), small or large
+    assert lib.attn_bwd_noalloc(ctypes.byref(binding.make_params(1, 64, 2, 1, 64, 64, "fp8", "causal")), *ptrs) == -2
+    assert lib.attn_bwd_noalloc(ctypes.byref(binding.make_params(8, 16384, 64, 64, 64, 64, "fp8", "causal")),
+                                *ptrs) == -2
 
 
 def test_bias_arguments_checked_before_any_hip_call():
