@@ -9,6 +9,10 @@
  *   DIR/alpha.bin       float32 [Hq];  DIR/seqlens.bin int32 [B] if has_seqlens
  *   writes DIR/{o,dq,dk,dv}.bin, DIR/lse.bin (float32 [B,Hq,S]) and, for
  *   sink softmax, DIR/doff.bin (float32 [Hq]).
+ * dtype ATTN_FP8 runs attn_fwd_fp8 and attn_bwd_fp8 instead: q, k, v hold
+ * E4M3 codes and do E5M2 codes (one byte each), DIR/descales.bin float32 [4]
+ * (q, k, v, do) and DIR/ds_scale.bin float32 [1]; O and the gradients are
+ * bf16, and DIR/amax.bin (float32 [1]) receives the amax of dS.
  * Exit status 0 on success; any failure prints its cause and exits 1. */
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
@@ -86,7 +90,9 @@ int main(int argc, char** argv) {
     if (n != 17) return fail("params.txt needs 17 fields");
   }
   if (attn_validate(&p) != ATTN_OK) return fail("attn_validate rejected the problem");
-  const size_t es = p.dtype == ATTN_BF16 ? 2 : 4;
+  const int fp8 = p.dtype == ATTN_FP8;
+  const size_t es = fp8 ? 1 : (p.dtype == ATTN_BF16 ? 2 : 4);  /* input element size */
+  const size_t eo = fp8 ? 2 : es;                              /* output element size (bf16 for FP8) */
   const size_t rows = (size_t)p.batch * p.seqlen;
   const size_t nq = rows * p.num_heads * p.head_dim_qk, nk = rows * p.num_gqa_groups * p.head_dim_qk;
   const size_t nv = rows * p.num_gqa_groups * p.head_dim_v, no = rows * p.num_heads * p.head_dim_v;
@@ -101,25 +107,43 @@ int main(int argc, char** argv) {
   int32_t* seqlens = has_seqlens ? (int32_t*)upload("seqlens.bin", (size_t)p.batch * sizeof(int32_t)) : NULL;
   if (!q || !k || !v || !d_o || !alpha || (has_seqlens && !seqlens)) return fail("cannot read or upload inputs");
 
-  void *o = NULL, *dq = NULL, *dk = NULL, *dv = NULL, *ws = NULL;
-  float *lse = NULL, *doff = NULL;
+  void *o = NULL, *dq = NULL, *dk = NULL, *dv = NULL, *ws = NULL, *wsf = NULL;
+  float *lse = NULL, *doff = NULL, *amax = NULL, *descales = NULL, *ds_scale = NULL;
   const size_t ws_bytes = attn_bwd_workspace_size(&p);
-  if (hipMalloc(&o, no * es) != hipSuccess || hipMalloc((void**)&lse, nlse * sizeof(float)) != hipSuccess ||
-      hipMalloc(&dq, nq * es) != hipSuccess || hipMalloc(&dk, nk * es) != hipSuccess ||
-      hipMalloc(&dv, nv * es) != hipSuccess || hipMalloc((void**)&doff, (size_t)p.num_heads * sizeof(float)) != hipSuccess ||
-      hipMalloc(&ws, ws_bytes) != hipSuccess)
+  const size_t wsf_bytes = attn_fwd_workspace_size(&p);
+  if (hipMalloc(&o, no * eo) != hipSuccess || hipMalloc((void**)&lse, nlse * sizeof(float)) != hipSuccess ||
+      hipMalloc(&dq, nq * eo) != hipSuccess || hipMalloc(&dk, nk * eo) != hipSuccess ||
+      hipMalloc(&dv, nv * eo) != hipSuccess || hipMalloc((void**)&doff, (size_t)p.num_heads * sizeof(float)) != hipSuccess ||
+      hipMalloc(&ws, ws_bytes ? ws_bytes : 1) != hipSuccess || hipMalloc(&wsf, wsf_bytes ? wsf_bytes : 1) != hipSuccess ||
+      hipMalloc((void**)&amax, sizeof(float)) != hipSuccess)
     return fail("hipMalloc failed");
+  if (fp8) {
+    descales = (float*)upload("descales.bin", 4 * sizeof(float));
+    ds_scale = (float*)upload("ds_scale.bin", sizeof(float));
+    if (!descales || !ds_scale) return fail("cannot read or upload the FP8 scales");
+  }
 
-  int rc = attn_fwd(&p, q, k, v, alpha, seqlens, NULL, o, lse, NULL, 0, NULL);
+  int rc = fp8 ? attn_fwd_fp8(&p, q, k, v, descales, alpha, seqlens, NULL, o, lse, wsf, wsf_bytes, NULL)
+               : attn_fwd(&p, q, k, v, alpha, seqlens, NULL, o, lse, NULL, 0, NULL);
   if (rc != ATTN_OK) return fail(attn_status_string(rc));
-  rc = attn_bwd(&p, q, k, v, o, d_o, lse, alpha, seqlens, NULL, dq, dk, dv, sink ? doff : NULL, ws, ws_bytes, NULL);
+  rc = fp8 ? attn_bwd_fp8(&p, q, k, v, o, d_o, lse, descales, ds_scale, amax, alpha, seqlens, NULL, dq, dk, dv,
+                          sink ? doff : NULL, ws, ws_bytes, NULL)
+           : attn_bwd(&p, q, k, v, o, d_o, lse, alpha, seqlens, NULL, dq, dk, dv, sink ? doff : NULL, ws, ws_bytes,
+                      NULL);
   if (rc != ATTN_OK) return fail(attn_status_string(rc));
   if (hipDeviceSynchronize() != hipSuccess) return fail("hipDeviceSynchronize failed");
 
-  if (download("o.bin", o, no * es) || download("lse.bin", lse, nlse * sizeof(float)) ||
-      download("dq.bin", dq, nq * es) || download("dk.bin", dk, nk * es) || download("dv.bin", dv, nv * es) ||
-      (sink && download("doff.bin", doff, (size_t)p.num_heads * sizeof(float))))
+  if (download("o.bin", o, no * eo) || download("lse.bin", lse, nlse * sizeof(float)) ||
+      download("dq.bin", dq, nq * eo) || download("dk.bin", dk, nk * eo) || download("dv.bin", dv, nv * eo) ||
+      (sink && download("doff.bin", doff, (size_t)p.num_heads * sizeof(float))) ||
+      (fp8 && download("amax.bin", amax, sizeof(float))))
     return fail("cannot write outputs");
+  if (fp8) {
+    hipFree(descales);
+    hipFree(ds_scale);
+  }
+  hipFree(wsf);
+  hipFree(amax);
   hipFree(q);
   hipFree(k);
   hipFree(v);

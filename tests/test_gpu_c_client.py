@@ -91,3 +91,60 @@ def test_c_client_parity(tmp_path, dtype, dqk, dv, st, drop):
         stats["doff_maxabs"] = float(np.abs(doff - r["dalpha"]).max())
     gc.log(f"  {stats}")
     gc.check(p, stats, f"C client {dtype}/{st}/{drop}")
+
+
+def test_c_client_fp8(tmp_path):
+    """attn_fwd_fp8 + attn_bwd_fp8 from C: E4M3 Q, K, V and E5M2 dO codes with
+    descales, compared with the FP8 oracle (forward and backward) within the
+    per-element bounds the FP8 tests derive."""
+    from oracle import fp8
+    from tests import test_gpu_fp8 as tf
+    p = inputs.Problem(B=2, S=190, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16", causal=True, window=(70, 0),
+                       softmax_type="learnable")
+    arr, q8, k8, v8, ds = tf._fp8_inputs(p, 89_000)
+    arr["seqlens"] = np.array([190, 77], dtype=np.int32)
+    do8 = fp8.fp8_encode(arr["do"].astype(np.float64) * tf.S_DO, fp8.E5M2)
+    gc.log("C client fp8")
+    d = tmp_path
+    for n, x in (("q", q8), ("k", k8), ("v", v8), ("do", do8)):
+        np.ascontiguousarray(x).tofile(d / f"{n}.bin")
+    arr["alpha"].astype(np.float32).tofile(d / "alpha.bin")
+    arr["seqlens"].tofile(d / "seqlens.bin")
+    np.array([ds, ds, ds, 1.0 / tf.S_DO], np.float32).tofile(d / "descales.bin")
+    np.array([tf.S_DS], np.float32).tofile(d / "ds_scale.bin")
+    (d / "params.txt").write_text(f"{p.B} {p.S} {p.Hq} {p.Hkv} 128 128 {binding.ATTN_FP8} 1 70 0 0 "
+                                  f"{binding.SOFTMAX['learnable']} 0 0 0 0 1\n")
+    res = subprocess.run([CLIENT, str(d)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stderr
+    o = _from_bf16((d / "o.bin").read_bytes(), (p.B, p.S, p.Hq, 128))
+    lse = np.fromfile(d / "lse.bin", np.float32).astype(np.float64).reshape(p.B, p.Hq, p.S)
+    grads = {n: _from_bf16((d / f"{n}.bin").read_bytes(), shape)
+             for n, shape in (("dq", q8.shape), ("dk", k8.shape), ("dv", v8.shape))}
+    doff = np.fromfile(d / "doff.bin", np.float32).astype(np.float64)
+    amax = float(np.fromfile(d / "amax.bin", np.float32)[0])
+    kw = dict(num_gqa_groups=p.Hkv, causal=True, window=p.window, softmax_type="learnable",
+              softmax_offset=arr["alpha"].astype(np.float64), seqlens=arr["seqlens"])
+    f = fp8.attention_fp8(q8, k8, v8, ds, ds, ds, **kw)
+    fin = np.isfinite(f["lse"])
+    assert (np.isfinite(lse) == fin).all() and np.abs(lse[fin] - f["lse"][fin]).max() <= 1e-3
+    assert (np.abs(o - f["o"]) <= tf._o_bound(f, v8, ds, p)).all()
+    r = fp8.attention_fp8_bwd(q8, k8, v8, o, do8, lse, ds, ds, ds, 1.0 / tf.S_DO, tf.S_DS, **kw)
+    Q = fp8.fp8_decode(q8, fp8.E4M3) * ds
+    K = fp8.fp8_decode(k8, fp8.E4M3) * ds
+    dO = fp8.fp8_decode(do8, fp8.E5M2) / tf.S_DO
+    scale = 1.0 / np.sqrt(128)
+    bounds = {n: np.zeros(r[n].shape) for n in ("dq", "dk", "dv")}
+    for b in range(p.B):
+        for h in range(p.Hq):
+            g = h // 2
+            sds = tf._ds_steps(r["p"][b, h], r["ds"][b, h], r["dp_abs"][b, h], r["delta"][b, h], tf.S_DS)
+            dsa = np.abs(fp8.fp8_decode(r["ds8"][b, h], fp8.E5M2)) / tf.S_DS
+            pa = fp8.fp8_decode(r["p8"][b, h], fp8.E4M3) / 256.0
+            bounds["dq"][b, :, h] = scale * (sds + 2e-4 * dsa) @ np.abs(K[b, :, g])
+            bounds["dk"][b, :, g] += scale * (sds + 2e-4 * dsa).T @ np.abs(Q[b, :, h])
+            bounds["dv"][b, :, g] += (tf._p_steps(r["p"][b, h]) + 2e-4 * pa).T @ np.abs(dO[b, :, h])
+    for n in ("dq", "dk", "dv"):
+        bound = bounds[n] + 2.0 ** -8 * (np.abs(r[n]) + bounds[n]) + 1e-6
+        assert (np.abs(grads[n] - r[n]) <= bound).all(), (n, float((np.abs(grads[n] - r[n]) - bound).max()))
+    assert np.abs(doff - r["dalpha"]).max() <= 1e-3 * (1 + np.abs(r["dalpha"]).max())
+    assert abs(amax - r["amax_ds"]) <= 1e-3 * r["amax_ds"]
