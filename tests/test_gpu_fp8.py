@@ -376,6 +376,60 @@ def test_fp8_backward_full_length_sampled():
             assert (np.abs(g64 - r[n]) <= bound).all(), (n, b, g, float((np.abs(g64 - r[n]) - bound).max()))
 
 
+def test_fp8_sink_padding_s8192_sampled():
+    """Learnable sink + padded lengths, S=8192 (B=4, Hq=32, Hkv=8, d=128,
+    window (4096, 0)), where the dK/dV grid splits each group's heads: the
+    forward and dQ on sampled rows, dK and dV on sampled keys."""
+    import torch
+    p = inputs.workload_configs()[5][1]
+    arr, q8, k8, v8, ds = _fp8_inputs(p, 90_000)
+    sl = arr["seqlens"]
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, 128, 128, "fp8", "causal", p.window, None, p.softmax_type)
+    gc.log(f"fp8 sink + padding S=8192, seqlens {sl.tolist()}, head splits {binding.host_dkdv_splits(pp)}")
+    do8, o, lse, dq, dk, dv, doff, amax = _bwd_run(p, arr, q8, k8, v8, ds, 90_000, sl, True, p.window, p.softmax_type)
+    o64, lse64 = inputs.exact_f64(o), inputs.exact_f64(lse)
+    alpha = arr["alpha"].astype(np.float64)
+    kw = dict(num_gqa_groups=p.Hkv, causal=True, window=p.window, seqlens=sl)
+    args = (q8, k8, v8, o64, do8, lse64, ds, ds, ds, 1.0 / S_DO, S_DS)
+    K = fp8.fp8_decode(k8, fp8.E4M3) * ds
+    Q = fp8.fp8_decode(q8, fp8.E4M3) * ds
+    dO = fp8.fp8_decode(do8, fp8.E5M2) / S_DO
+    scale = 1.0 / np.sqrt(128)
+    for b, h in ((0, 0), (2, 13), (3, 31)):
+        L = int(sl[b])
+        rows = np.array(sorted({0, 1, 4095, L // 2, L - 1, min(L, p.S - 1), p.S - 1}))
+        rf = fp8.attention_fp8_rows(q8, k8, v8, ds, ds, ds, b=b, h=h, rows=rows, softmax_type=p.softmax_type,
+                                    softmax_offset=alpha, **kw)
+        fin = np.isfinite(rf["lse"])
+        assert (np.isfinite(lse64[b, h, rows]) == fin).all()
+        assert np.abs(lse64[b, h, rows][fin] - rf["lse"][fin]).max() <= 1e-3
+        assert np.abs(o64[b, rows, h] - rf["o"]).max() <= gc.TOL["bf16"]["o_maxabs"]
+        r = fp8.attention_fp8_bwd_rows(*args, b=b, h=h, rows=rows, **kw)
+        sds = _ds_steps(r["p"], r["ds"], r["dp_abs"], r["delta"], S_DS)
+        dsa = np.abs(fp8.fp8_decode(r["ds8"], fp8.E5M2)) / S_DS
+        bound = scale * (sds + 2e-4 * dsa) @ np.abs(K[b, :, h // 4])
+        bound = bound + 2.0 ** -8 * (np.abs(r["dq"]) + bound) + 1e-6
+        got = inputs.exact_f64(dq[b, rows, h])
+        assert (np.abs(got - r["dq"]) <= bound).all(), (b, h, float((np.abs(got - r["dq"]) - bound).max()))
+    for b, g in ((0, 0), (1, 5), (3, 7)):
+        L = int(sl[b])
+        keys = np.array(sorted({0, 127, 128, L // 3, L - 1, min(L, p.S - 1)}))
+        r = fp8.attention_fp8_bwd_keys(*args, b=b, g=g, keys=keys, **kw)
+        bdk = np.zeros(r["dk"].shape)
+        bdv = np.zeros(r["dv"].shape)
+        for n, h in enumerate(range(g * 4, g * 4 + 4)):
+            sds = _ds_steps(r["p"][n], r["ds"][n], r["dp_abs"][n], r["delta"][n], S_DS)
+            dsa = np.abs(fp8.fp8_decode(r["ds8"][n], fp8.E5M2)) / S_DS
+            pa = fp8.fp8_decode(r["p8"][n], fp8.E4M3) / 256.0
+            bdk += scale * (sds + 2e-4 * dsa).T @ np.abs(Q[b, :, h])
+            bdv += (_p_steps(r["p"][n]) + 2e-4 * pa).T @ np.abs(dO[b, :, h])
+        for n, got, bound in (("dk", dk[b, keys, g], bdk), ("dv", dv[b, keys, g], bdv)):
+            g64 = inputs.exact_f64(got)
+            bound = bound + 2.0 ** -8 * (np.abs(r[n]) + bound) + 1e-6
+            assert (np.abs(g64 - r[n]) <= bound).all(), (n, b, g, float((np.abs(g64 - r[n]) - bound).max()))
+    assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
+
+
 def test_fp8_backward_packed_equals_padded_and_reproducible():
     import torch
     p = inputs.Problem(B=3, S=256, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16", causal=True, window=(60, 0),
