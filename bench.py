@@ -482,6 +482,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(p, arr, args.cpu_groups)
+        res["cpu_baseline"]["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
     print(json.dumps(res), flush=True)
 
 

@@ -76,6 +76,9 @@
 
 namespace sdpa {
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 template <int DQK, int DV, bool BIAS>
 struct DkdvCfg {
   static constexpr int BN = 128;  // keys per workgroup (32 per wave)
@@ -85,20 +88,27 @@ struct DkdvCfg {
   static constexpr int QCH = DQK / 8, OCH = DV / 8;    // 16-byte chunks per row
   static constexpr int QT = BMQ * DQK, OT = BMQ * DV;  // elements per tile
   static constexpr int BT = BIAS ? BMQ * BN : 0;       // bias tile [BMQ][BN]
-  static constexpr int STAGE = QT + OT + BT + 2 * BMQ * 2;  // Q, dO, bias, lse2 and delta (f32)
-  static constexpr int LDS_ELEMS = NBUF * STAGE;
+  static constexpr int STAGE = QT + OT + BT;  // tiles of a ring slot: Q, dO, bias
+  static constexpr int RT = 2 * BMQ * 2;      // row terms of a ring slot: lse2 and delta (f32)
+  static constexpr int LDS_ELEMS = NBUF * (STAGE + RT);
 };
 
 template <int DQK, int DV, bool DROP, bool BIAS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   using C = DkdvCfg<DQK, DV, BIAS>;
+  // Without dropout, delta is folded into the dP products: their
+  // accumulator starts at delta and V enters negated, so it ends at
+  // delta - dP and P times it is -dS with no subtraction; dK then
+  // accumulates -dK, negated at the end (all exact sign changes).
+  constexpr bool FOLD = !DROP;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  // Ring slot `buf`: Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN] (swizzled),
-  // lse2 [BMQ], delta [BMQ].
+  // Ring slot `buf`: tiles Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN]
+  // (swizzled) at buf * STAGE; after the NBUF slots' tiles, its row terms
+  // lse2 [BMQ] and delta [BMQ].
   auto qtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE; };
   auto otile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::QT; };
   auto btile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::QT + C::OT; };
-  auto lse_s = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<float*>(lds + buf * C::STAGE + C::QT + C::OT + C::BT); };
+  auto lse_s = [&](int buf) __attribute__((always_inline)) { return reinterpret_cast<float*>(lds + C::NBUF * C::STAGE + buf * C::RT); };
   auto delta_s = [&](int buf) __attribute__((always_inline)) { return lse_s(buf) + C::BMQ; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -148,8 +158,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     for (int ks = 0; ks < DQK / 16; ++ks)
       kreg[ks] = as_bf16x8(buf_load16(kres, (uint32_t)(kj * kstride + ks * 16 + hf * 8) * 2));
 #pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-      vreg[ks] = as_bf16x8(buf_load16(vres, (uint32_t)(kj * vstride + ks * 16 + hf * 8) * 2));
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      u32x4 vw = buf_load16(vres, (uint32_t)(kj * vstride + ks * 16 + hf * 8) * 2);
+      if constexpr (FOLD) vw ^= 0x80008000u;  // -V, exact
+      vreg[ks] = as_bf16x8(vw);
+    }
   }
   f32x16 dk[DQK / 32], dv[DV / 32];
 #pragma unroll
@@ -196,6 +209,57 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   const RowReads<C::OCH> ord(lane);
   const TrReads<C::QCH> qtr(lane);
   const TrReads<C::OCH> otr(lane);
+  // A DS instruction's immediate offset has 16 bits.  Tiles that start at
+  // 64 KiB or beyond are read through copies of the per-lane offsets that
+  // already hold the 64 KiB, and the row terms through one per-lane base;
+  // both are opaque to the compiler, so they stay in registers instead of
+  // being rebuilt with an add before every read.  (Not in the 192-dim
+  // dropout variant, whose registers are full: there the compiler adds.)
+  constexpr int kFar = 65536;  // bytes
+  constexpr bool FAR = !(DROP && DQK > 128);
+  auto opaque = [](uint32_t& x) __attribute__((always_inline)) { asm volatile("" : "+v"(x)); };
+  RowReads<C::QCH> qrd_f = qrd;
+  TrReads<C::QCH> qtr_f = qtr;
+  RowReads<C::OCH> ord_f = ord;
+  TrReads<C::OCH> otr_f = otr;
+  if constexpr (FAR) {
+#pragma unroll
+    for (int i = 0; i < C::QCH / 2; ++i) { qrd_f.off[i] += kFar; opaque(qrd_f.off[i]); }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < C::QCH / 4; ++i) { qtr_f.off[h][i] += kFar; opaque(qtr_f.off[h][i]); }
+  }
+  if constexpr (FAR && C::OCH == C::QCH) {
+    ord_f = qrd_f;  // same offsets: share the registers
+    otr_f = qtr_f;
+  } else if constexpr (FAR) {
+#pragma unroll
+    for (int i = 0; i < C::OCH / 2; ++i) { ord_f.off[i] += kFar; opaque(ord_f.off[i]); }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < C::OCH / 4; ++i) { otr_f.off[h][i] += kFar; opaque(otr_f.off[h][i]); }
+  }
+  // Row reads / transpose reads of the tile at element offset O (a constant).
+  auto rows_at = [&](auto oc, const auto& near, const auto& far, int rb, int ks) __attribute__((always_inline)) {
+    constexpr int O = decltype(oc)::value;
+    if constexpr (FAR && 2 * O >= kFar) return far.read(lds + O - kFar / 2, rb, ks);
+    else return near.read(lds + O, rb, ks);
+  };
+  auto tr_at = [&](auto oc, const auto& near, const auto& far, int pos0, int db) __attribute__((always_inline)) {
+    constexpr int O = decltype(oc)::value;
+    if constexpr (FAR && 2 * O >= kFar) return far.read(lds + O - kFar / 2, pos0, db);
+    else return near.read(lds + O, pos0, db);
+  };
+  // lse2 (term 0) or delta (term 1) of rows r .. r+3 of ring slot buf, r a
+  // constant plus hf * 4 (the lane half's share).
+  uint32_t rt_lane = (uint32_t)(C::NBUF * C::STAGE * 2 + hf * 16);
+  if constexpr (FAR) opaque(rt_lane);
+  auto rterm = [&](int buf, int term, int r) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(lds) + rt_lane +
+                                           (buf * C::RT * 2 + term * C::BMQ * 4 + r * 4));
+  };
   const TileCopy<C::BMQ, C::BN / 8, C::NT> bcopy(tid, (uint32_t)a.S * 2);
   const TrReads<C::BN / 8> btr(lane);
   auto issue_stage = [&](const StageWalk& st, int buf) __attribute__((always_inline)) {
@@ -223,13 +287,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   };
 
   const float c = a.scale_log2;
+  // delta of rows rb + acc_row(i, hf) of a stage: the dP accumulator's start.
+  auto delta_init = [&](int buf, int rb) __attribute__((always_inline)) {
+    f32x16 r;
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const f32x4 d = rterm(buf, 1, rb + ig * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[ig * 4 + e] = d[e];
+    }
+    return r;
+  };
   f32x16 S[2], DP[2];        // S / dP of the block in B and of the one in A
   u32x4 PW[2][2], DW[2][2];  // bf16 P / dS pairs: B operands of the block's two 16-row K-steps
 
   // A(u): S and dP of block u (rows rb .. rb+31 of a ring slot).
   auto phase_a = [&](const uint16_t* Qs, const uint16_t* Os, int rb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     s = f32x16{};
-    dp = f32x16{};
+    dp = FOLD ? delta_init(0, rb) : f32x16{};
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) s = mfma32(as_bf16x8(qrd.read(Qs, rb, ks)), kreg[ks], s);
 #pragma unroll
@@ -259,14 +334,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       return sv;
     }
   };
-  auto phase_b = [&](const float* ls, const float* dl, const uint16_t* bt, int rb, int qrow0, const uint32_t(&rnd4)[4],
+  auto phase_b = [&](int buf, const uint16_t* bt, int rb, int qrow0, const uint32_t(&rnd4)[4],
                      const f32x16& s, const f32x16& dp, u32x4(&pw)[2], u32x4(&dw)[2]) __attribute__((always_inline)) {
     const int lo_r = qlo_k - (qrow0 + hf * 4), hi_r = qhi_k - (qrow0 + hf * 4);
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const int qo = rb + ig * 8 + hf * 4;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qo);
+      const f32x4 l4 = rterm(buf, 0, rb + ig * 8);
+      f32x4 d4 = {};
+      if constexpr (!FOLD) d4 = rterm(buf, 1, rb + ig * 8);
       u32x2 bw = {0u, 0u};
       if constexpr (BIAS) bw = bias_chunk(bt, rb, ig);
       const uint32_t rnd = rnd4[ig];  // dropout bytes of rows qrow0 + ig*8 + hf*4 + 0..3, key kj
@@ -287,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
             dpz = kp ? dpz * dg.scale : 0.0f;
           }
           p2[v] = pk;
-          s2[v] = pv * (dpz - d4[e]);
+          s2[v] = FOLD ? pv * dpz : pv * (dpz - d4[e]);
         }
         pp[u2] = pack_bf16(p2[0], p2[1]);
         dd[u2] = pack_bf16(s2[0], s2[1]);
@@ -330,6 +405,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // next iteration, read during the last chunk of the current one.
   bf16x8 opa[2][EA], opc[2][EC];
   f32x4 l4[2], d4[2];
+  f32x16 dini;  // FOLD: start of the dP accumulator of block u+1
+  constexpr int KDP = NSK / EA;  // chunk whose A products start dP
+  static_assert(KDP > 0, "the dP start is read a chunk ahead");
   u32x2 b4[2] = {{0u, 0u}, {0u, 0u}};  // bias of the chunk's four rows (BIAS)
   // Chunk k's LDS reads for the iteration of phase P into set st: A(u+1)'s
   // operands (RA), C(u-1)'s (RC), B(u)'s lse2 / delta (RL).
@@ -341,22 +419,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int e = 0; e < EA; ++e) {
         const int i = k * EA + e;
-        opa[st][e] = as_bf16x8(i < NSK ? qrd.read(qtile(slot_n), nxt * 32, i)
-                                       : ord.read(otile(slot_n), nxt * 32, i - NSK));
+        opa[st][e] = as_bf16x8(i < NSK ? rows_at(IC<slot_n * C::STAGE>{}, qrd, qrd_f, nxt * 32, i)
+                                       : rows_at(IC<slot_n * C::STAGE + C::QT>{}, ord, ord_f, nxt * 32, i - NSK));
       }
+      if constexpr (FOLD && k == KDP) dini = delta_init(slot_n, nxt * 32);
     }
     if constexpr (decltype(rc)::value) {
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
         const int i = k * EC + e, kk = i / (NDV + NDK), j = i % (NDV + NDK);
-        opc[st][e] = j < NDV ? otr.read(otile(slot_p), nxt * 32 + kk * 16, j)
-                             : qtr.read(qtile(slot_p), nxt * 32 + kk * 16, j - NDV);
+        opc[st][e] = j < NDV ? tr_at(IC<slot_p * C::STAGE + C::QT>{}, otr, otr_f, nxt * 32 + kk * 16, j)
+                             : tr_at(IC<slot_p * C::STAGE>{}, qtr, qtr_f, nxt * 32 + kk * 16, j - NDV);
       }
     }
     if constexpr (decltype(rl)::value) {
-      const int qo = cur * 32 + k * 8 + hf * 4;
-      l4[st] = *reinterpret_cast<const f32x4*>(lse_s(slot_u) + qo);
-      d4[st] = *reinterpret_cast<const f32x4*>(delta_s(slot_u) + qo);
+      l4[st] = rterm(slot_u, 0, cur * 32 + k * 8);
+      if constexpr (!FOLD) d4[st] = rterm(slot_u, 1, cur * 32 + k * 8);
       if constexpr (BIAS) b4[st] = bias_chunk(btile(slot_u), cur * 32, k);
     }
   };
@@ -391,8 +469,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     } else {
       walk_next(b_walk);  // block u opens a new stage
     }
-    const float* ls = lse_s(slot_u);  // B(u): rows cur*32 of its stage
-    const float* dl = delta_s(slot_u);
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
     const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
     uint32_t rnd_u[4] = {0u, 0u, 0u, 0u};
@@ -410,7 +486,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       for (int e = 0; e < EA; ++e) {
         const int i = k * EA + e;
         if (i < NSK) S[nxt] = mfma32(opa[st][e], kreg[i], i == 0 ? f32x16{} : S[nxt]);
-        else DP[nxt] = mfma32(opa[st][e], vreg[i - NSK], i == NSK ? f32x16{} : DP[nxt]);
+        else DP[nxt] = mfma32(opa[st][e], vreg[i - NSK], i == NSK ? (FOLD ? dini : f32x16{}) : DP[nxt]);
       }
       // B(u) without the mask, rows k*8 + hf*4 + 0..3 of the block:
       // accumulator elements 4k .. 4k+3, which are B-operand elements
@@ -431,7 +507,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
             dpz = kp ? dpz * dg.scale : 0.0f;
           }
           p2[v] = pk;
-          s2[v] = pv * (dpz - d4[st][e]);
+          s2[v] = FOLD ? pv * dpz : pv * (dpz - d4[st][e]);
         }
         pp[u2] = pack_bf16(p2[0], p2[1]);
         dd[u2] = pack_bf16(s2[0], s2[1]);
@@ -480,7 +556,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Blocks that some of this wave's (row, key) pairs cannot see (diagonal,
     // window edge, padding): redo B with the mask.
     if (!(q_u >= all_lo && q_u + 31 <= all_hi))
-      phase_b(ls, dl, btile(slot_u), cur * 32, q_u, rnd_u, S[cur], DP[cur], PW[cur], DW[cur]);
+      phase_b(slot_u, btile(slot_u), cur * 32, q_u, rnd_u, S[cur], DP[cur], PW[cur], DW[cur]);
   };
 
   if (NB > 0) {
@@ -497,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     phase_a(qtile(0), otile(0), 32, S[1], DP[1]);
     uint32_t rnd_0[4] = {0u, 0u, 0u, 0u};
     if constexpr (DROP) drop_rows(b * a.Hq + g * a.G + hs * Gs + b_walk.hh, b_walk.q0, rnd_0);
-    phase_b(lse_s(0), delta_s(0), btile(0), 0, b_walk.q0, rnd_0, S[0], DP[0], PW[0], DW[0]);
+    phase_b(0, btile(0), 0, b_walk.q0, rnd_0, S[0], DP[0], PW[0], DW[0]);
     read_ahead(std::integral_constant<int, 0>{});  // first chunk of iteration 1
     // Iterations 1 .. NI in trips of six (one per phase), padded past the
     // last block NB-1 with empty blocks: their stages copy rows past the
@@ -527,8 +603,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
       for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
-          u32x2 val = {pack_bf16(dk[db][ig * 4] * a.scale, dk[db][ig * 4 + 1] * a.scale),
-                       pack_bf16(dk[db][ig * 4 + 2] * a.scale, dk[db][ig * 4 + 3] * a.scale)};
+          const float ks = FOLD ? -a.scale : a.scale;
+          u32x2 val = {pack_bf16(dk[db][ig * 4] * ks, dk[db][ig * 4 + 1] * ks),
+                       pack_bf16(dk[db][ig * 4 + 2] * ks, dk[db][ig * 4 + 3] * ks)};
           *reinterpret_cast<u32x2*>(dkp + db * 32 + ig * 8) = val;
         }
 #pragma unroll
@@ -551,7 +628,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig)
           *reinterpret_cast<f32x4*>(dkp + db * 32 + ig * 8) =
-              f32x4{dk[db][ig * 4], dk[db][ig * 4 + 1], dk[db][ig * 4 + 2], dk[db][ig * 4 + 3]};
+              FOLD ? -f32x4{dk[db][ig * 4], dk[db][ig * 4 + 1], dk[db][ig * 4 + 2], dk[db][ig * 4 + 3]}
+                   : f32x4{dk[db][ig * 4], dk[db][ig * 4 + 1], dk[db][ig * 4 + 2], dk[db][ig * 4 + 3]};
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
