@@ -59,6 +59,12 @@ struct DqCfg {
 template <int DQK, int DV, bool DROP, bool BIAS>
 __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) ? 2 : 1) void bwd_dq_bf16_kernel(KArgs a) {
   using C = DqCfg<DQK, DV>;
+  // Without dropout or bias (and below 192 dims, whose registers are
+  // full), delta is folded into the dP products: the accumulator starts at
+  // delta (a loop-invariant register block) and dO enters negated, so it
+  // ends at delta - dP and P times it is -dS with no subtraction; dQ then
+  // accumulates -dQ, negated by the final scale (exact sign changes).
+  constexpr bool FOLD = !DROP && !BIAS && DQK <= 128;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT); };
   auto vtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT) + C::KT; };
@@ -138,6 +144,10 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
   f32x16 dq[DQK / 32];
 #pragma unroll
   for (int i = 0; i < DQK / 32; ++i) dq[i] = f32x16{};
+  // -dO^T for the folded dP products.
+  bf16x8 oneg[DV / 16];
+#pragma unroll
+  for (int ks = 0; ks < DV / 16; ++ks) oneg[ks] = as_bf16x8(__builtin_bit_cast(u32x4, oreg[ks]) ^ 0x80008000u);
 
   int lo = 0, hi = -1;
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
@@ -192,7 +202,15 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     }
     f32x16 st[C::BN / 32], dpt[C::BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < C::BN / 32; ++kb) { st[kb] = f32x16{}; dpt[kb] = f32x16{}; }
+    for (int kb = 0; kb < C::BN / 32; ++kb) {
+      st[kb] = f32x16{};
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dpt[kb][i] = dl;
+      } else {
+        dpt[kb] = f32x16{};
+      }
+    }
     prio_mfma();
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks)
@@ -206,7 +224,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     for (int ks = 0; ks < DV / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < C::BN / 32; ++kb)
-        dpt[kb] = mfma32(as_bf16x8(vrd.read(Vs, kb * 32, ks)), oreg[ks], dpt[kb]);
+        dpt[kb] = mfma32(as_bf16x8(vrd.read(Vs, kb * 32, ks)), FOLD ? oneg[ks] : oreg[ks], dpt[kb]);
     prio_valu();
     const int lo_r = klo - base, hi_r = khi - base;
     bf16x8 dsb[C::BN / 16];
@@ -228,7 +246,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
             }
             float dpz = dpt[kb][i];
             if constexpr (DROP) dpz = drop_keep(rnd[kb][i >> 2], i & 3, dg.t) ? dpz * dg.scale : 0.0f;
-            v2[u] = pv * (dpz - dl);
+            v2[u] = FOLD ? pv * dpz : pv * (dpz - dl);
           }
           t[e] = pack_bf16(v2[0], v2[1]);
         }
@@ -329,8 +347,9 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
     for (int db = 0; db < DQK / 32; ++db)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
-        u32x2 val = {pack_bf16(dq[db][ig * 4] * a.scale, dq[db][ig * 4 + 1] * a.scale),
-                     pack_bf16(dq[db][ig * 4 + 2] * a.scale, dq[db][ig * 4 + 3] * a.scale)};
+        const float qs = FOLD ? -a.scale : a.scale;
+        u32x2 val = {pack_bf16(dq[db][ig * 4] * qs, dq[db][ig * 4 + 1] * qs),
+                     pack_bf16(dq[db][ig * 4 + 2] * qs, dq[db][ig * 4 + 3] * qs)};
         *reinterpret_cast<u32x2*>(dqp + db * 32 + ig * 8) = val;
       }
   }
