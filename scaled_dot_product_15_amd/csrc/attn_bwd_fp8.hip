@@ -14,11 +14,12 @@
 //     dQ_i  = scale dk / s_ds sum_j E5M2(s_ds dS_ij) K8_j
 // summed over the query heads of a KV head's group for dK, dV; amax = max |dS|.
 //
-// Launch order: a pre-pass (delta, LSE log2 e, sink-gradient partials per 32
-// rows), transposes of K, Q and dO into the workspace ([dims][positions] with
-// the positions of each 64-group in the byte order of the accumulator-side
-// operands, fp8_key_slot), then the dQ kernel and the dK/dV kernel; both
-// recompute S and dP (deterministic, no atomics on the gradients).
+// Launch order: transposes of K, Q and dO into the workspace ([dims]
+// [positions] with the positions of each 64-group in the byte order of the
+// accumulator-side operands, fp8_key_slot), then the dQ kernel, which also
+// runs the pre-pass for its rows (delta, LSE log2 e, sink-gradient partials
+// per 32 rows), and the dK/dV kernel; both recompute S and dP
+// (deterministic, no atomics on the gradients).
 //
 // Products and operand formats (A x B, cbsz / blgp = 0 E4M3, 1 E5M2):
 //   dQ kernel (lane = query row, 16 keys of each 32-key block per lane):
@@ -139,64 +140,6 @@ __global__ __launch_bounds__(256) void fp8_transpose_kernel(KArgs a, const uint8
   }
 }
 
-// Pre-pass: delta' = ddo (dO8 . O) s_ds / 256 and l8 = LSE log2 e - 8 (both 0
-// past the valid length), and the sink-gradient partial -sum exp(z - LSE_i)
-// delta_i of the block's 32 rows (unscaled delta).  Grid (32-row chunks, Hq,
-// B); 16 lanes per row, each 8 (D = 128) or 4 (D = 64) dims; the lane sums
-// meet in a fixed butterfly.
-template <int DV>
-__global__ __launch_bounds__(256) void fp8_bwd_pre_kernel(KArgs a) {
-  constexpr int PER = DV / 16;
-  __shared__ float dzs[32];
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
-  const int L = seq_len(a, b);
-  const float ddo = a.fp8_descale[3];
-  const float dsc = a.ds_scale[0] * (1.0f / 256.0f);
-  const float z = sink_logit(a, h);
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = grp * 2 + rr, i = chunk * 32 + r;
-    float part = 0.0f;
-    if (i < L) {
-      const size_t row = (seq_row0(a, b) + i) * a.Hq + h;
-      const uint8_t* dop = static_cast<const uint8_t*>(a.d_o) + row * DV + sub * PER;
-      const uint16_t* op = static_cast<const uint16_t*>(a.o) + row * DV + sub * PER;
-      uint32_t cw[PER / 4];
-      uint32_t ow[PER / 2];
-#pragma unroll
-      for (int e = 0; e < PER / 4; ++e) cw[e] = reinterpret_cast<const uint32_t*>(dop)[e];
-#pragma unroll
-      for (int e = 0; e < PER / 2; ++e) ow[e] = reinterpret_cast<const uint32_t*>(op)[e];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float ov = (e & 1) ? bf16_hi(ow[e >> 1]) : bf16_lo(ow[e >> 1]);
-        part += e5m2_value(cw[e >> 2] >> (8 * (e & 3))) * ov;
-      }
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off);
-    if (sub == 0) {
-      const float delta = i < L ? part * ddo : 0.0f;
-      float dz = 0.0f;
-      if (i < a.S) {
-        const size_t idx = ((size_t)b * a.Hq + h) * a.S + i;
-        const float lse = i < L ? a.lse[idx] : 0.0f;
-        a.delta[idx] = delta * dsc;
-        a.lse2[idx] = i < L ? lse * kLog2e - 8.0f : 0.0f;
-        if (a.softmax_type != 0 && i < L && lse > -__builtin_inff()) dz = -expf(z - lse) * delta;
-      }
-      dzs[r] = dz;
-    }
-  }
-  __syncthreads();
-  if (tid == 0 && a.softmax_type != 0) {
-    float s = 0.0f;
-    for (int r = 0; r < 32; ++r) s += dzs[r];
-    a.dz_partial[((size_t)b * a.Hq + h) * a.n_chunks + chunk] = s;
-  }
-}
-
 template <int D>
 struct Fp8BwdCfg {
   static constexpr int BM = 128;  // dQ: query rows per workgroup (32 per wave)
@@ -256,9 +199,49 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
                       buf_load16(ores, (uint32_t)(qi * stride + (4 * k + 2 + hf) * 16)));
     }
   }
-  const size_t rowx = ((size_t)b * a.Hq + h) * a.S + (qi < a.S ? qi : a.S - 1);
-  const float l8 = qi < m.L ? a.lse2[rowx] : 0.0f;  // LSE log2 e - 8
-  const float dl = qi < m.L ? a.delta[rowx] : 0.0f;  // delta s_ds / 256
+  // Backward pre-pass for this wave's 32 rows, fused here (the dK/dV kernel
+  // runs after this one): delta = rowsum(dO * O) from the dequantized dO
+  // codes (each lane half holds half of the row's dims), stored pre-scaled
+  // as delta s_ds / 256 with LSE log2 e - 8 for both kernels (0 past the
+  // valid length); for a sink logit z, the partial sum over the 32 rows of
+  // dL/dz_i = -exp(z - LSE_i) delta_i, added up over the chunks later.
+  float l8 = 0.0f, dl = 0.0f;  // LSE log2 e - 8, delta s_ds / 256
+  {
+    const size_t stride = (size_t)a.Hq * D;  // elements between rows
+    const __amdgpu_buffer_rsrc_t outres = buf_rsrc(static_cast<const uint16_t*>(a.o) + (seq_row0(a, b) * a.Hq + h) * D,
+                                                   (uint32_t)(m.L * stride * 2));
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < C::NKS; ++k)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = 4 * k + 2 * c + hf;  // 16-dim chunk held in words 4c .. 4c+3 of oreg[k]
+        const u32x4 o0 = buf_load16(outres, (uint32_t)((qi * stride + ch * 16) * 2));
+        const u32x4 o1 = buf_load16(outres, (uint32_t)((qi * stride + ch * 16 + 8) * 2));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t ow = e < 8 ? o0[e >> 1] : o1[(e - 8) >> 1];
+          const float ov = (e & 1) ? bf16_hi(ow) : bf16_lo(ow);
+          part += e5m2_value((uint32_t)oreg[k][4 * c + (e >> 2)] >> (8 * (e & 3))) * ov;
+        }
+      }
+    const float delta = qi < m.L ? halves_sum(part) * a.fp8_descale[3] : 0.0f;
+    const size_t row = ((size_t)b * a.Hq + h) * a.S + qi;
+    const float lse = qi < m.L ? a.lse[row] : 0.0f;
+    l8 = qi < m.L ? lse * kLog2e - 8.0f : 0.0f;
+    dl = delta * (a.ds_scale[0] * (1.0f / 256.0f));
+    if (hf == 0 && qi < a.S) {
+      a.delta[row] = dl;
+      a.lse2[row] = l8;
+    }
+    if (a.softmax_type != 0) {
+      float dz = (hf == 0 && qi < m.L && lse > -__builtin_inff()) ? -expf(sink_logit(a, h) - lse) * delta : 0.0f;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) dz += __shfl_xor(dz, off);
+      const int qw0 = i0 + w * 32;
+      if (lane == 0 && qw0 < a.S) a.dz_partial[((size_t)b * a.Hq + h) * a.n_chunks + qw0 / 32] = dz;
+    }
+  }
   const float dsk = a.fp8_descale[1];
   const float s_ds = a.ds_scale[0];
   const float c8 = a.scale_log2 * a.fp8_descale[0] * dsk;                      // raw score -> log2 units
@@ -600,8 +583,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_fp8_kernel(KArgs a) {
 
 template __global__ void fp8_transpose_kernel<64>(KArgs, const uint8_t*, int, uint8_t*);
 template __global__ void fp8_transpose_kernel<128>(KArgs, const uint8_t*, int, uint8_t*);
-template __global__ void fp8_bwd_pre_kernel<64>(KArgs);
-template __global__ void fp8_bwd_pre_kernel<128>(KArgs);
 template __global__ void bwd_dq_fp8_kernel<64>(KArgs);
 template __global__ void bwd_dq_fp8_kernel<128>(KArgs);
 template __global__ void bwd_dkdv_fp8_kernel<64>(KArgs);
@@ -628,7 +609,6 @@ static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
   a.s_pad = (a.S + 63) / 64 * 64;
   a.n_chunks = (a.S + 31) / 32;
   hipLaunchKernelGGL(fp8_amax_zero_kernel, dim3(1), dim3(64), 0, stream, a.amax_out);
-  hipLaunchKernelGGL(fp8_bwd_pre_kernel<D>, dim3(a.n_chunks, a.Hq, a.B), dim3(256), 0, stream, a);
   launch_fp8_transpose(a, a.k, a.Hkv, a.kt_t, D, stream);
   launch_fp8_transpose(a, a.q, a.Hq, a.qt_t, D, stream);
   launch_fp8_transpose(a, a.d_o, a.Hq, a.dot_t, D, stream);
