@@ -246,6 +246,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
   const float s_ds = a.ds_scale[0];
   const float c8 = a.scale_log2 * a.fp8_descale[0] * dsk;                      // raw score -> log2 units
   const float cdp = a.fp8_descale[3] * a.fp8_descale[2] * s_ds * (1.0f / 256.0f);  // raw dP -> dP s_ds / 256
+  // The dQ products need only x = 256 P (cdp dP_raw - delta'), so cdp moves
+  // into the exponent and delta' / cdp into the start of the dP accumulator:
+  // x = exp2(s c8 - (l8 - log2 cdp)) (dP_raw - delta' / cdp), one multiply
+  // per element (the descales and s_ds are positive).
+  const float l8c = l8 - __log2f(cdp);
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dinit[i] = -dl / cdp;
 
   int lo = 0, hi = -1;
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      dp[kb] = dinit;
     }
 #pragma unroll
     for (int k = 0; k < C::NKS; ++k)
@@ -320,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_fp8_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * q + e, off = kb * 32 + q * 8 + e;
-          float pp = fast_exp2(fmaf(s[kb][i], c8, -l8));
+          float pp = fast_exp2(fmaf(s[kb][i], c8, -l8c));
           if constexpr (MASKED) pp = (off >= lo_r && off <= hi_r) ? pp : 0.0f;
-          x[e] = pp * fmaf(dp[kb][i], cdp, -dl);
+          x[e] = pp * dp[kb][i];
           amax = fmaxf(amax, fabsf(x[e]));
         }
         dw[kb * 4 + q] = pack_e5m2(x[0], x[1], x[2], x[3]);
