@@ -85,12 +85,13 @@ def effective_flops(pairs, d_qk, d_v):
     return 2 * pairs * (d_qk + d_v), 2 * pairs * (3 * d_qk + 2 * d_v)
 
 
-def kernel_flops_per_pair(d_qk, d_v):
-    """Algorithmic MFMA FLOPs per visible pair of each kernel."""
+def kernel_flops_per_pair(d_qk, d_v, stored_ds=False):
+    """Algorithmic MFMA FLOPs per visible pair of each kernel (with stored dS
+    the dQ kernel only contracts dS with K)."""
     return {
         "fwd": 2 * (d_qk + d_v),                 # S = QK^T, O = PV
         "bwd_dkdv": 2 * (2 * d_qk + 2 * d_v),    # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
-        "bwd_dq": 2 * (2 * d_qk + d_v),          # S, dP, dQ = dS K
+        "bwd_dq": 2 * d_qk if stored_ds else 2 * (2 * d_qk + d_v),  # [S, dP,] dQ = dS K
     }
 
 
@@ -302,6 +303,10 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 (E4M3) forward instead: Q, K, V quantized on the device with "
                          "delayed-scaling scales, then attn_fwd_fp8")
+    ap.add_argument("--dq-path", choices=("default", "recompute", "stored-ds"), default="default",
+                    help="backward path: the dQ kernel recomputes S and dP (smaller workspace), or computes "
+                         "dQ from the dS the dK/dV kernel stores; default = the binding's choice "
+                         "(binding.prefers_stored_ds)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 launches) to "
                          "calibrate the HBM byte counters, then exit")
@@ -365,14 +370,23 @@ def main():
     outs = (dq, dk, dv, doff)
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"],
                              p.window, kw["scale_factor"], p.softmax_type, args.dropout)
-    ws = torch.empty(binding.attn_bwd_workspace_size(pp), dtype=torch.uint8, device="cuda")
+    # The workspace decides the backward's path: with room for the dS blocks
+    # the dK/dV kernel stores dS and the dQ kernel contracts it with K.
+    ds_size = binding.attn_bwd_ds_workspace_size(pp) if args.bias == "none" else 0
+    stored_ds = ds_size > 0 and (args.dq_path == "stored-ds" or
+                                 (args.dq_path == "default" and binding.prefers_stored_ds(pp)))
+    ws = torch.empty(ds_size if stored_ds else binding.attn_bwd_workspace_size(pp), dtype=torch.uint8,
+                     device="cuda")
     fast = dict(kw, check_seqlens=False)
     stream = torch.cuda.current_stream()
-    # Backward stages (1..4) that launch a kernel for this workload: in bf16 the
-    # pre-pass runs inside the dQ kernel, and the offset-gradient reduction
-    # runs only when a softmax-offset gradient is requested.
-    stages = [(s, n) for s, n in ((1, "bwd_pre"), (2, "bwd_dq"), (3, "bwd_dkdv"), (4, "bwd_offset"))
-              if not (s == 1 and p.dtype == "bf16") and not (s == 4 and not want)]
+    # Backward stages that launch a kernel for this workload, in the order the
+    # one-call backward runs them: 1, 2, 3, 4, where in bf16 the pre-pass runs
+    # inside the dQ kernel; with stored dS 1, 3, 2, 4.  The offset-gradient
+    # reduction runs only when a softmax-offset gradient is requested.
+    order = ((1, "bwd_pre"), (3, "bwd_dkdv"), (2, "bwd_dq"), (4, "bwd_offset")) if stored_ds else \
+        ((1, "bwd_pre"), (2, "bwd_dq"), (3, "bwd_dkdv"), (4, "bwd_offset"))
+    stages = [(s, n) for s, n in order
+              if not (s == 1 and p.dtype == "bf16" and not stored_ds) and not (s == 4 and not want)]
     if args.bias != "none":
         stages = [(0, "bwd")]  # the biased backward runs as one call (dQ, dK/dV, dBias)
     names = ["fwd"] + [n for _, n in stages]
@@ -432,7 +446,7 @@ def main():
     t_fwd = statistics.median(ev[0].elapsed_time(ev[1]) for ev in split)
     t_bwd = statistics.median(ev[1].elapsed_time(ev[2]) for ev in split)
 
-    kflops = kernel_flops_per_pair(p.d_qk, p.d_v)
+    kflops = kernel_flops_per_pair(p.d_qk, p.d_v, stored_ds)
     # With a bias the backward is timed as one call; the roofline then covers
     # the forward, the one kernel its events bracket alone.
     dominant = max((n for n in ("fwd", "bwd_dkdv", "bwd_dq") if n in avg_ms), key=lambda n: avg_ms[n])
@@ -462,7 +476,7 @@ def main():
                    "mask": "causal" if p.causal else "none", "window": list(p.window),
                    "softmax_type": p.softmax_type, "seed": seed,
                    "seqlens": None if seq is None else [int(x) for x in seq], "layout": args.layout,
-                   "dropout": args.dropout, "bias": args.bias,
+                   "dropout": args.dropout, "bias": args.bias, "dq_from_stored_ds": stored_ds,
                    "tokens": int(t["q"].shape[0]) if packed else p.B * p.S},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "pairs": pairs,

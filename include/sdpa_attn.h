@@ -150,6 +150,25 @@ int attn_validate(const struct attn_params* p);
 size_t attn_fwd_workspace_size(const struct attn_params* p);
 size_t attn_bwd_workspace_size(const struct attn_params* p);
 
+/* Workspace bytes with which attn_bwd also keeps the backward's dS matrix
+ * (codelab "Speed up attention on GPU with cuDNN and TransformerEngine",
+ * "How attention works": the score gradient that dK = scale dS^T Q and
+ * dQ = scale dS K share) and computes dQ from it instead of recomputing
+ * S = QK^T and dP = dO V^T a second time; 0 when the problem has no such path
+ * (fp32, FP8, dropout) or p is invalid.  The extra room is
+ * B * Hq * n * 8 KiB: dS in bf16 blocks of 32 rows x 128 keys, n the number
+ * of blocks over all 128-key tiles of the rows that see each tile (in 64-row
+ * steps, at the full length S): about S^2 / 4096 without a mask, half that
+ * causal, S (window + 192) / 4096 with a window (1.1 GB for B=4, S=4096,
+ * Hq=32 and a 1024-key causal window; 4.4 GB for B=2, S=4096, Hq=128,
+ * causal).  attn_bwd takes this path whenever workspace_bytes is at least
+ * this size (and > 0), and so does attn_bwd_stage (stage order 1, 3, 2, 4
+ * then); attn_bwd_bias and attn_bwd_noalloc never do.  Results agree with
+ * the recomputing path to rounding (dS is the same bf16 value either way; S,
+ * dP and delta are summed in another order), and are bitwise reproducible
+ * run to run on either path. */
+size_t attn_bwd_ds_workspace_size(const struct attn_params* p);
+
 /* Forward.  Writes O [B,S,Hq,Dv] (packed: [T,Hq,Dv]) and LSE [B,Hq,S].
  *   softmax_offset: [Hq] float32 sink logits; required for LEARNABLE,
  *                   ignored otherwise (may be NULL).
@@ -168,7 +187,9 @@ int attn_fwd(const struct attn_params* p, const void* q, const void* k, const vo
  *   d_softmax_offset: [Hq] float32, overwritten with d(loss)/d(z_h) summed
  *     over batches and rows.  Required for LEARNABLE; optional for OFF_BY_ONE
  *     (gradient w.r.t. the implicit zero logit); must be NULL for VANILLA.
- *   workspace: at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
+ *   workspace: at least attn_bwd_workspace_size(p) bytes, 256-byte aligned;
+ *     with attn_bwd_ds_workspace_size(p) bytes or more (when that is > 0)
+ *     dQ comes from the stored dS (see there).
  *   seqlens, seq_offsets: as for attn_fwd, and the same values.
  * dK/dV accumulate the query heads of a GQA group in a fixed order, and dQ and
  * d_softmax_offset are reduced in a fixed order: results are bitwise
@@ -179,8 +200,12 @@ int attn_bwd(const struct attn_params* p, const void* q, const void* k, const vo
              float* d_softmax_offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of attn_bwd, same arguments and checks as attn_bwd.  attn_bwd
- * runs the stages 1..4 in order on one stream; each stage needs the ones
- * before it (stage 4 needs only stages 1 and 2).
+ * runs the stages 1..4 in order on one stream, or 1, 3, 2, 4 when the
+ * workspace holds the stored dS (at least attn_bwd_ds_workspace_size bytes:
+ * stage 1 is then the pre-pass for bf16 too, stage 3 stores dS and stage 2
+ * computes dQ from it); each stage needs the ones before it in that order
+ * (stage 4 needs only stages 1 and 2 on the recomputing path, stage 1 on the
+ * other).
  *   1 ATTN_BWD_STAGE_PREPROCESS  delta = rowsum(dO * O), LSE * log2(e) and
  *                                per-block partials of the sink gradient
  *                                (fp32; for bf16 stage 2 does this work and

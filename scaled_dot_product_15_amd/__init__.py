@@ -6,7 +6,7 @@ the library nor the GPU; the first call of an entry point loads the library and
 raises if it is missing.
 """
 _API = ("attn_fwd", "attn_bwd", "attn_validate", "attn_fwd_workspace_size",
-        "attn_bwd_workspace_size", "attn_status_string", "debug_tile_map",
+        "attn_bwd_workspace_size", "attn_bwd_ds_workspace_size", "attn_status_string", "debug_tile_map",
         "debug_mask_probe", "host_tile_map", "host_key_range", "host_query_range",
         "load_library", "AttnError", "Params", "make_params", "fwd_tile_shape")
 

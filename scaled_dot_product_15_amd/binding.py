@@ -50,6 +50,7 @@ EXPORTS = {
     "attn_validate": (ctypes.c_int, [ctypes.POINTER(Params)]),
     "attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "attn_bwd_ds_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "attn_fwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]),
     "attn_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -133,6 +134,27 @@ def attn_fwd_workspace_size(p: Params) -> int:
 
 def attn_bwd_workspace_size(p: Params) -> int:
     return load_library().attn_bwd_workspace_size(ctypes.byref(p))
+
+
+def attn_bwd_ds_workspace_size(p: Params) -> int:
+    return load_library().attn_bwd_ds_workspace_size(ctypes.byref(p))
+
+
+# Largest workspace attn_bwd allocates by itself to keep dS (store_ds=None).
+DS_WORKSPACE_LIMIT = 8 << 30
+# Smallest Q/K head dim for which attn_bwd keeps dS by default (store_ds=None).
+# Measured on one MI355X: with 192/128 heads (causal, S=4096, 128 heads) the
+# stored-dS backward takes a step from 8.41 to 7.45 ms, since the dQ kernel that
+# recomputes S and dP runs one wave per SIMD there; with 128/128 heads (GQA,
+# 1024-key window, S=4096) the recomputing one is faster (1.229 vs 1.266 ms):
+# the dK/dV kernel's dS stores cost more than the dQ recomputation saves.
+DS_DEFAULT_MIN_HEAD_DIM = 192
+
+
+def prefers_stored_ds(p: Params) -> bool:
+    """Whether attn_bwd keeps dS by default (store_ds=None) for problem p."""
+    size = attn_bwd_ds_workspace_size(p)
+    return 0 < size <= DS_WORKSPACE_LIMIT and p.head_dim_qk >= DS_DEFAULT_MIN_HEAD_DIM
 
 
 def attn_status_string(rc: int) -> str:
@@ -344,9 +366,15 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
              window_size=(-1, -1), scale_factor=None, softmax_type="vanilla", softmax_offset=None,
              seqlens=None, seq_offsets=None, max_seqlen=None, dropout_p=0.0, rng_state=(0, 0),
              want_d_offset=None, workspace=None, outs=None, stream=None, check_seqlens=True, stage=0,
-             bias=None, d_bias=None, want_d_bias=True):
+             bias=None, d_bias=None, want_d_bias=True, store_ds=None):
     """Backward attention.  Returns (dQ, dK, dV, d_softmax_offset or None),
     and with a bias (dQ, dK, dV, d_softmax_offset or None, d_bias or None).
+
+    store_ds (without a caller workspace): True allocates the workspace that
+    lets the library keep dS and compute dQ from it (attn_bwd_ds_workspace_size;
+    ValueError if the problem has no such path), False the smaller one with
+    which dQ recomputes S and dP, None whichever prefers_stored_ds picks.  A
+    caller workspace decides by its size.
 
     d_softmax_offset is returned for learnable softmax (always) and for
     off-by-one when want_d_offset is true; vanilla returns None.  Layouts as
@@ -357,12 +385,13 @@ def attn_bwd(q, k, v, o, lse, d_o, *, num_gqa_groups=None, attn_mask_type="causa
         return _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
                          softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p,
                          rng_state, want_d_offset, workspace, outs, stream, check_seqlens, stage, bias, d_bias,
-                         want_d_bias)
+                         want_d_bias, store_ds)
 
 
 def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size, scale_factor,
               softmax_type, softmax_offset, seqlens, seq_offsets, max_seqlen, dropout_p, rng_state,
-              want_d_offset, workspace, outs, stream, check_seqlens, stage, bias, d_bias, want_d_bias):
+              want_d_offset, workspace, outs, stream, check_seqlens, stage, bias, d_bias, want_d_bias,
+              store_ds=None):
     torch = _torch()
     packed = _layout(q, seq_offsets, seqlens, max_seqlen, check_seqlens)
     p = _problem(q, k, v, num_gqa_groups, attn_mask_type, window_size, scale_factor, softmax_type, packed,
@@ -408,6 +437,12 @@ def _attn_bwd(q, k, v, o, lse, d_o, num_gqa_groups, attn_mask_type, window_size,
     if workspace is not None and (not workspace.is_cuda or workspace.numel() * workspace.element_size() < ws_bytes):
         raise ValueError(f"workspace must be a device tensor of at least {ws_bytes} bytes")
     if workspace is None:
+        if bias is None and not stage and store_ds is not False:
+            ds_bytes = lib.attn_bwd_ds_workspace_size(ctypes.byref(p))
+            if store_ds and ds_bytes == 0:
+                raise ValueError("this problem has no stored-dS backward")
+            if store_ds or prefers_stored_ds(p):
+                ws_bytes = ds_bytes
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
             _ptr(softmax_offset), _ptr(seqlens), _ptr(seq_offsets), _ptr(dq), _ptr(dk), _ptr(dv),

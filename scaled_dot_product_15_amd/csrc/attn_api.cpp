@@ -70,6 +70,24 @@ size_t kv_part_bytes(const attn_params* p) {
                   sizeof(float));
 }
 
+// bf16 backward with stored dS: plain problems (no dropout), every bf16 head
+// dim pair.  Per (batch, head) the slabs of the 128-key tiles, back to back,
+// each ds_tile_blocks blocks of 8 KiB (mask at the full length).
+bool ds_eligible(const attn_params* p) {
+  if (p->dtype != ATTN_BF16) return false;
+  return floor(256.0 * (double)p->dropout_p + 0.5) == 0.0;
+}
+long long ds_head_blocks(const attn_params* p) {
+  const MaskSpec m = make_mask(p->seqlen, p->seqlen, p->mask_type == ATTN_MASK_CAUSAL, p->window_left, p->window_right);
+  long long n = 0;
+  for (int kt = 0; kt < (p->seqlen + kDkdvKeyTile - 1) / kDkdvKeyTile; ++kt) n += ds_tile_blocks(m, kt);
+  return n;
+}
+constexpr size_t kDsBlockBytes = 8192;  // 32 rows x 128 keys, bf16
+size_t ds_bytes(const attn_params* p) {
+  return align256((size_t)p->batch * p->num_heads * (size_t)ds_head_blocks(p) * kDsBlockBytes);
+}
+
 KArgs make_args(const attn_params* p) {
   KArgs a = {};
   a.B = p->batch;
@@ -144,6 +162,11 @@ size_t attn_fwd_workspace_size(const attn_params* p) {
   if (attn_validate(p) != ATTN_OK) return 0;
   if (p->dtype != ATTN_FP8) return 0;
   return align256(fp8_vt_bytes(p->batch, p->seqlen, p->num_gqa_groups, p->head_dim_v));
+}
+
+size_t attn_bwd_ds_workspace_size(const attn_params* p) {
+  if (attn_validate(p) != ATTN_OK || !ds_eligible(p)) return 0;
+  return attn_bwd_workspace_size(p) + ds_bytes(p);
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
@@ -258,18 +281,33 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == ATTN_BF16;
   const int dqk = p->head_dim_qk, dvd = p->head_dim_v;
-  // bf16: the dQ kernel also runs the pre-pass, so stage 1 launches nothing.
-  if ((stage == 0 || stage == ATTN_BWD_STAGE_PREPROCESS) && !bf16) {
-    if (launch_bwd_pre(a, p->dtype, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
+  // With room for the dS blocks (and no bias): pre-pass, dK/dV storing dS,
+  // dQ from the stored dS -- stages 1, 3, 2, 4.  Otherwise 1, 2, 3, 4, the
+  // bf16 dQ kernel running the pre-pass itself.
+  const size_t ds_ws = bias ? 0 : attn_bwd_ds_workspace_size(p);
+  const bool use_ds = ds_ws > 0 && workspace_bytes >= ds_ws;
+  if (use_ds) {
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + attn_bwd_workspace_size(p));
+    a.ds_head_blocks = (int)ds_head_blocks(p);
+    a.n_chunks = (p->seqlen + kPreRows - 1) / kPreRows;  // sink-gradient partials of the pre-pass
   }
-  if (stage == 0 || stage == ATTN_BWD_STAGE_DQ) {
-    hipError_t e = bf16 ? launch_bwd_dq_bf16(a, dqk, dvd, s) : launch_bwd_dq_f32(a, dqk, dvd, s);
-    if (e != hipSuccess) return ATTN_ERR_HIP;
+  if ((stage == 0 || stage == ATTN_BWD_STAGE_PREPROCESS) && (!bf16 || use_ds)) {
+    if (launch_bwd_pre(a, bf16 ? 1 : 0, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
   }
-  if (stage == 0 || stage == ATTN_BWD_STAGE_DKDV) {
+  auto run_dq = [&]() {
+    if (use_ds) return launch_bwd_dq_ds_bf16(a, dqk, dvd, s);
+    return bf16 ? launch_bwd_dq_bf16(a, dqk, dvd, s) : launch_bwd_dq_f32(a, dqk, dvd, s);
+  };
+  auto run_dkdv = [&]() {
     hipError_t e = bf16 ? launch_bwd_dkdv_bf16(a, dqk, dvd, s) : launch_bwd_dkdv_f32(a, dqk, dvd, s);
     if (e == hipSuccess && a.n_splits > 1) e = launch_dkdv_split_reduce(a, dqk, dvd, s);
-    if (e != hipSuccess) return ATTN_ERR_HIP;
+    return e;
+  };
+  if (stage == 0 && use_ds) {
+    if (run_dkdv() != hipSuccess || run_dq() != hipSuccess) return ATTN_ERR_HIP;
+  } else {
+    if ((stage == 0 || stage == ATTN_BWD_STAGE_DQ) && run_dq() != hipSuccess) return ATTN_ERR_HIP;
+    if ((stage == 0 || stage == ATTN_BWD_STAGE_DKDV) && run_dkdv() != hipSuccess) return ATTN_ERR_HIP;
   }
   if (stage == 0 && a.bias && a.d_bias && !a.dbias_direct) {
     if (launch_bwd_dbias_bf16(a, dqk, dvd, s) != hipSuccess) return ATTN_ERR_HIP;

@@ -93,7 +93,7 @@ struct DkdvCfg {
   static constexpr int LDS_ELEMS = NBUF * (STAGE + RT);
 };
 
-template <int DQK, int DV, bool DROP, bool BIAS>
+template <int DQK, int DV, bool DROP, bool BIAS, bool DSOUT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   using C = DkdvCfg<DQK, DV, BIAS>;
   // Without dropout, delta is folded into the dP products: their
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // delta - dP and P times it is -dS with no subtraction; dK then
   // accumulates -dK, negated at the end (all exact sign changes).
   constexpr bool FOLD = !DROP;
+  static_assert(!DSOUT || (!DROP && !BIAS), "stored dS: plain variant only");
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   // Ring slot `buf`: tiles Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN]
   // (swizzled) at buf * STAGE; after the NBUF slots' tiles, its row terms
@@ -390,6 +391,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 
   StageWalk b_walk{0, 0, T > 0 ? q_first : a.S};  // stage of the block in B
   StageWalk copy_walk = b_walk;                    // next stage to copy
+
+  // DSOUT: each block's bf16 dS (the B operand of its dK products, which is
+  // -dS here: the fold's sign) goes to block (q - q_first) / 32 of the slab
+  // of (batch, head, key tile) (ds_slab): wave w's 32 keys at w * 2 KiB, lane l's 16
+  // values (rows q + acc_row(i, l / 32), key l % 32, i = 0..15) at l * 32
+  // bytes.  Nothing is stored (empty resource) for padding blocks (index NB
+  // and up) and for blocks none of whose rows see a key of the wave
+  // (tile_class SKIP: the dQ kernel reads none of those).  A block's dS is complete once its masked redo has
+  // run; the two blocks of a stage go out together right after the barrier
+  // that opens the stage two blocks later, so the stores have two
+  // iterations to drain before the next copy wait (which counts them too).
+  int ds_first = 0, ds_nblk = 0;  // this tile's slab: first block, blocks written
+  if constexpr (DSOUT) {
+    int count;
+    ds_slab(a, kt, ds_first, count);
+    ds_nblk = 2 * nsteps < count ? 2 * nsteps : count;
+  }
+  // Non-temporal stores (cache policy nt): the blocks are read once, by the
+  // next kernel, and otherwise push this kernel's Q / dO tiles out of L2
+  // (measured: 4-5 % on the kernel against default-policy stores).
+  constexpr int kNonTemporal = 2;
+  int ds_bh = 0, ds_q = 0;  // second block of the previous stage
+  auto store_ds = [&](int blk, int bh, int q, const u32x4(&dw)[2]) __attribute__((always_inline)) {
+    if constexpr (DSOUT) {
+      const int r = (q - q_first) >> 5;
+      const bool ok = blk >= 0 && blk < NB && r >= 0 && r < ds_nblk &&
+                      tile_class(m, q, 32, j0 + w * 32, 32) != TILE_SKIP;
+      const uint16_t* base = a.ds + ((size_t)bh * a.ds_head_blocks + ds_first + (ok ? r : 0)) * 4096;
+      const __amdgpu_buffer_rsrc_t res = buf_rsrc(base, ok ? 8192u : 0u);
+      const uint32_t off = (uint32_t)(w * 2048 + lane * 32);
+      __builtin_amdgcn_raw_buffer_store_b128(dw[0], res, off, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b128(dw[1], res, off + 16, 0, kNonTemporal);
+    }
+  };
+
   // Iteration u, with P = u % 6 fixing the register sets and ring slots:
   // block u sits in slot (u/2) % 3 = (P/2) % 3 at row offset (P%2)*32.
   // The three phases are cut into four chunks, each holding a quarter of
@@ -467,10 +503,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         walk_next(copy_walk);
       }
     } else {
+      if constexpr (DSOUT) {
+        ds_bh = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // block u-1: second half of the stage left
+        ds_q = b_walk.q0 + 32;
+      }
       walk_next(b_walk);  // block u opens a new stage
     }
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
     const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
+    if constexpr (DSOUT && (P & 1) != 0) {
+      // Blocks u-2 (set cur, not yet overwritten by B(u)) and u-1 (set nxt).
+      store_ds(u - 2, ds_bh, ds_q, DW[cur]);
+      store_ds(u - 1, bh_u, b_walk.q0, DW[nxt]);
+    }
     uint32_t rnd_u[4] = {0u, 0u, 0u, 0u};
     if constexpr (DROP) drop_rows(bh_u, q_u, rnd_u);
 
@@ -590,6 +635,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     }
     // Block NI (even, first half of stage NI/2, ring slot 0) still owes C.
     phase_c(qtile(0), otile(0), 0, PW[0], DW[0]);
+    // Blocks NI-1 (set 1, second half of the previous stage) and NI (set 0).
+    store_ds(NI - 1, ds_bh, ds_q, DW[1]);
+    store_ds(NI, b * a.Hq + g * a.G + hs * Gs + b_walk.hh, b_walk.q0, DW[0]);
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
@@ -666,18 +714,22 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(const float* par
 // Explicit instantiations: with only the implicit ones from the launchers
 // below, the host pass of this compiler drops the launch stub of the last
 // kernel instantiated in the file.
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false, false>(KArgs);
+// Stored-dS variants (no dropout, no bias).
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, true>(KArgs);
 // Bias variants: a stage grows by a 64 x 128 bf16 tile (147 KB of LDS in all
 // at head dim 128; the 192-dim stages would not fit).
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, true>(KArgs);
-template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, true, false>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, true, false>(KArgs);
 
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
@@ -685,18 +737,23 @@ static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   static_assert(D::BN == kDkdvKeyTile, "split rule uses the kernel's key tile");
   const int nkt = (a.S + D::BN - 1) / D::BN;
   const dim3 grid((unsigned)(nkt * a.B * a.Hkv * a.n_splits));
+  if (a.ds) {
+    if (a.bias || a.drop_t > 0) return hipErrorInvalidValue;  // stored dS: plain variant only
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, true>), grid, dim3(D::NT), 0, stream, a);
+    return hipGetLastError();
+  }
   if constexpr (DQK <= 128) {
     static_assert(DkdvCfg<DQK, DV, true>::LDS_ELEMS * 2 <= 160 * 1024, "bias stages fit the LDS");
     if (a.bias) {
-      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, true>), grid, dim3(D::NT), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true>), grid, dim3(D::NT), 0, stream, a);
+      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, true, false>), grid, dim3(D::NT), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true, false>), grid, dim3(D::NT), 0, stream, a);
       return hipGetLastError();
     }
   } else if (a.bias) {
     return hipErrorInvalidValue;  // no bias variant for these head dims
   }
-  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, false>), grid, dim3(D::NT), 0, stream, a);
-  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false>), grid, dim3(D::NT), 0, stream, a);
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, false, false>), grid, dim3(D::NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, false>), grid, dim3(D::NT), 0, stream, a);
   return hipGetLastError();
 }
 

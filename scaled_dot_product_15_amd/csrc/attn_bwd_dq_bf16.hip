@@ -73,18 +73,7 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
   // Same tile order as the forward: heavy query tiles first, the heads of a
   // GQA group on consecutive ids kept on one XCD.
   int b, h, qt;
-  {
-    const int N = a.B * a.Hq * a.n_tiles, chunk = a.G, full = (N / (8 * chunk)) * (8 * chunk);
-    int l = blockIdx.x;
-    if (l < full) {
-      const int xcd = l & 7, slot = l >> 3;
-      l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
-    }
-    const int per_tile = a.B * a.Hq;
-    qt = a.n_tiles - 1 - l / per_tile;
-    b = (l % per_tile) / a.Hq;
-    h = (l % per_tile) % a.Hq;
-  }
+  dq_tile_of(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int bh = b * a.Hq + h;

@@ -1,0 +1,185 @@
+// Backward attention, dQ from stored dS, bf16, fp32 accumulation, gfx950
+// MFMA 32x32x16.
+//
+// dQ = scale * dS K (PR #2225 backward: grad_q; dS = P * (dP - delta) as in
+// the other backward kernels).  When the workspace holds the bf16 dS blocks
+// the dK/dV kernel wrote (the B operands of its dK products, -dS there: that
+// kernel starts the dP accumulator at delta and negates V), dQ is a
+// contraction of those blocks with K, with no recomputation of S or dP; the
+// pass is bound by streaming the blocks from HBM.  Deterministic: each
+// workgroup owns its rows' dQ and adds the key tiles in ascending order.
+//
+// Work decomposition: one workgroup of 4 waves owns 128 query rows of one
+// (batch, query head), 32 per wave, and walks the visible keys in steps of
+// 64 (half a dK/dV key tile).  Per step, direct memory-to-LDS copies (double
+// buffered, one barrier per step) bring the K rows ([64][DQK], swizzled) and
+// each wave's dS block ([64 keys][32 positions], swizzled 64-byte rows).
+//
+// Layouts.  In a stored block a lane of the dK/dV kernel holds key c = l % 32
+// and the 16 rows acc_row(i, l / 32), i = 0..15, of a 32-row block; here
+// those are positions p = (l / 32) * 16 + i of key c's 64-byte row.  The
+// contraction runs over keys, so both operands come from LDS transpose loads
+// (TrReads), which hand a lane the same 8 keys of each 16-key step:
+//     dQ^T (dims x positions) += K^T (dims x keys) dS^T (keys x positions).
+// Accumulator element i of dim block db, lane l: dim db*32 + acc_row(i, l/32),
+// position p = l % 32, i.e. row acc_row(p % 16, p / 16) of the wave's block.
+#include <type_traits>
+
+#include "launch.h"
+
+namespace sdpa {
+
+template <int DQK>
+struct DqDsCfg {
+  static constexpr int BM = 128;         // query rows per workgroup (32 per wave)
+  static constexpr int BK = 64;          // keys per step
+  static constexpr int NT = 256;
+  static constexpr int KCH = DQK / 8;    // 16-byte chunks per K row
+  static constexpr int KT = BK * DQK;    // K tile elements
+  static constexpr int DT = BK * 32;     // one wave's dS tile elements
+  static constexpr int STAGE = KT + 4 * DT;
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+};
+
+template <int DQK>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
+  using C = DqDsCfg<DQK>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE; };
+  auto dtile = [&](int buf, int wv) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::KT + wv * C::DT; };
+
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  int b, h, qt;
+  dq_tile_of(a, blockIdx.x, b, h, qt);
+  const int g = h / a.G;
+  const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+  const int i0 = qt * C::BM, qw0 = i0 + w * 32;
+
+  f32x16 dq[DQK / 32];
+#pragma unroll
+  for (int i = 0; i < DQK / 32; ++i) dq[i] = f32x16{};
+
+  int lo = 0, hi = -1;
+  const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
+  if (!key_range(m, i0, nrow, lo, hi)) { lo = 0; hi = -1; }
+  const int s0 = lo / C::BK, s1 = hi < 0 ? -1 : hi / C::BK;
+
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
+  const size_t kstride = (size_t)a.Hkv * DQK;
+  const TileCopy<C::BK, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
+  const TrReads<C::KCH> ktr(lane);
+  const TrReads<4> dtr(lane);
+  // dS copy: wave w fills its own tile with four 64-lane instructions; lane l
+  // of instruction k fills physical chunk k*64 + l, i.e. key row (k*64+l)/4,
+  // logical chunk ch = slot ^ swz<4>(row): positions 8ch .. 8ch+7, which are
+  // 16 bytes of the stored lane (row % 32) + 32 (ch / 2) of the row's 32-key
+  // group.
+  uint32_t dvoff[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = k * 64 + lane, row = idx >> 2, ch = (idx & 3) ^ swz<4>(row);
+    dvoff[k] = (uint32_t)((row >> 5) * 2048 + ((row & 31) + 32 * (ch >> 1)) * 32 + (ch & 1) * 16);
+  }
+  const uint16_t* dsh = a.ds + (size_t)(b * a.Hq + h) * a.ds_head_blocks * 4096;
+  // Slab of the key tile being copied (ds_slab), advanced tile by tile as
+  // the steps ascend.
+  const MaskSpec mf = make_mask(a.S, a.S, a.causal, a.wl, a.wr);
+  int sl_kt = s0 >> 1, sl_first, sl_count;
+  ds_slab(a, sl_kt, sl_first, sl_count);
+  auto issue_step = [&](int st, int buf) __attribute__((always_inline)) {
+    const int j0 = st * C::BK;
+    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
+    // Block of this wave's rows in the slab of key tile kt = st / 2: rows
+    // from q_first, the tile's first visible row rounded down to 64, for
+    // 2 * nsteps blocks at this batch's length; blocks outside that range
+    // were never written and are not read (empty resource: zeros).
+    const int kt = st >> 1;
+    while (sl_kt < kt) {
+      sl_first += sl_count;
+      sl_count = ds_tile_blocks(mf, ++sl_kt);
+    }
+    int qlo, qhi;
+    int r = -1, nblk = 0;
+    if (query_range(m, kt * 128, kt * 128 + 127, qlo, qhi)) {
+      nblk = 2 * (qhi / 64 - qlo / 64 + 1);
+      if (nblk > sl_count) nblk = sl_count;
+      r = (qw0 - (qlo / 64) * 64) >> 5;
+    }
+    const bool ok = r >= 0 && r < nblk;
+    const uint16_t* src = dsh + ((size_t)sl_first + (ok ? r : 0)) * 4096 + (st & 1) * 2048;
+    const uint32_t dst = lds_addr(dtile(buf, w));
+    // One resource per 32-key group (instructions 2g, 2g+1): the dK/dV kernel
+    // stores only the groups whose keys some row of the block sees, so the
+    // others are not read (they land as zeros and their products are skipped).
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const bool vis = ok && tile_class(m, qw0, 32, j0 + kg * 32, 32) != TILE_SKIP;
+      const BufDesc d = buf_desc(src + kg * 1024, vis ? 2048u : 0u);
+#pragma unroll
+      for (int k = 2 * kg; k < 2 * kg + 2; ++k) lds_dma16(d, dst + k * 1024, dvoff[k] - kg * 2048);
+    }
+  };
+  auto step = [&](int st, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    if (st < s1) issue_step(st + 1, buf ^ 1);
+    // 32-key groups the wave's rows do not see hold zeros: skipped.
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      if (tile_class(m, qw0, 32, st * C::BK + kg * 32, 32) == TILE_SKIP) continue;
+#pragma unroll
+      for (int t = 2 * kg; t < 2 * kg + 2; ++t) {
+        const bf16x8 dsb = dtr.read(dtile(buf, w), t * 16, 0);
+#pragma unroll
+        for (int db = 0; db < DQK / 32; ++db) dq[db] = mfma32(ktr.read(ktile(buf), t * 16, db), dsb, dq[db]);
+      }
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (s0 <= s1) issue_step(s0, 0);
+  lds_dma_wait();
+  __syncthreads();
+  for (int st = s0; st <= s1; st += 2) {
+    step(st, B0{});
+    if (st + 1 <= s1) step(st + 1, B1{});
+  }
+
+  // Lane: position l32 -> row qw0 + acc_row(l32 % 16, l32 / 16); dims
+  // db*32 + ig*8 + hf*4 + 0..3 from elements 4 ig .. 4 ig + 3.  The blocks
+  // hold -dS, so dQ = -scale * acc.
+  const int qi = qw0 + acc_row(l32 & 15, l32 >> 4);
+  if (qi < seq_rows(a, b)) {
+    uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK + hf * 4;
+    const float qs = -a.scale;
+#pragma unroll
+    for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        u32x2 val = {pack_bf16(dq[db][ig * 4] * qs, dq[db][ig * 4 + 1] * qs),
+                     pack_bf16(dq[db][ig * 4 + 2] * qs, dq[db][ig * 4 + 3] * qs)};
+        *reinterpret_cast<u32x2*>(dqp + db * 32 + ig * 8) = val;
+      }
+  }
+}
+
+template __global__ void bwd_dq_ds_bf16_kernel<64>(KArgs);
+template __global__ void bwd_dq_ds_bf16_kernel<128>(KArgs);
+template __global__ void bwd_dq_ds_bf16_kernel<192>(KArgs);
+static_assert(DqDsCfg<192>::LDS_ELEMS * 2 * 2 <= 160 * 1024, "two workgroups per CU at head dim 192");
+
+hipError_t launch_bwd_dq_ds_bf16(const KArgs& a0, int dqk, int dv, hipStream_t stream) {
+  (void)dv;  // dQ needs only K
+  if (!a0.ds) return hipErrorInvalidValue;
+  KArgs a = a0;
+  a.n_tiles = (a.S + DqDsCfg<64>::BM - 1) / DqDsCfg<64>::BM;
+  const dim3 grid((unsigned)(a.n_tiles * a.B * a.Hq));
+  if (dqk == 64) hipLaunchKernelGGL((bwd_dq_ds_bf16_kernel<64>), grid, dim3(256), 0, stream, a);
+  else if (dqk == 128) hipLaunchKernelGGL((bwd_dq_ds_bf16_kernel<128>), grid, dim3(256), 0, stream, a);
+  else if (dqk == 192) hipLaunchKernelGGL((bwd_dq_ds_bf16_kernel<192>), grid, dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -617,9 +617,10 @@ static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
   a.s_pad = (a.S + 63) / 64 * 64;
   a.n_chunks = (a.S + 31) / 32;
   hipLaunchKernelGGL(fp8_amax_zero_kernel, dim3(1), dim3(64), 0, stream, a.amax_out);
-  launch_fp8_transpose(a, a.k, a.Hkv, a.kt_t, D, stream);
-  launch_fp8_transpose(a, a.q, a.Hq, a.qt_t, D, stream);
-  launch_fp8_transpose(a, a.d_o, a.Hq, a.dot_t, D, stream);
+  hipError_t e = launch_fp8_transpose(a, a.k, a.Hkv, a.kt_t, D, stream);
+  if (e == hipSuccess) e = launch_fp8_transpose(a, a.q, a.Hq, a.qt_t, D, stream);
+  if (e == hipSuccess) e = launch_fp8_transpose(a, a.d_o, a.Hq, a.dot_t, D, stream);
+  if (e != hipSuccess) return e;
   a.n_tiles = (a.S + C::BM - 1) / C::BM;
   hipLaunchKernelGGL(bwd_dq_fp8_kernel<D>, dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)), dim3(C::NT), 0,
                      stream, a);
@@ -631,7 +632,7 @@ static hipError_t launch_bwd_fp8_cfg(KArgs a, hipStream_t stream) {
     KArgs r = a;
     r.scale = 1.0f;
     r.drop_t = 0;
-    const hipError_t e = launch_dkdv_split_reduce(r, D, D, stream);
+    e = launch_dkdv_split_reduce(r, D, D, stream);
     if (e != hipSuccess) return e;
   }
   if (a.d_offset && a.softmax_type != 0) return launch_dz_reduce(a, stream);

@@ -64,7 +64,42 @@ struct KArgs {
   int drop_t;           // dropout byte threshold round(256 p); 0 = no dropout
   float drop_scale;     // 1 / (1 - drop_t / 256)
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;  // generator key and counter word 3
+  // bf16 backward with stored dS: the dK/dV kernel writes its bf16 dS blocks
+  // here and the dQ kernel reads them instead of recomputing S and dP
+  // (nullptr: dQ recomputes).  Per (batch, query head) ds_head_blocks blocks
+  // of 32 rows x 128 keys (8 KiB): the slabs of the 128-key tiles in order,
+  // ds_tile_blocks(kt) blocks each, block r of a slab holding the rows
+  // q_first + 32 r .. +31, q_first the tile's first visible row rounded down
+  // to a multiple of 64.
+  uint16_t* ds;
+  int ds_head_blocks;
 };
+
+// Stored-dS slab of key tile kt: its first block within the (batch, head)
+// region and its block count, from the mask at the full length S (a loop over
+// the tiles before it: a few scalar instructions each, once per workgroup).
+__device__ __forceinline__ void ds_slab(const KArgs& a, int kt, int& first, int& count) {
+  const MaskSpec mf = make_mask(a.S, a.S, a.causal, a.wl, a.wr);
+  first = 0;
+  for (int t = 0; t < kt; ++t) first += ds_tile_blocks(mf, t);
+  count = ds_tile_blocks(mf, kt);
+}
+
+// Query tile, batch and head of workgroup `id` of the dQ kernels (n_tiles
+// query tiles per head): tiles with the most keys first (the last ones under a
+// causal mask), the heads of a GQA group on consecutive ids kept on one XCD.
+__device__ __forceinline__ void dq_tile_of(const KArgs& a, int id, int& b, int& h, int& qt) {
+  const int N = a.B * a.Hq * a.n_tiles, chunk = a.G, full = (N / (8 * chunk)) * (8 * chunk);
+  int l = id;
+  if (l < full) {
+    const int xcd = l & 7, slot = l >> 3;
+    l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+  }
+  const int per_tile = a.B * a.Hq;
+  qt = a.n_tiles - 1 - l / per_tile;
+  b = (l % per_tile) / a.Hq;
+  h = (l % per_tile) % a.Hq;
+}
 
 // First row of batch b along the token axis of Q, K, V, O and the gradients:
 // b * S for BSHD tensors; the start of segment b for packed (THD) tensors.

@@ -50,6 +50,8 @@ extern "C" int attn_bwd_noalloc(const attn_params* p, const void* q, const void*
   void* ws = nullptr;
   const int e = scratch_ptr(&ws);
   if (e != ATTN_OK) return e;
+  // The minimum workspace size: dQ recomputes S and dP, as attn_bwd does with
+  // a workspace of attn_bwd_workspace_size bytes (no stored dS).
   return sdpa::bwd_run(0, p, q, k, v, o, d_o, lse, softmax_offset, seqlens, seq_offsets, dq, dk, dv,
-                       d_softmax_offset, ws, (size_t)ATTN_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+                       d_softmax_offset, ws, attn_bwd_workspace_size(p), stream, nullptr);
 }

@@ -37,6 +37,9 @@ int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, 
 // dK / dV = sum over the splits of the partials, in split order (bf16 out).
 hipError_t launch_dkdv_split_reduce(const KArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// dQ from the dS blocks the dK/dV kernel stored in a.ds (a.ds_nkt, a.ds_nqb
+// set; head dims 64/64 or 128/128).
+hipError_t launch_bwd_dq_ds_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
 // Gradient of the attention bias (needs the pre-pass's delta and LSE * log2 e).
 int dbias_key_chunks(int n_mats, int n_qt, int n_kt);
 hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);

@@ -105,4 +105,16 @@ ME_HD bool full_key_tiles(const MaskSpec& m, int i0, int bm, int bn, int& f0, in
   return f0 <= f1;
 }
 
+// 32-row blocks of the stored-dS workspace's slab for the 128-key tile kt
+// (keys 128 kt .. 128 kt + 127): the rows that see any of its keys, from the
+// first one rounded down to a multiple of 64 to the end of the last one's
+// 64-row step; 0 when no row sees the tile.  Slabs are sized with the mask at
+// the full length S (a shorter valid length only drops rows from the end, and
+// leaves the first row in place), one slab per tile back to back.
+ME_HD int ds_tile_blocks(const MaskSpec& m_full, int kt) {
+  int lo, hi;
+  if (!query_range(m_full, kt * 128, kt * 128 + 127, lo, hi)) return 0;
+  return 2 * (hi / 64 - lo / 64 + 1);
+}
+
 }  // namespace sdpa

@@ -40,9 +40,10 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
 
 
-def run_gpu(p: inputs.Problem, t: dict, want_d_offset=True, dropout=None):
+def run_gpu(p: inputs.Problem, t: dict, want_d_offset=True, dropout=None, store_ds=None):
     """fwd + bwd on the GPU; returns torch tensors (o, lse, dq, dk, dv, doff).
-    dropout = (p, seed, offset) or None."""
+    dropout = (p, seed, offset) or None; store_ds as for binding.attn_bwd
+    (None: dQ from the stored dS where the problem has that path)."""
     import torch
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask",
               window_size=p.window, scale_factor=p.scale_factor or None,
@@ -51,7 +52,7 @@ def run_gpu(p: inputs.Problem, t: dict, want_d_offset=True, dropout=None):
         kw.update(dropout_p=dropout[0], rng_state=(dropout[1], dropout[2]))
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"],
-                                        want_d_offset=want_d_offset, **kw)
+                                        want_d_offset=want_d_offset, store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv, doff
 

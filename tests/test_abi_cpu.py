@@ -109,6 +109,47 @@ def test_workspace_sizes():
     assert binding.attn_bwd_workspace_size(P(B=0)) == 0
 
 
+def _ds_blocks_expected(S, causal, wl, wr):
+    """32-row blocks per (batch, head) of the stored-dS workspace, from the
+    oracle's visibility matrix: for each 128-key tile, the rows that see any
+    of its keys, from the first one rounded down to 64 to the end of the last
+    one's 64-row step, summed over the tiles."""
+    vis = oracle.visible_mask(S, S, causal, wl, wr)
+    total = 0
+    for j0 in range(0, S, 128):
+        rows = np.nonzero(vis[:, j0:j0 + 128].any(axis=1))[0]
+        if rows.size:
+            total += 2 * (rows[-1] // 64 - rows[0] // 64 + 1)
+    return total
+
+
+@pytest.mark.parametrize("S,mask,win,dims", [
+    (333, "causal", (37, 0), (128, 128)), (256, "no_mask", (-1, -1), (64, 64)),
+    (1000, "no_mask", (100, 50), (128, 128)), (700, "causal", (-1, -1), (192, 128)),
+    (129, "causal", (0, 0), (128, 128)), (4096, "causal", (1024, 0), (128, 128))])
+def test_ds_workspace_size(S, mask, win, dims):
+    p = P(B=3, S=S, Hq=4, Hkv=2, d_qk=dims[0], d_v=dims[1], attn_mask_type=mask, window_size=win)
+    want = 3 * 4 * _ds_blocks_expected(S, mask == "causal", win[0], win[1]) * 8192
+    want = -(-want // 256) * 256
+    assert binding.attn_bwd_ds_workspace_size(p) == binding.attn_bwd_workspace_size(p) + want
+
+
+def test_ds_workspace_size_zero_without_the_path():
+    assert binding.attn_bwd_ds_workspace_size(P(dtype="f32", d_qk=64, d_v=64)) == 0
+    assert binding.attn_bwd_ds_workspace_size(P(B=0)) == 0
+    pd = P()
+    pd.dropout_p = 0.1
+    assert binding.attn_bwd_ds_workspace_size(pd) == 0
+    pd.dropout_p = 0.001  # rounds to no dropout (t = 0)
+    assert binding.attn_bwd_ds_workspace_size(pd) > 0
+    # GQA+SWA S=4096 workload: 1.1 GB of dS blocks; MLA causal S=4096: 4.4 GB
+    big = P(B=4, S=4096, Hq=32, Hkv=8, window_size=(1024, 0))
+    n = _ds_blocks_expected(4096, True, 1024, 0)
+    assert binding.attn_bwd_ds_workspace_size(big) - binding.attn_bwd_workspace_size(big) == 4 * 32 * n * 8192
+    mla = P(B=2, S=4096, Hq=128, Hkv=128, d_qk=192, d_v=128)
+    assert binding.attn_bwd_ds_workspace_size(mla) - binding.attn_bwd_workspace_size(mla) == 2 * 128 * 2112 * 8192
+
+
 def _expected_splits(B, S, Hkv, G, causal=True, wl=-1, wr=-1, key_tile=128, min_grid=1024, max_blocks=512,
                      dims=128, max_partial=1 << 30):
     """Split rule for the bf16 dK/dV grid, written out independently: the

@@ -2,7 +2,8 @@
 
 Shapes span several query/key tiles and end in a ragged tail (S not a multiple
 of any tile size); the grid covers every softmax type, mask kind, head-dim
-instantiation, GQA/MQA/MHA and padded batches including an empty one.
+instantiation, GQA/MQA/MHA and padded batches including an empty one; bf16
+cases run both backward paths (dQ recomputed, dQ from the stored dS).
 """
 import itertools
 
@@ -36,10 +37,12 @@ def test_small_parity(dims, mask, st, padded):
         arr["seqlens"] = np.array([333, 150, 0], dtype=np.int32)
     t = inputs.to_torch(arr, dtype, "cuda")
     gc.log(f"case {dims} {mask} {st} padded={padded} seed={seed}")
-    g = gc.run_gpu(p, t)
     r = gc.oracle_full(p, t)
-    stats = gc.compare_full(p, t, g, r, tag=f"{dims}/{mask}/{st}/{padded}")
-    gc.log(f"  {stats}")
+    # bf16: both backward paths (dQ recomputed, dQ from the stored dS)
+    for store_ds in ((False, True) if dtype == "bf16" else (None,)):
+        g = gc.run_gpu(p, t, store_ds=store_ds)
+        stats = gc.compare_full(p, t, g, r, tag=f"{dims}/{mask}/{st}/{padded}/store_ds={store_ds}")
+        gc.log(f"  store_ds={store_ds} {stats}")
 
 
 @pytest.mark.parametrize("hkv", [1, 4, 8])

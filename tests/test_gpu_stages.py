@@ -1,9 +1,11 @@
 """The staged backward (attn_bwd_stage 1..4, in order, on one stream) gives
-bitwise the same dQ, dK, dV and d(softmax offset) as the one-call attn_bwd.
+bitwise the same dQ, dK, dV and d(softmax offset) as the one-call attn_bwd
+with the same workspace.
 
 Cases cover the bf16 path (pre-pass fused into the dQ stage), the fp32 path
 (separate pre-pass stage), the sink-gradient stage, padded batches and the
-dK/dV head split (fp32 partials reduced inside the dK/dV stage).
+dK/dV head split (fp32 partials reduced inside the dK/dV stage); with a
+workspace that holds the stored dS, the stages run in the order 1, 3, 2, 4.
 """
 import numpy as np
 import pytest
@@ -26,26 +28,31 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_stages_match_one_call(name):
+STORED_DS = ("bf16_learnable_padded", "bf16_offbyone_64", "bf16_mla_vanilla")
+
+
+@pytest.mark.parametrize("name,stored", [(n, False) for n in CASES] + [(n, True) for n in STORED_DS])
+def test_stages_match_one_call(name, stored):
     import torch
     p = CASES[name]
     arr = inputs.draw(p, 30_000 + list(CASES).index(name))
     if name == "bf16_learnable_padded":
         arr["seqlens"] = np.array([333, 100, 0], dtype=np.int32)
     t = inputs.to_torch(arr, p.dtype, "cuda")
-    gc.log(f"stages {name}")
+    gc.log(f"stages {name} stored_ds={stored}")
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask", window_size=p.window,
               scale_factor=p.scale_factor or None, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
               seqlens=t["seqlens"])
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     want = p.softmax_type != "vanilla"
-    ref = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, **kw)
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"], p.window,
                              kw["scale_factor"], p.softmax_type)
-    ws = torch.empty(binding.attn_bwd_workspace_size(pp), dtype=torch.uint8, device="cuda")
+    size = binding.attn_bwd_ds_workspace_size(pp) if stored else binding.attn_bwd_workspace_size(pp)
+    assert size > 0
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    ref = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws, **kw)
     outs = tuple(torch.empty_like(x) if x is not None else None for x in ref)
-    for stage in (1, 2, 3, 4):
+    for stage in ((1, 3, 2, 4) if stored else (1, 2, 3, 4)):
         binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want, workspace=ws, outs=outs,
                          stage=stage, **kw)
     torch.cuda.synchronize()

@@ -1,8 +1,9 @@
 """The allocation-free backward (attn_bwd_noalloc) against attn_bwd.
 
 attn_bwd_noalloc runs attn_bwd's kernels with the library's static per-GPU
-scratch as workspace.  Two calls in a row, the second on a smaller problem,
-each equal to attn_bwd's result bitwise (both are deterministic and run the
+scratch as workspace (the minimum workspace size: dQ recomputes S and dP).
+Two calls in a row, the second on a smaller problem, each equal bitwise to
+attn_bwd's result with that workspace (both are deterministic and run the
 same kernels), so the second call cannot be reading anything the first left in
 the scratch; a third case has dK/dV head splits, whose fp32 partials also live
 in the scratch.
@@ -27,7 +28,7 @@ def _case(p, seed, seqlens=None):
               window_size=p.window, softmax_type=p.softmax_type,
               softmax_offset=t["alpha"] if p.softmax_type == "learnable" else None, seqlens=t["seqlens"])
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
-    ref = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=True, **kw)
+    ref = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=True, store_ds=False, **kw)
     torch.cuda.synchronize()
     return t, kw, o, lse, ref
 
