@@ -394,32 +394,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
 
   // DSOUT: each block's bf16 dS (the B operand of its dK products, which is
   // -dS here: the fold's sign) goes to block (q - q_first) / 32 of the slab
-  // of (batch, head, key tile) (ds_slab): wave w's 32 keys at w * 2 KiB, lane l's 16
-  // values (rows q + acc_row(i, l / 32), key l % 32, i = 0..15) at l * 32
-  // bytes.  Nothing is stored (empty resource) for padding blocks (index NB
-  // and up) and for blocks none of whose rows see a key of the wave
-  // (tile_class SKIP: the dQ kernel reads none of those).  A block's dS is complete once its masked redo has
-  // run; the two blocks of a stage go out together right after the barrier
-  // that opens the stage two blocks later, so the stores have two
-  // iterations to drain before the next copy wait (which counts them too).
-  int ds_first = 0, ds_nblk = 0;  // this tile's slab: first block, blocks written
-  if constexpr (DSOUT) {
-    int count;
-    ds_slab(a, kt, ds_first, count);
-    ds_nblk = 2 * nsteps < count ? 2 * nsteps : count;
-  }
-  // Non-temporal stores (cache policy nt): the blocks are read once, by the
-  // next kernel, and otherwise push this kernel's Q / dO tiles out of L2
-  // (measured: 4-5 % on the kernel against default-policy stores).
+  // of (batch, head, key tile) (ds_slab; a head's slab is ds_head_blocks
+  // blocks after the previous head's): wave w's 32 keys at w * 2 KiB, lane
+  // l's 16 values (rows q + acc_row(i, l / 32), key l % 32, i = 0..15) at
+  // l * 32 bytes.  A block is stored when some row of it sees a key of this
+  // wave, i.e. when it meets the rows [ds_lo, ds_hi] that see any of the
+  // wave's keys (one interval: both ends grow with the key, and a valid key
+  // is seen at least by its own row) -- the test tile_class makes, with
+  // which the dQ kernel decides what it reads; padding blocks (index NB and
+  // up) store nothing (empty resource).  A block's dS is complete once its
+  // masked redo has run; the two blocks of a stage go out together right
+  // after the barrier that opens the stage two blocks later, so the stores
+  // have two iterations to drain before the next copy wait (which counts
+  // them too).  Non-temporal stores (cache policy nt): the blocks are read
+  // once, by the next kernel, and would otherwise push this kernel's Q / dO
+  // tiles out of L2 (measured: 4-5 % on the kernel).
   constexpr int kNonTemporal = 2;
-  int ds_bh = 0, ds_q = 0;  // second block of the previous stage
-  auto store_ds = [&](int blk, int bh, int q, const u32x4(&dw)[2]) __attribute__((always_inline)) {
+  const uint16_t* ds_base = nullptr;
+  size_t ds_hstride = 0;
+  int ds_lo = 1, ds_hi = 0;
+  if constexpr (DSOUT) {
+    int first, count;
+    ds_slab(a, kt, first, count);
+    ds_hstride = (size_t)a.ds_head_blocks * 4096;
+    ds_base = a.ds + (size_t)(b * a.Hq + g * a.G + hs * Gs) * ds_hstride + (size_t)first * 4096;
+    const int kw0 = j0 + w * 32, kw1 = (kw0 + 31 < m.L ? kw0 + 31 : m.L - 1);
+    if (kw0 < m.L) {
+      int lo0, hi0, lo1, hi1;
+      col_query_bounds(m, kw0, lo0, hi0);
+      col_query_bounds(m, kw1, lo1, hi1);
+      ds_lo = lo0;
+      ds_hi = hi1;
+    }
+  }
+  // First block of the stage of the block in B (its first row is
+  // b_walk.q0), and of the stage before it.
+  const uint16_t* ds_cur = ds_base;
+  const uint16_t* ds_prev = ds_base;
+  int ds_cur_q = b_walk.q0, ds_prev_q = b_walk.q0;
+  auto store_ds = [&](int blk, const uint16_t* blk_ptr, int q, const u32x4(&dw)[2]) __attribute__((always_inline)) {
     if constexpr (DSOUT) {
-      const int r = (q - q_first) >> 5;
-      const bool ok = blk >= 0 && blk < NB && r >= 0 && r < ds_nblk &&
-                      tile_class(m, q, 32, j0 + w * 32, 32) != TILE_SKIP;
-      const uint16_t* base = a.ds + ((size_t)bh * a.ds_head_blocks + ds_first + (ok ? r : 0)) * 4096;
-      const __amdgpu_buffer_rsrc_t res = buf_rsrc(base, ok ? 8192u : 0u);
+      const bool ok = blk >= 0 && blk < NB && q <= ds_hi && q + 31 >= ds_lo;
+      const __amdgpu_buffer_rsrc_t res = buf_rsrc(blk_ptr, ok ? 8192u : 0u);
       const uint32_t off = (uint32_t)(w * 2048 + lane * 32);
       __builtin_amdgcn_raw_buffer_store_b128(dw[0], res, off, 0, kNonTemporal);
       __builtin_amdgcn_raw_buffer_store_b128(dw[1], res, off + 16, 0, kNonTemporal);
@@ -503,18 +519,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
         walk_next(copy_walk);
       }
     } else {
-      if constexpr (DSOUT) {
-        ds_bh = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // block u-1: second half of the stage left
-        ds_q = b_walk.q0 + 32;
-      }
       walk_next(b_walk);  // block u opens a new stage
+      if constexpr (DSOUT) {
+        ds_prev = ds_cur;
+        ds_prev_q = ds_cur_q;
+        ds_cur = ds_base + (size_t)b_walk.hh * ds_hstride + (size_t)((b_walk.q0 - q_first) >> 5) * 4096;
+        ds_cur_q = b_walk.q0;
+      }
     }
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
     const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
     if constexpr (DSOUT && (P & 1) != 0) {
-      // Blocks u-2 (set cur, not yet overwritten by B(u)) and u-1 (set nxt).
-      store_ds(u - 2, ds_bh, ds_q, DW[cur]);
-      store_ds(u - 1, bh_u, b_walk.q0, DW[nxt]);
+      // Blocks u-2 (second half of the previous stage; set cur, not yet
+      // overwritten by B(u)) and u-1 (first half of this one; set nxt).
+      store_ds(u - 2, ds_prev + 4096, ds_prev_q + 32, DW[cur]);
+      store_ds(u - 1, ds_cur, ds_cur_q, DW[nxt]);
     }
     uint32_t rnd_u[4] = {0u, 0u, 0u, 0u};
     if constexpr (DROP) drop_rows(bh_u, q_u, rnd_u);
@@ -636,8 +655,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     // Block NI (even, first half of stage NI/2, ring slot 0) still owes C.
     phase_c(qtile(0), otile(0), 0, PW[0], DW[0]);
     // Blocks NI-1 (set 1, second half of the previous stage) and NI (set 0).
-    store_ds(NI - 1, ds_bh, ds_q, DW[1]);
-    store_ds(NI, b * a.Hq + g * a.G + hs * Gs + b_walk.hh, b_walk.q0, DW[0]);
+    store_ds(NI - 1, ds_prev + 4096, ds_prev_q + 32, DW[1]);
+    store_ds(NI, ds_cur, ds_cur_q, DW[0]);
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
