@@ -9,11 +9,13 @@
 // pass is bound by streaming the blocks from HBM.  Deterministic: each
 // workgroup owns its rows' dQ and adds the key tiles in ascending order.
 //
-// Work decomposition: one workgroup of 4 waves owns 128 query rows of one
-// (batch, query head), 32 per wave, and walks the visible keys in steps of
-// 64 (half a dK/dV key tile).  Per step, direct memory-to-LDS copies (double
-// buffered, one barrier per step) bring the K rows ([64][DQK], swizzled) and
-// each wave's dS block ([64 keys][32 positions], swizzled 64-byte rows).
+// Work decomposition: one workgroup of 4 waves owns 256 query rows of one
+// (batch, query head), 64 per wave (two 32-row blocks, so each K^T operand
+// read from LDS feeds two products), and walks the visible keys in steps of
+// 32 (a quarter of a dK/dV key tile).  Per step, direct memory-to-LDS copies
+// (double buffered, one barrier per step) bring the K rows ([32][DQK],
+// swizzled) and each block's dS ([32 keys][32 positions], swizzled 64-byte
+// rows).
 //
 // Layouts.  In a stored block a lane of the dK/dV kernel holds key c = l % 32
 // and the 16 rows acc_row(i, l / 32), i = 0..15, of a 32-row block; here
@@ -22,7 +24,7 @@
 // (TrReads), which hand a lane the same 8 keys of each 16-key step:
 //     dQ^T (dims x positions) += K^T (dims x keys) dS^T (keys x positions).
 // Accumulator element i of dim block db, lane l: dim db*32 + acc_row(i, l/32),
-// position p = l % 32, i.e. row acc_row(p % 16, p / 16) of the wave's block.
+// position p = l % 32, i.e. row acc_row(p % 16, p / 16) of the block.
 #include <type_traits>
 
 #include "launch.h"
@@ -31,13 +33,13 @@ namespace sdpa {
 
 template <int DQK>
 struct DqDsCfg {
-  static constexpr int BM = 128;         // query rows per workgroup (32 per wave)
-  static constexpr int BK = 64;          // keys per step
+  static constexpr int BM = 256;         // query rows per workgroup (64 per wave)
+  static constexpr int BK = 32;          // keys per step
   static constexpr int NT = 256;
   static constexpr int KCH = DQK / 8;    // 16-byte chunks per K row
   static constexpr int KT = BK * DQK;    // K tile elements
-  static constexpr int DT = BK * 32;     // one wave's dS tile elements
-  static constexpr int STAGE = KT + 4 * DT;
+  static constexpr int DT = BK * 32;     // one block's dS tile elements
+  static constexpr int STAGE = KT + 8 * DT;
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
@@ -46,18 +48,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
   using C = DqDsCfg<DQK>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   auto ktile = [&](int buf) __attribute__((always_inline)) { return lds + buf * C::STAGE; };
-  auto dtile = [&](int buf, int wv) __attribute__((always_inline)) { return lds + buf * C::STAGE + C::KT + wv * C::DT; };
+  // dS tile of row block rb (0, 1) of wave wv
+  auto dtile = [&](int buf, int wv, int rb) __attribute__((always_inline)) {
+    return lds + buf * C::STAGE + C::KT + (wv * 2 + rb) * C::DT;
+  };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
   dq_tile_of(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
-  const int i0 = qt * C::BM, qw0 = i0 + w * 32;
+  const int i0 = qt * C::BM, qw0 = i0 + w * 64;
 
-  f32x16 dq[DQK / 32];
+  f32x16 dq[2][DQK / 32];
 #pragma unroll
-  for (int i = 0; i < DQK / 32; ++i) dq[i] = f32x16{};
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < DQK / 32; ++i) dq[rb][i] = f32x16{};
 
   int lo = 0, hi = -1;
   const int nrow = (i0 + C::BM < m.L ? i0 + C::BM : m.L) - 1;
@@ -69,68 +76,70 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
   const TileCopy<C::BK, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
   const TrReads<C::KCH> ktr(lane);
   const TrReads<4> dtr(lane);
-  // dS copy: wave w fills its own tile with four 64-lane instructions; lane l
-  // of instruction k fills physical chunk k*64 + l, i.e. key row (k*64+l)/4,
-  // logical chunk ch = slot ^ swz<4>(row): positions 8ch .. 8ch+7, which are
-  // 16 bytes of the stored lane (row % 32) + 32 (ch / 2) of the row's 32-key
-  // group.
-  uint32_t dvoff[4];
+  // dS copy of one block: two 64-lane instructions; lane l of instruction k
+  // fills physical chunk k*64 + l, i.e. key row (k*64+l)/4, logical chunk
+  // ch = slot ^ swz<4>(row): positions 8ch .. 8ch+7, which are 16 bytes of
+  // the stored lane row + 32 (ch / 2).
+  uint32_t dvoff[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2; ++k) {
     const int idx = k * 64 + lane, row = idx >> 2, ch = (idx & 3) ^ swz<4>(row);
-    dvoff[k] = (uint32_t)((row >> 5) * 2048 + ((row & 31) + 32 * (ch >> 1)) * 32 + (ch & 1) * 16);
+    dvoff[k] = (uint32_t)((row + 32 * (ch >> 1)) * 32 + (ch & 1) * 16);
   }
   const uint16_t* dsh = a.ds + (size_t)(b * a.Hq + h) * a.ds_head_blocks * 4096;
   // Slab of the key tile being copied (ds_slab), advanced tile by tile as
   // the steps ascend.
   const MaskSpec mf = make_mask(a.S, a.S, a.causal, a.wl, a.wr);
-  int sl_kt = s0 >> 1, sl_first, sl_count;
+  int sl_kt = s0 >> 2, sl_first, sl_count;
   ds_slab(a, sl_kt, sl_first, sl_count);
   auto issue_step = [&](int st, int buf) __attribute__((always_inline)) {
     const int j0 = st * C::BK;
     kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
-    // Block of this wave's rows in the slab of key tile kt = st / 2: rows
-    // from q_first, the tile's first visible row rounded down to 64, for
-    // 2 * nsteps blocks at this batch's length; blocks outside that range
-    // were never written and are not read (empty resource: zeros).
-    const int kt = st >> 1;
+    // Each row block's block in the slab of key tile kt = st / 4: rows from
+    // q_first, the tile's first visible row rounded down to 64, for 2 nsteps
+    // blocks at this batch's length; its 32-key group st % 4.  Groups no row
+    // of the block sees were not stored (tile_class SKIP), nor were blocks
+    // outside that range: those are not read (empty resource: zeros).
+    const int kt = st >> 2;
     while (sl_kt < kt) {
       sl_first += sl_count;
       sl_count = ds_tile_blocks(mf, ++sl_kt);
     }
     int qlo, qhi;
-    int r = -1, nblk = 0;
+    int r0 = -1, nblk = 0;
     if (query_range(m, kt * 128, kt * 128 + 127, qlo, qhi)) {
       nblk = 2 * (qhi / 64 - qlo / 64 + 1);
       if (nblk > sl_count) nblk = sl_count;
-      r = (qw0 - (qlo / 64) * 64) >> 5;
+      r0 = (qw0 - (qlo / 64) * 64) >> 5;
     }
-    const bool ok = r >= 0 && r < nblk;
-    const uint16_t* src = dsh + ((size_t)sl_first + (ok ? r : 0)) * 4096 + (st & 1) * 2048;
-    const uint32_t dst = lds_addr(dtile(buf, w));
-    // One resource per 32-key group (instructions 2g, 2g+1): the dK/dV kernel
-    // stores only the groups whose keys some row of the block sees, so the
-    // others are not read (they land as zeros and their products are skipped).
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const bool vis = ok && tile_class(m, qw0, 32, j0 + kg * 32, 32) != TILE_SKIP;
-      const BufDesc d = buf_desc(src + kg * 1024, vis ? 2048u : 0u);
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = r0 + rb;
+      const bool ok = r >= 0 && r < nblk && tile_class(m, qw0 + rb * 32, 32, j0, C::BK) != TILE_SKIP;
+      const uint16_t* src = dsh + ((size_t)sl_first + (ok ? r : 0)) * 4096 + (st & 3) * 1024;
+      const BufDesc d = buf_desc(src, ok ? 2048u : 0u);
+      const uint32_t dst = lds_addr(dtile(buf, w, rb));
 #pragma unroll
-      for (int k = 2 * kg; k < 2 * kg + 2; ++k) lds_dma16(d, dst + k * 1024, dvoff[k] - kg * 2048);
+      for (int k = 0; k < 2; ++k) lds_dma16(d, dst + k * 1024, dvoff[k]);
     }
   };
   auto step = [&](int st, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     if (st < s1) issue_step(st + 1, buf ^ 1);
-    // 32-key groups the wave's rows do not see hold zeros: skipped.
+    // Blocks whose rows see none of the step's keys hold zeros: a step that
+    // neither block of the wave sees is skipped.
+    const int j0 = st * C::BK;
+    if (tile_class(m, qw0, 32, j0, C::BK) != TILE_SKIP || tile_class(m, qw0 + 32, 32, j0, C::BK) != TILE_SKIP) {
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      if (tile_class(m, qw0, 32, st * C::BK + kg * 32, 32) == TILE_SKIP) continue;
+      for (int t = 0; t < C::BK / 16; ++t) {
+        const bf16x8 ds0 = dtr.read(dtile(buf, w, 0), t * 16, 0);
+        const bf16x8 ds1 = dtr.read(dtile(buf, w, 1), t * 16, 0);
 #pragma unroll
-      for (int t = 2 * kg; t < 2 * kg + 2; ++t) {
-        const bf16x8 dsb = dtr.read(dtile(buf, w), t * 16, 0);
-#pragma unroll
-        for (int db = 0; db < DQK / 32; ++db) dq[db] = mfma32(ktr.read(ktile(buf), t * 16, db), dsb, dq[db]);
+        for (int db = 0; db < DQK / 32; ++db) {
+          const bf16x8 kop = ktr.read(ktile(buf), t * 16, db);
+          dq[0][db] = mfma32(kop, ds0, dq[0][db]);
+          dq[1][db] = mfma32(kop, ds1, dq[1][db]);
+        }
       }
     }
     lds_dma_wait();
@@ -146,21 +155,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
     if (st + 1 <= s1) step(st + 1, B1{});
   }
 
-  // Lane: position l32 -> row qw0 + acc_row(l32 % 16, l32 / 16); dims
-  // db*32 + ig*8 + hf*4 + 0..3 from elements 4 ig .. 4 ig + 3.  The blocks
-  // hold -dS, so dQ = -scale * acc.
-  const int qi = qw0 + acc_row(l32 & 15, l32 >> 4);
-  if (qi < seq_rows(a, b)) {
-    uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK + hf * 4;
-    const float qs = -a.scale;
+  // Lane: position l32 -> row acc_row(l32 % 16, l32 / 16) of each block;
+  // dims db*32 + ig*8 + hf*4 + 0..3 from elements 4 ig .. 4 ig + 3.  The
+  // blocks hold -dS, so dQ = -scale * acc.
+  const float qs = -a.scale;
 #pragma unroll
-    for (int db = 0; db < DQK / 32; ++db)
+  for (int rb = 0; rb < 2; ++rb) {
+    const int qi = qw0 + rb * 32 + acc_row(l32 & 15, l32 >> 4);
+    if (qi < seq_rows(a, b)) {
+      uint16_t* dqp = static_cast<uint16_t*>(a.dq) + ((seq_row0(a, b) + qi) * a.Hq + h) * DQK + hf * 4;
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        u32x2 val = {pack_bf16(dq[db][ig * 4] * qs, dq[db][ig * 4 + 1] * qs),
-                     pack_bf16(dq[db][ig * 4 + 2] * qs, dq[db][ig * 4 + 3] * qs)};
-        *reinterpret_cast<u32x2*>(dqp + db * 32 + ig * 8) = val;
-      }
+      for (int db = 0; db < DQK / 32; ++db)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          u32x2 val = {pack_bf16(dq[rb][db][ig * 4] * qs, dq[rb][db][ig * 4 + 1] * qs),
+                       pack_bf16(dq[rb][db][ig * 4 + 2] * qs, dq[rb][db][ig * 4 + 3] * qs)};
+          *reinterpret_cast<u32x2*>(dqp + db * 32 + ig * 8) = val;
+        }
+    }
   }
 }
 
