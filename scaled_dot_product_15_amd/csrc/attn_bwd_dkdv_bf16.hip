@@ -403,10 +403,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // is seen at least by its own row) -- the test tile_class makes, with
   // which the dQ kernel decides what it reads; padding blocks (index NB and
   // up) store nothing (empty resource).  A block's dS is complete once its
-  // masked redo has run; the two blocks of a stage go out together right
-  // after the barrier that opens the stage two blocks later, so the stores
-  // have two iterations to drain before the next copy wait (which counts
-  // them too).  Non-temporal stores (cache policy nt): the blocks are read
+  // masked redo has run, so iteration u stores block u - 1, whose registers
+  // its C products read anyway (storing two blocks after each stage barrier,
+  // to give the stores longer before the next copy wait, kept one block's dS
+  // live an iteration longer: 8 % slower at head dim 192, no faster below).
+  // Non-temporal stores (cache policy nt): the blocks are read
   // once, by the next kernel, and would otherwise push this kernel's Q / dO
   // tiles out of L2 (measured: 4-5 % on the kernel).
   constexpr int kNonTemporal = 2;
@@ -529,11 +530,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     }
     const int q_u = b_walk.q0 + cur * 32;  // first row of block u
     const int bh_u = b * a.Hq + g * a.G + hs * Gs + b_walk.hh;  // its (batch, query head)
-    if constexpr (DSOUT && (P & 1) != 0) {
-      // Blocks u-2 (second half of the previous stage; set cur, not yet
-      // overwritten by B(u)) and u-1 (first half of this one; set nxt).
-      store_ds(u - 2, ds_prev + 4096, ds_prev_q + 32, DW[cur]);
-      store_ds(u - 1, ds_cur, ds_cur_q, DW[nxt]);
+    if constexpr (DSOUT) {
+      // Block u-1 (set nxt, read by C(u-1) in this iteration anyway): the
+      // first half of this stage (odd u) or the second half of the previous
+      // one (even u).
+      if constexpr ((P & 1) != 0) store_ds(u - 1, ds_cur, ds_cur_q, DW[nxt]);
+      else store_ds(u - 1, ds_prev + 4096, ds_prev_q + 32, DW[nxt]);
     }
     uint32_t rnd_u[4] = {0u, 0u, 0u, 0u};
     if constexpr (DROP) drop_rows(bh_u, q_u, rnd_u);
@@ -654,9 +656,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
     }
     // Block NI (even, first half of stage NI/2, ring slot 0) still owes C.
     phase_c(qtile(0), otile(0), 0, PW[0], DW[0]);
-    // Blocks NI-1 (set 1, second half of the previous stage) and NI (set 0).
-    store_ds(NI - 1, ds_prev + 4096, ds_prev_q + 32, DW[1]);
-    store_ds(NI, ds_cur, ds_cur_q, DW[0]);
+    store_ds(NI, ds_cur, ds_cur_q, DW[0]);  // block NI (set 0)
   }
 
   // Epilogue: lane owns key kj, dims db*32 + acc_row(i, hf).
