@@ -13,9 +13,11 @@
 // (batch, query head), 64 per wave (two 32-row blocks, so each K^T operand
 // read from LDS feeds two products), and walks the visible keys in steps of
 // 32 (a quarter of a dK/dV key tile).  Per step, direct memory-to-LDS copies
-// (double buffered, one barrier per step) bring the K rows ([32][DQK],
-// swizzled) and each block's dS ([32 keys][32 positions], swizzled 64-byte
-// rows).
+// bring the K rows ([32][DQK], swizzled) and each block's dS ([32 keys][32
+// positions], swizzled 64-byte rows) into a ring of LDS slots, one barrier
+// per step.  The pass waits on its copies (the products are short), so the
+// ring is as deep as two workgroups per CU allow: three slots, copies two
+// steps ahead, up to head dim 128; two at 192.
 //
 // Layouts.  In a stored block a lane of the dK/dV kernel holds key c = l % 32
 // and the 16 rows acc_row(i, l / 32), i = 0..15, of a 32-row block; here
@@ -40,8 +42,18 @@ struct DqDsCfg {
   static constexpr int KT = BK * DQK;    // K tile elements
   static constexpr int DT = BK * 32;     // one block's dS tile elements
   static constexpr int STAGE = KT + 8 * DT;
-  static constexpr int LDS_ELEMS = 2 * STAGE;
+  static constexpr int NSLOT = DQK <= 128 ? 3 : 2;  // ring slots (copies NSLOT - 1 steps ahead)
+  static constexpr int LDS_ELEMS = NSLOT * STAGE;
+  // Copy instructions per wave and step: the K tile's share and two dS blocks.
+  static constexpr int COPIES = BK * KCH / NT + 4;
 };
+
+// s_waitcnt with vmcnt = n (< 64), expcnt and lgkmcnt at their no-wait maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int DQK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
@@ -74,6 +86,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (seq_row0(a, b) * a.Hkv + g) * DQK;
   const size_t kstride = (size_t)a.Hkv * DQK;
   const TileCopy<C::BK, C::KCH, C::NT> kcopy(tid, (uint32_t)(kstride * 2));
+  static_assert(TileCopy<C::BK, C::KCH, C::NT>::PER_WAVE + 4 == C::COPIES, "copy count");
   const TrReads<C::KCH> ktr(lane);
   const TrReads<4> dtr(lane);
   // dS copy of one block: two 64-lane instructions; lane l of instruction k
@@ -92,9 +105,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
   const MaskSpec mf = make_mask(a.S, a.S, a.causal, a.wl, a.wr);
   int sl_kt = s0 >> 2, sl_first, sl_count;
   ds_slab(a, sl_kt, sl_first, sl_count);
+  // Copies of step st into slot buf; steps past s1 copy nothing (empty
+  // resources land zeros) but keep the per-step instruction count, so the
+  // waits below count whole steps.
   auto issue_step = [&](int st, int buf) __attribute__((always_inline)) {
     const int j0 = st * C::BK;
-    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, m.L, ktile(buf));
+    const bool live = st <= s1;
+    kcopy.issue(Kg, (uint32_t)(kstride * 2), j0, live ? m.L : 0, ktile(buf));
     // Each row block's block in the slab of key tile kt = st / 4: rows from
     // q_first, the tile's first visible row rounded down to 64, for 2 nsteps
     // blocks at this batch's length; its 32-key group st % 4.  Groups no row
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
     }
     int qlo, qhi;
     int r0 = -1, nblk = 0;
-    if (query_range(m, kt * 128, kt * 128 + 127, qlo, qhi)) {
+    if (live && query_range(m, kt * 128, kt * 128 + 127, qlo, qhi)) {
       nblk = 2 * (qhi / 64 - qlo / 64 + 1);
       if (nblk > sl_count) nblk = sl_count;
       r0 = (qw0 - (qlo / 64) * 64) >> 5;
@@ -123,9 +140,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
       for (int k = 0; k < 2; ++k) lds_dma16(d, dst + k * 1024, dvoff[k]);
     }
   };
+  // Step st from slot buf: wait for its copies (those of the NSLOT - 2 later
+  // steps may still be in flight; only these copies are outstanding in the
+  // loop, and loads complete in order), barrier, refill the slot read in the
+  // previous step with step st + NSLOT - 1, then the products.
   auto step = [&](int st, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    if (st < s1) issue_step(st + 1, buf ^ 1);
+    wait_vmcnt<(C::NSLOT - 2) * C::COPIES>();
+    __syncthreads();
+    issue_step(st + C::NSLOT - 1, (buf + C::NSLOT - 1) % C::NSLOT);
     // Blocks whose rows see none of the step's keys hold zeros: a step that
     // neither block of the wave sees is skipped.
     const int j0 = st * C::BK;
@@ -142,18 +165,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
         }
       }
     }
-    lds_dma_wait();
-    __syncthreads();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  if (s0 <= s1) issue_step(s0, 0);
-  lds_dma_wait();
-  __syncthreads();
-  for (int st = s0; st <= s1; st += 2) {
-    step(st, B0{});
-    if (st + 1 <= s1) step(st + 1, B1{});
+  using B2 = std::integral_constant<int, 2>;
+  if (s0 <= s1) {
+#pragma unroll
+    for (int k = 0; k < C::NSLOT - 1; ++k) issue_step(s0 + k, k);
+    if constexpr (C::NSLOT == 3) {
+      for (int st = s0; st <= s1; st += 3) {
+        step(st, B0{});
+        if (st + 1 <= s1) step(st + 1, B1{});
+        if (st + 2 <= s1) step(st + 2, B2{});
+      }
+    } else {
+      for (int st = s0; st <= s1; st += 2) {
+        step(st, B0{});
+        if (st + 1 <= s1) step(st + 1, B1{});
+      }
+    }
   }
+  // Copies of the steps past s1 may still be in flight: wait before the
+  // workgroup's LDS can pass to another one.
+  lds_dma_wait();
 
   // Lane: position l32 -> row acc_row(l32 % 16, l32 / 16) of each block;
   // dims db*32 + ig*8 + hf*4 + 0..3 from elements 4 ig .. 4 ig + 3.  The
@@ -179,7 +213,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
 template __global__ void bwd_dq_ds_bf16_kernel<64>(KArgs);
 template __global__ void bwd_dq_ds_bf16_kernel<128>(KArgs);
 template __global__ void bwd_dq_ds_bf16_kernel<192>(KArgs);
-static_assert(DqDsCfg<192>::LDS_ELEMS * 2 * 2 <= 160 * 1024, "two workgroups per CU at head dim 192");
+static_assert(DqDsCfg<128>::LDS_ELEMS * 2 * 2 <= 160 * 1024 && DqDsCfg<192>::LDS_ELEMS * 2 * 2 <= 160 * 1024,
+              "two workgroups per CU");
 
 hipError_t launch_bwd_dq_ds_bf16(const KArgs& a0, int dqk, int dv, hipStream_t stream) {
   (void)dv;  // dQ needs only K
