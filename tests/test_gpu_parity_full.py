@@ -6,6 +6,7 @@ and sampled keys (dK, dV, summed over every row and head that sees them) in
 float64, for the first, the last and a seeded middle query head (and their KV
 heads); the sink gradient is checked for three heads over all batches and rows.
 Padded rows and keys are checked to be exactly zero over the whole tensor.
+Both backward paths (dQ recomputed, dQ from the stored dS) run at full size.
 """
 import numpy as np
 import pytest
@@ -43,20 +44,23 @@ def _sample_keys(rng, p, L):
     return np.array(sorted(picks))
 
 
-# (config, case, dropout rate): the last two run attention dropout at full size.
-RUNS = [(c, k, 0.0) for c, k in CASES] + [(2, 0, 0.1), (5, 1, 0.1)]
+# (config, case, dropout rate, backward path): attention dropout at full size
+# on two workloads; the backward path the binding does not pick by default
+# (dQ from the stored dS, or recomputed for the 192/128 heads) on four.
+RUNS = ([(c, k, 0.0, None) for c, k in CASES] + [(2, 0, 0.1, None), (5, 1, 0.1, None)] +
+        [(2, 0, 0.0, True), (3, 5, 0.0, True), (5, 1, 0.0, True), (4, 0, 0.0, False)])
 
 
-@pytest.mark.parametrize("cfg,case,drop", RUNS, ids=lambda x: str(x))
-def test_full_size(cfg, case, drop):
+@pytest.mark.parametrize("cfg,case,drop,store_ds", RUNS, ids=lambda x: str(x))
+def test_full_size(cfg, case, drop, store_ds):
     import torch
     p = inputs.workload_configs()[cfg][case]
     seed = 1000 * cfg + case
-    gc.log(f"config {cfg} case {case}: {p.name} seed={seed} dropout={drop}")
+    gc.log(f"config {cfg} case {case}: {p.name} seed={seed} dropout={drop} store_ds={store_ds}")
     arr = inputs.draw(p, seed)
     t = inputs.to_torch(arr, p.dtype, "cuda")
     dropout = (drop, seed, 77) if drop else None
-    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout)
+    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout, store_ds=store_ds)
     B, S = p.B, p.S
     L = np.full(B, S) if arr["seqlens"] is None else arr["seqlens"]
     for b in range(B):
@@ -133,7 +137,7 @@ def test_long_sequence(st, drop):
     arr = inputs.draw(p, seed)
     t = inputs.to_torch(arr, "bf16", "cuda")
     dropout = (drop, seed, 5) if drop else None
-    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout)
+    o, lse, dq, dk, dv, doff = gc.run_gpu(p, t, dropout=dropout, store_ds=store_ds)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
     assert bool(torch.isfinite(dk).all()) and bool(torch.isfinite(dv).all())
     host = {n: t[n].float().cpu().numpy() for n in ("q", "k", "v", "do")}
