@@ -113,15 +113,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   auto delta_s = [&](int buf) __attribute__((always_inline)) { return lse_s(buf) + C::BMQ; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  // Workgroup id -> (key tile, batch, kv head, head split): consecutive ids
-  // cover all of one key tile, so with B*Hkv*n_splits a multiple of 8 a given
-  // (batch, kv head, split) always lands on the same XCD and its Q/dO tiles,
-  // read again by the neighbouring key tiles, stay in that XCD's L2.  Key tiles in
-  // ascending order: under a causal mask the first ones see the most queries.
-  // Head split hs of n_splits covers query heads hs*Gs .. hs*Gs+Gs-1 of the group.
+  // Workgroup id -> (batch, kv head, head split; key tile).  Grouped order:
+  // the key tiles of one (batch, kv head, split) read overlapping Q / dO
+  // rows, so they run together on one XCD (xcd_group_item) and the rows a
+  // tile copies are still in that XCD's L2 when its neighbours reach them.
+  // Otherwise consecutive ids cover all groups of one key tile (with
+  // B*Hkv*n_splits a multiple of 8 a group always lands on the same XCD).
+  // Key tiles in ascending order: under a causal mask the first ones see the
+  // most queries.  Head split hs of n_splits covers query heads
+  // hs*Gs .. hs*Gs+Gs-1 of the group.
   const int nsp = a.n_splits, Gs = a.G / nsp;
-  const int kt = blockIdx.x / (a.B * a.Hkv * nsp);
-  int r = blockIdx.x % (a.B * a.Hkv * nsp);
+  int r, kt;
+  if constexpr (kGroupedOrder<DQK>) {
+    xcd_group_item(blockIdx.x, a.B * a.Hkv * nsp, (a.S + C::BN - 1) / C::BN, r, kt);
+  } else {
+    kt = blockIdx.x / (a.B * a.Hkv * nsp);
+    r = blockIdx.x % (a.B * a.Hkv * nsp);
+  }
+  kt = __builtin_amdgcn_readfirstlane(kt);  // wave-uniform: scalar registers
+  r = __builtin_amdgcn_readfirstlane(r);
   const int hs = r % nsp;
   r /= nsp;
   const int b = r / a.Hkv, g = r % a.Hkv;

@@ -70,10 +70,22 @@ __global__ __launch_bounds__(64 * SDPA_DQ_WAVES, ((DROP != BIAS) && DQK <= 128) 
   auto vtile = [&](int buf) __attribute__((always_inline)) { return lds + buf * (C::KT + C::VT) + C::KT; };
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  // Same tile order as the forward: heavy query tiles first, the heads of a
-  // GQA group on consecutive ids kept on one XCD.
+  // Same tile order as the forward (q_tile_of).  Below 128 dims it is
+  // written here through xcd_group_item (groups of the G heads of one query
+  // tile; the same assignment q_tile_of computes): with that arithmetic the
+  // compiler fits the 64-dim kernel in 168 registers, three waves per SIMD
+  // instead of two (dQ 5-7 % faster on the 64-dim sweep).
   int b, h, qt;
-  dq_tile_of(a, blockIdx.x, b, h, qt);
+  if constexpr (kGroupedOrder<DQK>) {
+    q_tile_of<true>(a, blockIdx.x, b, h, qt);
+  } else {
+    int grp, item;
+    xcd_group_item(blockIdx.x, a.B * a.Hkv * a.n_tiles, a.G, grp, item);
+    const int per_tile = a.B * a.Hkv;
+    qt = a.n_tiles - 1 - grp / per_tile;
+    b = (grp % per_tile) / a.Hkv;
+    h = (grp % per_tile) % a.Hkv * a.G + item;
+  }
   const int g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int bh = b * a.Hq + h;

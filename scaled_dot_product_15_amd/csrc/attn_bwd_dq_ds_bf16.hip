@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
-  dq_tile_of(a, blockIdx.x, b, h, qt);
+  q_tile_of<kGroupedOrder<DQK>>(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
   const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
   const int i0 = qt * C::BM, qw0 = i0 + w * 64;

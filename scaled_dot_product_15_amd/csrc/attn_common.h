@@ -75,6 +75,15 @@ struct KArgs {
   int ds_head_blocks;
 };
 
+// Workgroup order of the bf16 kernels (q_tile_of, the dK/dV kernel): for head
+// dims of 128 and up the items that share K / V (or Q / dO) rows are grouped
+// on one XCD, where those rows are large (measured per step: GQA+SWA S=4096
+// 2-5 %, MLA 192/128 10 %, sink + padding S=8192 4 % faster); the 64-dim
+// kernels keep the heaviest tiles first over the whole grid (the 64-dim
+// sweep's short sequences ran 10 % slower grouped).
+template <int DQK>
+constexpr bool kGroupedOrder = DQK >= 128;
+
 // Stored-dS slab of key tile kt: its first block within the (batch, head)
 // region and its block count, from the mask at the full length S (a loop over
 // the tiles before it: a few scalar instructions each, once per workgroup).
@@ -85,20 +94,54 @@ __device__ __forceinline__ void ds_slab(const KArgs& a, int kt, int& first, int&
   count = ds_tile_blocks(mf, kt);
 }
 
-// Query tile, batch and head of workgroup `id` of the dQ kernels (n_tiles
-// query tiles per head): tiles with the most keys first (the last ones under a
-// causal mask), the heads of a GQA group on consecutive ids kept on one XCD.
-__device__ __forceinline__ void dq_tile_of(const KArgs& a, int id, int& b, int& h, int& qt) {
-  const int N = a.B * a.Hq * a.n_tiles, chunk = a.G, full = (N / (8 * chunk)) * (8 * chunk);
-  int l = id;
-  if (l < full) {
-    const int xcd = l & 7, slot = l >> 3;
-    l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+// Group and item of workgroup `id` in a grid of n_groups x per_group work
+// items where the items of one group read the same rows (the K tiles of a KV
+// head, the Q / dO rows of a key tile's neighbours): the hardware deals
+// consecutive workgroups round-robin over the 8 XCDs, each with its own L2, so
+// group n's items go to XCD n % 8 in consecutive slots there and run at the
+// same time, sharing that L2.  Groups past the last multiple of 8 are dealt
+// in plain order.  A bijection of [0, n_groups * per_group).
+__device__ __forceinline__ void xcd_group_item(int id, int n_groups, int per_group, int& group, int& item) {
+  const int full = (n_groups / 8) * 8 * per_group;
+  if (id < full) {
+    const int xcd = id & 7, slot = id >> 3;
+    group = (slot / per_group) * 8 + xcd;
+    item = slot % per_group;
+  } else {
+    group = id / per_group;
+    item = id % per_group;
   }
-  const int per_tile = a.B * a.Hq;
-  qt = a.n_tiles - 1 - l / per_tile;
-  b = (l % per_tile) / a.Hq;
-  h = (l % per_tile) % a.Hq;
+}
+
+// Query tile, batch and head of workgroup `id` of the forward and dQ kernels
+// (n_tiles query tiles per head).  Grouped order: the G heads x n_tiles tiles
+// of a (batch, KV head) read the same K / V tiles, so they run together on
+// one XCD (xcd_group_item), heaviest query tiles first (the last ones under a
+// causal mask) and the G heads of a tile side by side.  Otherwise the
+// heaviest tiles of every head come first over the whole grid (the tail is
+// balanced best) and only the G heads of a tile share an XCD.
+template <bool GROUPED>
+__device__ __forceinline__ void q_tile_of(const KArgs& a, int id, int& b, int& h, int& qt) {
+  if constexpr (GROUPED) {
+    int grp, item;
+    xcd_group_item(id, a.B * a.Hkv, a.G * a.n_tiles, grp, item);
+    b = grp / a.Hkv;
+    const int g = grp % a.Hkv;
+    qt = a.n_tiles - 1 - item / a.G;
+    h = g * a.G + item % a.G;
+  } else {
+    // the G heads of one query tile on consecutive ids of one XCD
+    const int N = a.B * a.Hq * a.n_tiles, chunk = a.G, full = (N / (8 * chunk)) * (8 * chunk);
+    int l = id;
+    if (l < full) {
+      const int xcd = l & 7, slot = l >> 3;
+      l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+    }
+    const int per_tile = a.B * a.Hq;
+    qt = a.n_tiles - 1 - l / per_tile;
+    b = (l % per_tile) / a.Hq;
+    h = (l % per_tile) % a.Hq;
+  }
 }
 
 // First row of batch b along the token axis of Q, K, V, O and the gradients:

@@ -69,27 +69,6 @@ struct FwdBf16Cfg {
   static_assert(BN % 32 == 0 && DQK % 32 == 0 && DV % 32 == 0, "tile shape");
 };
 
-// Logical tile order for a linear workgroup id: heaviest query tiles first
-// (for causal masks the last tiles see the most keys), and the G query heads
-// sharing a KV head on consecutive ids, which are then kept on one XCD (the
-// hardware deals consecutive workgroups round-robin over the 8 XCDs, each with
-// its own L2) so the group reads its K/V tiles through a shared L2.
-__device__ __forceinline__ void fwd_tile_of(const KArgs& a, int bid, int& b, int& h, int& qt) {
-  const int N = a.B * a.Hq * a.n_tiles;
-  const int chunk = a.G;
-  const int full = (N / (8 * chunk)) * (8 * chunk);
-  int l = bid;
-  if (bid < full) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    l = ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
-  }
-  const int per_tile = a.B * a.Hq;
-  qt = a.n_tiles - 1 - l / per_tile;
-  const int r = l % per_tile;
-  b = r / a.Hq;
-  h = r % a.Hq;
-}
-
 template <int DQK, int DV, int BN, int OCC, bool DROP, bool BIAS>
 __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArgs a) {
   using C = FwdBf16Cfg<DQK, DV, BN>;
@@ -97,7 +76,7 @@ __global__ __launch_bounds__(64 * SDPA_FWD_WAVES, OCC) void fwd_bf16_kernel(KArg
 
   const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   int b, h, qt;
-  fwd_tile_of(a, blockIdx.x, b, h, qt);
+  q_tile_of<kGroupedOrder<DQK>>(a, blockIdx.x, b, h, qt);
   const int g = h / a.G;
   const int bh = b * a.Hq + h;
   const DropGen dg = drop_gen(a);
