@@ -143,13 +143,14 @@ def attn_bwd_ds_workspace_size(p: Params) -> int:
 # Largest workspace attn_bwd allocates by itself to keep dS (store_ds=None).
 DS_WORKSPACE_LIMIT = 8 << 30
 # Smallest Q/K head dim for which attn_bwd keeps dS by default (store_ds=None).
-# Measured on one MI355X (fwd + bwd step): 192/128 heads (causal, S=4096, 128
-# heads) 8.36 -> 7.10 ms with stored dS, since the dQ kernel that recomputes S
-# and dP runs one wave per SIMD there; 128/128 heads within noise (GQA with a
-# 1024-key window at S=4096: 1.266 -> 1.249 ms; 4096-key window at S=8192:
-# 4.32 -> 4.31 and 4.88 -> 4.98 ms) for 1-9 GB more workspace; 64/64 heads
-# (causal, S=512..16384) 5-18 % slower: the dK/dV kernel's dS stores cost more
-# than recomputing the cheap 64-dim products saves.
+# Measured on one MI355X (fwd + bwd step, both paths in one run): 192/128 heads
+# (causal, S=4096, 128 heads) 7.49 -> 6.10 ms with stored dS, since the dQ
+# kernel that recomputes S and dP runs one wave per SIMD there; 128/128 heads
+# 1-3 % faster (GQA with a 1024-key window at S=4096: 1.253 -> 1.216 ms; a
+# 4096-key window at S=8192: 4.08 -> 4.04 ms) for 1.1-9 GB more workspace, so
+# left to the caller (store_ds=True); 64/64 heads (causal, S=4096..8192)
+# 9-12 % slower: the dK/dV kernel's dS stores cost more than recomputing the
+# cheap 64-dim products saves.
 DS_DEFAULT_MIN_HEAD_DIM = 192
 
 
