@@ -124,16 +124,17 @@ def test_full_size(cfg, case, drop, store_ds):
     gc.check(p, stats, f"config {cfg} case {case}")
 
 
-@pytest.mark.parametrize("st,drop", [("vanilla", 0.0), ("learnable", 0.1)], ids=str)
-def test_long_sequence(st, drop):
+@pytest.mark.parametrize("st,drop,store_ds", [("vanilla", 0.0, True), ("learnable", 0.1, None)], ids=str)
+def test_long_sequence(st, drop, store_ds):
     """S = 131072 tokens (sliding window 1024, causal, GQA 4:1, d = 128): row and
     byte offsets far past every listed workload, checked on sampled rows and
-    keys (start, middle, end) against the row/key-sampled oracle."""
+    keys (start, middle, end) against the row/key-sampled oracle; the case
+    without dropout takes the stored-dS backward (1.2 GB of dS blocks)."""
     import torch
     p = inputs.Problem(B=1, S=131072, Hq=4, Hkv=1, d_qk=128, d_v=128, dtype="bf16", causal=True,
                        window=(1024, 0), softmax_type=st)
     seed = 70_000 + int(drop * 10)
-    gc.log(f"long sequence S={p.S} {st} dropout={drop} seed={seed}")
+    gc.log(f"long sequence S={p.S} {st} dropout={drop} store_ds={store_ds} seed={seed}")
     arr = inputs.draw(p, seed)
     t = inputs.to_torch(arr, "bf16", "cuda")
     dropout = (drop, seed, 5) if drop else None
