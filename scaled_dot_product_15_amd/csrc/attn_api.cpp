@@ -166,6 +166,8 @@ size_t attn_fwd_workspace_size(const attn_params* p) {
 
 size_t attn_bwd_ds_workspace_size(const attn_params* p) {
   if (attn_validate(p) != ATTN_OK || !ds_eligible(p)) return 0;
+  // The kernels index a head's blocks with 32-bit integers.
+  if (ds_head_blocks(p) > 0x7fffffffLL) return 0;
   return attn_bwd_workspace_size(p) + ds_bytes(p);
 }
 

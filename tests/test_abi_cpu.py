@@ -146,6 +146,9 @@ def test_ds_workspace_size_zero_without_the_path():
     big = P(B=4, S=4096, Hq=32, Hkv=8, window_size=(1024, 0))
     n = _ds_blocks_expected(4096, True, 1024, 0)
     assert binding.attn_bwd_ds_workspace_size(big) - binding.attn_bwd_workspace_size(big) == 4 * 32 * n * 8192
+    # a head's blocks must fit a 32-bit index (no mask, S = 2^22: 2^32 blocks)
+    assert binding.attn_bwd_ds_workspace_size(P(B=1, S=1 << 22, Hq=1, Hkv=1, d_qk=64, d_v=64,
+                                                attn_mask_type="no_mask")) == 0
     mla = P(B=2, S=4096, Hq=128, Hkv=128, d_qk=192, d_v=128)
     assert binding.attn_bwd_ds_workspace_size(mla) - binding.attn_bwd_workspace_size(mla) == 2 * 128 * 2112 * 8192
 
