@@ -55,6 +55,11 @@
 // random bytes of a lane's key and one 4-row group come from one generator
 // call, which is exactly one pipeline chunk's share of B.
 //
+// DSOUT (the stored-dS backward): the kernel also writes each block's bf16 dS
+// (the B operand of its dK products) to the workspace, block by block, for a
+// dQ kernel that contracts it with K instead of recomputing S and dP
+// (attn_bwd_dq_ds_bf16.hip); layout and store rules at the stores below.
+//
 // BIAS (additive post-scale attention bias, P = exp(scale q.k + bias - LSE)):
 // each stage also holds the bias tile of its 64 rows x the workgroup's 128
 // keys (swizzled rows, copied with Q and dO).  A lane needs its key's values

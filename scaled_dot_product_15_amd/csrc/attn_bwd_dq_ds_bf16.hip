@@ -17,7 +17,9 @@
 // positions], swizzled 64-byte rows) into a ring of LDS slots, one barrier
 // per step.  The pass waits on its copies (the products are short), so the
 // ring is as deep as two workgroups per CU allow: three slots, copies two
-// steps ahead, up to head dim 128; two at 192.
+// steps ahead, up to head dim 128; two at 192.  Workgroups run in the
+// forward's order (q_tile_of): from head dim 128 up, a KV head's query tiles
+// run together on one XCD and share its K tiles through that XCD's L2.
 //
 // Layouts.  In a stored block a lane of the dK/dV kernel holds key c = l % 32
 // and the 16 rows acc_row(i, l / 32), i = 0..15, of a 32-row block; here
