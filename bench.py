@@ -372,9 +372,9 @@ def main():
                              p.window, kw["scale_factor"], p.softmax_type, args.dropout)
     # The workspace decides the backward's path: with room for the dS blocks
     # the dK/dV kernel stores dS and the dQ kernel contracts it with K.
-    ds_size = binding.attn_bwd_ds_workspace_size(pp) if args.bias == "none" else 0
+    ds_size = binding.attn_bwd_ds_workspace_size(pp)
     stored_ds = ds_size > 0 and (args.dq_path == "stored-ds" or
-                                 (args.dq_path == "default" and binding.prefers_stored_ds(pp)))
+                                 (args.dq_path == "default" and binding.prefers_stored_ds(pp, kw.get("bias"))))
     ws = torch.empty(ds_size if stored_ds else binding.attn_bwd_workspace_size(pp), dtype=torch.uint8,
                      device="cuda")
     fast = dict(kw, check_seqlens=False)

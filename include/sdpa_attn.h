@@ -163,11 +163,13 @@ size_t attn_bwd_workspace_size(const struct attn_params* p);
  * causal, S (window + 192) / 4096 with a window (1.1 GB for B=4, S=4096,
  * Hq=32 and a 1024-key causal window; 4.4 GB for B=2, S=4096, Hq=128,
  * causal).  attn_bwd takes this path whenever workspace_bytes is at least
- * this size (and > 0), and so does attn_bwd_stage (stage order 1, 3, 2, 4
- * then); attn_bwd_bias and attn_bwd_noalloc never do.  Results agree with
- * the recomputing path to rounding (dS is the same bf16 value either way; S,
- * dP and delta are summed in another order), and are bitwise reproducible
- * run to run on either path. */
+ * this size (and > 0), and so do attn_bwd_stage (stage order 1, 3, 2, 4
+ * then) and attn_bwd_bias (dBias then summed from the stored blocks);
+ * attn_bwd_noalloc never does.  Results agree with the recomputing path to
+ * rounding (dS is the same bf16 value either way; S, dP and delta are summed
+ * in another order, and a shared bias's gradient sums the bf16 dS blocks
+ * where the other path sums fp32 dS), and are bitwise reproducible run to
+ * run on either path. */
 size_t attn_bwd_ds_workspace_size(const struct attn_params* p);
 
 /* Forward.  Writes O [B,S,Hq,Dv] (packed: [T,Hq,Dv]) and LSE [B,Hq,S].
@@ -247,7 +249,10 @@ int attn_fwd_bias(const struct attn_params* p, const void* q, const void* k, con
  * array of the bias's shape, overwritten with d(loss)/d(bias): dS = P * (dP -
  * delta) on the pairs each sharing (batch, head) sees, zero elsewhere,
  * summed over the batches and heads that share a bias matrix in ascending
- * order (bitwise reproducible). */
+ * order (bitwise reproducible).  With attn_bwd_ds_workspace_size(p) bytes of
+ * workspace or more (no dropout) the dK/dV kernel stores dS and dQ and dBias
+ * are computed from it, which for a bias shared over batches or heads saves
+ * recomputing S and dP once per sharing (batch, head) pair. */
 int attn_bwd_bias(const struct attn_params* p, const void* q, const void* k, const void* v,
                   const void* o, const void* d_o, const float* lse, const void* bias,
                   int32_t bias_batch, int32_t bias_heads, void* d_bias, const float* softmax_offset,

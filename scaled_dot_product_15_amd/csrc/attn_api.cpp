@@ -260,9 +260,15 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   }
   KArgs a = make_args(p);
   if (bias) set_bias(a, bias->bias, bias->d_bias, bias->batch, bias->heads);
-  // A bias with one matrix per (batch, head) has dBias = dS: the dQ kernel
-  // writes it (its dS values, zeros elsewhere) and no separate pass runs.
-  a.dbias_direct = bias && bias->d_bias && bias->batch == p->batch && bias->heads == p->num_heads;
+  // With room for the dS blocks: pre-pass, dK/dV storing dS, dQ from the
+  // stored dS (and dBias summed from it) -- stages 1, 3, 2, 4.  Otherwise
+  // 1, 2, 3, 4, the bf16 dQ kernel running the pre-pass itself.
+  const size_t ds_ws = attn_bwd_ds_workspace_size(p);
+  const bool use_ds = ds_ws > 0 && workspace_bytes >= ds_ws;
+  // A bias with one matrix per (batch, head) has dBias = dS: on the
+  // recomputing path the dQ kernel writes it (its dS values, zeros
+  // elsewhere) and no separate pass runs.
+  a.dbias_direct = !use_ds && bias && bias->d_bias && bias->batch == p->batch && bias->heads == p->num_heads;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -283,11 +289,6 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == ATTN_BF16;
   const int dqk = p->head_dim_qk, dvd = p->head_dim_v;
-  // With room for the dS blocks (and no bias): pre-pass, dK/dV storing dS,
-  // dQ from the stored dS -- stages 1, 3, 2, 4.  Otherwise 1, 2, 3, 4, the
-  // bf16 dQ kernel running the pre-pass itself.
-  const size_t ds_ws = bias ? 0 : attn_bwd_ds_workspace_size(p);
-  const bool use_ds = ds_ws > 0 && workspace_bytes >= ds_ws;
   if (use_ds) {
     a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + attn_bwd_workspace_size(p));
     a.ds_head_blocks = (int)ds_head_blocks(p);
@@ -312,7 +313,8 @@ int bwd_run(int stage, const attn_params* p, const void* q, const void* k, const
     if ((stage == 0 || stage == ATTN_BWD_STAGE_DKDV) && run_dkdv() != hipSuccess) return ATTN_ERR_HIP;
   }
   if (stage == 0 && a.bias && a.d_bias && !a.dbias_direct) {
-    if (launch_bwd_dbias_bf16(a, dqk, dvd, s) != hipSuccess) return ATTN_ERR_HIP;
+    if ((use_ds ? launch_dbias_from_ds(a, s) : launch_bwd_dbias_bf16(a, dqk, dvd, s)) != hipSuccess)
+      return ATTN_ERR_HIP;
   }
   if ((stage == 0 || stage == ATTN_BWD_STAGE_OFFSET_GRAD) && d_softmax_offset &&
       p->softmax_type != ATTN_SOFTMAX_VANILLA) {

@@ -20,6 +20,9 @@
 // LSE * log2(e) come from the backward pre-pass in the workspace.  The tile is
 // then written whole (zeros where no sharing pair sees it), so the output
 // needs no clearing.
+//
+// On the stored-dS backward dS is already in the workspace and
+// dbias_from_ds_kernel (end of this file) only sums it.
 #include "dropout.h"
 #include "launch.h"
 
@@ -211,6 +214,104 @@ hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t st
   if (dqk == 64 && dv == 64) return launch_dbias_cfg<64, 64>(a, stream);
   if (dqk == 128 && dv == 128) return launch_dbias_cfg<128, 128>(a, stream);
   return hipErrorInvalidValue;
+}
+
+// ---- dBias from the stored dS ------------------------------------------------
+//
+// On the stored-dS backward the dK/dV kernel has written every visible 32-row
+// x 32-key block of dS (-dS, in its register order: lane l of key group w holds
+// key w*32 + l%32 and rows acc_row(i, l/32), i = 0..15, 32 bytes at
+// w*2048 + l*32 of the 8 KiB block of 32 rows x 128 keys).  dBias of a bias
+// matrix is then the sum of those blocks over the sharing (batch, query head)
+// pairs, in ascending pair order, with no recomputation.  A workgroup owns
+// kDbRowBlocks blocks of 32 rows x 128 keys of one bias matrix, one after the
+// other: each thread adds up one key's 16 rows over the pairs whose block
+// exists (the tests the dK/dV kernel stores by: the key tile's slab range at
+// the batch's length, and tile_class of the 32 x 32 block), the block is
+// transposed through LDS and written as whole 16-byte row pieces, zeros where
+// no pair sees it.
+constexpr int kDbRowBlocks = 4;
+
+// First block of key tile kt's slab (ds_slab's `first`), the tiles before it
+// dealt over a wave's lanes and summed: these workgroups are small, and the
+// one-lane loop of ds_slab would cost more than their memory traffic.
+__device__ __forceinline__ int ds_slab_first_lanes(const KArgs& a, int kt, int lane) {
+  const MaskSpec mf = make_mask(a.S, a.S, a.causal, a.wl, a.wr);
+  int n = 0;
+  for (int t = lane; t < kt; t += 64) n += ds_tile_blocks(mf, t);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+  return __builtin_amdgcn_readfirstlane(n);
+}
+
+__global__ __launch_bounds__(256) void dbias_from_ds_kernel(KArgs a) {
+  __shared__ float tile[32][128 + 4];
+  const int tid = threadIdx.x, w = wave_id(tid), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int n_kt = (a.S + 127) / 128, n_rc = (a.S + 32 * kDbRowBlocks - 1) / (32 * kDbRowBlocks);
+  const int kt = blockIdx.x % n_kt;
+  const int rc = (blockIdx.x / n_kt) % n_rc;
+  const int mat = blockIdx.x / (n_kt * n_rc);
+  const int bb = mat / a.bias_h, hh = mat % a.bias_h;
+  const int nb = a.bias_b == 1 ? a.B : 1, nh = a.bias_h == 1 ? a.Hq : 1;
+  const int k0 = kt * 128 + w * 32;  // this wave's key group
+  const int first = ds_slab_first_lanes(a, kt, lane);
+  const int count = ds_tile_blocks(make_mask(a.S, a.S, a.causal, a.wl, a.wr), kt);
+  uint16_t* out = static_cast<uint16_t*>(a.d_bias) + ((size_t)bb * a.bias_h + hh) * a.S * a.S;
+  for (int j = 0; j < kDbRowBlocks; ++j) {
+    const int r0 = (rc * kDbRowBlocks + j) * 32;
+    if (r0 >= a.S) break;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int bi = 0; bi < nb; ++bi) {
+      const int b = a.bias_b == 1 ? bi : bb;
+      const MaskSpec m = make_mask(seq_len(a, b), a.S, a.causal, a.wl, a.wr);
+      int qlo, qhi;
+      if (!query_range(m, kt * 128, kt * 128 + 127, qlo, qhi)) continue;
+      int nblk = 2 * (qhi / 64 - qlo / 64 + 1);
+      nblk = nblk < count ? nblk : count;
+      const int r = (r0 - (qlo / 64) * 64) >> 5;
+      if (r < 0 || r >= nblk || tile_class(m, r0, 32, k0, 32) == TILE_SKIP) continue;
+#pragma unroll 4
+      for (int hi = 0; hi < nh; ++hi) {
+        const int h = a.bias_h == 1 ? hi : hh;
+        const uint16_t* blk =
+            a.ds + ((size_t)(b * a.Hq + h) * a.ds_head_blocks + first + r) * 4096 + w * 1024 + lane * 16;
+        const u32x4 v0 = ldg16(blk), v1 = ldg16(blk + 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(v0[e]);
+          acc[2 * e + 1] += bf16_hi(v0[e]);
+          acc[8 + 2 * e] += bf16_lo(v1[e]);
+          acc[8 + 2 * e + 1] += bf16_hi(v1[e]);
+        }
+      }
+    }
+    if (j > 0) __syncthreads();  // the previous block's rows are read out
+    // The blocks hold -dS.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[acc_row(i, hf)][w * 32 + l32] = -acc[i];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = tid + 256 * k, row = c >> 4, kc = (c & 15) * 8;
+      const int gr = r0 + row, gk = kt * 128 + kc;
+      if (gr < a.S && gk < a.S) {
+        const float* t = &tile[row][kc];
+        *reinterpret_cast<u32x4*>(out + (size_t)gr * a.S + gk) =
+            u32x4{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3]), pack_bf16(t[4], t[5]), pack_bf16(t[6], t[7])};
+      }
+    }
+  }
+}
+
+hipError_t launch_dbias_from_ds(const KArgs& a, hipStream_t stream) {
+  if (!a.ds || !a.d_bias) return hipErrorInvalidValue;
+  const long long n = (long long)a.bias_b * a.bias_h * ((a.S + 127) / 128) *
+                      ((a.S + 32 * kDbRowBlocks - 1) / (32 * kDbRowBlocks));
+  if (n > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dbias_from_ds_kernel, dim3((unsigned)n), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace sdpa

@@ -58,7 +58,8 @@
 // DSOUT (the stored-dS backward): the kernel also writes each block's bf16 dS
 // (the B operand of its dK products) to the workspace, block by block, for a
 // dQ kernel that contracts it with K instead of recomputing S and dP
-// (attn_bwd_dq_ds_bf16.hip); layout and store rules at the stores below.
+// (attn_bwd_dq_ds_bf16.hip) and, with a bias, for the dBias sum
+// (dbias_from_ds_kernel); layout and store rules at the stores below.
 //
 // BIAS (additive post-scale attention bias, P = exp(scale q.k + bias - LSE)):
 // each stage also holds the bias tile of its 64 rows x the workgroup's 128
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // delta - dP and P times it is -dS with no subtraction; dK then
   // accumulates -dK, negated at the end (all exact sign changes).
   constexpr bool FOLD = !DROP;
-  static_assert(!DSOUT || (!DROP && !BIAS), "stored dS: plain variant only");
+  static_assert(!DSOUT || !DROP, "stored dS: no dropout variant");
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   // Ring slot `buf`: tiles Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN]
   // (swizzled) at buf * STAGE; after the NBUF slots' tiles, its row terms
@@ -754,10 +755,12 @@ template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, false>(KAr
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false, false>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false, false>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false, false>(KArgs);
-// Stored-dS variants (no dropout, no bias).
+// Stored-dS variants (no dropout; with a bias at head dims 64 and 128).
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true, true>(KArgs);
 // Bias variants: a stage grows by a 64 x 128 bf16 tile (147 KB of LDS in all
 // at head dim 128; the 192-dim stages would not fit).
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true, false>(KArgs);
@@ -772,7 +775,15 @@ static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   const int nkt = (a.S + D::BN - 1) / D::BN;
   const dim3 grid((unsigned)(nkt * a.B * a.Hkv * a.n_splits));
   if (a.ds) {
-    if (a.bias || a.drop_t > 0) return hipErrorInvalidValue;  // stored dS: plain variant only
+    if (a.drop_t > 0) return hipErrorInvalidValue;  // stored dS: no dropout variant
+    if constexpr (DQK <= 128) {
+      if (a.bias) {
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true, true>), grid, dim3(D::NT), 0, stream, a);
+        return hipGetLastError();
+      }
+    } else if (a.bias) {
+      return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, true>), grid, dim3(D::NT), 0, stream, a);
     return hipGetLastError();
   }

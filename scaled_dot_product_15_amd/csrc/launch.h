@@ -43,6 +43,9 @@ hipError_t launch_bwd_dq_ds_bf16(const KArgs& a, int dqk, int dv, hipStream_t st
 // Gradient of the attention bias (needs the pre-pass's delta and LSE * log2 e).
 int dbias_key_chunks(int n_mats, int n_qt, int n_kt);
 hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t stream);
+// dBias from the stored dS blocks (the stored-dS backward: a.ds set, after the
+// dK/dV kernel).
+hipError_t launch_dbias_from_ds(const KArgs& a, hipStream_t stream);
 
 // FP8 forward (E4M3 Q, K, V): V^T pre-pass into a.vt, then the two-pass kernel.
 size_t fp8_vt_bytes(int B, int S, int Hkv, int dv);

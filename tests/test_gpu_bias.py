@@ -35,20 +35,22 @@ def _bias(p, shape, seed):
                        dtype=torch.float32).to(torch.bfloat16)
 
 
-def _run(p, t, bias, dropout=None):
+def _run(p, t, bias, dropout=None, store_ds=False):
     import torch
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask", window_size=p.window,
               softmax_type=p.softmax_type, softmax_offset=t["alpha"], seqlens=t["seqlens"], bias=bias)
     if dropout is not None:
         kw.update(dropout_p=dropout[0], rng_state=(dropout[1], dropout[2]))
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
-    dq, dk, dv, doff, dbias = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=True, **kw)
+    dq, dk, dv, doff, dbias = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=True,
+                                               store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     return (o, lse, dq, dk, dv, doff), dbias
 
 
+@pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
 @pytest.mark.parametrize("dims,shape,mask,st", CASES, ids=lambda x: str(x))
-def test_bias_small_parity(dims, shape, mask, st):
+def test_bias_small_parity(dims, shape, mask, st, store_ds):
     d = DIMS[dims]
     causal, win = MASKS[mask]
     p = inputs.Problem(B=3, S=336, Hq=4, Hkv=2, d_qk=d, d_v=d, dtype="bf16", causal=causal, window=win,
@@ -58,8 +60,8 @@ def test_bias_small_parity(dims, shape, mask, st):
     arr["seqlens"] = np.array([336, 150, 0], dtype=np.int32)
     t = inputs.to_torch(arr, "bf16", "cuda")
     bias = _bias(p, shape, seed)
-    gc.log(f"bias {dims} {shape} {mask} {st} seed={seed}")
-    g, dbias = _run(p, t, bias)
+    gc.log(f"bias {dims} {shape} {mask} {st} seed={seed} store_ds={store_ds}")
+    g, dbias = _run(p, t, bias, store_ds=store_ds)
     b64 = gc.to64(bias)
     r = oracle.attention(gc.to64(t["q"]), gc.to64(t["k"]), gc.to64(t["v"]), gc.to64(t["do"]),
                          num_gqa_groups=p.Hkv, causal=causal, window=win, softmax_type=st,
@@ -118,7 +120,8 @@ def test_bias_with_dropout():
     assert (db[:, :, hidden] == 0).all()
 
 
-def test_bias_full_length_shared():
+@pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
+def test_bias_full_length_shared(store_ds):
     """S = 4096, window (1024, 0), GQA 32:8: one bias matrix shared by every
     batch and head.  Sampled rows of two heads (O, LSE, dQ), sampled keys of two
     KV heads (dK, dV), and sampled rows of the bias gradient, which sums dS over
@@ -130,8 +133,8 @@ def test_bias_full_length_shared():
     arr = inputs.draw(p, seed)
     t = inputs.to_torch(arr, "bf16", "cuda")
     bias = _bias(p, "shared", seed)
-    gc.log("bias full length, shared [1, 1, 4096, 4096]")
-    (o, lse, dq, dk, dv, _), dbias = _run(p, t, bias)
+    gc.log(f"bias full length, shared [1, 1, 4096, 4096], store_ds={store_ds}")
+    (o, lse, dq, dk, dv, _), dbias = _run(p, t, bias, store_ds=store_ds)
     q, k, v, do = (x.cpu() for x in (t["q"], t["k"], t["v"], t["do"]))
     q, k, v, do = (gc.to64(x) for x in (q, k, v, do))
     b64 = gc.to64(bias)
@@ -163,7 +166,8 @@ def test_bias_full_length_shared():
     torch.cuda.empty_cache()
 
 
-def test_bias_packed_equals_padded():
+@pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
+def test_bias_packed_equals_padded(store_ds):
     """Packed (THD) segments with a bias give bitwise the padded (BSHD)
     results: bias rows and keys are positions within the sequence."""
     import torch
@@ -175,14 +179,14 @@ def test_bias_packed_equals_padded():
     arr["seqlens"] = np.array(sizes, dtype=np.int32)
     t = inputs.to_torch(arr, "bf16", "cuda")
     bias = _bias(p, "heads", seed)
-    gc.log("bias packed vs padded")
-    (o, lse, dq, dk, dv, doff), dbias = _run(p, t, bias)
+    gc.log(f"bias packed vs padded, store_ds={store_ds}")
+    (o, lse, dq, dk, dv, doff), dbias = _run(p, t, bias, store_ds=store_ds)
     tp = inputs.to_torch_packed(inputs.pack(arr, sizes), "bf16", "cuda")
     kw = dict(num_gqa_groups=p.Hkv, window_size=p.window, softmax_type=p.softmax_type, seq_offsets=tp["seq_offsets"],
               max_seqlen=p.S, bias=bias)
     po, plse = binding.attn_fwd(tp["q"], tp["k"], tp["v"], **kw)
     pdq, pdk, pdv, pdoff, pdb = binding.attn_bwd(tp["q"], tp["k"], tp["v"], po, plse, tp["do"], want_d_offset=True,
-                                                 **kw)
+                                                 store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     off = [0, 256, 356, 357]
     for b in range(p.B):
@@ -194,16 +198,55 @@ def test_bias_packed_equals_padded():
     assert torch.equal(pdoff, doff) and torch.equal(pdb, dbias)
 
 
-def test_bias_bitwise_reproducible():
+@pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
+def test_bias_bitwise_reproducible(store_ds):
     p = inputs.Problem(B=2, S=296, Hq=4, Hkv=1, d_qk=64, d_v=64, dtype="bf16", causal=True, window=(-1, -1),
                        softmax_type="vanilla")
     t = inputs.to_torch(inputs.draw(p, 74_000), "bf16", "cuda")
     bias = _bias(p, "shared", 74_000)
-    r1, d1 = _run(p, t, bias)
-    r2, d2 = _run(p, t, bias)
+    gc.log(f"bias reproducible, store_ds={store_ds}")
+    r1, d1 = _run(p, t, bias, store_ds=store_ds)
+    r2, d2 = _run(p, t, bias, store_ds=store_ds)
     for a, b in zip(r1, r2):
         assert (a is None and b is None) or torch_equal(a, b)
     assert torch_equal(d1, d2)
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_bias_stored_ds_matches_recompute_with_stale_workspace(shape):
+    """The stored-dS backward with a bias, its workspace filled with NaN
+    patterns before each call: every output finite and bitwise the same on
+    two calls (no unwritten dS block is read, every dBias element is
+    written); dV bitwise the recomputing path's (P is computed the same way),
+    dQ, dK and dBias equal to rounding (dS rounded to bf16 before the sums)."""
+    import torch
+    p = inputs.Problem(B=2, S=264, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16", causal=True, window=(90, 0),
+                       softmax_type="learnable")
+    seed = 75_000 + list(SHAPES).index(shape)
+    arr = inputs.draw(p, seed)
+    arr["seqlens"] = np.array([264, 97], dtype=np.int32)
+    t = inputs.to_torch(arr, "bf16", "cuda")
+    bias = _bias(p, shape, seed)
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal", window_size=p.window, softmax_type=p.softmax_type,
+              softmax_offset=t["alpha"], seqlens=t["seqlens"], bias=bias)
+    o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, "bf16", "causal", p.window, None, p.softmax_type)
+    size = binding.attn_bwd_ds_workspace_size(pp)
+    gc.log(f"bias {shape} stored dS, stale workspace of {size} bytes")
+    ws = torch.full((size,), 0xFF, dtype=torch.uint8, device="cuda")
+    first = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], workspace=ws, **kw)
+    ws.fill_(0xFF)
+    second = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], workspace=ws, **kw)
+    recomputed = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], store_ds=False, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.isfinite(a).all() and torch.equal(a, b)
+    assert torch.equal(first[2], recomputed[2])
+    for i, name in ((0, "dq"), (1, "dk"), (4, "dbias")):
+        rel = gc.rel_l2(gc.to64(first[i]), gc.to64(recomputed[i]))
+        gc.log(f"  {name} stored vs recomputed rel_l2={rel:.3g}")
+        assert rel <= 5e-3, (name, rel)
+    assert np.allclose(first[3].cpu().numpy(), recomputed[3].cpu().numpy(), rtol=1e-3, atol=1e-5)
 
 
 def torch_equal(a, b):
