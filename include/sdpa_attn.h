@@ -154,8 +154,9 @@ size_t attn_bwd_workspace_size(const struct attn_params* p);
  * (codelab "Speed up attention on GPU with cuDNN and TransformerEngine",
  * "How attention works": the score gradient that dK = scale dS^T Q and
  * dQ = scale dS K share) and computes dQ from it instead of recomputing
- * S = QK^T and dP = dO V^T a second time; 0 when the problem has no such path
- * (fp32, FP8, dropout, or more than 2^31 - 1 blocks per head: sequences of
+ * S = QK^T and dP = dO V^T a second time (with dropout the stored dS has the
+ * dropout applied, so dQ needs no random bytes); 0 when the problem has no
+ * such path (fp32, FP8, or more than 2^31 - 1 blocks per head: sequences of
  * millions of tokens without a window) or p is invalid.  The extra room is
  * B * Hq * n * 8 KiB: dS in bf16 blocks of 32 rows x 128 keys, n the number
  * of blocks over all 128-key tiles of the rows that see each tile (in 64-row

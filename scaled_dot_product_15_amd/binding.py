@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import contextlib
 import ctypes
+import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -147,7 +148,7 @@ DS_WORKSPACE_LIMIT = 8 << 30
 # (causal, S=4096, 128 heads) 7.49 -> 6.10 ms with stored dS, since the dQ
 # kernel that recomputes S and dP runs one wave per SIMD there; 128/128 heads
 # 1-3 % faster (GQA with a 1024-key window at S=4096: 1.253 -> 1.216 ms; a
-# 4096-key window at S=8192: 4.08 -> 4.04 ms) for 1.1-9 GB more workspace, so
+# 4096-key window at S=8192: 4.08 -> 4.04 ms) for 1.1-6.6 GB more workspace, so
 # left to the caller (store_ds=True); 64/64 heads (causal, S=4096..8192)
 # 9-12 % slower: the dK/dV kernel's dS stores cost more than recomputing the
 # cheap 64-dim products saves.
@@ -163,11 +164,17 @@ def prefers_stored_ds(p: Params, bias=None) -> bool:
     path runs S and dP once more for every sharing (batch, head) pair
     (measured, GQA 32:8 with a 1024-key window at S=4096, head dim 128:
     backward 2.4-2.7 -> 1.2-1.5 ms).  A bias per (batch, head) gains little
-    (2.09 -> 2.0 ms) and follows the head-dim rule."""
+    (2.09 -> 2.0 ms) and follows the head-dim rule.  With dropout the
+    recomputing dQ kernel also regenerates every random byte, and from head
+    dim 128 the stored dS is the faster path (same workload, p = 0.1: step
+    1.50 -> 1.43 ms; sink + padding S=8192, 6.6 GB of dS: 5.84 -> 5.57 ms);
+    at head dim 64 it is 2 % slower."""
     size = attn_bwd_ds_workspace_size(p)
     if not 0 < size <= DS_WORKSPACE_LIMIT:
         return False
     if bias is not None and (bias.shape[0] == 1 < p.batch or bias.shape[1] == 1 < p.num_heads):
+        return True
+    if math.floor(256.0 * p.dropout_p + 0.5) > 0 and p.head_dim_qk >= 128:
         return True
     return p.head_dim_qk >= DS_DEFAULT_MIN_HEAD_DIM
 

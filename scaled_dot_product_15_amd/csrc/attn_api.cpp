@@ -70,13 +70,11 @@ size_t kv_part_bytes(const attn_params* p) {
                   sizeof(float));
 }
 
-// bf16 backward with stored dS: plain problems (no dropout), every bf16 head
-// dim pair.  Per (batch, head) the slabs of the 128-key tiles, back to back,
-// each ds_tile_blocks blocks of 8 KiB (mask at the full length).
-bool ds_eligible(const attn_params* p) {
-  if (p->dtype != ATTN_BF16) return false;
-  return floor(256.0 * (double)p->dropout_p + 0.5) == 0.0;
-}
+// bf16 backward with stored dS: every bf16 head dim pair, with or without
+// dropout (the stored dS has the dropout applied, so dQ = scale dS K needs no
+// random bytes).  Per (batch, head) the slabs of the 128-key tiles, back to
+// back, each ds_tile_blocks blocks of 8 KiB (mask at the full length).
+bool ds_eligible(const attn_params* p) { return p->dtype == ATTN_BF16; }
 long long ds_head_blocks(const attn_params* p) {
   const MaskSpec m = make_mask(p->seqlen, p->seqlen, p->mask_type == ATTN_MASK_CAUSAL, p->window_left, p->window_right);
   long long n = 0;

@@ -219,9 +219,9 @@ hipError_t launch_bwd_dbias_bf16(const KArgs& a, int dqk, int dv, hipStream_t st
 // ---- dBias from the stored dS ------------------------------------------------
 //
 // On the stored-dS backward the dK/dV kernel has written every visible 32-row
-// x 32-key block of dS (-dS, in its register order: lane l of key group w holds
-// key w*32 + l%32 and rows acc_row(i, l/32), i = 0..15, 32 bytes at
-// w*2048 + l*32 of the 8 KiB block of 32 rows x 128 keys).  dBias of a bias
+// x 32-key block of dS (times ds_stored_sign, in its register order: lane l
+// of key group w holds key w*32 + l%32 and rows acc_row(i, l/32), i = 0..15,
+// 32 bytes at w*2048 + l*32 of the 8 KiB block of 32 rows x 128 keys).  dBias of a bias
 // matrix is then the sum of those blocks over the sharing (batch, query head)
 // pairs, in ascending pair order, with no recomputation.  A workgroup owns
 // kDbRowBlocks blocks of 32 rows x 128 keys of one bias matrix, one after the
@@ -257,6 +257,7 @@ __global__ __launch_bounds__(256) void dbias_from_ds_kernel(KArgs a) {
   const int first = ds_slab_first_lanes(a, kt, lane);
   const int count = ds_tile_blocks(make_mask(a.S, a.S, a.causal, a.wl, a.wr), kt);
   uint16_t* out = static_cast<uint16_t*>(a.d_bias) + ((size_t)bb * a.bias_h + hh) * a.S * a.S;
+  const float sgn = ds_stored_sign(a);
   for (int j = 0; j < kDbRowBlocks; ++j) {
     const int r0 = (rc * kDbRowBlocks + j) * 32;
     if (r0 >= a.S) break;
@@ -288,9 +289,8 @@ __global__ __launch_bounds__(256) void dbias_from_ds_kernel(KArgs a) {
       }
     }
     if (j > 0) __syncthreads();  // the previous block's rows are read out
-    // The blocks hold -dS.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tile[acc_row(i, hf)][w * 32 + l32] = -acc[i];
+    for (int i = 0; i < 16; ++i) tile[acc_row(i, hf)][w * 32 + l32] = sgn * acc[i];
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 2; ++k) {

@@ -107,7 +107,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   // delta - dP and P times it is -dS with no subtraction; dK then
   // accumulates -dK, negated at the end (all exact sign changes).
   constexpr bool FOLD = !DROP;
-  static_assert(!DSOUT || !DROP, "stored dS: no dropout variant");
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
   // Ring slot `buf`: tiles Q [BMQ][DQK], dO [BMQ][DV], bias [BMQ][BN]
   // (swizzled) at buf * STAGE; after the NBUF slots' tiles, its row terms
@@ -409,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(KArgs a) {
   StageWalk copy_walk = b_walk;                    // next stage to copy
 
   // DSOUT: each block's bf16 dS (the B operand of its dK products, which is
-  // -dS here: the fold's sign) goes to block (q - q_first) / 32 of the slab
+  // -dS under the fold, dS with dropout: ds_stored_sign) goes to block (q - q_first) / 32 of the slab
   // of (batch, head, key tile) (ds_slab; a head's slab is ds_head_blocks
   // blocks after the previous head's): wave w's 32 keys at w * 2 KiB, lane
   // l's 16 values (rows q + acc_row(i, l / 32), key l % 32, i = 0..15) at
@@ -755,12 +754,17 @@ template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, false>(KAr
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false, false>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false, false>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false, false>(KArgs);
-// Stored-dS variants (no dropout; with a bias at head dims 64 and 128).
+// Stored-dS variants (with dropout and / or a bias; a bias at head dims 64 and 128).
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, false, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, false, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<192, 128, false, false, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true, true>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<192, 128, true, false, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, true, true>(KArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, true, true>(KArgs);
 // Bias variants: a stage grows by a 64 x 128 bf16 tile (147 KB of LDS in all
 // at head dim 128; the 192-dim stages would not fit).
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, false, true, false>(KArgs);
@@ -768,38 +772,32 @@ template __global__ void bwd_dkdv_bf16_kernel<128, 128, false, true, false>(KArg
 template __global__ void bwd_dkdv_bf16_kernel<64, 64, true, true, false>(KArgs);
 template __global__ void bwd_dkdv_bf16_kernel<128, 128, true, true, false>(KArgs);
 
+// The variant for a's dropout and bias; DSOUT: the stored-dS one.
+template <int DQK, int DV, bool DSOUT>
+static hipError_t launch_dkdv_variant(const KArgs& a, dim3 grid, hipStream_t stream) {
+  constexpr int NT = DkdvCfg<DQK, DV, false>::NT;
+  if constexpr (DQK <= 128) {
+    static_assert(DkdvCfg<DQK, DV, true>::LDS_ELEMS * 2 <= 160 * 1024, "bias stages fit the LDS");
+    if (a.bias) {
+      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, true, DSOUT>), grid, dim3(NT), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true, DSOUT>), grid, dim3(NT), 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.bias) {
+    return hipErrorInvalidValue;  // no bias variant for these head dims
+  }
+  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, false, DSOUT>), grid, dim3(NT), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, DSOUT>), grid, dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int DQK, int DV>
 static hipError_t launch_dkdv_cfg(KArgs a, hipStream_t stream) {
   using D = DkdvCfg<DQK, DV, false>;
   static_assert(D::BN == kDkdvKeyTile, "split rule uses the kernel's key tile");
   const int nkt = (a.S + D::BN - 1) / D::BN;
   const dim3 grid((unsigned)(nkt * a.B * a.Hkv * a.n_splits));
-  if (a.ds) {
-    if (a.drop_t > 0) return hipErrorInvalidValue;  // stored dS: no dropout variant
-    if constexpr (DQK <= 128) {
-      if (a.bias) {
-        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true, true>), grid, dim3(D::NT), 0, stream, a);
-        return hipGetLastError();
-      }
-    } else if (a.bias) {
-      return hipErrorInvalidValue;
-    }
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, true>), grid, dim3(D::NT), 0, stream, a);
-    return hipGetLastError();
-  }
-  if constexpr (DQK <= 128) {
-    static_assert(DkdvCfg<DQK, DV, true>::LDS_ELEMS * 2 <= 160 * 1024, "bias stages fit the LDS");
-    if (a.bias) {
-      if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, true, false>), grid, dim3(D::NT), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, true, false>), grid, dim3(D::NT), 0, stream, a);
-      return hipGetLastError();
-    }
-  } else if (a.bias) {
-    return hipErrorInvalidValue;  // no bias variant for these head dims
-  }
-  if (a.drop_t > 0) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, true, false, false>), grid, dim3(D::NT), 0, stream, a);
-  else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DQK, DV, false, false, false>), grid, dim3(D::NT), 0, stream, a);
-  return hipGetLastError();
+  return a.ds ? launch_dkdv_variant<DQK, DV, true>(a, grid, stream) : launch_dkdv_variant<DQK, DV, false>(a, grid, stream);
 }
 
 int dkdv_head_splits(int B, int S, int Hkv, int G, bool causal, int wl, int wr, int dqk, int dv) {

@@ -3,8 +3,9 @@
 //
 // dQ = scale * dS K (PR #2225 backward: grad_q; dS = P * (dP - delta) as in
 // the other backward kernels).  When the workspace holds the bf16 dS blocks
-// the dK/dV kernel wrote (the B operands of its dK products, -dS there: that
-// kernel starts the dP accumulator at delta and negates V), dQ is a
+// the dK/dV kernel wrote (the B operands of its dK products: -dS without
+// dropout, where that kernel starts the dP accumulator at delta and negates
+// V, dS with it; ds_stored_sign), dQ is a
 // contraction of those blocks with K, with no recomputation of S or dP; the
 // pass is bound by streaming the blocks from HBM.  Deterministic: each
 // workgroup owns its rows' dQ and adds the key tiles in ascending order.
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
 
   // Lane: position l32 -> row acc_row(l32 % 16, l32 / 16) of each block;
   // dims db*32 + ig*8 + hf*4 + 0..3 from elements 4 ig .. 4 ig + 3.  The
-  // blocks hold -dS, so dQ = -scale * acc.
-  const float qs = -a.scale;
+  // blocks hold dS times ds_stored_sign, so dQ = sign * scale * acc.
+  const float qs = ds_stored_sign(a) * a.scale;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int qi = qw0 + rb * 32 + acc_row(l32 & 15, l32 >> 4);

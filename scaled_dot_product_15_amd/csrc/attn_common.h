@@ -84,6 +84,11 @@ struct KArgs {
 template <int DQK>
 constexpr bool kGroupedOrder = DQK >= 128;
 
+// Sign of the stored dS blocks: the dK/dV kernel stores the B operand of its
+// dK products, which is -dS where delta is folded into its dP products (no
+// dropout) and dS with dropout.
+__device__ __forceinline__ float ds_stored_sign(const KArgs& a) { return a.drop_t > 0 ? 1.0f : -1.0f; }
+
 // Stored-dS slab of key tile kt: its first block within the (batch, head)
 // region and its block count, from the mask at the full length S (a loop over
 // the tiles before it: a few scalar instructions each, once per workgroup).

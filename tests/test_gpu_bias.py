@@ -80,7 +80,8 @@ def test_bias_small_parity(dims, shape, mask, st, store_ds):
     assert rel <= gc.TOL["bf16"]["grad_rel_l2"], rel
 
 
-def test_bias_with_dropout():
+@pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
+def test_bias_with_dropout(store_ds):
     """Bias and attention dropout together, against the row- and key-sampled
     oracle evaluated on every row and key (small shape); the bias gradient of a
     full-shape bias is the rows' dS."""
@@ -91,8 +92,8 @@ def test_bias_with_dropout():
     t = inputs.to_torch(arr, "bf16", "cuda")
     bias = _bias(p, "full", seed)
     drop = (0.2, 1234, 7)
-    gc.log("bias + dropout")
-    (o, lse, dq, dk, dv, doff), dbias = _run(p, t, bias, dropout=drop)
+    gc.log(f"bias + dropout, store_ds={store_ds}")
+    (o, lse, dq, dk, dv, doff), dbias = _run(p, t, bias, dropout=drop, store_ds=store_ds)
     q, k, v, do, al, b64 = (gc.to64(x) for x in (t["q"], t["k"], t["v"], t["do"], t["alpha"], bias))
     kw = dict(num_gqa_groups=p.Hkv, causal=True, window=p.window, softmax_type=p.softmax_type, softmax_offset=al,
               dropout=drop, bias=b64)

@@ -92,19 +92,25 @@ MASKS = {"causal": (True, (-1, -1)), "causal_swa": (True, (37, 0)), "window": (F
 CASES = list(itertools.product(DIMS, MASKS, ("vanilla", "off_by_one", "learnable")))
 
 
-def _run(p, t, dropout_p, rng_state, want_d_offset=True):
+def _run(p, t, dropout_p, rng_state, want_d_offset=True, store_ds=False):
     import torch
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask", window_size=p.window,
               softmax_type=p.softmax_type, softmax_offset=t["alpha"], seqlens=t["seqlens"], dropout_p=dropout_p,
               rng_state=rng_state)
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
-    dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want_d_offset, **kw)
+    dq, dk, dv, doff = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], want_d_offset=want_d_offset,
+                                        store_ds=store_ds, **kw)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv, doff
 
 
-@pytest.mark.parametrize("dims,mask,st", CASES, ids=str)
-def test_dropout_parity(dims, mask, st):
+# bf16 cases also on the stored-dS backward (dK/dV stores the dropped dS, dQ
+# is contracted from it); fp32 has only the recomputing one.
+PATH_CASES = [c + (sd,) for c in CASES for sd in (False, True) if not (sd and DIMS[c[0]][0] == "f32")]
+
+
+@pytest.mark.parametrize("dims,mask,st,store_ds", PATH_CASES, ids=str)
+def test_dropout_parity(dims, mask, st, store_ds):
     dtype, dqk, dv = DIMS[dims]
     causal, win = MASKS[mask]
     p = inputs.Problem(B=2, S=200, Hq=4, Hkv=2, d_qk=dqk, d_v=dv, dtype=dtype, causal=causal, window=win,
@@ -113,8 +119,8 @@ def test_dropout_parity(dims, mask, st):
     arr = inputs.draw(p, seed)
     arr["seqlens"] = np.array([200, 131], dtype=np.int32)
     t = inputs.to_torch(arr, dtype, "cuda")
-    gc.log(f"dropout {dims} {mask} {st} seed={seed}")
-    g = _run(p, t, 0.2, (SEED + seed, OFFSET))
+    gc.log(f"dropout {dims} {mask} {st} seed={seed} store_ds={store_ds}")
+    g = _run(p, t, 0.2, (SEED + seed, OFFSET), store_ds=store_ds)
     f64 = inputs.exact_f64
     r = oracle.attention_dropout(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), p=0.2, seed=SEED + seed,
                                  offset=OFFSET, num_gqa_groups=p.Hkv, causal=causal, window=win, softmax_type=st,
@@ -143,8 +149,10 @@ def test_dropout_reproducible_and_p0(dims):
         assert torch.equal(x, y), "p = 0 must ignore the rng state"
 
 
-@pytest.mark.parametrize("dims,rate", [("bf16_128", 0.9), ("bf16_64", 0.6), ("f32_64", 0.9)], ids=str)
-def test_dropout_edge_cases(dims, rate):
+@pytest.mark.parametrize("dims,rate,store_ds", [("bf16_128", 0.9, False), ("bf16_64", 0.6, False),
+                                                ("f32_64", 0.9, False), ("bf16_128", 0.9, True),
+                                                ("bf16_64", 0.6, True)], ids=str)
+def test_dropout_edge_cases(dims, rate, store_ds):
     """High rates (large 1 / (1 - p)), an empty batch and a one-token batch."""
     dtype, dqk, dv = DIMS[dims]
     p = inputs.Problem(B=3, S=150, Hq=4, Hkv=1, d_qk=dqk, d_v=dv, dtype=dtype, causal=True, window=(40, 0),
@@ -153,11 +161,49 @@ def test_dropout_edge_cases(dims, rate):
     arr = inputs.draw(p, seed)
     arr["seqlens"] = np.array([150, 0, 1], dtype=np.int32)
     t = inputs.to_torch(arr, dtype, "cuda")
-    gc.log(f"dropout edge {dims} p={rate} seed={seed}")
-    g = _run(p, t, rate, (seed, 9))
+    gc.log(f"dropout edge {dims} p={rate} seed={seed} store_ds={store_ds}")
+    g = _run(p, t, rate, (seed, 9), store_ds=store_ds)
     f64 = inputs.exact_f64
     r = oracle.attention_dropout(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), p=rate, seed=seed, offset=9,
                                  num_gqa_groups=p.Hkv, causal=True, window=(40, 0), softmax_type="learnable",
                                  softmax_offset=f64(t["alpha"]), seqlens=arr["seqlens"])
     stats = gc.compare_full(p, t, g, r, tag=f"dropout edge/{dims}/{rate}", o_scale=_zscale(rate))
     gc.log(f"  {stats}")
+
+
+@pytest.mark.parametrize("dims", ["bf16_128", "bf16_192_128", "bf16_64"])
+def test_dropout_stored_ds_matches_recompute(dims):
+    """Dropout on the stored-dS backward, the workspace filled with NaN
+    patterns first: finite and bitwise the same on two calls; dV bitwise the
+    recomputing path's (the dK/dV kernel is the same but for its stores), dQ,
+    dK and the sink gradient equal to rounding."""
+    import torch
+    dtype, dqk, dv_ = DIMS[dims]
+    p = inputs.Problem(B=2, S=330, Hq=4, Hkv=2, d_qk=dqk, d_v=dv_, dtype=dtype, causal=True, window=(120, 0),
+                       softmax_type="learnable")
+    seed = 63_000 + dqk
+    arr = inputs.draw(p, seed)
+    arr["seqlens"] = np.array([330, 141], dtype=np.int32)
+    t = inputs.to_torch(arr, dtype, "cuda")
+    kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal", window_size=p.window, softmax_type=p.softmax_type,
+              softmax_offset=t["alpha"], seqlens=t["seqlens"], dropout_p=0.3, rng_state=(seed, 5))
+    o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, dqk, dv_, "bf16", "causal", p.window, None, p.softmax_type,
+                             0.3, (seed, 5))
+    size = binding.attn_bwd_ds_workspace_size(pp)
+    assert size > binding.attn_bwd_workspace_size(pp)
+    gc.log(f"dropout stored dS {dims}, stale workspace of {size} bytes")
+    ws = torch.full((size,), 0xFF, dtype=torch.uint8, device="cuda")
+    first = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], workspace=ws, **kw)
+    ws.fill_(0xFF)
+    second = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], workspace=ws, **kw)
+    recomputed = binding.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], store_ds=False, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.isfinite(a).all() and torch.equal(a, b)
+    assert torch.equal(first[2], recomputed[2])
+    for i, name in ((0, "dq"), (1, "dk")):
+        rel = gc.rel_l2(inputs.exact_f64(first[i]), inputs.exact_f64(recomputed[i]))
+        gc.log(f"  {name} stored vs recomputed rel_l2={rel:.3g}")
+        assert rel <= 5e-3, (name, rel)
+    assert np.allclose(first[3].cpu().numpy(), recomputed[3].cpu().numpy(), rtol=1e-3, atol=1e-5)
