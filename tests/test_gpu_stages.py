@@ -4,8 +4,9 @@ with the same workspace.
 
 Cases cover the bf16 path (pre-pass fused into the dQ stage), the fp32 path
 (separate pre-pass stage), the sink-gradient stage, padded batches and the
-dK/dV head split (fp32 partials reduced inside the dK/dV stage); with a
-workspace that holds the stored dS, the stages run in the order 1, 3, 2, 4.
+dK/dV head split (fp32 partials reduced inside the dK/dV stage), attention
+dropout; with a workspace that holds the stored dS, the stages run in the
+order 1, 3, 2, 4.
 """
 import numpy as np
 import pytest
@@ -25,10 +26,14 @@ CASES = {
                                        causal=True, window=(-1, -1), softmax_type="vanilla"),
     "f32_learnable": inputs.Problem(B=2, S=150, Hq=4, Hkv=2, d_qk=64, d_v=64, dtype="f32",
                                     causal=True, window=(-1, -1), softmax_type="learnable"),
+    "bf16_dropout_learnable": inputs.Problem(B=2, S=270, Hq=4, Hkv=2, d_qk=128, d_v=128, dtype="bf16",
+                                             causal=True, window=(90, 0), softmax_type="learnable"),
 }
+# attention dropout (rate, seed, offset) of the cases that use it
+DROPOUT = {"bf16_dropout_learnable": (0.2, 4242, 3)}
 
 
-STORED_DS = ("bf16_learnable_padded", "bf16_offbyone_64", "bf16_mla_vanilla")
+STORED_DS = ("bf16_learnable_padded", "bf16_offbyone_64", "bf16_mla_vanilla", "bf16_dropout_learnable")
 
 
 @pytest.mark.parametrize("name,stored", [(n, False) for n in CASES] + [(n, True) for n in STORED_DS])
@@ -43,10 +48,13 @@ def test_stages_match_one_call(name, stored):
     kw = dict(num_gqa_groups=p.Hkv, attn_mask_type="causal" if p.causal else "no_mask", window_size=p.window,
               scale_factor=p.scale_factor or None, softmax_type=p.softmax_type, softmax_offset=t["alpha"],
               seqlens=t["seqlens"])
+    drop = DROPOUT.get(name, (0.0, 0, 0))
+    if drop[0]:
+        kw.update(dropout_p=drop[0], rng_state=drop[1:])
     o, lse = binding.attn_fwd(t["q"], t["k"], t["v"], **kw)
     want = p.softmax_type != "vanilla"
     pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, p.dtype, kw["attn_mask_type"], p.window,
-                             kw["scale_factor"], p.softmax_type)
+                             kw["scale_factor"], p.softmax_type, drop[0], drop[1:])
     size = binding.attn_bwd_ds_workspace_size(pp) if stored else binding.attn_bwd_workspace_size(pp)
     assert size > 0
     ws = torch.empty(size, dtype=torch.uint8, device="cuda")
