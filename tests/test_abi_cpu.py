@@ -426,3 +426,30 @@ def test_fp8_validation_before_any_hip_call():
     assert lib.attn_fp8_update_scale(f, 0, f, 0, 0, f, f, None) == -1
     assert lib.attn_fp8_update_scale(f, 4097, f, 0, 0, f, f, None) == -1
     assert lib.attn_fp8_update_scale(f, 16, f, 3, 0, f, f, None) == -1
+
+
+def test_default_backward_path_rules():
+    """binding.prefers_stored_ds (the default of attn_bwd's store_ds): 192-dim
+    heads, dropout from head dim 128, biases shared over batches or heads; never
+    beyond DS_WORKSPACE_LIMIT or where the library has no such path."""
+    import torch
+
+    def bias(b, h, S=256):
+        return torch.empty((b, h, S, S), dtype=torch.bfloat16)
+
+    prefers = binding.prefers_stored_ds
+    assert not prefers(P())                                  # 128/128, no dropout, no bias
+    assert not prefers(P(d_qk=64, d_v=64))
+    assert prefers(P(d_qk=192, d_v=128))
+    d128, d64 = P(), P(d_qk=64, d_v=64)
+    d128.dropout_p = d64.dropout_p = 0.1
+    assert prefers(d128) and not prefers(d64)
+    d128.dropout_p = 0.001                                   # rounds to no dropout
+    assert not prefers(d128)
+    for b, h, want in ((1, 1, True), (1, 8, True), (2, 1, True), (2, 8, False)):
+        assert prefers(P(), bias(b, h)) == want, (b, h)
+        assert prefers(P(d_qk=64, d_v=64), bias(b, h)) == want, (b, h)
+    assert not prefers(P(dtype="f32", d_qk=64, d_v=64), bias(1, 1))      # no stored path in fp32
+    big = P(B=8, S=16384, Hq=64, Hkv=8, d_qk=192, d_v=128)               # causal, no window: > 8 GiB
+    assert binding.attn_bwd_ds_workspace_size(big) > binding.DS_WORKSPACE_LIMIT
+    assert not prefers(big)
