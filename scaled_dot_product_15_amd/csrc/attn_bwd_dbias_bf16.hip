@@ -278,7 +278,9 @@ __global__ __launch_bounds__(256) void dbias_from_ds_kernel(KArgs a) {
         const int h = a.bias_h == 1 ? hi : hh;
         const uint16_t* blk =
             a.ds + ((size_t)(b * a.Hq + h) * a.ds_head_blocks + first + r) * 4096 + w * 1024 + lane * 16;
-        const u32x4 v0 = ldg16(blk), v1 = ldg16(blk + 8);
+        // read once: non-temporal loads
+        const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk));
+        const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + 8));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[2 * e] += bf16_lo(v0[e]);

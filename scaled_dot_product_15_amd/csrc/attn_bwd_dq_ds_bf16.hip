@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(KArgs a) {
       const BufDesc d = buf_desc(src, ok ? 2048u : 0u);
       const uint32_t dst = lds_addr(dtile(buf, w, rb));
 #pragma unroll
-      for (int k = 0; k < 2; ++k) lds_dma16(d, dst + k * 1024, dvoff[k]);
+      for (int k = 0; k < 2; ++k) lds_dma16_nt(d, dst + k * 1024, dvoff[k]);
     }
   };
   // Step st from slot buf: wait for its copies (those of the NSLOT - 2 later

@@ -347,6 +347,14 @@ __device__ __forceinline__ void lds_dma16(const BufDesc& d, uint32_t lds_dst, ui
                : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_dst)), "v"(voff), "s"(uniform4(d.w))
                : "memory", "m0");
 }
+// The same copy with the non-temporal cache policy, for data read once
+// (streamed blocks that should not displace reused tiles in L2).
+__device__ __forceinline__ void lds_dma16_nt(const BufDesc& d, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_dst)), "v"(voff), "s"(uniform4(d.w))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4(const BufDesc& d, uint32_t lds_dst, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
