@@ -167,7 +167,7 @@ def prefers_stored_ds(p: Params, bias=None) -> bool:
     (2.09 -> 2.0 ms) and follows the head-dim rule.  With dropout the
     recomputing dQ kernel also regenerates every random byte, and from head
     dim 128 the stored dS is the faster path (same workload, p = 0.1: step
-    1.50 -> 1.43 ms; sink + padding S=8192, 6.6 GB of dS: 5.84 -> 5.57 ms);
+    1.55 -> 1.44 ms; sink + padding S=8192, 6.6 GB of dS: 5.97 -> 5.65 ms);
     at head dim 64 it is 2 % slower."""
     size = attn_bwd_ds_workspace_size(p)
     if not 0 < size <= DS_WORKSPACE_LIMIT:
