@@ -167,6 +167,43 @@ def test_bias_full_length_shared(store_ds):
     torch.cuda.empty_cache()
 
 
+def test_bias_full_length_per_head_default_path():
+    """S = 4096, window (1024, 0), GQA 32:8, one bias matrix per query head
+    shared by the 4 batches [1, Hq, S, S], on the binding's default backward
+    (the stored dS: dBias summed from the stored blocks).  Sampled rows of two
+    heads' bias gradients (each the sum of 4 batches' dS) and of dQ, plus the
+    exact zeros the window hides."""
+    import torch
+    p = inputs.Problem(B=4, S=4096, Hq=32, Hkv=8, d_qk=128, d_v=128, dtype="bf16", causal=True,
+                       window=(1024, 0), softmax_type="vanilla")
+    seed = 72_500
+    arr = inputs.draw(p, seed)
+    t = inputs.to_torch(arr, "bf16", "cuda")
+    bias = _bias(p, "heads", seed)
+    pp = binding.make_params(p.B, p.S, p.Hq, p.Hkv, p.d_qk, p.d_v, "bf16", "causal", p.window, None, "vanilla")
+    assert binding.prefers_stored_ds(pp, bias)
+    gc.log("bias full length, per head [1, 32, 4096, 4096], default (stored-dS) backward")
+    (o, lse, dq, dk, dv, _), dbias = _run(p, t, bias, store_ds=None)
+    q, k, v, do = (gc.to64(x.cpu()) for x in (t["q"], t["k"], t["v"], t["do"]))
+    kw = dict(num_gqa_groups=p.Hkv, causal=True, window=p.window, bias=gc.to64(bias))
+    brows = np.array([0, 777, 2048, 4095])
+    for h in (3, 30):
+        ref = np.zeros((len(brows), p.S))
+        for b in range(p.B):
+            rr = oracle.attention_rows(q, k, v, do, b=b, h=h, rows=brows, **kw)
+            ref[:, rr["cols"][0]:rr["cols"][1]] += rr["ds"]
+            if b == 1:
+                assert gc.rel_l2(gc.to64(dq[b, brows, h]), rr["dq"]) <= gc.TOL["bf16"]["grad_rel_l2"]
+        got = gc.to64(dbias[0, h, brows])
+        rel = gc.rel_l2(got, ref)
+        gc.log(f"  head {h}: dbias sampled rows rel_l2={rel:.3g}")
+        assert rel <= gc.TOL["bf16"]["grad_rel_l2"]
+        hidden = ~oracle.visible_rows(brows, p.S, p.S, True, p.window[0], p.window[1])
+        assert (got[hidden] == 0).all()
+    del bias, dbias
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("store_ds", (False, True), ids=("recompute", "stored_ds"))
 def test_bias_packed_equals_padded(store_ds):
     """Packed (THD) segments with a bias give bitwise the padded (BSHD)
