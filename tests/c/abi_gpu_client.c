@@ -5,6 +5,8 @@
  *   abi_gpu_client DIR
  *   DIR/params.txt: B S Hq Hkv Dqk Dv dtype mask window_left window_right
  *                   scale softmax_type dropout_p seed_lo seed_hi offset has_seqlens
+ *                   [store_ds]  (1: give attn_bwd attn_bwd_ds_workspace_size
+ *                   bytes, the stored-dS backward; default 0)
  *   DIR/{q,k,v,do}.bin  raw tensors of the problem's element type (BSHD)
  *   DIR/alpha.bin       float32 [Hq];  DIR/seqlens.bin int32 [B] if has_seqlens
  *   writes DIR/{o,dq,dk,dv}.bin, DIR/lse.bin (float32 [B,Hq,S]) and, for
@@ -76,7 +78,7 @@ int main(int argc, char** argv) {
   g_dir = argv[1];
   struct attn_params p;
   memset(&p, 0, sizeof p);
-  int has_seqlens = 0;
+  int has_seqlens = 0, store_ds = 0;
   {
     char path[4096];
     snprintf(path, sizeof path, "%s/params.txt", g_dir);
@@ -86,6 +88,7 @@ int main(int argc, char** argv) {
                          &p.num_gqa_groups, &p.head_dim_qk, &p.head_dim_v, &p.dtype, &p.mask_type, &p.window_left,
                          &p.window_right, &p.scale_factor, &p.softmax_type, &p.dropout_p, &p.dropout_seed_lo,
                          &p.dropout_seed_hi, &p.dropout_offset, &has_seqlens);
+    if (n == 17 && fscanf(f, "%d", &store_ds) != 1) store_ds = 0;
     fclose(f);
     if (n != 17) return fail("params.txt needs 17 fields");
   }
@@ -109,7 +112,8 @@ int main(int argc, char** argv) {
 
   void *o = NULL, *dq = NULL, *dk = NULL, *dv = NULL, *ws = NULL, *wsf = NULL;
   float *lse = NULL, *doff = NULL, *amax = NULL, *descales = NULL, *ds_scale = NULL;
-  const size_t ws_bytes = attn_bwd_workspace_size(&p);
+  const size_t ws_bytes = store_ds ? attn_bwd_ds_workspace_size(&p) : attn_bwd_workspace_size(&p);
+  if (store_ds && ws_bytes == 0) return fail("no stored-dS backward for this problem");
   const size_t wsf_bytes = attn_fwd_workspace_size(&p);
   if (hipMalloc(&o, no * eo) != hipSuccess || hipMalloc((void**)&lse, nlse * sizeof(float)) != hipSuccess ||
       hipMalloc(&dq, nq * eo) != hipSuccess || hipMalloc(&dk, nk * eo) != hipSuccess ||

@@ -1,5 +1,6 @@
 """The library driven from C alone: tests/c/abi_gpu_client (built by the build
-step with gcc) allocates with the HIP runtime, calls attn_fwd / attn_bwd
+step with gcc) allocates with the HIP runtime, calls attn_fwd / attn_bwd (with the
+minimum workspace, or with attn_bwd_ds_workspace_size bytes: the stored-dS path)
 through the C ABI and writes its outputs to files; no PyTorch in that
 process.  Its outputs are compared element by element with the float64
 oracle on the same seeded inputs, to the same bar as the other parity tests."""
@@ -30,17 +31,19 @@ def _from_bf16(raw, shape):
     return u.view(np.float32).astype(np.float64).reshape(shape)
 
 
-@pytest.mark.parametrize("dtype,dqk,dv,st,drop", [("bf16", 128, 128, "learnable", 0.15),
-                                                  ("bf16", 192, 128, "off_by_one", 0.0),
-                                                  ("f32", 64, 64, "vanilla", 0.0)], ids=str)
-def test_c_client_parity(tmp_path, dtype, dqk, dv, st, drop):
+@pytest.mark.parametrize("dtype,dqk,dv,st,drop,store_ds", [("bf16", 128, 128, "learnable", 0.15, 0),
+                                                           ("bf16", 192, 128, "off_by_one", 0.0, 0),
+                                                           ("f32", 64, 64, "vanilla", 0.0, 0),
+                                                           ("bf16", 128, 128, "learnable", 0.15, 1),
+                                                           ("bf16", 64, 64, "vanilla", 0.0, 1)], ids=str)
+def test_c_client_parity(tmp_path, dtype, dqk, dv, st, drop, store_ds):
     assert os.path.exists(CLIENT), "C client not built (the build step builds it)"
     p = inputs.Problem(B=2, S=190, Hq=4, Hkv=2, d_qk=dqk, d_v=dv, dtype=dtype, causal=True, window=(70, 0),
                        softmax_type=st)
     seed = 80_000 + dqk + int(drop * 100)
     arr = inputs.draw(p, seed)
     arr["seqlens"] = np.array([190, 77], dtype=np.int32)
-    gc.log(f"C client {dtype} {dqk}/{dv} {st} dropout={drop} seed={seed}")
+    gc.log(f"C client {dtype} {dqk}/{dv} {st} dropout={drop} store_ds={store_ds} seed={seed}")
     d = tmp_path
     vals = {}
     for n in ("q", "k", "v", "do"):
@@ -56,7 +59,7 @@ def test_c_client_parity(tmp_path, dtype, dqk, dv, st, drop):
     seed64 = 0x0123456789ABCDEF
     (d / "params.txt").write_text(
         f"{p.B} {p.S} {p.Hq} {p.Hkv} {dqk} {dv} {1 if dtype == 'bf16' else 0} 1 70 0 0 "
-        f"{binding.SOFTMAX[st]} {drop} {seed64 & 0xFFFFFFFF} {seed64 >> 32} 3 1\n")
+        f"{binding.SOFTMAX[st]} {drop} {seed64 & 0xFFFFFFFF} {seed64 >> 32} 3 1 {store_ds}\n")
     res = subprocess.run([CLIENT, str(d)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and res.stdout.strip() == "ok", res.stderr
 
